@@ -1,0 +1,196 @@
+"""Seeded synthetic inputs shared by the tests, the smoke check and the bench.
+
+This module holds none of the attention or codec arithmetic: it only draws
+random numbers with stated distributions and structure, and casts them to the
+storage dtype.  Everything it returns is an input; expected values are
+computed elsewhere from these same inputs.
+
+Two flavours:
+  * host (numpy, fp64 draws, cast to the storage dtype): small cases that the
+    fp64 oracle checks exhaustively;
+  * device (torch generator on the GPU): full-size buffers, for timing and for
+    parity on sampled sequences (the sampled slices are copied to the host).
+"""
+from dataclasses import dataclass
+from typing import Dict, Optional
+
+import numpy as np
+import torch
+
+TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def rng(*key: int) -> np.random.Generator:
+    return np.random.default_rng([int(k) for k in key])
+
+
+def as_stored(x: np.ndarray, dtype: str) -> torch.Tensor:
+    """Cast fp64 draws to the storage dtype (a CPU tensor)."""
+    return torch.from_numpy(np.ascontiguousarray(x)).to(TORCH_DTYPE[dtype])
+
+
+def gaussian_orthonormal(g: np.random.Generator, rows: int, cols: int,
+                         scale: float = 1.0) -> np.ndarray:
+    """Gaussian matrix orthonormalised by QR: orthonormal rows when wide,
+    orthonormal columns when tall; times `scale`."""
+    if rows >= cols:
+        q, r = np.linalg.qr(g.standard_normal((rows, cols)))
+        q = q * np.sign(np.diag(r))[None, :]
+        return q * scale
+    q, r = np.linalg.qr(g.standard_normal((cols, rows)))
+    q = q * np.sign(np.diag(r))[None, :]
+    return q.T * scale
+
+
+def frequency_paired_decoder(g: np.random.Generator, heads: int, d_h: int, r_k: int,
+                             scale: float = 1.0, complex_coeffs: bool = True) -> np.ndarray:
+    """Key decoders A [heads, d_h, r_k] built only from same-frequency pair blocks.
+
+    The key latent is m = r_k / d_h blocks of d_h numbers; in each block, as in
+    head space, dimension f pairs with f + d_h/2 (one rotary frequency per pair).
+    For head h and frequency f a coefficient vector alpha in C^m (unit norm)
+    maps the m latent pairs of frequency f to head pair f:
+        [a -c; c a] per block, with alpha_b = a + i c.
+    With complex_coeffs=False the coefficients are real (c = 0).
+    Rows of each A[h] are orthonormal (times `scale`)."""
+    assert d_h % 2 == 0 and r_k % d_h == 0
+    m, half = r_k // d_h, d_h // 2
+    A = np.zeros((heads, d_h, r_k))
+    for h in range(heads):
+        for f in range(half):
+            if complex_coeffs:
+                v = g.standard_normal(m) + 1j * g.standard_normal(m)
+            else:
+                v = g.standard_normal(m).astype(complex)
+            v = v / np.linalg.norm(v)
+            for b in range(m):
+                a, c = v[b].real, v[b].imag
+                A[h, f, b * d_h + f] = a
+                A[h, f, b * d_h + f + half] = -c
+                A[h, f + half, b * d_h + f] = c
+                A[h, f + half, b * d_h + f + half] = a
+    return A * scale
+
+
+def block_table(g: np.random.Generator, batch: int, pages_per_seq: int,
+                spare: int = 0) -> (np.ndarray, int):
+    """Each sequence gets `pages_per_seq` distinct physical pages drawn from a
+    random permutation of batch*pages_per_seq + spare pages (fragmentation)."""
+    n_pages = batch * pages_per_seq + spare
+    perm = g.permutation(n_pages)[: batch * pages_per_seq]
+    return perm.reshape(batch, pages_per_seq).astype(np.int32), n_pages
+
+
+@dataclass
+class DecodeInputs:
+    """One decode call's inputs, all CPU tensors in the storage dtype (int32
+    for indices).  Shapes: pages [n_pages, G*P*(r_k+r_v)], block_table
+    [B, max_pages], pos [B], q/k_cur/v_cur [B, H, d_h], ring_k/ring_v
+    [B, W+1, H, d_h], A [H, d_h, r_k], Bv [H, r_v, d_h]."""
+    heads: int
+    head_dim: int
+    groups: int
+    r_k: int
+    r_v: int
+    page_size: int
+    window: int
+    loop: int
+    loop_first: int
+    loop_last: int
+    rope_base: float
+    rope_baked: int
+    dtype: str
+    pages: torch.Tensor
+    block_table: torch.Tensor
+    pos: torch.Tensor
+    q: torch.Tensor
+    k_cur: torch.Tensor
+    v_cur: torch.Tensor
+    ring_k: torch.Tensor
+    ring_v: torch.Tensor
+    A: torch.Tensor
+    Bv: torch.Tensor
+
+    @property
+    def batch(self) -> int:
+        return int(self.pos.shape[0])
+
+    @property
+    def n_pages(self) -> int:
+        return int(self.pages.shape[0])
+
+
+def decode_inputs(seed: int, *, batch: int, heads: int, head_dim: int, groups: int,
+                  r_k: int, r_v: int, positions, window: int, dtype: str,
+                  page_size: int = 64, rope_base: float = 0.0, rope_baked: int = 0,
+                  loop: int = 2, loop_first: int = 2, loop_last: int = 4,
+                  latent_std: float = 1.0, exact_std: float = 1.0,
+                  map_scale: float = 1.0, paired: Optional[bool] = None,
+                  spare_pages: int = 3) -> DecodeInputs:
+    """Random decode-call inputs with the given shapes.
+
+    latents ~ N(0, latent_std^2); q ~ N(0, 1); exact window / current K and V
+    ~ N(0, exact_std^2); A frequency-paired when the key latent holds whole
+    d_h blocks and `paired` is not False (Gaussian-QR otherwise); B Gaussian-QR
+    with orthonormal columns.  Maps are multiplied by `map_scale`."""
+    g = rng(seed)
+    positions = np.asarray(positions, dtype=np.int64).reshape(batch)
+    max_pos = int(positions.max())
+    pages_per_seq = max(1, -(-(max_pos + 1) // page_size))
+    bt, n_pages = block_table(g, batch, pages_per_seq, spare_pages)
+    row = groups * page_size * (r_k + r_v)
+    pages = g.standard_normal((n_pages, row)) * latent_std
+    q = g.standard_normal((batch, heads, head_dim))
+    k_cur = g.standard_normal((batch, heads, head_dim)) * exact_std
+    v_cur = g.standard_normal((batch, heads, head_dim)) * exact_std
+    ring_k = g.standard_normal((batch, window + 1, heads, head_dim)) * exact_std
+    ring_v = g.standard_normal((batch, window + 1, heads, head_dim)) * exact_std
+    if paired is None:
+        paired = r_k % head_dim == 0
+    if paired:
+        A = frequency_paired_decoder(g, heads, head_dim, r_k, map_scale)
+    else:
+        A = np.stack([gaussian_orthonormal(g, head_dim, r_k, map_scale) for _ in range(heads)])
+    Bv = np.stack([gaussian_orthonormal(g, r_v, head_dim, map_scale) for _ in range(heads)])
+    return DecodeInputs(
+        heads=heads, head_dim=head_dim, groups=groups, r_k=r_k, r_v=r_v,
+        page_size=page_size, window=window, loop=loop, loop_first=loop_first,
+        loop_last=loop_last, rope_base=rope_base, rope_baked=rope_baked, dtype=dtype,
+        pages=as_stored(pages, dtype), block_table=torch.from_numpy(bt),
+        pos=torch.from_numpy(positions.astype(np.int32)),
+        q=as_stored(q, dtype), k_cur=as_stored(k_cur, dtype), v_cur=as_stored(v_cur, dtype),
+        ring_k=as_stored(ring_k, dtype), ring_v=as_stored(ring_v, dtype),
+        A=as_stored(A, dtype), Bv=as_stored(Bv, dtype))
+
+
+@dataclass
+class WriterInputs:
+    """Writer-call inputs: x [B, n_tok, n_loops, G, d_in], enc
+    [n_loops, G, r_k+r_v, d_in], pos [B, n_tok] (CPU tensors)."""
+    x: torch.Tensor
+    enc: torch.Tensor
+    pos: torch.Tensor
+
+
+def writer_inputs(seed: int, *, batch: int, n_tok: int, n_loops: int, groups: int,
+                  r_k: int, r_v: int, d_in: int, dtype: str, positions,
+                  enc_scale: float = 1.0, x_std: float = 1.0) -> WriterInputs:
+    """x ~ N(0, x_std^2); each encoder E_t (per group) Gaussian-QR with
+    orthonormal rows (or columns when r_k+r_v > d_in), times enc_scale."""
+    g = rng(seed)
+    x = g.standard_normal((batch, n_tok, n_loops, groups, d_in)) * x_std
+    enc = np.stack([np.stack([gaussian_orthonormal(g, r_k + r_v, d_in, enc_scale)
+                              for _ in range(groups)]) for _ in range(n_loops)])
+    pos = np.asarray(positions, dtype=np.int32).reshape(batch, n_tok)
+    return WriterInputs(x=as_stored(x, dtype), enc=as_stored(enc, dtype),
+                        pos=torch.from_numpy(pos))
+
+
+def device_normal(shape, dtype: str, seed: int, std: float = 1.0,
+                  device: str = "cuda") -> torch.Tensor:
+    """N(0, std^2) filled on the device from a seeded torch generator."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed))
+    t = torch.empty(shape, dtype=torch.float32, device=device)
+    t.normal_(0.0, std, generator=gen)
+    return t.to(TORCH_DTYPE[dtype])

@@ -1,0 +1,468 @@
+"""Pins of the fp64 oracle to facts that do not come from the oracle itself:
+numbers printed on the pages, closed forms, library routines on special cases,
+algebraic identities, and brute force on tiny inputs.
+
+Sources: "Hybrid Latent Attention" summary (picx.dev/p/a0K1YZ), sections
+"Summary (Overview)", "Key Problem", "Latent Writer" (Eq. 2), "Latent Reader"
+(Eqs. 3-4) and "Rotary Embedding Alignment"; "Looped Latent Attention" abstracts
+(acceptodds.com/papers/iclr2027-34396, searcharxiv.org/abs/2607.15456).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from synth import gen
+from tests.util import golden_kv, golden_lines, max_rel_err
+
+
+# ---------------------------------------------------------------- cache bytes
+def test_cache_bytes_match_printed_values():
+    """768 KiB -> 72 KiB per token, 10.7x ("Summary (Overview)", "Latent Writer")."""
+    g = golden_kv("cache_bytes.txt")
+    full = O.full_cache_bytes_per_token(int(g["layers"]), int(g["loops"]), int(g["d_model"]),
+                                        int(g["elem_bytes"]))
+    hla = O.hla_bytes_per_token(int(g["layers"]), int(g["r_k"]), int(g["r_v"]), int(g["r_1"]),
+                                int(g["elem_bytes"]))
+    assert full == g["full_cache_kib"] * 1024
+    assert hla == g["hla_kib"] * 1024
+    assert round(full / hla, 1) == g["ratio_1dp"]
+
+
+def test_cache_bytes_other_workloads():
+    # per-head LLA rank 32 on Ouro-1.4B: 16 heads x 64 numbers x 2 B x 24 layers = 48 KiB (16x)
+    per_layer = O.set_bytes_per_token(16, 32, 32, 2)
+    assert 24 * per_layer == 48 * 1024
+    assert O.full_cache_bytes_per_token(24, 4, 2048, 2) // (24 * per_layer) == 16
+    # LLA-2D, Huginn-like: one 5280 K + one 5280 V latent per token-layer vs 2*32*5280 (32x)
+    assert O.set_bytes_per_token(1, 5280, 5280, 2) * 32 == O.full_cache_bytes_per_token(1, 32, 5280, 2)
+
+
+# ---------------------------------------------------------------- rotary embedding
+def test_rope_closed_form():
+    theta = O.rope_theta(4, 10000.0)
+    np.testing.assert_allclose(theta, [1.0, 0.01], rtol=0, atol=1e-15)
+    for line in golden_lines("rope_closed_form.txt"):
+        idx, vals = line.split(":")
+        e = np.zeros(4)
+        e[int(idx)] = 1.0
+        want = np.array([float(v) for v in vals.split()])
+        np.testing.assert_allclose(O.rope_head(e, 3, 10000.0), want, rtol=0, atol=1e-15)
+
+
+def test_rope_group_properties():
+    g = gen.rng(11)
+    d_h, base = 16, 10000.0
+    x = g.standard_normal((5, d_h))
+    # R_0 = I, R_p orthogonal, R_p R_q = R_{p+q}
+    np.testing.assert_allclose(O.rope_head(x, 0, base), x, atol=1e-15)
+    np.testing.assert_allclose(np.linalg.norm(O.rope_head(x, 123, base), axis=1),
+                               np.linalg.norm(x, axis=1), rtol=1e-14)
+    np.testing.assert_allclose(O.rope_head(O.rope_head(x, 17, base), 40, base),
+                               O.rope_head(x, 57, base), atol=1e-12)
+    # inner product depends on the position difference only
+    y = g.standard_normal(d_h)
+    a = O.rope_head(x, 100, base) @ O.rope_head(y, 93, base)
+    b = O.rope_head(x, 7, base) @ O.rope_head(y, 0, base)
+    np.testing.assert_allclose(a, b, rtol=1e-12)
+    # no rotary embedding
+    np.testing.assert_array_equal(O.rope_head(x, 99, 0.0), x)
+
+
+def test_rope_latent_rotates_every_block_alike():
+    g = gen.rng(12)
+    d_h, m = 8, 3
+    c = g.standard_normal(d_h * m)
+    out = O.rope_latent(c, 29, 10000.0, d_h)
+    for b in range(m):
+        np.testing.assert_allclose(out[b * d_h:(b + 1) * d_h],
+                                   O.rope_head(c[b * d_h:(b + 1) * d_h], 29, 10000.0), atol=1e-15)
+
+
+@pytest.mark.parametrize("complex_coeffs", [True, False])
+def test_frequency_paired_decoders_commute(complex_coeffs):
+    """"Rotary Embedding Alignment": rotation commutes with combinations of key
+    pairs that share a frequency:  R_p A = A R~_p."""
+    g = gen.rng(13)
+    d_h, r_k, H = 8, 32, 3
+    A = gen.frequency_paired_decoder(g, H, d_h, r_k, complex_coeffs=complex_coeffs)
+    c = g.standard_normal(r_k)
+    for h in range(H):
+        for p in (0, 1, 77, 4095):
+            lhs = O.rope_head(A[h] @ c, p, 10000.0)
+            rhs = A[h] @ O.rope_latent(c, p, 10000.0, d_h)
+            np.testing.assert_allclose(lhs, rhs, atol=1e-13)
+        # orthonormal rows
+        np.testing.assert_allclose(A[h] @ A[h].T, np.eye(d_h), atol=1e-13)
+
+
+def test_dense_decoder_does_not_commute():
+    """Negative control: a dense map does not commute with the rotation."""
+    g = gen.rng(14)
+    d_h, r_k = 8, 32
+    A = gen.gaussian_orthonormal(g, d_h, r_k)
+    c = g.standard_normal(r_k)
+    lhs = O.rope_head(A @ c, 5, 10000.0)
+    rhs = A @ O.rope_latent(c, 5, 10000.0, d_h)
+    assert np.abs(lhs - rhs).max() > 1e-2
+
+
+# ---------------------------------------------------------------- store layout
+def test_store_layout_fixture():
+    kw = dict(groups=2, page_size=32, r_k=16, r_v=32)
+    for line in golden_lines("store_layout.txt"):
+        lhs, want = line.split(":")
+        kind, page, group, slot, dim = lhs.split()
+        fn = O.store_key_offset if kind == "key" else O.store_value_offset
+        assert int(fn(int(page), int(group), int(slot), int(dim), **kw)) == int(want)
+
+
+def test_store_layout_is_a_bijection():
+    kw = dict(groups=3, page_size=48, r_k=32, r_v=16)
+    n_pages = 2
+    R = kw["r_k"] + kw["r_v"]
+    p, g, s = np.meshgrid(np.arange(n_pages), np.arange(3), np.arange(48), indexing="ij")
+    ko = O.store_key_offset(p[..., None], g[..., None], s[..., None], np.arange(32), **kw)
+    vo = O.store_value_offset(p[..., None], g[..., None], s[..., None], np.arange(16), **kw)
+    allo = np.concatenate([ko.ravel(), vo.ravel()])
+    assert np.array_equal(np.sort(allo), np.arange(n_pages * 3 * 48 * R))
+
+
+def test_gather_follows_block_table():
+    kw = dict(groups=2, page_size=16, r_k=16, r_v=16)
+    n_pages = 4
+    pages = np.arange(n_pages * 2 * 16 * 32, dtype=np.float64).reshape(n_pages, -1)
+    bt = np.array([[2, 0], [3, 1]])
+    sK, sV = O.gather_latents(pages, bt, 1, 20, **kw)
+    # token 17 of sequence 1 sits in physical page 1, slot 1
+    assert sK[17, 1, 3] == O.store_key_offset(1, 1, 1, 3, **kw)
+    assert sV[17, 0, 9] == O.store_value_offset(1, 0, 1, 9, **kw)
+    assert sK[2, 0, 0] == O.store_key_offset(3, 0, 2, 0, **kw)
+
+
+# ---------------------------------------------------------------- writer (Eq. 2)
+def test_writer_placement_encoders_stack_inputs():
+    """With encoders that place loop t's input in its own block, c is exactly
+    the stack of the per-loop inputs (Eq. 2's sum of E_t h_t)."""
+    g = gen.rng(21)
+    B, n, T, G, d_in = 2, 3, 3, 2, 4
+    x = g.standard_normal((B, n, T, G, d_in))
+    R = T * d_in
+    enc = np.zeros((T, G, R, d_in))
+    for t in range(T):
+        for gg in range(G):
+            enc[t, gg, t * d_in:(t + 1) * d_in, :] = np.eye(d_in)
+    c = O.write_latents(x, enc, np.zeros((B, n), dtype=np.int64), r_k=R // 2)
+    np.testing.assert_array_equal(c, np.concatenate([x[:, :, t] for t in range(T)], axis=-1))
+
+
+def test_writer_linear_and_brute_force():
+    g = gen.rng(22)
+    B, n, T, G, d_in, r_k, r_v, d_h = 1, 2, 2, 2, 5, 8, 4, 4
+    x1 = g.standard_normal((B, n, T, G, d_in))
+    x2 = g.standard_normal((B, n, T, G, d_in))
+    enc = g.standard_normal((T, G, r_k + r_v, d_in))
+    pos = np.array([[3, 9]])
+    kw = dict(r_k=r_k, rope_base=10000.0, rope_baked=1, head_dim=d_h)
+    c1 = O.write_latents(x1, enc, pos, **kw)
+    c2 = O.write_latents(x2, enc, pos, **kw)
+    np.testing.assert_allclose(O.write_latents(x1 + 2 * x2, enc, pos, **kw), c1 + 2 * c2, atol=1e-12)
+    # brute force: explicit sums, then the rotation written with math.cos / math.sin
+    for tok in range(n):
+        p = int(pos[0, tok])
+        for gg in range(G):
+            raw = [sum(enc[t, gg, o, k] * x1[0, tok, t, gg, k] for t in range(T) for k in range(d_in))
+                   for o in range(r_k + r_v)]
+            want = list(raw)
+            half = d_h // 2
+            for blk in range(r_k // d_h):
+                for f in range(half):
+                    th = 10000.0 ** (-2.0 * f / d_h)
+                    a, b = raw[blk * d_h + f], raw[blk * d_h + f + half]
+                    want[blk * d_h + f] = a * math.cos(p * th) - b * math.sin(p * th)
+                    want[blk * d_h + f + half] = a * math.sin(p * th) + b * math.cos(p * th)
+            np.testing.assert_allclose(c1[0, tok, gg], want, atol=1e-12)
+
+
+# ---------------------------------------------------------------- decode
+def _complex_rope(x, p, base):
+    """Independent rotation for the references: pairs as complex numbers
+    z_f = x_f + i x_{f+d_h/2}, multiplied by exp(i p theta_f)."""
+    d_h = x.shape[-1]
+    half = d_h // 2
+    th = base ** (-2.0 * np.arange(half) / d_h) if base else np.zeros(half)
+    z = (x[..., :half] + 1j * x[..., half:]) * np.exp(1j * np.asarray(p)[..., None] * th)
+    return np.concatenate([z.real, z.imag], axis=-1)
+
+
+def _identity_hla(seed, *, H=2, d_h=4, T=3, n_tok=12, base=10000.0):
+    """Uncompressed looped K/V plus a full-rank identity HLA codec built from it."""
+    g = gen.rng(seed)
+    hd = H * d_h
+    k = g.standard_normal((T, n_tok, H, d_h))   # pre-rotation keys per loop
+    v = g.standard_normal((T, n_tok, H, d_h))
+    q = g.standard_normal((T, H, d_h))
+    # main set: loops 2..T, r_k = r_v = (T-1) H d_h ; loop-1 set: r_1 = H d_h
+    r_main = (T - 1) * hd
+    x_main = np.zeros((1, n_tok, T - 1, 1, 2 * hd))
+    enc_main = np.zeros((T - 1, 1, 2 * r_main, 2 * hd))
+    for t in range(2, T + 1):
+        x_main[0, :, t - 2, 0, :hd] = k[t - 1].reshape(n_tok, hd)
+        x_main[0, :, t - 2, 0, hd:] = v[t - 1].reshape(n_tok, hd)
+        enc_main[t - 2, 0, (t - 2) * hd:(t - 1) * hd, :hd] = np.eye(hd)
+        enc_main[t - 2, 0, r_main + (t - 2) * hd:r_main + (t - 1) * hd, hd:] = np.eye(hd)
+    x1 = np.zeros((1, n_tok, 1, 1, 2 * hd))
+    x1[0, :, 0, 0, :hd] = k[0].reshape(n_tok, hd)
+    x1[0, :, 0, 0, hd:] = v[0].reshape(n_tok, hd)
+    enc1 = np.zeros((1, 1, 2 * hd, 2 * hd))
+    enc1[0, 0] = np.eye(2 * hd)
+    pos = np.arange(n_tok)[None, :]
+    c_main = O.write_latents(x_main, enc_main, pos, r_k=r_main, rope_base=base, rope_baked=1, head_dim=d_h)
+    c_one = O.write_latents(x1, enc1, pos, r_k=hd, rope_base=base, rope_baked=1, head_dim=d_h)
+
+    def maps(t):
+        blk = 0 if t == 1 else t - 2
+        r = hd if t == 1 else r_main
+        A = np.zeros((H, d_h, r))
+        Bv = np.zeros((H, r, d_h))
+        for h in range(H):
+            A[h, :, blk * hd + h * d_h: blk * hd + (h + 1) * d_h] = np.eye(d_h)
+            Bv[h, blk * hd + h * d_h: blk * hd + (h + 1) * d_h, :] = np.eye(d_h)
+        c = c_one if t == 1 else c_main
+        return c[0, :, :, :r], c[0, :, :, r:], A, Bv
+
+    return k, v, q, maps
+
+
+def _ring(k_t, v_t, i, W, base):
+    H, d_h = k_t.shape[1:]
+    rk = np.full((1, W + 1, H, d_h), np.nan)
+    rv = np.full((1, W + 1, H, d_h), np.nan)
+    for j in range(max(0, i - W), i):
+        rk[0, j % (W + 1)] = _complex_rope(k_t[j], j, base)
+        rv[0, j % (W + 1)] = v_t[j]
+    return rk, rv
+
+
+def _sdpa_reference(k_t, v_t, q_t, i, base):
+    """Uncompressed attention of loop t at position i: torch's scaled dot
+    product attention in fp64 on the CPU over all tokens 0..i."""
+    H, d_h = q_t.shape
+    keys = np.stack([_complex_rope(k_t[j], j, base) for j in range(i + 1)])      # [i+1, H, d_h]
+    qr = _complex_rope(q_t, i, base)                                                # [H, d_h]
+    qq = torch.from_numpy(qr)[None, :, None, :]
+    kk = torch.from_numpy(keys.transpose(1, 0, 2).copy())[None]
+    vv = torch.from_numpy(v_t[: i + 1].transpose(1, 0, 2).copy())[None]
+    return torch.nn.functional.scaled_dot_product_attention(qq, kk, vv)[0, :, 0, :].numpy()
+
+
+@pytest.mark.parametrize("form", ["textbook", "absorbed"])
+@pytest.mark.parametrize("t", [1, 2, 3])
+@pytest.mark.parametrize("W", [0, 1, 4, 9, 20])
+def test_identity_codec_equals_uncompressed_attention(form, t, W):
+    """A full-rank identity codec must reproduce uncompressed looped attention,
+    for every window W (Eq. 4's single softmax makes the output W-independent)."""
+    base = 10000.0
+    k, v, q, maps = _identity_hla(31, base=base)
+    i = 10
+    sK, sV, A, Bv = maps(t)
+    rk, rv = _ring(k[t - 1], v[t - 1], i, W, base)
+    fn = O.textbook_decode if form == "textbook" else O.absorbed_decode
+    out = fn([sK], [sV], [i], q[t - 1][None], k[t - 1][i][None], v[t - 1][i][None], rk, rv, A, Bv,
+             window=W, rope_base=base)
+    ref = _sdpa_reference(k[t - 1], v[t - 1], q[t - 1], i, base)
+    np.testing.assert_allclose(out[0], ref, atol=1e-12)
+
+
+@pytest.mark.parametrize("form", ["textbook", "absorbed"])
+def test_identity_codec_per_head_lla(form):
+    """Per-head LLA identity codec (G = H, one set for loops 1..T)."""
+    g = gen.rng(32)
+    H, d_h, T, n_tok, base, W, i = 3, 4, 2, 9, 10000.0, 2, 8
+    k = g.standard_normal((T, n_tok, H, d_h))
+    v = g.standard_normal((T, n_tok, H, d_h))
+    q = g.standard_normal((H, d_h))
+    r = T * d_h
+    x = np.zeros((1, n_tok, T, H, 2 * d_h))
+    enc = np.zeros((T, H, 2 * r, 2 * d_h))
+    for t in range(T):
+        x[0, :, t, :, :d_h] = k[t]
+        x[0, :, t, :, d_h:] = v[t]
+        for h in range(H):
+            enc[t, h, t * d_h:(t + 1) * d_h, :d_h] = np.eye(d_h)
+            enc[t, h, r + t * d_h: r + (t + 1) * d_h, d_h:] = np.eye(d_h)
+    c = O.write_latents(x, enc, np.arange(n_tok)[None], r_k=r, rope_base=base, rope_baked=1, head_dim=d_h)
+    for t in range(1, T + 1):
+        A = np.zeros((H, d_h, r))
+        Bv = np.zeros((H, r, d_h))
+        for h in range(H):
+            A[h, :, (t - 1) * d_h: t * d_h] = np.eye(d_h)
+            Bv[h, (t - 1) * d_h: t * d_h, :] = np.eye(d_h)
+        rk, rv = _ring(k[t - 1], v[t - 1], i, W, base)
+        fn = O.textbook_decode if form == "textbook" else O.absorbed_decode
+        out = fn([c[0, :, :, :r]], [c[0, :, :, r:]], [i], q[None], k[t - 1][i][None],
+                 v[t - 1][i][None], rk, rv, A, Bv, window=W, rope_base=base)
+        np.testing.assert_allclose(out[0], _sdpa_reference(k[t - 1], v[t - 1], q, i, base), atol=1e-12)
+
+
+def test_sequential_steps_with_ring_update():
+    """Three decode steps in a row, the window maintained only by ring_update
+    and the latents only by the writer, still match uncompressed attention."""
+    base, W, t = 10000.0, 3, 2
+    k, v, q, maps = _identity_hla(33, n_tok=14, base=base)
+    sK, sV, A, Bv = maps(t)
+    i0 = 9
+    rk, rv = _ring(k[t - 1], v[t - 1], i0, W, base)
+    for i in range(i0, i0 + 3):
+        out = O.textbook_decode([sK], [sV], [i], q[t - 1][None], k[t - 1][i][None], v[t - 1][i][None],
+                                rk, rv, A, Bv, window=W, rope_base=base)
+        np.testing.assert_allclose(out[0], _sdpa_reference(k[t - 1], v[t - 1], q[t - 1], i, base),
+                                   atol=1e-12)
+        slot, nk, nv = O.ring_update([i], k[t - 1][i][None], v[t - 1][i][None], window=W,
+                                     rope_base=base)
+        rk[0, slot[0]] = nk[0]
+        rv[0, slot[0]] = nv[0]
+
+
+def _random_case(seed, *, B=2, H=4, G=2, d_h=8, r_k=16, r_v=12, W=3, base=10000.0, n=30,
+                 paired=True):
+    g = gen.rng(seed)
+    sK = [g.standard_normal((n, G, r_k)) for _ in range(B)]
+    sV = [g.standard_normal((n, G, r_v)) for _ in range(B)]
+    q = g.standard_normal((B, H, d_h))
+    kc = g.standard_normal((B, H, d_h))
+    vc = g.standard_normal((B, H, d_h))
+    rk = g.standard_normal((B, W + 1, H, d_h))
+    rv = g.standard_normal((B, W + 1, H, d_h))
+    if paired:
+        A = gen.frequency_paired_decoder(g, H, d_h, r_k)
+    else:
+        A = np.stack([gen.gaussian_orthonormal(g, d_h, r_k) for _ in range(H)])
+    Bv = np.stack([gen.gaussian_orthonormal(g, r_v, d_h) for _ in range(H)])
+    return sK, sV, q, kc, vc, rk, rv, A, Bv
+
+
+@pytest.mark.parametrize("pos", [[0, 29], [3, 4], [17, 2], [29, 25]])
+def test_absorbed_equals_textbook(pos):
+    """Step-6 identity: the absorbed read (Eq. 3/4) equals reconstruct-then-attend
+    when every key decoder is frequency-paired."""
+    args = _random_case(41)
+    kw = dict(window=3, rope_base=10000.0)
+    a = O.absorbed_decode(*args[:2], pos, *args[2:], **kw)
+    t = O.textbook_decode(*args[:2], pos, *args[2:], **kw)
+    assert max_rel_err(a, t) < 1e-12
+
+
+def test_absorbed_differs_from_textbook_for_dense_decoders():
+    """Negative control: with rotary embedding on and dense key decoders the two
+    forms disagree (so the previous test can fail)."""
+    args = _random_case(42, paired=False)
+    kw = dict(window=3, rope_base=10000.0)
+    a = O.absorbed_decode(*args[:2], [29, 20], *args[2:], **kw)
+    t = O.textbook_decode(*args[:2], [29, 20], *args[2:], **kw)
+    assert max_rel_err(a, t) > 1e-3
+    # ...and agree again without rotary embedding
+    kw0 = dict(window=3, rope_base=0.0)
+    assert max_rel_err(O.absorbed_decode(*args[:2], [29, 20], *args[2:], **kw0),
+                       O.textbook_decode(*args[:2], [29, 20], *args[2:], **kw0)) < 1e-12
+
+
+def test_first_token_returns_current_value():
+    """i = 0: the only attended token is the current one, so o = v_cur."""
+    sK, sV, q, kc, vc, rk, rv, A, Bv = _random_case(43)
+    for fn in (O.textbook_decode, O.absorbed_decode):
+        out = fn(sK, sV, [0, 0], q, kc, vc, rk, rv, A, Bv, window=3, rope_base=10000.0)
+        np.testing.assert_allclose(out, vc, atol=1e-15)
+
+
+def test_window_covering_context_ignores_latents():
+    """W >= i: no latent token is read, so changing the store changes nothing."""
+    sK, sV, q, kc, vc, rk, rv, A, Bv = _random_case(44)
+    sK2 = [x + 5.0 for x in sK]
+    sV2 = [x - 3.0 for x in sV]
+    for fn in (O.textbook_decode, O.absorbed_decode):
+        a = fn(sK, sV, [3, 2], q, kc, vc, rk, rv, A, Bv, window=3, rope_base=10000.0)
+        b = fn(sK2, sV2, [3, 2], q, kc, vc, rk, rv, A, Bv, window=3, rope_base=10000.0)
+        np.testing.assert_array_equal(a, b)
+
+
+def test_relative_position_invariance():
+    """Scores depend on positions only through i - j: with the query rotated at
+    i + delta and latents baked by the writer at j + delta, every latent score
+    of Eq. 3 is unchanged, and so is every exact-window score."""
+    g = gen.rng(45)
+    H, d_h, r, d_in, n, base = 2, 8, 16, 6, 20, 10000.0
+    x = g.standard_normal((1, n, 2, 1, d_in))
+    enc = g.standard_normal((2, 1, 2 * r, d_in))
+    A = gen.frequency_paired_decoder(g, H, d_h, r)
+    q = g.standard_normal(d_h)
+    k_ex = g.standard_normal((n, d_h))
+    i = n - 1
+    ref = None
+    for delta in (0, 37, 1000, 16000):
+        pos = np.arange(n)[None] + delta
+        c = O.write_latents(x, enc, pos, r_k=r, rope_base=base, rope_baked=1, head_dim=d_h)
+        s_lat = np.stack([c[0, :, 0, :r] @ O.rope_latent(A[h].T @ q, i + delta, base, d_h)
+                          for h in range(H)])
+        s_ex = O.rope_head(k_ex, np.arange(n) + delta, base) @ O.rope_head(q, i + delta, base)
+        if ref is None:
+            ref = (s_lat, s_ex)
+        else:
+            np.testing.assert_allclose(s_lat, ref[0], atol=1e-9)
+            np.testing.assert_allclose(s_ex, ref[1], atol=1e-9)
+
+
+def test_brute_force_loops_match_textbook():
+    """A pure-Python loop form (explicit sums, math.exp, math.cos/sin) on tiny
+    shapes, with dense non-square decoders and several groups."""
+    B, H, G, d_h, r_k, r_v, W, base = 2, 4, 2, 4, 6, 5, 2, 10000.0
+    sK, sV, q, kc, vc, rk, rv, A, Bv = _random_case(46, B=B, H=H, G=G, d_h=d_h, r_k=r_k, r_v=r_v,
+                                                    W=W, n=9, paired=False)
+    pos = [8, 1]
+
+    def rot(vec, p):
+        half = d_h // 2
+        out = list(vec)
+        for f in range(half):
+            th = base ** (-2.0 * f / d_h)
+            a, b = vec[f], vec[f + half]
+            out[f] = a * math.cos(p * th) - b * math.sin(p * th)
+            out[f + half] = a * math.sin(p * th) + b * math.cos(p * th)
+        return out
+
+    want = np.zeros((B, H, d_h))
+    for b in range(B):
+        i = pos[b]
+        for h in range(H):
+            g = h // (H // G)
+            keys, vals = [], []
+            for j in range(i + 1):
+                if j < i - W:
+                    keys.append([sum(A[h, e, r] * sK[b][j, g, r] for r in range(r_k)) for e in range(d_h)])
+                    vals.append([sum(Bv[h, r, e] * sV[b][j, g, r] for r in range(r_v)) for e in range(d_h)])
+                elif j < i:
+                    keys.append(list(rk[b, j % (W + 1), h]))
+                    vals.append(list(rv[b, j % (W + 1), h]))
+                else:
+                    keys.append(rot(kc[b, h], i))
+                    vals.append(list(vc[b, h]))
+            qr = rot(q[b, h], i)
+            logits = [sum(qr[e] * kk[e] for e in range(d_h)) / math.sqrt(d_h) for kk in keys]
+            mx = max(logits)
+            w = [math.exp(l - mx) for l in logits]
+            s = sum(w)
+            for e in range(d_h):
+                want[b, h, e] = sum(w[j] * vals[j][e] for j in range(len(keys))) / s
+    got = O.textbook_decode(sK, sV, pos, q, kc, vc, rk, rv, A, Bv, window=W, rope_base=base)
+    np.testing.assert_allclose(got, want, atol=1e-12)
+
+
+def test_ring_update_slot_and_rotation():
+    pos = np.array([0, 5, 130])
+    kc = np.ones((3, 1, 4))
+    slot, k, v = O.ring_update(pos, kc, 2 * kc, window=128, rope_base=10000.0)
+    assert list(slot) == [0, 5, 1]
+    np.testing.assert_allclose(k[2, 0], _complex_rope(np.ones(4), 130, 10000.0), atol=1e-14)
+    np.testing.assert_array_equal(v, 2 * kc)
