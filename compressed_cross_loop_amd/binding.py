@@ -1,0 +1,183 @@
+"""Thin Python binding of liblla.so (C ABI in include/lla.h).
+
+Argument marshalling only: torch tensors are passed as device pointers and
+the current torch stream as the HIP stream.  Every step of the decode path
+runs in the library's HIP kernels; if the library is missing this module
+raises at import time rather than falling back to anything else.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblla.so")
+
+LLA_OK = 0
+LLA_ERR_INVALID_ARGUMENT = 1
+LLA_ERR_UNSUPPORTED = 2
+LLA_ERR_WORKSPACE_TOO_SMALL = 3
+LLA_ERR_HIP = 4
+LLA_F32 = 0
+LLA_BF16 = 1
+LLA_FLAG_GENERIC = 1
+
+_DTYPES = {torch.float32: LLA_F32, torch.bfloat16: LLA_BF16}
+_TORCH = {LLA_F32: torch.float32, LLA_BF16: torch.bfloat16}
+
+
+class LlaSetDesc(ctypes.Structure):
+    _fields_ = [("n_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("groups", ctypes.c_int32), ("r_k", ctypes.c_int32), ("r_v", ctypes.c_int32),
+                ("loop_first", ctypes.c_int32), ("loop_last", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("rope_baked", ctypes.c_int32),
+                ("rope_base", ctypes.c_float), ("dtype", ctypes.c_int32)]
+
+
+class LlaStore(ctypes.Structure):
+    _fields_ = [("pages", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
+                ("max_pages_per_seq", ctypes.c_int32)]
+
+
+class LlaDecodeArgs(ctypes.Structure):
+    _fields_ = [("loop", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("max_pos_hint", ctypes.c_int32), ("splits", ctypes.c_int32),
+                ("flags", ctypes.c_int32), ("pos", ctypes.c_void_p), ("q", ctypes.c_void_p),
+                ("k_cur", ctypes.c_void_p), ("v_cur", ctypes.c_void_p),
+                ("ring_k", ctypes.c_void_p), ("ring_v", ctypes.c_void_p),
+                ("A", ctypes.c_void_p), ("B", ctypes.c_void_p), ("out", ctypes.c_void_p),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run compressed_cross_loop_amd/build.py "
+                      "(or __graft_entry__.build()) first")
+lib = ctypes.CDLL(LIB_PATH)
+
+_P = ctypes.POINTER
+lib.lla_write_latents.restype = ctypes.c_int
+lib.lla_write_latents.argtypes = [_P(LlaSetDesc), _P(LlaStore), ctypes.c_int32, ctypes.c_int32,
+                                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                                  ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+lib.lla_write_workspace_bytes.restype = ctypes.c_size_t
+lib.lla_write_workspace_bytes.argtypes = [_P(LlaSetDesc), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+for _name in ("lla_decode_reconstruct", "lla_decode_absorbed", "hla_decode_windowed"):
+    _f = getattr(lib, _name)
+    _f.restype = ctypes.c_int
+    _f.argtypes = [_P(LlaSetDesc), _P(LlaStore), ctypes.c_int32, _P(LlaDecodeArgs), ctypes.c_void_p]
+lib.lla_decode_workspace_bytes.restype = ctypes.c_size_t
+lib.lla_decode_workspace_bytes.argtypes = [_P(LlaSetDesc), ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.c_int32, ctypes.c_int32]
+lib.lla_decode_plan_splits.restype = ctypes.c_int32
+lib.lla_decode_plan_splits.argtypes = [_P(LlaSetDesc), ctypes.c_int32, ctypes.c_int32,
+                                       ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+lib.lla_bytes_per_token.restype = ctypes.c_size_t
+lib.lla_bytes_per_token.argtypes = [_P(LlaSetDesc)]
+lib.lla_status_string.restype = ctypes.c_char_p
+lib.lla_status_string.argtypes = [ctypes.c_int]
+lib.lla_abi_version.restype = ctypes.c_int32
+lib.lla_abi_version.argtypes = []
+
+
+class LlaError(RuntimeError):
+    def __init__(self, status):
+        self.status = status
+        super().__init__(f"lla status {status}: {lib.lla_status_string(status).decode()}")
+
+
+def _check(status):
+    if status != LLA_OK:
+        raise LlaError(status)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to liblla must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def set_desc(*, n_heads, head_dim, groups, r_k, r_v, loop_first, loop_last, page_size=64,
+             rope_baked=0, rope_base=0.0, dtype=LLA_BF16):
+    if isinstance(dtype, torch.dtype):
+        dtype = _DTYPES[dtype]
+    return LlaSetDesc(n_heads, head_dim, groups, r_k, r_v, loop_first, loop_last, page_size,
+                      rope_baked, rope_base, dtype)
+
+
+def store(pages, block_table, max_pages_per_seq=None):
+    if max_pages_per_seq is None:
+        max_pages_per_seq = block_table.shape[-1]
+    return LlaStore(_ptr(pages), _ptr(block_table), int(max_pages_per_seq))
+
+
+def lla_abi_version():
+    return lib.lla_abi_version()
+
+
+def lla_status_string(status):
+    return lib.lla_status_string(status).decode()
+
+
+def lla_bytes_per_token(desc):
+    return lib.lla_bytes_per_token(ctypes.byref(desc))
+
+
+def lla_write_workspace_bytes(desc, batch, n_tok, d_in):
+    return lib.lla_write_workspace_bytes(ctypes.byref(desc), batch, n_tok, d_in)
+
+
+def lla_decode_workspace_bytes(desc, batch, max_pos, window, splits=0):
+    return lib.lla_decode_workspace_bytes(ctypes.byref(desc), batch, max_pos, window, splits)
+
+
+def lla_decode_plan_splits(desc, batch, max_pos, window, splits=0, entry=1):
+    return lib.lla_decode_plan_splits(ctypes.byref(desc), batch, max_pos, window, splits, entry)
+
+
+def lla_write_latents(desc, st, *, pos, x, enc, workspace=None, stream=None):
+    """pos [B, n_tok] int32, x [B, n_tok, n_loops, G, d_in], enc [n_loops, G, r_k+r_v, d_in]."""
+    batch, n_tok = int(pos.shape[0]), int(pos.shape[1])
+    d_in = int(x.shape[-1])
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.lla_write_latents(ctypes.byref(desc), ctypes.byref(st), batch, n_tok, _ptr(pos),
+                                 _ptr(x), d_in, _ptr(enc), _ptr(workspace), ws_bytes,
+                                 _stream(stream)))
+
+
+def decode_args(*, loop, window, pos, q, k_cur, v_cur, ring_k, ring_v, A, B, out, workspace,
+                max_pos_hint, splits=0, flags=0):
+    ws_bytes = 0 if workspace is None or isinstance(workspace, int) else \
+        workspace.numel() * workspace.element_size()
+    return LlaDecodeArgs(loop, window, int(max_pos_hint), splits, flags, _ptr(pos), _ptr(q),
+                         _ptr(k_cur), _ptr(v_cur), _ptr(ring_k), _ptr(ring_v), _ptr(A), _ptr(B),
+                         _ptr(out), _ptr(workspace), ws_bytes)
+
+
+def _decode(fn, desc, st, batch, args, stream):
+    _check(fn(ctypes.byref(desc), ctypes.byref(st), batch, ctypes.byref(args), _stream(stream)))
+
+
+def lla_decode_reconstruct(desc, st, batch, args, stream=None):
+    _decode(lib.lla_decode_reconstruct, desc, st, batch, args, stream)
+
+
+def lla_decode_absorbed(desc, st, batch, args, stream=None):
+    _decode(lib.lla_decode_absorbed, desc, st, batch, args, stream)
+
+
+def hla_decode_windowed(desc, st, batch, args, stream=None):
+    _decode(lib.hla_decode_windowed, desc, st, batch, args, stream)
+
+
+def torch_dtype(desc):
+    return _TORCH[desc.dtype]

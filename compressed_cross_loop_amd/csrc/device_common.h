@@ -1,0 +1,58 @@
+// Device helpers shared by the gfx950 kernels: element conversion, paged
+// store addressing, rotary angles, wave reductions.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <math.h>
+
+namespace lla {
+
+typedef __bf16 bf16;
+
+__device__ __forceinline__ float to_f(float x) { return x; }
+__device__ __forceinline__ float to_f(bf16 x) { return static_cast<float>(x); }
+
+template <typename T> __device__ __forceinline__ T from_f(float x);
+template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f<bf16>(float x) { return static_cast<bf16>(x); }
+
+// Paged store: [page][group][P/16 tiles][16 key rows of rk | rv/16 x (16 dims x 16 tokens)]
+__device__ __forceinline__ int64_t tile_base(int64_t page, int g, int slot, int G, int P, int R) {
+  return ((page * G + g) * (int64_t)P + (slot & ~15)) * (int64_t)R;
+}
+__device__ __forceinline__ int64_t key_off(int64_t page, int g, int slot, int d, int G, int P, int R,
+                                           int rk) {
+  return tile_base(page, g, slot, G, P, R) + (slot & 15) * rk + d;
+}
+__device__ __forceinline__ int64_t val_off(int64_t page, int g, int slot, int d, int G, int P, int R,
+                                           int rk) {
+  return tile_base(page, g, slot, G, P, R) + 16 * rk + (d >> 4) * 256 + (d & 15) * 16 + (slot & 15);
+}
+
+// cos / sin of p * theta_f, theta_f = base^(-2f/d_h), evaluated in fp64
+// (positions reach 16K, where an fp32 angle would lose ~1e-3 rad).
+__device__ __forceinline__ void rope_cs(float base, int dh, int f, int pos, float& c, float& s) {
+  const double th = pow((double)base, -2.0 * (double)f / (double)dh);
+  double sd, cd;
+  sincos((double)pos * th, &sd, &cd);
+  c = (float)cd;
+  s = (float)sd;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// exp2 of (x - m) for the online softmax; m == -inf (nothing seen yet) gives 0
+__device__ __forceinline__ float exp2_diff(float x, float m) {
+  return (m == -INFINITY) ? 0.f : exp2f(x - m);
+}
+
+}  // namespace lla

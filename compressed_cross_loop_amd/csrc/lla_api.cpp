@@ -1,0 +1,261 @@
+// Host layer of the C ABI declared in include/lla.h: argument validation
+// (before anything is enqueued), the context-split plan, workspace layout,
+// and dispatch of the gfx950 kernels on the caller's stream.
+#include "lla.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+
+#include "lla_internal.h"
+
+namespace {
+
+using namespace lla;
+
+constexpr int kMaxHeadDim = 256;
+constexpr int kMaxLatent = 16384;     // r_k + r_v limit of the general kernels
+constexpr int kMaxWindow = 8192;
+constexpr int kTargetWorkgroups = 512;  // two per compute unit on MI355X (256 CUs)
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t elem_bytes(const lla_set_desc& d) { return d.dtype == LLA_BF16 ? 2 : 4; }
+
+lla_status check_desc(const lla_set_desc* d) {
+  if (!d) return LLA_ERR_INVALID_ARGUMENT;
+  if (d->n_heads <= 0 || d->head_dim <= 0 || (d->head_dim & 1)) return LLA_ERR_INVALID_ARGUMENT;
+  if (d->groups <= 0 || d->n_heads % d->groups) return LLA_ERR_INVALID_ARGUMENT;
+  if (d->r_k <= 0 || d->r_v <= 0 || d->r_k % kTile || d->r_v % kTile) return LLA_ERR_INVALID_ARGUMENT;
+  if (d->loop_first < 1 || d->loop_last < d->loop_first) return LLA_ERR_INVALID_ARGUMENT;
+  if (d->page_size <= 0 || d->page_size % kTile) return LLA_ERR_INVALID_ARGUMENT;
+  if (d->dtype != LLA_F32 && d->dtype != LLA_BF16) return LLA_ERR_INVALID_ARGUMENT;
+  if (!(d->rope_base >= 0.f) || !std::isfinite(d->rope_base)) return LLA_ERR_INVALID_ARGUMENT;
+  if (d->rope_baked != 0 && d->rope_baked != 1) return LLA_ERR_INVALID_ARGUMENT;
+  if (d->rope_baked && d->rope_base == 0.f) return LLA_ERR_INVALID_ARGUMENT;
+  if (d->rope_baked && d->r_k % d->head_dim) return LLA_ERR_UNSUPPORTED;
+  if (d->head_dim > kMaxHeadDim) return LLA_ERR_UNSUPPORTED;
+  if (d->r_k + d->r_v > kMaxLatent) return LLA_ERR_UNSUPPORTED;
+  return LLA_OK;
+}
+
+lla_status check_store(const lla_store* s) {
+  if (!s || !s->pages || !s->block_table || s->max_pages_per_seq <= 0) return LLA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(s->pages)) return LLA_ERR_INVALID_ARGUMENT;
+  return LLA_OK;
+}
+
+// ---------------------------------------------------------------- split plan
+struct Plan {
+  int S;
+  int chunk;
+};
+
+// Latent tokens of the longest sequence are cut into S contiguous ranges of
+// `chunk` tokens (a multiple of 64); `wgs` workgroups work on each
+// (sequence, range).  S aims at kTargetWorkgroups in flight.
+Plan make_plan(int batch, int max_pos, int window, int splits, int wgs) {
+  const int64_t n_lat = std::max<int64_t>(0, (int64_t)max_pos - window);
+  const int64_t tiles = std::max<int64_t>(1, (n_lat + kChunk - 1) / kChunk);
+  int64_t S = splits > 0 ? splits
+                         : (kTargetWorkgroups + (int64_t)batch * wgs - 1) / ((int64_t)batch * wgs);
+  S = std::min<int64_t>(std::max<int64_t>(S, 1), tiles);
+  const int64_t per = (tiles + S - 1) / S;
+  S = (tiles + per - 1) / per;
+  return Plan{(int)S, (int)(per * kChunk)};
+}
+
+bool use_mfma_scan(const lla_set_desc& d, int flags) {
+  if (flags & LLA_FLAG_GENERIC) return false;
+  if (d.dtype != LLA_BF16) return false;
+  DecodeParams p{};
+  p.hpg = d.n_heads / d.groups;
+  p.rk = d.r_k;
+  p.rv = d.r_v;
+  p.dh = d.head_dim;
+  p.bf16 = 1;
+  return scan_absorbed_mfma_supports(p);
+}
+
+Plan plan_for(const lla_set_desc& d, int batch, int max_pos, int window, int splits, int entry,
+              int flags) {
+  const bool absorbed = entry != 0;
+  const int wgs = (absorbed && use_mfma_scan(d, flags)) ? d.groups : d.n_heads;
+  return make_plan(batch, max_pos, window, splits, wgs);
+}
+
+struct WsLayout {
+  size_t qlat, qhead, part_ml, part_o, win_ml, win_o, total;
+};
+
+size_t up256(size_t x) { return (x + 255) & ~size_t(255); }
+
+WsLayout ws_layout(const lla_set_desc& d, int B, int S, int Dp) {
+  WsLayout w{};
+  const size_t H = d.n_heads, dh = d.head_dim;
+  size_t off = 0;
+  w.qlat = off;    off = up256(off + (size_t)B * H * d.r_k * elem_bytes(d));
+  w.qhead = off;   off = up256(off + (size_t)B * H * dh * 4);
+  w.part_ml = off; off = up256(off + (size_t)B * S * H * 2 * 4);
+  w.part_o = off;  off = up256(off + (size_t)B * S * H * Dp * 4);
+  w.win_ml = off;  off = up256(off + (size_t)B * H * 2 * 4);
+  w.win_o = off;   off = up256(off + (size_t)B * H * dh * 4);
+  w.total = off;
+  return w;
+}
+
+size_t decode_ws_bytes(const lla_set_desc& d, int batch, int max_pos, int window, int splits) {
+  // enough for every entry point and kernel family at these sizes
+  int S = 1;
+  for (int entry = 0; entry < 2; ++entry)
+    for (int flags = 0; flags < 2; ++flags)
+      S = std::max(S, plan_for(d, batch, max_pos, window, splits, entry, flags).S);
+  return ws_layout(d, batch, S, std::max(d.r_v, d.head_dim)).total;
+}
+
+lla_status hip_status(hipError_t e) { return e == hipSuccess ? LLA_OK : LLA_ERR_HIP; }
+
+lla_status decode(const lla_set_desc* d, const lla_store* st, int32_t batch,
+                  const lla_decode_args* a, lla_stream_t stream, int entry) {
+  // entry: 0 reconstruct, 1 absorbed (LLA-D), 2 HLA windowed
+  lla_status r = check_desc(d);
+  if (r != LLA_OK) return r;
+  if ((r = check_store(st)) != LLA_OK) return r;
+  if (batch <= 0 || !a) return LLA_ERR_INVALID_ARGUMENT;
+  if (a->loop < d->loop_first || a->loop > d->loop_last) return LLA_ERR_INVALID_ARGUMENT;
+  if (a->window < 0 || a->max_pos_hint < 0 || a->splits < 0) return LLA_ERR_INVALID_ARGUMENT;
+  if (a->flags & ~LLA_FLAG_GENERIC) return LLA_ERR_INVALID_ARGUMENT;
+  const void* ptrs[] = {a->pos, a->q, a->k_cur, a->v_cur, a->ring_k, a->ring_v, a->A, a->B, a->out};
+  for (const void* p : ptrs)
+    if (!p || !aligned16(p)) return LLA_ERR_INVALID_ARGUMENT;
+  if (entry == 2 && d->groups != 1) return LLA_ERR_INVALID_ARGUMENT;
+  if (a->window > kMaxWindow) return LLA_ERR_UNSUPPORTED;
+  if (d->rope_base > 0.f && !d->rope_baked) return LLA_ERR_UNSUPPORTED;
+  const size_t need = decode_ws_bytes(*d, batch, a->max_pos_hint, a->window, a->splits);
+  if (!a->workspace || a->workspace_bytes < need) return LLA_ERR_WORKSPACE_TOO_SMALL;
+  if (!aligned16(a->workspace)) return LLA_ERR_INVALID_ARGUMENT;
+
+  const bool absorbed = entry != 0;
+  const Plan plan = plan_for(*d, batch, a->max_pos_hint, a->window, a->splits, absorbed ? 1 : 0, a->flags);
+  const int Dp = std::max(d->r_v, d->head_dim);
+  const WsLayout w = ws_layout(*d, batch, plan.S, Dp);
+  char* ws = static_cast<char*>(a->workspace);
+
+  DecodeParams p{};
+  p.B = batch; p.H = d->n_heads; p.dh = d->head_dim; p.G = d->groups; p.hpg = d->n_heads / d->groups;
+  p.rk = d->r_k; p.rv = d->r_v; p.P = d->page_size; p.W = a->window;
+  p.S = plan.S; p.chunk = plan.chunk; p.Dp = Dp; p.max_pages = st->max_pages_per_seq;
+  p.mode = absorbed ? kAbsorbed : kReconstruct;
+  p.bf16 = d->dtype == LLA_BF16;
+  p.rope_base = d->rope_base;
+  p.scale = (float)(1.4426950408889634 / std::sqrt((double)d->head_dim));
+  p.pos = a->pos; p.bt = st->block_table; p.pages = st->pages;
+  p.q = a->q; p.k_cur = a->k_cur; p.v_cur = a->v_cur; p.ring_k = a->ring_k; p.ring_v = a->ring_v;
+  p.A = a->A; p.Bm = a->B; p.out = a->out;
+  p.qlat = ws + w.qlat;
+  p.qhead = reinterpret_cast<float*>(ws + w.qhead);
+  p.part_ml = reinterpret_cast<float*>(ws + w.part_ml);
+  p.part_o = reinterpret_cast<float*>(ws + w.part_o);
+  p.win_ml = reinterpret_cast<float*>(ws + w.win_ml);
+  p.win_o = reinterpret_cast<float*>(ws + w.win_o);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_qmap(p, absorbed, s);
+  if (e == hipSuccess) e = launch_window(p, s);
+  if (e == hipSuccess) {
+    if (!absorbed)
+      e = launch_scan_reconstruct_generic(p, s);
+    else if (use_mfma_scan(*d, a->flags))
+      e = launch_scan_absorbed_mfma(p, s);
+    else
+      e = launch_scan_absorbed_generic(p, s);
+  }
+  if (e == hipSuccess) e = launch_combine(p, s);
+  return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+lla_status lla_write_latents(const lla_set_desc* desc, const lla_store* store, int32_t batch,
+                             int32_t n_tok, const int32_t* pos, const void* x, int32_t d_in,
+                             const void* enc, void* workspace, size_t workspace_bytes,
+                             lla_stream_t stream) {
+  lla_status r = check_desc(desc);
+  if (r != LLA_OK) return r;
+  if ((r = check_store(store)) != LLA_OK) return r;
+  if (batch <= 0 || n_tok <= 0 || d_in <= 0) return LLA_ERR_INVALID_ARGUMENT;
+  const void* ptrs[] = {pos, x, enc};
+  for (const void* p : ptrs)
+    if (!p || !aligned16(p)) return LLA_ERR_INVALID_ARGUMENT;
+  const size_t need = lla_write_workspace_bytes(desc, batch, n_tok, d_in);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return LLA_ERR_WORKSPACE_TOO_SMALL;
+  if (workspace && !aligned16(workspace)) return LLA_ERR_INVALID_ARGUMENT;
+  (void)workspace_bytes;
+
+  WriterParams p{};
+  p.B = batch; p.n_tok = n_tok; p.n_loops = desc->loop_last - desc->loop_first + 1;
+  p.G = desc->groups; p.rk = desc->r_k; p.rv = desc->r_v; p.R = desc->r_k + desc->r_v;
+  p.d_in = d_in; p.P = desc->page_size; p.dh = desc->head_dim;
+  p.max_pages = store->max_pages_per_seq;
+  p.rope_baked = desc->rope_baked; p.bf16 = desc->dtype == LLA_BF16; p.rope_base = desc->rope_base;
+  p.pos = pos; p.bt = store->block_table; p.pages = store->pages; p.x = x; p.enc = enc;
+  p.acc = static_cast<float*>(workspace);
+  p.ksplit = 1;
+  return hip_status(launch_writer_generic(p, static_cast<hipStream_t>(stream)));
+}
+
+size_t lla_write_workspace_bytes(const lla_set_desc* desc, int32_t batch, int32_t n_tok, int32_t d_in) {
+  if (check_desc(desc) != LLA_OK || batch <= 0 || n_tok <= 0 || d_in <= 0) return 0;
+  return 0;
+}
+
+lla_status lla_decode_reconstruct(const lla_set_desc* desc, const lla_store* store, int32_t batch,
+                                  const lla_decode_args* args, lla_stream_t stream) {
+  return decode(desc, store, batch, args, stream, 0);
+}
+
+lla_status lla_decode_absorbed(const lla_set_desc* desc, const lla_store* store, int32_t batch,
+                               const lla_decode_args* args, lla_stream_t stream) {
+  return decode(desc, store, batch, args, stream, 1);
+}
+
+lla_status hla_decode_windowed(const lla_set_desc* desc, const lla_store* store, int32_t batch,
+                               const lla_decode_args* args, lla_stream_t stream) {
+  return decode(desc, store, batch, args, stream, 2);
+}
+
+size_t lla_decode_workspace_bytes(const lla_set_desc* desc, int32_t batch, int32_t max_pos,
+                                  int32_t window, int32_t splits) {
+  if (check_desc(desc) != LLA_OK || batch <= 0 || max_pos < 0 || window < 0 || splits < 0) return 0;
+  return decode_ws_bytes(*desc, batch, max_pos, window, splits);
+}
+
+int32_t lla_decode_plan_splits(const lla_set_desc* desc, int32_t batch, int32_t max_pos,
+                               int32_t window, int32_t splits, int32_t entry) {
+  if (check_desc(desc) != LLA_OK || batch <= 0 || max_pos < 0 || window < 0 || splits < 0) return 0;
+  return plan_for(*desc, batch, max_pos, window, splits, entry ? 1 : 0, 0).S;
+}
+
+size_t lla_bytes_per_token(const lla_set_desc* desc) {
+  if (check_desc(desc) != LLA_OK) return 0;
+  return (size_t)desc->groups * (desc->r_k + desc->r_v) * elem_bytes(*desc);
+}
+
+const char* lla_status_string(lla_status status) {
+  switch (status) {
+    case LLA_OK: return "ok";
+    case LLA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case LLA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case LLA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case LLA_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+int32_t lla_abi_version(void) { return LLA_ABI_VERSION; }
+
+}  // extern "C"

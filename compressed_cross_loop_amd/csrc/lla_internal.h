@@ -1,0 +1,72 @@
+// Internal interface between the host layer (lla_api.cpp) and the gfx950
+// kernels: plain parameter blocks passed by value, and launcher functions.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lla {
+
+constexpr int kTile = 16;        // tokens per store tile
+constexpr int kChunk = 64;       // split granularity in tokens
+
+enum Mode : int32_t { kAbsorbed = 1, kReconstruct = 0 };
+
+struct DecodeParams {
+  // shapes
+  int32_t B, H, dh, G, hpg, rk, rv, P, W;
+  int32_t S, chunk;               // context splits and tokens per split
+  int32_t Dp;                     // width of latent partial rows (r_v or d_h)
+  int32_t max_pages;
+  int32_t mode;
+  int32_t bf16;                   // storage dtype: 1 = bf16, 0 = fp32
+  float rope_base;
+  float scale;                    // log2(e) / sqrt(d_h)
+  // caller buffers
+  const int32_t* pos;
+  const int32_t* bt;
+  const void* pages;
+  const void* q;
+  const void* k_cur;
+  const void* v_cur;
+  void* ring_k;
+  void* ring_v;
+  const void* A;
+  const void* Bm;
+  void* out;
+  // workspace regions
+  void* qlat;                     // [B][H][rk]  storage dtype
+  float* qhead;                   // [B][H][dh]
+  float* part_ml;                 // [B][S][H][2]
+  float* part_o;                  // [B][S][H][Dp]
+  float* win_ml;                  // [B][H][2]
+  float* win_o;                   // [B][H][dh]
+};
+
+struct WriterParams {
+  int32_t B, n_tok, n_loops, G, rk, rv, R, d_in, P, dh, max_pages;
+  int32_t rope_baked;
+  int32_t bf16;
+  float rope_base;
+  const int32_t* pos;
+  const int32_t* bt;
+  void* pages;
+  const void* x;
+  const void* enc;
+  float* acc;                     // workspace [ksplit][B*n_tok][G][R] (MFMA path)
+  int32_t ksplit;
+};
+
+hipError_t launch_qmap(const DecodeParams& p, bool want_qlat, hipStream_t s);
+hipError_t launch_window(const DecodeParams& p, hipStream_t s);
+hipError_t launch_scan_absorbed_generic(const DecodeParams& p, hipStream_t s);
+hipError_t launch_scan_reconstruct_generic(const DecodeParams& p, hipStream_t s);
+hipError_t launch_combine(const DecodeParams& p, hipStream_t s);
+
+// matrix-core kernels (bf16 only); return hipErrorNotSupported for shapes
+// they do not cover, before launching anything
+bool scan_absorbed_mfma_supports(const DecodeParams& p);
+hipError_t launch_scan_absorbed_mfma(const DecodeParams& p, hipStream_t s);
+
+hipError_t launch_writer_generic(const WriterParams& p, hipStream_t s);
+
+}  // namespace lla

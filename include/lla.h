@@ -1,0 +1,235 @@
+/*
+ * lla.h -- C ABI of the MI355X (gfx950) decode-attention library for looped
+ * Transformers whose per-loop KV cache is replaced by cross-loop latents:
+ * Looped Latent Attention (LLA: reconstruct keys/values on read; LLA-D: read
+ * latents directly) and Hybrid Latent Attention (HLA: direct latent read plus
+ * an exact window of recent tokens).
+ *
+ * Sources (cited by page title and section / equation):
+ *   [HLA]   "Hybrid Latent Attention" summary, picx.dev/p/a0K1YZ -- sections
+ *           "Latent Writer" (Eq. 2), "Latent Reader" (Eqs. 3 and 4), "Rotary
+ *           Embedding Alignment", "Key Insight", "Key Problem".
+ *   [LLA-A] "Looped Latent Attention: Cross-Loop Key-Value Compression For
+ *           Looped Transformers", abstract (acceptodds.com/papers/iclr2027-34396).
+ *   [LLA-S] "Looped Latent Attention: Cross-Loop KV Compression for Looped
+ *           Transformers", abstract (searcharxiv.org/abs/2607.15456).
+ *
+ * Conventions shared by every entry point
+ *   - Pointers are device pointers unless marked (host).  Every device buffer
+ *     is owned by the caller; the library never allocates, frees or keeps a
+ *     pointer after it returns, and never synchronises the stream.  Work is
+ *     enqueued on `stream` (a hipStream_t; NULL = the null stream); buffers
+ *     must stay alive until the stream has passed the call.
+ *   - Arguments are validated on the host before anything is enqueued: an
+ *     error status means nothing was launched and no buffer was touched.
+ *     LLA_ERR_HIP means a launch failed; the store, ring or output may then
+ *     be partly written.
+ *   - Device-resident indices (positions, block tables) are not validated on
+ *     the host; out-of-range values are undefined behaviour.
+ *   - Every device pointer must be 16-byte aligned.
+ *   - dtype LLA_BF16: latents, activations, maps, ring and outputs are bf16,
+ *     arithmetic is fp32 with fp32 accumulation (roundings to bf16 are
+ *     round-to-nearest-even).  LLA_F32: everything fp32.
+ *   - Rotary embedding: pairs (f, f + d_h/2) of a head vector rotate by
+ *     angle p*theta_f, theta_f = rope_base^(-2f/d_h), p the 0-based absolute
+ *     position; in a key latent of m = r_k/d_h blocks every block rotates the
+ *     same way (R~_p = I_m (x) R_p, [HLA] "Rotary Embedding Alignment").
+ *     rope_base == 0 disables it.
+ *   - The library is re-entrant and holds no state.  Calls that share a
+ *     workspace, store or ring must be ordered on one stream by the caller.
+ */
+#ifndef LLA_H
+#define LLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LLA_ABI_VERSION 1
+
+typedef void* lla_stream_t; /* a hipStream_t */
+
+typedef enum {
+  LLA_OK = 0,
+  LLA_ERR_INVALID_ARGUMENT = 1,
+  LLA_ERR_UNSUPPORTED = 2,
+  LLA_ERR_WORKSPACE_TOO_SMALL = 3,
+  LLA_ERR_HIP = 4
+} lla_status;
+
+typedef enum { LLA_F32 = 0, LLA_BF16 = 1 } lla_dtype;
+
+/* Decode flags (lla_decode_args.flags). */
+#define LLA_FLAG_GENERIC 1 /* use the general VALU kernels even where a
+                              matrix-core kernel exists (testing, tuning) */
+
+/*
+ * One latent set of one layer (host struct).  A set serves loops
+ * loop_first..loop_last: HLA has a loop-1 set {1,1} and a main set {2,T}
+ * ([HLA] "Latent Writer", Eq. 2); LLA has one set {1,T} ([LLA-A]).
+ *   n_heads, head_dim   H, d_h of the attention that reads the set
+ *   groups              G latents per token: 1 = shared by all heads (HLA,
+ *                       LLA-2D), H = one per head (per-head LLA); head h
+ *                       reads group h / (H/G).  H % G == 0.
+ *   r_k, r_v            key / value latent width per group; multiples of 16
+ *   page_size           tokens per store page; a multiple of 16
+ *   rope_baked          1: key latents are stored rotated, R~_p c^K
+ *                       (needs r_k % head_dim == 0 and rope_base > 0)
+ *   rope_base           0 = no rotary embedding
+ *   dtype               storage and map dtype
+ */
+typedef struct {
+  int32_t n_heads, head_dim;
+  int32_t groups;
+  int32_t r_k, r_v;
+  int32_t loop_first, loop_last;
+  int32_t page_size;
+  int32_t rope_baked;
+  float rope_base;
+  lla_dtype dtype;
+} lla_set_desc;
+
+/*
+ * Paged latent store of one set of one layer.
+ *   pages        [n_pages][G][P/16 tiles][tile], one tile = 16 tokens:
+ *                  16 key rows of r_k numbers (token-major), then
+ *                  r_v/16 value sub-blocks of 16 dims x 16 tokens, each
+ *                  stored dimension-major (16 tokens of one dim contiguous).
+ *                Element offset of key dim d of slot u, group g, page pg:
+ *                  ((pg*G + g)*P + (u/16)*16)*(r_k+r_v) + (u%16)*r_k + d
+ *                and of value dim d:
+ *                  ((pg*G + g)*P + (u/16)*16)*(r_k+r_v) + 16*r_k
+ *                    + (d/16)*256 + (d%16)*16 + u%16
+ *   block_table  [batch][max_pages_per_seq] physical page of logical page
+ *                p/P of each sequence (host-side: only its shape is used)
+ */
+typedef struct {
+  void* pages;
+  const int32_t* block_table;
+  int32_t max_pages_per_seq;
+} lla_store;
+
+/*
+ * Latent writer, [HLA] "Latent Writer" Eq. 2: for every token (b, n) at
+ * position p = pos[b*n_tok + n] and every group g,
+ *     c = sum over the set's loops t of E_t x_t      (fp32 accumulation)
+ * the key part is replaced by R~_p c^K when rope_baked, the result is
+ * rounded to the storage dtype and written to page block_table[b][p/P],
+ * slot p % P.
+ *   x     [batch][n_tok][n_loops][G][d_in]   per-loop inputs h_{j,t}
+ *   enc   [n_loops][G][r_k + r_v][d_in]      encoders E_t, c = E_t x
+ *   workspace  scratch of lla_write_workspace_bytes() bytes (may be NULL
+ *              when that is 0)
+ * Errors: INVALID_ARGUMENT (null pointer, bad sizes, misalignment),
+ * UNSUPPORTED (rope_baked with r_k % head_dim != 0), WORKSPACE_TOO_SMALL.
+ */
+lla_status lla_write_latents(const lla_set_desc* desc, const lla_store* store,
+                             int32_t batch, int32_t n_tok, const int32_t* pos,
+                             const void* x, int32_t d_in, const void* enc,
+                             void* workspace, size_t workspace_bytes,
+                             lla_stream_t stream);
+size_t lla_write_workspace_bytes(const lla_set_desc* desc, int32_t batch,
+                                 int32_t n_tok, int32_t d_in);
+
+/*
+ * Arguments of one decode call: one layer, one loop t, every sequence b at
+ * its current position i = pos[b] (N = i + 1 tokens attended).  Tokens
+ * j < i - W are read from the latent store, tokens i-W <= j < i from the
+ * exact ring, and the current token from k_cur / v_cur; one softmax spans
+ * all of them ([HLA] "Latent Reader", Eq. 4).  Scores are scaled by
+ * 1/sqrt(d_h) (Eq. 3).
+ *   loop          t, in [loop_first, loop_last] of the set
+ *   window        W >= 0; the ring has W+1 slots
+ *   max_pos_hint  (host) an upper bound of pos[], used only to plan the
+ *                 context split; a larger pos[] stays correct
+ *   splits        0 = plan automatically; > 0 forces the number of context
+ *                 splits (results then are bitwise reproducible)
+ *   flags         LLA_FLAG_* bits
+ *   pos           [batch] int32 current positions
+ *   q, k_cur, v_cur  [batch][H][d_h]: this loop's query, key (both before
+ *                 rotation) and value of the current token
+ *   ring_k, ring_v   [batch][W+1][H][d_h]: slot j mod (W+1) holds the
+ *                 rotated key / the value of exact token j.  The call writes
+ *                 slot i mod (W+1) with R_i k_cur and v_cur (that slot's old
+ *                 token, i-W-1, is a latent token from now on).
+ *   A             [H][d_h][r_k]  key decoder A_t of this loop (per head)
+ *   B             [H][r_v][d_h]  value map B_t (o = B_t^T c^V)
+ *   out           [batch][H][d_h]
+ *   workspace     scratch of lla_decode_workspace_bytes() bytes; contents
+ *                 on entry are irrelevant
+ */
+typedef struct {
+  int32_t loop;
+  int32_t window;
+  int32_t max_pos_hint;
+  int32_t splits;
+  int32_t flags;
+  const int32_t* pos;
+  const void* q;
+  const void* k_cur;
+  const void* v_cur;
+  void* ring_k;
+  void* ring_v;
+  const void* A;
+  const void* B;
+  void* out;
+  void* workspace;
+  size_t workspace_bytes;
+} lla_decode_args;
+
+/*
+ * Reconstruct-on-read (LLA, [LLA-A] / [LLA-S]: "reconstructs loop-specific
+ * K/V vectors only when attention reads them"): every latent token's key
+ * k_j = A^(h) sK_j and value v_j = B^(h)T sV_j are rebuilt, then ordinary
+ * attention with q' = R_i q runs over latent, window and current tokens.
+ * With a baked store, A^(h) sK_j is the rotated key when A_t is
+ * frequency-paired.  UNSUPPORTED when rope_base > 0 and rope_baked == 0.
+ */
+lla_status lla_decode_reconstruct(const lla_set_desc* desc, const lla_store* store,
+                                  int32_t batch, const lla_decode_args* args,
+                                  lla_stream_t stream);
+
+/*
+ * Absorbed read (LLA-D, [LLA-A]: "reads latents without reconstruction";
+ * [HLA] Eqs. 3-4): q~ = R~_i A_t^T q, latent scores q~ . sK_j / sqrt(d_h),
+ * o = B_t^T sum_lat a_j sV_j + sum_exact a_j v_j.  Any G.  Needs
+ * rope_baked == 1 or rope_base == 0 (else UNSUPPORTED).
+ */
+lla_status lla_decode_absorbed(const lla_set_desc* desc, const lla_store* store,
+                               int32_t batch, const lla_decode_args* args,
+                               lla_stream_t stream);
+
+/*
+ * Hybrid Latent Attention decode ([HLA] Eqs. 3-4 with the exact window of
+ * "Key Insight"): the absorbed read on an HLA set (G == 1).  Pass the loop-1
+ * set and its maps for t = 1 and the main set for t >= 2.
+ */
+lla_status hla_decode_windowed(const lla_set_desc* desc, const lla_store* store,
+                               int32_t batch, const lla_decode_args* args,
+                               lla_stream_t stream);
+
+/* Workspace bytes any decode entry point needs for these sizes (splits as
+ * in lla_decode_args; 0 = automatic). */
+size_t lla_decode_workspace_bytes(const lla_set_desc* desc, int32_t batch,
+                                  int32_t max_pos, int32_t window, int32_t splits);
+
+/* Number of context splits the planner uses for these sizes and entry
+ * (0 = reconstruct, 1 = absorbed / HLA); 0 on invalid arguments. */
+int32_t lla_decode_plan_splits(const lla_set_desc* desc, int32_t batch, int32_t max_pos,
+                               int32_t window, int32_t splits, int32_t entry);
+
+/* Bytes one set stores per token (all groups): G*(r_k + r_v)*sizeof(dtype)
+ * ([HLA] "Latent Writer": r_k + r_v (+ 2 r_1) numbers per token per layer).
+ * 0 on an invalid descriptor. */
+size_t lla_bytes_per_token(const lla_set_desc* desc);
+
+const char* lla_status_string(lla_status status);
+int32_t lla_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LLA_H */

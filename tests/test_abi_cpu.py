@@ -1,0 +1,174 @@
+"""Host-only checks of the C-ABI library: it loads, exports every function
+include/lla.h declares, and rejects invalid arguments with the documented
+status before anything is enqueued (these calls never reach a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle as O
+from compressed_cross_loop_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lla.h")
+
+FAKE = 0x10000  # aligned, non-null, never dereferenced: validation fails first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:lla_status|size_t|int32_t|const char\s*\*)\s+(\w+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert len(names) >= 10
+    lib = ctypes.CDLL(B.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_and_status_strings():
+    assert B.lla_abi_version() == 1
+    for s in range(5):
+        assert B.lla_status_string(s)
+    assert B.lla_status_string(99) == "unknown status"
+
+
+def hla_main(**kw):
+    d = dict(n_heads=16, head_dim=128, groups=1, r_k=512, r_v=512, loop_first=2, loop_last=4,
+             page_size=64, rope_baked=1, rope_base=10000.0, dtype=B.LLA_BF16)
+    d.update(kw)
+    return B.set_desc(**d)
+
+
+def test_bytes_per_token_matches_closed_form():
+    main = hla_main()
+    one = hla_main(r_k=256, r_v=256, loop_first=1, loop_last=1)
+    per_layer = B.lla_bytes_per_token(main) + B.lla_bytes_per_token(one)
+    assert 24 * per_layer == O.hla_bytes_per_token(24, 512, 512, 256, 2) == 72 * 1024
+    lla = hla_main(groups=16, r_k=32, r_v=32, loop_first=1, loop_last=4, rope_baked=0, rope_base=0.0)
+    assert B.lla_bytes_per_token(lla) == O.set_bytes_per_token(16, 32, 32, 2)
+    f32 = hla_main(dtype=B.LLA_F32)
+    assert B.lla_bytes_per_token(f32) == 2 * B.lla_bytes_per_token(main)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(n_heads=0), dict(head_dim=127), dict(groups=3), dict(r_k=500), dict(r_v=0),
+    dict(loop_first=0), dict(loop_first=3, loop_last=2), dict(page_size=40), dict(dtype=7),
+    dict(rope_base=-1.0), dict(rope_baked=2), dict(rope_baked=1, rope_base=0.0),
+])
+def test_invalid_descriptor(bad):
+    d = hla_main(**bad)
+    assert B.lla_bytes_per_token(d) == 0
+    assert B.lla_decode_workspace_bytes(d, 4, 100, 16) == 0
+
+
+def test_unsupported_descriptor():
+    # rope baked into a key latent that is not whole d_h blocks
+    d = hla_main(r_k=96, r_v=96)
+    st = B.LlaStore(FAKE, FAKE, 4)
+    args = B.LlaDecodeArgs(2, 16, 100, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30)
+    assert B.lib.hla_decode_windowed(ctypes.byref(d), ctypes.byref(st), 4, ctypes.byref(args), None) \
+        == B.LLA_ERR_UNSUPPORTED
+    big = hla_main(head_dim=512, r_k=512)
+    assert B.lib.hla_decode_windowed(ctypes.byref(big), ctypes.byref(st), 4, ctypes.byref(args), None) \
+        == B.LLA_ERR_UNSUPPORTED
+
+
+def _args(**kw):
+    a = dict(loop=2, window=16, max_pos_hint=100, splits=0, flags=0, pos=FAKE, q=FAKE, k_cur=FAKE,
+             v_cur=FAKE, ring_k=FAKE, ring_v=FAKE, A=FAKE, B=FAKE, out=FAKE, workspace=FAKE,
+             workspace_bytes=1 << 40)
+    a.update(kw)
+    return B.LlaDecodeArgs(*[a[f] for f, _ in B.LlaDecodeArgs._fields_])
+
+
+ENTRIES = ["lla_decode_reconstruct", "lla_decode_absorbed", "hla_decode_windowed"]
+
+
+@pytest.mark.parametrize("entry", ENTRIES)
+@pytest.mark.parametrize("bad, want", [
+    (dict(loop=1), B.LLA_ERR_INVALID_ARGUMENT),
+    (dict(loop=5), B.LLA_ERR_INVALID_ARGUMENT),
+    (dict(window=-1), B.LLA_ERR_INVALID_ARGUMENT),
+    (dict(splits=-2), B.LLA_ERR_INVALID_ARGUMENT),
+    (dict(flags=8), B.LLA_ERR_INVALID_ARGUMENT),
+    (dict(q=None), B.LLA_ERR_INVALID_ARGUMENT),
+    (dict(ring_v=None), B.LLA_ERR_INVALID_ARGUMENT),
+    (dict(out=FAKE + 2), B.LLA_ERR_INVALID_ARGUMENT),
+    (dict(pos=None), B.LLA_ERR_INVALID_ARGUMENT),
+    (dict(window=100000), B.LLA_ERR_UNSUPPORTED),
+    (dict(workspace=None), B.LLA_ERR_WORKSPACE_TOO_SMALL),
+    (dict(workspace_bytes=1024), B.LLA_ERR_WORKSPACE_TOO_SMALL),
+])
+def test_decode_argument_errors(entry, bad, want):
+    d = hla_main()
+    st = B.LlaStore(FAKE, FAKE, 4)
+    fn = getattr(B.lib, entry)
+    assert fn(ctypes.byref(d), ctypes.byref(st), 4, ctypes.byref(_args(**bad)), None) == want
+
+
+@pytest.mark.parametrize("entry", ENTRIES)
+def test_decode_null_struct_and_store(entry):
+    d = hla_main()
+    fn = getattr(B.lib, entry)
+    st = B.LlaStore(FAKE, FAKE, 4)
+    a = _args(workspace_bytes=1024)
+    assert fn(None, ctypes.byref(st), 4, ctypes.byref(a), None) == B.LLA_ERR_INVALID_ARGUMENT
+    assert fn(ctypes.byref(d), None, 4, ctypes.byref(a), None) == B.LLA_ERR_INVALID_ARGUMENT
+    assert fn(ctypes.byref(d), ctypes.byref(st), 4, None, None) == B.LLA_ERR_INVALID_ARGUMENT
+    assert fn(ctypes.byref(d), ctypes.byref(st), 0, ctypes.byref(a), None) == B.LLA_ERR_INVALID_ARGUMENT
+    for bad in (B.LlaStore(None, FAKE, 4), B.LlaStore(FAKE, None, 4), B.LlaStore(FAKE, FAKE, 0),
+                B.LlaStore(FAKE + 8, FAKE, 4)):
+        assert fn(ctypes.byref(d), ctypes.byref(bad), 4, ctypes.byref(a), None) == B.LLA_ERR_INVALID_ARGUMENT
+
+
+def test_hla_requires_one_group_and_rotation_needs_baking():
+    st = B.LlaStore(FAKE, FAKE, 4)
+    per_head = hla_main(groups=16, r_k=32, r_v=32, rope_baked=0, rope_base=0.0, loop_first=1)
+    a = _args()
+    assert B.lib.hla_decode_windowed(ctypes.byref(per_head), ctypes.byref(st), 4, ctypes.byref(a), None) \
+        == B.LLA_ERR_INVALID_ARGUMENT
+    unbaked = hla_main(rope_baked=0)
+    for entry in ("lla_decode_reconstruct", "lla_decode_absorbed"):
+        assert getattr(B.lib, entry)(ctypes.byref(unbaked), ctypes.byref(st), 4, ctypes.byref(a), None) \
+            == B.LLA_ERR_UNSUPPORTED
+
+
+def test_writer_argument_errors():
+    d = hla_main()
+    st = B.LlaStore(FAKE, FAKE, 4)
+    f = B.lib.lla_write_latents
+    ok = (ctypes.byref(d), ctypes.byref(st), 4, 1, FAKE, FAKE, 2048, FAKE, None, 0, None)
+
+    def call(**kw):
+        a = list(ok)
+        names = ["desc", "store", "batch", "n_tok", "pos", "x", "d_in", "enc", "ws", "wsb", "stream"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return f(*a)
+
+    assert call(batch=0) == B.LLA_ERR_INVALID_ARGUMENT
+    assert call(n_tok=0) == B.LLA_ERR_INVALID_ARGUMENT
+    assert call(d_in=0) == B.LLA_ERR_INVALID_ARGUMENT
+    assert call(pos=None) == B.LLA_ERR_INVALID_ARGUMENT
+    assert call(x=FAKE + 4) == B.LLA_ERR_INVALID_ARGUMENT
+    assert call(enc=None) == B.LLA_ERR_INVALID_ARGUMENT
+    assert call(desc=None) == B.LLA_ERR_INVALID_ARGUMENT
+    assert call(store=None) == B.LLA_ERR_INVALID_ARGUMENT
+
+
+def test_workspace_and_plan():
+    d = hla_main()
+    # workspace grows with batch and context; the plan never exceeds the tile count
+    assert B.lla_decode_workspace_bytes(d, 128, 4095, 128) > B.lla_decode_workspace_bytes(d, 32, 4095, 128)
+    assert B.lla_decode_plan_splits(d, 1, 10, 16) == 1          # no latent tokens: one empty split
+    assert B.lla_decode_plan_splits(d, 1, 4095, 128, splits=1000) == (4095 - 128 + 63) // 64
+    assert B.lla_decode_plan_splits(d, 128, 4095, 128, splits=3) == 3
+    for b, ctx in ((128, 4096), (32, 16384), (1, 256)):
+        s = B.lla_decode_plan_splits(d, b, ctx - 1, 128)
+        assert 1 <= s <= max(1, (ctx - 1 - 128 + 63) // 64)
