@@ -1,0 +1,291 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the C-ABI library on one MI355X.
+
+One step = one decode step of every sequence in the batch: for each loop t
+in order and each layer, one decode call (latent scan + exact window +
+combine), then each layer's latent writes (Eq. 2 of the Hybrid Latent
+Attention summary).  Inputs are synthetic and resident in HBM before timing.
+
+Prints ONE JSON line: decode tokens/s, the step's algorithmic HBM bytes per
+second and its fraction of 8 TB/s, the dominant kernel's roofline figures
+(timed live with HIP events around its launches), and the fp64 oracle timed
+on the host cores on a bounded sample.
+"""
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "decode tokens/s and achieved HBM GB/s (% roofline), Ouro-1.4B shape, 4k ctx"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=3, help="workload number (3 = HLA, batch 128, 4k)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--splits", type=int, default=0)
+    return ap.parse_args()
+
+
+class Hip:
+    """Raw HIP events (the library's kernels run on torch's current stream)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        assert self.lib.hipEventCreate(ctypes.byref(e)) == 0
+        return e
+
+    def record(self, e, stream):
+        assert self.lib.hipEventRecord(e, ctypes.c_void_p(stream)) == 0
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        assert self.lib.hipEventSynchronize(b) == 0
+        assert self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return float(ms.value)
+
+
+# --------------------------------------------------------------------------- HLA
+class HlaStep:
+    """Every buffer of one HLA decode step (all layers, all loops), on the GPU."""
+
+    def __init__(self, w, splits=0, seed=0):
+        import torch
+        from compressed_cross_loop_amd import binding as B
+        from synth import gen
+        self.torch, self.B, self.w = torch, B, w
+        dev = "cuda"
+        dt = gen.TORCH_DTYPE[w.dtype]
+        L, T, H, dh, Bt, P, W = w.layers, w.loops, w.heads, w.head_dim, w.batch, w.page_size, w.window
+        self.i = w.context - 1
+        ppseq = -(-w.context // P)
+        self.sets = []
+        for k, s in enumerate(w.sets):
+            desc = B.set_desc(n_heads=H, head_dim=dh, groups=s.groups, r_k=s.r_k, r_v=s.r_v,
+                              loop_first=s.loop_first, loop_last=s.loop_last, page_size=P,
+                              rope_baked=w.rope_baked, rope_base=w.rope_base,
+                              dtype=B.LLA_BF16 if w.dtype == "bf16" else B.LLA_F32)
+            g = gen.rng(seed, 77, k)
+            bt = torch.from_numpy(gen.block_table(g, Bt, ppseq)[0]).to(dev)
+            n_pages = Bt * ppseq
+            row = s.groups * P * (s.r_k + s.r_v)
+            std = float(np.sqrt(s.n_loops))  # latents of |L_s| unit-variance loops
+            pages = [gen.device_normal((n_pages, row), w.dtype, seed * 1000 + 10 * l + k, std)
+                     for l in range(L)]
+            enc = [gen.device_normal((s.n_loops, s.groups, s.r_k + s.r_v, s.d_in), w.dtype,
+                                     seed * 1000 + 500 + 10 * l + k, 1.0 / np.sqrt(s.d_in)) for l in range(L)]
+            x = [gen.device_normal((Bt, 1, s.n_loops, s.groups, s.d_in), w.dtype,
+                                   seed * 1000 + 700 + 10 * l + k) for l in range(L)]
+            self.sets.append(dict(spec=s, desc=desc, bt=bt, pages=pages, enc=enc, x=x,
+                                  stores=[B.store(pg, bt) for pg in pages]))
+        self.pos = torch.full((Bt,), self.i, dtype=torch.int32, device=dev)
+        self.wpos = torch.full((Bt, 1), self.i, dtype=torch.int32, device=dev)
+        ws = max(B.lla_decode_workspace_bytes(st["desc"], Bt, self.i, W, splits) for st in self.sets)
+        self.ws = torch.empty(ws, dtype=torch.uint8, device=dev)
+        wws = max(B.lla_write_workspace_bytes(st["desc"], Bt, 1, st["spec"].d_in) for st in self.sets)
+        self.wws = torch.empty(max(wws, 256), dtype=torch.uint8, device=dev)
+        self.calls = []   # (loop, set index, desc, store, args)
+        self.outs = []
+        for t in range(1, T + 1):
+            k = w.set_for_loop(t)
+            s = w.sets[k]
+            for l in range(L):
+                sd = seed * 100000 + 1000 * t + 10 * l
+                q = gen.device_normal((Bt, H, dh), w.dtype, sd + 1)
+                kc = gen.device_normal((Bt, H, dh), w.dtype, sd + 2, float(np.sqrt(s.n_loops)))
+                vc = gen.device_normal((Bt, H, dh), w.dtype, sd + 3, float(np.sqrt(s.n_loops)))
+                rk = gen.device_normal((Bt, W + 1, H, dh), w.dtype, sd + 4, float(np.sqrt(s.n_loops)))
+                rv = gen.device_normal((Bt, W + 1, H, dh), w.dtype, sd + 5, float(np.sqrt(s.n_loops)))
+                A = gen.device_normal((H, dh, s.r_k), w.dtype, sd + 6, 1.0 / np.sqrt(s.r_k))
+                Bm = gen.device_normal((H, s.r_v, dh), w.dtype, sd + 7, 1.0 / np.sqrt(s.r_v))
+                out = torch.empty((Bt, H, dh), dtype=dt, device=dev)
+                bufs = (q, kc, vc, rk, rv, A, Bm, out)
+                args = B.decode_args(loop=t, window=W, pos=self.pos, q=q, k_cur=kc, v_cur=vc, ring_k=rk,
+                                     ring_v=rv, A=A, B=Bm, out=out, workspace=self.ws,
+                                     max_pos_hint=self.i, splits=splits)
+                self.calls.append((t, k, l, self.sets[k]["desc"], self.sets[k]["stores"][l], args, bufs))
+        self.entry = B.hla_decode_windowed if w.family == "hla" else B.lla_decode_absorbed
+        torch.cuda.synchronize()
+
+    def step(self):
+        B = self.B
+        for (t, k, l, desc, st, args, _) in self.calls:
+            self.entry(desc, st, self.w.batch, args)
+        for l in range(self.w.layers):
+            for st in self.sets:
+                B.lla_write_latents(st["desc"], st["stores"][l], pos=self.wpos, x=st["x"][l],
+                                    enc=st["enc"][l], workspace=self.wws)
+
+    def step_bytes(self):
+        """Algorithmic HBM bytes of one step (what the method itself must move)."""
+        w = self.w
+        e = 2 if w.dtype == "bf16" else 4
+        H, dh, Bt, W = w.heads, w.head_dim, w.batch, w.window
+        n_lat = max(0, self.i - W)
+        n_win = min(W, self.i)
+        total = 0
+        per_call = {}
+        for (t, k, l, *_rest) in self.calls:
+            s = w.sets[k]
+            lat = Bt * n_lat * s.groups * (s.r_k + s.r_v) * e
+            win = Bt * n_win * H * dh * 2 * e
+            act = Bt * H * dh * e * (4 + 2)          # q, k_cur, v_cur, out + ring slot write (K, V)
+            maps = H * dh * (s.r_k + s.r_v) * e
+            per_call[k] = (lat + win, lat + win + act + maps)
+            total += lat + win + act + maps
+        for s in w.sets:
+            total += w.layers * (Bt * s.n_loops * s.groups * s.d_in * e
+                                 + s.n_loops * s.groups * (s.r_k + s.r_v) * s.d_in * e
+                                 + Bt * s.groups * (s.r_k + s.r_v) * e)
+        return total, per_call
+
+
+def cpu_baseline(w, budget_s, seed=0):
+    """The fp64 oracle's absorbed read (the function that checks
+    hla_decode_windowed), timed on the host cores on whole sequences of the
+    same workload, scaled to decode tokens/s of the full step."""
+    import threadpoolctl
+    import oracle as O
+    from synth import gen
+    H, dh, W, P = w.heads, w.head_dim, w.window, w.page_size
+    i = w.context - 1
+    n_lat = max(0, i - W)
+    g = gen.rng(seed, 991)
+    per_set = []
+    for s in w.sets:
+        nps = -(-w.context // P)
+        pages = (g.standard_normal((nps, s.groups * P * (s.r_k + s.r_v))) * np.sqrt(s.n_loops)) \
+            .astype(np.float32).astype(np.float64)
+        bt = np.arange(nps, dtype=np.int64)[None]
+        q = g.standard_normal((1, H, dh))
+        kc = g.standard_normal((1, H, dh))
+        vc = g.standard_normal((1, H, dh))
+        rk = g.standard_normal((1, W + 1, H, dh))
+        rv = g.standard_normal((1, W + 1, H, dh))
+        A = g.standard_normal((H, dh, s.r_k)) / np.sqrt(s.r_k)
+        Bv = g.standard_normal((H, s.r_v, dh)) / np.sqrt(s.r_v)
+        per_set.append((s, pages, bt, q, kc, vc, rk, rv, A, Bv))
+
+    def one_sequence(k):
+        s, pages, bt, q, kc, vc, rk, rv, A, Bv = per_set[k]
+        sK, sV = O.gather_latents(pages, bt, 0, n_lat, groups=s.groups, page_size=P, r_k=s.r_k, r_v=s.r_v)
+        O.absorbed_decode([sK], [sV], [i], q, kc, vc, rk, rv, A, Bv, window=W, rope_base=w.rope_base)
+
+    t_set = []
+    n_done = 0
+    t_start = time.perf_counter()
+    per_share = budget_s / len(w.sets)
+    for k in range(len(w.sets)):
+        n, t0 = 0, time.perf_counter()
+        while True:
+            one_sequence(k)
+            n += 1
+            if time.perf_counter() - t0 >= per_share or n >= w.batch:
+                break
+        t_set.append((time.perf_counter() - t0) / n)
+        n_done += n
+    wall = time.perf_counter() - t_start
+    # one step of one sequence: every (layer, loop) call
+    t_seq_step = sum(w.layers * w.sets[k].n_loops * t_set[k] for k in range(len(w.sets)))
+    info = threadpoolctl.threadpool_info()
+    blas_threads = max([d.get("num_threads", 1) for d in info] or [1])
+    return {
+        "value": 1.0 / t_seq_step, "unit": "tokens/s", "cores": int(blas_threads),
+        "host_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
+        "sample": (f"oracle absorbed_decode (fp64 numpy) on {n_done} whole sequences "
+                   f"({', '.join(f'{t * 1e3:.1f} ms/seq/call set{k}' for k, t in enumerate(t_set))}) "
+                   f"in {wall:.1f} s, scaled to {w.layers} layers x {w.loops} loops per token"),
+    }
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    import torch
+    from synth import configs
+    w = configs.get(a.workload)
+    hip = Hip()
+    st = HlaStep(w, splits=a.splits)
+    stream = torch.cuda.current_stream().cuda_stream
+    for _ in range(a.warmup):
+        st.step()
+    torch.cuda.synchronize()
+    e0, e1 = hip.event(), hip.event()
+    hip.record(e0, stream)
+    for _ in range(a.steps):
+        st.step()
+    hip.record(e1, stream)
+    torch.cuda.synchronize()
+    ms = hip.elapsed_ms(e0, e1) / a.steps
+    step_bytes, per_call = st.step_bytes()
+
+    # dominant kernel: the latent scan of the main set (loops 2..T), timed live
+    main_k = max(per_call, key=lambda k: per_call[k][0] * w.sets[k].n_loops)
+    evs = []
+    rsteps = max(2, min(a.steps, 5))
+    for _ in range(rsteps):
+        for (t, k, l, desc, stc, args, _) in st.calls:
+            if k == main_k:
+                pair = (ctypes.c_void_p * 2)(hip.event().value, hip.event().value)
+                args.scan_events = ctypes.addressof(pair)
+                evs.append(pair)
+            st.entry(desc, stc, w.batch, args)
+            args.scan_events = None
+    torch.cuda.synchronize()
+    scan_ms = float(np.mean([hip.elapsed_ms(ctypes.c_void_p(p[0]), ctypes.c_void_p(p[1])) for p in evs]))
+    lat_bytes = per_call[main_k][0]
+    s_main = w.sets[main_k]
+    q_bytes = w.batch * w.heads * s_main.r_k * (2 if w.dtype == "bf16" else 4)
+    achieved = (lat_bytes + q_bytes) / (scan_ms * 1e-3) / 1e9
+    traffic = None
+    tp = os.path.join(ROOT, "profiles", "traffic.json")
+    if os.path.exists(tp):
+        traffic = json.load(open(tp)).get(w.name)
+
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    rec = {
+        "metric": METRIC, "value": w.batch / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "layers": w.layers, "loops": w.loops, "batch": w.batch,
+                   "context": w.context, "window": w.window, "heads": w.heads,
+                   "head_dim": w.head_dim,
+                   "sets": [dict(loops=[s.loop_first, s.loop_last], groups=s.groups, r_k=s.r_k,
+                                 r_v=s.r_v) for s in w.sets],
+                   "splits": a.splits or "auto"},
+        "step_bytes": step_bytes, "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+        "roofline": {"kernel": "k_scan_absorbed_mfma<512,512> (main set: latent scan + exact window)",
+                     "bound": "hbm",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "avg_launch_ms": scan_ms, "bytes_per_launch": lat_bytes + q_bytes},
+    }
+    if not a.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds)
+    print(json.dumps(rec))
+
+
+if __name__ == "__main__":
+    main()

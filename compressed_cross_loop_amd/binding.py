@@ -46,7 +46,8 @@ class LlaDecodeArgs(ctypes.Structure):
                 ("k_cur", ctypes.c_void_p), ("v_cur", ctypes.c_void_p),
                 ("ring_k", ctypes.c_void_p), ("ring_v", ctypes.c_void_p),
                 ("A", ctypes.c_void_p), ("B", ctypes.c_void_p), ("out", ctypes.c_void_p),
-                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("scan_events", ctypes.c_void_p)]
 
 
 if not os.path.exists(LIB_PATH):
@@ -155,12 +156,14 @@ def lla_write_latents(desc, st, *, pos, x, enc, workspace=None, stream=None):
 
 
 def decode_args(*, loop, window, pos, q, k_cur, v_cur, ring_k, ring_v, A, B, out, workspace,
-                max_pos_hint, splits=0, flags=0):
+                max_pos_hint, splits=0, flags=0, scan_events=None):
+    """scan_events: optional ctypes array of two hipEvent_t handles."""
     ws_bytes = 0 if workspace is None or isinstance(workspace, int) else \
         workspace.numel() * workspace.element_size()
+    ev = ctypes.cast(scan_events, ctypes.c_void_p) if scan_events is not None else None
     return LlaDecodeArgs(loop, window, int(max_pos_hint), splits, flags, _ptr(pos), _ptr(q),
                          _ptr(k_cur), _ptr(v_cur), _ptr(ring_k), _ptr(ring_v), _ptr(A), _ptr(B),
-                         _ptr(out), _ptr(workspace), ws_bytes)
+                         _ptr(out), _ptr(workspace), ws_bytes, ev)
 
 
 def _decode(fn, desc, st, batch, args, stream):

@@ -1,0 +1,470 @@
+// bf16 decode kernels around the latent scan, shaped for gfx950:
+//   k_qmap_mfma     q~ = s R~_i A_t^T q for a block of sequences and one
+//                   d_h-wide latent block, on the matrix cores; the latent
+//                   rotation pairs (f, f + d_h/2) sit in the same lane, so
+//                   R~_i is applied in registers ("Hybrid Latent Attention"
+//                   summary, "Latent Reader" Eq. 3, "Rotary Embedding
+//                   Alignment")
+//   k_window_fast   the exact tokens i-W <= j <= i of Eq. 4 for one sequence
+//                   and one slice of the window: all heads at once, each
+//                   thread owning 8 dims of one head (16-byte loads of the
+//                   contiguous [H][d_h] ring rows), per-head online softmax
+//   k_combine_mfma  merge of the latent and window partials of 16 sequences
+//                   and one head, then o = (B_t^T O_latent + O_window) / l
+//                   with the B_t^T product on the fp32 matrix cores
+#include "device_common.h"
+#include "lla_internal.h"
+
+namespace lla {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+
+// ------------------------------------------------------------------ q map
+// grid (H, r_k / NB, ceil(B / 16)); NB = latent columns per workgroup (d_h
+// when rotary, so a block holds both members of every pair).  The A^(h)
+// block is stored transposed in LDS ([n][e], 8 consecutive e per 16 bytes)
+// so each B fragment is one ds_read_b128; the 16 sequences' rotation angles
+// are tabulated once per workgroup.
+template <int DH, int NB>
+__global__ __launch_bounds__(kThreads) void k_qmap_mfma(DecodeParams p, int want_qlat) {
+  __shared__ __attribute__((aligned(16))) bf16 AtT[NB][DH + 8];
+  __shared__ float csn[16][DH / 2][2];
+  const int h = blockIdx.x, blk = blockIdx.y, b0 = blockIdx.z * 16;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int H = p.H, rk = p.rk;
+  const bool rope = p.rope_base != 0.f;
+  const bf16* q = static_cast<const bf16*>(p.q);
+
+  // issue the A^(h) block loads first: 16-byte rows of 8 consecutive columns
+  const bf16* Ah = static_cast<const bf16*>(p.A) + (int64_t)h * DH * rk + (int64_t)blk * NB;
+  constexpr int NL = (DH * NB / 8 + kThreads - 1) / kThreads;
+  bf16x8 av[NL];
+#pragma unroll
+  for (int u = 0; u < NL; ++u) {
+    const int x = tid + u * kThreads;
+    if (x < DH * NB / 8) {
+      const int e = x / (NB / 8), n8 = (x % (NB / 8)) * 8;
+      av[u] = *reinterpret_cast<const bf16x8*>(Ah + (int64_t)e * rk + n8);
+    }
+  }
+  if (rope) {
+    for (int x = tid; x < 16 * (DH / 2); x += kThreads) {
+      const int bl = x / (DH / 2), f = x % (DH / 2);
+      const int bb = min(b0 + bl, p.B - 1);
+      float c, sn;
+      rope_cs(p.rope_base, DH, f, p.pos[bb], c, sn);
+      csn[bl][f][0] = c;
+      csn[bl][f][1] = sn;
+    }
+  }
+  // q' = s R_i q (head space, fp32) when a later kernel reads it
+  if (blk == 0 && p.need_qhead) {
+    for (int x = tid; x < 16 * (DH / 2); x += kThreads) {
+      const int bl = x / (DH / 2), f = x % (DH / 2), bb = b0 + bl;
+      if (bb >= p.B) continue;
+      float c = 1.f, sn = 0.f;
+      if (rope) rope_cs(p.rope_base, DH, f, p.pos[bb], c, sn);
+      const bf16* qr = q + ((int64_t)bb * H + h) * DH;
+      const float a = to_f(qr[f]), b = to_f(qr[f + DH / 2]);
+      float* qh = p.qhead + ((int64_t)bb * H + h) * DH;
+      qh[f] = p.scale * (a * c - b * sn);
+      qh[f + DH / 2] = p.scale * (a * sn + b * c);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < NL; ++u) {
+    const int x = tid + u * kThreads;
+    if (x < DH * NB / 8) {
+      const int e = x / (NB / 8), n8 = (x % (NB / 8)) * 8;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) AtT[n8 + k][e] = av[u][k];
+    }
+  }
+  __syncthreads();
+  if (!want_qlat) return;
+
+  // A operand: q rows of the 16 sequences
+  const int brow = b0 + col;
+  bf16x8 aq[DH / 32];
+#pragma unroll
+  for (int st = 0; st < DH / 32; ++st) {
+    if (brow < p.B) {
+      aq[st] = *reinterpret_cast<const bf16x8*>(q + ((int64_t)brow * H + h) * DH + st * 32 + grp * 8);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) aq[st][k] = static_cast<bf16>(0.f);
+    }
+  }
+  constexpr int NT = NB / 16;       // column tiles
+  constexpr int HT = DH / 32;       // tile distance of a rotary pair (rope: NB == DH)
+  auto tile = [&](int j) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < DH / 32; ++st) {
+      const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&AtT[j * 16 + col][st * 32 + grp * 8]);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[st], bv, acc, 0, 0, 0);
+    }
+    return acc;   // lane: C[b0 + 4 grp + r][blk*NB + 16 j + col]
+  };
+  bf16* ql = static_cast<bf16*>(p.qlat);
+  if (rope) {
+    if (wave < HT) {
+      const f32x4 lo = tile(wave), hi = tile(wave + HT);
+      const int f = wave * 16 + col;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int bl = 4 * grp + r, bb = b0 + bl;
+        if (bb >= p.B) continue;
+        const float c = csn[bl][f][0], sn = csn[bl][f][1];
+        bf16* qo = ql + ((int64_t)bb * H + h) * rk + (int64_t)blk * NB;
+        qo[f] = static_cast<bf16>((lo[r] * c - hi[r] * sn) * p.scale);
+        qo[f + DH / 2] = static_cast<bf16>((lo[r] * sn + hi[r] * c) * p.scale);
+      }
+    }
+  } else {
+    for (int j = wave; j < NT; j += 4) {
+      const f32x4 v = tile(j);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int bb = b0 + 4 * grp + r;
+        if (bb < p.B)
+          ql[((int64_t)bb * H + h) * rk + (int64_t)blk * NB + j * 16 + col] = static_cast<bf16>(v[r] * p.scale);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ window
+// grid (B, WS); thread (h = tid / (DH/8), c = tid % (DH/8)) owns dims 8c..8c+7
+template <int DH>
+__global__ __launch_bounds__(kThreads) void k_window_fast(DecodeParams p) {
+  constexpr int TPH = DH / 8;
+  __shared__ double theta[DH / 2];
+  const int b = blockIdx.x, ws = blockIdx.y, tid = threadIdx.x;
+  if (p.rope_base != 0.f && tid < DH / 2) theta[tid] = rope_theta(p.rope_base, DH, tid);
+  __syncthreads();
+  const int H = p.H, W = p.W, WS = p.WS;
+  const int h = tid / TPH, c = tid % TPH;
+  const bool active = h < H;
+  const int hh = active ? h : 0;
+  const int i = p.pos[b];
+  const int j0 = max(0, i - W);
+  const int nw = i - j0;                       // ring tokens; token nw is the current one
+  const int t0 = ws * p.tw, t1 = min(t0 + p.tw, nw + 1);
+  float qf[8];
+  if (p.need_qhead) {
+    const float* qh = p.qhead + ((int64_t)b * H + hh) * DH + 8 * c;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) qf[k] = qh[k];
+  } else {
+    // q' = s R_i q for this thread's 8 dims (partner dims are d +- DH/2)
+    const bf16* qr = static_cast<const bf16*>(p.q) + ((int64_t)b * H + hh) * DH;
+    const bf16x8 qv = *reinterpret_cast<const bf16x8*>(qr + 8 * c);
+    const int pc = (8 * c < DH / 2) ? 8 * c + DH / 2 : 8 * c - DH / 2;
+    const bf16x8 qp = *reinterpret_cast<const bf16x8*>(qr + pc);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int d = 8 * c + k;
+      const int f = d < DH / 2 ? d : d - DH / 2;
+      float cs = 1.f, sn = 0.f;
+      if (p.rope_base != 0.f) rope_cs_theta(theta[f], i, cs, sn);
+      const float r = d < DH / 2 ? to_f(qv[k]) * cs - to_f(qp[k]) * sn : to_f(qp[k]) * sn + to_f(qv[k]) * cs;
+      qf[k] = p.scale * r;
+    }
+  }
+  const bf16* ring_k = static_cast<const bf16*>(p.ring_k);
+  const bf16* ring_v = static_cast<const bf16*>(p.ring_v);
+  const int64_t rs = (int64_t)H * DH;          // elements per ring slot
+  const int64_t base = (int64_t)b * (W + 1) * rs + (int64_t)hh * DH + 8 * c;
+
+  // current token: rotated key R_i k_cur and v_cur (only the slice holding it)
+  float kself[8], vself[8];
+  const bool has_self = t0 <= nw && nw < t1;
+  if (has_self) {
+    const bf16* kc = static_cast<const bf16*>(p.k_cur) + ((int64_t)b * H + hh) * DH;
+    const bf16* vc = static_cast<const bf16*>(p.v_cur) + ((int64_t)b * H + hh) * DH;
+    const bf16x8 kv = *reinterpret_cast<const bf16x8*>(kc + 8 * c);
+    const int pc = (8 * c < DH / 2) ? 8 * c + DH / 2 : 8 * c - DH / 2;
+    const bf16x8 kp = *reinterpret_cast<const bf16x8*>(kc + pc);
+    const bf16x8 vv = *reinterpret_cast<const bf16x8*>(vc + 8 * c);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int d = 8 * c + k;
+      float cs = 1.f, sn = 0.f;
+      const int f = d < DH / 2 ? d : d - DH / 2;
+      if (p.rope_base != 0.f) rope_cs_theta(theta[f], i, cs, sn);
+      kself[k] = d < DH / 2 ? to_f(kv[k]) * cs - to_f(kp[k]) * sn : to_f(kp[k]) * sn + to_f(kv[k]) * cs;
+      vself[k] = to_f(vv[k]);
+    }
+  }
+  float m = -INFINITY, l = 0.f, o[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) o[k] = 0.f;
+  constexpr int U = 8;
+  for (int tb = t0; tb < t1; tb += U) {
+    bf16x8 kr[U], vr[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = tb + u;
+      if (t < t1 && t < nw) {
+        const int slot = (j0 + t) % (W + 1);
+        kr[u] = *reinterpret_cast<const bf16x8*>(ring_k + base + slot * rs);
+        vr[u] = *reinterpret_cast<const bf16x8*>(ring_v + base + slot * rs);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = tb + u;
+      if (t >= t1) break;
+      float kk[8], vv[8];
+      if (t < nw) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) { kk[k] = to_f(kr[u][k]); vv[k] = to_f(vr[u][k]); }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) { kk[k] = kself[k]; vv[k] = vself[k]; }
+      }
+      float s = 0.f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) s += qf[k] * kk[k];
+#pragma unroll
+      for (int off = 1; off < TPH; off <<= 1) s += __shfl_xor(s, off);
+      const float mn = fmaxf(m, s);
+      const float alpha = exp2_diff(m, mn);
+      const float pw = exp2f(s - mn);
+      l = l * alpha + pw;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) o[k] = o[k] * alpha + pw * vv[k];
+      m = mn;
+    }
+  }
+  if (active) {
+    const int64_t row = ((int64_t)b * WS + ws) * H + h;
+    if (c == 0) {
+      p.win_ml[row * 2 + 0] = m;
+      p.win_ml[row * 2 + 1] = l;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) p.win_o[row * DH + 8 * c + k] = o[k];
+    if (has_self) {
+      // ring append: slot i mod (W+1) held token i-W-1, read by no slice
+      const int64_t so = (int64_t)b * (W + 1) * rs + (int64_t)(i % (W + 1)) * rs + (int64_t)h * DH + 8 * c;
+      bf16x8 kw, vw;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        kw[k] = static_cast<bf16>(kself[k]);
+        vw[k] = static_cast<bf16>(vself[k]);
+      }
+      *reinterpret_cast<bf16x8*>(static_cast<bf16*>(p.ring_k) + so) = kw;
+      *reinterpret_cast<bf16x8*>(static_cast<bf16*>(p.ring_v) + so) = vw;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ combine
+// grid (H, ceil(B / 16)); 4 waves; out[b][h] for 16 sequences, d_h = 128.
+// B_t^(h) (RV x 128 bf16) is requested in full at entry (RV/16 16-byte loads
+// per thread, one 16-row chunk per load) so its latency overlaps the merge;
+// each chunk then goes through LDS as fp32 to feed v_mfma_f32_16x16x4_f32.
+template <int RV>
+__global__ __launch_bounds__(kThreads) void k_combine_mfma(DecodeParams p) {
+  constexpr int DH = 128;
+  constexpr int NC = RV / 16;
+  __shared__ float ob[16][RV + 1];     // latent-space sums
+  __shared__ float wo[16][DH];         // window sums
+  __shared__ float wl[16];             // 1 / l
+  __shared__ float bs[2][16][DH + 4];  // B_t chunk, double-buffered
+  const int H = p.H, S = p.S, WS = p.WS;
+  const int h = blockIdx.x, b0 = blockIdx.y * 16, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const bf16* Bh = static_cast<const bf16*>(p.Bm) + (int64_t)h * RV * DH;
+  const int brow = tid / 16, bcol = (tid % 16) * 8;
+  bf16x8 breg[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+    breg[c] = *reinterpret_cast<const bf16x8*>(Bh + (int64_t)(16 * c + brow) * DH + bcol);
+
+  // (m, l) of every split and window slice of the 16 sequences: one load per
+  // thread, all in flight together, then the per-sequence softmax merge
+  __shared__ float pm[16][40], pl[16][40];   // S + WS <= 40
+  {
+    const int NP = S + WS;
+    for (int x = tid; x < 16 * NP; x += kThreads) {
+      const int bl = x / NP, j = x % NP, b = b0 + bl;
+      float mm = -INFINITY, ll = 0.f;
+      if (b < p.B) {
+        const float* src = (j < S) ? p.part_ml + (((int64_t)b * S + j) * H + h) * 2
+                                   : p.win_ml + (((int64_t)b * WS + (j - S)) * H + h) * 2;
+        mm = src[0];
+        ll = src[1];
+      }
+      pm[bl][j] = mm;
+      pl[bl][j] = ll;
+    }
+  }
+  __syncthreads();
+  if (tid < 16) {
+    const int NP = S + WS;
+    float M = -INFINITY;
+    for (int j = 0; j < NP; ++j) M = fmaxf(M, pm[tid][j]);
+    float l = 0.f;
+    for (int j = 0; j < NP; ++j) {
+      const float w = exp2_diff(pm[tid][j], M);
+      pm[tid][j] = w;        // from here on: merge weight of split / slice j
+      l += w * pl[tid][j];
+    }
+    wl[tid] = (b0 + tid < p.B) ? 1.f / l : 0.f;
+  }
+  __syncthreads();
+  {
+    // thread -> (sequence bl, float4 columns k4, k4 + 16, ...); loads for four
+    // splits are issued together
+    constexpr int C4 = RV / 4;
+    constexpr int PER = (C4 + 15) / 16;
+    const int bl = tid / 16, k4 = tid % 16, b = b0 + bl;
+    f32x4 sum[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) sum[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (b < p.B) {
+      for (int s0 = 0; s0 < S; s0 += 4) {
+        f32x4 v[4][PER];
+#pragma unroll
+        for (int ss = 0; ss < 4; ++ss) {
+          const int s = s0 + ss;
+          const float4* row = reinterpret_cast<const float4*>(
+              p.part_o + (((int64_t)b * S + min(s, S - 1)) * H + h) * p.Dp);
+#pragma unroll
+          for (int u = 0; u < PER; ++u) {
+            const int cc = k4 + 16 * u;
+            if (s < S && cc < C4) {
+              const float4 t = row[cc];
+              v[ss][u] = f32x4{t.x, t.y, t.z, t.w};
+            } else {
+              v[ss][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+          }
+        }
+#pragma unroll
+        for (int ss = 0; ss < 4; ++ss) {
+          const float w = (s0 + ss < S) ? pm[bl][s0 + ss] : 0.f;
+#pragma unroll
+          for (int u = 0; u < PER; ++u) sum[u] += w * v[ss][u];
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int cc = k4 + 16 * u;
+      if (cc < C4) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) ob[bl][4 * cc + k] = sum[u][k];
+      }
+    }
+  }
+  for (int x = tid; x < 16 * DH; x += kThreads) {
+    const int bl = x / DH, e = x % DH, b = b0 + bl;
+    float acc = 0.f;
+    if (b < p.B)
+      for (int s = 0; s < WS; ++s) acc += pm[bl][S + s] * p.win_o[(((int64_t)b * WS + s) * H + h) * DH + e];
+    wo[bl][e] = acc;
+  }
+  // out[16 b x 128] = ob[16 x RV] . B^(h)[RV x 128]; wave w owns column tiles w and w+4
+  const int col = lane & 15, kq = lane >> 4;
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) acc[u][0] = acc[u][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int buf = c & 1;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) bs[buf][brow][bcol + k] = to_f(breg[c][k]);
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const float a = ob[col][16 * c + 4 * kk + kq];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const float bv = bs[buf][4 * kk + kq][(wave + 4 * u) * 16 + col];
+        acc[u][kk & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bv, acc[u][kk & 1], 0, 0, 0);
+      }
+    }
+  }
+  bf16* out = static_cast<bf16*>(p.out);
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int e = (wave + 4 * u) * 16 + col;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int bl = 4 * kq + r, b = b0 + bl;
+      if (b < p.B)
+        out[((int64_t)b * H + h) * DH + e] =
+            static_cast<bf16>((acc[u][0][r] + acc[u][1][r] + wo[bl][e]) * wl[bl]);
+    }
+  }
+}
+
+template <int DH, int NB>
+hipError_t qmap_launch(const DecodeParams& p, bool want, hipStream_t s) {
+  const dim3 grid(p.H, want ? p.rk / NB : 1, (p.B + 15) / 16);
+  hipLaunchKernelGGL((k_qmap_mfma<DH, NB>), grid, dim3(kThreads), 0, s, p, want ? 1 : 0);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool qmap_mfma_supports(const DecodeParams& p) {
+  if (!p.bf16) return false;
+  if (p.dh != 64 && p.dh != 128) return false;
+  if (p.rope_base != 0.f) return p.rk % p.dh == 0;
+  return p.rk % p.dh == 0 || p.rk == 32;
+}
+
+hipError_t launch_qmap_mfma(const DecodeParams& p, bool want_qlat, hipStream_t s) {
+  if (!qmap_mfma_supports(p)) return hipErrorNotSupported;
+  if (p.dh == 128) {
+    if (p.rk % 128 == 0) return qmap_launch<128, 128>(p, want_qlat, s);
+    return qmap_launch<128, 32>(p, want_qlat, s);
+  }
+  if (p.rk % 64 == 0) return qmap_launch<64, 64>(p, want_qlat, s);
+  return qmap_launch<64, 32>(p, want_qlat, s);
+}
+
+bool window_fast_supports(const DecodeParams& p) {
+  return p.bf16 && (p.dh == 64 || p.dh == 128) && p.H * (p.dh / 8) <= kThreads;
+}
+
+hipError_t launch_window_fast(const DecodeParams& p, hipStream_t s) {
+  if (!window_fast_supports(p)) return hipErrorNotSupported;
+  const dim3 grid(p.B, p.WS);
+  if (p.dh == 128)
+    hipLaunchKernelGGL(k_window_fast<128>, grid, dim3(kThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL(k_window_fast<64>, grid, dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+bool combine_mfma_supports(const DecodeParams& p) {
+  if (!p.bf16 || p.mode != kAbsorbed || p.dh != 128 || p.S + p.WS > 40) return false;
+  return p.rv == 32 || p.rv == 64 || p.rv == 128 || p.rv == 256 || p.rv == 512;
+}
+
+hipError_t launch_combine_mfma(const DecodeParams& p, hipStream_t s) {
+  if (!combine_mfma_supports(p)) return hipErrorNotSupported;
+  const dim3 grid(p.H, (p.B + 15) / 16);
+  switch (p.rv) {
+    case 32: hipLaunchKernelGGL(k_combine_mfma<32>, grid, dim3(kThreads), 0, s, p); break;
+    case 64: hipLaunchKernelGGL(k_combine_mfma<64>, grid, dim3(kThreads), 0, s, p); break;
+    case 128: hipLaunchKernelGGL(k_combine_mfma<128>, grid, dim3(kThreads), 0, s, p); break;
+    case 256: hipLaunchKernelGGL(k_combine_mfma<256>, grid, dim3(kThreads), 0, s, p); break;
+    default: hipLaunchKernelGGL(k_combine_mfma<512>, grid, dim3(kThreads), 0, s, p); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace lla

@@ -127,7 +127,7 @@ __global__ __launch_bounds__(kThreads) void k_window(DecodeParams p) {
   __syncthreads();
   ls = 0.f;
   for (int w = 0; w < kThreads / 64; ++w) ls += red[w];
-  float* wo = p.win_o + ((int64_t)b * H + h) * dh;
+  float* wo = p.win_o + ((int64_t)b * p.WS * H + h) * dh;
   for (int e = tid; e < dh; e += kThreads) {
     float acc = 0.f;
     for (int t = 0; t < nw; ++t) {
@@ -138,8 +138,16 @@ __global__ __launch_bounds__(kThreads) void k_window(DecodeParams p) {
     wo[e] = acc;
   }
   if (tid == 0) {
-    p.win_ml[((int64_t)b * H + h) * 2 + 0] = mx;
-    p.win_ml[((int64_t)b * H + h) * 2 + 1] = ls;
+    p.win_ml[((int64_t)b * p.WS * H + h) * 2 + 0] = mx;
+    p.win_ml[((int64_t)b * p.WS * H + h) * 2 + 1] = ls;
+  }
+  for (int ws = 1; ws < p.WS; ++ws) {
+    const int64_t row = ((int64_t)b * p.WS + ws) * H + h;
+    if (tid == 0) {
+      p.win_ml[row * 2 + 0] = -INFINITY;
+      p.win_ml[row * 2 + 1] = 0.f;
+    }
+    for (int e = tid; e < dh; e += kThreads) p.win_o[row * dh + e] = 0.f;
   }
   // ring append: slot i mod (W+1) was token i-W-1, which no read above touches
   const int si = i % (W + 1);
@@ -317,26 +325,35 @@ __global__ __launch_bounds__(kThreads) void k_scan_reconstruct_generic(DecodePar
 template <typename T>
 __global__ __launch_bounds__(kThreads) void k_combine(DecodeParams p) {
   extern __shared__ float sm[];
-  const int S = p.S, H = p.H, dh = p.dh;
-  float* ws = sm;        // [S]
-  float* ob = sm + S;    // [Dp] (absorbed: latent-space sum)
+  const int S = p.S, WS = p.WS, H = p.H, dh = p.dh;
+  float* ws = sm;            // [S]   latent split weights
+  float* ww = sm + S;        // [WS]  window slice weights
+  float* ob = sm + S + WS;   // [Dp]  (absorbed: latent-space sum)
   const int b = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
-  const float mw = p.win_ml[((int64_t)b * H + h) * 2 + 0];
-  const float lw = p.win_ml[((int64_t)b * H + h) * 2 + 1];
-  float M = mw;
+  float M = -INFINITY;
   for (int s = 0; s < S; ++s) M = fmaxf(M, p.part_ml[(((int64_t)b * S + s) * H + h) * 2]);
-  float l = exp2_diff(mw, M) * lw;
+  for (int s = 0; s < WS; ++s) M = fmaxf(M, p.win_ml[(((int64_t)b * WS + s) * H + h) * 2]);
+  float l = 0.f;
   for (int s = 0; s < S; ++s) {
     const int64_t row = ((int64_t)b * S + s) * H + h;
     const float w = exp2_diff(p.part_ml[row * 2], M);
     l += w * p.part_ml[row * 2 + 1];
     if (tid == 0) ws[s] = w;
   }
-  const float ww = exp2_diff(mw, M);
+  for (int s = 0; s < WS; ++s) {
+    const int64_t row = ((int64_t)b * WS + s) * H + h;
+    const float w = exp2_diff(p.win_ml[row * 2], M);
+    l += w * p.win_ml[row * 2 + 1];
+    if (tid == 0) ww[s] = w;
+  }
   const float inv = 1.f / l;
   __syncthreads();
   T* out = static_cast<T*>(p.out) + ((int64_t)b * H + h) * dh;
-  const float* wo = p.win_o + ((int64_t)b * H + h) * dh;
+  auto window_sum = [&](int e) {
+    float acc = 0.f;
+    for (int s = 0; s < WS; ++s) acc += ww[s] * p.win_o[(((int64_t)b * WS + s) * H + h) * dh + e];
+    return acc;
+  };
   if (p.mode == kAbsorbed) {
     const int rv = p.rv;
     for (int k = tid; k < rv; k += kThreads) {
@@ -349,13 +366,13 @@ __global__ __launch_bounds__(kThreads) void k_combine(DecodeParams p) {
     for (int e = tid; e < dh; e += kThreads) {
       float acc = 0.f;
       for (int k = 0; k < rv; ++k) acc += to_f(Bh[(int64_t)k * dh + e]) * ob[k];
-      out[e] = from_f<T>((acc + ww * wo[e]) * inv);
+      out[e] = from_f<T>((acc + window_sum(e)) * inv);
     }
   } else {
     for (int e = tid; e < dh; e += kThreads) {
       float acc = 0.f;
       for (int s = 0; s < S; ++s) acc += ws[s] * p.part_o[(((int64_t)b * S + s) * H + h) * p.Dp + e];
-      out[e] = from_f<T>((acc + ww * wo[e]) * inv);
+      out[e] = from_f<T>((acc + window_sum(e)) * inv);
     }
   }
 }
@@ -400,7 +417,7 @@ hipError_t launch_scan_reconstruct_generic(const DecodeParams& p, hipStream_t s)
 }
 
 hipError_t launch_combine(const DecodeParams& p, hipStream_t s) {
-  const size_t lds = (size_t)(p.S + (p.mode == kAbsorbed ? p.rv : 0)) * sizeof(float);
+  const size_t lds = (size_t)(p.S + p.WS + (p.mode == kAbsorbed ? p.rv : 0)) * sizeof(float);
   if (p.bf16)
     hipLaunchKernelGGL(k_combine<bf16>, dim3(p.B, p.H), dim3(kThreads), lds, s, p);
   else

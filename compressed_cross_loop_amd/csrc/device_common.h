@@ -29,14 +29,22 @@ __device__ __forceinline__ int64_t val_off(int64_t page, int g, int slot, int d,
   return tile_base(page, g, slot, G, P, R) + 16 * rk + (d >> 4) * 256 + (d & 15) * 16 + (slot & 15);
 }
 
-// cos / sin of p * theta_f, theta_f = base^(-2f/d_h), evaluated in fp64
-// (positions reach 16K, where an fp32 angle would lose ~1e-3 rad).
+// Rotary angle p * theta_f, theta_f = base^(-2f/d_h).  theta_f and the
+// product are fp64 (positions reach 16K and beyond, where an fp32 angle would
+// be off by ~1e-3 rad); the product is reduced by whole turns in fp64 and
+// only the reduced angle (|r| <= pi) goes through fp32 sincosf.
+__device__ __forceinline__ double rope_theta(float base, int dh, int f) {
+  return pow((double)base, -2.0 * (double)f / (double)dh);
+}
+__device__ __forceinline__ void rope_cs_theta(double theta, int pos, float& c, float& s) {
+  const double two_pi = 6.283185307179586476925;
+  const double a = (double)pos * theta;
+  const double turns = rint(a / two_pi);
+  const float r = (float)fma(-turns, two_pi, a);
+  sincosf(r, &s, &c);
+}
 __device__ __forceinline__ void rope_cs(float base, int dh, int f, int pos, float& c, float& s) {
-  const double th = pow((double)base, -2.0 * (double)f / (double)dh);
-  double sd, cd;
-  sincos((double)pos * th, &sd, &cd);
-  c = (float)cd;
-  s = (float)sd;
+  rope_cs_theta(rope_theta(base, dh, f), pos, c, s);
 }
 
 __device__ __forceinline__ float wave_sum(float v) {

@@ -18,7 +18,7 @@ using namespace lla;
 constexpr int kMaxHeadDim = 256;
 constexpr int kMaxLatent = 16384;     // r_k + r_v limit of the general kernels
 constexpr int kMaxWindow = 8192;
-constexpr int kTargetWorkgroups = 512;  // two per compute unit on MI355X (256 CUs)
+constexpr int kTargetWorkgroups = 256;  // one per compute unit on MI355X (256 CUs)
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -92,7 +92,11 @@ struct WsLayout {
 
 size_t up256(size_t x) { return (x + 255) & ~size_t(255); }
 
-WsLayout ws_layout(const lla_set_desc& d, int B, int S, int Dp) {
+constexpr int kWindowSlice = 32;   // exact tokens per window slice (fast window kernel)
+
+int window_slices(int window) { return (window + 1 + kWindowSlice - 1) / kWindowSlice; }
+
+WsLayout ws_layout(const lla_set_desc& d, int B, int S, int WS, int Dp) {
   WsLayout w{};
   const size_t H = d.n_heads, dh = d.head_dim;
   size_t off = 0;
@@ -100,8 +104,8 @@ WsLayout ws_layout(const lla_set_desc& d, int B, int S, int Dp) {
   w.qhead = off;   off = up256(off + (size_t)B * H * dh * 4);
   w.part_ml = off; off = up256(off + (size_t)B * S * H * 2 * 4);
   w.part_o = off;  off = up256(off + (size_t)B * S * H * Dp * 4);
-  w.win_ml = off;  off = up256(off + (size_t)B * H * 2 * 4);
-  w.win_o = off;   off = up256(off + (size_t)B * H * dh * 4);
+  w.win_ml = off;  off = up256(off + (size_t)B * WS * H * 2 * 4);
+  w.win_o = off;   off = up256(off + (size_t)B * WS * H * dh * 4);
   w.total = off;
   return w;
 }
@@ -112,7 +116,7 @@ size_t decode_ws_bytes(const lla_set_desc& d, int batch, int max_pos, int window
   for (int entry = 0; entry < 2; ++entry)
     for (int flags = 0; flags < 2; ++flags)
       S = std::max(S, plan_for(d, batch, max_pos, window, splits, entry, flags).S);
-  return ws_layout(d, batch, S, std::max(d.r_v, d.head_dim)).total;
+  return ws_layout(d, batch, S, std::max(S, window_slices(window)), std::max(d.r_v, d.head_dim)).total;
 }
 
 lla_status hip_status(hipError_t e) { return e == hipSuccess ? LLA_OK : LLA_ERR_HIP; }
@@ -138,9 +142,11 @@ lla_status decode(const lla_set_desc* d, const lla_store* st, int32_t batch,
   if (!aligned16(a->workspace)) return LLA_ERR_INVALID_ARGUMENT;
 
   const bool absorbed = entry != 0;
+  const bool generic = (a->flags & LLA_FLAG_GENERIC) != 0;
   const Plan plan = plan_for(*d, batch, a->max_pos_hint, a->window, a->splits, absorbed ? 1 : 0, a->flags);
   const int Dp = std::max(d->r_v, d->head_dim);
-  const WsLayout w = ws_layout(*d, batch, plan.S, Dp);
+  const int WSmax = window_slices(a->window);
+  const WsLayout w = ws_layout(*d, batch, plan.S, std::max(plan.S, WSmax), Dp);
   char* ws = static_cast<char*>(a->workspace);
 
   DecodeParams p{};
@@ -160,19 +166,36 @@ lla_status decode(const lla_set_desc* d, const lla_store* st, int32_t batch,
   p.part_o = reinterpret_cast<float*>(ws + w.part_o);
   p.win_ml = reinterpret_cast<float*>(ws + w.win_ml);
   p.win_o = reinterpret_cast<float*>(ws + w.win_o);
-
+  const bool mfma_scan = absorbed && use_mfma_scan(*d, a->flags);
+  const bool fast_window = !generic && window_fast_supports(p);
+  // the matrix-core scan takes the window along when its group's heads fit
+  // one workgroup (thread per 8 dims of a head)
+  p.fuse_window = (mfma_scan && fast_window && p.hpg * (p.dh / 8) <= 256) ? 1 : 0;
+  if (p.fuse_window) {
+    p.WS = plan.S;
+    p.tw = (a->window + 1 + plan.S - 1) / plan.S;
+  } else {
+    p.tw = fast_window ? kWindowSlice : a->window + 1;
+    p.WS = fast_window ? WSmax : 1;
+  }
+  p.need_qhead = (!fast_window || !absorbed) ? 1 : 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = launch_qmap(p, absorbed, s);
-  if (e == hipSuccess) e = launch_window(p, s);
+  hipError_t e = (!generic && qmap_mfma_supports(p)) ? launch_qmap_mfma(p, absorbed, s)
+                                                     : launch_qmap(p, absorbed, s);
+  if (e == hipSuccess && !p.fuse_window) e = fast_window ? launch_window_fast(p, s) : launch_window(p, s);
+  hipEvent_t* ev = static_cast<hipEvent_t*>(a->scan_events);
+  if (e == hipSuccess && ev) e = hipEventRecord(ev[0], s);
   if (e == hipSuccess) {
     if (!absorbed)
       e = launch_scan_reconstruct_generic(p, s);
-    else if (use_mfma_scan(*d, a->flags))
+    else if (mfma_scan)
       e = launch_scan_absorbed_mfma(p, s);
     else
       e = launch_scan_absorbed_generic(p, s);
   }
-  if (e == hipSuccess) e = launch_combine(p, s);
+  if (e == hipSuccess && ev) e = hipEventRecord(ev[1], s);
+  if (e == hipSuccess)
+    e = (!generic && combine_mfma_supports(p)) ? launch_combine_mfma(p, s) : launch_combine(p, s);
   return hip_status(e);
 }
 
@@ -194,7 +217,6 @@ lla_status lla_write_latents(const lla_set_desc* desc, const lla_store* store, i
   const size_t need = lla_write_workspace_bytes(desc, batch, n_tok, d_in);
   if (need > 0 && (!workspace || workspace_bytes < need)) return LLA_ERR_WORKSPACE_TOO_SMALL;
   if (workspace && !aligned16(workspace)) return LLA_ERR_INVALID_ARGUMENT;
-  (void)workspace_bytes;
 
   WriterParams p{};
   p.B = batch; p.n_tok = n_tok; p.n_loops = desc->loop_last - desc->loop_first + 1;
@@ -204,13 +226,24 @@ lla_status lla_write_latents(const lla_set_desc* desc, const lla_store* store, i
   p.rope_baked = desc->rope_baked; p.bf16 = desc->dtype == LLA_BF16; p.rope_base = desc->rope_base;
   p.pos = pos; p.bt = store->block_table; p.pages = store->pages; p.x = x; p.enc = enc;
   p.acc = static_cast<float*>(workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (writer_mfma_supports(p)) {
+    p.ksplit = writer_mfma_ksplit(batch * n_tok, p.G, p.R, p.n_loops, d_in);
+    return hip_status(launch_writer_mfma(p, s));
+  }
   p.ksplit = 1;
-  return hip_status(launch_writer_generic(p, static_cast<hipStream_t>(stream)));
+  return hip_status(launch_writer_generic(p, s));
 }
 
 size_t lla_write_workspace_bytes(const lla_set_desc* desc, int32_t batch, int32_t n_tok, int32_t d_in) {
   if (check_desc(desc) != LLA_OK || batch <= 0 || n_tok <= 0 || d_in <= 0) return 0;
-  return 0;
+  WriterParams p{};
+  p.bf16 = desc->dtype == LLA_BF16;
+  p.d_in = d_in;
+  if (!writer_mfma_supports(p)) return 0;
+  const int R = desc->r_k + desc->r_v, n_loops = desc->loop_last - desc->loop_first + 1;
+  const int ks = writer_mfma_ksplit(batch * n_tok, desc->groups, R, n_loops, d_in);
+  return (size_t)ks * batch * n_tok * desc->groups * R * sizeof(float);
 }
 
 lla_status lla_decode_reconstruct(const lla_set_desc* desc, const lla_store* store, int32_t batch,

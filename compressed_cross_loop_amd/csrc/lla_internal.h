@@ -15,10 +15,15 @@ struct DecodeParams {
   // shapes
   int32_t B, H, dh, G, hpg, rk, rv, P, W;
   int32_t S, chunk;               // context splits and tokens per split
+  int32_t WS, tw;                 // exact-window slices and tokens per slice
   int32_t Dp;                     // width of latent partial rows (r_v or d_h)
   int32_t max_pages;
   int32_t mode;
   int32_t bf16;                   // storage dtype: 1 = bf16, 0 = fp32
+  int32_t need_qhead;             // a later kernel reads qhead (else the window
+                                  // kernel rotates q itself)
+  int32_t fuse_window;            // the matrix-core scan also does the exact
+                                  // window: split s handles window slice s
   float rope_base;
   float scale;                    // log2(e) / sqrt(d_h)
   // caller buffers
@@ -38,8 +43,8 @@ struct DecodeParams {
   float* qhead;                   // [B][H][dh]
   float* part_ml;                 // [B][S][H][2]
   float* part_o;                  // [B][S][H][Dp]
-  float* win_ml;                  // [B][H][2]
-  float* win_o;                   // [B][H][dh]
+  float* win_ml;                  // [B][WS][H][2]
+  float* win_o;                   // [B][WS][H][dh]
 };
 
 struct WriterParams {
@@ -67,6 +72,16 @@ hipError_t launch_combine(const DecodeParams& p, hipStream_t s);
 bool scan_absorbed_mfma_supports(const DecodeParams& p);
 hipError_t launch_scan_absorbed_mfma(const DecodeParams& p, hipStream_t s);
 
+bool qmap_mfma_supports(const DecodeParams& p);
+hipError_t launch_qmap_mfma(const DecodeParams& p, bool want_qlat, hipStream_t s);
+bool window_fast_supports(const DecodeParams& p);
+hipError_t launch_window_fast(const DecodeParams& p, hipStream_t s);
+bool combine_mfma_supports(const DecodeParams& p);
+hipError_t launch_combine_mfma(const DecodeParams& p, hipStream_t s);
+
 hipError_t launch_writer_generic(const WriterParams& p, hipStream_t s);
+bool writer_mfma_supports(const WriterParams& p);
+int writer_mfma_ksplit(int M, int G, int R, int n_loops, int d_in);
+hipError_t launch_writer_mfma(const WriterParams& p, hipStream_t s);
 
 }  // namespace lla

@@ -19,8 +19,11 @@
 //            as the score MFMA left them in registers (its C layout is this
 //            MFMA's B layout), rounded to bf16
 //
-// The tile loop is software-pipelined: the next tile's key loads are issued
-// right after the score MFMAs, its value loads right after the value MFMAs.  At the end the
+// With fuse_window set, split s also handles slice s of the exact window
+// (window_slice below), so those bytes stream in the same launch.
+//
+// The tile loop is software-pipelined: keys two tiles ahead, values one.
+// q~ is read from LDS to leave registers for the deeper key pipeline.  At the end the
 // four waves are merged (same-max rescale, fixed order) in LDS and one
 // partial (m, l, O_latent) per head is written for the combine kernel.
 #include "device_common.h"
@@ -56,12 +59,16 @@ __device__ __forceinline__ short bf16_bits(float x) {
 }
 
 // Scores of one tile; lane (head = lane&15, grp) gets tokens 4*grp + r.
+// q~ rows live in LDS (row stride RK + 8 bf16, so the 16 lanes of a group
+// read 16 distinct bank quads).
 template <int RK>
-__device__ __forceinline__ f32x4 tile_scores(const bf16x8 (&k)[RK / 32], const bf16x8 (&qreg)[RK / 32]) {
+__device__ __forceinline__ f32x4 tile_scores(const bf16x8 (&k)[RK / 32], const bf16* qrow) {
   f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int st = 0; st < RK / 32; ++st)
-    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k[st], qreg[st], sc, 0, 0, 0);
+  for (int st = 0; st < RK / 32; ++st) {
+    const bf16x8 qv = *reinterpret_cast<const bf16x8*>(qrow + st * 32);
+    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k[st], qv, sc, 0, 0, 0);
+  }
   return sc;
 }
 
@@ -112,6 +119,129 @@ __device__ __forceinline__ void tile_values(s16x4 (&v)[RV / 16], s16x4 pb, f32x4
     acc[vt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v[vt], pb, acc[vt], 0, 0, 0);
 }
 
+// Exact tokens i-W <= j <= i of Eq. 4 (ring slots and the current token) for
+// window slice `slice` of sequence b, heads of group g: thread (head hl, c)
+// owns dims 8c..8c+7 of head hl (16-byte loads of the [H][d_h] ring rows),
+// per-head online softmax, partial (m, l, o) in head space.  The slice that
+// holds the current token also appends R_i k_cur, v_cur to the ring.
+// cs[f] = (cos, sin) of i * theta_f.
+__device__ void window_slice(const DecodeParams& p, int b, int slice, int g, const float (*cs)[2]) {
+  const int DH = p.dh, TPH = DH / 8, H = p.H, W = p.W;
+  const int tid = threadIdx.x;
+  const int hl = tid / TPH, c = tid % TPH;
+  if (hl >= p.hpg) return;                 // whole TPH-lane groups drop out together
+  const int h = g * p.hpg + hl;
+  const int i = p.pos[b];
+  const int j0 = max(0, i - W);
+  const int nw = i - j0;
+  const int t0 = slice * p.tw, t1 = min(t0 + p.tw, nw + 1);
+  const bool rope = p.rope_base != 0.f;
+  const int pc = (8 * c < DH / 2) ? 8 * c + DH / 2 : 8 * c - DH / 2;
+  auto rotate = [&](const bf16x8& x, const bf16x8& xp, float* out, float scale) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int d = 8 * c + k;
+      const int f = d < DH / 2 ? d : d - DH / 2;
+      const float cc = rope ? cs[f][0] : 1.f, sn = rope ? cs[f][1] : 0.f;
+      const float a = to_f(x[k]), bp = to_f(xp[k]);
+      out[k] = scale * (d < DH / 2 ? a * cc - bp * sn : bp * sn + a * cc);
+    }
+  };
+  const int64_t hrow = ((int64_t)b * H + h) * DH;
+  float qf[8];
+  {
+    const bf16* qr = static_cast<const bf16*>(p.q) + hrow;
+    rotate(*reinterpret_cast<const bf16x8*>(qr + 8 * c), *reinterpret_cast<const bf16x8*>(qr + pc), qf,
+           p.scale);
+  }
+  const bool has_self = t0 <= nw && nw < t1;
+  float kself[8], vself[8];
+  if (has_self) {
+    const bf16* kc = static_cast<const bf16*>(p.k_cur) + hrow;
+    rotate(*reinterpret_cast<const bf16x8*>(kc + 8 * c), *reinterpret_cast<const bf16x8*>(kc + pc), kself,
+           1.f);
+    const bf16x8 vv = *reinterpret_cast<const bf16x8*>(static_cast<const bf16*>(p.v_cur) + hrow + 8 * c);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) vself[k] = to_f(vv[k]);
+  }
+  const bf16* ring_k = static_cast<const bf16*>(p.ring_k);
+  const bf16* ring_v = static_cast<const bf16*>(p.ring_v);
+  const int64_t rs = (int64_t)H * DH;
+  const int64_t base = (int64_t)b * (W + 1) * rs + (int64_t)h * DH + 8 * c;
+  float m = -INFINITY, l = 0.f, o[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) o[k] = 0.f;
+  // batches of U ring tokens, double-buffered: batch n+1 is requested before
+  // batch n is consumed.  Loads past the slice reread a valid slot, so every
+  // refill is unconditional.
+  constexpr int U = 16;
+  auto slot_of = [&](int t) { return (j0 + min(t, max(nw - 1, 0))) % (W + 1); };
+  auto load_batch = [&](bf16x8 (&kr)[U], bf16x8 (&vr)[U], int tb) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t off = base + slot_of(tb + u) * rs;
+      kr[u] = *reinterpret_cast<const bf16x8*>(ring_k + off);
+      vr[u] = *reinterpret_cast<const bf16x8*>(ring_v + off);
+    }
+  };
+  auto consume = [&](const bf16x8 (&kr)[U], const bf16x8 (&vr)[U], int tb) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = tb + u;
+      if (t >= t1) break;
+      float kk[8], vv[8];
+      if (t < nw) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) { kk[k] = to_f(kr[u][k]); vv[k] = to_f(vr[u][k]); }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) { kk[k] = kself[k]; vv[k] = vself[k]; }
+      }
+      float sc = 0.f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) sc += qf[k] * kk[k];
+      for (int off = 1; off < TPH; off <<= 1) sc += __shfl_xor(sc, off);
+      const float mn = fmaxf(m, sc);
+      const float alpha = exp2_diff(m, mn);
+      const float pw = exp2f(sc - mn);
+      l = l * alpha + pw;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) o[k] = o[k] * alpha + pw * vv[k];
+      m = mn;
+    }
+  };
+  if (t0 < t1) {
+    bf16x8 kA[U], vA[U], kB[U], vB[U];
+    load_batch(kA, vA, t0);
+    for (int tb = t0; tb < t1; tb += 2 * U) {
+      load_batch(kB, vB, tb + U);
+      consume(kA, vA, tb);
+      if (tb + U >= t1) break;
+      load_batch(kA, vA, tb + 2 * U);
+      consume(kB, vB, tb + U);
+    }
+  }
+  const int64_t row = ((int64_t)b * p.WS + slice) * H + h;
+  if (c == 0) {
+    p.win_ml[row * 2 + 0] = m;
+    p.win_ml[row * 2 + 1] = l;
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) p.win_o[row * DH + 8 * c + k] = o[k];
+  if (has_self) {
+    // slot i mod (W+1) held token i-W-1, which no slice reads
+    const int64_t so = (int64_t)b * (W + 1) * rs + (int64_t)(i % (W + 1)) * rs + (int64_t)h * DH + 8 * c;
+    bf16x8 kw, vw;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      kw[k] = static_cast<bf16>(kself[k]);
+      vw[k] = static_cast<bf16>(vself[k]);
+    }
+    *reinterpret_cast<bf16x8*>(static_cast<bf16*>(p.ring_k) + so) = kw;
+    *reinterpret_cast<bf16x8*>(static_cast<bf16*>(p.ring_v) + so) = vw;
+  }
+}
+
 template <int RK, int RV>
 __global__ __launch_bounds__(kThreads, 1) void k_scan_absorbed_mfma(DecodeParams p) {
   const int s = blockIdx.x, b = blockIdx.y, g = blockIdx.z;
@@ -124,21 +254,24 @@ __global__ __launch_bounds__(kThreads, 1) void k_scan_absorbed_mfma(DecodeParams
   int t1 = (s == p.S - 1) ? n_lat : min(n_lat, t0 + p.chunk);
   if (t0 > n_lat) t0 = n_lat;
 
-  // q~ of the group's heads, as the B operand of the score MFMA
-  bf16x8 qreg[RK / 32];
+  // q~ of the group's heads (B operand of the score MFMA), staged in LDS
+  __shared__ __attribute__((aligned(16))) bf16 qs[16][RK + 8];
   {
-    const bf16* qsrc = static_cast<const bf16*>(p.qlat) +
-                       ((int64_t)b * p.H + (int64_t)g * hpg + col) * RK + grp * 8;
-#pragma unroll
-    for (int st = 0; st < RK / 32; ++st) {
-      if (col < hpg) {
-        qreg[st] = *reinterpret_cast<const bf16x8*>(qsrc + st * 32);
+    const bf16* qsrc = static_cast<const bf16*>(p.qlat) + ((int64_t)b * p.H + (int64_t)g * hpg) * RK;
+    for (int x = tid; x < 16 * RK / 8; x += kThreads) {
+      const int hh = x / (RK / 8), c8 = (x % (RK / 8)) * 8;
+      bf16x8 v;
+      if (hh < hpg) {
+        v = *reinterpret_cast<const bf16x8*>(qsrc + (int64_t)hh * RK + c8);
       } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) qreg[st][e] = static_cast<bf16>(0.f);
+        for (int e = 0; e < 8; ++e) v[e] = static_cast<bf16>(0.f);
       }
+      *reinterpret_cast<bf16x8*>(&qs[hh][c8]) = v;
     }
   }
+  __syncthreads();
+  const bf16* qrow = &qs[col][grp * 8];
   f32x4 acc[RV / 16];
 #pragma unroll
   for (int vt = 0; vt < RV / 16; ++vt) acc[vt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -155,30 +288,58 @@ __global__ __launch_bounds__(kThreads, 1) void k_scan_absorbed_mfma(DecodeParams
   };
   auto tile_valid = [&](int ti) -> int { return min(16, t1 - (t0 + ti * 16)); };
 
-  // Staggered pipeline: the next tile's keys are requested as soon as the
-  // score MFMAs have consumed the current ones, its values as soon as the
-  // value MFMAs have; about one tile per wave stays in flight.
-  bf16x8 kreg[RK / 32];
-  s16x4 vreg[RV / 16];
+  // Keys run two tiles ahead, values one: tile n+2's keys are requested as
+  // soon as the score MFMAs have consumed tile n's, tile n+1's values as soon
+  // as tile n's value MFMAs are issued.  Refills are unconditional (clamped
+  // to the last tile, still cached) so no register set has to survive a
+  // skipped refill.
+  bf16x8 kA[RK / 32], kB[RK / 32];
+  s16x4 vv[RV / 16];
   int ti = wave;
   if (ti < ntiles) {
     const bf16* tp = tile_ptr(ti);
-    load_keys<RK>(kreg, tp, col, grp);
-    load_values<RK, RV>(vreg, tp, col, grp);
+    load_keys<RK>(kA, tp, col, grp);
+    load_values<RK, RV>(vv, tp, col, grp);
+    load_keys<RK>(kB, tile_ptr(min(ti + kWaves, ntiles - 1)), col, grp);
   }
   while (ti < ntiles) {
-    const int tn = ti + kWaves;
-    const int nvalid = tile_valid(ti);
-    const bf16* np = (tn < ntiles) ? tile_ptr(tn) : nullptr;
-    const f32x4 sc = tile_scores<RK>(kreg, qreg);
-    if (np) load_keys<RK>(kreg, np, col, grp);
-    const s16x4 pb = tile_softmax<RV>(sc, acc, m, lsum, nvalid, grp);
-    tile_values<RV>(vreg, pb, acc, nvalid, grp);
-    if (np) load_values<RK, RV>(vreg, np, col, grp);
-    ti = tn;
+    {
+      const f32x4 sc = tile_scores<RK>(kA, qrow);
+      __builtin_amdgcn_sched_barrier(0);   // keep each refill below its consumer
+      load_keys<RK>(kA, tile_ptr(min(ti + 2 * kWaves, ntiles - 1)), col, grp);
+      const s16x4 pb = tile_softmax<RV>(sc, acc, m, lsum, tile_valid(ti), grp);
+      tile_values<RV>(vv, pb, acc, tile_valid(ti), grp);
+      __builtin_amdgcn_sched_barrier(0);
+      load_values<RK, RV>(vv, tile_ptr(min(ti + kWaves, ntiles - 1)), col, grp);
+      ti += kWaves;
+    }
+    if (ti >= ntiles) break;
+    {
+      const f32x4 sc = tile_scores<RK>(kB, qrow);
+      __builtin_amdgcn_sched_barrier(0);
+      load_keys<RK>(kB, tile_ptr(min(ti + 2 * kWaves, ntiles - 1)), col, grp);
+      const s16x4 pb = tile_softmax<RV>(sc, acc, m, lsum, tile_valid(ti), grp);
+      tile_values<RV>(vv, pb, acc, tile_valid(ti), grp);
+      __builtin_amdgcn_sched_barrier(0);
+      load_values<RK, RV>(vv, tile_ptr(min(ti + kWaves, ntiles - 1)), col, grp);
+      ti += kWaves;
+    }
   }
   lsum += __shfl_xor(lsum, 16);
   lsum += __shfl_xor(lsum, 32);
+
+  // ---- this split's slice of the exact window (same launch, same HBM stream)
+  if (p.fuse_window) {
+    __shared__ float cs[64][2];
+    if (tid < p.dh / 2) {
+      float c = 1.f, sn = 0.f;
+      if (p.rope_base != 0.f) rope_cs(p.rope_base, p.dh, tid, i, c, sn);
+      cs[tid][0] = c;
+      cs[tid][1] = sn;
+    }
+    __syncthreads();
+    window_slice(p, b, s, g, cs);
+  }
 
   // ---- merge the four waves (fixed order) and write the split's partial
   __shared__ float mw[kWaves][16];

@@ -160,6 +160,9 @@ size_t lla_write_workspace_bytes(const lla_set_desc* desc, int32_t batch,
  *   out           [batch][H][d_h]
  *   workspace     scratch of lla_decode_workspace_bytes() bytes; contents
  *                 on entry are irrelevant
+ *   scan_events   optional (host) array of two hipEvent_t, recorded on
+ *                 `stream` right before and right after the latent-scan
+ *                 kernel (profiling); NULL = none
  */
 typedef struct {
   int32_t loop;
@@ -178,6 +181,7 @@ typedef struct {
   void* out;
   void* workspace;
   size_t workspace_bytes;
+  void* scan_events;
 } lla_decode_args;
 
 /*

@@ -71,7 +71,7 @@ def test_unsupported_descriptor():
     # rope baked into a key latent that is not whole d_h blocks
     d = hla_main(r_k=96, r_v=96)
     st = B.LlaStore(FAKE, FAKE, 4)
-    args = B.LlaDecodeArgs(2, 16, 100, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30)
+    args = B.LlaDecodeArgs(2, 16, 100, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None)
     assert B.lib.hla_decode_windowed(ctypes.byref(d), ctypes.byref(st), 4, ctypes.byref(args), None) \
         == B.LLA_ERR_UNSUPPORTED
     big = hla_main(head_dim=512, r_k=512)
@@ -82,7 +82,7 @@ def test_unsupported_descriptor():
 def _args(**kw):
     a = dict(loop=2, window=16, max_pos_hint=100, splits=0, flags=0, pos=FAKE, q=FAKE, k_cur=FAKE,
              v_cur=FAKE, ring_k=FAKE, ring_v=FAKE, A=FAKE, B=FAKE, out=FAKE, workspace=FAKE,
-             workspace_bytes=1 << 40)
+             workspace_bytes=1 << 40, scan_events=None)
     a.update(kw)
     return B.LlaDecodeArgs(*[a[f] for f, _ in B.LlaDecodeArgs._fields_])
 

@@ -49,6 +49,20 @@ def test_hla_bf16(r, splits, generic):
     check(c, "hla", "absorbed", splits=splits, flags=1 if generic else 0)
 
 
+@pytest.mark.parametrize("W, positions", [(128, (4095, 700, 129, 128)), (40, (500, 41, 12))])
+def test_hla_bf16_window_slices(W, positions):
+    """Exact windows spanning several 32-token slices, ragged last slice."""
+    c = hla_case(150 + W, positions=positions, W=W)
+    check(c, "hla", "absorbed")
+    check(hla_case(150 + W, positions=positions, W=W), "hla", "absorbed", flags=1)
+
+
+def test_hla_bf16_many_splits():
+    """More context splits than the fast combine takes: the general combine merges them."""
+    c = hla_case(160, positions=(4700,), W=16)
+    check(c, "hla", "absorbed", splits=40)
+
+
 def test_hla_bf16_matches_textbook_form_too():
     c = hla_case(7)
     out, _, _ = run_decode("hla", c)

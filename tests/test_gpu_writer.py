@@ -1,0 +1,127 @@
+"""Parity of the latent writer (Eq. 2 of the Hybrid Latent Attention summary)
+with the fp64 oracle, through the C ABI, and writer -> decode end to end."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from compressed_cross_loop_amd import binding as B
+from synth import gen
+from tests.gpu_cases import TOL
+from tests.util import max_rel_err
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL = 7.0
+
+
+def run_writer(*, batch, n_tok, n_loops, groups, r_k, r_v, d_in, dtype, positions, head_dim=128,
+               rope_base=0.0, rope_baked=0, page_size=64, seed=0, max_pos=None):
+    print(f"[case] writer B={batch} n_tok={n_tok} loops={n_loops} G={groups} r={r_k}/{r_v} "
+          f"d_in={d_in} dtype={dtype} rope={rope_base}", flush=True)
+    wi = gen.writer_inputs(seed, batch=batch, n_tok=n_tok, n_loops=n_loops, groups=groups, r_k=r_k,
+                           r_v=r_v, d_in=d_in, dtype=dtype, positions=positions)
+    max_pos = int(np.max(positions)) if max_pos is None else max_pos
+    pps = -(-(max_pos + 1) // page_size)
+    bt, n_pages = gen.block_table(gen.rng(seed, 5), batch, pps, 2)
+    dt = gen.TORCH_DTYPE[dtype]
+    pages = torch.full((n_pages, groups * page_size * (r_k + r_v)), SENTINEL, dtype=dt, device="cuda")
+    bt_d = torch.from_numpy(bt).cuda()
+    desc = B.set_desc(n_heads=groups, head_dim=head_dim, groups=groups, r_k=r_k, r_v=r_v,
+                      loop_first=1, loop_last=n_loops, page_size=page_size, rope_baked=rope_baked,
+                      rope_base=rope_base, dtype=B.LLA_BF16 if dtype == "bf16" else B.LLA_F32)
+    nbytes = B.lla_write_workspace_bytes(desc, batch, n_tok, d_in)
+    ws = torch.full((max(nbytes, 4) // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    B.lla_write_latents(desc, B.store(pages, bt_d), pos=wi.pos.cuda(), x=wi.x.cuda(),
+                        enc=wi.enc.cuda(), workspace=ws)
+    torch.cuda.synchronize()
+    want = O.write_latents(wi.x.double().numpy(), wi.enc.double().numpy(), wi.pos.numpy(), r_k=r_k,
+                           rope_base=rope_base, rope_baked=rope_baked, head_dim=head_dim)
+    got_pages = pages.double().cpu().numpy()
+    kw = dict(groups=groups, page_size=page_size, r_k=r_k, r_v=r_v)
+    touched = np.zeros(got_pages.size, dtype=bool)
+    got = np.zeros_like(want)
+    for b in range(batch):
+        for n in range(n_tok):
+            p = int(wi.pos[b, n])
+            pg, sl = int(bt[b, p // page_size]), p % page_size
+            for g in range(groups):
+                ko = O.store_key_offset(pg, g, sl, np.arange(r_k), **kw)
+                vo = O.store_value_offset(pg, g, sl, np.arange(r_v), **kw)
+                got[b, n, g] = np.concatenate([got_pages.ravel()[ko], got_pages.ravel()[vo]])
+                touched[ko] = touched[vo] = True
+    # nothing outside the written slots changed
+    assert np.all(got_pages.ravel()[~touched] == SENTINEL)
+    return got, want
+
+
+@pytest.mark.parametrize("set_key", [0, 1])
+def test_writer_fp32_tiny(set_key):
+    """Workload 1 shapes: loop-1 set (r_1 = 32) and main set (128 + 128), d = 128."""
+    n_loops, r = (1, 32) if set_key == 0 else (3, 128)
+    got, want = run_writer(batch=1, n_tok=5, n_loops=n_loops, groups=1, r_k=r, r_v=r, d_in=128,
+                           dtype="f32", positions=[[0, 17, 100, 254, 255]], head_dim=64, seed=3)
+    assert max_rel_err(got, want) < 1e-5
+
+
+def test_writer_bf16_hla_rope_baked():
+    """Main HLA set at the Ouro-1.4B shape: 3 loops x d = 2048 -> 512 + 512, RoPE baked."""
+    got, want = run_writer(batch=3, n_tok=2, n_loops=3, groups=1, r_k=512, r_v=512, d_in=2048,
+                           dtype="bf16", positions=[[5, 4095], [1000, 77], [64, 63]],
+                           rope_base=10000.0, rope_baked=1, seed=4)
+    assert max_rel_err(got, want) < TOL["bf16"]
+
+
+def test_writer_bf16_per_head():
+    """Per-head LLA set: 16 groups, [k; v] of 256 per loop -> 32 + 32, 4 loops."""
+    got, want = run_writer(batch=2, n_tok=3, n_loops=4, groups=16, r_k=32, r_v=32, d_in=256,
+                           dtype="bf16", positions=[[0, 1, 2], [300, 301, 302]], seed=5)
+    assert max_rel_err(got, want) < TOL["bf16"]
+
+
+def test_writer_bf16_generic_path():
+    """d_in not a multiple of 32 takes the general kernel."""
+    got, want = run_writer(batch=2, n_tok=2, n_loops=2, groups=2, r_k=64, r_v=48, d_in=48,
+                           dtype="bf16", positions=[[3, 9], [70, 71]], head_dim=64,
+                           rope_base=10000.0, rope_baked=1, seed=6)
+    assert max_rel_err(got, want) < TOL["bf16"]
+
+
+def test_writer_then_decode_end_to_end():
+    """GPU writer fills the whole store, GPU decode reads it; the oracle writes
+    fp64 latents and decodes them.  Same seeded inputs on both sides."""
+    H, dh, r, W, n_loops, d_in, P = 16, 128, 256, 8, 3, 256, 64
+    N = 150
+    Bsz = 2
+    base = 10000.0
+    wi = gen.writer_inputs(7, batch=Bsz, n_tok=N, n_loops=n_loops, groups=1, r_k=r, r_v=r, d_in=d_in,
+                           dtype="bf16", positions=np.tile(np.arange(N), (Bsz, 1)), enc_scale=1.0)
+    dc = gen.decode_inputs(8, batch=Bsz, heads=H, head_dim=dh, groups=1, r_k=r, r_v=r,
+                           positions=[N - 1, N - 1], window=W, dtype="bf16", page_size=P,
+                           rope_base=base, rope_baked=1, loop=3, loop_first=2, loop_last=4,
+                           exact_std=np.sqrt(3.0))
+    desc = B.set_desc(n_heads=H, head_dim=dh, groups=1, r_k=r, r_v=r, loop_first=2, loop_last=4,
+                      page_size=P, rope_baked=1, rope_base=base, dtype=B.LLA_BF16)
+    pages = torch.full(tuple(dc.pages.shape), float("nan"), dtype=torch.bfloat16, device="cuda")
+    bt = dc.block_table.cuda()
+    st = B.store(pages, bt)
+    ws = torch.empty(max(B.lla_write_workspace_bytes(desc, Bsz, N, d_in), 4), dtype=torch.uint8,
+                     device="cuda")
+    B.lla_write_latents(desc, st, pos=wi.pos.cuda(), x=wi.x.cuda(), enc=wi.enc.cuda(), workspace=ws)
+    out = torch.empty(tuple(dc.q.shape), dtype=torch.bfloat16, device="cuda")
+    dws = torch.empty(B.lla_decode_workspace_bytes(desc, Bsz, N - 1, W), dtype=torch.uint8, device="cuda")
+    rk, rv = dc.ring_k.cuda(), dc.ring_v.cuda()
+    args = B.decode_args(loop=3, window=W, pos=dc.pos.cuda(), q=dc.q.cuda(), k_cur=dc.k_cur.cuda(),
+                         v_cur=dc.v_cur.cuda(), ring_k=rk, ring_v=rv, A=dc.A.cuda(), B=dc.Bv.cuda(),
+                         out=out, workspace=dws, max_pos_hint=N - 1)
+    B.hla_decode_windowed(desc, st, Bsz, args)
+    torch.cuda.synchronize()
+    c = O.write_latents(wi.x.double().numpy(), wi.enc.double().numpy(), wi.pos.numpy(), r_k=r,
+                        rope_base=base, rope_baked=1, head_dim=dh)
+    sK = [c[b, :, :, :r] for b in range(Bsz)]
+    sV = [c[b, :, :, r:] for b in range(Bsz)]
+    f = [t.double().numpy() for t in (dc.q, dc.k_cur, dc.v_cur, dc.ring_k, dc.ring_v, dc.A, dc.Bv)]
+    ref = O.absorbed_decode(sK, sV, dc.pos.numpy(), *f, window=W, rope_base=base)
+    ref_t = O.textbook_decode(sK, sV, dc.pos.numpy(), *f, window=W, rope_base=base)
+    assert max_rel_err(ref, ref_t) < 1e-10
+    assert max_rel_err(out.float().cpu().numpy(), ref) < TOL["bf16"]
