@@ -36,6 +36,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run one device-to-device copy of BYTES (HBM counter calibration)")
     return ap.parse_args()
 
 
@@ -218,11 +220,44 @@ def cpu_baseline(w, budget_s, seed=0):
     }
 
 
+def calibrate_copy(nbytes):
+    """One plain copy of known size, so that profiler HBM byte counters can be
+    scaled (a copy reads and writes nbytes each)."""
+    import torch
+    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration_copy_bytes": nbytes}))
+
+
+def scan_source_sha():
+    import hashlib
+    path = os.path.join(ROOT, "compressed_cross_loop_amd", "csrc", "scan_absorbed_mfma.hip")
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(workload_name):
+    """HBM bytes per launch of the scan kernel from the profiler counters kept
+    in profiles/traffic.json, or None when they were taken on other source."""
+    tp = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(tp):
+        return None
+    rec = json.load(open(tp))
+    if rec.get("scan_source_sha") != scan_source_sha():
+        return None
+    return rec.get("workloads", {}).get(workload_name)
+
+
 def main():
     a = parse()
     if a.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
+    if a.calibrate_copy:
+        calibrate_copy(a.calibrate_copy)
+        return
     import torch
     from synth import configs
     w = configs.get(a.workload)
@@ -259,10 +294,7 @@ def main():
     s_main = w.sets[main_k]
     q_bytes = w.batch * w.heads * s_main.r_k * (2 if w.dtype == "bf16" else 4)
     achieved = (lat_bytes + q_bytes) / (scan_ms * 1e-3) / 1e9
-    traffic = None
-    tp = os.path.join(ROOT, "profiles", "traffic.json")
-    if os.path.exists(tp):
-        traffic = json.load(open(tp)).get(w.name)
+    traffic = measured_traffic(w.name)
 
     gbs = step_bytes / (ms * 1e-3) / 1e9
     rec = {

@@ -34,6 +34,8 @@ template <int DH, int NB>
 __global__ __launch_bounds__(kThreads) void k_qmap_mfma(DecodeParams p, int want_qlat) {
   __shared__ __attribute__((aligned(16))) bf16 AtT[NB][DH + 8];
   __shared__ float csn[16][DH / 2][2];
+  __shared__ double theta[DH / 2];
+  __shared__ int posb[16];
   const int h = blockIdx.x, blk = blockIdx.y, b0 = blockIdx.z * 16;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
@@ -53,12 +55,26 @@ __global__ __launch_bounds__(kThreads) void k_qmap_mfma(DecodeParams p, int want
       av[u] = *reinterpret_cast<const bf16x8*>(Ah + (int64_t)e * rk + n8);
     }
   }
+  // A operand (q rows of the 16 sequences), requested together with A
+  const int brow = b0 + col;
+  bf16x8 aq[DH / 32];
+#pragma unroll
+  for (int st = 0; st < DH / 32; ++st) {
+    if (brow < p.B) {
+      aq[st] = *reinterpret_cast<const bf16x8*>(q + ((int64_t)brow * H + h) * DH + st * 32 + grp * 8);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) aq[st][k] = static_cast<bf16>(0.f);
+    }
+  }
+  if (tid < 16) posb[tid] = p.pos[min(b0 + tid, p.B - 1)];
+  if (rope && tid < DH / 2) theta[tid] = rope_theta(p.rope_base, DH, tid);
+  __syncthreads();
   if (rope) {
     for (int x = tid; x < 16 * (DH / 2); x += kThreads) {
       const int bl = x / (DH / 2), f = x % (DH / 2);
-      const int bb = min(b0 + bl, p.B - 1);
       float c, sn;
-      rope_cs(p.rope_base, DH, f, p.pos[bb], c, sn);
+      rope_cs_theta(theta[f], posb[bl], c, sn);
       csn[bl][f][0] = c;
       csn[bl][f][1] = sn;
     }
@@ -69,7 +85,7 @@ __global__ __launch_bounds__(kThreads) void k_qmap_mfma(DecodeParams p, int want
       const int bl = x / (DH / 2), f = x % (DH / 2), bb = b0 + bl;
       if (bb >= p.B) continue;
       float c = 1.f, sn = 0.f;
-      if (rope) rope_cs(p.rope_base, DH, f, p.pos[bb], c, sn);
+      if (rope) rope_cs_theta(theta[f], posb[bl], c, sn);
       const bf16* qr = q + ((int64_t)bb * H + h) * DH;
       const float a = to_f(qr[f]), b = to_f(qr[f + DH / 2]);
       float* qh = p.qhead + ((int64_t)bb * H + h) * DH;
@@ -89,18 +105,6 @@ __global__ __launch_bounds__(kThreads) void k_qmap_mfma(DecodeParams p, int want
   __syncthreads();
   if (!want_qlat) return;
 
-  // A operand: q rows of the 16 sequences
-  const int brow = b0 + col;
-  bf16x8 aq[DH / 32];
-#pragma unroll
-  for (int st = 0; st < DH / 32; ++st) {
-    if (brow < p.B) {
-      aq[st] = *reinterpret_cast<const bf16x8*>(q + ((int64_t)brow * H + h) * DH + st * 32 + grp * 8);
-    } else {
-#pragma unroll
-      for (int k = 0; k < 8; ++k) aq[st][k] = static_cast<bf16>(0.f);
-    }
-  }
   constexpr int NT = NB / 16;       // column tiles
   constexpr int HT = DH / 32;       // tile distance of a rotary pair (rope: NB == DH)
   auto tile = [&](int j) {
@@ -367,13 +371,38 @@ __global__ __launch_bounds__(kThreads) void k_combine_mfma(DecodeParams p) {
       }
     }
   }
-  for (int x = tid; x < 16 * DH; x += kThreads) {
-    const int bl = x / DH, e = x % DH, b = b0 + bl;
-    float acc = 0.f;
-    if (b < p.B)
-      for (int s = 0; s < WS; ++s) acc += pm[bl][S + s] * p.win_o[(((int64_t)b * WS + s) * H + h) * DH + e];
-    wo[bl][e] = acc;
+  {
+    // window sums: thread -> (sequence bl, 8 consecutive dims), all slices'
+    // loads issued together (four at a time)
+    const int bl = tid / 16, e8 = (tid % 16) * 8, b = b0 + bl;
+    f32x4 w0 = {0.f, 0.f, 0.f, 0.f}, w1 = {0.f, 0.f, 0.f, 0.f};
+    if (b < p.B) {
+      for (int s0 = 0; s0 < WS; s0 += 4) {
+        f32x4 v[4][2];
+#pragma unroll
+        for (int ss = 0; ss < 4; ++ss) {
+          const int sl = min(s0 + ss, WS - 1);
+          const float4* src = reinterpret_cast<const float4*>(
+              p.win_o + (((int64_t)b * WS + sl) * H + h) * DH + e8);
+          const float4 a = src[0], c = src[1];
+          v[ss][0] = f32x4{a.x, a.y, a.z, a.w};
+          v[ss][1] = f32x4{c.x, c.y, c.z, c.w};
+        }
+#pragma unroll
+        for (int ss = 0; ss < 4; ++ss) {
+          const float w = (s0 + ss < WS) ? pm[bl][S + s0 + ss] : 0.f;
+          w0 += w * v[ss][0];
+          w1 += w * v[ss][1];
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      wo[bl][e8 + k] = w0[k];
+      wo[bl][e8 + 4 + k] = w1[k];
+    }
   }
+  __syncthreads();
   // out[16 b x 128] = ob[16 x RV] . B^(h)[RV x 128]; wave w owns column tiles w and w+4
   const int col = lane & 15, kq = lane >> 4;
   f32x4 acc[2][2];
