@@ -36,6 +36,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--entry", choices=["auto", "hla", "absorbed", "reconstruct"], default="auto",
+                    help="decode entry point (auto: hla for HLA workloads, reconstruct for LLA ones)")
+    ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = workload's)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run one device-to-device copy of BYTES (HBM counter calibration)")
     return ap.parse_args()
@@ -68,10 +71,14 @@ class Hip:
 
 
 # --------------------------------------------------------------------------- HLA
-class HlaStep:
-    """Every buffer of one HLA decode step (all layers, all loops), on the GPU."""
+ENTRY_KERNEL = {"hla": "k_scan_absorbed_mfma", "absorbed": "k_scan_absorbed_mfma",
+                "reconstruct": "k_scan_reconstruct_generic"}
 
-    def __init__(self, w, splits=0, seed=0):
+
+class DecodeStep:
+    """Every buffer of one decode step (all layers, all loops), on the GPU."""
+
+    def __init__(self, w, splits=0, seed=0, entry="auto"):
         import torch
         from compressed_cross_loop_amd import binding as B
         from synth import gen
@@ -126,7 +133,11 @@ class HlaStep:
                                      ring_v=rv, A=A, B=Bm, out=out, workspace=self.ws,
                                      max_pos_hint=self.i, splits=splits)
                 self.calls.append((t, k, l, self.sets[k]["desc"], self.sets[k]["stores"][l], args, bufs))
-        self.entry = B.hla_decode_windowed if w.family == "hla" else B.lla_decode_absorbed
+        if entry == "auto":
+            entry = "hla" if w.family == "hla" else "reconstruct"
+        self.entry_name = entry
+        self.entry = {"hla": B.hla_decode_windowed, "absorbed": B.lla_decode_absorbed,
+                      "reconstruct": B.lla_decode_reconstruct}[entry]
         torch.cuda.synchronize()
 
     def step(self):
@@ -153,7 +164,13 @@ class HlaStep:
             win = Bt * n_win * H * dh * 2 * e
             act = Bt * H * dh * e * (4 + 2)          # q, k_cur, v_cur, out + ring slot write (K, V)
             maps = H * dh * (s.r_k + s.r_v) * e
-            per_call[k] = (lat + win, lat + win + act + maps)
+            # bytes the scan kernel itself must read: latents (+ the exact window,
+            # fused into the scan on the matrix-core path) (+ the decoders when
+            # keys and values are rebuilt)
+            scan = lat + (win if self.entry_name != "reconstruct" else maps)
+            flop = 2 * Bt * n_lat * s.groups * (s.r_k + s.r_v) * (H // s.groups) * \
+                (dh if self.entry_name == "reconstruct" else 1) * (1 if self.entry_name == "reconstruct" else 2)
+            per_call[k] = (scan, lat + win + act + maps, flop)
             total += lat + win + act + maps
         for s in w.sets:
             total += w.layers * (Bt * s.n_loops * s.groups * s.d_in * e
@@ -162,10 +179,11 @@ class HlaStep:
         return total, per_call
 
 
-def cpu_baseline(w, budget_s, seed=0):
-    """The fp64 oracle's absorbed read (the function that checks
-    hla_decode_windowed), timed on the host cores on whole sequences of the
-    same workload, scaled to decode tokens/s of the full step."""
+def cpu_baseline(w, budget_s, seed=0, entry="hla"):
+    """The fp64 oracle form that checks the timed entry point (absorbed_decode
+    for the absorbed/HLA read, textbook_decode for reconstruct-on-read), timed
+    on the host cores on whole sequences of the same workload, scaled to
+    decode tokens/s of the full step."""
     import threadpoolctl
     import oracle as O
     from synth import gen
@@ -191,7 +209,8 @@ def cpu_baseline(w, budget_s, seed=0):
     def one_sequence(k):
         s, pages, bt, q, kc, vc, rk, rv, A, Bv = per_set[k]
         sK, sV = O.gather_latents(pages, bt, 0, n_lat, groups=s.groups, page_size=P, r_k=s.r_k, r_v=s.r_v)
-        O.absorbed_decode([sK], [sV], [i], q, kc, vc, rk, rv, A, Bv, window=W, rope_base=w.rope_base)
+        fn = O.textbook_decode if entry == "reconstruct" else O.absorbed_decode
+        fn([sK], [sV], [i], q, kc, vc, rk, rv, A, Bv, window=W, rope_base=w.rope_base)
 
     t_set = []
     n_done = 0
@@ -202,7 +221,7 @@ def cpu_baseline(w, budget_s, seed=0):
         while True:
             one_sequence(k)
             n += 1
-            if time.perf_counter() - t0 >= per_share or n >= w.batch:
+            if time.perf_counter() - t0 >= per_share:
                 break
         t_set.append((time.perf_counter() - t0) / n)
         n_done += n
@@ -214,7 +233,8 @@ def cpu_baseline(w, budget_s, seed=0):
     return {
         "value": 1.0 / t_seq_step, "unit": "tokens/s", "cores": int(blas_threads),
         "host_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
-        "sample": (f"oracle absorbed_decode (fp64 numpy) on {n_done} whole sequences "
+        "sample": (f"oracle {'textbook' if entry == 'reconstruct' else 'absorbed'}_decode (fp64 numpy) "
+                   f"on {n_done} whole sequences "
                    f"({', '.join(f'{t * 1e3:.1f} ms/seq/call set{k}' for k, t in enumerate(t_set))}) "
                    f"in {wall:.1f} s, scaled to {w.layers} layers x {w.loops} loops per token"),
     }
@@ -262,7 +282,9 @@ def main():
     from synth import configs
     w = configs.get(a.workload)
     hip = Hip()
-    st = HlaStep(w, splits=a.splits)
+    if a.layers:
+        w = w.with_(layers=a.layers)
+    st = DecodeStep(w, splits=a.splits, entry=a.entry)
     stream = torch.cuda.current_stream().cuda_stream
     for _ in range(a.warmup):
         st.step()
@@ -276,7 +298,7 @@ def main():
     ms = hip.elapsed_ms(e0, e1) / a.steps
     step_bytes, per_call = st.step_bytes()
 
-    # dominant kernel: the latent scan of the main set (loops 2..T), timed live
+    # dominant kernel: the scan of the set serving the most loops, timed live
     main_k = max(per_call, key=lambda k: per_call[k][0] * w.sets[k].n_loops)
     evs = []
     rsteps = max(2, min(a.steps, 5))
@@ -290,32 +312,42 @@ def main():
             args.scan_events = None
     torch.cuda.synchronize()
     scan_ms = float(np.mean([hip.elapsed_ms(ctypes.c_void_p(p[0]), ctypes.c_void_p(p[1])) for p in evs]))
-    lat_bytes = per_call[main_k][0]
+    scan_bytes, _, scan_flop = per_call[main_k]
     s_main = w.sets[main_k]
-    q_bytes = w.batch * w.heads * s_main.r_k * (2 if w.dtype == "bf16" else 4)
-    achieved = (lat_bytes + q_bytes) / (scan_ms * 1e-3) / 1e9
-    traffic = measured_traffic(w.name)
+    scan_bytes += w.batch * w.heads * s_main.r_k * (2 if w.dtype == "bf16" else 4) \
+        if st.entry_name != "reconstruct" else 0
+    kname = ENTRY_KERNEL[st.entry_name]
+    if st.entry_name == "reconstruct" and w.dtype == "bf16" and s_main.groups == w.heads and \
+            s_main.r_k == s_main.r_v and s_main.r_k in (32, 64) and w.head_dim in (64, 128):
+        kname = "k_scan_reconstruct_mfma"
+    reconstruct_mfma_bound = st.entry_name == "reconstruct" and scan_flop / scan_bytes > 312
+    if reconstruct_mfma_bound:
+        roof = {"bound": "mfma", "achieved": scan_flop / (scan_ms * 1e-3) / 1e12, "peak": 2500.0,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": scan_bytes / (scan_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = measured_traffic(w.name) if kname == "k_scan_absorbed_mfma" else None
+    roof.update({"kernel": f"{kname} (set serving loops {s_main.loop_first}..{s_main.loop_last})",
+                 "avg_launch_ms": scan_ms, "bytes_per_launch": scan_bytes, "flop_per_launch": scan_flop})
 
     gbs = step_bytes / (ms * 1e-3) / 1e9
     rec = {
         "metric": METRIC, "value": w.batch / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
         "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
-        "config": {"workload": w.name, "layers": w.layers, "loops": w.loops, "batch": w.batch,
-                   "context": w.context, "window": w.window, "heads": w.heads,
+        "config": {"workload": w.name, "entry": st.entry_name, "layers": w.layers, "loops": w.loops,
+                   "batch": w.batch, "context": w.context, "window": w.window, "heads": w.heads,
                    "head_dim": w.head_dim,
                    "sets": [dict(loops=[s.loop_first, s.loop_last], groups=s.groups, r_k=s.r_k,
                                  r_v=s.r_v) for s in w.sets],
                    "splits": a.splits or "auto"},
         "step_bytes": step_bytes, "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
-        "roofline": {"kernel": "k_scan_absorbed_mfma<512,512> (main set: latent scan + exact window)",
-                     "bound": "hbm",
-                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "avg_launch_ms": scan_ms, "bytes_per_launch": lat_bytes + q_bytes},
+        "roofline": roof,
     }
     if not a.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds)
+        rec["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds, entry=st.entry_name)
     print(json.dumps(rec))
 
 

@@ -237,8 +237,7 @@ __global__ __launch_bounds__(kThreads) void k_window_fast(DecodeParams p) {
       float s = 0.f;
 #pragma unroll
       for (int k = 0; k < 8; ++k) s += qf[k] * kk[k];
-#pragma unroll
-      for (int off = 1; off < TPH; off <<= 1) s += __shfl_xor(s, off);
+      s = group_sum(s, TPH);   // the TPH lanes of this head
       const float mn = fmaxf(m, s);
       const float alpha = exp2_diff(m, mn);
       const float pw = exp2f(s - mn);

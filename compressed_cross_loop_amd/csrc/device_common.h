@@ -58,6 +58,36 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Reductions over the 16 lanes of a DPP row (lanes 16k .. 16k+15) with DPP
+// moves instead of LDS permutes: quad_perm [1,0,3,2] and [2,3,0,1] (xor 1,
+// xor 2 inside each quad), row_half_mirror (lane i <-> 7-i inside each half
+// row), row_mirror (lane i <-> 15-i inside the row).  Every lane ends with the
+// row's total.  The 8-lane form stops after the half-row step.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row_sum8(float v) {
+  v += dpp_mov<0xB1>(v);    // quad_perm [1,0,3,2]
+  v += dpp_mov<0x4E>(v);    // quad_perm [2,3,0,1]
+  v += dpp_mov<0x141>(v);   // row_half_mirror
+  return v;
+}
+__device__ __forceinline__ float row_sum16(float v) {
+  v = row_sum8(v);
+  v += dpp_mov<0x140>(v);   // row_mirror
+  return v;
+}
+__device__ __forceinline__ float row_max16(float v) {
+  v = fmaxf(v, dpp_mov<0xB1>(v));
+  v = fmaxf(v, dpp_mov<0x4E>(v));
+  v = fmaxf(v, dpp_mov<0x141>(v));
+  v = fmaxf(v, dpp_mov<0x140>(v));
+  return v;
+}
+// sum over groups of n = 8 or 16 consecutive lanes (n uniform)
+__device__ __forceinline__ float group_sum(float v, int n) { return n == 16 ? row_sum16(v) : row_sum8(v); }
+
 // exp2 of (x - m) for the online softmax; m == -inf (nothing seen yet) gives 0
 __device__ __forceinline__ float exp2_diff(float x, float m) {
   return (m == -INFINITY) ? 0.f : exp2f(x - m);

@@ -56,11 +56,11 @@ struct Plan {
 // Latent tokens of the longest sequence are cut into S contiguous ranges of
 // `chunk` tokens (a multiple of 64); `wgs` workgroups work on each
 // (sequence, range).  S aims at kTargetWorkgroups in flight.
-Plan make_plan(int batch, int max_pos, int window, int splits, int wgs) {
+Plan make_plan(int batch, int max_pos, int window, int splits, int wgs, int target = kTargetWorkgroups) {
   const int64_t n_lat = std::max<int64_t>(0, (int64_t)max_pos - window);
   const int64_t tiles = std::max<int64_t>(1, (n_lat + kChunk - 1) / kChunk);
   int64_t S = splits > 0 ? splits
-                         : (kTargetWorkgroups + (int64_t)batch * wgs - 1) / ((int64_t)batch * wgs);
+                         : (target + (int64_t)batch * wgs - 1) / ((int64_t)batch * wgs);
   S = std::min<int64_t>(std::max<int64_t>(S, 1), tiles);
   const int64_t per = (tiles + S - 1) / S;
   S = (tiles + per - 1) / per;
@@ -79,11 +79,28 @@ bool use_mfma_scan(const lla_set_desc& d, int flags) {
   return scan_absorbed_mfma_supports(p);
 }
 
+bool use_mfma_reconstruct(const lla_set_desc& d, int flags) {
+  if (flags & LLA_FLAG_GENERIC) return false;
+  DecodeParams p{};
+  p.hpg = d.n_heads / d.groups;
+  p.rk = d.r_k;
+  p.rv = d.r_v;
+  p.dh = d.head_dim;
+  p.bf16 = d.dtype == LLA_BF16;
+  return scan_reconstruct_mfma_supports(p);
+}
+
 Plan plan_for(const lla_set_desc& d, int batch, int max_pos, int window, int splits, int entry,
               int flags) {
   const bool absorbed = entry != 0;
-  const int wgs = (absorbed && use_mfma_scan(d, flags)) ? d.groups : d.n_heads;
-  return make_plan(batch, max_pos, window, splits, wgs);
+  int wgs = d.n_heads;                                  // general kernels: one per head
+  int target = kTargetWorkgroups;
+  if (absorbed && use_mfma_scan(d, flags)) wgs = d.groups;
+  if (!absorbed && use_mfma_reconstruct(d, flags)) {
+    wgs = (d.n_heads + 3) / 4;
+    target = 2 * kTargetWorkgroups;   // small workgroups: two resident per CU
+  }
+  return make_plan(batch, max_pos, window, splits, wgs, target);
 }
 
 struct WsLayout {
@@ -187,7 +204,8 @@ lla_status decode(const lla_set_desc* d, const lla_store* st, int32_t batch,
   if (e == hipSuccess && ev) e = hipEventRecord(ev[0], s);
   if (e == hipSuccess) {
     if (!absorbed)
-      e = launch_scan_reconstruct_generic(p, s);
+      e = (!generic && scan_reconstruct_mfma_supports(p)) ? launch_scan_reconstruct_mfma(p, s)
+                                                          : launch_scan_reconstruct_generic(p, s);
     else if (mfma_scan)
       e = launch_scan_absorbed_mfma(p, s);
     else

@@ -63,13 +63,17 @@ __device__ __forceinline__ short bf16_bits(float x) {
 // read 16 distinct bank quads).
 template <int RK>
 __device__ __forceinline__ f32x4 tile_scores(const bf16x8 (&k)[RK / 32], const bf16* qrow) {
-  f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+  // two independent accumulator chains over the K steps
+  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int st = 0; st < RK / 32; ++st) {
     const bf16x8 qv = *reinterpret_cast<const bf16x8*>(qrow + st * 32);
-    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k[st], qv, sc, 0, 0, 0);
+    if (st & 1)
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k[st], qv, s1, 0, 0, 0);
+    else
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k[st], qv, s0, 0, 0, 0);
   }
-  return sc;
+  return s0 + s1;
 }
 
 // Online-softmax update for one tile; returns the bf16 probabilities in the
@@ -184,31 +188,48 @@ __device__ void window_slice(const DecodeParams& p, int b, int slice, int g, con
       vr[u] = *reinterpret_cast<const bf16x8*>(ring_v + off);
     }
   };
+  // one batch: U independent score reductions, one max, then the weighted
+  // sum (no per-token dependency chain)
   auto consume = [&](const bf16x8 (&kr)[U], const bf16x8 (&vr)[U], int tb) {
+    float sc[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int t = tb + u;
-      if (t >= t1) break;
-      float kk[8], vv[8];
+      float a = 0.f;
       if (t < nw) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) { kk[k] = to_f(kr[u][k]); vv[k] = to_f(vr[u][k]); }
+        for (int k = 0; k < 8; ++k) a += qf[k] * to_f(kr[u][k]);
       } else {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) { kk[k] = kself[k]; vv[k] = vself[k]; }
+        for (int k = 0; k < 8; ++k) a += qf[k] * kself[k];
       }
-      float sc = 0.f;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) sc += qf[k] * kk[k];
-      for (int off = 1; off < TPH; off <<= 1) sc += __shfl_xor(sc, off);
-      const float mn = fmaxf(m, sc);
-      const float alpha = exp2_diff(m, mn);
-      const float pw = exp2f(sc - mn);
-      l = l * alpha + pw;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) o[k] = o[k] * alpha + pw * vv[k];
-      m = mn;
+      sc[u] = group_sum(a, TPH);   // the TPH lanes of this head
     }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (tb + u >= t1) sc[u] = -INFINITY;
+      mx = fmaxf(mx, sc[u]);
+    }
+    const float mn = fmaxf(m, mx);
+    const float alpha = exp2_diff(m, mn);
+    l *= alpha;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) o[k] *= alpha;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = tb + u;
+      const float pw = exp2f(sc[u] - mn);
+      l += pw;
+      if (t < nw) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) o[k] += pw * to_f(vr[u][k]);
+      } else if (t < t1) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) o[k] += pw * vself[k];
+      }
+    }
+    m = mn;
   };
   if (t0 < t1) {
     bf16x8 kA[U], vA[U], kB[U], vB[U];

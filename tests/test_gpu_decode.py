@@ -107,8 +107,8 @@ def test_tiny_fp32(entry, form, set_key, loop):
     assert err < 1e-5
 
 
-def per_head_case(seed, *, positions=(200, 77), W=0, dtype="bf16", r=32, H=16):
-    c = gen.decode_inputs(seed, batch=len(positions), heads=H, head_dim=128, groups=H, r_k=r, r_v=r,
+def per_head_case(seed, *, positions=(200, 77), W=0, dtype="bf16", r=32, H=16, d_h=128):
+    c = gen.decode_inputs(seed, batch=len(positions), heads=H, head_dim=d_h, groups=H, r_k=r, r_v=r,
                           positions=positions, window=W, dtype=dtype, loop=2, loop_first=1,
                           loop_last=4, latent_std=4.0, exact_std=1.0, paired=False)
     return poison_unread(c)
@@ -117,6 +117,17 @@ def per_head_case(seed, *, positions=(200, 77), W=0, dtype="bf16", r=32, H=16):
 @pytest.mark.parametrize("W", [0, 5])
 def test_reconstruct_per_head_bf16(W):
     check(per_head_case(400 + W, W=W), "reconstruct", "textbook")
+
+
+@pytest.mark.parametrize("r, d_h, H", [(32, 128, 16), (64, 128, 6), (32, 64, 5), (64, 64, 8)])
+@pytest.mark.parametrize("generic", [False, True])
+def test_reconstruct_per_head_shapes(r, d_h, H, generic):
+    """Matrix-core and general reconstruct kernels: latent widths, head dims,
+    head counts that leave a partial workgroup, ragged contexts, splits."""
+    c = per_head_case(440 + r + d_h + H, positions=(333, 17, 64, 1), W=3, r=r, H=H, d_h=d_h)
+    check(c, "reconstruct", "textbook", flags=1 if generic else 0)
+    c = per_head_case(441 + r + d_h + H, positions=(333, 17, 64, 1), W=3, r=r, H=H, d_h=d_h)
+    check(c, "reconstruct", "textbook", splits=3, flags=1 if generic else 0)
 
 
 @pytest.mark.parametrize("generic", [False, True])

@@ -1,0 +1,132 @@
+"""Parity at the workloads' full sizes, in the launch configuration the bench
+times (automatic split plan): the GPU runs the whole batch, the fp64 oracle
+checks sampled sequences (all heads) one by one.  Workload 5 runs on a
+2-sequence batch at its full context and latent width."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from compressed_cross_loop_amd import binding as B
+from synth import configs, gen
+from tests.util import max_rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+def build(w, set_key, loop, *, batch=None, seed=0, paired=None):
+    """Device buffers of one decode call of workload w (one layer)."""
+    s = w.sets[set_key]
+    Bt = batch or w.batch
+    H, dh, P, W = w.heads, w.head_dim, w.page_size, w.window
+    dt = gen.TORCH_DTYPE[w.dtype]
+    i = w.context - 1
+    pps = -(-w.context // P)
+    g = gen.rng(seed, 1)
+    bt, n_pages = gen.block_table(g, Bt, pps, 2)
+    std = float(np.sqrt(s.n_loops))
+    pages = gen.device_normal((n_pages, s.groups * P * (s.r_k + s.r_v)), w.dtype, seed * 10 + 1, std)
+    q = gen.device_normal((Bt, H, dh), w.dtype, seed * 10 + 2)
+    kc = gen.device_normal((Bt, H, dh), w.dtype, seed * 10 + 3, std)
+    vc = gen.device_normal((Bt, H, dh), w.dtype, seed * 10 + 4, std)
+    rk = gen.device_normal((Bt, W + 1, H, dh), w.dtype, seed * 10 + 5, std)
+    rv = gen.device_normal((Bt, W + 1, H, dh), w.dtype, seed * 10 + 6, std)
+    if paired is None:
+        paired = w.rope_base != 0
+    if paired:
+        A = gen.frequency_paired_decoder(g, H, dh, s.r_k)
+        Bv = np.stack([gen.gaussian_orthonormal(g, s.r_v, dh) for _ in range(H)])
+    else:  # dense decoders, entries N(0, 1/r): decoded K/V of about unit variance
+        A = g.standard_normal((H, dh, s.r_k)) / np.sqrt(s.r_k)
+        Bv = g.standard_normal((H, s.r_v, dh)) / np.sqrt(s.r_v)
+    c = dict(w=w, s=s, loop=loop, batch=Bt, i=i, bt=bt, pages=pages, q=q, kc=kc, vc=vc, rk=rk, rv=rv,
+             A=gen.as_stored(A, w.dtype).cuda(), Bv=gen.as_stored(Bv, w.dtype).cuda(),
+             pos=torch.full((Bt,), i, dtype=torch.int32, device="cuda"))
+    c["desc"] = B.set_desc(n_heads=H, head_dim=dh, groups=s.groups, r_k=s.r_k, r_v=s.r_v,
+                           loop_first=s.loop_first, loop_last=s.loop_last, page_size=P,
+                           rope_baked=w.rope_baked, rope_base=w.rope_base,
+                           dtype=B.LLA_BF16 if w.dtype == "bf16" else B.LLA_F32)
+    return c
+
+
+def run(c, entry):
+    w = c["w"]
+    ring0 = (c["rk"].clone(), c["rv"].clone())
+    out = torch.full(tuple(c["q"].shape), float("nan"), dtype=c["q"].dtype, device="cuda")
+    ws = torch.empty(B.lla_decode_workspace_bytes(c["desc"], c["batch"], c["i"], w.window), dtype=torch.uint8,
+                     device="cuda")
+    args = B.decode_args(loop=c["loop"], window=w.window, pos=c["pos"], q=c["q"], k_cur=c["kc"], v_cur=c["vc"],
+                         ring_k=c["rk"], ring_v=c["rv"], A=c["A"], B=c["Bv"], out=out, workspace=ws,
+                         max_pos_hint=c["i"])
+    fn = {"hla": B.hla_decode_windowed, "absorbed": B.lla_decode_absorbed,
+          "reconstruct": B.lla_decode_reconstruct}[entry]
+    print(f"[case] full-size {w.name} entry={entry} loop={c['loop']} B={c['batch']}", flush=True)
+    fn(c["desc"], B.store(c["pages"], torch.from_numpy(c["bt"]).cuda()), c["batch"], args)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy(), ring0
+
+
+def oracle_for(c, seqs, form, ring0):
+    """The oracle on the sampled sequences: their pages are copied to the host
+    (re-indexed: sequence k's pages become 0..pps-1 of a compact array)."""
+    w, s = c["w"], c["s"]
+    P = w.page_size
+    kw = dict(groups=s.groups, page_size=P, r_k=s.r_k, r_v=s.r_v)
+    n_lat = max(0, c["i"] - w.window)
+    sK, sV = [], []
+    for b in seqs:
+        phys = torch.from_numpy(c["bt"][b].astype(np.int64)).cuda()
+        sub = c["pages"].index_select(0, phys).double().cpu().numpy()
+        k, v = O.gather_latents(sub, np.arange(len(phys))[None], 0, n_lat, **kw)
+        sK.append(k)
+        sV.append(v)
+    idx = torch.tensor(seqs, device="cuda")
+    f = lambda t: t.index_select(0, idx).double().cpu().numpy()
+    fn = O.textbook_decode if form == "textbook" else O.absorbed_decode
+    return fn(sK, sV, [c["i"]] * len(seqs), f(c["q"]), f(c["kc"]), f(c["vc"]), f(ring0[0]), f(ring0[1]),
+              c["A"].double().cpu().numpy(), c["Bv"].double().cpu().numpy(), window=w.window,
+              rope_base=w.rope_base)
+
+
+@pytest.mark.parametrize("key, set_key, loop", [(3, 1, 3), (3, 0, 1), (4, 1, 2)])
+def test_hla_full_size(key, set_key, loop):
+    w = configs.get(key)
+    c = build(w, set_key, loop, seed=key * 7 + loop)
+    out, ring0 = run(c, "hla")
+    seqs = [0, w.batch // 3, w.batch - 1]
+    ref = oracle_for(c, seqs, "absorbed", ring0)
+    err = max_rel_err(out[seqs], ref)
+    print(f"max_rel_err={err:.3e}")
+    assert err < 2e-2
+    assert np.all(np.isfinite(out))
+
+
+def test_lla_per_head_reconstruct_full_size():
+    w = configs.get(2)
+    c = build(w, 0, 2, seed=21)
+    out, ring0 = run(c, "reconstruct")
+    seqs = [0, 17, 31]
+    err = max_rel_err(out[seqs], oracle_for(c, seqs, "textbook", ring0))
+    print(f"max_rel_err={err:.3e}")
+    assert err < 2e-2
+    assert np.all(np.isfinite(out))
+
+
+def test_lla_per_head_absorbed_full_size():
+    w = configs.get(2)
+    c = build(w, 0, 4, seed=22)
+    out, ring0 = run(c, "absorbed")
+    seqs = [3, 30]
+    err = max_rel_err(out[seqs], oracle_for(c, seqs, "absorbed", ring0))
+    assert err < 2e-2
+
+
+@pytest.mark.parametrize("entry, form", [("reconstruct", "textbook"), ("absorbed", "absorbed")])
+def test_lla2d_full_width(entry, form):
+    """LLA-2D: 55 heads x 96 from one 5280-wide K and V latent, 4k context."""
+    w = configs.get(5)
+    c = build(w, 0, 17, batch=2, seed=51)
+    out, ring0 = run(c, entry)
+    err = max_rel_err(out, oracle_for(c, [0, 1], form, ring0))
+    print(f"max_rel_err={err:.3e}")
+    assert err < 2e-2
