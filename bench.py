@@ -320,6 +320,9 @@ def main():
     if st.entry_name == "reconstruct" and w.dtype == "bf16" and s_main.groups == w.heads and \
             s_main.r_k == s_main.r_v and s_main.r_k in (32, 64) and w.head_dim in (64, 128):
         kname = "k_scan_reconstruct_mfma"
+    elif st.entry_name == "reconstruct" and w.dtype == "bf16" and s_main.groups == 1 and \
+            s_main.r_k == s_main.r_v and s_main.r_k % 32 == 0 and w.head_dim in (64, 96, 128):
+        kname = "k_scan_reconstruct_gemm"
     reconstruct_mfma_bound = st.entry_name == "reconstruct" and scan_flop / scan_bytes > 312
     if reconstruct_mfma_bound:
         roof = {"bound": "mfma", "achieved": scan_flop / (scan_ms * 1e-3) / 1e12, "peak": 2500.0,

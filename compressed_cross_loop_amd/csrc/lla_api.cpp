@@ -56,15 +56,16 @@ struct Plan {
 // Latent tokens of the longest sequence are cut into S contiguous ranges of
 // `chunk` tokens (a multiple of 64); `wgs` workgroups work on each
 // (sequence, range).  S aims at kTargetWorkgroups in flight.
-Plan make_plan(int batch, int max_pos, int window, int splits, int wgs, int target = kTargetWorkgroups) {
+Plan make_plan(int batch, int max_pos, int window, int splits, int wgs, int target = kTargetWorkgroups,
+               int gran = kChunk) {
   const int64_t n_lat = std::max<int64_t>(0, (int64_t)max_pos - window);
-  const int64_t tiles = std::max<int64_t>(1, (n_lat + kChunk - 1) / kChunk);
+  const int64_t tiles = std::max<int64_t>(1, (n_lat + gran - 1) / gran);
   int64_t S = splits > 0 ? splits
                          : (target + (int64_t)batch * wgs - 1) / ((int64_t)batch * wgs);
   S = std::min<int64_t>(std::max<int64_t>(S, 1), tiles);
   const int64_t per = (tiles + S - 1) / S;
   S = (tiles + per - 1) / per;
-  return Plan{(int)S, (int)(per * kChunk)};
+  return Plan{(int)S, (int)(per * gran)};
 }
 
 bool use_mfma_scan(const lla_set_desc& d, int flags) {
@@ -90,17 +91,32 @@ bool use_mfma_reconstruct(const lla_set_desc& d, int flags) {
   return scan_reconstruct_mfma_supports(p);
 }
 
+bool use_gemm_reconstruct(const lla_set_desc& d, int flags) {
+  if (flags & LLA_FLAG_GENERIC) return false;
+  DecodeParams p{};
+  p.G = d.groups;
+  p.rk = d.r_k;
+  p.rv = d.r_v;
+  p.dh = d.head_dim;
+  p.bf16 = d.dtype == LLA_BF16;
+  return scan_reconstruct_gemm_supports(p);
+}
+
 Plan plan_for(const lla_set_desc& d, int batch, int max_pos, int window, int splits, int entry,
               int flags) {
   const bool absorbed = entry != 0;
   int wgs = d.n_heads;                                  // general kernels: one per head
   int target = kTargetWorkgroups;
   if (absorbed && use_mfma_scan(d, flags)) wgs = d.groups;
+  int gran = kChunk;
   if (!absorbed && use_mfma_reconstruct(d, flags)) {
     wgs = (d.n_heads + 3) / 4;
     target = 2 * kTargetWorkgroups;   // small workgroups: two resident per CU
+  } else if (!absorbed && use_gemm_reconstruct(d, flags)) {
+    wgs = (d.n_heads + 1) / 2;          // two heads per workgroup
+    gran = scan_reconstruct_gemm_tile();
   }
-  return make_plan(batch, max_pos, window, splits, wgs, target);
+  return make_plan(batch, max_pos, window, splits, wgs, target, gran);
 }
 
 struct WsLayout {
@@ -127,13 +143,20 @@ WsLayout ws_layout(const lla_set_desc& d, int B, int S, int WS, int Dp) {
   return w;
 }
 
+// width of a latent-scan partial row: latent space (r_v) for the absorbed
+// read, head space (d_h) when keys and values are rebuilt
+int partial_width(const lla_set_desc& d, int entry) { return entry ? d.r_v : d.head_dim; }
+
 size_t decode_ws_bytes(const lla_set_desc& d, int batch, int max_pos, int window, int splits) {
   // enough for every entry point and kernel family at these sizes
-  int S = 1;
+  size_t best = 0;
   for (int entry = 0; entry < 2; ++entry)
-    for (int flags = 0; flags < 2; ++flags)
-      S = std::max(S, plan_for(d, batch, max_pos, window, splits, entry, flags).S);
-  return ws_layout(d, batch, S, std::max(S, window_slices(window)), std::max(d.r_v, d.head_dim)).total;
+    for (int flags = 0; flags < 2; ++flags) {
+      const int S = plan_for(d, batch, max_pos, window, splits, entry, flags).S;
+      best = std::max(best, ws_layout(d, batch, S, std::max(S, window_slices(window)),
+                                      partial_width(d, entry)).total);
+    }
+  return best;
 }
 
 lla_status hip_status(hipError_t e) { return e == hipSuccess ? LLA_OK : LLA_ERR_HIP; }
@@ -161,7 +184,7 @@ lla_status decode(const lla_set_desc* d, const lla_store* st, int32_t batch,
   const bool absorbed = entry != 0;
   const bool generic = (a->flags & LLA_FLAG_GENERIC) != 0;
   const Plan plan = plan_for(*d, batch, a->max_pos_hint, a->window, a->splits, absorbed ? 1 : 0, a->flags);
-  const int Dp = std::max(d->r_v, d->head_dim);
+  const int Dp = partial_width(*d, absorbed ? 1 : 0);
   const int WSmax = window_slices(a->window);
   const WsLayout w = ws_layout(*d, batch, plan.S, std::max(plan.S, WSmax), Dp);
   char* ws = static_cast<char*>(a->workspace);
@@ -203,9 +226,14 @@ lla_status decode(const lla_set_desc* d, const lla_store* st, int32_t batch,
   hipEvent_t* ev = static_cast<hipEvent_t*>(a->scan_events);
   if (e == hipSuccess && ev) e = hipEventRecord(ev[0], s);
   if (e == hipSuccess) {
-    if (!absorbed)
-      e = (!generic && scan_reconstruct_mfma_supports(p)) ? launch_scan_reconstruct_mfma(p, s)
-                                                          : launch_scan_reconstruct_generic(p, s);
+    if (!absorbed) {
+      if (!generic && scan_reconstruct_mfma_supports(p))
+        e = launch_scan_reconstruct_mfma(p, s);
+      else if (!generic && scan_reconstruct_gemm_supports(p))
+        e = launch_scan_reconstruct_gemm(p, s);
+      else
+        e = launch_scan_reconstruct_generic(p, s);
+    }
     else if (mfma_scan)
       e = launch_scan_absorbed_mfma(p, s);
     else

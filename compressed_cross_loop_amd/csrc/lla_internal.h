@@ -75,6 +75,10 @@ hipError_t launch_scan_absorbed_mfma(const DecodeParams& p, hipStream_t s);
 bool scan_reconstruct_mfma_supports(const DecodeParams& p);
 hipError_t launch_scan_reconstruct_mfma(const DecodeParams& p, hipStream_t s);
 
+bool scan_reconstruct_gemm_supports(const DecodeParams& p);
+int scan_reconstruct_gemm_tile();
+hipError_t launch_scan_reconstruct_gemm(const DecodeParams& p, hipStream_t s);
+
 bool qmap_mfma_supports(const DecodeParams& p);
 hipError_t launch_qmap_mfma(const DecodeParams& p, bool want_qlat, hipStream_t s);
 bool window_fast_supports(const DecodeParams& p);

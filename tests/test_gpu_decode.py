@@ -155,3 +155,15 @@ def test_reconstruct_shared_latent_bf16():
                           loop_last=8, latent_std=1.0, exact_std=1.0, paired=False,
                           map_scale=np.sqrt(192 / 96))
     check(poison_unread(c), "absorbed", "absorbed")
+
+
+@pytest.mark.parametrize("H, d_h, r", [(5, 96, 192), (4, 128, 256), (3, 64, 96), (2, 96, 5280)])
+@pytest.mark.parametrize("splits", [0, 2])
+def test_reconstruct_shared_latent_shapes(H, d_h, r, splits):
+    """Head-folded reconstruct (one latent shared by all heads): odd head
+    counts, ragged 128-token tiles, an exact window, forced splits."""
+    c = gen.decode_inputs(460 + H + r + splits, batch=3, heads=H, head_dim=d_h, groups=1, r_k=r, r_v=r,
+                          positions=(300, 129, 7), window=4, dtype="bf16", loop=3, loop_first=1,
+                          loop_last=8, latent_std=1.0, exact_std=1.0, paired=False,
+                          map_scale=float(np.sqrt(r / d_h)))
+    check(poison_unread(c), "reconstruct", "textbook", splits=splits)
