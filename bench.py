@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--entry", choices=["auto", "hla", "absorbed", "reconstruct"], default="auto",
                     help="decode entry point (auto: hla for HLA workloads, reconstruct for LLA ones)")
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = workload's)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="launch every kernel eagerly instead of replaying the step as one HIP graph")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run one device-to-device copy of BYTES (HBM counter calibration)")
     return ap.parse_args()
@@ -286,13 +288,27 @@ def main():
         w = w.with_(layers=a.layers)
     st = DecodeStep(w, splits=a.splits, entry=a.entry)
     stream = torch.cuda.current_stream().cuda_stream
-    for _ in range(a.warmup):
+    for _ in range(max(1, a.warmup)):
         st.step()
     torch.cuda.synchronize()
+    run_step = st.step
+    if not a.no_graph:
+        # the whole step (every decode call and latent write) as one HIP graph:
+        # the library allocates, clears and synchronises nothing, so its
+        # launches capture as they are
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            st.step()
+        torch.cuda.synchronize()
+        run_step = graph.replay
+        for _ in range(max(1, a.warmup)):
+            run_step()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream().cuda_stream
     e0, e1 = hip.event(), hip.event()
     hip.record(e0, stream)
     for _ in range(a.steps):
-        st.step()
+        run_step()
     hip.record(e1, stream)
     torch.cuda.synchronize()
     ms = hip.elapsed_ms(e0, e1) / a.steps
@@ -345,7 +361,7 @@ def main():
                    "head_dim": w.head_dim,
                    "sets": [dict(loops=[s.loop_first, s.loop_last], groups=s.groups, r_k=s.r_k,
                                  r_v=s.r_v) for s in w.sets],
-                   "splits": a.splits or "auto"},
+                   "splits": a.splits or "auto", "launch": "eager" if a.no_graph else "hip_graph"},
         "step_bytes": step_bytes, "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
         "roofline": roof,
     }
