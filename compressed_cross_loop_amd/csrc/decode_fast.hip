@@ -1,7 +1,7 @@
 // bf16 decode kernels around the latent scan, shaped for gfx950:
-//   k_qmap_mfma     q~ = s R~_i A_t^T q for a block of sequences and one
-//                   d_h-wide latent block, on the matrix cores; the latent
-//                   rotation pairs (f, f + d_h/2) sit in the same lane, so
+//   k_qmap_mfma     q~ = s R~_i A_t^T q for a block of sequences and 128
+//                   latent columns per wave, on the matrix cores; the latent
+//                   rotation pairs (f, f + d_h/2) land one lane swap apart, so
 //                   R~_i is applied in registers ("Hybrid Latent Attention"
 //                   summary, "Latent Reader" Eq. 3, "Rotary Embedding
 //                   Alignment")
@@ -11,7 +11,7 @@
 //                   contiguous [H][d_h] ring rows), per-head online softmax
 //   k_combine_mfma  merge of the latent and window partials of 16 sequences
 //                   and one head, then o = (B_t^T O_latent + O_window) / l
-//                   with the B_t^T product on the fp32 matrix cores
+//                   with the B_t^T product on the bf16 matrix cores
 #include "device_common.h"
 #include "lla_internal.h"
 
@@ -25,41 +25,49 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 
 // ------------------------------------------------------------------ q map
-// grid (H, r_k / NB, ceil(B / 16)); NB = latent columns per workgroup (d_h
-// when rotary, so a block holds both members of every pair).  The A^(h)
-// block is stored transposed in LDS ([n][e], 8 consecutive e per 16 bytes)
-// so each B fragment is one ds_read_b128; the 16 sequences' rotation angles
-// are tabulated once per workgroup.
-template <int DH, int NB>
+// grid (H, ceil(r_k / 512), ceil(B / 16)); wave w of a workgroup produces the
+// 128 latent columns n0 = 128 (4 blockIdx.y + w) .. n0 + 127 of q~ for 16
+// sequences.  q~[b][n] = sum_e q[b][e] A[e][n] runs on
+// v_mfma_f32_16x16x32_bf16, which wants 8 consecutive e per lane while rows
+// of A^(h) are contiguous along n: each lane loads 8 rows x 8 columns
+// (columns n0 + 8c .. n0 + 8c + 7, c = lane % 16) and regroups them in
+// registers, so product j yields the columns {n0 + 8c + j}.  With rotary the
+// partner column n +- d_h/2 of a pair then sits in lane c ^ (d_h / 16) of the
+// same product, one lane swap away.  The sequences' rotation angles are
+// tabulated once per workgroup.
+template <int DH>
 __global__ __launch_bounds__(kThreads) void k_qmap_mfma(DecodeParams p, int want_qlat) {
-  __shared__ __attribute__((aligned(16))) bf16 AtT[NB][DH + 8];
-  __shared__ float csn[16][DH / 2][2];
+  constexpr int KS = DH / 32;
+  __shared__ __attribute__((aligned(16))) float csn[16][DH / 2][2];   // (cos, sin)
   __shared__ double theta[DH / 2];
   __shared__ int posb[16];
-  const int h = blockIdx.x, blk = blockIdx.y, b0 = blockIdx.z * 16;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = blockIdx.x, b0 = blockIdx.z * 16;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
   const int H = p.H, rk = p.rk;
   const bool rope = p.rope_base != 0.f;
   const bf16* q = static_cast<const bf16*>(p.q);
+  const int n0 = (blockIdx.y * 4 + wave) * 128;
+  const bool active = want_qlat && n0 < rk;   // uniform over the wave
+  const int ncol = n0 + 8 * col;
 
-  // issue the A^(h) block loads first: 16-byte rows of 8 consecutive columns
-  const bf16* Ah = static_cast<const bf16*>(p.A) + (int64_t)h * DH * rk + (int64_t)blk * NB;
-  constexpr int NL = (DH * NB / 8 + kThreads - 1) / kThreads;
-  bf16x8 av[NL];
+  // A^(h) rows e = 32 st + 8 grp + i, columns ncol .. ncol + 7 (clamped into
+  // the row; lanes past r_k store nothing)
+  bf16x8 araw[KS][8];
+  if (active) {
+    const bf16* Ah = static_cast<const bf16*>(p.A) + (int64_t)h * DH * rk + min(ncol, rk - 8);
 #pragma unroll
-  for (int u = 0; u < NL; ++u) {
-    const int x = tid + u * kThreads;
-    if (x < DH * NB / 8) {
-      const int e = x / (NB / 8), n8 = (x % (NB / 8)) * 8;
-      av[u] = *reinterpret_cast<const bf16x8*>(Ah + (int64_t)e * rk + n8);
-    }
+    for (int st = 0; st < KS; ++st)
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        araw[st][i] = *reinterpret_cast<const bf16x8*>(Ah + (int64_t)(32 * st + 8 * grp + i) * rk);
   }
-  // A operand (q rows of the 16 sequences), requested together with A
+  // A operand: q row of sequence b0 + col, dims 32 st + 8 grp ..
   const int brow = b0 + col;
-  bf16x8 aq[DH / 32];
+  bf16x8 aq[KS];
 #pragma unroll
-  for (int st = 0; st < DH / 32; ++st) {
+  for (int st = 0; st < KS; ++st) {
     if (brow < p.B) {
       aq[st] = *reinterpret_cast<const bf16x8*>(q + ((int64_t)brow * H + h) * DH + st * 32 + grp * 8);
     } else {
@@ -80,7 +88,7 @@ __global__ __launch_bounds__(kThreads) void k_qmap_mfma(DecodeParams p, int want
     }
   }
   // q' = s R_i q (head space, fp32) when a later kernel reads it
-  if (blk == 0 && p.need_qhead) {
+  if (blockIdx.y == 0 && p.need_qhead) {
     for (int x = tid; x < 16 * (DH / 2); x += kThreads) {
       const int bl = x / (DH / 2), f = x % (DH / 2), bb = b0 + bl;
       if (bb >= p.B) continue;
@@ -93,53 +101,51 @@ __global__ __launch_bounds__(kThreads) void k_qmap_mfma(DecodeParams p, int want
       qh[f + DH / 2] = p.scale * (a * sn + b * c);
     }
   }
-#pragma unroll
-  for (int u = 0; u < NL; ++u) {
-    const int x = tid + u * kThreads;
-    if (x < DH * NB / 8) {
-      const int e = x / (NB / 8), n8 = (x % (NB / 8)) * 8;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) AtT[n8 + k][e] = av[u][k];
-    }
-  }
   __syncthreads();
-  if (!want_qlat) return;
+  if (!active) return;
 
-  constexpr int NT = NB / 16;       // column tiles
-  constexpr int HT = DH / 32;       // tile distance of a rotary pair (rope: NB == DH)
-  auto tile = [&](int j) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[8];
 #pragma unroll
-    for (int st = 0; st < DH / 32; ++st) {
-      const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&AtT[j * 16 + col][st * 32 + grp * 8]);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[st], bv, acc, 0, 0, 0);
+  for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int st = 0; st < KS; ++st)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      bf16x8 bj;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) bj[i] = araw[st][i][j];
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[st], bj, acc[j], 0, 0, 0);
     }
-    return acc;   // lane: C[b0 + 4 grp + r][blk*NB + 16 j + col]
-  };
+  // lane: C[b0 + 4 grp + r][ncol + j]
   bf16* ql = static_cast<bf16*>(p.qlat);
-  if (rope) {
-    if (wave < HT) {
-      const f32x4 lo = tile(wave), hi = tile(wave + HT);
-      const int f = wave * 16 + col;
+  const bool lo_half = (8 * col) % DH < DH / 2;   // n0 is a multiple of d_h
+  const int f0 = (8 * col) % (DH / 2);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int bl = 4 * grp + r, bb = b0 + bl;
-        if (bb >= p.B) continue;
-        const float c = csn[bl][f][0], sn = csn[bl][f][1];
-        bf16* qo = ql + ((int64_t)bb * H + h) * rk + (int64_t)blk * NB;
-        qo[f] = static_cast<bf16>((lo[r] * c - hi[r] * sn) * p.scale);
-        qo[f + DH / 2] = static_cast<bf16>((lo[r] * sn + hi[r] * c) * p.scale);
+  for (int r = 0; r < 4; ++r) {
+    const int bl = 4 * grp + r, bb = b0 + bl;
+    float v[8];
+    if (rope) {
+      const float4* cs = reinterpret_cast<const float4*>(&csn[bl][f0][0]);
+#pragma unroll
+      for (int j2 = 0; j2 < 4; ++j2) {
+        const float4 t = cs[j2];   // (cos, sin) of frequencies f0 + 2 j2, f0 + 2 j2 + 1
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int j = 2 * j2 + u;
+          const float c = u ? t.z : t.x, sn = u ? t.w : t.y;
+          const float mine = acc[j][r], other = __shfl_xor(mine, DH / 16);
+          v[j] = lo_half ? (mine * c - other * sn) : (other * sn + mine * c);
+        }
       }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = acc[j][r];
     }
-  } else {
-    for (int j = wave; j < NT; j += 4) {
-      const f32x4 v = tile(j);
+    if (bb < p.B && ncol < rk) {
+      bf16x8 o;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int bb = b0 + 4 * grp + r;
-        if (bb < p.B)
-          ql[((int64_t)bb * H + h) * rk + (int64_t)blk * NB + j * 16 + col] = static_cast<bf16>(v[r] * p.scale);
-      }
+      for (int j = 0; j < 8; ++j) o[j] = static_cast<bf16>(v[j] * p.scale);
+      *reinterpret_cast<bf16x8*>(ql + ((int64_t)bb * H + h) * rk + ncol) = o;
     }
   }
 }
@@ -272,26 +278,40 @@ __global__ __launch_bounds__(kThreads) void k_window_fast(DecodeParams p) {
 
 // ------------------------------------------------------------------ combine
 // grid (H, ceil(B / 16)); 4 waves; out[b][h] for 16 sequences, d_h = 128.
-// B_t^(h) (RV x 128 bf16) is requested in full at entry (RV/16 16-byte loads
-// per thread, one 16-row chunk per load) so its latency overlaps the merge;
-// each chunk then goes through LDS as fp32 to feed v_mfma_f32_16x16x4_f32.
+// The B_t^T product runs on v_mfma_f32_16x16x32_bf16, which wants 8
+// consecutive latent dims k per lane, while B_t rows are contiguous along
+// d_h.  Each lane therefore loads an 8 x 8 block of B_t (rows k0..k0+7,
+// columns 8c..8c+7, c = lane % 16) with eight 16-byte loads and regroups it
+// in registers: product j takes column 8c + j of every row, so output tile j
+// holds the columns {8c + j}.  Wave w takes the 32-row k steps w, w+4, ...;
+// all its loads are issued at entry so their latency overlaps the merge.  The
+// fp32 latent sums enter as bf16 hi + lo parts (two products), which keeps
+// the product at fp32-level accuracy.  The four waves' partial results are
+// summed through LDS and written as 16-byte rows.
 template <int RV>
 __global__ __launch_bounds__(kThreads) void k_combine_mfma(DecodeParams p) {
   constexpr int DH = 128;
-  constexpr int NC = RV / 16;
-  __shared__ float ob[16][RV + 1];     // latent-space sums
-  __shared__ float wo[16][DH];         // window sums
-  __shared__ float wl[16];             // 1 / l
-  __shared__ float bs[2][16][DH + 4];  // B_t chunk, double-buffered
+  constexpr int KS = RV / 32;              // k steps
+  constexpr int KW = (KS + 3) / 4;         // k steps per wave
+  __shared__ float ob[16][RV + 1];         // latent-space sums
+  __shared__ float wo[16][DH];             // window sums
+  __shared__ float wl[16];                 // 1 / l
+  __shared__ __attribute__((aligned(16))) float red[4][16][DH + 4];   // per-wave products
   const int H = p.H, S = p.S, WS = p.WS;
   const int h = blockIdx.x, b0 = blockIdx.y * 16, tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15, grp = lane >> 4;
   const bf16* Bh = static_cast<const bf16*>(p.Bm) + (int64_t)h * RV * DH;
-  const int brow = tid / 16, bcol = (tid % 16) * 8;
-  bf16x8 breg[NC];
+  bf16x8 braw[KW][8];
 #pragma unroll
-  for (int c = 0; c < NC; ++c)
-    breg[c] = *reinterpret_cast<const bf16x8*>(Bh + (int64_t)(16 * c + brow) * DH + bcol);
+  for (int u = 0; u < KW; ++u) {
+    const int st = wave + 4 * u;
+    if (st < KS) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        braw[u][i] = *reinterpret_cast<const bf16x8*>(Bh + (int64_t)(32 * st + 8 * grp + i) * DH + 8 * col);
+    }
+  }
 
   // (m, l) of every split and window slice of the 16 sequences: one load per
   // thread, all in flight together, then the per-sequence softmax merge
@@ -402,45 +422,65 @@ __global__ __launch_bounds__(kThreads) void k_combine_mfma(DecodeParams p) {
     }
   }
   __syncthreads();
-  // out[16 b x 128] = ob[16 x RV] . B^(h)[RV x 128]; wave w owns column tiles w and w+4
-  const int col = lane & 15, kq = lane >> 4;
-  f32x4 acc[2][2];
+  f32x4 acc[8];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) acc[u][0] = acc[u][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    const int buf = c & 1;
+  for (int u = 0; u < KW; ++u) {
+    const int st = wave + 4 * u;
+    if (st < KS) {
+      // A operand: row b = col of the latent sums, k = 32 st + 8 grp + i
+      bf16x8 ahi, alo;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) bs[buf][brow][bcol + k] = to_f(breg[c][k]);
-    __syncthreads();
+      for (int i = 0; i < 8; ++i) {
+        const float x = ob[col][32 * st + 8 * grp + i];
+        const bf16 hi = static_cast<bf16>(x);
+        ahi[i] = hi;
+        alo[i] = static_cast<bf16>(x - static_cast<float>(hi));
+      }
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const float a = ob[col][16 * c + 4 * kk + kq];
+      for (int j = 0; j < 8; ++j) {
+        bf16x8 bj;
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const float bv = bs[buf][4 * kk + kq][(wave + 4 * u) * 16 + col];
-        acc[u][kk & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bv, acc[u][kk & 1], 0, 0, 0);
+        for (int i = 0; i < 8; ++i) bj[i] = braw[u][i][j];
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bj, acc[j], 0, 0, 0);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, bj, acc[j], 0, 0, 0);
       }
     }
   }
-  bf16* out = static_cast<bf16*>(p.out);
+  // lane holds C[b = 4 grp + r][e = 8 col + j]
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int e = (wave + 4 * u) * 16 + col;
+  for (int r = 0; r < 4; ++r) {
+    float4* dst = reinterpret_cast<float4*>(&red[wave][4 * grp + r][8 * col]);
+    dst[0] = float4{acc[0][r], acc[1][r], acc[2][r], acc[3][r]};
+    dst[1] = float4{acc[4][r], acc[5][r], acc[6][r], acc[7][r]};
+  }
+  __syncthreads();
+  {
+    const int bl = tid / 16, e8 = (tid % 16) * 8, b = b0 + bl;
+    if (b < p.B) {
+      float v[8];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int bl = 4 * kq + r, b = b0 + bl;
-      if (b < p.B)
-        out[((int64_t)b * H + h) * DH + e] =
-            static_cast<bf16>((acc[u][0][r] + acc[u][1][r] + wo[bl][e]) * wl[bl]);
+      for (int k = 0; k < 8; ++k) v[k] = wo[bl][e8 + k];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float4 x0 = *reinterpret_cast<const float4*>(&red[w][bl][e8]);
+        const float4 x1 = *reinterpret_cast<const float4*>(&red[w][bl][e8 + 4]);
+        v[0] += x0.x; v[1] += x0.y; v[2] += x0.z; v[3] += x0.w;
+        v[4] += x1.x; v[5] += x1.y; v[6] += x1.z; v[7] += x1.w;
+      }
+      bf16x8 o;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) o[k] = static_cast<bf16>(v[k] * wl[bl]);
+      *reinterpret_cast<bf16x8*>(static_cast<bf16*>(p.out) + ((int64_t)b * H + h) * DH + e8) = o;
     }
   }
 }
 
-template <int DH, int NB>
+template <int DH>
 hipError_t qmap_launch(const DecodeParams& p, bool want, hipStream_t s) {
-  const dim3 grid(p.H, want ? p.rk / NB : 1, (p.B + 15) / 16);
-  hipLaunchKernelGGL((k_qmap_mfma<DH, NB>), grid, dim3(kThreads), 0, s, p, want ? 1 : 0);
+  const dim3 grid(p.H, want ? (p.rk + 511) / 512 : 1, (p.B + 15) / 16);
+  hipLaunchKernelGGL((k_qmap_mfma<DH>), grid, dim3(kThreads), 0, s, p, want ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -450,17 +490,12 @@ bool qmap_mfma_supports(const DecodeParams& p) {
   if (!p.bf16) return false;
   if (p.dh != 64 && p.dh != 128) return false;
   if (p.rope_base != 0.f) return p.rk % p.dh == 0;
-  return p.rk % p.dh == 0 || p.rk == 32;
+  return p.rk % 8 == 0;
 }
 
 hipError_t launch_qmap_mfma(const DecodeParams& p, bool want_qlat, hipStream_t s) {
   if (!qmap_mfma_supports(p)) return hipErrorNotSupported;
-  if (p.dh == 128) {
-    if (p.rk % 128 == 0) return qmap_launch<128, 128>(p, want_qlat, s);
-    return qmap_launch<128, 32>(p, want_qlat, s);
-  }
-  if (p.rk % 64 == 0) return qmap_launch<64, 64>(p, want_qlat, s);
-  return qmap_launch<64, 32>(p, want_qlat, s);
+  return p.dh == 128 ? qmap_launch<128>(p, want_qlat, s) : qmap_launch<64>(p, want_qlat, s);
 }
 
 bool window_fast_supports(const DecodeParams& p) {

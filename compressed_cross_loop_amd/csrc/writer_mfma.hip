@@ -22,10 +22,14 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
-constexpr int kTileM = 64;   // tokens per workgroup (16 per wave)
-constexpr int kTileN = 64;   // latent outputs per workgroup
-constexpr int kUnroll = 4;   // K steps whose loads are issued together
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTileM = 16 * kWaves;   // tokens per workgroup (16 per wave)
+constexpr int kTileN = 64;            // latent outputs per workgroup
+constexpr int kRound = 12;            // 32-wide K steps staged per round
+constexpr int kPieces = kTileN * kRound * 4;            // 16-byte pieces of an E round
+constexpr int kPiecesPerThread = kPieces / kThreads;    // 6
+constexpr int kReduceThreads = 256;
 
 __device__ __forceinline__ bf16x8 zero8() {
   bf16x8 z;
@@ -34,14 +38,22 @@ __device__ __forceinline__ bf16x8 zero8() {
   return z;
 }
 
+// grid (ceil(R / 64), ceil(M / 128), G * ksplit).  Each workgroup owns a
+// 128-token x 64-output tile and one contiguous K range of the concatenated
+// loops; per round of up to 12 K steps the 64 encoder rows' slice is staged
+// in LDS (shared by the eight waves) and each wave keeps its 16 tokens'
+// inputs for the whole round in registers.  All loads of a round are issued
+// before its first product.
 __global__ __launch_bounds__(kThreads) void k_writer_mfma(WriterParams p) {
+  __shared__ __attribute__((aligned(16))) bf16 es[kTileN][kRound * 32 + 8];
   const int nt = blockIdx.x, mt = blockIdx.y;
   const int g = blockIdx.z / p.ksplit, ks = blockIdx.z % p.ksplit;
   const int M = p.B * p.n_tok, R = p.R, d_in = p.d_in, G = p.G;
   const int ksteps = p.n_loops * d_in / 32;
   const int per = (ksteps + p.ksplit - 1) / p.ksplit;
-  const int s0 = ks * per, s1 = min(ksteps, s0 + per);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int s0 = min(ksteps, ks * per), s1 = min(ksteps, s0 + per);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
   const int m = mt * kTileM + wave * 16 + col;       // A-operand row (token)
   const bool m_ok = m < M;
@@ -50,39 +62,55 @@ __global__ __launch_bounds__(kThreads) void k_writer_mfma(WriterParams p) {
   f32x4 acc[kTileN / 16];
 #pragma unroll
   for (int j = 0; j < kTileN / 16; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  bool n_ok[kTileN / 16];
-#pragma unroll
-  for (int j = 0; j < kTileN / 16; ++j) n_ok[j] = nt * kTileN + 16 * j + col < R;
 
-  for (int st = s0; st < s1; st += kUnroll) {
-    bf16x8 a[kUnroll], bb[kUnroll][kTileN / 16];
+  for (int r0 = s0; r0 < s1; r0 += kRound) {
+    const int ns = min(kRound, s1 - r0);
+    // this thread's pieces of the E slice: (row, step, 8-wide sub-block)
+    bf16x8 ev[kPiecesPerThread];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int k0 = (st + u) * 32;
-      const bool ok = st + u < s1;
+    for (int u = 0; u < kPiecesPerThread; ++u) {
+      const int xq = tid + u * kThreads;
+      const int row = xq / (kRound * 4), st = (xq % (kRound * 4)) / 4, sub = xq % 4;
+      const int n = nt * kTileN + row;
+      const int k0 = (r0 + st) * 32;
+      const int t = k0 / d_in, kk = k0 % d_in + sub * 8;
+      ev[u] = (st < ns && n < R)
+                  ? *reinterpret_cast<const bf16x8*>(enc + (((int64_t)t * G + g) * R + n) * d_in + kk)
+                  : zero8();
+    }
+    bf16x8 a[kRound];
+#pragma unroll
+    for (int st = 0; st < kRound; ++st) {
+      const int k0 = (r0 + st) * 32;
       const int t = k0 / d_in, kk = k0 % d_in + grp * 8;
-      a[u] = (ok && m_ok) ? *reinterpret_cast<const bf16x8*>(
-                                x + (((int64_t)m * p.n_loops + t) * G + g) * d_in + kk)
-                          : zero8();
+      a[st] = (st < ns && m_ok) ? *reinterpret_cast<const bf16x8*>(
+                                      x + (((int64_t)m * p.n_loops + t) * G + g) * d_in + kk)
+                                : zero8();
+    }
+    __syncthreads();   // the previous round's reads of es are done
 #pragma unroll
-      for (int j = 0; j < kTileN / 16; ++j) {
-        const int n = nt * kTileN + 16 * j + col;
-        bb[u][j] = (ok && n_ok[j]) ? *reinterpret_cast<const bf16x8*>(
-                                         enc + (((int64_t)t * G + g) * R + n) * d_in + kk)
-                                   : zero8();
+    for (int u = 0; u < kPiecesPerThread; ++u) {
+      const int xq = tid + u * kThreads;
+      const int row = xq / (kRound * 4), st = (xq % (kRound * 4)) / 4, sub = xq % 4;
+      *reinterpret_cast<bf16x8*>(&es[row][st * 32 + sub * 8]) = ev[u];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int st = 0; st < kRound; ++st) {
+      if (st < ns) {
+#pragma unroll
+        for (int j = 0; j < kTileN / 16; ++j) {
+          const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&es[16 * j + col][st * 32 + grp * 8]);
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[st], bv, acc[j], 0, 0, 0);
+        }
       }
     }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
-#pragma unroll
-      for (int j = 0; j < kTileN / 16; ++j)
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], bb[u][j], acc[j], 0, 0, 0);
   }
   // lane holds C[row 4*grp + r][col] of each 16x16 tile
 #pragma unroll
   for (int j = 0; j < kTileN / 16; ++j) {
     const int n = nt * kTileN + 16 * j + col;
-    if (!n_ok[j]) continue;
+    if (n >= R) continue;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int mm = mt * kTileM + wave * 16 + 4 * grp + r;
@@ -91,43 +119,59 @@ __global__ __launch_bounds__(kThreads) void k_writer_mfma(WriterParams p) {
   }
 }
 
-// Sum the K-split partials of one (token, group), then rotate/round/scatter.
-__global__ __launch_bounds__(kThreads) void k_writer_reduce(WriterParams p) {
+// Sum the K-split partials of one (token, group) in split order, then
+// rotate the key part by R~_p (baked sets), round to bf16 and scatter into
+// the paged store.  The partial sums are read as float4 rows, eight splits'
+// loads in flight at a time; the rotation angles come from a per-token table.
+__global__ __launch_bounds__(kReduceThreads) void k_writer_reduce(WriterParams p) {
   extern __shared__ float c[];
-  __shared__ double theta[128];     // d_h / 2 <= 128
-  const int m = blockIdx.x, g = blockIdx.y;
-  if (p.rope_baked && (int)threadIdx.x < p.dh / 2) theta[threadIdx.x] = rope_theta(p.rope_base, p.dh, threadIdx.x);
-  const int M = p.B * p.n_tok, R = p.R, G = p.G;
-  for (int o = threadIdx.x; o < R; o += kThreads) {
-    float v = 0.f;
-    for (int ks = 0; ks < p.ksplit; ++ks) v += p.acc[(((int64_t)ks * M + m) * G + g) * R + o];
-    c[o] = v;
+  __shared__ float csn[128][2];     // d_h / 2 <= 128
+  const int m = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
+  const int M = p.B * p.n_tok, R = p.R, G = p.G, KS = p.ksplit;
+  const int b = m / p.n_tok, n = m % p.n_tok;
+  const int pos = p.pos[(int64_t)b * p.n_tok + n];
+  if (p.rope_baked && tid < p.dh / 2) {
+    float cs, sn;
+    rope_cs(p.rope_base, p.dh, tid, pos, cs, sn);
+    csn[tid][0] = cs;
+    csn[tid][1] = sn;
+  }
+  const float* src = p.acc + ((int64_t)m * G + g) * R;
+  const int64_t kstride = (int64_t)M * G * R;
+  for (int u = tid; u < R / 4; u += kReduceThreads) {
+    f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < KS; k0 += 8) {
+      float4 v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        v[q] = reinterpret_cast<const float4*>(src + min(k0 + q, KS - 1) * kstride)[u];
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (k0 + q < KS) sum += f32x4{v[q].x, v[q].y, v[q].z, v[q].w};
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) c[4 * u + e] = sum[e];
   }
   __syncthreads();
-  const int b = m / p.n_tok, n = m % p.n_tok;
-  const int R_ = R, rk = p.rk, dh = p.dh, half = dh / 2;
-  const int pos = p.pos[(int64_t)b * p.n_tok + n];
+  const int rk = p.rk, dh = p.dh, half = dh / 2;
   const int64_t page = p.bt[(int64_t)b * p.max_pages + pos / p.P];
   const int slot = pos % p.P;
   bf16* pages = static_cast<bf16*>(p.pages);
-  for (int o = threadIdx.x; o < R_; o += kThreads) {
+  for (int o = tid; o < R; o += kReduceThreads) {
     float v = c[o];
     int64_t off;
     if (o < rk) {
       if (p.rope_baked) {
         const int f = o % dh;
-        float cs, sn;
         if (f < half) {
-          rope_cs_theta(theta[f], pos, cs, sn);
-          v = c[o] * cs - c[o + half] * sn;
+          v = c[o] * csn[f][0] - c[o + half] * csn[f][1];
         } else {
-          rope_cs_theta(theta[f - half], pos, cs, sn);
-          v = c[o - half] * sn + c[o] * cs;
+          v = c[o - half] * csn[f - half][1] + c[o] * csn[f - half][0];
         }
       }
-      off = key_off(page, g, slot, o, G, p.P, R_, rk);
+      off = key_off(page, g, slot, o, G, p.P, R, rk);
     } else {
-      off = val_off(page, g, slot, o - rk, G, p.P, R_, rk);
+      off = val_off(page, g, slot, o - rk, G, p.P, R, rk);
     }
     pages[off] = static_cast<bf16>(v);
   }
@@ -140,8 +184,9 @@ bool writer_mfma_supports(const WriterParams& p) { return p.bf16 && p.d_in % 32 
 int writer_mfma_ksplit(int M, int G, int R, int n_loops, int d_in) {
   const int64_t tiles = (int64_t)((R + kTileN - 1) / kTileN) * ((M + kTileM - 1) / kTileM) * G;
   const int ksteps = n_loops * d_in / 32;
-  int64_t ks = (512 + tiles - 1) / tiles;
-  ks = std::min<int64_t>(ks, std::max(1, ksteps / 8));
+  int64_t ks = (256 + tiles - 1) / tiles;                       // about one workgroup per CU
+  ks = std::min<int64_t>(ks, std::max(1, ksteps / 8));          // at least 8 K steps each
+  ks = std::max<int64_t>(ks, (ksteps + 32 * kRound - 1) / (32 * kRound));   // at most 32 rounds each
   return (int)std::max<int64_t>(ks, 1);
 }
 
@@ -152,7 +197,7 @@ hipError_t launch_writer_mfma(const WriterParams& p, hipStream_t s) {
   hipLaunchKernelGGL(k_writer_mfma, grid, dim3(kThreads), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_writer_reduce, dim3(M, p.G), dim3(kThreads), (size_t)p.R * sizeof(float), s, p);
+  hipLaunchKernelGGL(k_writer_reduce, dim3(M, p.G), dim3(kReduceThreads), (size_t)p.R * sizeof(float), s, p);
   return hipGetLastError();
 }
 

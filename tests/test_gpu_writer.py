@@ -125,3 +125,29 @@ def test_writer_then_decode_end_to_end():
     ref_t = O.textbook_decode(sK, sV, dc.pos.numpy(), *f, window=W, rope_base=base)
     assert max_rel_err(ref, ref_t) < 1e-10
     assert max_rel_err(out.float().cpu().numpy(), ref) < TOL["bf16"]
+
+
+@pytest.mark.parametrize("case", [
+    # decode shape of the main HLA set: 128 tokens, 3 loops x 2048 -> 512 + 512, 16 K splits
+    dict(batch=128, n_tok=1, n_loops=3, groups=1, r_k=512, r_v=512, d_in=2048, rope_base=10000.0,
+         rope_baked=1, head_dim=128, positions="decode"),
+    # 150 tokens (second 128-token tile ragged), R = 80 (64-wide output tile ragged), 2 groups
+    dict(batch=3, n_tok=50, n_loops=2, groups=2, r_k=48, r_v=32, d_in=64, head_dim=64,
+         positions="prefix"),
+    # 256 output tiles -> one K split of 16 steps: two rounds, the second ragged
+    dict(batch=1, n_tok=2, n_loops=1, groups=1, r_k=8192, r_v=8192, d_in=512, rope_base=500.0,
+         rope_baked=1, head_dim=128, positions="prefix"),
+    # tiny output, long K: 64 K splits, summed in eight batches of eight
+    dict(batch=2, n_tok=1, n_loops=4, groups=1, r_k=32, r_v=32, d_in=4096, head_dim=64,
+         positions="decode"),
+], ids=["hla-decode-b128", "ragged-m-and-n", "two-rounds", "many-splits"])
+def test_writer_bf16_shapes(case):
+    case = dict(case)
+    kind = case.pop("positions")
+    Bsz, n_tok = case["batch"], case["n_tok"]
+    if kind == "decode":
+        positions = gen.rng(11, 1).integers(0, 4096, size=(Bsz, 1))
+    else:
+        positions = np.tile(np.arange(n_tok), (Bsz, 1)) + 7 * np.arange(Bsz)[:, None]
+    got, want = run_writer(dtype="bf16", positions=positions, seed=12, **case)
+    assert max_rel_err(got, want) < TOL["bf16"]
