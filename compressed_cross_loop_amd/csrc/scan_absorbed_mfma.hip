@@ -22,8 +22,9 @@
 // With fuse_window set, split s also handles slice s of the exact window
 // (window_slice below), so those bytes stream in the same launch.
 //
-// The tile loop is software-pipelined: keys two tiles ahead, values one.
-// q~ is read from LDS to leave registers for the deeper key pipeline.  At the end the
+// The tile loop is software-pipelined (keys two to four tiles ahead, values
+// one to four, by latent width).  q~ is read from LDS to leave registers for
+// the key pipeline.  At the end the
 // four waves are merged (same-max rescale, fixed order) in LDS and one
 // partial (m, l, O_latent) per head is written for the combine kernel.
 #include "device_common.h"
@@ -39,6 +40,14 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
+
+// Prefetch depth per latent width: narrow tiles carry few bytes, so they run
+// further ahead to keep enough of HBM's latency covered; r = 512 is limited
+// by registers.
+template <int RK> struct Pipe { static constexpr int keys = 4, values = 4, unroll = 4; };
+template <> struct Pipe<128> { static constexpr int keys = 4, values = 2, unroll = 4; };
+template <> struct Pipe<256> { static constexpr int keys = 3, values = 2, unroll = 6; };
+template <> struct Pipe<512> { static constexpr int keys = 2, values = 1, unroll = 2; };
 
 template <int RK>
 __device__ __forceinline__ void load_keys(bf16x8 (&k)[RK / 32], const bf16* tile, int col, int grp) {
@@ -178,7 +187,7 @@ __device__ void window_slice(const DecodeParams& p, int b, int slice, int g, con
   // batches of U ring tokens, double-buffered: batch n+1 is requested before
   // batch n is consumed.  Loads past the slice reread a valid slot, so every
   // refill is unconditional.
-  constexpr int U = 16;
+  constexpr int U = 8;
   auto slot_of = [&](int t) { return (j0 + min(t, max(nw - 1, 0))) % (W + 1); };
   auto load_batch = [&](bf16x8 (&kr)[U], bf16x8 (&vr)[U], int tb) {
 #pragma unroll
@@ -309,41 +318,35 @@ __global__ __launch_bounds__(kThreads, 1) void k_scan_absorbed_mfma(DecodeParams
   };
   auto tile_valid = [&](int ti) -> int { return min(16, t1 - (t0 + ti * 16)); };
 
-  // Keys run two tiles ahead, values one: tile n+2's keys are requested as
-  // soon as the score MFMAs have consumed tile n's, tile n+1's values as soon
-  // as tile n's value MFMAs are issued.  Refills are unconditional (clamped
-  // to the last tile, still cached) so no register set has to survive a
-  // skipped refill.
-  bf16x8 kA[RK / 32], kB[RK / 32];
-  s16x4 vv[RV / 16];
+  // Keys run NK tiles (of this wave) ahead, values NV: tile n+NK's keys are
+  // requested as soon as the score MFMAs have consumed tile n's, tile n+NV's
+  // values as soon as tile n's value MFMAs are issued.  The register sets
+  // rotate with the loop unrolled by lcm(NK, NV), so every index is static.
+  // Refills are unconditional (clamped to the last tile, still cached) so no
+  // register set has to survive a skipped refill.
+  constexpr int NK = Pipe<RK>::keys, NV = Pipe<RK>::values, UN = Pipe<RK>::unroll;
+  bf16x8 kb[NK][RK / 32];
+  s16x4 vb[NV][RV / 16];
   int ti = wave;
   if (ti < ntiles) {
-    const bf16* tp = tile_ptr(ti);
-    load_keys<RK>(kA, tp, col, grp);
-    load_values<RK, RV>(vv, tp, col, grp);
-    load_keys<RK>(kB, tile_ptr(min(ti + kWaves, ntiles - 1)), col, grp);
+#pragma unroll
+    for (int u = 0; u < NK; ++u) load_keys<RK>(kb[u], tile_ptr(min(ti + u * kWaves, ntiles - 1)), col, grp);
+#pragma unroll
+    for (int u = 0; u < NV; ++u)
+      load_values<RK, RV>(vb[u], tile_ptr(min(ti + u * kWaves, ntiles - 1)), col, grp);
   }
   while (ti < ntiles) {
-    {
-      const f32x4 sc = tile_scores<RK>(kA, qrow);
+#pragma unroll
+    for (int u = 0; u < UN; ++u) {
+      const f32x4 sc = tile_scores<RK>(kb[u % NK], qrow);
       __builtin_amdgcn_sched_barrier(0);   // keep each refill below its consumer
-      load_keys<RK>(kA, tile_ptr(min(ti + 2 * kWaves, ntiles - 1)), col, grp);
+      load_keys<RK>(kb[u % NK], tile_ptr(min(ti + NK * kWaves, ntiles - 1)), col, grp);
       const s16x4 pb = tile_softmax<RV>(sc, acc, m, lsum, tile_valid(ti), grp);
-      tile_values<RV>(vv, pb, acc, tile_valid(ti), grp);
+      tile_values<RV>(vb[u % NV], pb, acc, tile_valid(ti), grp);
       __builtin_amdgcn_sched_barrier(0);
-      load_values<RK, RV>(vv, tile_ptr(min(ti + kWaves, ntiles - 1)), col, grp);
+      load_values<RK, RV>(vb[u % NV], tile_ptr(min(ti + NV * kWaves, ntiles - 1)), col, grp);
       ti += kWaves;
-    }
-    if (ti >= ntiles) break;
-    {
-      const f32x4 sc = tile_scores<RK>(kB, qrow);
-      __builtin_amdgcn_sched_barrier(0);
-      load_keys<RK>(kB, tile_ptr(min(ti + 2 * kWaves, ntiles - 1)), col, grp);
-      const s16x4 pb = tile_softmax<RV>(sc, acc, m, lsum, tile_valid(ti), grp);
-      tile_values<RV>(vv, pb, acc, tile_valid(ti), grp);
-      __builtin_amdgcn_sched_barrier(0);
-      load_values<RK, RV>(vv, tile_ptr(min(ti + kWaves, ntiles - 1)), col, grp);
-      ti += kWaves;
+      if (ti >= ntiles) break;
     }
   }
   lsum += __shfl_xor(lsum, 16);

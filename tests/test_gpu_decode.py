@@ -87,6 +87,21 @@ def test_hla_pos_beyond_hint_and_split_determinism():
     assert np.array_equal(a, b)
 
 
+@pytest.mark.parametrize("r, d_h, H, G", [(64, 64, 4, 1), (128, 64, 8, 2), (128, 128, 6, 3), (32, 64, 6, 2)])
+@pytest.mark.parametrize("splits", [0, 3])
+def test_absorbed_bf16_widths_and_groups(r, d_h, H, G, splits):
+    """Matrix-core absorbed scan at the narrow latent widths (deeper prefetch
+    than r = 256 / 512) and with several heads per latent group."""
+    seed = 600 + r + d_h + H + G + splits
+    baked = r % d_h == 0   # rotary needs whole d_h blocks in the key latent
+    c = gen.decode_inputs(seed, batch=3, heads=H, head_dim=d_h, groups=G, r_k=r, r_v=r,
+                          positions=(613, 66, 9), window=5, dtype="bf16", page_size=64,
+                          rope_base=10000.0 if baked else 0.0, rope_baked=int(baked), loop=2,
+                          loop_first=1, loop_last=3, latent_std=np.sqrt(3.0), exact_std=np.sqrt(3.0),
+                          paired=baked)
+    check(poison_unread(c), "absorbed", "absorbed", splits=splits)
+
+
 def tiny_fp32_case(seed, set_key, loop):
     """Workload 1 shape: 2 heads x 64, fp32, N = 256, W = 16, RoPE off."""
     r = 32 if set_key == 0 else 128
