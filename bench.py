@@ -73,8 +73,7 @@ class Hip:
 
 
 # --------------------------------------------------------------------------- HLA
-ENTRY_KERNEL = {"hla": "k_scan_absorbed_mfma", "absorbed": "k_scan_absorbed_mfma",
-                "reconstruct": "k_scan_reconstruct_generic"}
+ENTRY_CODE = {"reconstruct": 0, "absorbed": 1, "hla": 2}
 
 
 class DecodeStep:
@@ -332,13 +331,8 @@ def main():
     s_main = w.sets[main_k]
     scan_bytes += w.batch * w.heads * s_main.r_k * (2 if w.dtype == "bf16" else 4) \
         if st.entry_name != "reconstruct" else 0
-    kname = ENTRY_KERNEL[st.entry_name]
-    if st.entry_name == "reconstruct" and w.dtype == "bf16" and s_main.groups == w.heads and \
-            s_main.r_k == s_main.r_v and s_main.r_k in (32, 64) and w.head_dim in (64, 128):
-        kname = "k_scan_reconstruct_mfma"
-    elif st.entry_name == "reconstruct" and w.dtype == "bf16" and s_main.groups == 1 and \
-            s_main.r_k == s_main.r_v and s_main.r_k % 32 == 0 and w.head_dim in (64, 96, 128):
-        kname = "k_scan_reconstruct_gemm"
+    main_desc = next(c[3] for c in st.calls if c[1] == main_k)
+    kname = st.B.lla_decode_scan_kernel(main_desc, ENTRY_CODE[st.entry_name])
     reconstruct_mfma_bound = st.entry_name == "reconstruct" and scan_flop / scan_bytes > 312
     if reconstruct_mfma_bound:
         roof = {"bound": "mfma", "achieved": scan_flop / (scan_ms * 1e-3) / 1e12, "peak": 2500.0,

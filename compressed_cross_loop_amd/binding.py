@@ -72,6 +72,8 @@ lib.lla_decode_workspace_bytes.argtypes = [_P(LlaSetDesc), ctypes.c_int32, ctype
 lib.lla_decode_plan_splits.restype = ctypes.c_int32
 lib.lla_decode_plan_splits.argtypes = [_P(LlaSetDesc), ctypes.c_int32, ctypes.c_int32,
                                        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+lib.lla_decode_scan_kernel.restype = ctypes.c_char_p
+lib.lla_decode_scan_kernel.argtypes = [_P(LlaSetDesc), ctypes.c_int32, ctypes.c_int32]
 lib.lla_bytes_per_token.restype = ctypes.c_size_t
 lib.lla_bytes_per_token.argtypes = [_P(LlaSetDesc)]
 lib.lla_status_string.restype = ctypes.c_char_p
@@ -143,6 +145,13 @@ def lla_decode_workspace_bytes(desc, batch, max_pos, window, splits=0):
 
 def lla_decode_plan_splits(desc, batch, max_pos, window, splits=0, entry=1):
     return lib.lla_decode_plan_splits(ctypes.byref(desc), batch, max_pos, window, splits, entry)
+
+
+def lla_decode_scan_kernel(desc, entry, flags=0):
+    """Latent-scan kernel family a decode call launches (entry 0 reconstruct,
+    1 absorbed, 2 HLA windowed); None on invalid arguments."""
+    r = lib.lla_decode_scan_kernel(ctypes.byref(desc), entry, flags)
+    return None if r is None else r.decode()
 
 
 def lla_write_latents(desc, st, *, pos, x, enc, workspace=None, stream=None):

@@ -102,6 +102,14 @@ bool use_gemm_reconstruct(const lla_set_desc& d, int flags) {
   return scan_reconstruct_gemm_supports(p);
 }
 
+// the latent-scan kernel family a decode call launches for this set
+const char* scan_kernel_name(const lla_set_desc& d, int absorbed, int flags) {
+  if (absorbed) return use_mfma_scan(d, flags) ? "k_scan_absorbed_mfma" : "k_scan_absorbed_generic";
+  if (use_mfma_reconstruct(d, flags)) return "k_scan_reconstruct_mfma";
+  if (use_gemm_reconstruct(d, flags)) return "k_scan_reconstruct_gemm";
+  return "k_scan_reconstruct_generic";
+}
+
 Plan plan_for(const lla_set_desc& d, int batch, int max_pos, int window, int splits, int entry,
               int flags) {
   const bool absorbed = entry != 0;
@@ -227,9 +235,9 @@ lla_status decode(const lla_set_desc* d, const lla_store* st, int32_t batch,
   if (e == hipSuccess && ev) e = hipEventRecord(ev[0], s);
   if (e == hipSuccess) {
     if (!absorbed) {
-      if (!generic && scan_reconstruct_mfma_supports(p))
+      if (use_mfma_reconstruct(*d, a->flags))
         e = launch_scan_reconstruct_mfma(p, s);
-      else if (!generic && scan_reconstruct_gemm_supports(p))
+      else if (use_gemm_reconstruct(*d, a->flags))
         e = launch_scan_reconstruct_gemm(p, s);
       else
         e = launch_scan_reconstruct_generic(p, s);
@@ -317,6 +325,11 @@ int32_t lla_decode_plan_splits(const lla_set_desc* desc, int32_t batch, int32_t 
                                int32_t window, int32_t splits, int32_t entry) {
   if (check_desc(desc) != LLA_OK || batch <= 0 || max_pos < 0 || window < 0 || splits < 0) return 0;
   return plan_for(*desc, batch, max_pos, window, splits, entry ? 1 : 0, 0).S;
+}
+
+const char* lla_decode_scan_kernel(const lla_set_desc* desc, int32_t entry, int32_t flags) {
+  if (check_desc(desc) != LLA_OK || entry < 0 || entry > 2 || (flags & ~LLA_FLAG_GENERIC)) return nullptr;
+  return scan_kernel_name(*desc, entry != 0, flags);
 }
 
 size_t lla_bytes_per_token(const lla_set_desc* desc) {

@@ -225,6 +225,14 @@ size_t lla_decode_workspace_bytes(const lla_set_desc* desc, int32_t batch,
 int32_t lla_decode_plan_splits(const lla_set_desc* desc, int32_t batch, int32_t max_pos,
                                int32_t window, int32_t splits, int32_t entry);
 
+/* Name of the latent-scan kernel family a decode call with this set, entry
+ * (0 = lla_decode_reconstruct, 1 = lla_decode_absorbed, 2 =
+ * hla_decode_windowed) and flags launches: "k_scan_absorbed_mfma",
+ * "k_scan_absorbed_generic", "k_scan_reconstruct_mfma",
+ * "k_scan_reconstruct_gemm" or "k_scan_reconstruct_generic" (static
+ * strings, for profilers).  NULL on invalid arguments.  Host only. */
+const char* lla_decode_scan_kernel(const lla_set_desc* desc, int32_t entry, int32_t flags);
+
 /* Bytes one set stores per token (all groups): G*(r_k + r_v)*sizeof(dtype)
  * ([HLA] "Latent Writer": r_k + r_v (+ 2 r_1) numbers per token per layer).
  * 0 on an invalid descriptor. */

@@ -172,3 +172,29 @@ def test_workspace_and_plan():
     for b, ctx in ((128, 4096), (32, 16384), (1, 256)):
         s = B.lla_decode_plan_splits(d, b, ctx - 1, 128)
         assert 1 <= s <= max(1, (ctx - 1 - 128 + 63) // 64)
+
+
+def test_scan_kernel_query():
+    """The library names the latent-scan kernel family it would launch."""
+    def desc(dtype, G, H, r, dh):
+        return B.set_desc(n_heads=H, head_dim=dh, groups=G, r_k=r, r_v=r, loop_first=1, loop_last=4,
+                          page_size=64, rope_baked=0, rope_base=0.0, dtype=dtype)
+    hla = desc(B.LLA_BF16, 1, 16, 512, 128)
+    assert B.lla_decode_scan_kernel(hla, 2) == "k_scan_absorbed_mfma"
+    assert B.lla_decode_scan_kernel(hla, 1) == "k_scan_absorbed_mfma"
+    assert B.lla_decode_scan_kernel(hla, 2, B.LLA_FLAG_GENERIC) == "k_scan_absorbed_generic"
+    assert B.lla_decode_scan_kernel(hla, 0) == "k_scan_reconstruct_gemm"
+    per_head = desc(B.LLA_BF16, 16, 16, 32, 128)
+    assert B.lla_decode_scan_kernel(per_head, 0) == "k_scan_reconstruct_mfma"
+    assert B.lla_decode_scan_kernel(per_head, 0, B.LLA_FLAG_GENERIC) == "k_scan_reconstruct_generic"
+    tiny = desc(B.LLA_F32, 1, 2, 128, 64)   # fp32 storage: general kernels only
+    assert B.lla_decode_scan_kernel(tiny, 1) == "k_scan_absorbed_generic"
+    assert B.lla_decode_scan_kernel(tiny, 0) == "k_scan_reconstruct_generic"
+    wide = desc(B.LLA_BF16, 1, 55, 5280, 96)
+    assert B.lla_decode_scan_kernel(wide, 0) == "k_scan_reconstruct_gemm"
+    assert B.lla_decode_scan_kernel(wide, 1) == "k_scan_absorbed_generic"
+    assert B.lla_decode_scan_kernel(hla, 3) is None
+    assert B.lla_decode_scan_kernel(hla, 0, 2) is None
+    bad = desc(B.LLA_BF16, 1, 16, 512, 128)
+    bad.head_dim = 0
+    assert B.lla_decode_scan_kernel(bad, 0) is None
