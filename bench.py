@@ -127,7 +127,7 @@ class DecodeStep:
                 rk = gen.device_normal((Bt, W + 1, H, dh), w.dtype, sd + 4, float(np.sqrt(s.n_loops)))
                 rv = gen.device_normal((Bt, W + 1, H, dh), w.dtype, sd + 5, float(np.sqrt(s.n_loops)))
                 A = gen.device_normal((H, dh, s.r_k), w.dtype, sd + 6, 1.0 / np.sqrt(s.r_k))
-                Bm = gen.device_normal((H, s.r_v, dh), w.dtype, sd + 7, 1.0 / np.sqrt(s.r_v))
+                Bm = gen.device_normal((H, dh, s.r_v), w.dtype, sd + 7, 1.0 / np.sqrt(s.r_v))   # B_t^T
                 out = torch.empty((Bt, H, dh), dtype=dt, device=dev)
                 bufs = (q, kc, vc, rk, rv, A, Bm, out)
                 args = B.decode_args(loop=t, window=W, pos=self.pos, q=q, k_cur=kc, v_cur=vc, ring_k=rk,

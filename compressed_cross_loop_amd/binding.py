@@ -81,6 +81,11 @@ lib.lla_status_string.argtypes = [ctypes.c_int]
 lib.lla_abi_version.restype = ctypes.c_int32
 lib.lla_abi_version.argtypes = []
 
+ABI_VERSION = 2   # include/lla.h LLA_ABI_VERSION this binding marshals for
+if lib.lla_abi_version() != ABI_VERSION:
+    raise ImportError(f"{LIB_PATH} has ABI version {lib.lla_abi_version()}, the binding expects {ABI_VERSION}: "
+                      "rebuild it (python -c 'import __graft_entry__ as g; g.build()')")
+
 
 class LlaError(RuntimeError):
     def __init__(self, status):
@@ -120,7 +125,9 @@ def set_desc(*, n_heads, head_dim, groups, r_k, r_v, loop_first, loop_last, page
 def store(pages, block_table, max_pages_per_seq=None):
     if max_pages_per_seq is None:
         max_pages_per_seq = block_table.shape[-1]
-    return LlaStore(_ptr(pages), _ptr(block_table), int(max_pages_per_seq))
+    st = LlaStore(_ptr(pages), _ptr(block_table), int(max_pages_per_seq))
+    st._keep = (pages, block_table)   # the struct holds raw pointers: keep the tensors alive with it
+    return st
 
 
 def lla_abi_version():
@@ -170,9 +177,12 @@ def decode_args(*, loop, window, pos, q, k_cur, v_cur, ring_k, ring_v, A, B, out
     ws_bytes = 0 if workspace is None or isinstance(workspace, int) else \
         workspace.numel() * workspace.element_size()
     ev = ctypes.cast(scan_events, ctypes.c_void_p) if scan_events is not None else None
-    return LlaDecodeArgs(loop, window, int(max_pos_hint), splits, flags, _ptr(pos), _ptr(q),
+    args = LlaDecodeArgs(loop, window, int(max_pos_hint), splits, flags, _ptr(pos), _ptr(q),
                          _ptr(k_cur), _ptr(v_cur), _ptr(ring_k), _ptr(ring_v), _ptr(A), _ptr(B),
                          _ptr(out), _ptr(workspace), ws_bytes, ev)
+    # the struct holds raw pointers: keep every tensor (temporaries included) alive with it
+    args._keep = (pos, q, k_cur, v_cur, ring_k, ring_v, A, B, out, workspace)
+    return args
 
 
 def _decode(fn, desc, st, batch, args, stream):

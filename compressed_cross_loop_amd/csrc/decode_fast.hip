@@ -278,19 +278,18 @@ __global__ __launch_bounds__(kThreads) void k_window_fast(DecodeParams p) {
 
 // ------------------------------------------------------------------ combine
 // grid (H, ceil(B / 16)); 4 waves; out[b][h] for 16 sequences, d_h = 128.
-// The B_t^T product runs on v_mfma_f32_16x16x32_bf16, which wants 8
-// consecutive latent dims k per lane, while B_t rows are contiguous along
-// d_h.  Each lane therefore loads an 8 x 8 block of B_t (rows k0..k0+7,
-// columns 8c..8c+7, c = lane % 16) with eight 16-byte loads and regroups it
-// in registers: product j takes column 8c + j of every row, so output tile j
-// holds the columns {8c + j}.  Wave w takes the 32-row k steps w, w+4, ...;
-// all its loads are issued at entry so their latency overlaps the merge.  The
-// fp32 latent sums enter as bf16 hi + lo parts (two products), which keeps
-// the product at fp32-level accuracy.  The four waves' partial results are
-// summed through LDS and written as 16-byte rows.
+// The B_t^T product runs on v_mfma_f32_16x16x32_bf16.  The value decoder is
+// stored as B_t^T [d_h][r_v] (rows contiguous along the latent axis), so each
+// B-operand fragment (8 consecutive latent dims of one output column) is one
+// 16-byte load.  Wave w takes the 32-wide k steps w, w+4, ...; all its loads
+// are issued at entry so their latency overlaps the merge.  The fp32 latent
+// sums enter as bf16 hi + lo parts (two products), which keeps the product at
+// fp32-level accuracy.  The four waves' partial results are summed through LDS
+// and written as 16-byte rows.
 template <int RV>
 __global__ __launch_bounds__(kThreads) void k_combine_mfma(DecodeParams p) {
   constexpr int DH = 128;
+  constexpr int NT = DH / 16;              // output column tiles
   constexpr int KS = RV / 32;              // k steps
   constexpr int KW = (KS + 3) / 4;         // k steps per wave
   __shared__ float ob[16][RV + 1];         // latent-space sums
@@ -301,15 +300,15 @@ __global__ __launch_bounds__(kThreads) void k_combine_mfma(DecodeParams p) {
   const int h = blockIdx.x, b0 = blockIdx.y * 16, tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
-  const bf16* Bh = static_cast<const bf16*>(p.Bm) + (int64_t)h * RV * DH;
-  bf16x8 braw[KW][8];
+  const bf16* Bh = static_cast<const bf16*>(p.Bm) + (int64_t)h * DH * RV;   // [DH][RV]
+  bf16x8 bfr[KW][NT];
 #pragma unroll
   for (int u = 0; u < KW; ++u) {
     const int st = wave + 4 * u;
     if (st < KS) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        braw[u][i] = *reinterpret_cast<const bf16x8*>(Bh + (int64_t)(32 * st + 8 * grp + i) * DH + 8 * col);
+      for (int nt = 0; nt < NT; ++nt)
+        bfr[u][nt] = *reinterpret_cast<const bf16x8*>(Bh + (int64_t)(16 * nt + col) * RV + 32 * st + 8 * grp);
     }
   }
 
@@ -422,9 +421,9 @@ __global__ __launch_bounds__(kThreads) void k_combine_mfma(DecodeParams p) {
     }
   }
   __syncthreads();
-  f32x4 acc[8];
+  f32x4 acc[NT];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int u = 0; u < KW; ++u) {
     const int st = wave + 4 * u;
@@ -439,22 +438,17 @@ __global__ __launch_bounds__(kThreads) void k_combine_mfma(DecodeParams p) {
         alo[i] = static_cast<bf16>(x - static_cast<float>(hi));
       }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        bf16x8 bj;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) bj[i] = braw[u][i][j];
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bj, acc[j], 0, 0, 0);
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, bj, acc[j], 0, 0, 0);
+      for (int nt = 0; nt < NT; ++nt) {
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bfr[u][nt], acc[nt], 0, 0, 0);
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, bfr[u][nt], acc[nt], 0, 0, 0);
       }
     }
   }
-  // lane holds C[b = 4 grp + r][e = 8 col + j]
+  // lane holds C[b = 4 grp + r][e = 16 nt + col]
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    float4* dst = reinterpret_cast<float4*>(&red[wave][4 * grp + r][8 * col]);
-    dst[0] = float4{acc[0][r], acc[1][r], acc[2][r], acc[3][r]};
-    dst[1] = float4{acc[4][r], acc[5][r], acc[6][r], acc[7][r]};
-  }
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[wave][4 * grp + r][16 * nt + col] = acc[nt][r];
   __syncthreads();
   {
     const int bl = tid / 16, e8 = (tid % 16) * 8, b = b0 + bl;

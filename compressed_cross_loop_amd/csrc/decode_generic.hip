@@ -244,7 +244,7 @@ __global__ __launch_bounds__(kThreads) void k_scan_reconstruct_generic(DecodePar
   split_range(p, s, n_lat, t0, t1);
   const float* qh = p.qhead + ((int64_t)b * p.H + h) * dh;
   const T* Ah = static_cast<const T*>(p.A) + (int64_t)h * dh * rk;   // [dh][rk]
-  const T* Bh = static_cast<const T*>(p.Bm) + (int64_t)h * rv * dh;  // [rv][dh]
+  const T* Bh = static_cast<const T*>(p.Bm) + (int64_t)h * dh * rv;  // B_t^T: [dh][rv]
   const T* pages = static_cast<const T*>(p.pages);
   const int32_t* bt = p.bt + (int64_t)b * p.max_pages;
   const int e = tid;
@@ -279,7 +279,7 @@ __global__ __launch_bounds__(kThreads) void k_scan_reconstruct_generic(DecodePar
           for (int t = 0; t < kRecTok; ++t) kacc[t] += a * skt[t][r];
         }
         for (int r = 0; r < rvn; ++r) {
-          const float bb = to_f(Bh[(int64_t)(r0 + r) * dh + e]);
+          const float bb = to_f(Bh[(int64_t)e * rv + r0 + r]);
 #pragma unroll
           for (int t = 0; t < kRecTok; ++t) vacc[t] += bb * svt[t][r];
         }
@@ -362,10 +362,10 @@ __global__ __launch_bounds__(kThreads) void k_combine(DecodeParams p) {
       ob[k] = acc;
     }
     __syncthreads();
-    const T* Bh = static_cast<const T*>(p.Bm) + (int64_t)h * rv * dh;
+    const T* Bh = static_cast<const T*>(p.Bm) + (int64_t)h * dh * rv;   // B_t^T: [dh][rv]
     for (int e = tid; e < dh; e += kThreads) {
       float acc = 0.f;
-      for (int k = 0; k < rv; ++k) acc += to_f(Bh[(int64_t)k * dh + e]) * ob[k];
+      for (int k = 0; k < rv; ++k) acc += to_f(Bh[(int64_t)e * rv + k]) * ob[k];
       out[e] = from_f<T>((acc + window_sum(e)) * inv);
     }
   } else {

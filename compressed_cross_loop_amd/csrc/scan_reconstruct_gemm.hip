@@ -3,13 +3,13 @@
 // gfx950 matrix cores.  Rebuilding every head's keys and values is a GEMM per
 // sequence,
 //   K^[tokens x H d_h] = S^K[tokens x r] . A^T[r x H d_h]
-//   V^[tokens x H d_h] = S^V[tokens x r] . B  [r x H d_h]
+//   V^[tokens x H d_h] = S^V[tokens x r] . B_t[r x H d_h]
 // with an attention epilogue per head, so it is tiled like a GEMM: one
 // workgroup per (context split, sequence, 2 heads), 128-token tiles, K-loop
 // over the latent width in steps of 32.  Each step stages four operand tiles
-// in LDS (key rows and A rows as they are stored; the dimension-major value
-// blocks and the B rows transposed on the way in) while the next step's
-// global loads are in flight.  Eight waves: wave w computes K^ (w even) or V^
+// in LDS (key rows and both decoders' rows as they are stored; the
+// dimension-major value blocks transposed on the way in) while the next
+// step's global loads are in flight.  Eight waves: wave w computes K^ (w even) or V^
 // (w odd) of head (w/2)%2 for token half w/4 (4 x d_h/16
 // v_mfma_f32_16x16x32_bf16 tiles).  After a tile, the K waves score against
 // q' into LDS and the V waves run the online softmax and o += p . V^.
@@ -58,7 +58,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_scan_reconstruct_gemm(DecodePar
   const bf16* pages = static_cast<const bf16*>(p.pages);
   const int32_t* bt = p.bt + (int64_t)b * p.max_pages;
   const bf16* A = static_cast<const bf16*>(p.A);    // [H][DH][R]
-  const bf16* Bm = static_cast<const bf16*>(p.Bm);  // [H][R][DH]
+  const bf16* Bm = static_cast<const bf16*>(p.Bm);  // B_t^T: [H][DH][R]
 
   float qv[NT];
   {
@@ -92,12 +92,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_scan_reconstruct_gemm(DecodePar
       ruk[u] = *reinterpret_cast<const bf16x8*>(A + ((int64_t)hh * DH + e) * R + ks * KC + part * 8);
     }
 #pragma unroll
-    for (int u = 0; u < NU; ++u) {   // B rows: 2 heads x 32 dims x DH/8 chunks
+    for (int u = 0; u < NU; ++u) {   // B_t^T rows: 2 heads x DH rows x 4 chunks
       const int c = min(tid + u * kThreads, 2 * DH * KC / 8 - 1);
-      const int hh2 = c / (KC * DH / 8), rem = c % (KC * DH / 8);
-      const int r = rem / (DH / 8), e8 = (rem % (DH / 8)) * 8;
-      const int hh = min(2 * hb + hh2, H - 1);
-      ruv[u] = *reinterpret_cast<const bf16x8*>(Bm + ((int64_t)hh * R + ks * KC + r) * DH + e8);
+      const int row = c / 4, part = c % 4;
+      const int hh = min(2 * hb + row / DH, H - 1), e = row % DH;
+      ruv[u] = *reinterpret_cast<const bf16x8*>(Bm + ((int64_t)hh * DH + e) * R + ks * KC + part * 8);
     }
   };
   auto store_step = [&]() {
@@ -110,14 +109,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_scan_reconstruct_gemm(DecodePar
       if (c < 2 * DH * KC / 8) *reinterpret_cast<bf16x8*>(&uk[c / 4][(c % 4) * 8]) = ruk[u];
     }
 #pragma unroll
-    for (int u = 0; u < NU; ++u) {   // transpose: 8 columns of one dim -> 8 column rows
+    for (int u = 0; u < NU; ++u) {
       const int c = tid + u * kThreads;
-      if (c < 2 * DH * KC / 8) {
-        const int hh2 = c / (KC * DH / 8), rem = c % (KC * DH / 8);
-        const int r = rem / (DH / 8), e8 = (rem % (DH / 8)) * 8;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) uv[hh2 * DH + e8 + k][r] = ruv[u][k];
-      }
+      if (c < 2 * DH * KC / 8) *reinterpret_cast<bf16x8*>(&uv[c / 4][(c % 4) * 8]) = ruv[u];
     }
   };
 

@@ -6,13 +6,15 @@
 // workgroup, one workgroup per (context split, sequence, 4 heads).  Per
 // 16-token tile the wave rebuilds, for its head,
 //   K^ [16 tok x d_h] = S^K [16 x r] . A^T [r x d_h]   (v_mfma_f32_16x16x32_bf16)
-//   V^ [16 tok x d_h] = S^V [16 x r] . B   [r x d_h]   (same)
+//   V^ [16 tok x d_h] = S^V [16 x r] . B_t [r x d_h]   (same)
 // then scores K^ q' (the 16 lanes holding one token row reduce), an online
-// softmax over the tile, and o += p . V^.  A^(h) and B^(h) are held in
-// registers in B-operand layout for the whole scan.  Key rows are token-major
-// in the store (one 16-byte load per lane); the tile's value block is stored
-// dimension-major (for the absorbed read), so each wave transposes it through
-// its own LDS slice before the V^ product.  Several tiles are kept in flight.
+// softmax over the tile, and o += p . V^.  Both decoders are stored [d_h][r]
+// (rows contiguous along the latent axis), so each B-operand fragment is one
+// 16-byte load; they are held in registers for the whole scan.  Key rows are
+// token-major in the store (one 16-byte load per lane); the tile's value block
+// is stored dimension-major (for the absorbed read), so each wave transposes
+// it through its own LDS slice before the V^ product.  Several tiles are kept
+// in flight.
 #include "device_common.h"
 #include "lla_internal.h"
 
@@ -50,15 +52,14 @@ __global__ __launch_bounds__(kThreads, 2) void k_scan_reconstruct_mfma(DecodePar
   // decoders of this head, in B-operand layout (lane: column e = 16 nt + col,
   // 8 consecutive latent dims 32 st + 8 grp ..)
   const bf16* Ah = static_cast<const bf16*>(p.A) + (int64_t)h * DH * R;   // [DH][R]
-  const bf16* Bh = static_cast<const bf16*>(p.Bm) + (int64_t)h * R * DH;  // [R][DH]
+  const bf16* Bh = static_cast<const bf16*>(p.Bm) + (int64_t)h * DH * R;  // B_t^T: [DH][R]
   bf16x8 af[NT][KS], bfr[NT][KS];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
     for (int st = 0; st < KS; ++st) {
       af[nt][st] = *reinterpret_cast<const bf16x8*>(Ah + (int64_t)(16 * nt + col) * R + 32 * st + 8 * grp);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) bfr[nt][st][k] = Bh[(int64_t)(32 * st + 8 * grp + k) * DH + 16 * nt + col];
+      bfr[nt][st] = *reinterpret_cast<const bf16x8*>(Bh + (int64_t)(16 * nt + col) * R + 32 * st + 8 * grp);
     }
   float qv[NT];
   {

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define LLA_ABI_VERSION 1
+#define LLA_ABI_VERSION 2   /* 2: value decoder passed as B_t^T [H][d_h][r_v] */
 
 typedef void* lla_stream_t; /* a hipStream_t */
 
@@ -156,7 +156,9 @@ size_t lla_write_workspace_bytes(const lla_set_desc* desc, int32_t batch,
  *                 slot i mod (W+1) with R_i k_cur and v_cur (that slot's old
  *                 token, i-W-1, is a latent token from now on).
  *   A             [H][d_h][r_k]  key decoder A_t of this loop (per head)
- *   B             [H][r_v][d_h]  value map B_t (o = B_t^T c^V)
+ *   B             [H][d_h][r_v]  value decoder stored transposed, B_t^T
+ *                 (v = B_t^T c^V), the same orientation as A: rows
+ *                 contiguous along the latent axis
  *   out           [batch][H][d_h]
  *   workspace     scratch of lla_decode_workspace_bytes() bytes; contents
  *                 on entry are irrelevant

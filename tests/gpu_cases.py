@@ -68,7 +68,8 @@ def run_decode(entry, c: gen.DecodeInputs, *, splits=0, flags=0, max_pos_hint=No
     pos = c.pos.to(dev)
     q, kc, vc = c.q.to(dev), c.k_cur.to(dev), c.v_cur.to(dev)
     rk, rv = c.ring_k.to(dev), c.ring_v.to(dev)
-    A, Bv = c.A.to(dev), c.Bv.to(dev)
+    # the library takes the value decoder as B_t^T [H][d_h][r_v]
+    A, Bv = c.A.to(dev), c.Bv.transpose(1, 2).contiguous().to(dev)
     out = torch.full(tuple(c.q.shape), float("nan"), dtype=dt, device=dev)
     mp = int(c.pos.max()) if max_pos_hint is None else max_pos_hint
     nbytes = B.lla_decode_workspace_bytes(desc, c.batch, mp, c.window, splits)

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert B.lla_abi_version() == 1
+    assert B.lla_abi_version() == 2 == B.ABI_VERSION
     for s in range(5):
         assert B.lla_status_string(s)
     assert B.lla_status_string(99) == "unknown status"

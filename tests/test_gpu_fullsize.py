@@ -56,7 +56,7 @@ def run(c, entry):
     ws = torch.empty(B.lla_decode_workspace_bytes(c["desc"], c["batch"], c["i"], w.window), dtype=torch.uint8,
                      device="cuda")
     args = B.decode_args(loop=c["loop"], window=w.window, pos=c["pos"], q=c["q"], k_cur=c["kc"], v_cur=c["vc"],
-                         ring_k=c["rk"], ring_v=c["rv"], A=c["A"], B=c["Bv"], out=out, workspace=ws,
+                         ring_k=c["rk"], ring_v=c["rv"], A=c["A"], B=c["Bv"].transpose(1, 2).contiguous(), out=out, workspace=ws,
                          max_pos_hint=c["i"])
     fn = {"hla": B.hla_decode_windowed, "absorbed": B.lla_decode_absorbed,
           "reconstruct": B.lla_decode_reconstruct}[entry]

@@ -20,7 +20,8 @@ def test_graph_replays_match_eager():
                       page_size=64, rope_baked=1, rope_base=10000.0, dtype=B.LLA_BF16)
     dev = lambda t: t.cuda()
     pages, bt, pos = dev(c.pages), dev(c.block_table), dev(c.pos)
-    q, kc, vc, rk, rv, A, Bv = map(dev, (c.q, c.k_cur, c.v_cur, c.ring_k, c.ring_v, c.A, c.Bv))
+    q, kc, vc, rk, rv, A = map(dev, (c.q, c.k_cur, c.v_cur, c.ring_k, c.ring_v, c.A))
+    Bv = dev(c.Bv.transpose(1, 2).contiguous())   # value decoder as B_t^T
     out = torch.empty_like(q)
     ws = torch.empty(B.lla_decode_workspace_bytes(desc, 4, 700, 128), dtype=torch.uint8, device="cuda")
     st = B.store(pages, bt)

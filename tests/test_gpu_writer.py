@@ -112,7 +112,7 @@ def test_writer_then_decode_end_to_end():
     dws = torch.empty(B.lla_decode_workspace_bytes(desc, Bsz, N - 1, W), dtype=torch.uint8, device="cuda")
     rk, rv = dc.ring_k.cuda(), dc.ring_v.cuda()
     args = B.decode_args(loop=3, window=W, pos=dc.pos.cuda(), q=dc.q.cuda(), k_cur=dc.k_cur.cuda(),
-                         v_cur=dc.v_cur.cuda(), ring_k=rk, ring_v=rv, A=dc.A.cuda(), B=dc.Bv.cuda(),
+                         v_cur=dc.v_cur.cuda(), ring_k=rk, ring_v=rv, A=dc.A.cuda(), B=dc.Bv.transpose(1, 2).contiguous().cuda(),
                          out=out, workspace=dws, max_pos_hint=N - 1)
     B.hla_decode_windowed(desc, st, Bsz, args)
     torch.cuda.synchronize()
