@@ -2,17 +2,33 @@
 // per token shared by all heads; "Looped Latent Attention" abstracts) on the
 // gfx950 matrix cores.  Rebuilding every head's keys and values is a GEMM per
 // sequence,
-//   K^[tokens x H d_h] = S^K[tokens x r] . A^T[r x H d_h]
-//   V^[tokens x H d_h] = S^V[tokens x r] . B_t[r x H d_h]
-// with an attention epilogue per head, so it is tiled like a GEMM: one
-// workgroup per (context split, sequence, 2 heads), 128-token tiles, K-loop
-// over the latent width in steps of 32.  Each step stages four operand tiles
-// in LDS (key rows and both decoders' rows as they are stored; the
-// dimension-major value blocks transposed on the way in) while the next
-// step's global loads are in flight.  Eight waves: wave w computes K^ (w even) or V^
-// (w odd) of head (w/2)%2 for token half w/4 (4 x d_h/16
-// v_mfma_f32_16x16x32_bf16 tiles).  After a tile, the K waves score against
-// q' into LDS and the V waves run the online softmax and o += p . V^.
+//   K^[tokens x H d_h] = S^K[tokens x r] . A^T [r x H d_h]
+//   V^[tokens x H d_h] = S^V[tokens x r] . B_t [r x H d_h]
+// with an attention epilogue per head.  One workgroup = (context split,
+// sequence, 2 heads), four waves = {K^, V^} x 2 heads; each wave rebuilds a
+// 128-token x d_h tile of its head over the latent width in K steps of 32 on
+// v_mfma_f32_16x16x32_bf16.
+//
+// No operand is shared between the waves of a workgroup (each wave owns one
+// head's decoder and one latent half), so nothing goes through LDS: every
+// wave streams its own operands from L2/HBM straight into registers with
+// several K steps in flight and no barrier inside the K loop.
+//   K^ wave: A fragment of row tile j = key row of token 16 j + (lane % 16),
+//            8 consecutive latent dims (one 16-byte load from the store).
+//   V^ wave: the value block is dimension-major, so each lane loads 8 dims x 8
+//            tokens (eight 16-byte loads) and regroups them in registers; row
+//            tile j then holds tokens {8 m + j : m = 0..15}.
+//   both:    B fragment = 8 consecutive latent dims of one decoder row (A_t
+//            and B_t^T are both stored [d_h][r]).
+// After a tile the K^ waves reduce q' . k^ per token (DPP row sums) into LDS,
+// one barrier, and the V^ waves run the online softmax and o += p . v^ for
+// their (permuted) tokens.
+//
+// Workgroups are dispatched round-robin over the 8 XCDs, each with its own
+// L2.  The launch order is remapped so that each XCD works through a
+// contiguous range of (4 sequence splits x head pairs): the workgroups in
+// flight on one XCD share latent tiles (same split, other head pairs) and
+// decoders (same head pair, other splits) in that XCD's L2.
 #include "device_common.h"
 #include "lla_internal.h"
 
@@ -22,31 +38,36 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 512;
-constexpr int TM = 128;     // tokens per tile
-constexpr int KC = 32;      // latent dims per K step
-constexpr int LD = KC + 8;  // padded LDS row (80 bytes: 16 lanes hit distinct bank quads)
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int TM = 128;          // tokens per tile
+constexpr int MT = TM / 16;      // row tiles per tile
+constexpr int KC = 32;           // latent dims per K step
+constexpr int kXcds = 8;
+constexpr int kGroupItems = 4;   // splits grouped per head-pair sweep
 
-template <int DH>
-__global__ __launch_bounds__(kThreads, 1) void k_scan_reconstruct_gemm(DecodeParams p) {
+// K steps in flight per wave: limited by registers (the accumulators take
+// MT x d_h/16 x 4 of them); chosen so the K loop runs without spills
+template <int DH, int KIND> struct Stages {
+  static constexpr int value = DH == 128 ? 1 : (DH == 96 ? 2 : 3);
+};
+
+// Everything one wave of role KIND (0: K^, 1: V^) does for its work item.
+// The two roles are separate instantiations so that each gets its own
+// register allocation; both pass the same barriers (one per tile).
+template <int DH, int KIND>
+__device__ __forceinline__ void wave_main(const DecodeParams& p, float (*sc)[2][TM], int b, int s, int hb) {
   constexpr int NT = DH / 16;        // column tiles per head
-  constexpr int MT = TM / 2 / 16;    // row tiles per wave (half of the token tile)
-  __shared__ __attribute__((aligned(16))) bf16 sk[TM][LD];
-  __shared__ __attribute__((aligned(16))) bf16 sv[TM][LD];
-  __shared__ __attribute__((aligned(16))) bf16 uk[2 * DH][LD];
-  __shared__ __attribute__((aligned(16))) bf16 uv[2 * DH][LD];
-  __shared__ float sc[2][TM];
-  __shared__ float ox[2][DH + 1];    // second token half's o and l, per head
-
-  const int s = blockIdx.x, b = blockIdx.y, hb = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int col = lane & 15, grp = lane >> 4;
-  const int kind = wave & 1, hl = (wave >> 1) & 1, mh = wave >> 2;   // K^/V^, head, token half
+  constexpr int NS = Stages<DH, KIND>::value;
+  const int lane = threadIdx.x & 63;
+  const int hl = __builtin_amdgcn_readfirstlane(threadIdx.x >> 7);   // head of the pair
+  const int col = lane & 15, kg = lane >> 4;
   const int H = p.H, R = p.rk, Rt = 2 * p.rk, P = p.P;
   const int h = 2 * hb + hl;
   const bool head_ok = h < H;
+  const int hc = head_ok ? h : H - 1;
   const int i = p.pos[b];
   const int n_lat = max(0, i - p.W);
   int t0 = s * p.chunk;
@@ -57,61 +78,73 @@ __global__ __launch_bounds__(kThreads, 1) void k_scan_reconstruct_gemm(DecodePar
 
   const bf16* pages = static_cast<const bf16*>(p.pages);
   const int32_t* bt = p.bt + (int64_t)b * p.max_pages;
-  const bf16* A = static_cast<const bf16*>(p.A);    // [H][DH][R]
-  const bf16* Bm = static_cast<const bf16*>(p.Bm);  // B_t^T: [H][DH][R]
+  // Addresses are a wave-uniform base (scalar registers) plus one 32-bit
+  // lane offset, so the unrolled loads do not each hold a 64-bit pointer.
+  // This wave's decoder (A_t or B_t^T, both [DH][R]): fragment nt is row
+  // 16 nt + col, latent dims ks*32 + 8 kg ..
+  const bf16* dec = static_cast<const bf16*>(KIND ? p.Bm : p.A) + (int64_t)hc * DH * R;
+  const uint32_t lane_off = (uint32_t)(col * R + 8 * kg);   // row col, dims 8 kg .. (decoder and key rows)
 
   float qv[NT];
-  {
-    const float* qh = p.qhead + ((int64_t)b * H + (head_ok ? h : 0)) * DH;
+  if (KIND == 0) {
+    const float* qh = p.qhead + ((int64_t)b * H + hc) * DH;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) qv[nt] = qh[16 * nt + col];
   }
 
-  // ---- staging.  Thread tid stages one key chunk and one value chunk of
-  // 16-token sub-tile `wave` (its base pointer is resolved once per tile and
-  // clamped so that a sub-tile past the end rereads the last valid one,
-  // masked later), plus A-row and B-row chunks of the two heads.
-  constexpr int NU = (2 * DH * KC / 8 + kThreads - 1) / kThreads;
-  bf16x8 rsk, rsv, ruk[NU], ruv[NU];
-  const bf16* sub = pages;
-  auto set_tile = [&](int tile) {
-    int j = min(t0 + tile * TM + 16 * wave, t1 - 1);
-    j -= j & 15;
-    sub = pages + tile_base(bt[j / P], 0, j % P, 1, P, Rt);
+  // start of a latent token's 16-token tile in the store (j uniform)
+  auto tile_of = [&](int j) -> const bf16* {
+    const int pg = __builtin_amdgcn_readfirstlane(bt[j / P]);
+    return pages + tile_base(pg, 0, j % P, 1, P, Rt);
   };
-  const int krow = (tid >> 2) & 15, kpart = tid & 3;
-  const int vb = (tid >> 5) & 1, r16 = (tid >> 1) & 15, vhalf = tid & 1;
-  auto load_step = [&](int ks) {
-    rsk = *reinterpret_cast<const bf16x8*>(sub + krow * R + ks * KC + kpart * 8);
-    rsv = *reinterpret_cast<const bf16x8*>(sub + 16 * R + (2 * ks + vb) * 256 + r16 * 16 + 8 * vhalf);
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {   // A rows: 2 heads x DH rows x 4 chunks
-      const int c = min(tid + u * kThreads, 2 * DH * KC / 8 - 1);
-      const int row = c / 4, part = c % 4;
-      const int hh = min(2 * hb + row / DH, H - 1), e = row % DH;
-      ruk[u] = *reinterpret_cast<const bf16x8*>(A + ((int64_t)hh * DH + e) * R + ks * KC + part * 8);
-    }
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {   // B_t^T rows: 2 heads x DH rows x 4 chunks
-      const int c = min(tid + u * kThreads, 2 * DH * KC / 8 - 1);
-      const int row = c / 4, part = c % 4;
-      const int hh = min(2 * hb + row / DH, H - 1), e = row % DH;
-      ruv[u] = *reinterpret_cast<const bf16x8*>(Bm + ((int64_t)hh * DH + e) * R + ks * KC + part * 8);
-    }
+
+  struct Set {
+    bf16x8 a[MT];
+    bf16x8 d[NT];
   };
-  auto store_step = [&]() {
-    *reinterpret_cast<bf16x8*>(&sk[16 * wave + krow][kpart * 8]) = rsk;
+  Set set[NS];
+  const bf16* kbase[MT];   // K^: 16-token store tile of row tile j (uniform)
+  const bf16* vbase;       // V^: value rows of this lane's 8 tokens, dims 8 (kg%2) .. of sub-block kg/2
+  auto issue = [&](Set& st, int ks) {
+    if (KIND == 0) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) sv[16 * wave + 8 * vhalf + k][16 * vb + r16] = rsv[k];   // transpose
+      for (int j = 0; j < MT; ++j)
+        st.a[j] = *reinterpret_cast<const bf16x8*>(kbase[j] + ks * KC + lane_off);
+    } else {
+      // dims ks*32 + 8 kg + k (k = 0..7) of this lane's 8 tokens: sub-block
+      // 2 ks + kg/2, dim row 8 (kg%2) + k
+      const bf16* vp = vbase + ks * 512;
 #pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      const int c = tid + u * kThreads;
-      if (c < 2 * DH * KC / 8) *reinterpret_cast<bf16x8*>(&uk[c / 4][(c % 4) * 8]) = ruk[u];
+      for (int k = 0; k < 8; ++k) st.a[k] = *reinterpret_cast<const bf16x8*>(vp + k * 16);
     }
 #pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      const int c = tid + u * kThreads;
-      if (c < 2 * DH * KC / 8) *reinterpret_cast<bf16x8*>(&uv[c / 4][(c % 4) * 8]) = ruv[u];
+    for (int nt = 0; nt < NT; ++nt)
+      st.d[nt] = *reinterpret_cast<const bf16x8*>(dec + (nt * 16 * R + ks * KC) + lane_off);
+  };
+
+  f32x4 acc[MT][NT];
+  auto consume = [&](const Set& st) {
+#pragma unroll
+    for (int j = 0; j < MT; ++j) {
+      bf16x8 af;
+      if (KIND == 0) {
+        af = st.a[j];
+      } else {
+        // regroup: fragment j (token 8 m + j) = element j of each dim row;
+        // dword q packs rows 2q (low half) and 2q + 1 (high half), element j
+        // being the low (j even) or high (j odd) half of dword j/2
+        u32x4 f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const unsigned lo = __builtin_bit_cast(u32x4, st.a[2 * q])[j >> 1];
+          const unsigned hi = __builtin_bit_cast(u32x4, st.a[2 * q + 1])[j >> 1];
+          f[q] = (j & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+        }
+        af = __builtin_bit_cast(bf16x8, f);
+      }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        acc[j][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, st.d[nt], acc[j][nt], 0, 0, 0);
     }
   };
 
@@ -119,117 +152,123 @@ __global__ __launch_bounds__(kThreads, 1) void k_scan_reconstruct_gemm(DecodePar
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) o[nt] = 0.f;
 
-  if (ntile > 0) {
-    set_tile(0);
-    load_step(0);
-    for (int tile = 0; tile < ntile; ++tile) {
-      f32x4 acc[MT][NT];
+  for (int tile = 0; tile < ntile; ++tile) {
+    const int j0 = t0 + tile * TM;
+    const int last = t1 - 1;
+    if (KIND == 0) {
+      // row tile j = tokens j0 + 16 j .. + 15, one 16-token store tile; a
+      // tile wholly past the end rereads the last valid one (masked later)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+      for (int j = 0; j < MT; ++j) kbase[j] = tile_of(min(j0 + 16 * j, last));
+    } else {
+      // tokens 8 col .. 8 col + 7 (one half of a 16-token tile)
+      const int tok = min(j0 + 8 * col, last);
+      const int64_t pg = bt[tok / P];
+      vbase = pages + tile_base(pg, 0, tok % P, 1, P, Rt) + 16 * R + (kg >> 1) * 256 + 8 * (kg & 1) * 16 +
+              (tok & 8);
+    }
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int ks = 0; ks < nks; ++ks) {
-        __syncthreads();
-        store_step();
-        __syncthreads();
-        // next step's operands; unconditional (the very last step reloads
-        // itself) so no register set has to survive a skipped load
-        int kn = ks + 1;
-        if (kn == nks) {
-          kn = 0;
-          if (tile + 1 < ntile)
-            set_tile(tile + 1);
-          else
-            kn = ks;
-        }
-        load_step(kn);
-        const bf16 (*X)[LD] = kind ? sv : sk;
-        const bf16 (*U)[LD] = kind ? uv : uk;
-        bf16x8 bfr[NT];
+    for (int j = 0; j < MT; ++j)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-          bfr[nt] = *reinterpret_cast<const bf16x8*>(&U[hl * DH + 16 * nt + col][8 * grp]);
+      for (int nt = 0; nt < NT; ++nt) acc[j][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // K loop: NS steps in flight; refills are unconditional (clamped to the
+    // last step) so no register set has to survive a skipped refill
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&X[64 * mh + 16 * mt + col][8 * grp]);
+    for (int u = 0; u < NS; ++u) issue(set[u], min(u, nks - 1));
+    int ks = 0;
+    while (ks < nks) {
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt)
-            acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bfr[nt], acc[mt][nt], 0, 0, 0);
-        }
-      }
-      // ---- attention epilogue; lane holds token 64 mh + 16 mt + 4 grp + r,
-      // column 16 nt + col
-      const int j0 = t0 + tile * TM;
-      if (kind == 0) {
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float a = 0.f;
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) a += qv[nt] * acc[mt][nt][r];
-            a = row_sum16(a);
-            const int tok = 64 * mh + 16 * mt + 4 * grp + r;
-            if (col == 0) sc[hl][tok] = (j0 + tok < t1) ? a : -INFINITY;
-          }
-      }
-      __syncthreads();
-      if (kind == 1) {
-        // both token halves of a head see all 128 scores: same max, same rescale
-        float mx = fmaxf(sc[hl][lane], sc[hl][lane + 64]);
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-        const float mn = fmaxf(m, mx);
-        const float alpha = exp2_diff(m, mn);
-        float lp = 0.f;
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) o[nt] *= alpha;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int tok = 64 * mh + 16 * mt + 4 * grp + r;
-            const bool ok = j0 + tok < t1;
-            const float pw = ok ? exp2f(sc[hl][tok] - mn) : 0.f;
-            lp += pw;
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) o[nt] += ok ? pw * acc[mt][nt][r] : 0.f;
-          }
-        lp += __shfl_xor(lp, 16);
-        lp += __shfl_xor(lp, 32);
-        l = l * alpha + lp;
-        m = mn;
+      for (int u = 0; u < NS; ++u) {
+        consume(set[u]);
+        __builtin_amdgcn_sched_barrier(0);   // keep the refill below its consumer
+        issue(set[u], min(ks + NS, nks - 1));
+        if (++ks >= nks) break;
       }
     }
+
+    // ---- attention epilogue
+    const int par = tile & 1;
+    if (KIND == 0) {
+      // lane holds K^[token 16 j + 4 kg + r][dim 16 nt + col]
+#pragma unroll
+      for (int j = 0; j < MT; ++j) {
+        __builtin_amdgcn_sched_barrier(0);   // one row tile's accumulators at a time
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float a = 0.f;
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) a += qv[nt] * acc[j][nt][r];
+          a = row_sum16(a);
+          const int tok = 16 * j + 4 * kg + r;
+          if (col == 0) sc[par][hl][tok] = (j0 + tok < t1) ? a : -INFINITY;
+        }
+      }
+    }
+    __syncthreads();
+    if (KIND == 1) {
+      // lane holds V^[token 8 (4 kg + r) + j][dim 16 nt + col]
+      float mx = fmaxf(sc[par][hl][lane], sc[par][hl][lane + 64]);
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+      const float mn = fmaxf(m, mx);
+      const float alpha = exp2_diff(m, mn);
+      float lp = 0.f;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) o[nt] *= alpha;
+#pragma unroll
+      for (int j = 0; j < MT; ++j) {
+        __builtin_amdgcn_sched_barrier(0);   // one row tile's accumulators at a time
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int tok = 8 * (4 * kg + r) + j;
+          const bool ok = j0 + tok < t1;
+          const float pw = ok ? exp2f(sc[par][hl][tok] - mn) : 0.f;
+          lp += pw;
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) o[nt] += ok ? pw * acc[j][nt][r] : 0.f;
+        }
+      }
+      lp += __shfl_xor(lp, 16);
+      lp += __shfl_xor(lp, 32);
+      l = l * alpha + lp;
+      m = mn;
+    }
   }
-  // ---- add the two token halves of each head, write the split's partial
-  if (kind == 1) {
+
+  // ---- the V^ wave of each head writes the split's partial
+  if (KIND == 1 && head_ok) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       o[nt] += __shfl_xor(o[nt], 16);
       o[nt] += __shfl_xor(o[nt], 32);
     }
-  }
-  __syncthreads();
-  if (kind == 1 && mh == 1) {
-    if (grp == 0) {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) ox[hl][16 * nt + col] = o[nt];
-    }
-    if (lane == 0) ox[hl][DH] = l;
-  }
-  __syncthreads();
-  if (kind == 1 && mh == 0 && head_ok) {
     const int64_t row = ((int64_t)b * p.S + s) * H + h;
     if (lane == 0) {
       p.part_ml[row * 2 + 0] = m;
-      p.part_ml[row * 2 + 1] = l + ox[hl][DH];
+      p.part_ml[row * 2 + 1] = l;
     }
-    if (grp == 0) {
+    if (kg == 0) {
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) p.part_o[row * p.Dp + 16 * nt + col] = o[nt] + ox[hl][16 * nt + col];
+      for (int nt = 0; nt < NT; ++nt) p.part_o[row * p.Dp + 16 * nt + col] = o[nt];
     }
   }
+}
+
+template <int DH>
+__global__ __launch_bounds__(kThreads, 1) void k_scan_reconstruct_gemm(DecodeParams p, int n_hp, int n_wg) {
+  __shared__ float sc[2][2][TM];     // scores: tile parity, head of the pair, token
+  // work item, in XCD-aware order
+  const int L = blockIdx.x;
+  const int lam = (L % kXcds) * (n_wg / kXcds) + L / kXcds;
+  const int grp_i = lam / (kGroupItems * n_hp), hb = (lam / kGroupItems) % n_hp;
+  const int item = grp_i * kGroupItems + lam % kGroupItems;
+  if (item >= p.B * p.S) return;     // padding: the whole workgroup leaves
+  const int b = item / p.S, s = item % p.S;
+  // waves 0, 2: K^ of heads 2 hb, 2 hb + 1; waves 1, 3: V^
+  if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & 1)
+    wave_main<DH, 1>(p, sc, b, s, hb);
+  else
+    wave_main<DH, 0>(p, sc, b, s, hb);
 }
 
 }  // namespace
@@ -242,13 +281,18 @@ int scan_reconstruct_gemm_tile() { return TM; }
 
 hipError_t launch_scan_reconstruct_gemm(const DecodeParams& p, hipStream_t s) {
   if (!scan_reconstruct_gemm_supports(p)) return hipErrorNotSupported;
-  const dim3 grid(p.S, p.B, (p.H + 1) / 2);
+  const int n_hp = (p.H + 1) / 2;
+  const int64_t items = (int64_t)p.B * p.S;
+  const int64_t wg = (items + kGroupItems - 1) / kGroupItems * kGroupItems * n_hp;
+  const int64_t n_wg = (wg + kXcds - 1) / kXcds * kXcds;
+  if (n_wg > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)n_wg);
   if (p.dh == 96)
-    hipLaunchKernelGGL(k_scan_reconstruct_gemm<96>, grid, dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL(k_scan_reconstruct_gemm<96>, grid, dim3(kThreads), 0, s, p, n_hp, (int)n_wg);
   else if (p.dh == 128)
-    hipLaunchKernelGGL(k_scan_reconstruct_gemm<128>, grid, dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL(k_scan_reconstruct_gemm<128>, grid, dim3(kThreads), 0, s, p, n_hp, (int)n_wg);
   else
-    hipLaunchKernelGGL(k_scan_reconstruct_gemm<64>, grid, dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL(k_scan_reconstruct_gemm<64>, grid, dim3(kThreads), 0, s, p, n_hp, (int)n_wg);
   return hipGetLastError();
 }
 
