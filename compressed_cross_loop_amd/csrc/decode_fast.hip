@@ -246,7 +246,7 @@ __global__ __launch_bounds__(kThreads) void k_window_fast(DecodeParams p) {
       s = group_sum(s, TPH);   // the TPH lanes of this head
       const float mn = fmaxf(m, s);
       const float alpha = exp2_diff(m, mn);
-      const float pw = exp2f(s - mn);
+      const float pw = fast_exp2(s - mn);
       l = l * alpha + pw;
 #pragma unroll
       for (int k = 0; k < 8; ++k) o[k] = o[k] * alpha + pw * vv[k];

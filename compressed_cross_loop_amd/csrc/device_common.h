@@ -88,9 +88,14 @@ __device__ __forceinline__ float row_max16(float v) {
 // sum over groups of n = 8 or 16 consecutive lanes (n uniform)
 __device__ __forceinline__ float group_sum(float v, int n) { return n == 16 ? row_sum16(v) : row_sum8(v); }
 
+// 2^x on the hardware exp unit (v_exp_f32): -inf gives 0, results below the
+// normal range flush to 0, which is harmless for softmax weights (they are
+// relative to the running maximum, so at most 1)
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // exp2 of (x - m) for the online softmax; m == -inf (nothing seen yet) gives 0
 __device__ __forceinline__ float exp2_diff(float x, float m) {
-  return (m == -INFINITY) ? 0.f : exp2f(x - m);
+  return (m == -INFINITY) ? 0.f : fast_exp2(x - m);
 }
 
 }  // namespace lla

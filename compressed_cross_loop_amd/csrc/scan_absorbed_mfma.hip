@@ -102,7 +102,7 @@ __device__ __forceinline__ s16x4 tile_softmax(f32x4 sc, f32x4 (&acc)[RV / 16], f
   const float alpha = exp2_diff(m, mn);
   float pr[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) pr[r] = exp2f(sc[r] - mn);
+  for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(sc[r] - mn);
   lsum = lsum * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
   m = mn;
   // rescale only when some head's running max moved (rare after a few tiles)
@@ -228,7 +228,7 @@ __device__ void window_slice(const DecodeParams& p, int b, int slice, int g, con
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int t = tb + u;
-      const float pw = exp2f(sc[u] - mn);
+      const float pw = fast_exp2(sc[u] - mn);
       l += pw;
       if (t < nw) {
 #pragma unroll

@@ -222,7 +222,7 @@ __device__ __forceinline__ void wave_main(const DecodeParams& p, float (*sc)[2][
         for (int r = 0; r < 4; ++r) {
           const int tok = 8 * (4 * kg + r) + j;
           const bool ok = j0 + tok < t1;
-          const float pw = ok ? exp2f(sc[par][hl][tok] - mn) : 0.f;
+          const float pw = ok ? fast_exp2(sc[par][hl][tok] - mn) : 0.f;
           lp += pw;
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) o[nt] += ok ? pw * acc[j][nt][r] : 0.f;

@@ -15,6 +15,8 @@
 // is stored dimension-major (for the absorbed read), so each wave transposes
 // it through its own LDS slice before the V^ product.  Several tiles are kept
 // in flight.
+#include <type_traits>
+
 #include "device_common.h"
 #include "lla_internal.h"
 
@@ -93,8 +95,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_scan_reconstruct_mfma(DecodePar
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) o[nt] = 0.f;
 
-  auto step = [&](const Buf& buf, int ti) {
-    const int nvalid = min(16, t1 - (t0 + ti * 16));
+  // FULL: all 16 tokens of the tile are valid (every tile but a ragged last
+  // one), so no masking
+  auto step = [&](const Buf& buf, int nvalid, auto full) {
+    constexpr bool FULL = decltype(full)::value;
     // rebuild keys: lane holds K^[tok 4 grp + r][e = 16 nt + col]
     f32x4 kh[NT];
 #pragma unroll
@@ -121,7 +125,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_scan_reconstruct_mfma(DecodePar
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) a += qv[nt] * kh[nt][r];
       a = row_sum16(a);   // the 16 lanes of this lane group hold one token row
-      sc[r] = (4 * grp + r < nvalid) ? a : -INFINITY;
+      sc[r] = (FULL || 4 * grp + r < nvalid) ? a : -INFINITY;
     }
     float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
@@ -130,9 +134,13 @@ __global__ __launch_bounds__(kThreads, 2) void k_scan_reconstruct_mfma(DecodePar
     const float alpha = exp2_diff(m, mn);
     float pr[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) pr[r] = exp2f(sc[r] - mn);
+    for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(sc[r] - mn);
     lsum = lsum * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
     m = mn;
+    if (alpha != 1.f) {   // uniform: the wave holds one head
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) o[nt] *= alpha;
+    }
     // rebuild values: A operand = token rows of the transposed block
     bf16x8 sv[KS];
 #pragma unroll
@@ -142,9 +150,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_scan_reconstruct_mfma(DecodePar
       f32x4 vh = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int st = 0; st < KS; ++st) vh = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sv[st], bfr[nt][st], vh, 0, 0, 0);
-      float acc = o[nt] * alpha;
+      float acc = o[nt];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc += (4 * grp + r < nvalid) ? pr[r] * vh[r] : 0.f;
+      for (int r = 0; r < 4; ++r) acc += (FULL || 4 * grp + r < nvalid) ? pr[r] * vh[r] : 0.f;
       o[nt] = acc;
     }
   };
@@ -156,7 +164,13 @@ __global__ __launch_bounds__(kThreads, 2) void k_scan_reconstruct_mfma(DecodePar
     for (int base = 0; base < ntiles; base += kPF) {
 #pragma unroll
       for (int u = 0; u < kPF; ++u) {
-        if (base + u < ntiles) step(buf[u], base + u);
+        if (base + u < ntiles) {
+          const int nvalid = min(16, t1 - (t0 + (base + u) * 16));
+          if (nvalid == 16)
+            step(buf[u], 16, std::true_type{});
+          else
+            step(buf[u], nvalid, std::false_type{});
+        }
         load(buf[u], base + u + kPF);   // clamped: always a valid tile
       }
     }
