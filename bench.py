@@ -253,6 +253,25 @@ def calibrate_copy(nbytes):
     print(json.dumps({"calibration_copy_bytes": nbytes}))
 
 
+def stream_copy_gbs(nbytes=1 << 31, reps=10):
+    """HBM bandwidth a plain device copy reaches on this GPU (read + write
+    bytes per second): the practical streaming ceiling beside the 8 TB/s peak."""
+    import torch
+    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / reps
+    del x, y
+    torch.cuda.empty_cache()
+    return 2 * nbytes / dt / 1e9
+
+
 def scan_source_sha():
     import hashlib
     path = os.path.join(ROOT, "compressed_cross_loop_amd", "csrc", "scan_absorbed_mfma.hip")
@@ -357,6 +376,7 @@ def main():
                                  r_v=s.r_v) for s in w.sets],
                    "splits": a.splits or "auto", "launch": "eager" if a.no_graph else "hip_graph"},
         "step_bytes": step_bytes, "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+        "stream_copy_gbs": stream_copy_gbs(),
         "roofline": roof,
     }
     if not a.no_cpu_baseline:

@@ -39,6 +39,9 @@ Readings taken where the pages are silent (each also applies to the GPU path):
   R12 LLA has a single set serving loops 1..T (no separate loop-1 latent).
   R13 The exact window holds post-rotation keys and values for every loop.
   R14 context N = i+1; latent count max(0, i-W); exact count min(W+1, i+1).
+  R15 The uncompressed (full-cache) baseline keeps one exact paged cache per
+      (layer, loop), pages of [P][H][d_h] with rotated keys; a decode call
+      appends the current token and attends to tokens 0..i.
 """
 import numpy as np
 
@@ -249,6 +252,56 @@ def ring_update(pos, k_cur, v_cur, *, window: int, rope_base: float = 0.0):
     pos = np.asarray(pos, dtype=np.int64)
     k = rope_head(np.asarray(k_cur, dtype=np.float64), pos[:, None], rope_base)
     return pos % (window + 1), k, np.asarray(v_cur, dtype=np.float64).copy()
+
+
+# ----------------------------------------------------------------------------
+# Uncompressed (full-cache) looped decode: the teacher the codec replaces
+# ([HLA] "Key Problem": every loop keeps and attends to its own exact keys and
+# values, 2 T d numbers per token per layer).  Reading R15: the exact cache
+# of one (layer, loop) is paged like the latent store, a page holding
+# [P][H][d_h] (all heads of a token contiguous), keys stored rotated (R13).
+# ----------------------------------------------------------------------------
+def gather_kv_cache(k_pages, v_pages, block_table, b: int, n_tok: int, *, page_size: int):
+    """Keys and values [n_tok, H, d_h] of tokens 0..n_tok-1 of sequence b:
+    token j lives in page block_table[b][j // P], slot j % P."""
+    j = np.arange(n_tok)
+    pg = np.asarray(block_table)[b][j // page_size]
+    sl = j % page_size
+    return (np.asarray(k_pages, dtype=np.float64)[pg, sl],
+            np.asarray(v_pages, dtype=np.float64)[pg, sl])
+
+
+def full_cache_decode(k_pages, v_pages, block_table, pos, q, k_cur, v_cur, *, page_size: int,
+                      rope_base: float = 0.0):
+    """One decode call of the uncompressed model for one (layer, loop): at
+    position i the query q' = R_i q attends with scale 1/sqrt(d_h) (R4) to
+    the cached tokens 0..i-1 and to the current token R_i k_cur, v_cur, one
+    softmax over all of them.
+
+    k_pages, v_pages [n_pages, P, H, d_h]; block_table [B, max_pages];
+    q, k_cur, v_cur [B, H, d_h].  Returns out [B, H, d_h] (fp64)."""
+    B, H, d_h = np.asarray(q).shape
+    out = np.zeros((B, H, d_h))
+    for b in range(B):
+        i = int(pos[b])
+        K, V = gather_kv_cache(k_pages, v_pages, block_table, b, i, page_size=page_size)
+        for h in range(H):
+            k_self = rope_head(np.asarray(k_cur[b, h], dtype=np.float64), i, rope_base)
+            keys = np.vstack([K[:, h], k_self[None]])
+            vals = np.vstack([V[:, h], np.asarray(v_cur[b, h], dtype=np.float64)[None]])
+            qr = rope_head(np.asarray(q[b, h], dtype=np.float64), i, rope_base)
+            out[b, h] = _softmax(keys @ qr / np.sqrt(d_h)) @ vals
+    return out
+
+
+def kv_cache_update(pos, k_cur, v_cur, block_table, *, page_size: int, rope_base: float = 0.0):
+    """What a full-cache decode call writes: page block_table[b][i // P], slot
+    i % P of sequence b receives R_i k_cur[b] and v_cur[b].
+    Returns (page [B], slot [B], k [B, H, d_h], v [B, H, d_h])."""
+    pos = np.asarray(pos, dtype=np.int64)
+    page = np.asarray(block_table)[np.arange(len(pos)), pos // page_size]
+    k = rope_head(np.asarray(k_cur, dtype=np.float64), pos[:, None], rope_base)
+    return page, pos % page_size, k, np.asarray(v_cur, dtype=np.float64).copy()
 
 
 # ----------------------------------------------------------------------------

@@ -466,3 +466,90 @@ def test_ring_update_slot_and_rotation():
     assert list(slot) == [0, 5, 1]
     np.testing.assert_allclose(k[2, 0], _complex_rope(np.ones(4), 130, 10000.0), atol=1e-14)
     np.testing.assert_array_equal(v, 2 * kc)
+
+
+# ---------------------------------------------------------------- full-cache baseline
+def _full_cache_case(seed, *, B=3, H=2, d_h=8, P=16, positions=(0, 17, 40), base=10000.0):
+    """Random pre-rotation keys / values per sequence, laid into a paged exact
+    cache through a permuted block table; unused pages are NaN."""
+    g = gen.rng(seed)
+    pos = np.asarray(positions)
+    pps = int(pos.max()) // P + 1
+    n_pages = B * pps + 2
+    perm = g.permutation(n_pages)
+    bt = perm[: B * pps].reshape(B, pps)
+    kp = np.full((n_pages, P, H, d_h), np.nan)
+    vp = np.full((n_pages, P, H, d_h), np.nan)
+    k_raw = g.standard_normal((B, int(pos.max()) + 1, H, d_h))
+    v_raw = g.standard_normal((B, int(pos.max()) + 1, H, d_h))
+    for b in range(B):
+        for j in range(int(pos[b])):
+            kp[bt[b, j // P], j % P] = _complex_rope(k_raw[b, j], j, base)
+            vp[bt[b, j // P], j % P] = v_raw[b, j]
+    q = g.standard_normal((B, H, d_h))
+    kc = g.standard_normal((B, H, d_h))
+    vc = g.standard_normal((B, H, d_h))
+    return pos, bt, kp, vp, k_raw, v_raw, q, kc, vc
+
+
+@pytest.mark.parametrize("base", [0.0, 10000.0])
+def test_full_cache_equals_sdpa(base):
+    """The uncompressed baseline is ordinary attention over tokens 0..i (torch
+    SDPA in fp64 on the CPU, keys rotated by the independent complex form)."""
+    P = 16
+    pos, bt, kp, vp, k_raw, v_raw, q, kc, vc = _full_cache_case(31, P=P, base=base)
+    got = O.full_cache_decode(kp, vp, bt, pos, q, kc, vc, page_size=P, rope_base=base)
+    for b, i in enumerate(pos):
+        k_all = np.concatenate([k_raw[b, :i], kc[b][None]])
+        v_all = np.concatenate([v_raw[b, :i], vc[b][None]])
+        np.testing.assert_allclose(got[b], _sdpa_reference(k_all, v_all, q[b], int(i), base), atol=1e-12)
+
+
+def test_full_cache_equals_window_over_whole_context():
+    """With a window covering the whole context, the compressed path's exact
+    part sees the same tokens: textbook_decode then equals the baseline."""
+    P, base = 16, 10000.0
+    pos, bt, kp, vp, k_raw, v_raw, q, kc, vc = _full_cache_case(32, P=P, base=base)
+    W = int(pos.max())
+    B, H, d_h = q.shape
+    rk = np.full((B, W + 1, H, d_h), np.nan)
+    rv = np.full((B, W + 1, H, d_h), np.nan)
+    for b, i in enumerate(pos):
+        K, V = O.gather_kv_cache(kp, vp, bt, b, int(i), page_size=P)
+        rk[b, : int(i)] = K
+        rv[b, : int(i)] = V
+    sK = [np.zeros((0, 1, 4))] * B
+    sV = [np.zeros((0, 1, 4))] * B
+    A = np.zeros((H, d_h, 4))
+    Bv = np.zeros((H, 4, d_h))
+    want = O.textbook_decode(sK, sV, pos, q, kc, vc, rk, rv, A, Bv, window=W, rope_base=base)
+    got = O.full_cache_decode(kp, vp, bt, pos, q, kc, vc, page_size=P, rope_base=base)
+    np.testing.assert_allclose(got, want, atol=1e-13)
+
+
+def test_full_cache_brute_force():
+    """Pure-Python loops with math.exp on a tiny case (RoPE off)."""
+    P = 4
+    d_h = 4
+    pos, bt, kp, vp, k_raw, v_raw, q, kc, vc = _full_cache_case(33, B=2, H=2, d_h=d_h, P=P, positions=(5, 2),
+                                                               base=0.0)
+    got = O.full_cache_decode(kp, vp, bt, pos, q, kc, vc, page_size=P)
+    for b, i in enumerate(pos):
+        for h in range(2):
+            keys = [list(k_raw[b, j, h]) for j in range(i)] + [list(kc[b, h])]
+            vals = [list(v_raw[b, j, h]) for j in range(i)] + [list(vc[b, h])]
+            s = [sum(q[b, h, e] * k[e] for e in range(d_h)) / math.sqrt(d_h) for k in keys]
+            mx = max(s)
+            w = [math.exp(x - mx) for x in s]
+            want = [sum(w[j] * vals[j][e] for j in range(len(w))) / sum(w) for e in range(d_h)]
+            np.testing.assert_allclose(got[b, h], want, atol=1e-12)
+
+
+def test_kv_cache_update_page_slot_rotation():
+    bt = np.array([[7, 3, 9], [1, 2, 0]])
+    pos = np.array([20, 5])
+    kc = np.ones((2, 1, 4))
+    page, slot, k, v = O.kv_cache_update(pos, kc, 3 * kc, bt, page_size=16, rope_base=500.0)
+    assert list(page) == [3, 1] and list(slot) == [4, 5]
+    np.testing.assert_allclose(k[0, 0], _complex_rope(np.ones(4), 20, 500.0), atol=1e-14)
+    np.testing.assert_array_equal(v, 3 * kc)
