@@ -50,6 +50,24 @@ class LlaDecodeArgs(ctypes.Structure):
                 ("scan_events", ctypes.c_void_p)]
 
 
+class LlaKvDesc(ctypes.Structure):
+    _fields_ = [("n_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("rope_base", ctypes.c_float), ("dtype", ctypes.c_int32)]
+
+
+class LlaKvCache(ctypes.Structure):
+    _fields_ = [("k_pages", ctypes.c_void_p), ("v_pages", ctypes.c_void_p),
+                ("block_table", ctypes.c_void_p), ("max_pages_per_seq", ctypes.c_int32)]
+
+
+class LlaFullDecodeArgs(ctypes.Structure):
+    _fields_ = [("max_pos_hint", ctypes.c_int32), ("splits", ctypes.c_int32),
+                ("flags", ctypes.c_int32), ("pos", ctypes.c_void_p), ("q", ctypes.c_void_p),
+                ("k_cur", ctypes.c_void_p), ("v_cur", ctypes.c_void_p), ("out", ctypes.c_void_p),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("scan_events", ctypes.c_void_p)]
+
+
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run compressed_cross_loop_amd/build.py "
                       "(or __graft_entry__.build()) first")
@@ -72,6 +90,13 @@ lib.lla_decode_workspace_bytes.argtypes = [_P(LlaSetDesc), ctypes.c_int32, ctype
 lib.lla_decode_plan_splits.restype = ctypes.c_int32
 lib.lla_decode_plan_splits.argtypes = [_P(LlaSetDesc), ctypes.c_int32, ctypes.c_int32,
                                        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+lib.lla_decode_full_cache.restype = ctypes.c_int
+lib.lla_decode_full_cache.argtypes = [_P(LlaKvDesc), _P(LlaKvCache), ctypes.c_int32, _P(LlaFullDecodeArgs),
+                                      ctypes.c_void_p]
+lib.lla_full_decode_workspace_bytes.restype = ctypes.c_size_t
+lib.lla_full_decode_workspace_bytes.argtypes = [_P(LlaKvDesc), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+lib.lla_full_decode_plan_splits.restype = ctypes.c_int32
+lib.lla_full_decode_plan_splits.argtypes = [_P(LlaKvDesc), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
 lib.lla_decode_scan_kernel.restype = ctypes.c_char_p
 lib.lla_decode_scan_kernel.argtypes = [_P(LlaSetDesc), ctypes.c_int32, ctypes.c_int32]
 lib.lla_bytes_per_token.restype = ctypes.c_size_t
@@ -199,6 +224,45 @@ def lla_decode_absorbed(desc, st, batch, args, stream=None):
 
 def hla_decode_windowed(desc, st, batch, args, stream=None):
     _decode(lib.hla_decode_windowed, desc, st, batch, args, stream)
+
+
+# ---------------------------------------------------------------- full cache
+def kv_desc(*, n_heads, head_dim, page_size=64, rope_base=0.0, dtype=LLA_BF16):
+    if isinstance(dtype, torch.dtype):
+        dtype = _DTYPES[dtype]
+    return LlaKvDesc(n_heads, head_dim, page_size, rope_base, dtype)
+
+
+def kv_cache(k_pages, v_pages, block_table, max_pages_per_seq=None):
+    if max_pages_per_seq is None:
+        max_pages_per_seq = block_table.shape[-1]
+    c = LlaKvCache(_ptr(k_pages), _ptr(v_pages), _ptr(block_table), int(max_pages_per_seq))
+    c._keep = (k_pages, v_pages, block_table)   # raw pointers: keep the tensors alive with it
+    return c
+
+
+def full_decode_args(*, pos, q, k_cur, v_cur, out, workspace, max_pos_hint, splits=0, flags=0,
+                     scan_events=None):
+    ws_bytes = 0 if workspace is None or isinstance(workspace, int) else \
+        workspace.numel() * workspace.element_size()
+    ev = ctypes.cast(scan_events, ctypes.c_void_p) if scan_events is not None else None
+    args = LlaFullDecodeArgs(int(max_pos_hint), splits, flags, _ptr(pos), _ptr(q), _ptr(k_cur),
+                             _ptr(v_cur), _ptr(out), _ptr(workspace), ws_bytes, ev)
+    args._keep = (pos, q, k_cur, v_cur, out, workspace)
+    return args
+
+
+def lla_decode_full_cache(desc, cache, batch, args, stream=None):
+    _check(lib.lla_decode_full_cache(ctypes.byref(desc), ctypes.byref(cache), batch, ctypes.byref(args),
+                                     _stream(stream)))
+
+
+def lla_full_decode_workspace_bytes(desc, batch, max_pos, splits=0):
+    return lib.lla_full_decode_workspace_bytes(ctypes.byref(desc), batch, max_pos, splits)
+
+
+def lla_full_decode_plan_splits(desc, batch, max_pos, splits=0):
+    return lib.lla_full_decode_plan_splits(ctypes.byref(desc), batch, max_pos, splits)
 
 
 def torch_dtype(desc):

@@ -169,6 +169,36 @@ size_t decode_ws_bytes(const lla_set_desc& d, int batch, int max_pos, int window
 
 lla_status hip_status(hipError_t e) { return e == hipSuccess ? LLA_OK : LLA_ERR_HIP; }
 
+// ---------------------------------------------------------------- full cache
+lla_status check_kv_desc(const lla_kv_desc* d) {
+  if (!d) return LLA_ERR_INVALID_ARGUMENT;
+  if (d->n_heads <= 0 || d->head_dim <= 0 || (d->head_dim & 1)) return LLA_ERR_INVALID_ARGUMENT;
+  if (d->page_size <= 0 || d->page_size % 8) return LLA_ERR_INVALID_ARGUMENT;
+  if (d->dtype != LLA_F32 && d->dtype != LLA_BF16) return LLA_ERR_INVALID_ARGUMENT;
+  if (!(d->rope_base >= 0.f) || !std::isfinite(d->rope_base)) return LLA_ERR_INVALID_ARGUMENT;
+  if (d->head_dim != 64 && d->head_dim != 128) return LLA_ERR_UNSUPPORTED;
+  return LLA_OK;
+}
+
+Plan full_plan(const lla_kv_desc& d, int batch, int max_pos, int splits) {
+  const int hpb = full_scan_heads_per_block(d.head_dim);
+  return make_plan(batch, max_pos, 0, splits, (d.n_heads + hpb - 1) / hpb);
+}
+
+struct FullWs {
+  size_t part_ml, part_o, total;
+};
+
+FullWs full_ws_layout(const lla_kv_desc& d, int B, int S) {
+  FullWs w{};
+  const size_t H = d.n_heads;
+  w.part_ml = 0;
+  w.part_o = up256((size_t)B * S * H * 2 * 4);
+  w.total = up256(w.part_o + (size_t)B * S * H * d.head_dim * 4);
+  return w;
+}
+
+
 lla_status decode(const lla_set_desc* d, const lla_store* st, int32_t batch,
                   const lla_decode_args* a, lla_stream_t stream, int entry) {
   // entry: 0 reconstruct, 1 absorbed (LLA-D), 2 HLA windowed
@@ -330,6 +360,62 @@ int32_t lla_decode_plan_splits(const lla_set_desc* desc, int32_t batch, int32_t 
 const char* lla_decode_scan_kernel(const lla_set_desc* desc, int32_t entry, int32_t flags) {
   if (check_desc(desc) != LLA_OK || entry < 0 || entry > 2 || (flags & ~LLA_FLAG_GENERIC)) return nullptr;
   return scan_kernel_name(*desc, entry != 0, flags);
+}
+
+size_t lla_full_decode_workspace_bytes(const lla_kv_desc* desc, int32_t batch, int32_t max_pos,
+                                       int32_t splits) {
+  if (check_kv_desc(desc) != LLA_OK || batch <= 0 || max_pos < 0 || splits < 0) return 0;
+  return full_ws_layout(*desc, batch, full_plan(*desc, batch, max_pos, splits).S).total;
+}
+
+int32_t lla_full_decode_plan_splits(const lla_kv_desc* desc, int32_t batch, int32_t max_pos,
+                                    int32_t splits) {
+  if (check_kv_desc(desc) != LLA_OK || batch <= 0 || max_pos < 0 || splits < 0) return 0;
+  return full_plan(*desc, batch, max_pos, splits).S;
+}
+
+lla_status lla_decode_full_cache(const lla_kv_desc* d, const lla_kv_cache* c, int32_t batch,
+                                 const lla_full_decode_args* a, lla_stream_t stream) {
+  lla_status r = check_kv_desc(d);
+  if (r != LLA_OK) return r;
+  if (!c || !c->k_pages || !c->v_pages || !c->block_table || c->max_pages_per_seq <= 0)
+    return LLA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(c->k_pages) || !aligned16(c->v_pages)) return LLA_ERR_INVALID_ARGUMENT;
+  if (batch <= 0 || !a) return LLA_ERR_INVALID_ARGUMENT;
+  if (a->max_pos_hint < 0 || a->splits < 0 || a->flags != 0) return LLA_ERR_INVALID_ARGUMENT;
+  const void* ptrs[] = {a->pos, a->q, a->k_cur, a->v_cur, a->out};
+  for (const void* p : ptrs)
+    if (!p || !aligned16(p)) return LLA_ERR_INVALID_ARGUMENT;
+  const Plan plan = full_plan(*d, batch, a->max_pos_hint, a->splits);
+  const FullWs w = full_ws_layout(*d, batch, plan.S);
+  if (!a->workspace || a->workspace_bytes < w.total) return LLA_ERR_WORKSPACE_TOO_SMALL;
+  if (!aligned16(a->workspace)) return LLA_ERR_INVALID_ARGUMENT;
+  char* ws = static_cast<char*>(a->workspace);
+
+  FullParams f{};
+  f.B = batch; f.H = d->n_heads; f.dh = d->head_dim; f.P = d->page_size; f.S = plan.S;
+  f.chunk = plan.chunk; f.max_pages = c->max_pages_per_seq; f.bf16 = d->dtype == LLA_BF16;
+  f.rope_base = d->rope_base;
+  f.scale = (float)(1.4426950408889634 / std::sqrt((double)d->head_dim));
+  f.pos = a->pos; f.bt = c->block_table; f.k_pages = c->k_pages; f.v_pages = c->v_pages;
+  f.q = a->q; f.k_cur = a->k_cur; f.v_cur = a->v_cur;
+  f.part_ml = reinterpret_cast<float*>(ws + w.part_ml);
+  f.part_o = reinterpret_cast<float*>(ws + w.part_o);
+
+  // the merge: head-space partials, no window part
+  DecodeParams p{};
+  p.B = batch; p.H = d->n_heads; p.dh = d->head_dim; p.S = plan.S; p.WS = 0; p.Dp = d->head_dim;
+  p.mode = kReconstruct; p.bf16 = f.bf16;
+  p.part_ml = f.part_ml; p.part_o = f.part_o; p.out = a->out;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipEvent_t* ev = static_cast<hipEvent_t*>(a->scan_events);
+  hipError_t e = hipSuccess;
+  if (ev) e = hipEventRecord(ev[0], s);
+  if (e == hipSuccess) e = launch_full_scan(f, s);
+  if (e == hipSuccess && ev) e = hipEventRecord(ev[1], s);
+  if (e == hipSuccess) e = launch_combine(p, s);
+  return hip_status(e);
 }
 
 size_t lla_bytes_per_token(const lla_set_desc* desc) {

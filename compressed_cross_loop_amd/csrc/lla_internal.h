@@ -61,6 +61,23 @@ struct WriterParams {
   int32_t ksplit;
 };
 
+// full-cache (uncompressed) decode scan
+struct FullParams {
+  int32_t B, H, dh, P, S, chunk, max_pages, bf16;
+  float rope_base, scale;
+  const int32_t* pos;
+  const int32_t* bt;
+  void* k_pages;
+  void* v_pages;
+  const void* q;
+  const void* k_cur;
+  const void* v_cur;
+  float* part_ml;   // [B][S][H][2]
+  float* part_o;    // [B][S][H][dh]
+};
+int full_scan_heads_per_block(int dh);
+hipError_t launch_full_scan(const FullParams& p, hipStream_t s);
+
 hipError_t launch_qmap(const DecodeParams& p, bool want_qlat, hipStream_t s);
 hipError_t launch_window(const DecodeParams& p, hipStream_t s);
 hipError_t launch_scan_absorbed_generic(const DecodeParams& p, hipStream_t s);

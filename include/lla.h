@@ -243,6 +243,76 @@ size_t lla_bytes_per_token(const lla_set_desc* desc);
 const char* lla_status_string(lla_status status);
 int32_t lla_abi_version(void);
 
+/*
+ * ---------------------------------------------------------------------------
+ * Uncompressed (full-cache) looped decode: the baseline the codec replaces.
+ * Every loop keeps exact keys and values of every token ([HLA] "Key
+ * Problem": 2 T d numbers per token per layer, 768 KiB per token on the
+ * Ouro-1.4B shape in bf16), paged like the latent store.
+ * ---------------------------------------------------------------------------
+ *   n_heads, head_dim   H, d_h (d_h in {64, 128})
+ *   page_size           P tokens per page, a positive multiple of 8
+ *   rope_base           0 = no rotary embedding; keys are stored rotated
+ *   dtype               storage dtype of the cache and the activations
+ */
+typedef struct {
+  int32_t n_heads;
+  int32_t head_dim;
+  int32_t page_size;
+  float rope_base;
+  lla_dtype dtype;
+} lla_kv_desc;
+
+/* Exact cache of one (layer, loop): token j of sequence b lives in page
+ * block_table[b][j / P], slot j % P; a page is [P][H][d_h] (all heads of a
+ * token contiguous), keys post-rotation.  Device pointers, 16-byte aligned. */
+typedef struct {
+  void* k_pages;
+  void* v_pages;
+  const int32_t* block_table;   /* [batch][max_pages_per_seq] */
+  int32_t max_pages_per_seq;
+} lla_kv_cache;
+
+/*   max_pos_hint, splits, scan_events   as in lla_decode_args
+ *   flags         must be 0
+ *   pos           [batch] current positions i (tokens 0..i-1 are cached)
+ *   q, k_cur, v_cur  [batch][H][d_h], q and k_cur before rotation
+ *   out           [batch][H][d_h]
+ *   workspace     lla_full_decode_workspace_bytes() bytes, contents irrelevant */
+typedef struct {
+  int32_t max_pos_hint;
+  int32_t splits;
+  int32_t flags;
+  const int32_t* pos;
+  const void* q;
+  const void* k_cur;
+  const void* v_cur;
+  void* out;
+  void* workspace;
+  size_t workspace_bytes;
+  void* scan_events;
+} lla_full_decode_args;
+
+/*
+ * One decode call of the uncompressed model for one (layer, loop): writes
+ * R_i k_cur and v_cur at position i of the cache, then
+ * o = softmax(q' K^T / sqrt(d_h)) V over tokens 0..i with q' = R_i q.
+ * Errors as for the latent entry points (validation before any launch).
+ */
+lla_status lla_decode_full_cache(const lla_kv_desc* desc, const lla_kv_cache* cache,
+                                 int32_t batch, const lla_full_decode_args* args,
+                                 lla_stream_t stream);
+
+/* Workspace bytes lla_decode_full_cache needs (splits 0 = automatic); 0 on
+ * invalid arguments. */
+size_t lla_full_decode_workspace_bytes(const lla_kv_desc* desc, int32_t batch,
+                                       int32_t max_pos, int32_t splits);
+
+/* Context splits the planner uses for a full-cache decode; 0 on invalid
+ * arguments. */
+int32_t lla_full_decode_plan_splits(const lla_kv_desc* desc, int32_t batch, int32_t max_pos,
+                                    int32_t splits);
+
 #ifdef __cplusplus
 }
 #endif

@@ -186,6 +186,46 @@ def writer_inputs(seed: int, *, batch: int, n_tok: int, n_loops: int, groups: in
                         pos=torch.from_numpy(pos))
 
 
+@dataclass
+class KvCacheInputs:
+    """One full-cache decode call's inputs (CPU tensors): k_pages, v_pages
+    [n_pages, P, H, d_h] with every slot a call must not read (positions >= i
+    of each sequence, spare pages) set to NaN; block_table [B, max_pages];
+    pos [B]; q, k_cur, v_cur [B, H, d_h]."""
+    page_size: int
+    k_pages: torch.Tensor
+    v_pages: torch.Tensor
+    block_table: torch.Tensor
+    pos: torch.Tensor
+    q: torch.Tensor
+    k_cur: torch.Tensor
+    v_cur: torch.Tensor
+
+
+def kv_cache_inputs(seed: int, *, batch: int, heads: int, head_dim: int, positions, dtype: str,
+                    page_size: int = 64, spare_pages: int = 2, kv_std: float = 1.0) -> KvCacheInputs:
+    """Cached keys / values ~ N(0, kv_std^2), q, k_cur, v_cur ~ N(0, 1); the
+    cache holds tokens 0..i-1 of each sequence; the page of position i exists."""
+    g = rng(seed)
+    pos = np.asarray(positions, dtype=np.int64).reshape(batch)
+    pps = int(pos.max()) // page_size + 1
+    bt, n_pages = block_table(g, batch, pps, spare_pages)
+    kp = g.standard_normal((n_pages, page_size, heads, head_dim)) * kv_std
+    vp = g.standard_normal((n_pages, page_size, heads, head_dim)) * kv_std
+    valid = np.zeros((n_pages, page_size), dtype=bool)
+    for b in range(batch):
+        j = np.arange(int(pos[b]))
+        valid[bt[b, j // page_size], j % page_size] = True
+    kp[~valid] = np.nan
+    vp[~valid] = np.nan
+    q = g.standard_normal((batch, heads, head_dim))
+    kc = g.standard_normal((batch, heads, head_dim)) * kv_std
+    vc = g.standard_normal((batch, heads, head_dim)) * kv_std
+    return KvCacheInputs(page_size=page_size, k_pages=as_stored(kp, dtype), v_pages=as_stored(vp, dtype),
+                         block_table=torch.from_numpy(bt), pos=torch.from_numpy(pos.astype(np.int32)),
+                         q=as_stored(q, dtype), k_cur=as_stored(kc, dtype), v_cur=as_stored(vc, dtype))
+
+
 def device_normal(shape, dtype: str, seed: int, std: float = 1.0,
                   device: str = "cuda") -> torch.Tensor:
     """N(0, std^2) filled on the device from a seeded torch generator."""

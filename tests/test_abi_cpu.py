@@ -198,3 +198,57 @@ def test_scan_kernel_query():
     bad = desc(B.LLA_BF16, 1, 16, 512, 128)
     bad.head_dim = 0
     assert B.lla_decode_scan_kernel(bad, 0) is None
+
+
+def _kv(**kw):
+    base = dict(n_heads=16, head_dim=128, page_size=64, rope_base=10000.0, dtype=B.LLA_BF16)
+    base.update(kw)
+    return B.kv_desc(**base)
+
+
+def _full_call(desc=None, cache="ok", batch=2, **kw):
+    d = desc if desc is not None else _kv()
+    c = B.LlaKvCache(FAKE, FAKE, FAKE, 4) if cache == "ok" else cache
+    a = dict(max_pos_hint=100, splits=0, flags=0, pos=FAKE, q=FAKE, k_cur=FAKE, v_cur=FAKE, out=FAKE,
+             workspace=FAKE, workspace_bytes=1 << 40, scan_events=None)
+    a.update(kw)
+    args = B.LlaFullDecodeArgs(*[a[f] for f, _ in B.LlaFullDecodeArgs._fields_])
+    return B.lib.lla_decode_full_cache(ctypes.byref(d) if d is not None else None,
+                                       ctypes.byref(c) if c is not None else None, batch,
+                                       ctypes.byref(args), None)
+
+
+@pytest.mark.parametrize("bad, want", [
+    (dict(head_dim=96), B.LLA_ERR_UNSUPPORTED),
+    (dict(head_dim=0), B.LLA_ERR_INVALID_ARGUMENT),
+    (dict(n_heads=0), B.LLA_ERR_INVALID_ARGUMENT),
+    (dict(page_size=12), B.LLA_ERR_INVALID_ARGUMENT),
+    (dict(rope_base=-1.0), B.LLA_ERR_INVALID_ARGUMENT),
+    (dict(dtype=7), B.LLA_ERR_INVALID_ARGUMENT),
+])
+def test_full_cache_descriptor_errors(bad, want):
+    assert _full_call(desc=_kv(**bad)) == want
+    assert B.lla_full_decode_workspace_bytes(_kv(**bad), 2, 100) == 0
+
+
+@pytest.mark.parametrize("kw, want", [
+    (dict(flags=1), B.LLA_ERR_INVALID_ARGUMENT),
+    (dict(q=None), B.LLA_ERR_INVALID_ARGUMENT),
+    (dict(out=FAKE + 4), B.LLA_ERR_INVALID_ARGUMENT),
+    (dict(splits=-1), B.LLA_ERR_INVALID_ARGUMENT),
+    (dict(workspace_bytes=16), B.LLA_ERR_WORKSPACE_TOO_SMALL),
+    (dict(workspace=None), B.LLA_ERR_WORKSPACE_TOO_SMALL),
+])
+def test_full_cache_argument_errors(kw, want):
+    assert _full_call(**kw) == want
+
+
+def test_full_cache_null_structs_and_plan():
+    assert _full_call(cache=None) == B.LLA_ERR_INVALID_ARGUMENT
+    assert _full_call(cache=B.LlaKvCache(FAKE, None, FAKE, 4)) == B.LLA_ERR_INVALID_ARGUMENT
+    assert _full_call(cache=B.LlaKvCache(FAKE, FAKE, FAKE, 0)) == B.LLA_ERR_INVALID_ARGUMENT
+    assert _full_call(batch=0) == B.LLA_ERR_INVALID_ARGUMENT
+    d = _kv()
+    assert B.lla_full_decode_plan_splits(d, 1, 10) == 1
+    assert B.lla_full_decode_plan_splits(d, 32, 4095, splits=5) == 5
+    assert B.lla_full_decode_workspace_bytes(d, 32, 4095, 4) > B.lla_full_decode_workspace_bytes(d, 8, 4095, 4) > 0
