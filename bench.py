@@ -36,8 +36,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--splits", type=int, default=0)
-    ap.add_argument("--entry", choices=["auto", "hla", "absorbed", "reconstruct"], default="auto",
-                    help="decode entry point (auto: hla for HLA workloads, reconstruct for LLA ones)")
+    ap.add_argument("--entry", choices=["auto", "hla", "absorbed", "reconstruct", "full"], default="auto",
+                    help="decode entry point (auto: hla for HLA workloads, reconstruct for LLA ones; "
+                         "full: the uncompressed per-loop cache at the workload's attention shape)")
+    ap.add_argument("--batch", type=int, default=0, help="override the workload's batch (0 = workload's)")
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = workload's)")
     ap.add_argument("--no-graph", action="store_true",
                     help="launch every kernel eagerly instead of replaying the step as one HIP graph")
@@ -180,6 +182,96 @@ class DecodeStep:
         return total, per_call
 
 
+class FullStep:
+    """Every buffer of one decode step of the uncompressed model: one exact
+    paged K/V cache per (layer, loop), the same attention shape and context as
+    the workload.  The decode call appends the current token itself."""
+
+    def __init__(self, w, splits=0, seed=0):
+        import torch
+        from compressed_cross_loop_amd import binding as B
+        from synth import gen
+        self.torch, self.B, self.w = torch, B, w
+        dev = "cuda"
+        dt = gen.TORCH_DTYPE[w.dtype]
+        L, T, H, dh, Bt, P = w.layers, w.loops, w.heads, w.head_dim, w.batch, w.page_size
+        self.i = w.context - 1
+        ppseq = -(-w.context // P)
+        self.desc = B.kv_desc(n_heads=H, head_dim=dh, page_size=P, rope_base=w.rope_base,
+                              dtype=B.LLA_BF16 if w.dtype == "bf16" else B.LLA_F32)
+        n_pages = Bt * ppseq
+        need = L * T * 2 * n_pages * P * H * dh * (2 if w.dtype == "bf16" else 4)
+        free = torch.cuda.mem_get_info()[0]
+        if need > 0.97 * free:
+            raise MemoryError(f"the exact per-loop cache of {L} layers x {T} loops at batch {Bt}, context "
+                              f"{w.context} needs {need / 2**30:.1f} GiB; {free / 2**30:.1f} GiB of HBM is free")
+        bt = torch.from_numpy(gen.block_table(gen.rng(seed, 78), Bt, ppseq)[0]).to(dev)
+        self.pos = torch.full((Bt,), self.i, dtype=torch.int32, device=dev)
+        self.ws = torch.empty(B.lla_full_decode_workspace_bytes(self.desc, Bt, self.i, splits), dtype=torch.uint8,
+                              device=dev)
+        self.calls = []
+        for t in range(1, T + 1):
+            for l in range(L):
+                sd = seed * 100000 + 1000 * t + 10 * l
+                kp = gen.device_normal((n_pages, P, H, dh), w.dtype, sd + 4)
+                vp = gen.device_normal((n_pages, P, H, dh), w.dtype, sd + 5)
+                q = gen.device_normal((Bt, H, dh), w.dtype, sd + 1)
+                kc = gen.device_normal((Bt, H, dh), w.dtype, sd + 2)
+                vc = gen.device_normal((Bt, H, dh), w.dtype, sd + 3)
+                out = torch.empty((Bt, H, dh), dtype=dt, device=dev)
+                args = B.full_decode_args(pos=self.pos, q=q, k_cur=kc, v_cur=vc, out=out, workspace=self.ws,
+                                          max_pos_hint=self.i, splits=splits)
+                self.calls.append((t, 0, l, self.desc, B.kv_cache(kp, vp, bt), args, (kp, vp, q, kc, vc, out)))
+        self.entry_name = "full"
+        self.entry = B.lla_decode_full_cache
+        torch.cuda.synchronize()
+
+    def step(self):
+        for (t, k, l, desc, cache, args, _) in self.calls:
+            self.entry(desc, cache, self.w.batch, args)
+
+    def step_bytes(self):
+        """Algorithmic HBM bytes: every call reads the cached K and V of tokens
+        0..i-1 and moves q, k_cur, v_cur, out and the appended K/V row."""
+        w = self.w
+        e = 2 if w.dtype == "bf16" else 4
+        kv = w.batch * self.i * w.heads * w.head_dim * 2 * e
+        act = w.batch * w.heads * w.head_dim * e * 6
+        flop = 2 * 2 * w.batch * self.i * w.heads * w.head_dim
+        return len(self.calls) * (kv + act), {0: (kv, kv + act, flop)}
+
+
+def cpu_baseline_full(w, budget_s, seed=0):
+    """The fp64 oracle's full_cache_decode on whole sequences at the same
+    shape, on the host cores, scaled to decode tokens/s of the full step."""
+    import threadpoolctl
+    import oracle as O
+    from synth import gen
+    H, dh, P = w.heads, w.head_dim, w.page_size
+    i = w.context - 1
+    g = gen.rng(seed, 992)
+    nps = -(-w.context // P)
+    kp = g.standard_normal((nps, P, H, dh)).astype(np.float32).astype(np.float64)
+    vp = g.standard_normal((nps, P, H, dh)).astype(np.float32).astype(np.float64)
+    bt = np.arange(nps)[None]
+    q, kc, vc = (g.standard_normal((1, H, dh)) for _ in range(3))
+    n, t0 = 0, time.perf_counter()
+    while True:
+        O.full_cache_decode(kp, vp, bt, [i], q, kc, vc, page_size=P, rope_base=w.rope_base)
+        n += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    t_call = (time.perf_counter() - t0) / n
+    info = threadpoolctl.threadpool_info()
+    blas_threads = max([d.get("num_threads", 1) for d in info] or [1])
+    return {
+        "value": 1.0 / (w.layers * w.loops * t_call), "unit": "tokens/s", "cores": int(blas_threads),
+        "host_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
+        "sample": (f"oracle full_cache_decode (fp64 numpy) on {n} whole sequences ({t_call * 1e3:.1f} ms/seq/call) "
+                   f"in {time.perf_counter() - t0:.1f} s, scaled to {w.layers} layers x {w.loops} loops per token"),
+    }
+
+
 def cpu_baseline(w, budget_s, seed=0, entry="hla"):
     """The fp64 oracle form that checks the timed entry point (absorbed_decode
     for the absorbed/HLA read, textbook_decode for reconstruct-on-read), timed
@@ -304,7 +396,17 @@ def main():
     hip = Hip()
     if a.layers:
         w = w.with_(layers=a.layers)
-    st = DecodeStep(w, splits=a.splits, entry=a.entry)
+    if a.batch:
+        w = w.with_(batch=a.batch, name=f"{w.name}@b{a.batch}")
+    if a.entry == "full":
+        w = w.with_(name=f"full-cache-L{w.layers}xT{w.loops}-h{w.heads}x{w.head_dim}-b{w.batch}-ctx{w.context}")
+        try:
+            st = FullStep(w, splits=a.splits)
+        except MemoryError as err:
+            print(json.dumps({"error": str(err), "config": {"workload": w.name}}))
+            sys.exit(3)
+    else:
+        st = DecodeStep(w, splits=a.splits, entry=a.entry)
     stream = torch.cuda.current_stream().cuda_stream
     for _ in range(max(1, a.warmup)):
         st.step()
@@ -333,7 +435,7 @@ def main():
     step_bytes, per_call = st.step_bytes()
 
     # dominant kernel: the scan of the set serving the most loops, timed live
-    main_k = max(per_call, key=lambda k: per_call[k][0] * w.sets[k].n_loops)
+    main_k = 0 if st.entry_name == "full" else max(per_call, key=lambda k: per_call[k][0] * w.sets[k].n_loops)
     evs = []
     rsteps = max(2, min(a.steps, 5))
     for _ in range(rsteps):
@@ -347,11 +449,15 @@ def main():
     torch.cuda.synchronize()
     scan_ms = float(np.mean([hip.elapsed_ms(ctypes.c_void_p(p[0]), ctypes.c_void_p(p[1])) for p in evs]))
     scan_bytes, _, scan_flop = per_call[main_k]
-    s_main = w.sets[main_k]
-    scan_bytes += w.batch * w.heads * s_main.r_k * (2 if w.dtype == "bf16" else 4) \
-        if st.entry_name != "reconstruct" else 0
-    main_desc = next(c[3] for c in st.calls if c[1] == main_k)
-    kname = st.B.lla_decode_scan_kernel(main_desc, ENTRY_CODE[st.entry_name])
+    if st.entry_name == "full":
+        kname, loops_served = "k_full_scan", (1, w.loops)
+    else:
+        s_main = w.sets[main_k]
+        loops_served = (s_main.loop_first, s_main.loop_last)
+        scan_bytes += w.batch * w.heads * s_main.r_k * (2 if w.dtype == "bf16" else 4) \
+            if st.entry_name != "reconstruct" else 0
+        main_desc = next(c[3] for c in st.calls if c[1] == main_k)
+        kname = st.B.lla_decode_scan_kernel(main_desc, ENTRY_CODE[st.entry_name])
     reconstruct_mfma_bound = st.entry_name == "reconstruct" and scan_flop / scan_bytes > 312
     if reconstruct_mfma_bound:
         roof = {"bound": "mfma", "achieved": scan_flop / (scan_ms * 1e-3) / 1e12, "peak": 2500.0,
@@ -361,7 +467,8 @@ def main():
                 "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = measured_traffic(w.name) if kname == "k_scan_absorbed_mfma" else None
-    roof.update({"kernel": f"{kname} (set serving loops {s_main.loop_first}..{s_main.loop_last})",
+    roof.update({"kernel": f"{kname} (" + ("every (layer, loop) call" if st.entry_name == "full" else
+                                         f"set serving loops {loops_served[0]}..{loops_served[1]}") + ")",
                  "avg_launch_ms": scan_ms, "bytes_per_launch": scan_bytes, "flop_per_launch": scan_flop})
 
     gbs = step_bytes / (ms * 1e-3) / 1e9
@@ -372,15 +479,17 @@ def main():
         "config": {"workload": w.name, "entry": st.entry_name, "layers": w.layers, "loops": w.loops,
                    "batch": w.batch, "context": w.context, "window": w.window, "heads": w.heads,
                    "head_dim": w.head_dim,
-                   "sets": [dict(loops=[s.loop_first, s.loop_last], groups=s.groups, r_k=s.r_k,
-                                 r_v=s.r_v) for s in w.sets],
+                   "sets": ("exact K/V per loop" if st.entry_name == "full" else
+                            [dict(loops=[s.loop_first, s.loop_last], groups=s.groups, r_k=s.r_k, r_v=s.r_v)
+                             for s in w.sets]),
                    "splits": a.splits or "auto", "launch": "eager" if a.no_graph else "hip_graph"},
         "step_bytes": step_bytes, "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
         "stream_copy_gbs": stream_copy_gbs(),
         "roofline": roof,
     }
     if not a.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds, entry=st.entry_name)
+        rec["cpu_baseline"] = cpu_baseline_full(w, a.cpu_seconds) if st.entry_name == "full" else \
+            cpu_baseline(w, a.cpu_seconds, entry=st.entry_name)
     print(json.dumps(rec))
 
 
