@@ -42,6 +42,9 @@ Readings taken where the pages are silent (each also applies to the GPU path):
   R15 The uncompressed (full-cache) baseline keeps one exact paged cache per
       (layer, loop), pages of [P][H][d_h] with rotated keys; a decode call
       appends the current token and attends to tokens 0..i.
+  R16 fp8 latent storage: OCP e4m3 codes, round to nearest even, saturating
+      at 448, one fp32 scale per token, group and part = max|x| / 448 of that
+      part (1 when the part is all zero).
 """
 import numpy as np
 
@@ -123,6 +126,111 @@ def gather_latents(pages: np.ndarray, block_table: np.ndarray, b: int, n_tok: in
     vo = store_value_offset(page[:, None, None], g[None, :, None], slot[:, None, None],
                             np.arange(r_v)[None, None, :], **kw)
     return flat[ko], flat[vo]
+
+
+# ----------------------------------------------------------------------------
+# fp8 latent storage ([HLA] "Summary (Overview)": the codec combines with
+# quantization; reading R16): OCP e4m3 codes with one fp32 scale per token,
+# group and part (key, value).  A stored latent element is decode(code) *
+# scale.
+# ----------------------------------------------------------------------------
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(code):
+    """Values of OCP e4m3 codes: sign, 4 exponent bits (bias 7), 3 mantissa
+    bits; exponent field 0 is subnormal (m/8 * 2^-6); S.1111.111 is NaN; no
+    infinities."""
+    c = np.asarray(code, dtype=np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 7
+    v = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * 2.0 ** (e - 7.0))
+    v = np.where((e == 15) & (m == 7), np.nan, v)
+    return sign * v
+
+
+def e4m3_encode(x):
+    """Round to nearest, ties to even, onto the e4m3 grid, saturating at
+    +-448 (reading R16).  The grid spacing in the binade [2^e, 2^(e+1)) is
+    2^(e-3) for e >= -6; below 2^-6 it is the subnormal spacing 2^-9."""
+    x = np.asarray(x, dtype=np.float64)
+    neg = np.signbit(x)
+    a = np.minimum(np.abs(x), E4M3_MAX)
+    e = np.clip(np.floor(np.log2(np.where(a > 0, a, 1.0))), -6, 8)
+    quantum = 2.0 ** (e - 3)
+    v = np.minimum(np.round(a / quantum) * quantum, E4M3_MAX)   # np.round: halves to even
+    normal = v >= 2.0 ** -6
+    ev = np.floor(np.log2(np.where(normal, v, 1.0)))
+    code = np.where(normal, ((ev + 7) * 8 + (v / 2.0 ** ev * 8 - 8)), v / 2.0 ** -9)
+    return (code.astype(np.int64) | np.where(neg, 0x80, 0)).astype(np.uint8)
+
+
+def fp8_quantize_rows(rows):
+    """Per row (last axis): scale = max|x| / 448 (1 for an all-zero row) and
+    codes = e4m3_encode(x / scale).  Returns (codes uint8, scale)."""
+    rows = np.asarray(rows, dtype=np.float64)
+    amax = np.max(np.abs(rows), axis=-1)
+    scale = np.where(amax > 0, amax / E4M3_MAX, 1.0)
+    return e4m3_encode(rows / scale[..., None]), scale
+
+
+def fp8_tile_bytes(r_k: int, r_v: int) -> int:
+    """Bytes of one fp8 tile (16 tokens, one group): key codes, value codes,
+    16 key scales and 16 value scales (fp32)."""
+    return TILE * (r_k + r_v) + 2 * TILE * 4
+
+
+def _fp8_tile_base(page, group, slot, groups, page_size, r_k, r_v):
+    tb = fp8_tile_bytes(r_k, r_v)
+    return (page * groups + group) * (page_size // TILE) * tb + (slot // TILE) * tb
+
+
+def fp8_key_offset(page, group, slot, dim, *, groups, page_size, r_k, r_v):
+    """Byte offset of the key code of element `dim` (token-major rows of r_k
+    codes, as in the 16-bit store)."""
+    page, group, slot, dim = (np.asarray(a, dtype=np.int64) for a in (page, group, slot, dim))
+    return _fp8_tile_base(page, group, slot, groups, page_size, r_k, r_v) + (slot % TILE) * r_k + dim
+
+
+def fp8_value_offset(page, group, slot, dim, *, groups, page_size, r_k, r_v):
+    """Byte offset of the value code of element `dim`: the value block is
+    r_v/64 quads of four 16-dimension sub-blocks; inside a quad, dimension row
+    m (dim % 16) holds, for each group of 4 tokens, the 4 tokens of each of the
+    4 sub-blocks: [m][token // 4][sub-block][token % 4]."""
+    page, group, slot, dim = (np.asarray(a, dtype=np.int64) for a in (page, group, slot, dim))
+    t = slot % TILE
+    return (_fp8_tile_base(page, group, slot, groups, page_size, r_k, r_v) + TILE * r_k + (dim // 64) * 1024
+            + (dim % TILE) * 64 + (t // 4) * 16 + ((dim // TILE) % 4) * 4 + t % 4)
+
+
+def fp8_scale_offset(page, group, slot, part, *, groups, page_size, r_k, r_v):
+    """Byte offset of the fp32 scale of the token's key (part 0) or value
+    (part 1) codes."""
+    page, group, slot, part = (np.asarray(a, dtype=np.int64) for a in (page, group, slot, part))
+    return (_fp8_tile_base(page, group, slot, groups, page_size, r_k, r_v) + TILE * (r_k + r_v)
+            + part * TILE * 4 + (slot % TILE) * 4)
+
+
+def gather_latents_fp8(pages: np.ndarray, block_table: np.ndarray, b: int, n_tok: int, *,
+                       groups, page_size, r_k, r_v):
+    """Decoded key and value latents (code value x scale, fp64) of tokens
+    0..n_tok-1 of sequence b from an fp8 store given as raw bytes."""
+    raw = np.asarray(pages).reshape(-1).view(np.uint8)
+    j = np.arange(n_tok)
+    page = np.asarray(block_table)[b, j // page_size].astype(np.int64)
+    slot = j % page_size
+    kw = dict(groups=groups, page_size=page_size, r_k=r_k, r_v=r_v)
+    g = np.arange(groups)
+    P3, G3, S3 = page[:, None, None], g[None, :, None], slot[:, None, None]
+    kc = raw[fp8_key_offset(P3, G3, S3, np.arange(r_k)[None, None, :], **kw)]
+    vc = raw[fp8_value_offset(P3, G3, S3, np.arange(r_v)[None, None, :], **kw)]
+
+    def scale(part):
+        off = fp8_scale_offset(page[:, None], g[None, :], slot[:, None], part, **kw)
+        by = raw[off[..., None] + np.arange(4)].astype(np.uint8)
+        return by.copy().view(np.float32)[..., 0].astype(np.float64)
+    return e4m3_decode(kc) * scale(0)[..., None], e4m3_decode(vc) * scale(1)[..., None]
 
 
 # ----------------------------------------------------------------------------

@@ -553,3 +553,114 @@ def test_kv_cache_update_page_slot_rotation():
     assert list(page) == [3, 1] and list(slot) == [4, 5]
     np.testing.assert_allclose(k[0, 0], _complex_rope(np.ones(4), 20, 500.0), atol=1e-14)
     np.testing.assert_array_equal(v, 3 * kc)
+
+
+# ---------------------------------------------------------------- fp8 latent storage
+def _e4m3_brute(x):
+    """Nearest finite e4m3 value by exhaustive search over all codes, ties to
+    the even mantissa; |x| > 448 saturates."""
+    codes = [c for c in range(256) if not ((c >> 3) & 0xF == 15 and c & 7 == 7)]
+    vals = O.e4m3_decode(codes)
+    out = []
+    for v in np.atleast_1d(x):
+        v = float(np.clip(v, -448.0, 448.0))
+        d = np.abs(vals - v)
+        best = [codes[k] for k in np.flatnonzero(d == d.min())]
+        if len(best) > 1:                       # a tie: the even mantissa wins
+            best = [c for c in best if (c & 1) == 0] or best
+        if len(best) > 1:                       # +0 / -0: keep the sign of v
+            best = [c for c in best if bool(c & 0x80) == (math.copysign(1.0, v) < 0)]
+        out.append(best[0])
+    return np.array(out, dtype=np.uint8)
+
+
+def test_e4m3_closed_forms():
+    assert list(O.e4m3_decode([0x38, 0x7E, 0x08, 0x01, 0x07, 0xC0, 0x00])) == \
+        [1.0, 448.0, 2.0 ** -6, 2.0 ** -9, 7 * 2.0 ** -9, -2.0, 0.0]
+    assert np.isnan(O.e4m3_decode([0x7F, 0xFF])).all()
+    cases = {1.0: 0x38, 1.0625: 0x38, 1.1875: 0x3A, 500.0: 0x7E, -1e9: 0xFE, 2.0 ** -10: 0x00,
+             3 * 2.0 ** -10: 0x02, 15.5: 0x58, 447.0: 0x7E, -2.0: 0xC0, 0.0: 0x00}
+    for x, c in cases.items():
+        assert int(O.e4m3_encode(x)) == c, (x, hex(int(O.e4m3_encode(x))), hex(c))
+
+
+def test_e4m3_encode_is_nearest_even_by_brute_force():
+    g = gen.rng(51)
+    x = np.exp2(g.uniform(-12, 9.2, 4000)) * np.where(g.random(4000) < 0.5, -1, 1)
+    vals = np.sort(O.e4m3_decode(np.arange(0, 0x7F)))
+    mids = (vals[1:] + vals[:-1]) / 2          # every tie point between neighbours
+    x = np.concatenate([x, mids, -mids, vals, [449.0, 463.9, 480.0, 1e6]])
+    np.testing.assert_array_equal(O.e4m3_encode(x), _e4m3_brute(x))
+
+
+def test_e4m3_round_trip_of_every_finite_code():
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F and c != 0x80])
+    np.testing.assert_array_equal(O.e4m3_encode(O.e4m3_decode(codes)), codes)
+
+
+def test_fp8_store_layout_is_a_bijection():
+    G, P, r_k, r_v = 2, 32, 64, 128
+    kw = dict(groups=G, page_size=P, r_k=r_k, r_v=r_v)
+    pg, g, sl = np.meshgrid(np.arange(2), np.arange(G), np.arange(P), indexing="ij")
+    pg, g, sl = pg[..., None], g[..., None], sl[..., None]
+    k = O.fp8_key_offset(pg, g, sl, np.arange(r_k), **kw).ravel()
+    v = O.fp8_value_offset(pg, g, sl, np.arange(r_v), **kw).ravel()
+    sc = np.concatenate([O.fp8_scale_offset(pg, g, sl, part, **kw).ravel()[:, None] + np.arange(4)
+                         for part in (0, 1)]).ravel()
+    allb = np.sort(np.concatenate([k, v, sc]))
+    np.testing.assert_array_equal(allb, np.arange(2 * G * (P // 16) * O.fp8_tile_bytes(r_k, r_v)))
+
+
+def test_fp8_worked_offsets():
+    """Offsets worked by hand for G = 1, P = 32, r_k = r_v = 64: a tile is
+    16 * 128 code bytes + 64 bytes of key scales + 64 bytes of value scales =
+    2176 bytes; slot 19 is token 3 of the page's second tile."""
+    kw = dict(groups=1, page_size=32, r_k=64, r_v=64)
+    assert O.fp8_tile_bytes(64, 64) == 2176
+    assert int(O.fp8_key_offset(1, 0, 19, 10, **kw)) == 2 * 2176 + 2176 + 3 * 64 + 10
+    assert int(O.fp8_scale_offset(1, 0, 19, 0, **kw)) == 2 * 2176 + 2176 + 2048 + 3 * 4
+    assert int(O.fp8_scale_offset(1, 0, 19, 1, **kw)) == 2 * 2176 + 2176 + 2048 + 64 + 3 * 4
+    # value dim 37 = quad 0, sub-block 2, row 5; token 3 = group 0, position 3
+    assert int(O.fp8_value_offset(1, 0, 19, 37, **kw)) == 2 * 2176 + 2176 + 1024 + 5 * 64 + 0 * 16 + 2 * 4 + 3
+
+
+def test_fp8_value_fragment_is_contiguous():
+    """Worked offsets: dims 16 j + m of quad 0 for tokens 4 kg .. 4 kg + 3 are
+    the 16 bytes at m * 64 + kg * 16 after the key rows (j = 0..3)."""
+    kw = dict(groups=1, page_size=16, r_k=64, r_v=64)
+    m, kg = 5, 2
+    offs = [int(O.fp8_value_offset(0, 0, 4 * kg + t, 16 * j + m, **kw)) for j in range(4) for t in range(4)]
+    assert offs == list(range(16 * 64 + m * 64 + kg * 16, 16 * 64 + m * 64 + kg * 16 + 16))
+
+
+def test_fp8_quantize_rows_and_gather():
+    """Scale = max|x| / 448; each element's error is at most half a grid step
+    of its binade times the scale; gather decodes through the block table."""
+    g = gen.rng(52)
+    G, P, r_k, r_v = 2, 16, 64, 64
+    n = 20
+    c = g.standard_normal((n, G, r_k + r_v)) * 3
+    c[3, 1, :r_k] = 0.0                                   # an all-zero part
+    kq, ks = O.fp8_quantize_rows(c[..., :r_k])
+    vq, vs = O.fp8_quantize_rows(c[..., r_k:])
+    np.testing.assert_allclose(ks[0, 0], np.abs(c[0, 0, :r_k]).max() / 448.0, rtol=1e-15)
+    assert ks[3, 1] == 1.0 and not kq[3, 1].any()
+    for q, sc, x in ((kq, ks, c[..., :r_k]), (vq, vs, c[..., r_k:])):
+        y = x / sc[..., None]
+        step = 2.0 ** (np.clip(np.floor(np.log2(np.maximum(np.abs(y), 2.0 ** -9))), -6, 8) - 3)
+        assert np.all(np.abs(O.e4m3_decode(q) - y) <= step / 2 + 1e-12)
+    bt = np.array([[1, 0]])
+    nbytes = 2 * G * (P // 16) * O.fp8_tile_bytes(r_k, r_v)
+    raw = np.zeros(nbytes, dtype=np.uint8)
+    kw = dict(groups=G, page_size=P, r_k=r_k, r_v=r_v)
+    for j in range(n):
+        for gg in range(G):
+            pg, sl = bt[0, j // P], j % P
+            raw[O.fp8_key_offset(pg, gg, sl, np.arange(r_k), **kw)] = kq[j, gg]
+            raw[O.fp8_value_offset(pg, gg, sl, np.arange(r_v), **kw)] = vq[j, gg]
+            for part, sc in ((0, ks), (1, vs)):
+                o = int(O.fp8_scale_offset(pg, gg, sl, part, **kw))
+                raw[o:o + 4] = np.frombuffer(np.float32(sc[j, gg]).tobytes(), dtype=np.uint8)
+    sK, sV = O.gather_latents_fp8(raw, bt, 0, n, **kw)
+    np.testing.assert_allclose(sK, O.e4m3_decode(kq) * ks.astype(np.float32)[..., None], rtol=0, atol=0)
+    np.testing.assert_allclose(sV, O.e4m3_decode(vq) * vs.astype(np.float32)[..., None], rtol=0, atol=0)
