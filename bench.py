@@ -41,6 +41,8 @@ def parse():
                          "full: the uncompressed per-loop cache at the workload's attention shape)")
     ap.add_argument("--batch", type=int, default=0, help="override the workload's batch (0 = workload's)")
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = workload's)")
+    ap.add_argument("--latent-fp8", action="store_true",
+                    help="store latents as OCP e4m3 codes with per-token scales (absorbed / HLA entries)")
     ap.add_argument("--no-graph", action="store_true",
                     help="launch every kernel eagerly instead of replaying the step as one HIP graph")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -78,10 +80,28 @@ class Hip:
 ENTRY_CODE = {"reconstruct": 0, "absorbed": 1, "hla": 2}
 
 
+def fp8_store_fill(desc, n_pages, seed, std):
+    """A synthetic fp8 latent store on the device: codes uniform over the
+    finite e4m3 codes (0x7F and 0xFF, the NaNs, moved one code down) and
+    per-token scales std * 4/448 * U[0.5, 1.5) (a part's max |x| near 4 std
+    maps to the top code) in the 128 scale bytes that end each 16-token tile."""
+    import torch
+    from compressed_cross_loop_amd import binding as B
+    R = desc.r_k + desc.r_v
+    tb = 16 * R + 128
+    g = torch.Generator(device="cuda")
+    g.manual_seed(int(seed))
+    raw = torch.empty(B.store_bytes(desc, n_pages), dtype=torch.uint8, device="cuda").random_(0, 256, generator=g)
+    raw.sub_(((raw & 0x7F) == 0x7F).to(torch.uint8))
+    scales = raw.view(-1, tb)[:, 16 * R:].view(torch.float32)
+    scales.uniform_(0.5, 1.5, generator=g).mul_(std * 4.0 / 448.0)
+    return raw
+
+
 class DecodeStep:
     """Every buffer of one decode step (all layers, all loops), on the GPU."""
 
-    def __init__(self, w, splits=0, seed=0, entry="auto"):
+    def __init__(self, w, splits=0, seed=0, entry="auto", fp8=False):
         import torch
         from compressed_cross_loop_amd import binding as B
         from synth import gen
@@ -96,14 +116,17 @@ class DecodeStep:
             desc = B.set_desc(n_heads=H, head_dim=dh, groups=s.groups, r_k=s.r_k, r_v=s.r_v,
                               loop_first=s.loop_first, loop_last=s.loop_last, page_size=P,
                               rope_baked=w.rope_baked, rope_base=w.rope_base,
-                              dtype=B.LLA_BF16 if w.dtype == "bf16" else B.LLA_F32)
+                              dtype=B.LLA_BF16 if w.dtype == "bf16" else B.LLA_F32, latent_fp8=int(fp8))
             g = gen.rng(seed, 77, k)
             bt = torch.from_numpy(gen.block_table(g, Bt, ppseq)[0]).to(dev)
             n_pages = Bt * ppseq
             row = s.groups * P * (s.r_k + s.r_v)
             std = float(np.sqrt(s.n_loops))  # latents of |L_s| unit-variance loops
-            pages = [gen.device_normal((n_pages, row), w.dtype, seed * 1000 + 10 * l + k, std)
-                     for l in range(L)]
+            if fp8:
+                pages = [fp8_store_fill(desc, n_pages, seed * 1000 + 10 * l + k, std) for l in range(L)]
+            else:
+                pages = [gen.device_normal((n_pages, row), w.dtype, seed * 1000 + 10 * l + k, std)
+                         for l in range(L)]
             enc = [gen.device_normal((s.n_loops, s.groups, s.r_k + s.r_v, s.d_in), w.dtype,
                                      seed * 1000 + 500 + 10 * l + k, 1.0 / np.sqrt(s.d_in)) for l in range(L)]
             x = [gen.device_normal((Bt, 1, s.n_loops, s.groups, s.d_in), w.dtype,
@@ -116,6 +139,7 @@ class DecodeStep:
         self.ws = torch.empty(ws, dtype=torch.uint8, device=dev)
         wws = max(B.lla_write_workspace_bytes(st["desc"], Bt, 1, st["spec"].d_in) for st in self.sets)
         self.wws = torch.empty(max(wws, 256), dtype=torch.uint8, device=dev)
+        self.fp8 = fp8
         self.calls = []   # (loop, set index, desc, store, args)
         self.outs = []
         for t in range(1, T + 1):
@@ -161,9 +185,12 @@ class DecodeStep:
         n_win = min(W, self.i)
         total = 0
         per_call = {}
+        # one token's latent of one group: r_k + r_v elements, or as fp8 codes
+        # one byte each plus the two fp32 scales
+        row = (lambda s: s.r_k + s.r_v + 8) if self.fp8 else (lambda s: (s.r_k + s.r_v) * e)
         for (t, k, l, *_rest) in self.calls:
             s = w.sets[k]
-            lat = Bt * n_lat * s.groups * (s.r_k + s.r_v) * e
+            lat = Bt * n_lat * s.groups * row(s)
             win = Bt * n_win * H * dh * 2 * e
             act = Bt * H * dh * e * (4 + 2)          # q, k_cur, v_cur, out + ring slot write (K, V)
             maps = H * dh * (s.r_k + s.r_v) * e
@@ -178,7 +205,7 @@ class DecodeStep:
         for s in w.sets:
             total += w.layers * (Bt * s.n_loops * s.groups * s.d_in * e
                                  + s.n_loops * s.groups * (s.r_k + s.r_v) * s.d_in * e
-                                 + Bt * s.groups * (s.r_k + s.r_v) * e)
+                                 + Bt * s.groups * row(s))
         return total, per_call
 
 
@@ -272,11 +299,12 @@ def cpu_baseline_full(w, budget_s, seed=0):
     }
 
 
-def cpu_baseline(w, budget_s, seed=0, entry="hla"):
+def cpu_baseline(w, budget_s, seed=0, entry="hla", fp8=False):
     """The fp64 oracle form that checks the timed entry point (absorbed_decode
     for the absorbed/HLA read, textbook_decode for reconstruct-on-read), timed
     on the host cores on whole sequences of the same workload, scaled to
-    decode tokens/s of the full step."""
+    decode tokens/s of the full step.  With fp8 latents the oracle gathers
+    and dequantizes the codes (gather_latents_fp8) before the same decode."""
     import threadpoolctl
     import oracle as O
     from synth import gen
@@ -287,8 +315,15 @@ def cpu_baseline(w, budget_s, seed=0, entry="hla"):
     per_set = []
     for s in w.sets:
         nps = -(-w.context // P)
-        pages = (g.standard_normal((nps, s.groups * P * (s.r_k + s.r_v))) * np.sqrt(s.n_loops)) \
-            .astype(np.float32).astype(np.float64)
+        if fp8:
+            R = s.r_k + s.r_v
+            pages = g.integers(0, 256, size=(nps * s.groups * (P // 16), 16 * R + 128), dtype=np.uint8)
+            pages[(pages & 0x7F) == 0x7F] -= 1
+            sc = (g.uniform(0.5, 1.5, size=(pages.shape[0], 32)) * np.sqrt(s.n_loops) * 4 / 448).astype(np.float32)
+            pages[:, 16 * R:] = sc.view(np.uint8)
+        else:
+            pages = (g.standard_normal((nps, s.groups * P * (s.r_k + s.r_v))) * np.sqrt(s.n_loops)) \
+                .astype(np.float32).astype(np.float64)
         bt = np.arange(nps, dtype=np.int64)[None]
         q = g.standard_normal((1, H, dh))
         kc = g.standard_normal((1, H, dh))
@@ -301,7 +336,8 @@ def cpu_baseline(w, budget_s, seed=0, entry="hla"):
 
     def one_sequence(k):
         s, pages, bt, q, kc, vc, rk, rv, A, Bv = per_set[k]
-        sK, sV = O.gather_latents(pages, bt, 0, n_lat, groups=s.groups, page_size=P, r_k=s.r_k, r_v=s.r_v)
+        gather = O.gather_latents_fp8 if fp8 else O.gather_latents
+        sK, sV = gather(pages, bt, 0, n_lat, groups=s.groups, page_size=P, r_k=s.r_k, r_v=s.r_v)
         fn = O.textbook_decode if entry == "reconstruct" else O.absorbed_decode
         fn([sK], [sV], [i], q, kc, vc, rk, rv, A, Bv, window=W, rope_base=w.rope_base)
 
@@ -326,7 +362,8 @@ def cpu_baseline(w, budget_s, seed=0, entry="hla"):
     return {
         "value": 1.0 / t_seq_step, "unit": "tokens/s", "cores": int(blas_threads),
         "host_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
-        "sample": (f"oracle {'textbook' if entry == 'reconstruct' else 'absorbed'}_decode (fp64 numpy) "
+        "sample": (f"oracle {'gather_latents_fp8 + ' if fp8 else ''}"
+                   f"{'textbook' if entry == 'reconstruct' else 'absorbed'}_decode (fp64 numpy) "
                    f"on {n_done} whole sequences "
                    f"({', '.join(f'{t * 1e3:.1f} ms/seq/call set{k}' for k, t in enumerate(t_set))}) "
                    f"in {wall:.1f} s, scaled to {w.layers} layers x {w.loops} loops per token"),
@@ -406,7 +443,12 @@ def main():
             print(json.dumps({"error": str(err), "config": {"workload": w.name}}))
             sys.exit(3)
     else:
-        st = DecodeStep(w, splits=a.splits, entry=a.entry)
+        if a.latent_fp8:
+            if a.entry == "reconstruct" or (a.entry == "auto" and w.family != "hla") or w.dtype != "bf16":
+                print(json.dumps({"error": "fp8 latents serve the absorbed / HLA reads of bf16 workloads"}))
+                sys.exit(2)
+            w = w.with_(name=f"{w.name}-fp8")
+        st = DecodeStep(w, splits=a.splits, entry=a.entry, fp8=a.latent_fp8)
     stream = torch.cuda.current_stream().cuda_stream
     for _ in range(max(1, a.warmup)):
         st.step()
@@ -482,14 +524,15 @@ def main():
                    "sets": ("exact K/V per loop" if st.entry_name == "full" else
                             [dict(loops=[s.loop_first, s.loop_last], groups=s.groups, r_k=s.r_k, r_v=s.r_v)
                              for s in w.sets]),
-                   "splits": a.splits or "auto", "launch": "eager" if a.no_graph else "hip_graph"},
+                   "splits": a.splits or "auto", "launch": "eager" if a.no_graph else "hip_graph",
+                   "latents": "e4m3+scale" if getattr(st, "fp8", False) else w.dtype},
         "step_bytes": step_bytes, "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
         "stream_copy_gbs": stream_copy_gbs(),
         "roofline": roof,
     }
     if not a.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline_full(w, a.cpu_seconds) if st.entry_name == "full" else \
-            cpu_baseline(w, a.cpu_seconds, entry=st.entry_name)
+            cpu_baseline(w, a.cpu_seconds, entry=st.entry_name, fp8=getattr(st, "fp8", False))
     print(json.dumps(rec))
 
 

@@ -31,7 +31,7 @@ class LlaSetDesc(ctypes.Structure):
                 ("groups", ctypes.c_int32), ("r_k", ctypes.c_int32), ("r_v", ctypes.c_int32),
                 ("loop_first", ctypes.c_int32), ("loop_last", ctypes.c_int32),
                 ("page_size", ctypes.c_int32), ("rope_baked", ctypes.c_int32),
-                ("rope_base", ctypes.c_float), ("dtype", ctypes.c_int32)]
+                ("rope_base", ctypes.c_float), ("dtype", ctypes.c_int32), ("latent_fp8", ctypes.c_int32)]
 
 
 class LlaStore(ctypes.Structure):
@@ -106,7 +106,7 @@ lib.lla_status_string.argtypes = [ctypes.c_int]
 lib.lla_abi_version.restype = ctypes.c_int32
 lib.lla_abi_version.argtypes = []
 
-ABI_VERSION = 2   # include/lla.h LLA_ABI_VERSION this binding marshals for
+ABI_VERSION = 3   # include/lla.h LLA_ABI_VERSION this binding marshals for
 if lib.lla_abi_version() != ABI_VERSION:
     raise ImportError(f"{LIB_PATH} has ABI version {lib.lla_abi_version()}, the binding expects {ABI_VERSION}: "
                       "rebuild it (python -c 'import __graft_entry__ as g; g.build()')")
@@ -140,11 +140,19 @@ def _stream(stream):
 
 
 def set_desc(*, n_heads, head_dim, groups, r_k, r_v, loop_first, loop_last, page_size=64,
-             rope_baked=0, rope_base=0.0, dtype=LLA_BF16):
+             rope_baked=0, rope_base=0.0, dtype=LLA_BF16, latent_fp8=0):
     if isinstance(dtype, torch.dtype):
         dtype = _DTYPES[dtype]
     return LlaSetDesc(n_heads, head_dim, groups, r_k, r_v, loop_first, loop_last, page_size,
-                      rope_baked, rope_base, dtype)
+                      rope_baked, rope_base, dtype, latent_fp8)
+
+
+def store_bytes(desc, n_pages):
+    """Bytes of a latent store of n_pages pages for this set."""
+    G, P, R = desc.groups, desc.page_size, desc.r_k + desc.r_v
+    if desc.latent_fp8:
+        return n_pages * G * (P // 16) * (16 * R + 128)
+    return n_pages * G * P * R * (2 if desc.dtype == LLA_BF16 else 4)
 
 
 def store(pages, block_table, max_pages_per_seq=None):

@@ -173,8 +173,10 @@ __global__ __launch_bounds__(kThreads) void k_scan_absorbed_generic(DecodeParams
   float* o = sm + rk;          // [rv]
   __shared__ float sc[kChunk];
   __shared__ int64_t pg[kChunk];
+  __shared__ float kscale[kChunk], vscale[kChunk];   // fp8 stores: per-token scales
   const int s = blockIdx.x, b = blockIdx.y, h = blockIdx.z, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, g = h / p.hpg;
+  const uint8_t* bytes = static_cast<const uint8_t*>(p.pages);
   const int i = p.pos[b];
   const int n_lat = max(0, i - p.W);
   int t0, t1;
@@ -188,15 +190,27 @@ __global__ __launch_bounds__(kThreads) void k_scan_absorbed_generic(DecodeParams
   __syncthreads();
   for (int c0 = t0; c0 < t1; c0 += kChunk) {
     const int n = min(kChunk, t1 - c0);
-    if (tid < n) pg[tid] = bt[(c0 + tid) / P];
+    if (tid < n) {
+      pg[tid] = bt[(c0 + tid) / P];
+      if (p.fp8) {
+        const int slot = (c0 + tid) % P;
+        kscale[tid] = *reinterpret_cast<const float*>(bytes + scale_off8(pg[tid], g, slot, 0, G, P, rk, rv));
+        vscale[tid] = *reinterpret_cast<const float*>(bytes + scale_off8(pg[tid], g, slot, 1, G, P, rk, rv));
+      }
+    }
     __syncthreads();
     for (int t = wave; t < n; t += kThreads / 64) {
       const int slot = (c0 + t) % P;
-      const T* kr = pages + key_off(pg[t], g, slot, 0, G, P, R, rk);
       float acc = 0.f;
-      for (int k = lane; k < rk; k += 64) acc += ql[k] * to_f(kr[k]);
+      if (p.fp8) {
+        const uint8_t* kr = bytes + key_off8(pg[t], g, slot, 0, G, P, rk, rv);
+        for (int k = lane; k < rk; k += 64) acc += ql[k] * e4m3_to_f(kr[k]);
+      } else {
+        const T* kr = pages + key_off(pg[t], g, slot, 0, G, P, R, rk);
+        for (int k = lane; k < rk; k += 64) acc += ql[k] * to_f(kr[k]);
+      }
       acc = wave_sum(acc);
-      if (lane == 0) sc[t] = acc;
+      if (lane == 0) sc[t] = p.fp8 ? acc * kscale[t] : acc;
     }
     __syncthreads();
     float cm = -INFINITY;
@@ -211,7 +225,8 @@ __global__ __launch_bounds__(kThreads) void k_scan_absorbed_generic(DecodeParams
       float acc = o[k] * alpha;
       for (int t = 0; t < n; ++t) {
         const int slot = (c0 + t) % P;
-        acc += exp2f(sc[t] - mn) * to_f(pages[val_off(pg[t], g, slot, k, G, P, R, rk)]);
+        acc += p.fp8 ? exp2f(sc[t] - mn) * vscale[t] * e4m3_to_f(bytes[val_off8(pg[t], g, slot, k, G, P, rk, rv)])
+                     : exp2f(sc[t] - mn) * to_f(pages[val_off(pg[t], g, slot, k, G, P, R, rk)]);
       }
       o[k] = acc;
     }

@@ -29,6 +29,46 @@ __device__ __forceinline__ int64_t val_off(int64_t page, int g, int slot, int d,
   return tile_base(page, g, slot, G, P, R) + 16 * rk + (d >> 4) * 256 + (d & 15) * 16 + (slot & 15);
 }
 
+// fp8 latent store (byte offsets): a tile of 16 tokens of one group holds the
+// key codes (token-major rows of rk), the value codes (rv/64 quads of four
+// 16-dimension sub-blocks, inside a quad [dim % 16][token / 4][sub-block]
+// [token % 4], so that the 4 tokens x 4 sub-blocks a lane feeds to the value
+// MFMA are 16 contiguous bytes), then 16 fp32 key scales and 16 value scales.
+__device__ __forceinline__ int64_t tile_bytes8(int rk, int rv) { return 16 * (int64_t)(rk + rv) + 128; }
+__device__ __forceinline__ int64_t tile_base8(int64_t page, int g, int slot, int G, int P, int rk, int rv) {
+  return ((page * G + g) * (P / 16) + slot / 16) * tile_bytes8(rk, rv);
+}
+__device__ __forceinline__ int64_t key_off8(int64_t page, int g, int slot, int d, int G, int P, int rk, int rv) {
+  return tile_base8(page, g, slot, G, P, rk, rv) + (slot & 15) * rk + d;
+}
+__device__ __forceinline__ int64_t val_off8(int64_t page, int g, int slot, int d, int G, int P, int rk, int rv) {
+  const int t = slot & 15;
+  return tile_base8(page, g, slot, G, P, rk, rv) + 16 * rk + (d >> 6) * 1024 + (d & 15) * 64 + (t >> 2) * 16 +
+         ((d >> 4) & 3) * 4 + (t & 3);
+}
+__device__ __forceinline__ int64_t scale_off8(int64_t page, int g, int slot, int part, int G, int P, int rk,
+                                              int rv) {
+  return tile_base8(page, g, slot, G, P, rk, rv) + 16 * (int64_t)(rk + rv) + part * 64 + (slot & 15) * 4;
+}
+
+// OCP e4m3 code -> float on the gfx950 converter (exact: every e4m3 value is
+// a bf16 value)
+__device__ __forceinline__ float e4m3_to_f(uint32_t code) {
+  return static_cast<float>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(code, 1.0f, false)[0]);
+}
+// float -> OCP e4m3 code, round to nearest even, saturating at +-448.  In
+// the binade [2^e, 2^(e+1)) (e clipped below at -6, where the subnormals
+// share the spacing 2^-9) the grid spacing is 2^(e-3); n = rint(|y| / 2^(e-3))
+// is exact and lies in [0, 16], and the code is 8 (e + 7) + n - 8 (n = 16
+// carries into the next binade, n < 8 at e = -6 are the subnormals).
+__device__ __forceinline__ uint32_t f_to_e4m3(float y) {
+  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+  const float a = fminf(fabsf(y), 448.f);
+  const int e = max((int)((__float_as_uint(a) >> 23) & 0xFF) - 127, -6);
+  const int n = (int)rintf(ldexpf(a, 3 - e));
+  return sign | (uint32_t)(8 * e + 48 + n);
+}
+
 // Rotary angle p * theta_f, theta_f = base^(-2f/d_h).  theta_f and the
 // product are fp64 (positions reach 16K and beyond, where an fp32 angle would
 // be off by ~1e-3 rad); the product is reduced by whole turns in fp64 and

@@ -38,6 +38,9 @@ lla_status check_desc(const lla_set_desc* d) {
   if (d->rope_baked && d->r_k % d->head_dim) return LLA_ERR_UNSUPPORTED;
   if (d->head_dim > kMaxHeadDim) return LLA_ERR_UNSUPPORTED;
   if (d->r_k + d->r_v > kMaxLatent) return LLA_ERR_UNSUPPORTED;
+  if (d->latent_fp8 != 0 && d->latent_fp8 != 1) return LLA_ERR_INVALID_ARGUMENT;
+  if (d->latent_fp8 && d->dtype != LLA_BF16) return LLA_ERR_INVALID_ARGUMENT;
+  if (d->latent_fp8 && (d->r_k % 64 || d->r_v % 64)) return LLA_ERR_UNSUPPORTED;
   return LLA_OK;
 }
 
@@ -77,6 +80,7 @@ bool use_mfma_scan(const lla_set_desc& d, int flags) {
   p.rv = d.r_v;
   p.dh = d.head_dim;
   p.bf16 = 1;
+  p.fp8 = d.latent_fp8;
   return scan_absorbed_mfma_supports(p);
 }
 
@@ -213,6 +217,7 @@ lla_status decode(const lla_set_desc* d, const lla_store* st, int32_t batch,
   for (const void* p : ptrs)
     if (!p || !aligned16(p)) return LLA_ERR_INVALID_ARGUMENT;
   if (entry == 2 && d->groups != 1) return LLA_ERR_INVALID_ARGUMENT;
+  if (entry == 0 && d->latent_fp8) return LLA_ERR_UNSUPPORTED;   // fp8 latents: absorbed read only
   if (a->window > kMaxWindow) return LLA_ERR_UNSUPPORTED;
   if (d->rope_base > 0.f && !d->rope_baked) return LLA_ERR_UNSUPPORTED;
   const size_t need = decode_ws_bytes(*d, batch, a->max_pos_hint, a->window, a->splits);
@@ -233,6 +238,7 @@ lla_status decode(const lla_set_desc* d, const lla_store* st, int32_t batch,
   p.S = plan.S; p.chunk = plan.chunk; p.Dp = Dp; p.max_pages = st->max_pages_per_seq;
   p.mode = absorbed ? kAbsorbed : kReconstruct;
   p.bf16 = d->dtype == LLA_BF16;
+  p.fp8 = d->latent_fp8;
   p.rope_base = d->rope_base;
   p.scale = (float)(1.4426950408889634 / std::sqrt((double)d->head_dim));
   p.pos = a->pos; p.bt = st->block_table; p.pages = st->pages;
@@ -308,6 +314,7 @@ lla_status lla_write_latents(const lla_set_desc* desc, const lla_store* store, i
   p.d_in = d_in; p.P = desc->page_size; p.dh = desc->head_dim;
   p.max_pages = store->max_pages_per_seq;
   p.rope_baked = desc->rope_baked; p.bf16 = desc->dtype == LLA_BF16; p.rope_base = desc->rope_base;
+  p.fp8 = desc->latent_fp8;
   p.pos = pos; p.bt = store->block_table; p.pages = store->pages; p.x = x; p.enc = enc;
   p.acc = static_cast<float*>(workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -420,6 +427,7 @@ lla_status lla_decode_full_cache(const lla_kv_desc* d, const lla_kv_cache* c, in
 
 size_t lla_bytes_per_token(const lla_set_desc* desc) {
   if (check_desc(desc) != LLA_OK) return 0;
+  if (desc->latent_fp8) return (size_t)desc->groups * (desc->r_k + desc->r_v + 8);   // codes + 2 fp32 scales
   return (size_t)desc->groups * (desc->r_k + desc->r_v) * elem_bytes(*desc);
 }
 

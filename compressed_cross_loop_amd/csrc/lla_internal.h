@@ -20,6 +20,7 @@ struct DecodeParams {
   int32_t max_pages;
   int32_t mode;
   int32_t bf16;                   // storage dtype: 1 = bf16, 0 = fp32
+  int32_t fp8;                    // latents stored as e4m3 codes + per-token scales (bytes)
   int32_t need_qhead;             // a later kernel reads qhead (else the window
                                   // kernel rotates q itself)
   int32_t fuse_window;            // the matrix-core scan also does the exact
@@ -51,6 +52,7 @@ struct WriterParams {
   int32_t B, n_tok, n_loops, G, rk, rv, R, d_in, P, dh, max_pages;
   int32_t rope_baked;
   int32_t bf16;
+  int32_t fp8;                    // latents stored as e4m3 codes + per-token scales
   float rope_base;
   const int32_t* pos;
   const int32_t* bt;

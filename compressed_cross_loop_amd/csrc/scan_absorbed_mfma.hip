@@ -37,6 +37,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
@@ -48,17 +49,21 @@ template <int RK> struct Pipe { static constexpr int keys = 4, values = 4, unrol
 template <> struct Pipe<128> { static constexpr int keys = 4, values = 2, unroll = 4; };
 template <> struct Pipe<256> { static constexpr int keys = 3, values = 2, unroll = 6; };
 template <> struct Pipe<512> { static constexpr int keys = 2, values = 1, unroll = 2; };
+// fp8 tiles hold half the bytes (and registers) of bf16 ones: deeper
+template <int RK> struct Pipe8 { static constexpr int keys = 4, values = 4, unroll = 4; };
+template <> struct Pipe8<256> { static constexpr int keys = 4, values = 2, unroll = 4; };
+template <> struct Pipe8<512> { static constexpr int keys = 3, values = 2, unroll = 6; };
 
 template <int RK>
-__device__ __forceinline__ void load_keys(bf16x8 (&k)[RK / 32], const bf16* tile, int col, int grp) {
-  const bf16* kp = tile + col * RK + grp * 8;
+__device__ __forceinline__ void load_keys(bf16x8 (&k)[RK / 32], const char* tile_b, int col, int grp) {
+  const bf16* kp = reinterpret_cast<const bf16*>(tile_b) + col * RK + grp * 8;
 #pragma unroll
   for (int st = 0; st < RK / 32; ++st) k[st] = *reinterpret_cast<const bf16x8*>(kp + st * 32);
 }
 
 template <int RK, int RV>
-__device__ __forceinline__ void load_values(s16x4 (&v)[RV / 16], const bf16* tile, int col, int grp) {
-  const bf16* vp = tile + 16 * RK + col * 16 + grp * 4;
+__device__ __forceinline__ void load_values(s16x4 (&v)[RV / 16], const char* tile_b, int col, int grp) {
+  const bf16* vp = reinterpret_cast<const bf16*>(tile_b) + 16 * RK + col * 16 + grp * 4;
 #pragma unroll
   for (int vt = 0; vt < RV / 16; ++vt) v[vt] = *reinterpret_cast<const s16x4*>(vp + vt * 256);
 }
@@ -87,9 +92,9 @@ __device__ __forceinline__ f32x4 tile_scores(const bf16x8 (&k)[RK / 32], const b
 
 // Online-softmax update for one tile; returns the bf16 probabilities in the
 // B-operand layout of the value MFMA.
-template <int RV>
+template <int RV, bool SCALED = false>
 __device__ __forceinline__ s16x4 tile_softmax(f32x4 sc, f32x4 (&acc)[RV / 16], float& m, float& lsum,
-                                              int nvalid, int grp) {
+                                              int nvalid, int grp, f32x4 vscale = f32x4{1.f, 1.f, 1.f, 1.f}) {
   if (nvalid < 16) {
 #pragma unroll
     for (int r = 0; r < 4; ++r)
@@ -112,7 +117,12 @@ __device__ __forceinline__ s16x4 tile_softmax(f32x4 sc, f32x4 (&acc)[RV / 16], f
   }
   s16x4 pb;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) pb[r] = bf16_bits(pr[r]);
+  for (int r = 0; r < 4; ++r) {
+    // fp8 values carry a per-token scale; a token past the end may hold
+    // anything (even NaN) there: select, not multiply
+    const float w = SCALED ? ((4 * grp + r < nvalid) ? pr[r] * vscale[r] : 0.f) : pr[r];
+    pb[r] = bf16_bits(w);
+  }
   return pb;
 }
 
@@ -130,6 +140,85 @@ __device__ __forceinline__ void tile_values(s16x4 (&v)[RV / 16], s16x4 pb, f32x4
 #pragma unroll
   for (int vt = 0; vt < RV / 16; ++vt)
     acc[vt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v[vt], pb, acc[vt], 0, 0, 0);
+}
+
+// ---- fp8 latents (OCP e4m3 codes + per-token fp32 scales, the byte tile
+// layout of device_common.h).  Key codes are read 16 per lane (dims
+// 64u + 16 grp ..); the score MFMA sums over its 32 K values, so the two
+// 8-dim halves of a load feed two K steps, each against the q~ dims they hold.
+// Value codes: one 16-byte load per lane gives its 4 tokens of 4 sub-blocks.
+// Codes are converted exactly to bf16 (gfx950 converter), the MFMAs are the
+// bf16 ones; scales multiply the scores (key) and the probabilities (value).
+template <int RK> struct Keys8 {
+  u32x4 v[RK / 64];
+  f32x4 s;   // key scales of tokens 4 grp .. 4 grp + 3
+};
+template <int RV> struct Vals8 {
+  u32x4 v[RV / 64];
+  f32x4 s;   // value scales of tokens 4 grp .. 4 grp + 3
+};
+
+template <int RK, int RV>
+__device__ __forceinline__ void load_keys8(Keys8<RK>& k, const char* tile, int col, int grp) {
+  const char* kp = tile + col * RK + grp * 16;
+#pragma unroll
+  for (int u = 0; u < RK / 64; ++u) k.v[u] = *reinterpret_cast<const u32x4*>(kp + u * 64);
+  k.s = *reinterpret_cast<const f32x4*>(tile + 16 * (RK + RV) + 16 * grp);
+}
+
+template <int RK, int RV>
+__device__ __forceinline__ void load_values8(Vals8<RV>& v, const char* tile, int col, int grp) {
+  const char* vp = tile + 16 * RK + col * 64 + grp * 16;
+#pragma unroll
+  for (int q = 0; q < RV / 64; ++q) v.v[q] = *reinterpret_cast<const u32x4*>(vp + q * 1024);
+  v.s = *reinterpret_cast<const f32x4*>(tile + 16 * (RK + RV) + 64 + 16 * grp);
+}
+
+// two bf16 from the e4m3 codes in bytes (2 hi, 2 hi + 1) of w
+template <bool HI>
+__device__ __forceinline__ unsigned e4m3x2_to_bf16x2(unsigned w) {
+  return __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+
+template <int RK, int RV>
+__device__ __forceinline__ f32x4 tile_scores8(const Keys8<RK>& k, const bf16* qcol, int grp) {
+  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int u = 0; u < RK / 64; ++u) {
+    u32x4 a0, a1;   // dims 64u + 16 grp + 0..7 and + 8..15, as bf16 pairs
+    a0[0] = e4m3x2_to_bf16x2<false>(k.v[u][0]);
+    a0[1] = e4m3x2_to_bf16x2<true>(k.v[u][0]);
+    a0[2] = e4m3x2_to_bf16x2<false>(k.v[u][1]);
+    a0[3] = e4m3x2_to_bf16x2<true>(k.v[u][1]);
+    a1[0] = e4m3x2_to_bf16x2<false>(k.v[u][2]);
+    a1[1] = e4m3x2_to_bf16x2<true>(k.v[u][2]);
+    a1[2] = e4m3x2_to_bf16x2<false>(k.v[u][3]);
+    a1[3] = e4m3x2_to_bf16x2<true>(k.v[u][3]);
+    const bf16x8 q0 = *reinterpret_cast<const bf16x8*>(qcol + 64 * u + 16 * grp);
+    const bf16x8 q1 = *reinterpret_cast<const bf16x8*>(qcol + 64 * u + 16 * grp + 8);
+    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0), q0, s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1), q1, s1, 0, 0, 0);
+  }
+  return (s0 + s1) * k.s;
+}
+
+template <int RV>
+__device__ __forceinline__ void tile_values8(const Vals8<RV>& v, s16x4 pb, f32x4 (&acc)[RV / 16], int nvalid,
+                                             int grp) {
+#pragma unroll
+  for (int q = 0; q < RV / 64; ++q)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      // sub-block 4q + j, tokens 4 grp .. 4 grp + 3 of this lane's dim row
+      unsigned w2[2] = {e4m3x2_to_bf16x2<false>(v.v[q][j]), e4m3x2_to_bf16x2<true>(v.v[q][j])};
+      s16x4 a = __builtin_bit_cast(s16x4, w2);
+      if (nvalid < 16) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (4 * grp + r >= nvalid) a[r] = 0;
+      }
+      acc[4 * q + j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb, acc[4 * q + j], 0, 0, 0);
+    }
 }
 
 // Exact tokens i-W <= j <= i of Eq. 4 (ring slots and the current token) for
@@ -272,7 +361,7 @@ __device__ void window_slice(const DecodeParams& p, int b, int slice, int g, con
   }
 }
 
-template <int RK, int RV>
+template <int RK, int RV, bool F8>
 __global__ __launch_bounds__(kThreads, 1) void k_scan_absorbed_mfma(DecodeParams p) {
   const int s = blockIdx.x, b = blockIdx.y, g = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -307,14 +396,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_scan_absorbed_mfma(DecodeParams
   for (int vt = 0; vt < RV / 16; ++vt) acc[vt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, lsum = 0.f;
 
-  const bf16* pages = static_cast<const bf16*>(p.pages);
+  const char* pages = static_cast<const char*>(p.pages);
   const int32_t* bt = p.bt + (int64_t)b * p.max_pages;
   const int R = RK + RV;
   const int ntiles = (t1 - t0 + 15) / 16;
-  auto tile_ptr = [&](int ti) -> const bf16* {
+  auto tile_ptr = [&](int ti) -> const char* {   // byte address of a 16-token tile
     const int j0 = t0 + ti * 16;
     const int64_t page = bt[j0 / P];
-    return pages + tile_base(page, g, j0 % P, G, P, R);
+    if constexpr (F8) return pages + tile_base8(page, g, j0 % P, G, P, RK, RV);
+    return pages + 2 * tile_base(page, g, j0 % P, G, P, R);
   };
   auto tile_valid = [&](int ti) -> int { return min(16, t1 - (t0 + ti * 16)); };
 
@@ -324,29 +414,60 @@ __global__ __launch_bounds__(kThreads, 1) void k_scan_absorbed_mfma(DecodeParams
   // rotate with the loop unrolled by lcm(NK, NV), so every index is static.
   // Refills are unconditional (clamped to the last tile, still cached) so no
   // register set has to survive a skipped refill.
-  constexpr int NK = Pipe<RK>::keys, NV = Pipe<RK>::values, UN = Pipe<RK>::unroll;
-  bf16x8 kb[NK][RK / 32];
-  s16x4 vb[NV][RV / 16];
-  int ti = wave;
-  if (ti < ntiles) {
+  if constexpr (!F8) {
+    constexpr int NK = Pipe<RK>::keys, NV = Pipe<RK>::values, UN = Pipe<RK>::unroll;
+    bf16x8 kb[NK][RK / 32];
+    s16x4 vb[NV][RV / 16];
+    int ti = wave;
+    if (ti < ntiles) {
 #pragma unroll
-    for (int u = 0; u < NK; ++u) load_keys<RK>(kb[u], tile_ptr(min(ti + u * kWaves, ntiles - 1)), col, grp);
+      for (int u = 0; u < NK; ++u) load_keys<RK>(kb[u], tile_ptr(min(ti + u * kWaves, ntiles - 1)), col, grp);
 #pragma unroll
-    for (int u = 0; u < NV; ++u)
-      load_values<RK, RV>(vb[u], tile_ptr(min(ti + u * kWaves, ntiles - 1)), col, grp);
-  }
-  while (ti < ntiles) {
+      for (int u = 0; u < NV; ++u)
+        load_values<RK, RV>(vb[u], tile_ptr(min(ti + u * kWaves, ntiles - 1)), col, grp);
+    }
+    while (ti < ntiles) {
 #pragma unroll
-    for (int u = 0; u < UN; ++u) {
-      const f32x4 sc = tile_scores<RK>(kb[u % NK], qrow);
-      __builtin_amdgcn_sched_barrier(0);   // keep each refill below its consumer
-      load_keys<RK>(kb[u % NK], tile_ptr(min(ti + NK * kWaves, ntiles - 1)), col, grp);
-      const s16x4 pb = tile_softmax<RV>(sc, acc, m, lsum, tile_valid(ti), grp);
-      tile_values<RV>(vb[u % NV], pb, acc, tile_valid(ti), grp);
-      __builtin_amdgcn_sched_barrier(0);
-      load_values<RK, RV>(vb[u % NV], tile_ptr(min(ti + NV * kWaves, ntiles - 1)), col, grp);
-      ti += kWaves;
-      if (ti >= ntiles) break;
+      for (int u = 0; u < UN; ++u) {
+        const f32x4 sc = tile_scores<RK>(kb[u % NK], qrow);
+        __builtin_amdgcn_sched_barrier(0);   // keep each refill below its consumer
+        load_keys<RK>(kb[u % NK], tile_ptr(min(ti + NK * kWaves, ntiles - 1)), col, grp);
+        const s16x4 pb = tile_softmax<RV>(sc, acc, m, lsum, tile_valid(ti), grp);
+        tile_values<RV>(vb[u % NV], pb, acc, tile_valid(ti), grp);
+        __builtin_amdgcn_sched_barrier(0);
+        load_values<RK, RV>(vb[u % NV], tile_ptr(min(ti + NV * kWaves, ntiles - 1)), col, grp);
+        ti += kWaves;
+        if (ti >= ntiles) break;
+      }
+    }
+  } else {
+    constexpr int NK = Pipe8<RK>::keys, NV = Pipe8<RK>::values, UN = Pipe8<RK>::unroll;
+    Keys8<RK> kb[NK];
+    Vals8<RV> vb[NV];
+    const bf16* qcol = &qs[col][0];
+    int ti = wave;
+    if (ti < ntiles) {
+#pragma unroll
+      for (int u = 0; u < NK; ++u)
+        load_keys8<RK, RV>(kb[u], tile_ptr(min(ti + u * kWaves, ntiles - 1)), col, grp);
+#pragma unroll
+      for (int u = 0; u < NV; ++u)
+        load_values8<RK, RV>(vb[u], tile_ptr(min(ti + u * kWaves, ntiles - 1)), col, grp);
+    }
+    while (ti < ntiles) {
+#pragma unroll
+      for (int u = 0; u < UN; ++u) {
+        f32x4 sc = tile_scores8<RK, RV>(kb[u % NK], qcol, grp);
+        __builtin_amdgcn_sched_barrier(0);
+        const f32x4 vs = vb[u % NV].s;
+        load_keys8<RK, RV>(kb[u % NK], tile_ptr(min(ti + NK * kWaves, ntiles - 1)), col, grp);
+        const s16x4 pb = tile_softmax<RV, true>(sc, acc, m, lsum, tile_valid(ti), grp, vs);
+        tile_values8<RV>(vb[u % NV], pb, acc, tile_valid(ti), grp);
+        __builtin_amdgcn_sched_barrier(0);
+        load_values8<RK, RV>(vb[u % NV], tile_ptr(min(ti + NV * kWaves, ntiles - 1)), col, grp);
+        ti += kWaves;
+        if (ti >= ntiles) break;
+      }
     }
   }
   lsum += __shfl_xor(lsum, 16);
@@ -407,7 +528,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_scan_absorbed_mfma(DecodeParams
 
 template <int RK, int RV>
 hipError_t launch_rk(const DecodeParams& p, hipStream_t st) {
-  hipLaunchKernelGGL((k_scan_absorbed_mfma<RK, RV>), dim3(p.S, p.B, p.G), dim3(kThreads), 0, st, p);
+  if (p.fp8) {
+    if constexpr (RK % 64 == 0)
+      hipLaunchKernelGGL((k_scan_absorbed_mfma<RK, RV, true>), dim3(p.S, p.B, p.G), dim3(kThreads), 0, st, p);
+    else
+      return hipErrorNotSupported;
+  } else {
+    hipLaunchKernelGGL((k_scan_absorbed_mfma<RK, RV, false>), dim3(p.S, p.B, p.G), dim3(kThreads), 0, st, p);
+  }
   return hipGetLastError();
 }
 
@@ -415,6 +543,7 @@ hipError_t launch_rk(const DecodeParams& p, hipStream_t st) {
 
 bool scan_absorbed_mfma_supports(const DecodeParams& p) {
   if (!p.bf16 || p.hpg > 16 || p.rk != p.rv) return false;
+  if (p.fp8 && p.rk % 64) return false;
   switch (p.rk) {
     case 32: case 64: case 128: case 256: case 512: return true;
     default: return false;

@@ -1,10 +1,12 @@
 // Latent writer ("Hybrid Latent Attention" summary, "Latent Writer", Eq. 2):
 // for each token and group, c = sum over the set's loops of E_t x_t in fp32,
 // the key part rotated by R~_p when the set bakes rotary embedding into its
-// key latents, then rounded to the storage dtype and scattered into the
-// paged store at (block_table[b][p/P], p % P).
+// key latents, then rounded to the storage dtype (or to e4m3 codes with
+// per-token scales) and scattered into the paged store at
+// (block_table[b][p/P], p % P).
 #include "device_common.h"
 #include "lla_internal.h"
+#include "writer_common.h"
 
 namespace lla {
 
@@ -12,37 +14,6 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kXChunk = 4096;   // input elements staged in LDS at a time
-
-// Rotate (if baked), round and store one finished latent held in LDS (fp32).
-template <typename T>
-__device__ void store_latent(const WriterParams& p, const float* c, int b, int n, int g) {
-  const int R = p.R, rk = p.rk, dh = p.dh, half = dh / 2;
-  const int pos = p.pos[(int64_t)b * p.n_tok + n];
-  const int64_t page = p.bt[(int64_t)b * p.max_pages + pos / p.P];
-  const int slot = pos % p.P;
-  T* pages = static_cast<T*>(p.pages);
-  for (int o = threadIdx.x; o < R; o += kThreads) {
-    float v = c[o];
-    int64_t off;
-    if (o < rk) {
-      if (p.rope_baked) {
-        const int f = o % dh;
-        float cs, sn;
-        if (f < half) {
-          rope_cs(p.rope_base, dh, f, pos, cs, sn);
-          v = c[o] * cs - c[o + half] * sn;
-        } else {
-          rope_cs(p.rope_base, dh, f - half, pos, cs, sn);
-          v = c[o - half] * sn + c[o] * cs;
-        }
-      }
-      off = key_off(page, g, slot, o, p.G, p.P, R, rk);
-    } else {
-      off = val_off(page, g, slot, o - rk, p.G, p.P, R, rk);
-    }
-    pages[off] = from_f<T>(v);
-  }
-}
 
 // One workgroup per (token, group): plain fp32 dot products.
 template <typename T>
@@ -72,7 +43,9 @@ __global__ __launch_bounds__(kThreads) void k_writer_generic(WriterParams p) {
     }
   }
   __syncthreads();
-  store_latent<T>(p, c, b, n, g);
+  const int pos = p.pos[(int64_t)b * p.n_tok + n];
+  const int64_t page = p.bt[(int64_t)b * p.max_pages + pos / p.P];
+  finish_latent<T, kThreads>(p, c, nullptr, pos, page, pos % p.P, g);
 }
 
 }  // namespace

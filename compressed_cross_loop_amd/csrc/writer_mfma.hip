@@ -14,6 +14,7 @@
 
 #include "device_common.h"
 #include "lla_internal.h"
+#include "writer_common.h"
 
 namespace lla {
 
@@ -120,8 +121,8 @@ __global__ __launch_bounds__(kThreads) void k_writer_mfma(WriterParams p) {
 }
 
 // Sum the K-split partials of one (token, group) in split order, then
-// rotate the key part by R~_p (baked sets), round to bf16 and scatter into
-// the paged store.  The partial sums are read as float4 rows, eight splits'
+// rotate the key part by R~_p (baked sets) and store (bf16, or e4m3 codes
+// with per-token scales).  The partial sums are read as float4 rows, eight splits'
 // loads in flight at a time; the rotation angles come from a per-token table.
 __global__ __launch_bounds__(kReduceThreads) void k_writer_reduce(WriterParams p) {
   extern __shared__ float c[];
@@ -153,28 +154,8 @@ __global__ __launch_bounds__(kReduceThreads) void k_writer_reduce(WriterParams p
     for (int e = 0; e < 4; ++e) c[4 * u + e] = sum[e];
   }
   __syncthreads();
-  const int rk = p.rk, dh = p.dh, half = dh / 2;
   const int64_t page = p.bt[(int64_t)b * p.max_pages + pos / p.P];
-  const int slot = pos % p.P;
-  bf16* pages = static_cast<bf16*>(p.pages);
-  for (int o = tid; o < R; o += kReduceThreads) {
-    float v = c[o];
-    int64_t off;
-    if (o < rk) {
-      if (p.rope_baked) {
-        const int f = o % dh;
-        if (f < half) {
-          v = c[o] * csn[f][0] - c[o + half] * csn[f][1];
-        } else {
-          v = c[o - half] * csn[f - half][1] + c[o] * csn[f - half][0];
-        }
-      }
-      off = key_off(page, g, slot, o, G, p.P, R, rk);
-    } else {
-      off = val_off(page, g, slot, o - rk, G, p.P, R, rk);
-    }
-    pages[off] = static_cast<bf16>(v);
-  }
+  finish_latent<bf16, kReduceThreads>(p, c, csn, pos, page, pos % p.P, g);
 }
 
 }  // namespace

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define LLA_ABI_VERSION 2   /* 2: value decoder passed as B_t^T [H][d_h][r_v] */
+#define LLA_ABI_VERSION 3   /* 2: value decoder passed as B_t^T [H][d_h][r_v]; 3: latent_fp8 */
 
 typedef void* lla_stream_t; /* a hipStream_t */
 
@@ -80,6 +80,14 @@ typedef enum { LLA_F32 = 0, LLA_BF16 = 1 } lla_dtype;
  *                       (needs r_k % head_dim == 0 and rope_base > 0)
  *   rope_base           0 = no rotary embedding
  *   dtype               storage and map dtype
+ *   latent_fp8          1: the latents are stored as OCP e4m3 codes with one
+ *                       fp32 scale per token, group and part (key, value):
+ *                       element = code value x scale, scale = max|x| / 448 of
+ *                       the part ([HLA] "Summary (Overview)": the codec
+ *                       combines with quantization).  Needs dtype == LLA_BF16
+ *                       (maps, ring and activations stay bf16) and r_k, r_v
+ *                       multiples of 64; the absorbed / HLA entry points read
+ *                       it, lla_decode_reconstruct returns UNSUPPORTED.
  */
 typedef struct {
   int32_t n_heads, head_dim;
@@ -90,6 +98,7 @@ typedef struct {
   int32_t rope_baked;
   float rope_base;
   lla_dtype dtype;
+  int32_t latent_fp8;
 } lla_set_desc;
 
 /*
@@ -103,6 +112,14 @@ typedef struct {
  *                and of value dim d:
  *                  ((pg*G + g)*P + (u/16)*16)*(r_k+r_v) + 16*r_k
  *                    + (d/16)*256 + (d%16)*16 + u%16
+ *                With latent_fp8 the store is bytes: a tile is
+ *                  TB = 16*(r_k+r_v) + 128 bytes, tile base
+ *                  T = ((pg*G + g)*(P/16) + u/16)*TB; key code of dim d at
+ *                  T + (u%16)*r_k + d; value code of dim d at
+ *                  T + 16*r_k + (d/64)*1024 + (d%16)*64 + ((u%16)/4)*16
+ *                    + ((d/16)%4)*4 + u%4;
+ *                  fp32 key scale at T + 16*(r_k+r_v) + (u%16)*4 and value
+ *                  scale 64 bytes further.
  *   block_table  [batch][max_pages_per_seq] physical page of logical page
  *                p/P of each sequence (host-side: only its shape is used)
  */

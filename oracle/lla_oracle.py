@@ -35,14 +35,16 @@ Readings taken where the pages are silent (each also applies to the GPU path):
       d_h-blocks of the key latent ("m pairs per frequency").
   R10 Key latents are stored already rotated ("baked"), R~_p c^K, when the set
       uses rotary embedding; the reader rotates the query by R~_i.
-  R11 LLA-2D / per-head LLA decoders are dense maps from the group's latent.
-  R12 LLA has a single set serving loops 1..T (no separate loop-1 latent).
-  R13 The exact window holds post-rotation keys and values for every loop.
-  R14 context N = i+1; latent count max(0, i-W); exact count min(W+1, i+1).
-  R15 The uncompressed (full-cache) baseline keeps one exact paged cache per
+  (R11, R15, R17, R18 concern the synthetic maps, bf16 rounding, the error
+  metric and unsupported argument forms; nothing here depends on them.)
+  R12 LLA-2D / per-head LLA decoders are dense maps from the group's latent.
+  R13 LLA has a single set serving loops 1..T (no separate loop-1 latent).
+  R14 The exact window holds post-rotation keys and values for every loop.
+  R16 context N = i+1; latent count max(0, i-W); exact count min(W+1, i+1).
+  R19 The uncompressed (full-cache) baseline keeps one exact paged cache per
       (layer, loop), pages of [P][H][d_h] with rotated keys; a decode call
       appends the current token and attends to tokens 0..i.
-  R16 fp8 latent storage: OCP e4m3 codes, round to nearest even, saturating
+  R20 fp8 latent storage: OCP e4m3 codes, round to nearest even, saturating
       at 448, one fp32 scale per token, group and part = max|x| / 448 of that
       part (1 when the part is all zero).
 """
@@ -130,7 +132,7 @@ def gather_latents(pages: np.ndarray, block_table: np.ndarray, b: int, n_tok: in
 
 # ----------------------------------------------------------------------------
 # fp8 latent storage ([HLA] "Summary (Overview)": the codec combines with
-# quantization; reading R16): OCP e4m3 codes with one fp32 scale per token,
+# quantization; reading R20): OCP e4m3 codes with one fp32 scale per token,
 # group and part (key, value).  A stored latent element is decode(code) *
 # scale.
 # ----------------------------------------------------------------------------
@@ -152,7 +154,7 @@ def e4m3_decode(code):
 
 def e4m3_encode(x):
     """Round to nearest, ties to even, onto the e4m3 grid, saturating at
-    +-448 (reading R16).  The grid spacing in the binade [2^e, 2^(e+1)) is
+    +-448 (reading R20).  The grid spacing in the binade [2^e, 2^(e+1)) is
     2^(e-3) for e >= -6; below 2^-6 it is the subnormal spacing 2^-9."""
     x = np.asarray(x, dtype=np.float64)
     neg = np.signbit(x)
@@ -258,7 +260,7 @@ def write_latents(x: np.ndarray, enc: np.ndarray, pos: np.ndarray, *, r_k: int,
 
 
 # ----------------------------------------------------------------------------
-# Decode: shared bookkeeping of Eq. 4's ranges (readings R1, R2, R14)
+# Decode: shared bookkeeping of Eq. 4's ranges (readings R1, R2, R16)
 # ----------------------------------------------------------------------------
 def ranges(i: int, window: int):
     """(n_lat, exact window positions j < i) for current position i."""
@@ -274,7 +276,7 @@ def _softmax(logits: np.ndarray) -> np.ndarray:
 
 def _exact_part(b, h, i, window, ring_k, ring_v, k_cur, v_cur, rope_base):
     """Exact keys/values for positions max(0,i-W)..i: ring slots j mod (W+1)
-    hold positions j < i (post-rotation keys, R13); the current token's key is
+    hold positions j < i (post-rotation keys, R14); the current token's key is
     R_i k_cur and its value v_cur (R2)."""
     _, win = ranges(i, window)
     slots = win % (window + 1)
@@ -355,7 +357,7 @@ def absorbed_decode(sK, sV, pos, q, k_cur, v_cur, ring_k, ring_v, A, Bv, *,
 
 def ring_update(pos, k_cur, v_cur, *, window: int, rope_base: float = 0.0):
     """What a decode call writes into the exact window: slot i mod (W+1) of
-    sequence b receives R_i k_cur[b] and v_cur[b] (reading R13).
+    sequence b receives R_i k_cur[b] and v_cur[b] (reading R14).
     Returns (slot [B], k [B, H, d_h], v [B, H, d_h])."""
     pos = np.asarray(pos, dtype=np.int64)
     k = rope_head(np.asarray(k_cur, dtype=np.float64), pos[:, None], rope_base)
@@ -365,9 +367,9 @@ def ring_update(pos, k_cur, v_cur, *, window: int, rope_base: float = 0.0):
 # ----------------------------------------------------------------------------
 # Uncompressed (full-cache) looped decode: the teacher the codec replaces
 # ([HLA] "Key Problem": every loop keeps and attends to its own exact keys and
-# values, 2 T d numbers per token per layer).  Reading R15: the exact cache
+# values, 2 T d numbers per token per layer).  Reading R19: the exact cache
 # of one (layer, loop) is paged like the latent store, a page holding
-# [P][H][d_h] (all heads of a token contiguous), keys stored rotated (R13).
+# [P][H][d_h] (all heads of a token contiguous), keys stored rotated (R14).
 # ----------------------------------------------------------------------------
 def gather_kv_cache(k_pages, v_pages, block_table, b: int, n_tok: int, *, page_size: int):
     """Keys and values [n_tok, H, d_h] of tokens 0..n_tok-1 of sequence b:

@@ -186,6 +186,23 @@ def writer_inputs(seed: int, *, batch: int, n_tok: int, n_loops: int, groups: in
                         pos=torch.from_numpy(pos))
 
 
+def fp8_latent_draws(seed: int, *, n_pages: int, groups: int, page_size: int, r_k: int, r_v: int):
+    """Synthetic content of an fp8 latent store, drawn directly as codes and
+    scales: codes of finite e4m3 numbers with magnitudes in [1/8, 2) (exponent
+    fields 4..7, any mantissa, random sign) and per-token scales uniform in
+    [0.5, 1.5).  Returns codes uint8 [n_pages, G, P, r_k+r_v] and scales
+    float32 [n_pages, G, P, 2] (key, value)."""
+    g = rng(seed, 8)
+    shape = (n_pages, groups, page_size, r_k + r_v)
+    # six random bits per code: bit 5 the sign, bits 0..4 the low five bits
+    # of an exponent field in 4..7 and the mantissa (uint8 throughout, so a
+    # full-size store stays within a few bytes per element)
+    v = g.integers(0, 64, size=shape, dtype=np.uint8)
+    codes = ((v & 32) << 2) | 32 | (v & 31)
+    scales = g.uniform(0.5, 1.5, size=(n_pages, groups, page_size, 2)).astype(np.float32)
+    return codes, scales
+
+
 @dataclass
 class KvCacheInputs:
     """One full-cache decode call's inputs (CPU tensors): k_pages, v_pages

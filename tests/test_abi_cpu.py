@@ -32,7 +32,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert B.lla_abi_version() == 2 == B.ABI_VERSION
+    assert B.lla_abi_version() == 3 == B.ABI_VERSION
     for s in range(5):
         assert B.lla_status_string(s)
     assert B.lla_status_string(99) == "unknown status"
@@ -252,3 +252,30 @@ def test_full_cache_null_structs_and_plan():
     assert B.lla_full_decode_plan_splits(d, 1, 10) == 1
     assert B.lla_full_decode_plan_splits(d, 32, 4095, splits=5) == 5
     assert B.lla_full_decode_workspace_bytes(d, 32, 4095, 4) > B.lla_full_decode_workspace_bytes(d, 8, 4095, 4) > 0
+
+
+def test_fp8_descriptor_rules_and_bytes_per_token():
+    def d(**kw):
+        base = dict(n_heads=16, head_dim=128, groups=1, r_k=512, r_v=512, loop_first=2, loop_last=4,
+                    page_size=64, rope_baked=1, rope_base=10000.0, dtype=B.LLA_BF16, latent_fp8=1)
+        base.update(kw)
+        return B.set_desc(**base)
+    assert B.lla_bytes_per_token(d()) == 512 + 512 + 8
+    assert B.lla_bytes_per_token(d(groups=16, n_heads=16, r_k=64, r_v=64, rope_baked=0, rope_base=0.0)) == \
+        16 * (64 + 64 + 8)
+    assert B.store_bytes(d(), 3) == 3 * 4 * (16 * 1024 + 128)
+    for bad, want in ((dict(latent_fp8=2), B.LLA_ERR_INVALID_ARGUMENT),
+                      (dict(dtype=B.LLA_F32), B.LLA_ERR_INVALID_ARGUMENT),
+                      (dict(r_k=96, r_v=96, rope_baked=0, rope_base=0.0), B.LLA_ERR_UNSUPPORTED)):
+        assert B.lla_bytes_per_token(d(**bad)) == 0
+        assert B.lla_decode_workspace_bytes(d(**bad), 2, 100, 16) == 0
+    # fp8 latents are read by the absorbed entry points only
+    assert B.lla_decode_scan_kernel(d(), 2) == "k_scan_absorbed_mfma"
+
+
+def test_fp8_reconstruct_is_unsupported():
+    d = hla_main()
+    d.latent_fp8 = 1
+    st = B.LlaStore(FAKE, FAKE, 4)
+    assert B.lib.lla_decode_reconstruct(ctypes.byref(d), ctypes.byref(st), 4, ctypes.byref(_args()), None) \
+        == B.LLA_ERR_UNSUPPORTED
