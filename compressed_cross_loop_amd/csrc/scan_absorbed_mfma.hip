@@ -41,6 +41,10 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
+// Page ids of a split are staged in LDS: a block-table read inside the tile
+// loop is a vector load, and waiting for it (vmcnt counts loads in issue
+// order) would also wait for every tile load the pipeline has in flight.
+constexpr int kPageTab = 8192;
 
 // Prefetch depth per latent width: narrow tiles carry few bytes, so they run
 // further ahead to keep enough of HBM's latency covered; r = 512 is limited
@@ -205,19 +209,19 @@ __device__ __forceinline__ f32x4 tile_scores8(const Keys8<RK>& k, const bf16* qc
 template <int RV>
 __device__ __forceinline__ void tile_values8(const Vals8<RV>& v, s16x4 pb, f32x4 (&acc)[RV / 16], int nvalid,
                                              int grp) {
+  // tokens past the end may hold anything (even NaN codes): byte r of a word
+  // is token 4 grp + r, so one AND per word turns them into +0 codes
+  const int nv = nvalid - 4 * grp;
+  const unsigned keep = nv >= 4 ? 0xFFFFFFFFu : (nv <= 0 ? 0u : 0xFFFFFFFFu >> (8 * (4 - nv)));
 #pragma unroll
   for (int q = 0; q < RV / 64; ++q)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       // sub-block 4q + j, tokens 4 grp .. 4 grp + 3 of this lane's dim row
-      unsigned w2[2] = {e4m3x2_to_bf16x2<false>(v.v[q][j]), e4m3x2_to_bf16x2<true>(v.v[q][j])};
-      s16x4 a = __builtin_bit_cast(s16x4, w2);
-      if (nvalid < 16) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (4 * grp + r >= nvalid) a[r] = 0;
-      }
-      acc[4 * q + j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb, acc[4 * q + j], 0, 0, 0);
+      const unsigned w = v.v[q][j] & keep;
+      unsigned w2[2] = {e4m3x2_to_bf16x2<false>(w), e4m3x2_to_bf16x2<true>(w)};
+      acc[4 * q + j] =
+          __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, w2), pb, acc[4 * q + j], 0, 0, 0);
     }
 }
 
@@ -389,6 +393,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_scan_absorbed_mfma(DecodeParams
       *reinterpret_cast<bf16x8*>(&qs[hh][c8]) = v;
     }
   }
+  const int32_t* bt = p.bt + (int64_t)b * p.max_pages;
+  __shared__ int32_t ptab[kPageTab];
+  const int pfirst = t0 / P;
+  {
+    // pages of tokens t0 .. t1-1; never more than max_pages <= kPageTab
+    const int npt = t1 > t0 ? (t1 - 1) / P - pfirst + 1 : 0;
+    for (int x = tid; x < npt; x += kThreads) ptab[x] = bt[pfirst + x];
+  }
   __syncthreads();
   const bf16* qrow = &qs[col][grp * 8];
   f32x4 acc[RV / 16];
@@ -397,12 +409,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_scan_absorbed_mfma(DecodeParams
   float m = -INFINITY, lsum = 0.f;
 
   const char* pages = static_cast<const char*>(p.pages);
-  const int32_t* bt = p.bt + (int64_t)b * p.max_pages;
   const int R = RK + RV;
   const int ntiles = (t1 - t0 + 15) / 16;
   auto tile_ptr = [&](int ti) -> const char* {   // byte address of a 16-token tile
     const int j0 = t0 + ti * 16;
-    const int64_t page = bt[j0 / P];
+    const int64_t page = ptab[j0 / P - pfirst];
     if constexpr (F8) return pages + tile_base8(page, g, j0 % P, G, P, RK, RV);
     return pages + 2 * tile_base(page, g, j0 % P, G, P, R);
   };
@@ -542,7 +553,7 @@ hipError_t launch_rk(const DecodeParams& p, hipStream_t st) {
 }  // namespace
 
 bool scan_absorbed_mfma_supports(const DecodeParams& p) {
-  if (!p.bf16 || p.hpg > 16 || p.rk != p.rv) return false;
+  if (!p.bf16 || p.hpg > 16 || p.rk != p.rv || p.max_pages > kPageTab) return false;
   if (p.fp8 && p.rk % 64) return false;
   switch (p.rk) {
     case 32: case 64: case 128: case 256: case 512: return true;
