@@ -46,17 +46,20 @@ constexpr int kThreads = 64 * kWaves;
 // order) would also wait for every tile load the pipeline has in flight.
 constexpr int kPageTab = 8192;
 
-// Prefetch depth per latent width: narrow tiles carry few bytes, so they run
-// further ahead to keep enough of HBM's latency covered; r = 512 is limited
-// by registers.
+// Prefetch depth per latent width (measured): narrow tiles carry few bytes,
+// so they run further ahead to keep enough of HBM's latency covered; wide
+// tiles already keep enough in flight, and every CU streaming its own pages
+// with more requests outstanding only adds DRAM contention (r = 512 is
+// fastest one tile ahead).
 template <int RK> struct Pipe { static constexpr int keys = 4, values = 4, unroll = 4; };
 template <> struct Pipe<128> { static constexpr int keys = 4, values = 2, unroll = 4; };
 template <> struct Pipe<256> { static constexpr int keys = 3, values = 2, unroll = 6; };
-template <> struct Pipe<512> { static constexpr int keys = 2, values = 1, unroll = 2; };
-// fp8 tiles hold half the bytes (and registers) of bf16 ones: deeper
+template <> struct Pipe<512> { static constexpr int keys = 1, values = 1, unroll = 1; };
+// fp8 tiles hold half the bytes (and registers) of bf16 ones: deeper at
+// narrow widths, and again shallow at r = 512
 template <int RK> struct Pipe8 { static constexpr int keys = 4, values = 4, unroll = 4; };
 template <> struct Pipe8<256> { static constexpr int keys = 4, values = 2, unroll = 4; };
-template <> struct Pipe8<512> { static constexpr int keys = 3, values = 2, unroll = 6; };
+template <> struct Pipe8<512> { static constexpr int keys = 2, values = 1, unroll = 2; };
 
 template <int RK>
 __device__ __forceinline__ void load_keys(bf16x8 (&k)[RK / 32], const char* tile_b, int col, int grp) {
