@@ -47,6 +47,11 @@ Readings taken where the pages are silent (each also applies to the GPU path):
   R20 fp8 latent storage: OCP e4m3 codes, round to nearest even, saturating
       at 448, one fp32 scale per token, group and part = max|x| / 448 of that
       part (1 when the part is all zero).
+  R21 The parallel (second) pass of the two-pass procedure evaluates Eq. 4 at
+      every position i of whole sequences at once: latents of j < i-W from
+      the store (written by the first pass), this loop's exact keys and
+      values of j = max(0, i-W) .. i, positions 0-based from the start of
+      each sequence.
 """
 import numpy as np
 
@@ -362,6 +367,53 @@ def ring_update(pos, k_cur, v_cur, *, window: int, rope_base: float = 0.0):
     pos = np.asarray(pos, dtype=np.int64)
     k = rope_head(np.asarray(k_cur, dtype=np.float64), pos[:, None], rope_base)
     return pos % (window + 1), k, np.asarray(v_cur, dtype=np.float64).copy()
+
+
+# ----------------------------------------------------------------------------
+# Parallel HLA attention over whole sequences ([HLA] "Training Procedure": the
+# two-pass fine-tuning writes every token's latents in a first pass, then runs
+# HLA attention at all positions in parallel; reading R21)
+# ----------------------------------------------------------------------------
+def parallel_attention(sK, sV, n_tok, q, k, v, A, Bv, *, window: int, rope_base: float = 0.0,
+                       rows=None):
+    """Eq. 3 / Eq. 4 at every position i < n_tok[b] of every sequence b.
+
+    sK[b] [>= n_tok[b], G, r_k], sV[b] [>= n_tok[b], G, r_v]   latents of the
+        sequence's tokens (key latents stored rotated when the set bakes
+        rotary embedding, R10)
+    q, k, v [B, n_max, H, d_h]   this loop's query and exact key / value at
+        every position (q, k before rotation)
+    A [H, d_h, r_k]; Bv [H, r_v, d_h]
+    Position i scores latent tokens j < i-W with q~ = R~_i A_t^T q_i (Eq. 3)
+    and exact tokens max(0, i-W) <= j <= i with (R_i q_i).(R_j k_j), all
+    over sqrt(d_h), in one softmax (R3); o_i = B_t^T sum_lat a_j sV_j +
+    sum_exact a_j v_j.  `rows`: optional list of (b, i) to evaluate (the
+    rest stay zero).  Returns out [B, n_max, H, d_h] (fp64); rows at or past
+    n_tok[b] are zero."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, n_max, H, d_h = q.shape
+    G = np.asarray(sK[0]).shape[1]
+    hpg = H // G
+    if rows is None:
+        rows = [(b, i) for b in range(B) for i in range(int(n_tok[b]))]
+    out = np.zeros((B, n_max, H, d_h))
+    for b, i in rows:
+        assert i < int(n_tok[b])
+        n_lat = max(0, i - window)
+        j_ex = np.arange(n_lat, i + 1)
+        k_ex = rope_head(k[b, j_ex], j_ex[:, None], rope_base)        # [n_ex, H, d_h]
+        for h in range(H):
+            g = h // hpg
+            a_h = np.asarray(A[h], dtype=np.float64)
+            q_lat = rope_latent(a_h.T @ q[b, i, h], i, rope_base, d_h)
+            s_lat = np.asarray(sK[b][:n_lat, g], dtype=np.float64) @ q_lat / np.sqrt(d_h)
+            s_ex = k_ex[:, h] @ rope_head(q[b, i, h], i, rope_base) / np.sqrt(d_h)
+            a = _softmax(np.concatenate([s_lat, s_ex]))
+            o_lat = a[:n_lat] @ np.asarray(sV[b][:n_lat, g], dtype=np.float64)
+            out[b, i, h] = np.asarray(Bv[h], dtype=np.float64).T @ o_lat + a[n_lat:] @ v[b, j_ex, h]
+    return out
 
 
 # ----------------------------------------------------------------------------

@@ -664,3 +664,117 @@ def test_fp8_quantize_rows_and_gather():
     sK, sV = O.gather_latents_fp8(raw, bt, 0, n, **kw)
     np.testing.assert_allclose(sK, O.e4m3_decode(kq) * ks.astype(np.float32)[..., None], rtol=0, atol=0)
     np.testing.assert_allclose(sV, O.e4m3_decode(vq) * vs.astype(np.float32)[..., None], rtol=0, atol=0)
+
+
+# ---------------------------------------------------------------- parallel pass
+def _causal_sdpa(q, k, v, base):
+    """Causal attention over whole sequences: torch's scaled dot product
+    attention (fp64, CPU, is_causal) on R_i q_i and R_j k_j.  q, k, v [n, H, d_h]."""
+    n = q.shape[0]
+    qr = _complex_rope(q, np.arange(n)[:, None], base)
+    kr = _complex_rope(k, np.arange(n)[:, None], base)
+    t = lambda a: torch.from_numpy(a.transpose(1, 0, 2).copy())[None]
+    o = torch.nn.functional.scaled_dot_product_attention(t(qr), t(kr), t(v), is_causal=True)
+    return o[0].numpy().transpose(1, 0, 2)
+
+
+@pytest.mark.parametrize("t", [1, 2, 3])
+@pytest.mark.parametrize("W", [0, 2, 5, 20])
+def test_parallel_identity_codec_equals_causal_attention(t, W):
+    """Under a full-rank identity codec the parallel pass is causal attention
+    over the loop's exact keys and values at every position, for every W."""
+    base, n = 10000.0, 12
+    k, v, _, maps = _identity_hla(61, n_tok=n, base=base)
+    q = gen.rng(62).standard_normal((n,) + k.shape[2:])
+    sK, sV, A, Bv = maps(t)
+    out = O.parallel_attention([sK], [sV], [n], q[None], k[t - 1][None], v[t - 1][None], A, Bv, window=W,
+                               rope_base=base)
+    np.testing.assert_allclose(out[0], _causal_sdpa(q, k[t - 1], v[t - 1], base), atol=1e-12)
+
+
+def _parallel_case(seed, *, B=2, n=20, H=4, G=2, d_h=8, r_k=16, r_v=12, base=10000.0):
+    g = gen.rng(seed)
+    sK = [g.standard_normal((n, G, r_k)) for _ in range(B)]
+    sV = [g.standard_normal((n, G, r_v)) for _ in range(B)]
+    q, k, v = (g.standard_normal((B, n, H, d_h)) for _ in range(3))
+    A = gen.frequency_paired_decoder(g, H, d_h, r_k) if base else \
+        np.stack([gen.gaussian_orthonormal(g, d_h, r_k) for _ in range(H)])
+    Bv = np.stack([gen.gaussian_orthonormal(g, r_v, d_h) for _ in range(H)])
+    return sK, sV, q, k, v, A, Bv
+
+
+@pytest.mark.parametrize("W", [0, 3, 7])
+def test_parallel_equals_decode_at_every_position(W):
+    """Each position of the parallel pass is one decode call: the ring holds
+    R_j k_j, v_j of the W tokens before i and the current token is k_i, v_i."""
+    base = 10000.0
+    sK, sV, q, k, v, A, Bv = _parallel_case(63, base=base)
+    n_tok = [20, 13]
+    out = O.parallel_attention(sK, sV, n_tok, q, k, v, A, Bv, window=W, rope_base=base)
+    for b in range(2):
+        for i in range(n_tok[b]):
+            rk, rv = _ring(k[b], v[b], i, W, base)
+            want = O.absorbed_decode([sK[b]], [sV[b]], [i], q[b, i][None], k[b, i][None], v[b, i][None],
+                                     rk, rv, A, Bv, window=W, rope_base=base)
+            np.testing.assert_allclose(out[b, i], want[0], atol=1e-12)
+        assert np.all(out[b, n_tok[b]:] == 0)
+
+
+def test_parallel_window_over_whole_sequence_ignores_latents():
+    """W >= n-1: no position reads a latent (NaN latents stay unread) and the
+    pass is causal attention over the exact keys and values."""
+    base, n = 10000.0, 9
+    sK, sV, q, k, v, A, Bv = _parallel_case(64, B=1, n=n, base=base)
+    sK[0][:] = np.nan
+    sV[0][:] = np.nan
+    out = O.parallel_attention(sK, sV, [n], q, k, v, A, Bv, window=n - 1, rope_base=base)
+    np.testing.assert_allclose(out[0], _causal_sdpa(q[0], k[0], v[0], base), atol=1e-12)
+
+
+def test_parallel_rows_subset_and_ragged_lengths():
+    """Evaluating a subset of rows gives the same rows as the whole pass."""
+    sK, sV, q, k, v, A, Bv = _parallel_case(65)
+    full = O.parallel_attention(sK, sV, [20, 7], q, k, v, A, Bv, window=3, rope_base=10000.0)
+    sub = O.parallel_attention(sK, sV, [20, 7], q, k, v, A, Bv, window=3, rope_base=10000.0,
+                               rows=[(0, 19), (1, 0), (1, 6)])
+    for b, i in [(0, 19), (1, 0), (1, 6)]:
+        np.testing.assert_array_equal(sub[b, i], full[b, i])
+    assert np.all(sub[0, :19] == 0)
+
+
+def test_parallel_brute_force():
+    """Pure-Python loops (math.cos / sin / exp, explicit sums) on a tiny case:
+    one group, d_h = 4, r_k = r_v = 8, W = 2, rotary on."""
+    base, W, n, H, d_h, r = 10000.0, 2, 6, 2, 4, 8
+    sK, sV, q, k, v, A, Bv = _parallel_case(66, B=1, n=n, H=H, G=1, d_h=d_h, r_k=r, r_v=r, base=base)
+    out = O.parallel_attention(sK, sV, [n], q, k, v, A, Bv, window=W, rope_base=base)
+
+    def rot(vec, p):   # rotate-half pairs (f, f + d/2), theta_f = base^(-2f/d)
+        d = len(vec)
+        res = list(vec)
+        for f in range(d // 2):
+            th = p * base ** (-2.0 * f / d)
+            a, b2 = vec[f], vec[f + d // 2]
+            res[f] = a * math.cos(th) - b2 * math.sin(th)
+            res[f + d // 2] = a * math.sin(th) + b2 * math.cos(th)
+        return res
+
+    for h in range(H):
+        for i in range(n):
+            logits, vals = [], []
+            # latent tokens: score (R~_i A^T q) . sK_j / sqrt(d), value B^T sV_j
+            at_q = [sum(A[h][e][c] * q[0, i, h, e] for e in range(d_h)) for c in range(r)]
+            qt = rot(at_q[:4], i) + rot(at_q[4:], i)
+            for j in range(max(0, i - W)):
+                logits.append(sum(qt[c] * sK[0][j, 0, c] for c in range(r)) / math.sqrt(d_h))
+                vals.append([sum(Bv[h][c][e] * sV[0][j, 0, c] for c in range(r)) for e in range(d_h)])
+            qr = rot(list(q[0, i, h]), i)
+            for j in range(max(0, i - W), i + 1):
+                kr = rot(list(k[0, j, h]), j)
+                logits.append(sum(qr[e] * kr[e] for e in range(d_h)) / math.sqrt(d_h))
+                vals.append(list(v[0, j, h]))
+            mx = max(logits)
+            w = [math.exp(x - mx) for x in logits]
+            z = sum(w)
+            want = [sum(w[u] * vals[u][e] for u in range(len(w))) / z for e in range(d_h)]
+            np.testing.assert_allclose(out[0, i, h], want, atol=1e-12)
