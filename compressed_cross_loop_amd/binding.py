@@ -68,6 +68,13 @@ class LlaFullDecodeArgs(ctypes.Structure):
                 ("scan_events", ctypes.c_void_p)]
 
 
+class LlaParallelArgs(ctypes.Structure):
+    _fields_ = [("loop", ctypes.c_int32), ("window", ctypes.c_int32), ("n_max", ctypes.c_int32),
+                ("flags", ctypes.c_int32), ("n_tok", ctypes.c_void_p), ("q", ctypes.c_void_p),
+                ("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("A", ctypes.c_void_p), ("B", ctypes.c_void_p),
+                ("out", ctypes.c_void_p), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+
+
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run compressed_cross_loop_amd/build.py "
                       "(or __graft_entry__.build()) first")
@@ -97,6 +104,11 @@ lib.lla_full_decode_workspace_bytes.restype = ctypes.c_size_t
 lib.lla_full_decode_workspace_bytes.argtypes = [_P(LlaKvDesc), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
 lib.lla_full_decode_plan_splits.restype = ctypes.c_int32
 lib.lla_full_decode_plan_splits.argtypes = [_P(LlaKvDesc), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+lib.hla_attention_parallel.restype = ctypes.c_int
+lib.hla_attention_parallel.argtypes = [_P(LlaSetDesc), _P(LlaStore), ctypes.c_int32, _P(LlaParallelArgs),
+                                       ctypes.c_void_p]
+lib.lla_parallel_workspace_bytes.restype = ctypes.c_size_t
+lib.lla_parallel_workspace_bytes.argtypes = [_P(LlaSetDesc), ctypes.c_int32, ctypes.c_int32]
 lib.lla_decode_scan_kernel.restype = ctypes.c_char_p
 lib.lla_decode_scan_kernel.argtypes = [_P(LlaSetDesc), ctypes.c_int32, ctypes.c_int32]
 lib.lla_bytes_per_token.restype = ctypes.c_size_t
@@ -106,7 +118,7 @@ lib.lla_status_string.argtypes = [ctypes.c_int]
 lib.lla_abi_version.restype = ctypes.c_int32
 lib.lla_abi_version.argtypes = []
 
-ABI_VERSION = 3   # include/lla.h LLA_ABI_VERSION this binding marshals for
+ABI_VERSION = 4   # include/lla.h LLA_ABI_VERSION this binding marshals for
 if lib.lla_abi_version() != ABI_VERSION:
     raise ImportError(f"{LIB_PATH} has ABI version {lib.lla_abi_version()}, the binding expects {ABI_VERSION}: "
                       "rebuild it (python -c 'import __graft_entry__ as g; g.build()')")
@@ -271,6 +283,25 @@ def lla_full_decode_workspace_bytes(desc, batch, max_pos, splits=0):
 
 def lla_full_decode_plan_splits(desc, batch, max_pos, splits=0):
     return lib.lla_full_decode_plan_splits(ctypes.byref(desc), batch, max_pos, splits)
+
+
+def parallel_args(*, loop, window, n_tok, q, k, v, A, B, out, workspace, flags=0):
+    """n_tok [batch] int32; q, k, v, out [batch, n_max, H, d_h]; A [H, d_h, r_k]; B = B_t^T [H, d_h, r_v]."""
+    ws_bytes = 0 if workspace is None or isinstance(workspace, int) else \
+        workspace.numel() * workspace.element_size()
+    args = LlaParallelArgs(loop, window, int(q.shape[1]), flags, _ptr(n_tok), _ptr(q), _ptr(k), _ptr(v), _ptr(A),
+                           _ptr(B), _ptr(out), _ptr(workspace), ws_bytes)
+    args._keep = (n_tok, q, k, v, A, B, out, workspace)
+    return args
+
+
+def hla_attention_parallel(desc, st, batch, args, stream=None):
+    _check(lib.hla_attention_parallel(ctypes.byref(desc), ctypes.byref(st), batch, ctypes.byref(args),
+                                      _stream(stream)))
+
+
+def lla_parallel_workspace_bytes(desc, batch, n_max):
+    return lib.lla_parallel_workspace_bytes(ctypes.byref(desc), batch, n_max)
 
 
 def torch_dtype(desc):

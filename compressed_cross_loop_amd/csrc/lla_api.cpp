@@ -203,6 +203,39 @@ FullWs full_ws_layout(const lla_kv_desc& d, int B, int S) {
 }
 
 
+// ---------------------------------------------------------------- parallel pass
+lla_status check_parallel_desc(const lla_set_desc* d) {
+  lla_status r = check_desc(d);
+  if (r != LLA_OK) return r;
+  if (d->dtype != LLA_BF16 || d->latent_fp8) return LLA_ERR_UNSUPPORTED;
+  if (d->head_dim != 64 && d->head_dim != 128) return LLA_ERR_UNSUPPORTED;
+  if (d->r_k % 32 || d->r_v % 32) return LLA_ERR_UNSUPPORTED;
+  if (d->rope_base > 0.f && !d->rope_baked) return LLA_ERR_UNSUPPORTED;
+  return LLA_OK;
+}
+
+int parallel_pad(int n_max) { return (n_max + kParQueryTile - 1) / kParQueryTile * kParQueryTile; }
+
+struct ParWs {
+  size_t sk, sv, qr, kr, vt, kh, vht, total;
+};
+
+ParWs parallel_ws_layout(const lla_set_desc& d, int B, int n_max) {
+  ParWs w{};
+  const size_t np = parallel_pad(n_max), H = d.n_heads, dh = d.head_dim, G = d.groups;
+  const size_t head_rows = (size_t)B * np * H * dh * 2;
+  size_t off = 0;
+  w.sk = off;  off = up256(off + (size_t)B * np * G * d.r_k * 2);
+  w.sv = off;  off = up256(off + (size_t)B * np * G * d.r_v * 2);
+  w.qr = off;  off = up256(off + head_rows);
+  w.kr = off;  off = up256(off + head_rows);
+  w.vt = off;  off = up256(off + head_rows);
+  w.kh = off;  off = up256(off + head_rows);
+  w.vht = off; off = up256(off + head_rows);
+  w.total = off;
+  return w;
+}
+
 lla_status decode(const lla_set_desc* d, const lla_store* st, int32_t batch,
                   const lla_decode_args* a, lla_stream_t stream, int entry) {
   // entry: 0 reconstruct, 1 absorbed (LLA-D), 2 HLA windowed
@@ -367,6 +400,43 @@ int32_t lla_decode_plan_splits(const lla_set_desc* desc, int32_t batch, int32_t 
 const char* lla_decode_scan_kernel(const lla_set_desc* desc, int32_t entry, int32_t flags) {
   if (check_desc(desc) != LLA_OK || entry < 0 || entry > 2 || (flags & ~LLA_FLAG_GENERIC)) return nullptr;
   return scan_kernel_name(*desc, entry != 0, flags);
+}
+
+size_t lla_parallel_workspace_bytes(const lla_set_desc* desc, int32_t batch, int32_t n_max) {
+  if (check_parallel_desc(desc) != LLA_OK || batch <= 0 || n_max <= 0) return 0;
+  return parallel_ws_layout(*desc, batch, n_max).total;
+}
+
+lla_status hla_attention_parallel(const lla_set_desc* d, const lla_store* st, int32_t batch,
+                                  const lla_parallel_args* a, lla_stream_t stream) {
+  lla_status r = check_parallel_desc(d);
+  if (r != LLA_OK) return r;
+  if ((r = check_store(st)) != LLA_OK) return r;
+  if (batch <= 0 || !a) return LLA_ERR_INVALID_ARGUMENT;
+  if (a->loop < d->loop_first || a->loop > d->loop_last) return LLA_ERR_INVALID_ARGUMENT;
+  if (a->window < 0 || a->n_max <= 0 || a->flags != 0) return LLA_ERR_INVALID_ARGUMENT;
+  const void* ptrs[] = {a->n_tok, a->q, a->k, a->v, a->A, a->B, a->out};
+  for (const void* p : ptrs)
+    if (!p || !aligned16(p)) return LLA_ERR_INVALID_ARGUMENT;
+  // the latents some position reads: tokens below n_max - 1 - W
+  const int64_t n_lat = std::max<int64_t>(0, (int64_t)a->n_max - 1 - a->window);
+  if ((int64_t)st->max_pages_per_seq * d->page_size < n_lat) return LLA_ERR_INVALID_ARGUMENT;
+  const ParWs w = parallel_ws_layout(*d, batch, a->n_max);
+  if (!a->workspace || a->workspace_bytes < w.total) return LLA_ERR_WORKSPACE_TOO_SMALL;
+  if (!aligned16(a->workspace)) return LLA_ERR_INVALID_ARGUMENT;
+  char* ws = static_cast<char*>(a->workspace);
+
+  ParParams p{};
+  p.B = batch; p.H = d->n_heads; p.dh = d->head_dim; p.G = d->groups; p.hpg = d->n_heads / d->groups;
+  p.rk = d->r_k; p.rv = d->r_v; p.P = d->page_size; p.max_pages = st->max_pages_per_seq;
+  p.W = a->window; p.n_max = a->n_max; p.n_pad = parallel_pad(a->n_max);
+  p.rope_base = d->rope_base;
+  p.scale = (float)(1.4426950408889634 / std::sqrt((double)d->head_dim));
+  p.n_tok = a->n_tok; p.bt = st->block_table; p.pages = st->pages;
+  p.q = a->q; p.k = a->k; p.v = a->v; p.A = a->A; p.Bm = a->B; p.out = a->out;
+  p.sk = ws + w.sk; p.sv = ws + w.sv; p.qr = ws + w.qr; p.kr = ws + w.kr; p.vt = ws + w.vt;
+  p.kh = ws + w.kh; p.vht = ws + w.vht;
+  return hip_status(launch_parallel(p, static_cast<hipStream_t>(stream)));
 }
 
 size_t lla_full_decode_workspace_bytes(const lla_kv_desc* desc, int32_t batch, int32_t max_pos,

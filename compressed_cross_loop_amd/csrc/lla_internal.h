@@ -80,6 +80,32 @@ struct FullParams {
 int full_scan_heads_per_block(int dh);
 hipError_t launch_full_scan(const FullParams& p, hipStream_t s);
 
+// parallel attention over whole sequences (bf16)
+struct ParParams {
+  int32_t B, H, dh, G, hpg, rk, rv, P, max_pages, W, n_max, n_pad;
+  float rope_base;
+  float scale;                    // log2(e) / sqrt(d_h), folded into q'
+  const int32_t* n_tok;
+  const int32_t* bt;
+  const void* pages;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* A;                  // [H][d_h][r_k]
+  const void* Bm;                 // [H][d_h][r_v]
+  void* out;
+  // workspace regions (bf16)
+  void* sk;                       // [B][n_pad][G][r_k]  latents some position reads, token-major
+  void* sv;                       // [B][n_pad][G][r_v]
+  void* qr;                       // [B][n_pad][H][d_h]  R_i q * scale
+  void* kr;                       // [B][n_pad][H][d_h]  R_j k
+  void* vt;                       // [B][H][d_h][n_pad]  v, dimension-major
+  void* kh;                       // [B][n_pad][H][d_h]  rebuilt keys
+  void* vht;                      // [B][H][d_h][n_pad]  rebuilt values, dimension-major
+};
+constexpr int kParQueryTile = 256;   // positions per attention workgroup (n_pad multiple)
+hipError_t launch_parallel(const ParParams& p, hipStream_t s);
+
 hipError_t launch_qmap(const DecodeParams& p, bool want_qlat, hipStream_t s);
 hipError_t launch_window(const DecodeParams& p, hipStream_t s);
 hipError_t launch_scan_absorbed_generic(const DecodeParams& p, hipStream_t s);

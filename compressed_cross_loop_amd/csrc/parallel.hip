@@ -1,0 +1,599 @@
+// Parallel HLA attention over whole sequences: the second pass of the
+// two-pass procedure ("Hybrid Latent Attention" summary, "Training
+// Procedure"), i.e. Eq. 4 at every position i of a sequence, with Eq. 3
+// scores for the latent tokens j < i - W and the loop's exact keys and values
+// for max(0, i-W) <= j <= i.
+//
+// With many queries per latent token the keys and values are rebuilt once per
+// token, k^_j = A_t s^K_j and v^_j = B_t^T s^V_j, and attention runs in head
+// space (d_h-wide products instead of r_k- and r_v-wide ones); this equals
+// Eq. 3 when A_t commutes with the rotation (frequency-paired decoders) or
+// without rotary embedding.  Five launches:
+//
+//   k_par_prep    q' = R_i q * log2(e)/sqrt(d_h) and k' = R_j k (token-major,
+//                 bf16), v transposed to [H][d_h][tokens]; zero past n_tok
+//   k_par_gather  the latents a position can read (j < n_tok - 1 - W) as
+//                 token-major rows; the store's dimension-major value
+//                 sub-blocks are transposed through LDS; zero rows elsewhere
+//   k_gemm_nt     K^ [tokens][H d_h] = S^K A_t^T, per latent group
+//   k_gemm_nt     V^^T [H d_h][tokens] = B_t^T S^V^T (dimension-major, the
+//                 layout the attention's value product reads)
+//   k_par_attn    causal flash attention over the two key sources, one
+//                 online softmax per (position, head), exp2 domain
+//
+// k_par_attn: workgroup = (256 positions, sequence, head), four waves of 64
+// positions (four query blocks of 16).  Key tiles of 64 tokens are staged in
+// LDS (rebuilt and exact keys token-major, values dimension-major), the next
+// tile's global loads in flight while the current one is consumed; a source
+// is staged only when some position of the workgroup reads it.  Per 16-token
+// sub-tile and query block:
+//   scores  S^T[16 tok x 16 pos] = K[16 x d_h] . Q'^T   (v_mfma_f32_16x16x32_bf16)
+//           per element: j > i masked, j < i - W from the rebuilt keys, else
+//           from the exact keys
+//   values  O^T[d_h x 16 pos] += V^T[d_h x 32 tok] . P^T[32 tok x 16 pos]
+//           (v_mfma_f32_16x16x32_bf16; the 32 tokens are two sub-tiles, and
+//           each lane's 8 K values are tokens 4g..4g+3 of both, which is the
+//           score MFMA's output layout, so P never leaves registers), the
+//           latent and exact parts of P against their own values
+// Workgroups are issued longest (last positions) first.
+#include "device_common.h"
+#include "lla_internal.h"
+
+namespace lla {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kThreads = 256;
+
+// ------------------------------------------------------------------ prep
+template <int DH>
+__global__ __launch_bounds__(kThreads) void k_par_prep(ParParams p) {
+  constexpr int T = 64;   // tokens per workgroup
+  const int b = blockIdx.y, i0 = blockIdx.x * T, tid = threadIdx.x;
+  const int n = p.n_tok[b], H = p.H;
+  __shared__ float cs[T][DH / 2][2];
+  __shared__ __attribute__((aligned(16))) bf16 vtile[T][DH + 8];
+  const bool rope = p.rope_base != 0.f;
+  for (int x = tid; x < T * DH / 2; x += kThreads) {
+    const int t = x / (DH / 2), f = x % (DH / 2);
+    float c = 1.f, s = 0.f;
+    if (rope && i0 + t < n) rope_cs(p.rope_base, DH, f, i0 + t, c, s);
+    cs[t][f][0] = c;
+    cs[t][f][1] = s;
+  }
+  __syncthreads();
+  const bf16* q = static_cast<const bf16*>(p.q);
+  const bf16* k = static_cast<const bf16*>(p.k);
+  const bf16* v = static_cast<const bf16*>(p.v);
+  bf16* qr = static_cast<bf16*>(p.qr);
+  bf16* kr = static_cast<bf16*>(p.kr);
+  bf16* vt = static_cast<bf16*>(p.vt);
+  // q' and k': thread per (token, head, 8 dims); pair (f, f + d_h/2)
+  for (int x = tid; x < T * H * (DH / 8); x += kThreads) {
+    const int c8 = x % (DH / 8), th = x / (DH / 8), h = th % H, t = th / H;
+    const int i = i0 + t;
+    const int d0 = 8 * c8;
+    bf16x8 qo, ko;
+    if (i < n) {
+      const int64_t row = (((int64_t)b * p.n_max + i) * H + h) * DH;
+      const int pd = d0 < DH / 2 ? d0 + DH / 2 : d0 - DH / 2;
+      const bf16x8 qa = *reinterpret_cast<const bf16x8*>(q + row + d0);
+      const bf16x8 qp = *reinterpret_cast<const bf16x8*>(q + row + pd);
+      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(k + row + d0);
+      const bf16x8 kp = *reinterpret_cast<const bf16x8*>(k + row + pd);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int d = d0 + e;
+        const int f = d < DH / 2 ? d : d - DH / 2;
+        const float c = cs[t][f][0], s = cs[t][f][1];
+        // first half: x_f c - x_{f+h} s; second half: x_f s + x_{f+h} c
+        const float qv = d < DH / 2 ? (float)qa[e] * c - (float)qp[e] * s : (float)qp[e] * s + (float)qa[e] * c;
+        const float kv = d < DH / 2 ? (float)ka[e] * c - (float)kp[e] * s : (float)kp[e] * s + (float)ka[e] * c;
+        qo[e] = static_cast<bf16>(qv * p.scale);
+        ko[e] = static_cast<bf16>(kv);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qo[e] = ko[e] = static_cast<bf16>(0.f);
+    }
+    const int64_t orow = (((int64_t)b * p.n_pad + i) * H + h) * DH;
+    *reinterpret_cast<bf16x8*>(qr + orow + d0) = qo;
+    *reinterpret_cast<bf16x8*>(kr + orow + d0) = ko;
+  }
+  // v^T, one head at a time through LDS
+  for (int h = 0; h < H; ++h) {
+    for (int x = tid; x < T * (DH / 8); x += kThreads) {
+      const int t = x / (DH / 8), c8 = x % (DH / 8), i = i0 + t;
+      bf16x8 val;
+      if (i < n) {
+        val = *reinterpret_cast<const bf16x8*>(v + (((int64_t)b * p.n_max + i) * H + h) * DH + 8 * c8);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) val[e] = static_cast<bf16>(0.f);
+      }
+      *reinterpret_cast<bf16x8*>(&vtile[t][8 * c8]) = val;
+    }
+    __syncthreads();
+    for (int x = tid; x < DH * (T / 8); x += kThreads) {
+      const int d = x / (T / 8), t8 = 8 * (x % (T / 8));
+      bf16x8 o;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = vtile[t8 + e][d];
+      *reinterpret_cast<bf16x8*>(vt + (((int64_t)b * H + h) * DH + d) * p.n_pad + i0 + t8) = o;
+    }
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------------ gather
+// one 16-token store tile of one group per workgroup
+constexpr int kGatherDims = 512;   // value dimensions transposed per LDS round
+
+__global__ __launch_bounds__(kThreads) void k_par_gather(ParParams p) {
+  const int j0 = blockIdx.x * kTile, b = blockIdx.y, g = blockIdx.z, tid = threadIdx.x;
+  const int n = p.n_tok[b];
+  const int nl = max(0, n - 1 - p.W);    // tokens some position reads as latents
+  const int G = p.G, rk = p.rk, rv = p.rv, R = rk + rv;
+  bf16* sk = static_cast<bf16*>(p.sk) + (((int64_t)b * p.n_pad + j0) * G + g) * rk;   // row t: + t G rk
+  bf16* sv = static_cast<bf16*>(p.sv) + (((int64_t)b * p.n_pad + j0) * G + g) * rv;
+  const int nv = min(kTile, max(0, nl - j0));   // valid rows of this tile
+  bf16x8 z;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) z[e] = static_cast<bf16>(0.f);
+  const bf16* tile = nullptr;
+  if (nv > 0) {
+    const int64_t page = p.bt[(int64_t)b * p.max_pages + j0 / p.P];
+    tile = static_cast<const bf16*>(p.pages) + ((page * G + g) * (p.P / kTile) + (j0 % p.P) / kTile) * kTile * R;
+  }
+  // keys: 16 rows of r_k, token-major in the store as here
+  for (int x = tid; x < kTile * (rk / 8); x += kThreads) {
+    const int t = x / (rk / 8), c = 8 * (x % (rk / 8));
+    const bf16x8 val = t < nv ? *reinterpret_cast<const bf16x8*>(tile + t * rk + c) : z;
+    *reinterpret_cast<bf16x8*>(sk + (int64_t)t * G * rk + c) = val;
+  }
+  // values: sub-block d/16 holds [16 dims][16 tokens]
+  __shared__ __attribute__((aligned(16))) bf16 vs[kGatherDims / kTile][kTile][kTile + 8];
+  for (int d0 = 0; d0 < rv; d0 += kGatherDims) {
+    const int nd = min(kGatherDims, rv - d0);
+    if (nv > 0) {
+      for (int x = tid; x < nd * (kTile / 8); x += kThreads) {
+        const int dd = x / 2, half = 8 * (x % 2);   // dim row d0 + dd, tokens half .. half+7
+        const int d = d0 + dd;
+        const bf16x8 val = *reinterpret_cast<const bf16x8*>(tile + kTile * rk + (d / kTile) * kTile * kTile +
+                                                             (d % kTile) * kTile + half);
+        *reinterpret_cast<bf16x8*>(&vs[dd / kTile][dd % kTile][half]) = val;
+      }
+    }
+    __syncthreads();
+    for (int x = tid; x < kTile * (nd / 8); x += kThreads) {
+      const int t = x / (nd / 8), c = 8 * (x % (nd / 8));
+      bf16x8 o = z;
+      if (t < nv) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = vs[(c + e) / kTile][(c + e) % kTile][t];
+      }
+      *reinterpret_cast<bf16x8*>(sv + (int64_t)t * G * rv + d0 + c) = o;
+    }
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------------ GEMM
+// C[m][n] = sum_k X[m][k] Y[n][k] (bf16 in and out, fp32 accumulation), one
+// (batch, group) per blockIdx.z; 128 x 128 tiles, 4 waves of 64 x 64, K steps
+// of 32 staged in LDS (double-buffered, next step's loads in flight).  Rows
+// past M and N are clamped on load and skipped on store; K % 32 == 0.
+struct GemmParams {
+  const bf16* X;
+  const bf16* Y;
+  bf16* C;
+  int32_t M, N, K, ldx, ldy, ldc, G;
+  int64_t sxb, sxg, syb, syg, scb, scg;
+};
+
+__global__ __launch_bounds__(kThreads) void k_gemm_nt(GemmParams q) {
+  constexpr int BM = 128, BN = 128, BK = 32, LD = BK + 8;
+  const int z = blockIdx.z, zb = z / q.G, zg = z % q.G;
+  const bf16* X = q.X + zb * q.sxb + zg * q.sxg;
+  const bf16* Y = q.Y + zb * q.syb + zg * q.syg;
+  bf16* C = q.C + zb * q.scb + zg * q.scg;
+  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int wm = wave >> 1, wn = wave & 1;
+  __shared__ __attribute__((aligned(16))) bf16 xs[2][BM][LD];
+  __shared__ __attribute__((aligned(16))) bf16 ys[2][BN][LD];
+  // loader: 2 chunks of 16 B per thread per operand and K step
+  int xr[2], yr[2], kc[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int idx = tid + kThreads * c;
+    kc[c] = 8 * (idx % 4);
+    xr[c] = min(m0 + idx / 4, q.M - 1);
+    yr[c] = min(n0 + idx / 4, q.N - 1);
+  }
+  u32x4 rx[2], ry[2];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      rx[c] = *reinterpret_cast<const u32x4*>(X + (int64_t)xr[c] * q.ldx + k0 + kc[c]);
+      ry[c] = *reinterpret_cast<const u32x4*>(Y + (int64_t)yr[c] * q.ldy + k0 + kc[c]);
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int idx = tid + kThreads * c;
+      *reinterpret_cast<u32x4*>(&xs[buf][idx / 4][kc[c]]) = rx[c];
+      *reinterpret_cast<u32x4*>(&ys[buf][idx / 4][kc[c]]) = ry[c];
+    }
+  };
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nk = q.K / BK;
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int kk = 0; kk < nk; ++kk) {
+    const int cur = kk & 1;
+    if (kk + 1 < nk) load((kk + 1) * BK);
+    bf16x8 a[4], bb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const bf16x8*>(&xs[cur][64 * wm + 16 * i + col][8 * grp]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bb[j] = *reinterpret_cast<const bf16x8*>(&ys[cur][64 * wn + 16 * j + col][8 * grp]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bb[j], acc[i][j], 0, 0, 0);
+    if (kk + 1 < nk) store(cur ^ 1);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + 64 * wn + 16 * j + col;
+      if (n >= q.N) continue;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + 64 * wm + 16 * i + 4 * grp + r;
+        if (m < q.M) C[(int64_t)m * q.ldc + n] = static_cast<bf16>(acc[i][j][r]);
+      }
+    }
+}
+
+hipError_t launch_gemm(const GemmParams& g, int batches, hipStream_t s) {
+  const dim3 grid((g.N + 127) / 128, (g.M + 127) / 128, batches * g.G);
+  hipLaunchKernelGGL(k_gemm_nt, grid, dim3(kThreads), 0, s, g);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ attention
+template <int DH>
+__global__ __launch_bounds__(kThreads, 1) void k_par_attn(ParParams p) {
+  constexpr int KT = 64;            // keys per tile
+  constexpr int QB = 4;             // query blocks of 16 per wave
+  constexpr int KS = DH / 32;       // K steps of the score MFMA
+  constexpr int DB = DH / 16;       // 16-dim blocks of the output
+  constexpr int LDK = DH + 8;       // LDS row of a key tile (bf16)
+  constexpr int LDV = KT + 8;       // LDS row of a value^T tile
+  constexpr int CK = KT * DH / 8 / kThreads;   // 16-B chunks per thread per tile and operand
+  __shared__ __attribute__((aligned(16))) bf16 kl_s[KT * LDK];
+  __shared__ __attribute__((aligned(16))) bf16 ke_s[KT * LDK];
+  __shared__ __attribute__((aligned(16))) bf16 vl_s[DH * LDV];
+  __shared__ __attribute__((aligned(16))) bf16 ve_s[DH * LDV];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int H = p.H, W = p.W;
+  const int nqt = p.n_pad / kParQueryTile, BH = p.B * H;
+  const int L = blockIdx.x;
+  const int qt = nqt - 1 - L / BH, bh = L % BH, b = bh / H, h = bh % H;
+  const int n = p.n_tok[b];
+  const int q0 = qt * kParQueryTile;
+  if (q0 >= n) return;                                // whole workgroup
+  const int qe = min(q0 + kParQueryTile, n) - 1;      // last position of the workgroup
+  const int qw0 = q0 + 64 * wave;                     // this wave's first position
+  const bool wave_on = qw0 <= qe;
+  const int qw1 = min(qw0 + 63, qe);                  // its last valid position
+
+  const int64_t trow = (int64_t)H * DH;               // token row stride of [tokens][H][d_h]
+  const bf16* qr = static_cast<const bf16*>(p.qr) + (int64_t)b * p.n_pad * trow + h * DH;
+  const bf16* kh = static_cast<const bf16*>(p.kh) + (int64_t)b * p.n_pad * trow + h * DH;
+  const bf16* kr = static_cast<const bf16*>(p.kr) + (int64_t)b * p.n_pad * trow + h * DH;
+  const bf16* vht = static_cast<const bf16*>(p.vht) + ((int64_t)b * H + h) * DH * p.n_pad;
+  const bf16* vt = static_cast<const bf16*>(p.vt) + ((int64_t)b * H + h) * DH * p.n_pad;
+
+  bf16x8 qf[QB][KS];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qf[qb][ks] = *reinterpret_cast<const bf16x8*>(qr + (int64_t)(qw0 + 16 * qb + col) * trow + 32 * ks + 8 * grp);
+  f32x4 acc[QB][DB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m[QB], l[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m[qb] = -INFINITY;
+    l[qb] = 0.f;
+  }
+
+  // a tile's sources, for the whole workgroup: rebuilt when some j of the
+  // tile is below i - W for some position i <= qe, exact when some j lies in
+  // [i - W, i] for some i in [q0, qe]
+  auto need_lat = [&](int jt) { return jt * KT + W < qe; };
+  auto need_ex = [&](int jt) { return jt * KT + KT - 1 >= q0 - W; };
+  const int ntile = qe / KT + 1;
+
+  // The next tile's keys and values wait in registers while the current one
+  // is consumed: the rebuilt ones when the workgroup reads them, else the
+  // exact ones.  The exact source of a tile that needs both (the one to three
+  // tiles around the window edge) is copied on the spot when the tile is
+  // staged.
+  u32x4 rk_[CK], rv_[CK];
+  auto chunk_k = [&](const bf16* src, int j0, int c) {
+    const int idx = tid + kThreads * c;
+    return reinterpret_cast<const u32x4*>(src + (int64_t)(j0 + idx / (DH / 8)) * trow + 8 * (idx % (DH / 8)));
+  };
+  auto chunk_v = [&](const bf16* src, int j0, int c) {
+    const int idx = tid + kThreads * c;
+    return reinterpret_cast<const u32x4*>(src + (int64_t)(idx / (KT / 8)) * p.n_pad + j0 + 8 * (idx % (KT / 8)));
+  };
+  auto lds_k = [&](bf16* dst, int c) {
+    const int idx = tid + kThreads * c;
+    return reinterpret_cast<u32x4*>(dst + (idx / (DH / 8)) * LDK + 8 * (idx % (DH / 8)));
+  };
+  auto lds_v = [&](bf16* dst, int c) {
+    const int idx = tid + kThreads * c;
+    return reinterpret_cast<u32x4*>(dst + (idx / (KT / 8)) * LDV + 8 * (idx % (KT / 8)));
+  };
+  auto load_tile = [&](int jt) {
+    const int j0 = jt * KT;
+    const bool ln = need_lat(jt);
+    const bf16* ks = ln ? kh : kr;
+    const bf16* vs = ln ? vht : vt;
+#pragma unroll
+    for (int c = 0; c < CK; ++c) {
+      rk_[c] = *chunk_k(ks, j0, c);
+      rv_[c] = *chunk_v(vs, j0, c);
+    }
+  };
+  auto store_tile = [&](int jt) {
+    const int j0 = jt * KT;
+    const bool ln = need_lat(jt), en = need_ex(jt);
+#pragma unroll
+    for (int c = 0; c < CK; ++c) {
+      *lds_k(ln ? kl_s : ke_s, c) = rk_[c];
+      *lds_v(ln ? vl_s : ve_s, c) = rv_[c];
+    }
+    if (ln && en) {
+#pragma unroll
+      for (int c = 0; c < CK; ++c) {
+        *lds_k(ke_s, c) = *chunk_k(kr, j0, c);
+        *lds_v(ve_s, c) = *chunk_v(vt, j0, c);
+      }
+    }
+  };
+
+  // one tile: two halves of 32 keys (sub-tiles 2u, 2u+1), each scored,
+  // folded into the online softmax and multiplied into the values in turn
+  auto compute = [&](int jt) {
+    const int j0 = jt * KT;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      f32x4 sc[2][QB];
+      bool lat_u = false, ex_u = false;
+#pragma unroll
+      for (int hs = 0; hs < 2; ++hs) {
+        const int ts = 2 * u + hs;
+        const int jl = j0 + 16 * ts;   // first key of the sub-tile
+        // sources this wave needs for the sub-tile (over its positions qw0 .. qw1)
+        const bool any_l = jl + W < qw1;                       // some j < i - W
+        const bool any_e = jl + 15 >= qw0 - W && jl <= qw1;    // some i - W <= j <= i
+        lat_u |= any_l;
+        ex_u |= any_e;
+        // masked (j > i) by default; the rebuilt keys' scores where j < i - W,
+        // then the exact keys' where i - W <= j <= i
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) sc[hs][qb] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+        if (any_l) {
+          f32x4 sl[QB];
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) sl[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&kl_s[(16 * ts + col) * LDK + 32 * ks + 8 * grp]);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+              sl[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qb][ks], sl[qb], 0, 0, 0);
+          }
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (jl + 4 * grp + r < qw0 + 16 * qb + col - W) sc[hs][qb][r] = sl[qb][r];
+        }
+        if (any_e) {
+          f32x4 se[QB];
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) se[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&ke_s[(16 * ts + col) * LDK + 32 * ks + 8 * grp]);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+              se[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qb][ks], se[qb], 0, 0, 0);
+          }
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int j = jl + 4 * grp + r, i = qw0 + 16 * qb + col;
+              if (j >= i - W && j <= i) sc[hs][qb][r] = se[qb][r];
+            }
+        }
+      }
+      if (!lat_u && !ex_u) continue;   // every key of the half follows every position
+      // online softmax per position (column) over the 32 keys; sc becomes P
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        float mx = fmaxf(fmaxf(fmaxf(sc[0][qb][0], sc[0][qb][1]), fmaxf(sc[0][qb][2], sc[0][qb][3])),
+                         fmaxf(fmaxf(sc[1][qb][0], sc[1][qb][1]), fmaxf(sc[1][qb][2], sc[1][qb][3])));
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mn = fmaxf(m[qb], mx);
+        const float alpha = exp2_diff(m[qb], mn);
+        m[qb] = mn;
+        float sum = 0.f;
+#pragma unroll
+        for (int hs = 0; hs < 2; ++hs)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float pr = exp2_diff(sc[hs][qb][r], mn);
+            sc[hs][qb][r] = pr;
+            sum += pr;
+          }
+        l[qb] = l[qb] * alpha + sum;
+        if (__any(alpha != 1.f)) {
+#pragma unroll
+          for (int db = 0; db < DB; ++db) acc[qb][db] *= alpha;
+        }
+      }
+      // values: the latent and exact parts of P against their own values.
+      // The value MFMA's K index e of this lane is token 4 grp + e % 4 of
+      // sub-tile 2u + e / 4.
+      auto p_part = [&](int qb, bool latent) {
+        const int i = qw0 + 16 * qb + col;
+        bf16x8 pp;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int j = j0 + 16 * (2 * u + e / 4) + 4 * grp + e % 4;
+          pp[e] = static_cast<bf16>(((j < i - W) == latent) ? sc[e / 4][qb][e % 4] : 0.f);
+        }
+        return pp;
+      };
+      if (lat_u) {
+        bf16x8 pl[QB];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) pl[qb] = p_part(qb, true);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const bf16* vrow = &vl_s[(16 * db + col) * LDV + 32 * u + 4 * grp];
+          const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
+          const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 16);
+          const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            acc[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pl[qb], acc[qb][db], 0, 0, 0);
+        }
+      }
+      if (ex_u) {
+        bf16x8 pe[QB];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) pe[qb] = p_part(qb, false);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const bf16* vrow = &ve_s[(16 * db + col) * LDV + 32 * u + 4 * grp];
+          const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
+          const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 16);
+          const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            acc[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pe[qb], acc[qb][db], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  if (ntile > 1) load_tile(1);
+  for (int jt = 0; jt < ntile; ++jt) {
+    // a wave whose positions all precede the tile has nothing to add
+    if (wave_on && jt * KT <= qw1) compute(jt);
+    __syncthreads();
+    if (jt + 1 < ntile) store_tile(jt + 1);
+    if (jt + 2 < ntile) load_tile(jt + 2);
+    __syncthreads();
+  }
+
+  if (!wave_on) return;
+  bf16* out = static_cast<bf16*>(p.out);
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    float lt = l[qb];
+    lt += __shfl_xor(lt, 16);
+    lt += __shfl_xor(lt, 32);
+    const int i = qw0 + 16 * qb + col;
+    if (i > qe) continue;
+    const float inv = 1.f / lt;
+    bf16* orow = out + (((int64_t)b * p.n_max + i) * H + h) * DH;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      bf16x4 o;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[r] = static_cast<bf16>(acc[qb][db][r] * inv);
+      *reinterpret_cast<bf16x4*>(orow + 16 * db + 4 * grp) = o;
+    }
+  }
+}
+
+template <int DH>
+hipError_t launch_dh(const ParParams& p, hipStream_t s) {
+  hipLaunchKernelGGL((k_par_prep<DH>), dim3(p.n_pad / 64, p.B), dim3(kThreads), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_par_gather, dim3(p.n_pad / kTile, p.B, p.G), dim3(kThreads), 0, s, p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int hd = p.hpg * DH;   // output columns (rows) of one latent group
+  // K^[b][t][g hd + c] = sum_d S^K[b][t][g][d] A[g hd + c][d]
+  GemmParams gk{};
+  gk.X = static_cast<const bf16*>(p.sk);
+  gk.Y = static_cast<const bf16*>(p.A);
+  gk.C = static_cast<bf16*>(p.kh);
+  gk.M = p.n_pad; gk.N = hd; gk.K = p.rk;
+  gk.ldx = p.G * p.rk; gk.ldy = p.rk; gk.ldc = p.H * DH; gk.G = p.G;
+  gk.sxb = (int64_t)p.n_pad * p.G * p.rk; gk.sxg = p.rk;
+  gk.syb = 0; gk.syg = (int64_t)hd * p.rk;
+  gk.scb = (int64_t)p.n_pad * p.H * DH; gk.scg = hd;
+  if ((e = launch_gemm(gk, p.B, s)) != hipSuccess) return e;
+  // V^^T[b][g hd + c][t] = sum_d B^T[g hd + c][d] S^V[b][t][g][d]
+  GemmParams gv{};
+  gv.X = static_cast<const bf16*>(p.Bm);
+  gv.Y = static_cast<const bf16*>(p.sv);
+  gv.C = static_cast<bf16*>(p.vht);
+  gv.M = hd; gv.N = p.n_pad; gv.K = p.rv;
+  gv.ldx = p.rv; gv.ldy = p.G * p.rv; gv.ldc = p.n_pad; gv.G = p.G;
+  gv.sxb = 0; gv.sxg = (int64_t)hd * p.rv;
+  gv.syb = (int64_t)p.n_pad * p.G * p.rv; gv.syg = p.rv;
+  gv.scb = (int64_t)p.H * DH * p.n_pad; gv.scg = (int64_t)hd * p.n_pad;
+  if ((e = launch_gemm(gv, p.B, s)) != hipSuccess) return e;
+  const int wgs = (p.n_pad / kParQueryTile) * p.B * p.H;
+  hipLaunchKernelGGL((k_par_attn<DH>), dim3(wgs), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_parallel(const ParParams& p, hipStream_t s) {
+  if (p.dh == 128) return launch_dh<128>(p, s);
+  if (p.dh == 64) return launch_dh<64>(p, s);
+  return hipErrorNotSupported;
+}
+
+}  // namespace lla

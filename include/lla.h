@@ -48,7 +48,8 @@
 extern "C" {
 #endif
 
-#define LLA_ABI_VERSION 3   /* 2: value decoder passed as B_t^T [H][d_h][r_v]; 3: latent_fp8 */
+#define LLA_ABI_VERSION 4   /* 2: value decoder passed as B_t^T [H][d_h][r_v]; 3: latent_fp8;
+                                4: parallel attention over whole sequences */
 
 typedef void* lla_stream_t; /* a hipStream_t */
 
@@ -329,6 +330,67 @@ size_t lla_full_decode_workspace_bytes(const lla_kv_desc* desc, int32_t batch,
  * arguments. */
 int32_t lla_full_decode_plan_splits(const lla_kv_desc* desc, int32_t batch, int32_t max_pos,
                                     int32_t splits);
+
+/*
+ * ---------------------------------------------------------------------------
+ * Parallel HLA attention over whole sequences: the second pass of the
+ * two-pass procedure ([HLA] "Training Procedure": a first pass writes every
+ * token's latents -- lla_write_latents over the whole sequence -- and the
+ * second runs HLA attention at all positions at once).  Position i of
+ * sequence b gets Eq. 4 as a decode call at position i would, with the exact
+ * part taken from this loop's k, v of positions max(0, i-W) .. i:
+ *   o_i = B_t^T sum_{j < i-W} a_ij s^V_j + sum_{max(0,i-W) <= j <= i} a_ij v_j,
+ * latent scores from Eq. 3, exact scores (R_i q_i).(R_j k_j) / sqrt(d_h), one
+ * softmax per (position, head).
+ * The library rebuilds keys and values once per latent token
+ * (A_t s^K_j, B_t^T s^V_j) and attends in head space: with many queries per
+ * latent token that takes (r_k + r_v) / (2 d_h) times fewer products than
+ * scoring every query in latent space.  It equals Eq. 3 when A_t commutes
+ * with the rotation (frequency-paired decoders, [HLA] "Rotary Embedding
+ * Alignment") or when rope_base = 0 -- the same condition as
+ * lla_decode_reconstruct.
+ * ---------------------------------------------------------------------------
+ *   loop, window   t in [loop_first, loop_last]; W >= 0
+ *   n_max          positions per sequence in q, k, v and out (>= 1)
+ *   flags          must be 0
+ *   n_tok          [batch] (device) sequence lengths, 0 <= n_tok[b] <= n_max;
+ *                  positions 0 .. n_tok[b]-1.  Only latents of tokens
+ *                  j < n_tok[b] - 1 - W are read (the store must hold them);
+ *                  values outside 0..n_max are undefined behaviour
+ *   q, k, v        [batch][n_max][H][d_h], q and k before rotation; rows at
+ *                  or past n_tok[b] are never read
+ *   A, B           key decoder A_t [H][d_h][r_k], value decoder B_t^T
+ *                  [H][d_h][r_v], as for the decode entry points
+ *   out            [batch][n_max][H][d_h]; rows at or past n_tok[b] are left
+ *                  untouched
+ *   workspace      lla_parallel_workspace_bytes() bytes, contents irrelevant
+ * Supported: bf16 sets with latent_fp8 = 0, d_h in {64, 128}, r_k and r_v
+ * multiples of 32, rope_base = 0 or rope_baked = 1; other valid sets return
+ * LLA_ERR_UNSUPPORTED.  The block table must cover max(0, n_max - 1 - W)
+ * tokens (max_pages_per_seq * page_size).  Pointers 16-byte aligned.  Errors
+ * as for the decode entry points (validation before any launch).
+ */
+typedef struct {
+  int32_t loop;
+  int32_t window;
+  int32_t n_max;
+  int32_t flags;
+  const int32_t* n_tok;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* A;
+  const void* B;
+  void* out;
+  void* workspace;
+  size_t workspace_bytes;
+} lla_parallel_args;
+
+lla_status hla_attention_parallel(const lla_set_desc* desc, const lla_store* store, int32_t batch,
+                                  const lla_parallel_args* args, lla_stream_t stream);
+
+/* Workspace bytes hla_attention_parallel needs; 0 on invalid arguments. */
+size_t lla_parallel_workspace_bytes(const lla_set_desc* desc, int32_t batch, int32_t n_max);
 
 #ifdef __cplusplus
 }

@@ -204,6 +204,60 @@ def fp8_latent_draws(seed: int, *, n_pages: int, groups: int, page_size: int, r_
 
 
 @dataclass
+class ParallelInputs:
+    """One parallel-pass call's inputs (CPU tensors): latent store pages
+    [n_pages, G*P*(r_k+r_v)] (the store layout), block_table [B, pages],
+    n_tok [B], q, k, v [B, n_max, H, d_h], A [H, d_h, r_k], Bv [H, r_v, d_h]."""
+    heads: int
+    head_dim: int
+    groups: int
+    r_k: int
+    r_v: int
+    page_size: int
+    window: int
+    rope_base: float
+    rope_baked: int
+    pages: torch.Tensor
+    block_table: torch.Tensor
+    n_tok: torch.Tensor
+    q: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    A: torch.Tensor
+    Bv: torch.Tensor
+
+
+def parallel_inputs(seed: int, *, batch: int, heads: int, head_dim: int, groups: int, r_k: int, r_v: int,
+                    n_max: int, n_tok, window: int, dtype: str = "bf16", page_size: int = 64,
+                    rope_base: float = 0.0, paired: Optional[bool] = None, latent_std: float = 1.0,
+                    exact_std: float = 1.0, spare_pages: int = 2) -> ParallelInputs:
+    """Latents ~ N(0, latent_std^2) for every slot of every page; q ~ N(0, 1);
+    k, v ~ N(0, exact_std^2); A frequency-paired (complex coefficients) when
+    `paired` (default: with rotary embedding), Gaussian-QR otherwise; B
+    Gaussian-QR.  Sequences own random pages covering n_max tokens."""
+    g = rng(seed, 9)
+    pps = max(1, -(-n_max // page_size))
+    bt, n_pages = block_table(g, batch, pps, spare_pages)
+    pages = g.standard_normal((n_pages, groups * page_size * (r_k + r_v))) * latent_std
+    q = g.standard_normal((batch, n_max, heads, head_dim))
+    k = g.standard_normal((batch, n_max, heads, head_dim)) * exact_std
+    v = g.standard_normal((batch, n_max, heads, head_dim)) * exact_std
+    if paired is None:
+        paired = rope_base != 0
+    if paired:
+        A = frequency_paired_decoder(g, heads, head_dim, r_k)
+    else:
+        A = np.stack([gaussian_orthonormal(g, head_dim, r_k) for _ in range(heads)])
+    Bv = np.stack([gaussian_orthonormal(g, r_v, head_dim) for _ in range(heads)])
+    return ParallelInputs(heads=heads, head_dim=head_dim, groups=groups, r_k=r_k, r_v=r_v, page_size=page_size,
+                          window=window, rope_base=rope_base, rope_baked=1 if rope_base else 0,
+                          pages=as_stored(pages, dtype), block_table=torch.from_numpy(bt),
+                          n_tok=torch.from_numpy(np.asarray(n_tok, dtype=np.int32).reshape(batch)),
+                          q=as_stored(q, dtype), k=as_stored(k, dtype), v=as_stored(v, dtype),
+                          A=as_stored(A, dtype), Bv=as_stored(Bv, dtype))
+
+
+@dataclass
 class KvCacheInputs:
     """One full-cache decode call's inputs (CPU tensors): k_pages, v_pages
     [n_pages, P, H, d_h] with every slot a call must not read (positions >= i

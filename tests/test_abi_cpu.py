@@ -32,7 +32,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert B.lla_abi_version() == 3 == B.ABI_VERSION
+    assert B.lla_abi_version() == 4 == B.ABI_VERSION
     for s in range(5):
         assert B.lla_status_string(s)
     assert B.lla_status_string(99) == "unknown status"
@@ -279,3 +279,64 @@ def test_fp8_reconstruct_is_unsupported():
     st = B.LlaStore(FAKE, FAKE, 4)
     assert B.lib.lla_decode_reconstruct(ctypes.byref(d), ctypes.byref(st), 4, ctypes.byref(_args()), None) \
         == B.LLA_ERR_UNSUPPORTED
+
+
+def _par_call(desc="ok", store="ok", batch=2, **kw):
+    d = hla_main() if isinstance(desc, str) else desc
+    st = B.LlaStore(FAKE, FAKE, 64) if store == "ok" else store
+    a = dict(loop=3, window=128, n_max=4096, flags=0, n_tok=FAKE, q=FAKE, k=FAKE, v=FAKE, A=FAKE, B=FAKE,
+             out=FAKE, workspace=FAKE, workspace_bytes=1 << 40)
+    a.update(kw)
+    args = B.LlaParallelArgs(*[a[f] for f, _ in B.LlaParallelArgs._fields_])
+    return B.lib.hla_attention_parallel(ctypes.byref(d) if d is not None else None,
+                                        ctypes.byref(st) if st is not None else None, batch,
+                                        ctypes.byref(args), None)
+
+
+@pytest.mark.parametrize("bad, want", [
+    (dict(dtype=B.LLA_F32), B.LLA_ERR_UNSUPPORTED),
+    (dict(latent_fp8=1), B.LLA_ERR_UNSUPPORTED),
+    (dict(head_dim=96, r_k=480, r_v=480), B.LLA_ERR_UNSUPPORTED),
+    (dict(r_k=496, rope_baked=0, rope_base=0.0), B.LLA_ERR_UNSUPPORTED),
+    (dict(rope_baked=0), B.LLA_ERR_UNSUPPORTED),
+    (dict(groups=3), B.LLA_ERR_INVALID_ARGUMENT),
+    (dict(page_size=8), B.LLA_ERR_INVALID_ARGUMENT),
+])
+def test_parallel_descriptor_errors(bad, want):
+    assert _par_call(desc=hla_main(**bad)) == want
+    assert B.lla_parallel_workspace_bytes(hla_main(**bad), 2, 100) == 0
+
+
+@pytest.mark.parametrize("kw, want", [
+    (dict(flags=1), B.LLA_ERR_INVALID_ARGUMENT),
+    (dict(loop=1), B.LLA_ERR_INVALID_ARGUMENT),
+    (dict(loop=5), B.LLA_ERR_INVALID_ARGUMENT),
+    (dict(window=-1), B.LLA_ERR_INVALID_ARGUMENT),
+    (dict(n_max=0), B.LLA_ERR_INVALID_ARGUMENT),
+    (dict(n_tok=None), B.LLA_ERR_INVALID_ARGUMENT),
+    (dict(v=FAKE + 2), B.LLA_ERR_INVALID_ARGUMENT),
+    (dict(B=None), B.LLA_ERR_INVALID_ARGUMENT),
+    (dict(n_max=64 * 64 + 130), B.LLA_ERR_INVALID_ARGUMENT),       # block table covers 4096 latent tokens
+    (dict(workspace_bytes=1 << 20), B.LLA_ERR_WORKSPACE_TOO_SMALL),
+    (dict(workspace=None), B.LLA_ERR_WORKSPACE_TOO_SMALL),
+    (dict(workspace=FAKE + 8), B.LLA_ERR_INVALID_ARGUMENT),
+])
+def test_parallel_argument_errors(kw, want):
+    assert _par_call(**kw) == want
+
+
+def test_parallel_null_structs_and_workspace():
+    assert _par_call(desc=None) == B.LLA_ERR_INVALID_ARGUMENT
+    assert _par_call(store=None) == B.LLA_ERR_INVALID_ARGUMENT
+    assert _par_call(store=B.LlaStore(FAKE, FAKE, 0)) == B.LLA_ERR_INVALID_ARGUMENT
+    assert _par_call(batch=0) == B.LLA_ERR_INVALID_ARGUMENT
+    d = hla_main()
+    # W + 1 >= n_max: no latent is read, so any block table will do
+    assert _par_call(store=B.LlaStore(FAKE, FAKE, 1), n_max=129, workspace_bytes=16) == \
+        B.LLA_ERR_WORKSPACE_TOO_SMALL
+    w = B.lla_parallel_workspace_bytes
+    assert w(d, 2, 100) == w(d, 2, 256) < w(d, 2, 257) < w(d, 4, 257)
+    # rebuilt and exact keys / values plus rotated queries: 5 head-space rows
+    # of bf16 per padded position, and the gathered latents
+    assert w(d, 1, 256) >= 256 * (5 * 16 * 128 + 1024) * 2
+    assert w(d, 0, 256) == 0 and w(d, 1, 0) == 0
