@@ -25,6 +25,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "decode tokens/s and achieved HBM GB/s (% roofline), Ouro-1.4B shape, 4k ctx"
+METRIC_PARALLEL = "parallel-pass positions/s and attention MFMA TFLOP/s (% roofline), Ouro-1.4B shape"
 
 
 def parse():
@@ -36,9 +37,13 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--splits", type=int, default=0)
-    ap.add_argument("--entry", choices=["auto", "hla", "absorbed", "reconstruct", "full"], default="auto",
+    ap.add_argument("--entry", choices=["auto", "hla", "absorbed", "reconstruct", "full", "parallel"],
+                    default="auto",
                     help="decode entry point (auto: hla for HLA workloads, reconstruct for LLA ones; "
-                         "full: the uncompressed per-loop cache at the workload's attention shape)")
+                         "full: the uncompressed per-loop cache at the workload's attention shape; "
+                         "parallel: the second pass over whole sequences, batch 8 x 2048 positions "
+                         "unless --batch / --context say otherwise)")
+    ap.add_argument("--context", type=int, default=0, help="override the context / sequence length (0 = default)")
     ap.add_argument("--batch", type=int, default=0, help="override the workload's batch (0 = workload's)")
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = workload's)")
     ap.add_argument("--latent-fp8", action="store_true",
@@ -209,6 +214,89 @@ class DecodeStep:
         return total, per_call
 
 
+class ParallelStep:
+    """One step of the parallel (second) pass over whole sequences, every
+    layer: the latent writes of every token (both sets), then one parallel
+    attention call per (layer, loop) in loop order.  Every layer and loop has
+    its own store, maps and q / k / v."""
+
+    def __init__(self, w, seed=0):
+        import torch
+        from compressed_cross_loop_amd import binding as B
+        from synth import gen
+        self.torch, self.B, self.w = torch, B, w
+        dev = "cuda"
+        L, T, H, dh, Bt, P, W, n = w.layers, w.loops, w.heads, w.head_dim, w.batch, w.page_size, w.window, w.context
+        pps = -(-n // P)
+        self.sets = []
+        for k, s in enumerate(w.sets):
+            desc = B.set_desc(n_heads=H, head_dim=dh, groups=s.groups, r_k=s.r_k, r_v=s.r_v,
+                              loop_first=s.loop_first, loop_last=s.loop_last, page_size=P,
+                              rope_baked=w.rope_baked, rope_base=w.rope_base, dtype=B.LLA_BF16)
+            bt = torch.from_numpy(gen.block_table(gen.rng(seed, 79, k), Bt, pps)[0]).to(dev)
+            row = s.groups * P * (s.r_k + s.r_v)
+            pages = [gen.device_normal((Bt * pps, row), "bf16", seed * 1000 + 10 * l + k) for l in range(L)]
+            enc = [gen.device_normal((s.n_loops, s.groups, s.r_k + s.r_v, s.d_in), "bf16",
+                                     seed * 1000 + 500 + 10 * l + k, 1.0 / np.sqrt(s.d_in)) for l in range(L)]
+            x = [gen.device_normal((Bt, n, s.n_loops, s.groups, s.d_in), "bf16", seed * 1000 + 700 + 10 * l + k)
+                 for l in range(L)]
+            self.sets.append(dict(spec=s, desc=desc, enc=enc, x=x, stores=[B.store(pg, bt) for pg in pages]))
+        self.wpos = torch.arange(n, dtype=torch.int32, device=dev).repeat(Bt, 1).contiguous()
+        self.n_tok = torch.full((Bt,), n, dtype=torch.int32, device=dev)
+        ws = max(B.lla_parallel_workspace_bytes(st["desc"], Bt, n) for st in self.sets)
+        self.ws = torch.empty(ws, dtype=torch.uint8, device=dev)
+        wws = max(B.lla_write_workspace_bytes(st["desc"], Bt, n, st["spec"].d_in) for st in self.sets)
+        self.wws = torch.empty(max(wws, 256), dtype=torch.uint8, device=dev)
+        self.out = torch.empty((Bt, n, H, dh), dtype=torch.bfloat16, device=dev)
+        self.calls = []
+        for t in range(1, T + 1):
+            k = w.set_for_loop(t)
+            s = w.sets[k]
+            for l in range(L):
+                sd = seed * 100000 + 1000 * t + 10 * l
+                q = gen.device_normal((Bt, n, H, dh), "bf16", sd + 1)
+                kk = gen.device_normal((Bt, n, H, dh), "bf16", sd + 2, float(np.sqrt(s.n_loops)))
+                vv = gen.device_normal((Bt, n, H, dh), "bf16", sd + 3, float(np.sqrt(s.n_loops)))
+                A = gen.device_normal((H, dh, s.r_k), "bf16", sd + 6, 1.0 / np.sqrt(s.r_k))
+                Bm = gen.device_normal((H, dh, s.r_v), "bf16", sd + 7, 1.0 / np.sqrt(s.r_v))   # B_t^T
+                args = B.parallel_args(loop=t, window=W, n_tok=self.n_tok, q=q, k=kk, v=vv, A=A, B=Bm,
+                                       out=self.out, workspace=self.ws)
+                self.calls.append((t, k, l, self.sets[k]["desc"], self.sets[k]["stores"][l], args, None))
+        self.entry_name = "parallel"
+        self.entry = B.hla_attention_parallel
+        torch.cuda.synchronize()
+
+    def step(self):
+        B = self.B
+        for l in range(self.w.layers):
+            for st in self.sets:
+                B.lla_write_latents(st["desc"], st["stores"][l], pos=self.wpos, x=st["x"][l], enc=st["enc"][l],
+                                    workspace=self.wws)
+        for (t, k, l, desc, st, args, _) in self.calls:
+            self.entry(desc, st, self.w.batch, args)
+
+    def attn_flop(self):
+        """Algorithmic FLOPs of one attention kernel launch: causal attention in
+        head space, 4 d_h per (position, key) pair, n (n+1) / 2 pairs per
+        sequence and head."""
+        w = self.w
+        return 4 * w.head_dim * w.batch * w.heads * w.context * (w.context + 1) // 2
+
+    def step_bytes(self):
+        """(step FLOPs, per-call {set: (attention FLOPs, _, _)}): the step's
+        matrix work -- writer GEMMs, key/value rebuild GEMMs, attention."""
+        w = self.w
+        tok = w.batch * w.context
+        total = 0
+        per_call = {}
+        for k, s in enumerate(w.sets):
+            writer = 2 * tok * s.n_loops * s.groups * (s.r_k + s.r_v) * s.d_in
+            rebuild = 2 * tok * (s.r_k + s.r_v) * w.heads * w.head_dim
+            total += w.layers * writer + w.layers * s.n_loops * (rebuild + self.attn_flop())
+            per_call[k] = (self.attn_flop(), None, self.attn_flop())
+        return total, per_call
+
+
 class FullStep:
     """Every buffer of one decode step of the uncompressed model: one exact
     paged K/V cache per (layer, loop), the same attention shape and context as
@@ -296,6 +384,48 @@ def cpu_baseline_full(w, budget_s, seed=0):
         "host_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
         "sample": (f"oracle full_cache_decode (fp64 numpy) on {n} whole sequences ({t_call * 1e3:.1f} ms/seq/call) "
                    f"in {time.perf_counter() - t0:.1f} s, scaled to {w.layers} layers x {w.loops} loops per token"),
+    }
+
+
+def cpu_baseline_parallel(w, budget_s, seed=0):
+    """The fp64 oracle's parallel_attention, timed on the host cores on
+    evenly spaced positions of one sequence per set (a position's cost grows
+    with its index, so their mean is the mean over the sequence), scaled to
+    tokens/s of the full step (attention only: B n positions per step over
+    L T calls)."""
+    import threadpoolctl
+    import oracle as O
+    from synth import gen
+    H, dh, W, n = w.heads, w.head_dim, w.window, w.context
+    g = gen.rng(seed, 992)
+    t_row = []
+    n_rows = 0
+    t0 = time.perf_counter()
+    for s in w.sets:
+        sK = [g.standard_normal((n, s.groups, s.r_k))]
+        sV = [g.standard_normal((n, s.groups, s.r_v))]
+        q, k, v = (g.standard_normal((1, n, H, dh)) for _ in range(3))
+        A = g.standard_normal((H, dh, s.r_k)) / np.sqrt(s.r_k)
+        Bv = g.standard_normal((H, s.r_v, dh)) / np.sqrt(s.r_v)
+        rows, ts = 0, time.perf_counter()
+        for step in range(256):
+            i = int((step + 0.5) * n / 256)
+            O.parallel_attention(sK, sV, [n], q, k, v, A, Bv, window=W, rope_base=w.rope_base, rows=[(0, i)])
+            rows += 1
+            if time.perf_counter() - ts >= budget_s / len(w.sets):
+                break
+        t_row.append((time.perf_counter() - ts) / rows)
+        n_rows += rows
+    t_call = [w.batch * n * t for t in t_row]                   # one (layer, loop) call
+    t_step = sum(w.layers * w.sets[k].n_loops * t_call[k] for k in range(len(w.sets)))
+    info = threadpoolctl.threadpool_info()
+    return {
+        "value": w.batch * n / t_step, "unit": "tokens/s", "cores": int(max([d.get("num_threads", 1) for d in info] or [1])),
+        "host_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
+        "sample": (f"oracle parallel_attention (fp64 numpy) on {n_rows} evenly spaced positions (all heads) of one "
+                   f"{n}-position sequence per set in {time.perf_counter() - t0:.1f} s "
+                   f"({', '.join(f'{t * 1e3:.1f} ms/position set{k}' for k, t in enumerate(t_row))}), scaled to "
+                   f"{w.batch} x {n} positions x {w.layers} layers x {w.loops} loops (attention only)"),
     }
 
 
@@ -433,22 +563,32 @@ def main():
     hip = Hip()
     if a.layers:
         w = w.with_(layers=a.layers)
-    if a.batch:
-        w = w.with_(batch=a.batch, name=f"{w.name}@b{a.batch}")
-    if a.entry == "full":
-        w = w.with_(name=f"full-cache-L{w.layers}xT{w.loops}-h{w.heads}x{w.head_dim}-b{w.batch}-ctx{w.context}")
-        try:
-            st = FullStep(w, splits=a.splits)
-        except MemoryError as err:
-            print(json.dumps({"error": str(err), "config": {"workload": w.name}}))
-            sys.exit(3)
+    if a.entry == "parallel":
+        if w.family != "hla" or w.dtype != "bf16":
+            print(json.dumps({"error": "the parallel pass runs on the HLA bf16 workloads"}))
+            sys.exit(2)
+        w = w.with_(batch=a.batch or 8, context=a.context or 2048)
+        w = w.with_(name=f"hla-parallel-ouro1.4b-b{w.batch}-n{w.context}")
+        st = ParallelStep(w)
     else:
-        if a.latent_fp8:
-            if a.entry == "reconstruct" or (a.entry == "auto" and w.family != "hla") or w.dtype != "bf16":
-                print(json.dumps({"error": "fp8 latents serve the absorbed / HLA reads of bf16 workloads"}))
-                sys.exit(2)
-            w = w.with_(name=f"{w.name}-fp8")
-        st = DecodeStep(w, splits=a.splits, entry=a.entry, fp8=a.latent_fp8)
+        if a.batch:
+            w = w.with_(batch=a.batch, name=f"{w.name}@b{a.batch}")
+        if a.context:
+            w = w.with_(context=a.context, name=f"{w.name}@ctx{a.context}")
+        if a.entry == "full":
+            w = w.with_(name=f"full-cache-L{w.layers}xT{w.loops}-h{w.heads}x{w.head_dim}-b{w.batch}-ctx{w.context}")
+            try:
+                st = FullStep(w, splits=a.splits)
+            except MemoryError as err:
+                print(json.dumps({"error": str(err), "config": {"workload": w.name}}))
+                sys.exit(3)
+        else:
+            if a.latent_fp8:
+                if a.entry == "reconstruct" or (a.entry == "auto" and w.family != "hla") or w.dtype != "bf16":
+                    print(json.dumps({"error": "fp8 latents serve the absorbed / HLA reads of bf16 workloads"}))
+                    sys.exit(2)
+                w = w.with_(name=f"{w.name}-fp8")
+            st = DecodeStep(w, splits=a.splits, entry=a.entry, fp8=a.latent_fp8)
     stream = torch.cuda.current_stream().cuda_stream
     for _ in range(max(1, a.warmup)):
         st.step()
@@ -482,17 +622,21 @@ def main():
     rsteps = max(2, min(a.steps, 5))
     for _ in range(rsteps):
         for (t, k, l, desc, stc, args, _) in st.calls:
+            ev_field = "attn_events" if st.entry_name == "parallel" else "scan_events"
             if k == main_k:
                 pair = (ctypes.c_void_p * 2)(hip.event().value, hip.event().value)
-                args.scan_events = ctypes.addressof(pair)
+                setattr(args, ev_field, ctypes.addressof(pair))
                 evs.append(pair)
             st.entry(desc, stc, w.batch, args)
-            args.scan_events = None
+            setattr(args, ev_field, None)
     torch.cuda.synchronize()
     scan_ms = float(np.mean([hip.elapsed_ms(ctypes.c_void_p(p[0]), ctypes.c_void_p(p[1])) for p in evs]))
     scan_bytes, _, scan_flop = per_call[main_k]
     if st.entry_name == "full":
         kname, loops_served = "k_full_scan", (1, w.loops)
+    elif st.entry_name == "parallel":
+        s_main = w.sets[main_k]
+        kname, loops_served = "k_par_attn", (s_main.loop_first, s_main.loop_last)
     else:
         s_main = w.sets[main_k]
         loops_served = (s_main.loop_first, s_main.loop_last)
@@ -501,7 +645,7 @@ def main():
         main_desc = next(c[3] for c in st.calls if c[1] == main_k)
         kname = st.B.lla_decode_scan_kernel(main_desc, ENTRY_CODE[st.entry_name])
     reconstruct_mfma_bound = st.entry_name == "reconstruct" and scan_flop / scan_bytes > 312
-    if reconstruct_mfma_bound:
+    if reconstruct_mfma_bound or st.entry_name == "parallel":
         roof = {"bound": "mfma", "achieved": scan_flop / (scan_ms * 1e-3) / 1e12, "peak": 2500.0,
                 "unit": "TFLOP/s"}
     else:
@@ -513,9 +657,11 @@ def main():
                                          f"set serving loops {loops_served[0]}..{loops_served[1]}") + ")",
                  "avg_launch_ms": scan_ms, "bytes_per_launch": scan_bytes, "flop_per_launch": scan_flop})
 
+    parallel = st.entry_name == "parallel"
     gbs = step_bytes / (ms * 1e-3) / 1e9
     rec = {
-        "metric": METRIC, "value": w.batch / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "metric": METRIC_PARALLEL if parallel else METRIC,
+        "value": w.batch * (w.context if parallel else 1) / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
         "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "entry": st.entry_name, "layers": w.layers, "loops": w.loops,
@@ -526,13 +672,21 @@ def main():
                              for s in w.sets]),
                    "splits": a.splits or "auto", "launch": "eager" if a.no_graph else "hip_graph",
                    "latents": "e4m3+scale" if getattr(st, "fp8", False) else w.dtype},
-        "step_bytes": step_bytes, "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
         "stream_copy_gbs": stream_copy_gbs(),
         "roofline": roof,
     }
+    if parallel:
+        # step_bytes holds the step's matrix FLOPs here (writer, rebuild, attention)
+        rec.update({"step_flop": step_bytes, "step_tflops": step_bytes / (ms * 1e-3) / 1e12})
+    else:
+        rec.update({"step_bytes": step_bytes, "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS})
     if not a.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline_full(w, a.cpu_seconds) if st.entry_name == "full" else \
-            cpu_baseline(w, a.cpu_seconds, entry=st.entry_name, fp8=getattr(st, "fp8", False))
+        if st.entry_name == "full":
+            rec["cpu_baseline"] = cpu_baseline_full(w, a.cpu_seconds)
+        elif parallel:
+            rec["cpu_baseline"] = cpu_baseline_parallel(w, a.cpu_seconds)
+        else:
+            rec["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds, entry=st.entry_name, fp8=getattr(st, "fp8", False))
     print(json.dumps(rec))
 
 

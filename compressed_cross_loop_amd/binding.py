@@ -72,7 +72,8 @@ class LlaParallelArgs(ctypes.Structure):
     _fields_ = [("loop", ctypes.c_int32), ("window", ctypes.c_int32), ("n_max", ctypes.c_int32),
                 ("flags", ctypes.c_int32), ("n_tok", ctypes.c_void_p), ("q", ctypes.c_void_p),
                 ("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("A", ctypes.c_void_p), ("B", ctypes.c_void_p),
-                ("out", ctypes.c_void_p), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+                ("out", ctypes.c_void_p), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("attn_events", ctypes.c_void_p)]
 
 
 if not os.path.exists(LIB_PATH):
@@ -285,12 +286,14 @@ def lla_full_decode_plan_splits(desc, batch, max_pos, splits=0):
     return lib.lla_full_decode_plan_splits(ctypes.byref(desc), batch, max_pos, splits)
 
 
-def parallel_args(*, loop, window, n_tok, q, k, v, A, B, out, workspace, flags=0):
-    """n_tok [batch] int32; q, k, v, out [batch, n_max, H, d_h]; A [H, d_h, r_k]; B = B_t^T [H, d_h, r_v]."""
+def parallel_args(*, loop, window, n_tok, q, k, v, A, B, out, workspace, flags=0, attn_events=None):
+    """n_tok [batch] int32; q, k, v, out [batch, n_max, H, d_h]; A [H, d_h, r_k]; B = B_t^T [H, d_h, r_v];
+    attn_events: optional ctypes array of two hipEvent_t handles."""
     ws_bytes = 0 if workspace is None or isinstance(workspace, int) else \
         workspace.numel() * workspace.element_size()
+    ev = ctypes.cast(attn_events, ctypes.c_void_p) if attn_events is not None else None
     args = LlaParallelArgs(loop, window, int(q.shape[1]), flags, _ptr(n_tok), _ptr(q), _ptr(k), _ptr(v), _ptr(A),
-                           _ptr(B), _ptr(out), _ptr(workspace), ws_bytes)
+                           _ptr(B), _ptr(out), _ptr(workspace), ws_bytes, ev)
     args._keep = (n_tok, q, k, v, A, B, out, workspace)
     return args
 

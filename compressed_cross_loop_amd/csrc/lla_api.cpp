@@ -436,7 +436,7 @@ lla_status hla_attention_parallel(const lla_set_desc* d, const lla_store* st, in
   p.q = a->q; p.k = a->k; p.v = a->v; p.A = a->A; p.Bm = a->B; p.out = a->out;
   p.sk = ws + w.sk; p.sv = ws + w.sv; p.qr = ws + w.qr; p.kr = ws + w.kr; p.vt = ws + w.vt;
   p.kh = ws + w.kh; p.vht = ws + w.vht;
-  return hip_status(launch_parallel(p, static_cast<hipStream_t>(stream)));
+  return hip_status(launch_parallel(p, static_cast<hipStream_t>(stream), static_cast<hipEvent_t*>(a->attn_events)));
 }
 
 size_t lla_full_decode_workspace_bytes(const lla_kv_desc* desc, int32_t batch, int32_t max_pos,

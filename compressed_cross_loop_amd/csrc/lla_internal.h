@@ -104,7 +104,8 @@ struct ParParams {
   void* vht;                      // [B][H][d_h][n_pad]  rebuilt values, dimension-major
 };
 constexpr int kParQueryTile = 256;   // positions per attention workgroup (n_pad multiple)
-hipError_t launch_parallel(const ParParams& p, hipStream_t s);
+// events: optional pair recorded around the attention kernel
+hipError_t launch_parallel(const ParParams& p, hipStream_t s, hipEvent_t* events);
 
 hipError_t launch_qmap(const DecodeParams& p, bool want_qlat, hipStream_t s);
 hipError_t launch_window(const DecodeParams& p, hipStream_t s);

@@ -21,8 +21,11 @@
 //   k_par_attn    causal flash attention over the two key sources, one
 //                 online softmax per (position, head), exp2 domain
 //
-// k_par_attn: workgroup = (256 positions, sequence, head), four waves of 64
-// positions (four query blocks of 16).  Key tiles of 64 tokens are staged in
+// k_par_attn: workgroup = (128 positions, sequence, head), four waves of 32
+// positions (two query blocks of 16), two workgroups per CU (the second
+// wave on each SIMD runs its MFMAs while the first works through its
+// softmax; a wave of 64 positions needs more than the 256 registers that
+// allows and was 1.6x slower).  Key tiles of 64 tokens are staged in
 // LDS (rebuilt and exact keys token-major, values dimension-major), the next
 // tile's global loads in flight while the current one is consumed; a source
 // is staged only when some position of the workgroup reads it.  Per 16-token
@@ -50,20 +53,33 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
+constexpr float kLazy = 8.f;   // running-max slack of the attention softmax (exp2 units)
+constexpr int kAttnQB = 2;                  // query blocks of 16 positions per wave
+constexpr int kAttnQT = 4 * 16 * kAttnQB;   // positions per attention workgroup (4 waves)
+static_assert(kParQueryTile % kAttnQT == 0, "padding must cover whole query tiles");
 
 // ------------------------------------------------------------------ prep
+// workgroup = (64 positions, sequence, hpw heads); every thread first loads
+// all of its items, then rotates and stores them (one memory round trip)
+constexpr int kPrepTokens = 64;
+
 template <int DH>
-__global__ __launch_bounds__(kThreads) void k_par_prep(ParParams p) {
-  constexpr int T = 64;   // tokens per workgroup
-  const int b = blockIdx.y, i0 = blockIdx.x * T, tid = threadIdx.x;
+__global__ __launch_bounds__(kThreads) void k_par_prep(ParParams p, int hpw) {
+  constexpr int T = kPrepTokens;
+  constexpr int C8 = DH / 8;                      // 16-byte chunks per head row
+  constexpr int IPT = 4;                          // items per thread per round
+  const int b = blockIdx.y, i0 = blockIdx.x * T, h0 = blockIdx.z * hpw, tid = threadIdx.x;
   const int n = p.n_tok[b], H = p.H;
   __shared__ float cs[T][DH / 2][2];
+  __shared__ double theta[DH / 2];
   __shared__ __attribute__((aligned(16))) bf16 vtile[T][DH + 8];
   const bool rope = p.rope_base != 0.f;
+  if (tid < DH / 2) theta[tid] = rope ? rope_theta(p.rope_base, DH, tid) : 0.0;
+  __syncthreads();
   for (int x = tid; x < T * DH / 2; x += kThreads) {
     const int t = x / (DH / 2), f = x % (DH / 2);
     float c = 1.f, s = 0.f;
-    if (rope && i0 + t < n) rope_cs(p.rope_base, DH, f, i0 + t, c, s);
+    if (rope && i0 + t < n) rope_cs_theta(theta[f], i0 + t, c, s);
     cs[t][f][0] = c;
     cs[t][f][1] = s;
   }
@@ -74,49 +90,59 @@ __global__ __launch_bounds__(kThreads) void k_par_prep(ParParams p) {
   bf16* qr = static_cast<bf16*>(p.qr);
   bf16* kr = static_cast<bf16*>(p.kr);
   bf16* vt = static_cast<bf16*>(p.vt);
-  // q' and k': thread per (token, head, 8 dims); pair (f, f + d_h/2)
-  for (int x = tid; x < T * H * (DH / 8); x += kThreads) {
-    const int c8 = x % (DH / 8), th = x / (DH / 8), h = th % H, t = th / H;
-    const int i = i0 + t;
-    const int d0 = 8 * c8;
-    bf16x8 qo, ko;
-    if (i < n) {
-      const int64_t row = (((int64_t)b * p.n_max + i) * H + h) * DH;
-      const int pd = d0 < DH / 2 ? d0 + DH / 2 : d0 - DH / 2;
-      const bf16x8 qa = *reinterpret_cast<const bf16x8*>(q + row + d0);
-      const bf16x8 qp = *reinterpret_cast<const bf16x8*>(q + row + pd);
-      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(k + row + d0);
-      const bf16x8 kp = *reinterpret_cast<const bf16x8*>(k + row + pd);
+  bf16x8 z;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) z[e] = static_cast<bf16>(0.f);
+  // q' and k': item = (token, head, 8 dims); pair (f, f + d_h/2)
+  const int items = T * hpw * C8;
+  for (int x0 = 0; x0 < items; x0 += IPT * kThreads) {
+    bf16x8 qa[IPT], qp[IPT], ka[IPT], kp[IPT];
+#pragma unroll
+    for (int u = 0; u < IPT; ++u) {
+      const int x = x0 + u * kThreads + tid;
+      const int c8 = x % C8, th = x / C8, h = h0 + th % hpw, t = th / hpw, i = i0 + t;
+      qa[u] = qp[u] = ka[u] = kp[u] = z;
+      if (x < items && i < n) {
+        const int64_t row = (((int64_t)b * p.n_max + i) * H + h) * DH;
+        const int d0 = 8 * c8, pd = d0 < DH / 2 ? d0 + DH / 2 : d0 - DH / 2;
+        qa[u] = *reinterpret_cast<const bf16x8*>(q + row + d0);
+        qp[u] = *reinterpret_cast<const bf16x8*>(q + row + pd);
+        ka[u] = *reinterpret_cast<const bf16x8*>(k + row + d0);
+        kp[u] = *reinterpret_cast<const bf16x8*>(k + row + pd);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < IPT; ++u) {
+      const int x = x0 + u * kThreads + tid;
+      if (x >= items) continue;
+      const int c8 = x % C8, th = x / C8, h = h0 + th % hpw, t = th / hpw, i = i0 + t;
+      const int d0 = 8 * c8;
+      bf16x8 qo, ko;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int d = d0 + e;
         const int f = d < DH / 2 ? d : d - DH / 2;
-        const float c = cs[t][f][0], s = cs[t][f][1];
+        const float c = cs[t][f][0], sn = cs[t][f][1];
         // first half: x_f c - x_{f+h} s; second half: x_f s + x_{f+h} c
-        const float qv = d < DH / 2 ? (float)qa[e] * c - (float)qp[e] * s : (float)qp[e] * s + (float)qa[e] * c;
-        const float kv = d < DH / 2 ? (float)ka[e] * c - (float)kp[e] * s : (float)kp[e] * s + (float)ka[e] * c;
+        const float qv = d < DH / 2 ? (float)qa[u][e] * c - (float)qp[u][e] * sn
+                                    : (float)qp[u][e] * sn + (float)qa[u][e] * c;
+        const float kv = d < DH / 2 ? (float)ka[u][e] * c - (float)kp[u][e] * sn
+                                    : (float)kp[u][e] * sn + (float)ka[u][e] * c;
         qo[e] = static_cast<bf16>(qv * p.scale);
         ko[e] = static_cast<bf16>(kv);
       }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qo[e] = ko[e] = static_cast<bf16>(0.f);
+      const int64_t orow = (((int64_t)b * p.n_pad + i) * H + h) * DH;
+      *reinterpret_cast<bf16x8*>(qr + orow + d0) = qo;
+      *reinterpret_cast<bf16x8*>(kr + orow + d0) = ko;
     }
-    const int64_t orow = (((int64_t)b * p.n_pad + i) * H + h) * DH;
-    *reinterpret_cast<bf16x8*>(qr + orow + d0) = qo;
-    *reinterpret_cast<bf16x8*>(kr + orow + d0) = ko;
   }
-  // v^T, one head at a time through LDS
-  for (int h = 0; h < H; ++h) {
-    for (int x = tid; x < T * (DH / 8); x += kThreads) {
-      const int t = x / (DH / 8), c8 = x % (DH / 8), i = i0 + t;
-      bf16x8 val;
-      if (i < n) {
-        val = *reinterpret_cast<const bf16x8*>(v + (((int64_t)b * p.n_max + i) * H + h) * DH + 8 * c8);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) val[e] = static_cast<bf16>(0.f);
-      }
+  // v^T, one head at a time through LDS (T * C8 chunks: DH = 128 -> 4 per thread)
+  for (int hh = 0; hh < hpw; ++hh) {
+    const int h = h0 + hh;
+    for (int x = tid; x < T * C8; x += kThreads) {
+      const int t = x / C8, c8 = x % C8, i = i0 + t;
+      const bf16x8 val =
+          i < n ? *reinterpret_cast<const bf16x8*>(v + (((int64_t)b * p.n_max + i) * H + h) * DH + 8 * c8) : z;
       *reinterpret_cast<bf16x8*>(&vtile[t][8 * c8]) = val;
     }
     __syncthreads();
@@ -280,9 +306,9 @@ hipError_t launch_gemm(const GemmParams& g, int batches, hipStream_t s) {
 
 // ------------------------------------------------------------------ attention
 template <int DH>
-__global__ __launch_bounds__(kThreads, 1) void k_par_attn(ParParams p) {
+__global__ __launch_bounds__(kThreads, 2) void k_par_attn(ParParams p) {
   constexpr int KT = 64;            // keys per tile
-  constexpr int QB = 4;             // query blocks of 16 per wave
+  constexpr int QB = kAttnQB;       // query blocks of 16 per wave
   constexpr int KS = DH / 32;       // K steps of the score MFMA
   constexpr int DB = DH / 16;       // 16-dim blocks of the output
   constexpr int LDK = DH + 8;       // LDS row of a key tile (bf16)
@@ -296,16 +322,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_par_attn(ParParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
   const int H = p.H, W = p.W;
-  const int nqt = p.n_pad / kParQueryTile, BH = p.B * H;
+  const int nqt = p.n_pad / kAttnQT, BH = p.B * H;
   const int L = blockIdx.x;
   const int qt = nqt - 1 - L / BH, bh = L % BH, b = bh / H, h = bh % H;
   const int n = p.n_tok[b];
-  const int q0 = qt * kParQueryTile;
+  const int q0 = qt * kAttnQT;
   if (q0 >= n) return;                                // whole workgroup
-  const int qe = min(q0 + kParQueryTile, n) - 1;      // last position of the workgroup
-  const int qw0 = q0 + 64 * wave;                     // this wave's first position
+  const int qe = min(q0 + kAttnQT, n) - 1;            // last position of the workgroup
+  const int qw0 = q0 + 16 * QB * wave;                // this wave's first position
   const bool wave_on = qw0 <= qe;
-  const int qw1 = min(qw0 + 63, qe);                  // its last valid position
+  const int qw1 = min(qw0 + 16 * QB - 1, qe);         // its last valid position
 
   const int64_t trow = (int64_t)H * DH;               // token row stride of [tokens][H][d_h]
   const bf16* qr = static_cast<const bf16*>(p.qr) + (int64_t)b * p.n_pad * trow + h * DH;
@@ -396,7 +422,25 @@ __global__ __launch_bounds__(kThreads, 1) void k_par_attn(ParParams p) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       f32x4 sc[2][QB];
-      bool lat_u = false, ex_u = false;
+      // every key of the half is a latent token for every position of the
+      // wave (the common case, away from the window edge): no masks
+      const bool pure = j0 + 32 * u + 31 < qw0 - W;
+      bool lat_u = pure, ex_u = false;
+      if (pure) {
+#pragma unroll
+        for (int hs = 0; hs < 2; ++hs) {
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) sc[hs][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 kf =
+                *reinterpret_cast<const bf16x8*>(&kl_s[(16 * (2 * u + hs) + col) * LDK + 32 * ks + 8 * grp]);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+              sc[hs][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qb][ks], sc[hs][qb], 0, 0, 0);
+          }
+        }
+      } else {
 #pragma unroll
       for (int hs = 0; hs < 2; ++hs) {
         const int ts = 2 * u + hs;
@@ -447,6 +491,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_par_attn(ParParams p) {
             }
         }
       }
+      }
       if (!lat_u && !ex_u) continue;   // every key of the half follows every position
       // online softmax per position (column) over the 32 keys; sc becomes P
 #pragma unroll
@@ -455,7 +500,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_par_attn(ParParams p) {
                          fmaxf(fmaxf(sc[1][qb][0], sc[1][qb][1]), fmaxf(sc[1][qb][2], sc[1][qb][3])));
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mn = fmaxf(m[qb], mx);
+        // The running max moves only when the new one exceeds it by more than
+        // kLazy (exp2 units): weights relative to a slightly stale max stay
+        // below 2^kLazy, exact in fp32 and bf16, and the output divides by a
+        // sum taken relative to the same max.  The accumulators (in AGPRs)
+        // are then rescaled rarely instead of every few tiles.
+        const float mn = mx > m[qb] + kLazy ? mx : m[qb];
         const float alpha = exp2_diff(m[qb], mn);
         m[qb] = mn;
         float sum = 0.f;
@@ -482,7 +532,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_par_attn(ParParams p) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int j = j0 + 16 * (2 * u + e / 4) + 4 * grp + e % 4;
-          pp[e] = static_cast<bf16>(((j < i - W) == latent) ? sc[e / 4][qb][e % 4] : 0.f);
+          pp[e] = static_cast<bf16>((pure || (j < i - W) == latent) ? sc[e / 4][qb][e % 4] : 0.f);
         }
         return pp;
       };
@@ -554,8 +604,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_par_attn(ParParams p) {
 }
 
 template <int DH>
-hipError_t launch_dh(const ParParams& p, hipStream_t s) {
-  hipLaunchKernelGGL((k_par_prep<DH>), dim3(p.n_pad / 64, p.B), dim3(kThreads), 0, s, p);
+hipError_t launch_dh(const ParParams& p, hipStream_t s, hipEvent_t* ev) {
+  const int hpw = p.H % 4 == 0 ? 4 : (p.H % 2 == 0 ? 2 : 1);   // heads per prep workgroup
+  hipLaunchKernelGGL((k_par_prep<DH>), dim3(p.n_pad / kPrepTokens, p.B, p.H / hpw), dim3(kThreads), 0, s, p, hpw);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_par_gather, dim3(p.n_pad / kTile, p.B, p.G), dim3(kThreads), 0, s, p);
@@ -583,16 +634,18 @@ hipError_t launch_dh(const ParParams& p, hipStream_t s) {
   gv.syb = (int64_t)p.n_pad * p.G * p.rv; gv.syg = p.rv;
   gv.scb = (int64_t)p.H * DH * p.n_pad; gv.scg = (int64_t)hd * p.n_pad;
   if ((e = launch_gemm(gv, p.B, s)) != hipSuccess) return e;
-  const int wgs = (p.n_pad / kParQueryTile) * p.B * p.H;
+  const int wgs = (p.n_pad / kAttnQT) * p.B * p.H;
+  if (ev && (e = hipEventRecord(ev[0], s)) != hipSuccess) return e;
   hipLaunchKernelGGL((k_par_attn<DH>), dim3(wgs), dim3(kThreads), 0, s, p);
-  return hipGetLastError();
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return ev ? hipEventRecord(ev[1], s) : hipSuccess;
 }
 
 }  // namespace
 
-hipError_t launch_parallel(const ParParams& p, hipStream_t s) {
-  if (p.dh == 128) return launch_dh<128>(p, s);
-  if (p.dh == 64) return launch_dh<64>(p, s);
+hipError_t launch_parallel(const ParParams& p, hipStream_t s, hipEvent_t* events) {
+  if (p.dh == 128) return launch_dh<128>(p, s, events);
+  if (p.dh == 64) return launch_dh<64>(p, s, events);
   return hipErrorNotSupported;
 }
 

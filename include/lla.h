@@ -364,6 +364,9 @@ int32_t lla_full_decode_plan_splits(const lla_kv_desc* desc, int32_t batch, int3
  *   out            [batch][n_max][H][d_h]; rows at or past n_tok[b] are left
  *                  untouched
  *   workspace      lla_parallel_workspace_bytes() bytes, contents irrelevant
+ *   attn_events    optional (host) array of two hipEvent_t, recorded on the
+ *                  stream right before and after the attention kernel (for
+ *                  timing); NULL for none
  * Supported: bf16 sets with latent_fp8 = 0, d_h in {64, 128}, r_k and r_v
  * multiples of 32, rope_base = 0 or rope_baked = 1; other valid sets return
  * LLA_ERR_UNSUPPORTED.  The block table must cover max(0, n_max - 1 - W)
@@ -384,6 +387,7 @@ typedef struct {
   void* out;
   void* workspace;
   size_t workspace_bytes;
+  void* attn_events;
 } lla_parallel_args;
 
 lla_status hla_attention_parallel(const lla_set_desc* desc, const lla_store* store, int32_t batch,

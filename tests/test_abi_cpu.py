@@ -285,7 +285,7 @@ def _par_call(desc="ok", store="ok", batch=2, **kw):
     d = hla_main() if isinstance(desc, str) else desc
     st = B.LlaStore(FAKE, FAKE, 64) if store == "ok" else store
     a = dict(loop=3, window=128, n_max=4096, flags=0, n_tok=FAKE, q=FAKE, k=FAKE, v=FAKE, A=FAKE, B=FAKE,
-             out=FAKE, workspace=FAKE, workspace_bytes=1 << 40)
+             out=FAKE, workspace=FAKE, workspace_bytes=1 << 40, attn_events=None)
     a.update(kw)
     args = B.LlaParallelArgs(*[a[f] for f, _ in B.LlaParallelArgs._fields_])
     return B.lib.hla_attention_parallel(ctypes.byref(d) if d is not None else None,
