@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--context", type=int, default=0, help="override the context / sequence length (0 = default)")
     ap.add_argument("--batch", type=int, default=0, help="override the workload's batch (0 = workload's)")
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = workload's)")
+    ap.add_argument("--fused", action="store_true",
+                    help="absorbed / HLA reads as one fused launch per call (LLA_FLAG_FUSED)")
     ap.add_argument("--latent-fp8", action="store_true",
                     help="store latents as OCP e4m3 codes with per-token scales (absorbed / HLA entries)")
     ap.add_argument("--no-graph", action="store_true",
@@ -106,7 +108,7 @@ def fp8_store_fill(desc, n_pages, seed, std):
 class DecodeStep:
     """Every buffer of one decode step (all layers, all loops), on the GPU."""
 
-    def __init__(self, w, splits=0, seed=0, entry="auto", fp8=False):
+    def __init__(self, w, splits=0, seed=0, entry="auto", fp8=False, flags=0):
         import torch
         from compressed_cross_loop_amd import binding as B
         from synth import gen
@@ -145,6 +147,7 @@ class DecodeStep:
         wws = max(B.lla_write_workspace_bytes(st["desc"], Bt, 1, st["spec"].d_in) for st in self.sets)
         self.wws = torch.empty(max(wws, 256), dtype=torch.uint8, device=dev)
         self.fp8 = fp8
+        self.flags = flags
         self.calls = []   # (loop, set index, desc, store, args)
         self.outs = []
         for t in range(1, T + 1):
@@ -163,7 +166,7 @@ class DecodeStep:
                 bufs = (q, kc, vc, rk, rv, A, Bm, out)
                 args = B.decode_args(loop=t, window=W, pos=self.pos, q=q, k_cur=kc, v_cur=vc, ring_k=rk,
                                      ring_v=rv, A=A, B=Bm, out=out, workspace=self.ws,
-                                     max_pos_hint=self.i, splits=splits)
+                                     max_pos_hint=self.i, splits=splits, flags=flags)
                 self.calls.append((t, k, l, self.sets[k]["desc"], self.sets[k]["stores"][l], args, bufs))
         if entry == "auto":
             entry = "hla" if w.family == "hla" else "reconstruct"
@@ -588,7 +591,10 @@ def main():
                     print(json.dumps({"error": "fp8 latents serve the absorbed / HLA reads of bf16 workloads"}))
                     sys.exit(2)
                 w = w.with_(name=f"{w.name}-fp8")
-            st = DecodeStep(w, splits=a.splits, entry=a.entry, fp8=a.latent_fp8)
+            if a.fused:
+                w = w.with_(name=f"{w.name}-fused")
+            st = DecodeStep(w, splits=a.splits, entry=a.entry, fp8=a.latent_fp8,
+                            flags=2 if a.fused else 0)
     stream = torch.cuda.current_stream().cuda_stream
     for _ in range(max(1, a.warmup)):
         st.step()
@@ -643,7 +649,7 @@ def main():
         scan_bytes += w.batch * w.heads * s_main.r_k * (2 if w.dtype == "bf16" else 4) \
             if st.entry_name != "reconstruct" else 0
         main_desc = next(c[3] for c in st.calls if c[1] == main_k)
-        kname = st.B.lla_decode_scan_kernel(main_desc, ENTRY_CODE[st.entry_name])
+        kname = st.B.lla_decode_scan_kernel(main_desc, ENTRY_CODE[st.entry_name], getattr(st, "flags", 0))
     reconstruct_mfma_bound = st.entry_name == "reconstruct" and scan_flop / scan_bytes > 312
     if reconstruct_mfma_bound or st.entry_name == "parallel":
         roof = {"bound": "mfma", "achieved": scan_flop / (scan_ms * 1e-3) / 1e12, "peak": 2500.0,

@@ -21,6 +21,7 @@ LLA_ERR_HIP = 4
 LLA_F32 = 0
 LLA_BF16 = 1
 LLA_FLAG_GENERIC = 1
+LLA_FLAG_FUSED = 2     # absorbed / HLA reads: one fused launch per call (small batch x context)
 
 _DTYPES = {torch.float32: LLA_F32, torch.bfloat16: LLA_BF16}
 _TORCH = {LLA_F32: torch.float32, LLA_BF16: torch.bfloat16}

@@ -314,7 +314,7 @@ __global__ __launch_bounds__(kThreads) void k_combine_mfma(DecodeParams p) {
 
   // (m, l) of every split and window slice of the 16 sequences: one load per
   // thread, all in flight together, then the per-sequence softmax merge
-  __shared__ float pm[16][40], pl[16][40];   // S + WS <= 40
+  __shared__ float pm[16][kCombineMaxParts], pl[16][kCombineMaxParts];
   {
     const int NP = S + WS;
     for (int x = tid; x < 16 * NP; x += kThreads) {
@@ -507,7 +507,7 @@ hipError_t launch_window_fast(const DecodeParams& p, hipStream_t s) {
 }
 
 bool combine_mfma_supports(const DecodeParams& p) {
-  if (!p.bf16 || p.mode != kAbsorbed || p.dh != 128 || p.S + p.WS > 40) return false;
+  if (!p.bf16 || p.mode != kAbsorbed || p.dh != 128 || p.S + p.WS > kCombineMaxParts) return false;
   return p.rv == 32 || p.rv == 64 || p.rv == 128 || p.rv == 256 || p.rv == 512;
 }
 

@@ -60,11 +60,11 @@ struct Plan {
 // `chunk` tokens (a multiple of 64); `wgs` workgroups work on each
 // (sequence, range).  S aims at kTargetWorkgroups in flight.
 Plan make_plan(int batch, int max_pos, int window, int splits, int wgs, int target = kTargetWorkgroups,
-               int gran = kChunk) {
+               int gran = kChunk, int cap = 1 << 30) {
   const int64_t n_lat = std::max<int64_t>(0, (int64_t)max_pos - window);
   const int64_t tiles = std::max<int64_t>(1, (n_lat + gran - 1) / gran);
   int64_t S = splits > 0 ? splits
-                         : (target + (int64_t)batch * wgs - 1) / ((int64_t)batch * wgs);
+                         : std::min<int64_t>(cap, (target + (int64_t)batch * wgs - 1) / ((int64_t)batch * wgs));
   S = std::min<int64_t>(std::max<int64_t>(S, 1), tiles);
   const int64_t per = (tiles + S - 1) / S;
   S = (tiles + per - 1) / per;
@@ -106,8 +106,25 @@ bool use_gemm_reconstruct(const lla_set_desc& d, int flags) {
   return scan_reconstruct_gemm_supports(p);
 }
 
+bool fused_shape(const lla_set_desc& d) {
+  DecodeParams p{};
+  p.bf16 = d.dtype == LLA_BF16;
+  p.fp8 = d.latent_fp8;
+  p.rk = d.r_k;
+  p.rv = d.r_v;
+  p.dh = d.head_dim;
+  return fused_decode_supports(p);
+}
+
+constexpr int kValidFlags = LLA_FLAG_GENERIC | LLA_FLAG_FUSED;
+
+bool flags_ok(int flags) {
+  return !(flags & ~kValidFlags) && (flags & kValidFlags) != kValidFlags;
+}
+
 // the latent-scan kernel family a decode call launches for this set
 const char* scan_kernel_name(const lla_set_desc& d, int absorbed, int flags) {
+  if (absorbed && (flags & LLA_FLAG_FUSED)) return "k_fused_decode";
   if (absorbed) return use_mfma_scan(d, flags) ? "k_scan_absorbed_mfma" : "k_scan_absorbed_generic";
   if (use_mfma_reconstruct(d, flags)) return "k_scan_reconstruct_mfma";
   if (use_gemm_reconstruct(d, flags)) return "k_scan_reconstruct_gemm";
@@ -119,7 +136,17 @@ Plan plan_for(const lla_set_desc& d, int batch, int max_pos, int window, int spl
   const bool absorbed = entry != 0;
   int wgs = d.n_heads;                                  // general kernels: one per head
   int target = kTargetWorkgroups;
-  if (absorbed && use_mfma_scan(d, flags)) wgs = d.groups;
+  if (absorbed && (flags & LLA_FLAG_FUSED)) {
+    target = 2 * kTargetWorkgroups;   // small workgroups: a few resident per CU
+    const Plan pl = make_plan(batch, max_pos, window, splits, wgs, target, kChunk);
+    if (pl.S <= kMaxFusedSplits) return pl;
+    return make_plan(batch, max_pos, window, kMaxFusedSplits, wgs, target, kChunk);
+  } else if (absorbed && use_mfma_scan(d, flags)) {
+    wgs = d.groups;
+    // the matrix-core combine merges at most kCombineMaxParts splits + window
+    // slices (one window slice per split when the scan takes the window along)
+    return make_plan(batch, max_pos, window, splits, wgs, target, kChunk, kCombineMaxParts / 2);
+  }
   int gran = kChunk;
   if (!absorbed && use_mfma_reconstruct(d, flags)) {
     wgs = (d.n_heads + 3) / 4;
@@ -132,7 +159,7 @@ Plan plan_for(const lla_set_desc& d, int batch, int max_pos, int window, int spl
 }
 
 struct WsLayout {
-  size_t qlat, qhead, part_ml, part_o, win_ml, win_o, total;
+  size_t qlat, qhead, part_ml, part_o, win_ml, win_o, tickets, fpart, total;
 };
 
 size_t up256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -141,10 +168,16 @@ constexpr int kWindowSlice = 32;   // exact tokens per window slice (fast window
 
 int window_slices(int window) { return (window + 1 + kWindowSlice - 1) / kWindowSlice; }
 
-WsLayout ws_layout(const lla_set_desc& d, int B, int S, int WS, int Dp) {
+WsLayout ws_layout(const lla_set_desc& d, int B, int S, int WS, int Dp, bool fused = false) {
   WsLayout w{};
   const size_t H = d.n_heads, dh = d.head_dim;
   size_t off = 0;
+  if (fused) {   // tickets and the splits' partials only
+    w.tickets = off; off = up256(off + (size_t)B * H * 4);
+    w.fpart = off;   off = up256(off + (size_t)B * H * S * fused_partial_floats(d.r_k, d.head_dim) * 4);
+    w.total = off;
+    return w;
+  }
   w.qlat = off;    off = up256(off + (size_t)B * H * d.r_k * elem_bytes(d));
   w.qhead = off;   off = up256(off + (size_t)B * H * dh * 4);
   w.part_ml = off; off = up256(off + (size_t)B * S * H * 2 * 4);
@@ -168,6 +201,10 @@ size_t decode_ws_bytes(const lla_set_desc& d, int batch, int max_pos, int window
       best = std::max(best, ws_layout(d, batch, S, std::max(S, window_slices(window)),
                                       partial_width(d, entry)).total);
     }
+  if (fused_shape(d)) {
+    const int S = plan_for(d, batch, max_pos, window, splits, 1, LLA_FLAG_FUSED).S;
+    best = std::max(best, ws_layout(d, batch, S, S, d.r_v, true).total);
+  }
   return best;
 }
 
@@ -245,12 +282,14 @@ lla_status decode(const lla_set_desc* d, const lla_store* st, int32_t batch,
   if (batch <= 0 || !a) return LLA_ERR_INVALID_ARGUMENT;
   if (a->loop < d->loop_first || a->loop > d->loop_last) return LLA_ERR_INVALID_ARGUMENT;
   if (a->window < 0 || a->max_pos_hint < 0 || a->splits < 0) return LLA_ERR_INVALID_ARGUMENT;
-  if (a->flags & ~LLA_FLAG_GENERIC) return LLA_ERR_INVALID_ARGUMENT;
+  if (!flags_ok(a->flags)) return LLA_ERR_INVALID_ARGUMENT;
   const void* ptrs[] = {a->pos, a->q, a->k_cur, a->v_cur, a->ring_k, a->ring_v, a->A, a->B, a->out};
   for (const void* p : ptrs)
     if (!p || !aligned16(p)) return LLA_ERR_INVALID_ARGUMENT;
   if (entry == 2 && d->groups != 1) return LLA_ERR_INVALID_ARGUMENT;
   if (entry == 0 && d->latent_fp8) return LLA_ERR_UNSUPPORTED;   // fp8 latents: absorbed read only
+  const bool fused = (a->flags & LLA_FLAG_FUSED) != 0;
+  if (fused && (entry == 0 || !fused_shape(*d))) return LLA_ERR_UNSUPPORTED;
   if (a->window > kMaxWindow) return LLA_ERR_UNSUPPORTED;
   if (d->rope_base > 0.f && !d->rope_baked) return LLA_ERR_UNSUPPORTED;
   const size_t need = decode_ws_bytes(*d, batch, a->max_pos_hint, a->window, a->splits);
@@ -262,7 +301,7 @@ lla_status decode(const lla_set_desc* d, const lla_store* st, int32_t batch,
   const Plan plan = plan_for(*d, batch, a->max_pos_hint, a->window, a->splits, absorbed ? 1 : 0, a->flags);
   const int Dp = partial_width(*d, absorbed ? 1 : 0);
   const int WSmax = window_slices(a->window);
-  const WsLayout w = ws_layout(*d, batch, plan.S, std::max(plan.S, WSmax), Dp);
+  const WsLayout w = ws_layout(*d, batch, plan.S, std::max(plan.S, WSmax), Dp, fused);
   char* ws = static_cast<char*>(a->workspace);
 
   DecodeParams p{};
@@ -283,6 +322,17 @@ lla_status decode(const lla_set_desc* d, const lla_store* st, int32_t batch,
   p.part_o = reinterpret_cast<float*>(ws + w.part_o);
   p.win_ml = reinterpret_cast<float*>(ws + w.win_ml);
   p.win_o = reinterpret_cast<float*>(ws + w.win_o);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipEvent_t* ev = static_cast<hipEvent_t*>(a->scan_events);
+  if (fused) {
+    p.tickets = reinterpret_cast<int32_t*>(ws + w.tickets);
+    p.fpart = reinterpret_cast<float*>(ws + w.fpart);
+    p.tw = (a->window + 1 + plan.S - 1) / plan.S;
+    hipError_t e = ev ? hipEventRecord(ev[0], s) : hipSuccess;
+    if (e == hipSuccess) e = launch_fused_decode(p, s);
+    if (e == hipSuccess && ev) e = hipEventRecord(ev[1], s);
+    return hip_status(e);
+  }
   const bool mfma_scan = absorbed && use_mfma_scan(*d, a->flags);
   const bool fast_window = !generic && window_fast_supports(p);
   // the matrix-core scan takes the window along when its group's heads fit
@@ -296,11 +346,9 @@ lla_status decode(const lla_set_desc* d, const lla_store* st, int32_t batch,
     p.WS = fast_window ? WSmax : 1;
   }
   p.need_qhead = (!fast_window || !absorbed) ? 1 : 0;
-  hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = (!generic && qmap_mfma_supports(p)) ? launch_qmap_mfma(p, absorbed, s)
                                                      : launch_qmap(p, absorbed, s);
   if (e == hipSuccess && !p.fuse_window) e = fast_window ? launch_window_fast(p, s) : launch_window(p, s);
-  hipEvent_t* ev = static_cast<hipEvent_t*>(a->scan_events);
   if (e == hipSuccess && ev) e = hipEventRecord(ev[0], s);
   if (e == hipSuccess) {
     if (!absorbed) {
@@ -398,7 +446,8 @@ int32_t lla_decode_plan_splits(const lla_set_desc* desc, int32_t batch, int32_t 
 }
 
 const char* lla_decode_scan_kernel(const lla_set_desc* desc, int32_t entry, int32_t flags) {
-  if (check_desc(desc) != LLA_OK || entry < 0 || entry > 2 || (flags & ~LLA_FLAG_GENERIC)) return nullptr;
+  if (check_desc(desc) != LLA_OK || entry < 0 || entry > 2 || !flags_ok(flags)) return nullptr;
+  if ((flags & LLA_FLAG_FUSED) && (entry == 0 || !fused_shape(*desc))) return nullptr;
   return scan_kernel_name(*desc, entry != 0, flags);
 }
 

@@ -46,6 +46,9 @@ struct DecodeParams {
   float* part_o;                  // [B][S][H][Dp]
   float* win_ml;                  // [B][WS][H][2]
   float* win_o;                   // [B][WS][H][dh]
+  // fused single-launch path
+  int32_t* tickets;               // [B][H] arrival counters
+  float* fpart;                   // [B][H][S][2 + rv + dh]
 };
 
 struct WriterParams {
@@ -125,10 +128,16 @@ bool scan_reconstruct_gemm_supports(const DecodeParams& p);
 int scan_reconstruct_gemm_tile();
 hipError_t launch_scan_reconstruct_gemm(const DecodeParams& p, hipStream_t s);
 
+constexpr int kMaxFusedSplits = 1024;   // context splits per (sequence, head) of the fused path
+bool fused_decode_supports(const DecodeParams& p);
+int fused_partial_floats(int rk, int dh);
+hipError_t launch_fused_decode(const DecodeParams& p, hipStream_t s);
+
 bool qmap_mfma_supports(const DecodeParams& p);
 hipError_t launch_qmap_mfma(const DecodeParams& p, bool want_qlat, hipStream_t s);
 bool window_fast_supports(const DecodeParams& p);
 hipError_t launch_window_fast(const DecodeParams& p, hipStream_t s);
+constexpr int kCombineMaxParts = 160;   // splits + window slices the matrix-core combine merges
 bool combine_mfma_supports(const DecodeParams& p);
 hipError_t launch_combine_mfma(const DecodeParams& p, hipStream_t s);
 

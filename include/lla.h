@@ -66,6 +66,16 @@ typedef enum { LLA_F32 = 0, LLA_BF16 = 1 } lla_dtype;
 /* Decode flags (lla_decode_args.flags). */
 #define LLA_FLAG_GENERIC 1 /* use the general VALU kernels even where a
                               matrix-core kernel exists (testing, tuning) */
+#define LLA_FLAG_FUSED 2   /* absorbed / HLA reads: the query map, latent
+                              scan, exact window and value map in one kernel
+                              (workgroup per (split, head, sequence)) behind a
+                              one-line ticket reset, instead of three kernels;
+                              for small batch x context, where a call is bound
+                              by fixed latency rather than bytes.
+                              LLA_ERR_UNSUPPORTED where it does not apply
+                              (reconstruct entry, fp32 or fp8 sets, r_k != r_v,
+                              r not in {128, 256, 512, 1024}, d_h not in
+                              {64, 128}); not combinable with LLA_FLAG_GENERIC */
 
 /*
  * One latent set of one layer (host struct).  A set serves loops

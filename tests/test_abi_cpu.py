@@ -340,3 +340,26 @@ def test_parallel_null_structs_and_workspace():
     # of bf16 per padded position, and the gathered latents
     assert w(d, 1, 256) >= 256 * (5 * 16 * 128 + 1024) * 2
     assert w(d, 0, 256) == 0 and w(d, 1, 0) == 0
+
+
+def test_fused_flag_rules():
+    """LLA_FLAG_FUSED: absorbed / HLA entries on supported bf16 shapes only,
+    never together with LLA_FLAG_GENERIC (all rejected before any launch)."""
+    st = B.LlaStore(FAKE, FAKE, 4)
+    F, Gn = B.LLA_FLAG_FUSED, B.LLA_FLAG_GENERIC
+
+    def call(entry, d, flags):
+        return getattr(B.lib, entry)(ctypes.byref(d), ctypes.byref(st), 4,
+                                     ctypes.byref(_args(flags=flags, workspace_bytes=16)), None)
+    d = hla_main()
+    assert call("hla_decode_windowed", d, F | Gn) == B.LLA_ERR_INVALID_ARGUMENT
+    assert call("lla_decode_reconstruct", d, F) == B.LLA_ERR_UNSUPPORTED
+    for bad in (hla_main(dtype=B.LLA_F32), hla_main(latent_fp8=1), hla_main(r_k=512, r_v=256),
+                hla_main(r_k=64, r_v=64, rope_baked=0, rope_base=0.0), hla_main(head_dim=256, r_k=512, r_v=512)):
+        assert call("lla_decode_absorbed", bad, F) == B.LLA_ERR_UNSUPPORTED
+    # a supported shape gets as far as the workspace check
+    assert call("hla_decode_windowed", d, F) == B.LLA_ERR_WORKSPACE_TOO_SMALL
+    assert B.lla_decode_scan_kernel(d, 2, F) == "k_fused_decode"
+    assert B.lla_decode_scan_kernel(d, 0, F) is None
+    assert B.lla_decode_scan_kernel(d, 2, F | Gn) is None
+    assert B.lla_decode_scan_kernel(hla_main(r_k=64, r_v=64, rope_baked=0, rope_base=0.0), 1, F) is None
