@@ -40,6 +40,7 @@
 //           latent and exact parts of P against their own values
 // Workgroups are issued longest (last positions) first.
 #include "device_common.h"
+#include "gemm_nt.h"
 #include "lla_internal.h"
 
 namespace lla {
@@ -208,100 +209,6 @@ __global__ __launch_bounds__(kThreads) void k_par_gather(ParParams p) {
     }
     __syncthreads();
   }
-}
-
-// ------------------------------------------------------------------ GEMM
-// C[m][n] = sum_k X[m][k] Y[n][k] (bf16 in and out, fp32 accumulation), one
-// (batch, group) per blockIdx.z; 128 x 128 tiles, 4 waves of 64 x 64, K steps
-// of 32 staged in LDS (double-buffered, next step's loads in flight).  Rows
-// past M and N are clamped on load and skipped on store; K % 32 == 0.
-struct GemmParams {
-  const bf16* X;
-  const bf16* Y;
-  bf16* C;
-  int32_t M, N, K, ldx, ldy, ldc, G;
-  int64_t sxb, sxg, syb, syg, scb, scg;
-};
-
-__global__ __launch_bounds__(kThreads) void k_gemm_nt(GemmParams q) {
-  constexpr int BM = 128, BN = 128, BK = 32, LD = BK + 8;
-  const int z = blockIdx.z, zb = z / q.G, zg = z % q.G;
-  const bf16* X = q.X + zb * q.sxb + zg * q.sxg;
-  const bf16* Y = q.Y + zb * q.syb + zg * q.syg;
-  bf16* C = q.C + zb * q.scb + zg * q.scg;
-  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int col = lane & 15, grp = lane >> 4;
-  const int wm = wave >> 1, wn = wave & 1;
-  __shared__ __attribute__((aligned(16))) bf16 xs[2][BM][LD];
-  __shared__ __attribute__((aligned(16))) bf16 ys[2][BN][LD];
-  // loader: 2 chunks of 16 B per thread per operand and K step
-  int xr[2], yr[2], kc[2];
-#pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    const int idx = tid + kThreads * c;
-    kc[c] = 8 * (idx % 4);
-    xr[c] = min(m0 + idx / 4, q.M - 1);
-    yr[c] = min(n0 + idx / 4, q.N - 1);
-  }
-  u32x4 rx[2], ry[2];
-  auto load = [&](int k0) {
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      rx[c] = *reinterpret_cast<const u32x4*>(X + (int64_t)xr[c] * q.ldx + k0 + kc[c]);
-      ry[c] = *reinterpret_cast<const u32x4*>(Y + (int64_t)yr[c] * q.ldy + k0 + kc[c]);
-    }
-  };
-  auto store = [&](int buf) {
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int idx = tid + kThreads * c;
-      *reinterpret_cast<u32x4*>(&xs[buf][idx / 4][kc[c]]) = rx[c];
-      *reinterpret_cast<u32x4*>(&ys[buf][idx / 4][kc[c]]) = ry[c];
-    }
-  };
-  f32x4 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int nk = q.K / BK;
-  load(0);
-  store(0);
-  __syncthreads();
-  for (int kk = 0; kk < nk; ++kk) {
-    const int cur = kk & 1;
-    if (kk + 1 < nk) load((kk + 1) * BK);
-    bf16x8 a[4], bb[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const bf16x8*>(&xs[cur][64 * wm + 16 * i + col][8 * grp]);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) bb[j] = *reinterpret_cast<const bf16x8*>(&ys[cur][64 * wn + 16 * j + col][8 * grp]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bb[j], acc[i][j], 0, 0, 0);
-    if (kk + 1 < nk) store(cur ^ 1);
-    __syncthreads();
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = n0 + 64 * wn + 16 * j + col;
-      if (n >= q.N) continue;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = m0 + 64 * wm + 16 * i + 4 * grp + r;
-        if (m < q.M) C[(int64_t)m * q.ldc + n] = static_cast<bf16>(acc[i][j][r]);
-      }
-    }
-}
-
-hipError_t launch_gemm(const GemmParams& g, int batches, hipStream_t s) {
-  const dim3 grid((g.N + 127) / 128, (g.M + 127) / 128, batches * g.G);
-  hipLaunchKernelGGL(k_gemm_nt, grid, dim3(kThreads), 0, s, g);
-  return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ attention
@@ -613,22 +520,22 @@ hipError_t launch_dh(const ParParams& p, hipStream_t s, hipEvent_t* ev) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int hd = p.hpg * DH;   // output columns (rows) of one latent group
   // K^[b][t][g hd + c] = sum_d S^K[b][t][g][d] A[g hd + c][d]
-  GemmParams gk{};
+  GemmParams<bf16> gk{};
   gk.X = static_cast<const bf16*>(p.sk);
   gk.Y = static_cast<const bf16*>(p.A);
   gk.C = static_cast<bf16*>(p.kh);
-  gk.M = p.n_pad; gk.N = hd; gk.K = p.rk;
+  gk.M = p.n_pad; gk.N = hd; gk.K = p.rk; gk.kseg = p.rk;
   gk.ldx = p.G * p.rk; gk.ldy = p.rk; gk.ldc = p.H * DH; gk.G = p.G;
   gk.sxb = (int64_t)p.n_pad * p.G * p.rk; gk.sxg = p.rk;
   gk.syb = 0; gk.syg = (int64_t)hd * p.rk;
   gk.scb = (int64_t)p.n_pad * p.H * DH; gk.scg = hd;
   if ((e = launch_gemm(gk, p.B, s)) != hipSuccess) return e;
   // V^^T[b][g hd + c][t] = sum_d B^T[g hd + c][d] S^V[b][t][g][d]
-  GemmParams gv{};
+  GemmParams<bf16> gv{};
   gv.X = static_cast<const bf16*>(p.Bm);
   gv.Y = static_cast<const bf16*>(p.sv);
   gv.C = static_cast<bf16*>(p.vht);
-  gv.M = hd; gv.N = p.n_pad; gv.K = p.rv;
+  gv.M = hd; gv.N = p.n_pad; gv.K = p.rv; gv.kseg = p.rv;
   gv.ldx = p.rv; gv.ldy = p.G * p.rv; gv.ldc = p.n_pad; gv.G = p.G;
   gv.sxb = 0; gv.sxg = (int64_t)hd * p.rv;
   gv.syb = (int64_t)p.n_pad * p.G * p.rv; gv.syg = p.rv;

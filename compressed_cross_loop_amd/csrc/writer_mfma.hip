@@ -1,18 +1,21 @@
 // Latent writer on the gfx950 matrix cores ("Hybrid Latent Attention"
 // summary, "Latent Writer", Eq. 2).  Per group, the writer is one GEMM
 //     c[tokens x (r_k+r_v)] = sum_t X_t[tokens x d_in] . E_t^T[d_in x (r_k+r_v)]
-// with the loops concatenated along K.  The matrices are short and wide
-// (a decode step writes one token per sequence), so the GEMM is split along
-// K across workgroups: each writes an fp32 partial tile to the workspace, and
+// with the loops concatenated along K.  For a decode step the matrices are
+// short and wide (one token per sequence), so the GEMM is split along K
+// across workgroups: each writes an fp32 partial tile to the workspace, and
 // a second kernel sums the partials in a fixed order, rotates the key part
 // by R~_p when the set bakes rotary embedding, rounds to bf16 and scatters
-// into the paged store.
+// into the paged store.  A bulk write (a whole prompt or training sequence:
+// kBulkTokens tokens or more) runs the tiled GEMM of gemm_nt.h instead, one
+// K segment per loop, into a single fp32 partial for the same second kernel.
 //   v_mfma_f32_16x16x32_bf16: A = 8 consecutive inputs of one token (16-B
 //   load from x), B = 8 consecutive inputs of one encoder row (16-B load
 //   from E_t), both in their natural row-major layouts.
 #include <algorithm>
 
 #include "device_common.h"
+#include "gemm_nt.h"
 #include "lla_internal.h"
 #include "writer_common.h"
 
@@ -31,6 +34,7 @@ constexpr int kRound = 12;            // 32-wide K steps staged per round
 constexpr int kPieces = kTileN * kRound * 4;            // 16-byte pieces of an E round
 constexpr int kPiecesPerThread = kPieces / kThreads;    // 6
 constexpr int kReduceThreads = 256;
+constexpr int kBulkTokens = 1024;   // tokens per call from which the tiled GEMM writes
 
 __device__ __forceinline__ bf16x8 zero8() {
   bf16x8 z;
@@ -163,6 +167,7 @@ __global__ __launch_bounds__(kReduceThreads) void k_writer_reduce(WriterParams p
 bool writer_mfma_supports(const WriterParams& p) { return p.bf16 && p.d_in % 32 == 0; }
 
 int writer_mfma_ksplit(int M, int G, int R, int n_loops, int d_in) {
+  if (M >= kBulkTokens) return 1;   // tiled GEMM, no K split
   const int64_t tiles = (int64_t)((R + kTileN - 1) / kTileN) * ((M + kTileM - 1) / kTileM) * G;
   const int ksteps = n_loops * d_in / 32;
   int64_t ks = (256 + tiles - 1) / tiles;                       // about one workgroup per CU
@@ -174,9 +179,23 @@ int writer_mfma_ksplit(int M, int G, int R, int n_loops, int d_in) {
 hipError_t launch_writer_mfma(const WriterParams& p, hipStream_t s) {
   if (!writer_mfma_supports(p)) return hipErrorNotSupported;
   const int M = p.B * p.n_tok;
-  const dim3 grid((p.R + kTileN - 1) / kTileN, (M + kTileM - 1) / kTileM, p.G * p.ksplit);
-  hipLaunchKernelGGL(k_writer_mfma, grid, dim3(kThreads), 0, s, p);
-  hipError_t e = hipGetLastError();
+  hipError_t e;
+  if (M >= kBulkTokens) {
+    // c[m][g][r] = sum_t sum_d x[m][t][g][d] E[t][g][r][d]: K segment t per loop
+    GemmParams<float> q{};
+    q.X = static_cast<const bf16*>(p.x);
+    q.Y = static_cast<const bf16*>(p.enc);
+    q.C = p.acc;
+    q.M = M; q.N = p.R; q.K = p.n_loops * p.d_in; q.kseg = p.d_in; q.G = p.G;
+    q.ldx = p.n_loops * p.G * p.d_in; q.sxg = p.d_in; q.sxk = (int64_t)p.G * p.d_in;
+    q.ldy = p.d_in; q.syg = (int64_t)p.R * p.d_in; q.syk = (int64_t)p.G * p.R * p.d_in;
+    q.ldc = p.G * p.R; q.scg = p.R;
+    e = launch_gemm(q, 1, s);
+  } else {
+    const dim3 grid((p.R + kTileN - 1) / kTileN, (M + kTileM - 1) / kTileM, p.G * p.ksplit);
+    hipLaunchKernelGGL(k_writer_mfma, grid, dim3(kThreads), 0, s, p);
+    e = hipGetLastError();
+  }
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_writer_reduce, dim3(M, p.G), dim3(kReduceThreads), (size_t)p.R * sizeof(float), s, p);
   return hipGetLastError();

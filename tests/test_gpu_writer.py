@@ -140,7 +140,15 @@ def test_writer_then_decode_end_to_end():
     # tiny output, long K: 64 K splits, summed in eight batches of eight
     dict(batch=2, n_tok=1, n_loops=4, groups=1, r_k=32, r_v=32, d_in=4096, head_dim=64,
          positions="decode"),
-], ids=["hla-decode-b128", "ragged-m-and-n", "two-rounds", "many-splits"])
+    # bulk writes (1024 tokens or more) take the tiled GEMM: 1200 tokens (last
+    # 128-token tile ragged), R = 80 (one ragged 128-wide tile), 2 groups, 2 loops
+    dict(batch=3, n_tok=400, n_loops=2, groups=2, r_k=48, r_v=32, d_in=64, head_dim=64,
+         positions="prefix"),
+    # bulk write of the main HLA set with baked rotary embedding, 3 K segments
+    dict(batch=2, n_tok=600, n_loops=3, groups=1, r_k=512, r_v=512, d_in=2048, rope_base=10000.0,
+         rope_baked=1, head_dim=128, positions="prefix"),
+], ids=["hla-decode-b128", "ragged-m-and-n", "two-rounds", "many-splits", "bulk-ragged",
+        "bulk-hla"])
 def test_writer_bf16_shapes(case):
     case = dict(case)
     kind = case.pop("positions")
