@@ -153,7 +153,7 @@ Plan plan_for(const lla_set_desc& d, int batch, int max_pos, int window, int spl
     target = 2 * kTargetWorkgroups;   // small workgroups: two resident per CU
   } else if (!absorbed && use_gemm_reconstruct(d, flags)) {
     wgs = (d.n_heads + 1) / 2;          // two heads per workgroup
-    gran = scan_reconstruct_gemm_tile();
+    gran = scan_reconstruct_gemm_tile(d.head_dim);
   }
   return make_plan(batch, max_pos, window, splits, wgs, target, gran);
 }

@@ -125,7 +125,7 @@ bool scan_reconstruct_mfma_supports(const DecodeParams& p);
 hipError_t launch_scan_reconstruct_mfma(const DecodeParams& p, hipStream_t s);
 
 bool scan_reconstruct_gemm_supports(const DecodeParams& p);
-int scan_reconstruct_gemm_tile();
+int scan_reconstruct_gemm_tile(int dh);   // tokens per workgroup tile (split granularity)
 hipError_t launch_scan_reconstruct_gemm(const DecodeParams& p, hipStream_t s);
 
 constexpr int kMaxFusedSplits = 1024;   // context splits per (sequence, head) of the fused path

@@ -271,13 +271,333 @@ __global__ __launch_bounds__(kThreads, 1) void k_scan_reconstruct_gemm(DecodePar
     wave_main<DH, 0>(p, sc, b, s, hb);
 }
 
+// ---------------------------------------------------------------------------
+// LDS-staged form (d_h = 64 or 96).  One workgroup = (context split, sequence,
+// 2 heads), eight waves = {K^, V^} x 2 heads x 2 token halves of a 256-token
+// tile; each wave rebuilds 128 tokens x d_h of its head.  Per K step of 32
+// latent dims every operand the step needs -- the key rows and value blocks
+// of the 256 tokens, both heads' A_t and B_t^T rows -- is copied into LDS with
+// direct global -> LDS loads (lane i's 16 bytes land at base + 16 i, one
+// 1 KiB copy per instruction), double buffered with one barrier per step.
+// The four K^ (V^) waves share the latent tiles and the two token halves
+// share the decoder rows, so a latent or decoder byte crosses the load path
+// once per workgroup instead of once per wave, and every load instruction
+// covers whole 64-byte row pieces or a contiguous 1 KiB.
+//   copy slots: rows x 64 B copies (keys, decoders) put chunk c of row r at
+//   slot 4 r + (c ^ (r / 4 % 4)), so the 16 lanes of a 16-byte LDS read hit
+//   16 different bank groups.  A value copy holds two 16 x 16 dimension-major
+//   sub-blocks of a 16-token store tile; the V^ waves read it with the gfx950
+//   transposing LDS read (ds_read_b64_tr_b16: inside each 16-lane group,
+//   lane i receives element i % 4 of lanes i / 4, 4 + i / 4, 8 + i / 4 and
+//   12 + i / 4), which turns four dims x 16 tokens into the token-major
+//   A-operand pieces of the MFMA; chunk slots are XOR-swizzled (bit 3 ^= bit
+//   4) so the two 16-lane groups served together read different banks.
+// The two token halves of a head see the same 256 scores, so they keep the
+// same running maximum and their (l, o) simply add at the end.
+namespace staged {
+
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kPageTab = 4096;      // page ids of the split, staged in LDS
+
+template <int DH> struct Shape {
+  static constexpr int NT = DH / 16;            // column tiles per head
+  static constexpr int MTW = DH == 96 ? 6 : 8;  // row tiles per wave (registers: MTW x NT accumulators)
+  static constexpr int TMW = 16 * MTW;          // tokens per wave
+  static constexpr int TM = 2 * TMW;            // tokens per tile (two halves)
+  static constexpr int NTT = TM / 16;           // 16-token store tiles per tile
+  // 1 KiB copies per step, in LDS order: key pieces, value pieces, A rows of
+  // both heads, B rows of both heads
+  static constexpr int QV = NTT, QA = 2 * NTT, QB = 2 * NTT + 2 * NT, NQ = 2 * NTT + 4 * NT;
+  static constexpr int PER_WAVE = NQ / kWaves;
+  static constexpr int STAGE = NQ * 1024;
+  static constexpr int MAXP = (NTT + kWaves - 1) / kWaves;   // store tiles per wave, at most
+  static_assert(NQ % kWaves == 0 && PER_WAVE >= 2 * MAXP, "copies must divide evenly over the waves");
+};
+
+__device__ __forceinline__ int row_slot(int row, int c) { return 4 * row + (c ^ ((row >> 2) & 3)); }
+__device__ __forceinline__ int val_slot(int ch) { return ch ^ (((ch >> 4) & 1) << 3); }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+constexpr unsigned kWaitVm0 = 0x0F70;   // s_waitcnt vmcnt(0), expcnt / lgkmcnt untouched
+
+// LDS regions of the staged kernel.  The two stage buffers are separate
+// LDS variables and every access names one of them statically: the compiler
+// then knows that copies into one buffer cannot alias reads of the other and
+// does not wait for the copies in flight before reading.
+template <int DH> struct Smem {
+  float sc[2][2][Shape<DH>::TM];   // scores: tile parity, head of the pair, token
+  float qh[2][DH];                 // q' of both heads
+  float mrg[2][DH + 1];            // second half's (o, l) per head
+  int32_t ptab[kPageTab];          // page ids of the split
+};
+
+// Everything one wave of role KIND (0: K^, 1: V^) does for its work item;
+// the roles are separate instantiations so that each gets its own register
+// allocation.  Both pass the same barriers: one per K step, one per tile, one
+// at the end.
+template <int DH, int KIND>
+__device__ __forceinline__ void staged_wave(const DecodeParams& p, Smem<DH>& sm, unsigned char* stage0,
+                                            unsigned char* stage1, int b, int s, int hb, int hl,
+                                            int th, int wave, int t0, int t1) {
+  using Sh = Shape<DH>;
+  constexpr int NT = Sh::NT, MTW = Sh::MTW, TMW = Sh::TMW, TM = Sh::TM;
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 15, kg = lane >> 4;
+  const int H = p.H, R = p.rk, Rt = 2 * p.rk, P = p.P;
+  const int h = 2 * hb + hl;
+  const int ntile = (t1 - t0 + TM - 1) / TM;
+  const int nks = R / KC;
+  const int last = t1 - 1;
+  const int pfirst = t0 / P;
+
+  const bf16* pages = static_cast<const bf16*>(p.pages);
+  const bf16* decA = static_cast<const bf16*>(p.A);
+  const bf16* decB = static_cast<const bf16*>(p.Bm);
+
+  // This wave's copies of a step: the key and value pieces of store tiles
+  // wave, wave + 8, .. of the tile, then its share of the decoder rows.
+  // Sources are uniform bases (a store tile, per tile) plus lane offsets plus
+  // the K step times a uniform stride, so a step only adds and issues.
+  const int np = (Sh::NTT - wave + kWaves - 1) / kWaves;   // store tiles of this wave
+  int dstart = 0;                                          // first decoder copy of this wave
+  for (int w = 0; w < wave; ++w) dstart += Sh::PER_WAVE - 2 * ((Sh::NTT - w + kWaves - 1) / kWaves);
+  const int row = lane >> 2, cq = (lane & 3) ^ ((row >> 2) & 3);
+  const uint32_t koff = row * R + 8 * cq;                  // key rows: row, chunk cq
+  const int vch = val_slot(lane);
+  const uint32_t voff = 16 * R + (vch >> 5) * 256 + ((vch >> 1) & 15) * 16 + (vch & 1) * 8;
+  uint32_t doff[Sh::PER_WAVE];
+  int dslot[Sh::PER_WAVE];
+#pragma unroll
+  for (int u = 0; u < Sh::PER_WAVE; ++u) {
+    const int dq = min(max(dstart + u - 2 * np, 0), 4 * NT - 1);   // decoder copy (clamped where unused)
+    const int which = dq / NT, nt = dq % NT;               // which: A h0, A h1, B h0, B h1
+    const int hh = min(2 * hb + (which & 1), H - 1);
+    doff[u] = ((uint32_t)hh * DH + 16 * nt) * R + koff;
+    dslot[u] = Sh::QA + dq;
+  }
+  const bf16* tbase[Sh::MAXP];
+  auto prep = [&](int tile) {
+    const int j0 = t0 + tile * TM;
+#pragma unroll
+    for (int k = 0; k < Sh::MAXP; ++k) {
+      const int jt = min(j0 + 16 * (wave + kWaves * k), last);   // a piece wholly past the end rereads the last
+      const int pg = __builtin_amdgcn_readfirstlane(sm.ptab[jt / P - pfirst]);
+      tbase[k] = pages + tile_base(pg, 0, jt % P, 1, P, Rt);
+    }
+  };
+  auto issue = [&](int ks, unsigned char* dst) {
+#pragma unroll
+    for (int u = 0; u < Sh::PER_WAVE; ++u) {
+      const bf16* src;
+      int slot;
+      if (u < 2 * np) {
+        const int k = u >> 1, tt = wave + kWaves * k;
+        src = (u & 1) ? tbase[k] + (voff + (uint32_t)ks * 512) : tbase[k] + (koff + (uint32_t)ks * KC);
+        slot = (u & 1) ? Sh::QV + tt : tt;
+      } else {
+        src = (dslot[u] < Sh::QB ? decA : decB) + (doff[u] + (uint32_t)ks * KC);
+        slot = dslot[u];
+      }
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                       (__attribute__((address_space(3))) void*)(dst + slot * 1024), 16, 0, 0);
+    }
+  };
+
+  // operand read offsets inside a stage
+  const int kslot = row_slot(col, kg) * 16;   // key / decoder rows: row col, chunk kg
+  int vslot[2];                               // V^: dims 8 kg + 4 hh + col / 4, tokens 4 (col % 4) ..
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const int d = 8 * kg + 4 * hh + (col >> 2), c4 = col & 3;
+    vslot[hh] = val_slot((d >> 4) * 32 + (d & 15) * 2 + (c4 >> 1)) * 16 + (c4 & 1) * 8;
+  }
+  const int dec_off = ((KIND == 0 ? Sh::QA : Sh::QB) + hl * NT) * 1024 + kslot;
+  const int lat_off = ((KIND == 0 ? 0 : Sh::QV) + th * MTW) * 1024;
+
+  f32x4 acc[MTW][NT];
+  float m = -INFINITY, l = 0.f, o[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) o[nt] = 0.f;
+
+  // one K step on the operands staged in `st`
+  auto compute = [&](const unsigned char* st) {
+    bf16x8 bb[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) bb[nt] = *reinterpret_cast<const bf16x8*>(st + dec_off + nt * 1024);
+#pragma unroll
+    for (int j = 0; j < MTW; ++j) {
+      bf16x8 a;
+      if (KIND == 0) {
+        a = *reinterpret_cast<const bf16x8*>(st + lat_off + j * 1024 + kslot);
+      } else {
+        // token col of store tile j of this half, dims 8 kg .. 8 kg + 7
+        typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+        const unsigned char* vb = st + lat_off + j * 1024;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + vslot[0]));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + vslot[1]));
+        a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        acc[j][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bb[nt], acc[j][nt], 0, 0, 0);
+    }
+  };
+
+  for (int tile = 0; tile < ntile; ++tile) {
+#pragma unroll
+    for (int j = 0; j < MTW; ++j)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[j][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // Every tile starts in buffer 0 (K steps alternate 0, 1, 0, ..).  Buffer 0
+    // is free here: its last reader passed the previous tile's score barrier.
+    prep(tile);
+    issue(0, stage0);
+    for (int ks = 0; ks < nks; ks += 2) {
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);   // this wave's copies of step ks have landed
+      __syncthreads();                        // everyone's have; buffer 1 is free
+      if (ks + 1 < nks) issue(ks + 1, stage1);
+      compute(stage0);
+      if (ks + 1 < nks) {
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        __syncthreads();
+        if (ks + 2 < nks) issue(ks + 2, stage0);
+        compute(stage1);
+      }
+    }
+
+    // ---- attention epilogue; lane holds X^[token 16 j + 4 kg + r of this half][dim 16 nt + col]
+    const int par = tile & 1;
+    const int j0 = t0 + tile * TM;
+    if (KIND == 0) {
+      float qv[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) qv[nt] = sm.qh[hl][16 * nt + col];
+#pragma unroll
+      for (int j = 0; j < MTW; ++j) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float a = 0.f;
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) a += qv[nt] * acc[j][nt][r];
+          a = row_sum16(a);
+          const int tok = th * TMW + 16 * j + 4 * kg + r;
+          if (col == 0) sm.sc[par][hl][tok] = (j0 + tok < t1) ? a : -INFINITY;
+        }
+      }
+    }
+    __syncthreads();
+    if (KIND == 1) {
+      // both halves take the maximum over all scores of the head's tile
+      const float* sch = sm.sc[par][hl];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int x = 0; x < TM / 64; ++x) mx = fmaxf(mx, sch[lane + 64 * x]);
+      mx = wave_max(mx);
+      const float mn = fmaxf(m, mx);
+      const float alpha = exp2_diff(m, mn);
+      float lp = 0.f;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) o[nt] *= alpha;
+#pragma unroll
+      for (int j = 0; j < MTW; ++j) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int tok = th * TMW + 16 * j + 4 * kg + r;
+          const bool ok = j0 + tok < t1;
+          const float pw = ok ? fast_exp2(sch[tok] - mn) : 0.f;
+          lp += pw;
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) o[nt] += ok ? pw * acc[j][nt][r] : 0.f;
+        }
+      }
+      lp += __shfl_xor(lp, 16);
+      lp += __shfl_xor(lp, 32);
+      l = l * alpha + lp;
+      m = mn;
+    }
+  }
+
+  // ---- merge the two token halves of each head and write the split's partial
+  if (KIND == 1) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      o[nt] += __shfl_xor(o[nt], 16);
+      o[nt] += __shfl_xor(o[nt], 32);
+    }
+    if (th == 1 && kg == 0) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) sm.mrg[hl][16 * nt + col] = o[nt];
+      if (col == 0) sm.mrg[hl][DH] = l;
+    }
+  }
+  __syncthreads();
+  if (KIND == 1 && th == 0 && h < H) {
+    const int64_t prow = ((int64_t)b * p.S + s) * H + h;
+    if (lane == 0) {
+      p.part_ml[prow * 2 + 0] = m;
+      p.part_ml[prow * 2 + 1] = l + sm.mrg[hl][DH];
+    }
+    if (kg == 0) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) p.part_o[prow * p.Dp + 16 * nt + col] = o[nt] + sm.mrg[hl][16 * nt + col];
+    }
+  }
+}
+
+template <int DH>
+__global__ __launch_bounds__(kThreads, 1) void k_scan_reconstruct_staged(DecodeParams p, int n_hp, int n_wg) {
+  __shared__ __attribute__((aligned(1024))) Smem<DH> sm;
+  __shared__ __attribute__((aligned(1024))) unsigned char stage0[Shape<DH>::STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char stage1[Shape<DH>::STAGE];
+  const int L = blockIdx.x;
+  const int lam = (L % kXcds) * (n_wg / kXcds) + L / kXcds;
+  const int grp_i = lam / (kGroupItems * n_hp), hb = (lam / kGroupItems) % n_hp;
+  const int item = grp_i * kGroupItems + lam % kGroupItems;
+  if (item >= p.B * p.S) return;      // padding: the whole workgroup leaves
+  const int b = item / p.S, s = item % p.S;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int i = p.pos[b];
+  const int n_lat = max(0, i - p.W);
+  int t0 = s * p.chunk;
+  const int t1 = (s == p.S - 1) ? n_lat : min(n_lat, t0 + p.chunk);
+  if (t0 > n_lat) t0 = n_lat;
+
+  // page ids of tokens t0 .. t1-1 (never more than max_pages <= kPageTab) and q' of both heads
+  const int pfirst = t0 / p.P;
+  const int npg = t1 > t0 ? (t1 - 1) / p.P - pfirst + 1 : 0;
+  for (int x = tid; x < npg; x += kThreads) sm.ptab[x] = p.bt[(int64_t)b * p.max_pages + pfirst + x];
+  for (int x = tid; x < 2 * DH; x += kThreads) {
+    const int hh = min(2 * hb + x / DH, p.H - 1);
+    sm.qh[x / DH][x % DH] = p.qhead[((int64_t)b * p.H + hh) * DH + x % DH];
+  }
+  __syncthreads();
+
+  const int hl = (wave >> 1) & 1, th = wave >> 2;
+  if (wave & 1)
+    staged_wave<DH, 1>(p, sm, stage0, stage1, b, s, hb, hl, th, wave, t0, t1);
+  else
+    staged_wave<DH, 0>(p, sm, stage0, stage1, b, s, hb, hl, th, wave, t0, t1);
+}
+
+}  // namespace staged
+
 }  // namespace
 
 bool scan_reconstruct_gemm_supports(const DecodeParams& p) {
   return p.bf16 && p.G == 1 && p.rk == p.rv && p.rk % KC == 0 && (p.dh == 96 || p.dh == 128 || p.dh == 64);
 }
 
-int scan_reconstruct_gemm_tile() { return TM; }
+// the staged form serves d_h = 64, 96 when the split's page ids fit its LDS table
+static bool staged_form(const DecodeParams& p) {
+  return (p.dh == 64 || p.dh == 96) && p.max_pages <= staged::kPageTab;
+}
+
+int scan_reconstruct_gemm_tile(int dh) {
+  return dh == 96 ? staged::Shape<96>::TM : dh == 64 ? staged::Shape<64>::TM : TM;
+}
 
 hipError_t launch_scan_reconstruct_gemm(const DecodeParams& p, hipStream_t s) {
   if (!scan_reconstruct_gemm_supports(p)) return hipErrorNotSupported;
@@ -287,12 +607,20 @@ hipError_t launch_scan_reconstruct_gemm(const DecodeParams& p, hipStream_t s) {
   const int64_t n_wg = (wg + kXcds - 1) / kXcds * kXcds;
   if (n_wg > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid((unsigned)n_wg);
-  if (p.dh == 96)
+  if (staged_form(p)) {
+    if (p.dh == 96)
+      hipLaunchKernelGGL(staged::k_scan_reconstruct_staged<96>, grid, dim3(staged::kThreads), 0, s, p, n_hp,
+                         (int)n_wg);
+    else
+      hipLaunchKernelGGL(staged::k_scan_reconstruct_staged<64>, grid, dim3(staged::kThreads), 0, s, p, n_hp,
+                         (int)n_wg);
+  } else if (p.dh == 96) {
     hipLaunchKernelGGL(k_scan_reconstruct_gemm<96>, grid, dim3(kThreads), 0, s, p, n_hp, (int)n_wg);
-  else if (p.dh == 128)
+  } else if (p.dh == 128) {
     hipLaunchKernelGGL(k_scan_reconstruct_gemm<128>, grid, dim3(kThreads), 0, s, p, n_hp, (int)n_wg);
-  else
+  } else {
     hipLaunchKernelGGL(k_scan_reconstruct_gemm<64>, grid, dim3(kThreads), 0, s, p, n_hp, (int)n_wg);
+  }
   return hipGetLastError();
 }
 
