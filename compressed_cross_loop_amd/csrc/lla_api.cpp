@@ -159,7 +159,8 @@ Plan plan_for(const lla_set_desc& d, int batch, int max_pos, int window, int spl
 }
 
 struct WsLayout {
-  size_t qlat, qhead, part_ml, part_o, win_ml, win_o, tickets, fpart, total;
+  size_t qlat, qhead, part_ml, part_o, win_ml, win_o, dect, tickets, fpart, total;
+  bool has_dect;
 };
 
 size_t up256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -184,6 +185,11 @@ WsLayout ws_layout(const lla_set_desc& d, int B, int S, int WS, int Dp, bool fus
   w.part_o = off;  off = up256(off + (size_t)B * S * H * Dp * 4);
   w.win_ml = off;  off = up256(off + (size_t)B * WS * H * 2 * 4);
   w.win_o = off;   off = up256(off + (size_t)B * WS * H * dh * 4);
+  // head-folded reconstruct: A_t and B_t^T regrouped per K step
+  w.has_dect = scan_reconstruct_gemm_tiles_decoders(d.head_dim, d.groups, d.r_k, d.r_v, d.dtype == LLA_BF16);
+  if (w.has_dect) {
+    w.dect = off;  off = up256(off + (size_t)2 * H * dh * d.r_k * 2);
+  }
   w.total = off;
   return w;
 }
@@ -322,6 +328,7 @@ lla_status decode(const lla_set_desc* d, const lla_store* st, int32_t batch,
   p.part_o = reinterpret_cast<float*>(ws + w.part_o);
   p.win_ml = reinterpret_cast<float*>(ws + w.win_ml);
   p.win_o = reinterpret_cast<float*>(ws + w.win_o);
+  p.dect = w.has_dect ? ws + w.dect : nullptr;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipEvent_t* ev = static_cast<hipEvent_t*>(a->scan_events);
   if (fused) {
@@ -349,12 +356,14 @@ lla_status decode(const lla_set_desc* d, const lla_store* st, int32_t batch,
   hipError_t e = (!generic && qmap_mfma_supports(p)) ? launch_qmap_mfma(p, absorbed, s)
                                                      : launch_qmap(p, absorbed, s);
   if (e == hipSuccess && !p.fuse_window) e = fast_window ? launch_window_fast(p, s) : launch_window(p, s);
+  const bool gemm_reconstruct = !absorbed && !use_mfma_reconstruct(*d, a->flags) && use_gemm_reconstruct(*d, a->flags);
+  if (e == hipSuccess && gemm_reconstruct) e = launch_scan_reconstruct_gemm_prep(p, s);
   if (e == hipSuccess && ev) e = hipEventRecord(ev[0], s);
   if (e == hipSuccess) {
     if (!absorbed) {
       if (use_mfma_reconstruct(*d, a->flags))
         e = launch_scan_reconstruct_mfma(p, s);
-      else if (use_gemm_reconstruct(*d, a->flags))
+      else if (gemm_reconstruct)
         e = launch_scan_reconstruct_gemm(p, s);
       else
         e = launch_scan_reconstruct_generic(p, s);

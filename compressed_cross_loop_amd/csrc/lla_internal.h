@@ -46,6 +46,9 @@ struct DecodeParams {
   float* part_o;                  // [B][S][H][Dp]
   float* win_ml;                  // [B][WS][H][2]
   float* win_o;                   // [B][WS][H][dh]
+  // head-folded reconstruct (LDS-staged form): A_t and B_t^T rows regrouped
+  // per K step of 32 latent dims, [H][2][r/32][d_h][32] bf16
+  void* dect;
   // fused single-launch path
   int32_t* tickets;               // [B][H] arrival counters
   float* fpart;                   // [B][H][S][2 + rv + dh]
@@ -125,8 +128,11 @@ bool scan_reconstruct_mfma_supports(const DecodeParams& p);
 hipError_t launch_scan_reconstruct_mfma(const DecodeParams& p, hipStream_t s);
 
 bool scan_reconstruct_gemm_supports(const DecodeParams& p);
+bool scan_reconstruct_gemm_tiles_decoders(int dh, int G, int rk, int rv, int bf16);   // needs DecodeParams::dect
 int scan_reconstruct_gemm_tile(int dh);   // tokens per workgroup tile (split granularity)
 hipError_t launch_scan_reconstruct_gemm(const DecodeParams& p, hipStream_t s);
+// regroups the decoders into DecodeParams::dect when the scan will read them from there
+hipError_t launch_scan_reconstruct_gemm_prep(const DecodeParams& p, hipStream_t s);
 
 constexpr int kMaxFusedSplits = 1024;   // context splits per (sequence, head) of the fused path
 bool fused_decode_supports(const DecodeParams& p);

@@ -29,6 +29,8 @@
 // contiguous range of (4 sequence splits x head pairs): the workgroups in
 // flight on one XCD share latent tiles (same split, other head pairs) and
 // decoders (same head pair, other splits) in that XCD's L2.
+#include <algorithm>
+
 #include "device_common.h"
 #include "lla_internal.h"
 
@@ -292,8 +294,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_scan_reconstruct_gemm(DecodePar
 //   12 + i / 4), which turns four dims x 16 tokens into the token-major
 //   A-operand pieces of the MFMA; chunk slots are XOR-swizzled (bit 3 ^= bit
 //   4) so the two 16-lane groups served together read different banks.
-// The two token halves of a head see the same 256 scores, so they keep the
-// same running maximum and their (l, o) simply add at the end.
+// The decoder rows come from a copy regrouped per K step ([H][A_t, B_t^T]
+// [r/32][d_h][32], written by k_tile_decoders at the start of the call), so
+// each decoder copy is a contiguous 1 KiB as well; a copy of 16 strided row
+// pieces costs the address unit about twice as much.
+// The two token halves of a head see the same scores, so they keep the same
+// running maximum and their (l, o) simply add at the end.
 namespace staged {
 
 constexpr int kWaves = 8;
@@ -353,8 +359,7 @@ __device__ __forceinline__ void staged_wave(const DecodeParams& p, Smem<DH>& sm,
   const int pfirst = t0 / P;
 
   const bf16* pages = static_cast<const bf16*>(p.pages);
-  const bf16* decA = static_cast<const bf16*>(p.A);
-  const bf16* decB = static_cast<const bf16*>(p.Bm);
+  const bf16* dect = static_cast<const bf16*>(p.dect);
 
   // This wave's copies of a step: the key and value pieces of store tiles
   // wave, wave + 8, .. of the tile, then its share of the decoder rows.
@@ -374,7 +379,7 @@ __device__ __forceinline__ void staged_wave(const DecodeParams& p, Smem<DH>& sm,
     const int dq = min(max(dstart + u - 2 * np, 0), 4 * NT - 1);   // decoder copy (clamped where unused)
     const int which = dq / NT, nt = dq % NT;               // which: A h0, A h1, B h0, B h1
     const int hh = min(2 * hb + (which & 1), H - 1);
-    doff[u] = ((uint32_t)hh * DH + 16 * nt) * R + koff;
+    doff[u] = (((uint32_t)hh * 2 + (which >> 1)) * nks * DH + 16 * nt + row) * KC + 8 * cq;
     dslot[u] = Sh::QA + dq;
   }
   const bf16* tbase[Sh::MAXP];
@@ -397,7 +402,7 @@ __device__ __forceinline__ void staged_wave(const DecodeParams& p, Smem<DH>& sm,
         src = (u & 1) ? tbase[k] + (voff + (uint32_t)ks * 512) : tbase[k] + (koff + (uint32_t)ks * KC);
         slot = (u & 1) ? Sh::QV + tt : tt;
       } else {
-        src = (dslot[u] < Sh::QB ? decA : decB) + (doff[u] + (uint32_t)ks * KC);
+        src = dect + (doff[u] + (uint32_t)ks * (DH * KC));
         slot = dslot[u];
       }
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
@@ -582,6 +587,22 @@ __global__ __launch_bounds__(kThreads, 1) void k_scan_reconstruct_staged(DecodeP
     staged_wave<DH, 0>(p, sm, stage0, stage1, b, s, hb, hl, th, wave, t0, t1);
 }
 
+// dect[h][ab][ks][d][k] = (ab ? B_t^T : A_t)[h][d][32 ks + k], 16 bytes per thread
+__global__ __launch_bounds__(256) void k_tile_decoders(const bf16* __restrict__ A, const bf16* __restrict__ Bt,
+                                                       bf16* __restrict__ dect, int H, int DH, int R) {
+  const int64_t n8 = (int64_t)2 * H * DH * R / 8;
+  for (int64_t x = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; x < n8; x += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t e = 8 * x;                      // source element: [ab][h][d][r]
+    const int r = (int)(e % R);
+    const int64_t hd = e / R;                     // (ab, h, d)
+    const int d = (int)(hd % DH);
+    const int64_t abh = hd / DH;
+    const int h = (int)(abh % H), ab = (int)(abh / H);
+    const uint4 v = *reinterpret_cast<const uint4*>((ab ? Bt : A) + ((int64_t)h * DH + d) * R + r);
+    *reinterpret_cast<uint4*>(dect + ((((int64_t)h * 2 + ab) * (R / KC) + r / KC) * DH + d) * KC + r % KC) = v;
+  }
+}
+
 }  // namespace staged
 
 }  // namespace
@@ -590,9 +611,23 @@ bool scan_reconstruct_gemm_supports(const DecodeParams& p) {
   return p.bf16 && p.G == 1 && p.rk == p.rv && p.rk % KC == 0 && (p.dh == 96 || p.dh == 128 || p.dh == 64);
 }
 
-// the staged form serves d_h = 64, 96 when the split's page ids fit its LDS table
+bool scan_reconstruct_gemm_tiles_decoders(int dh, int G, int rk, int rv, int bf16) {
+  return bf16 && G == 1 && rk == rv && rk % KC == 0 && (dh == 64 || dh == 96);
+}
+
+// the staged form serves d_h = 64, 96 when the split's page ids fit its LDS
+// table and the call brought the regrouped decoder buffer
 static bool staged_form(const DecodeParams& p) {
-  return (p.dh == 64 || p.dh == 96) && p.max_pages <= staged::kPageTab;
+  return (p.dh == 64 || p.dh == 96) && p.max_pages <= staged::kPageTab && p.dect != nullptr;
+}
+
+hipError_t launch_scan_reconstruct_gemm_prep(const DecodeParams& p, hipStream_t s) {
+  if (!scan_reconstruct_gemm_supports(p) || !staged_form(p)) return hipSuccess;
+  const int64_t n8 = (int64_t)2 * p.H * p.dh * p.rk / 8;
+  const int tb = (int)std::min<int64_t>((n8 + 255) / 256, 4096);
+  hipLaunchKernelGGL(staged::k_tile_decoders, dim3(tb), dim3(256), 0, s, static_cast<const bf16*>(p.A),
+                     static_cast<const bf16*>(p.Bm), static_cast<bf16*>(p.dect), p.H, p.dh, p.rk);
+  return hipGetLastError();
 }
 
 int scan_reconstruct_gemm_tile(int dh) {
