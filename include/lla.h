@@ -246,7 +246,10 @@ lla_status hla_decode_windowed(const lla_set_desc* desc, const lla_store* store,
                                lla_stream_t stream);
 
 /* Workspace bytes any decode entry point needs for these sizes (splits as
- * in lla_decode_args; 0 = automatic). */
+ * in lla_decode_args; 0 = automatic).  For bf16 sets with one latent shared
+ * by all heads (groups == 1, r_k == r_v, d_h 64 or 96) it includes a copy of
+ * A_t and B_t^T regrouped per 32 latent dims (2 H d_h r_k bf16), which the
+ * reconstruct read refills on every call. */
 size_t lla_decode_workspace_bytes(const lla_set_desc* desc, int32_t batch,
                                   int32_t max_pos, int32_t window, int32_t splits);
 
