@@ -4,18 +4,33 @@
 //
 // One wave per head (each head has its own latent group), four waves per
 // workgroup, one workgroup per (context split, sequence, 4 heads).  Per
-// 16-token tile the wave rebuilds, for its head,
-//   K^ [16 tok x d_h] = S^K [16 x r] . A^T [r x d_h]   (v_mfma_f32_16x16x32_bf16)
-//   V^ [16 tok x d_h] = S^V [16 x r] . B_t [r x d_h]   (same)
-// then scores K^ q' (the 16 lanes holding one token row reduce), an online
-// softmax over the tile, and o += p . V^.  Both decoders are stored [d_h][r]
-// (rows contiguous along the latent axis), so each B-operand fragment is one
-// 16-byte load; they are held in registers for the whole scan.  Key rows are
-// token-major in the store (one 16-byte load per lane); the tile's value block
-// is stored dimension-major (for the absorbed read), so each wave transposes
-// it through its own LDS slice before the V^ product.  Several tiles are kept
-// in flight.
+// 16-token tile the wave rebuilds, for its head, the transposed keys and
+// values
+//   K^T [d_h x 16 tok] = A_t [d_h x r] . S^K^T [r x 16]   (v_mfma_f32_16x16x32_bf16)
+//   V^T [d_h x 16 tok] = B_t^T [d_h x r] . S^V^T [r x 16]
+// so that every lane ends with 4 dims of each 16-dim block for ONE token
+// (token = lane % 16).  Then, per lane and without cross-lane traffic except
+// one 4-lane reduction of the score:
+//   score  q' . k^_tok   (the lane's 4 NT partial dims, summed over the 4 lane
+//          groups holding the same token)
+//   p      2^(score - m), running maximum m moved lazily (only when a tile's
+//          maximum exceeds it by more than 2^8), so rescaling is rare
+//   o      += p v^_tok for the lane's dims; o and the weight sum stay per
+//          token lane and are summed over the 16 token lanes once per split.
+// Both decoders are stored [d_h][r] (rows contiguous along the latent axis),
+// i.e. directly in A-operand layout; they are held in registers for the whole
+// scan.  Key rows are token-major in the store: one 16-byte load per lane is
+// the B operand.  The tile's value block is dimension-major (for the absorbed
+// read); it is loaded into registers like the keys (16 contiguous bytes per
+// lane and KiB), written to a wave-private KiB of LDS when the tile is
+// consumed and read back as token-major B operands with the gfx950
+// transposing read ds_read_b64_tr_b16 (inside each 16-lane group lane i
+// receives element i % 4 of lanes i / 4, 4 + i / 4, 8 + i / 4, 12 + i / 4).
+// A wave's LDS operations run in order, so one slot per wave needs no
+// barrier.  Several tiles are in flight per wave, all in registers; the page
+// ids of the split are staged in LDS first.
 #include <type_traits>
+#include <utility>
 
 #include "device_common.h"
 #include "lla_internal.h"
@@ -26,33 +41,55 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
+constexpr int kPageTab = 4096;            // page ids of a split, staged in LDS
+constexpr float kLazy = 8.f;              // running-max slack (exp2 units)
+
+template <typename F, int... U>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, U...>) {
+  (f(std::integral_constant<int, U>{}), ...);
+}
+template <int N, typename F> __device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// 16-byte chunk slot of a value copy: bit 3 ^= bit 4, so that the two
+// 16-lane groups a transposing read serves together hit different banks
+__device__ __forceinline__ int val_slot(int ch) { return ch ^ (((ch >> 4) & 1) << 3); }
 
 template <int R, int DH>
-__global__ __launch_bounds__(kThreads, 2) void k_scan_reconstruct_mfma(DecodeParams p) {
-  constexpr int NT = DH / 16;     // column tiles of d_h
-  constexpr int KS = R / 32;      // K steps over the latent width
-  constexpr int VC = R / 32;      // 16-byte value chunks per lane per tile (16 tok x R / 64 lanes / 8)
-  constexpr int kPF = R == 32 ? 8 : 2;   // tiles in flight per wave
-  __shared__ __attribute__((aligned(16))) bf16 vt[kWaves][16][R + 8];
+__global__ __launch_bounds__(kThreads, (R == 32 || DH == 64) ? 2 : 1) void k_scan_reconstruct_mfma(DecodeParams p) {
+  constexpr int NT = DH / 16;            // 16-dim blocks of d_h
+  constexpr int KS = R / 32;             // K steps over the latent width = KiB of values per tile
+  constexpr int kPF = R == 32 ? 6 : 3;   // tiles in flight per wave
+  __shared__ int32_t ptab[kPageTab];
+  __shared__ __attribute__((aligned(16))) unsigned char vlds[kWaves][KS * 1024];
   const int s = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
   const int h = blockIdx.z * kWaves + wave;
-  if (h >= p.H) return;
-  const int g = h / p.hpg;
   const int G = p.G, P = p.P, Rt = 2 * R;
   const int i = p.pos[b];
   const int n_lat = max(0, i - p.W);
   int t0 = s * p.chunk;
   int t1 = (s == p.S - 1) ? n_lat : min(n_lat, t0 + p.chunk);
   if (t0 > n_lat) t0 = n_lat;
+  // page ids of tokens t0 .. t1-1 (never more than max_pages <= kPageTab):
+  // a block-table read in the loop would be a vector load, and waiting for it
+  // (load counts complete in issue order) would drain the tiles in flight
+  const int pfirst = t0 / P;
+  const int npg = t1 > t0 ? (t1 - 1) / P - pfirst + 1 : 0;
+  for (int x = tid; x < npg; x += kThreads) ptab[x] = p.bt[(int64_t)b * p.max_pages + pfirst + x];
+  __syncthreads();
+  if (h >= p.H) return;                  // wave-uniform; no barrier follows
+  const int g = h / p.hpg;
 
-  // decoders of this head, in B-operand layout (lane: column e = 16 nt + col,
-  // 8 consecutive latent dims 32 st + 8 grp ..)
+  // decoders of this head in A-operand layout (lane: row 16 nt + col, latent
+  // dims 32 st + 8 grp ..)
   const bf16* Ah = static_cast<const bf16*>(p.A) + (int64_t)h * DH * R;   // [DH][R]
   const bf16* Bh = static_cast<const bf16*>(p.Bm) + (int64_t)h * DH * R;  // B_t^T: [DH][R]
   bf16x8 af[NT][KS], bfr[NT][KS];
@@ -63,134 +100,151 @@ __global__ __launch_bounds__(kThreads, 2) void k_scan_reconstruct_mfma(DecodePar
       af[nt][st] = *reinterpret_cast<const bf16x8*>(Ah + (int64_t)(16 * nt + col) * R + 32 * st + 8 * grp);
       bfr[nt][st] = *reinterpret_cast<const bf16x8*>(Bh + (int64_t)(16 * nt + col) * R + 32 * st + 8 * grp);
     }
-  float qv[NT];
+  // q' at this lane's dims 16 nt + 4 grp + r
+  f32x4 qv[NT];
   {
     const float* qh = p.qhead + ((int64_t)b * p.H + h) * DH;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) qv[nt] = qh[16 * nt + col];
+    for (int nt = 0; nt < NT; ++nt) qv[nt] = *reinterpret_cast<const f32x4*>(qh + 16 * nt + 4 * grp);
   }
 
   const bf16* pages = static_cast<const bf16*>(p.pages);
-  const int32_t* bt = p.bt + (int64_t)b * p.max_pages;
   const int ntiles = (t1 - t0 + 15) / 16;
   auto tile_ptr = [&](int ti) -> const bf16* {
     const int j0 = t0 + min(ti, ntiles - 1) * 16;
-    return pages + tile_base(bt[j0 / P], g, j0 % P, G, P, Rt);
+    const int pg = __builtin_amdgcn_readfirstlane(ptab[j0 / P - pfirst]);
+    return pages + tile_base(pg, g, j0 % P, G, P, Rt);
   };
-  struct Buf {
-    bf16x8 k[KS];
-    bf16x8 v[VC];
-  };
-  auto load = [&](Buf& buf, int ti) {
+  // transposing-read offsets (bytes inside a KiB of values): dims 8 grp + 4 hh + col / 4,
+  // tokens 4 (col % 4) .. + 3
+  int vro[2];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const int d = 8 * grp + 4 * hh + (col >> 2), c4 = col & 3;
+    vro[hh] = val_slot((d >> 4) * 32 + (d & 15) * 2 + (c4 >> 1)) * 16 + (c4 & 1) * 8;
+  }
+  // this lane's 16-byte chunk of each value KiB: read from chunk
+  // val_slot(lane) of the block, stored at slot `lane` of the wave's LDS KiB
+  const int vsrc = val_slot(lane) * 8;
+  bf16x8 kbuf[kPF][KS], vbuf[kPF][KS];
+  // tile ti -> register set U
+  auto issue = [&](auto U, int ti) {
+    constexpr int u = decltype(U)::value;
     const bf16* tp = tile_ptr(ti);
 #pragma unroll
-    for (int st = 0; st < KS; ++st)
-      buf.k[st] = *reinterpret_cast<const bf16x8*>(tp + col * R + 32 * st + 8 * grp);
-#pragma unroll
-    for (int c = 0; c < VC; ++c)   // value block: 16 * R contiguous elements
-      buf.v[c] = *reinterpret_cast<const bf16x8*>(tp + 16 * R + (c * 64 + lane) * 8);
+    for (int st = 0; st < KS; ++st) {
+      kbuf[u][st] = *reinterpret_cast<const bf16x8*>(tp + col * R + 32 * st + 8 * grp);
+      vbuf[u][st] = *reinterpret_cast<const bf16x8*>(tp + 16 * R + st * 512 + vsrc);
+    }
   };
 
-  float m = -INFINITY, lsum = 0.f, o[NT];
+  float m = -INFINITY, lsum = 0.f;
+  f32x4 o[NT];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) o[nt] = 0.f;
+  for (int nt = 0; nt < NT; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // FULL: all 16 tokens of the tile are valid (every tile but a ragged last
-  // one), so no masking
-  auto step = [&](const Buf& buf, int nvalid, auto full) {
+  // consume slot U holding tile ti (nvalid tokens valid; FULL: all 16)
+  auto step = [&](auto U, int nvalid, auto full) {
+    constexpr int u = decltype(U)::value;
     constexpr bool FULL = decltype(full)::value;
-    // rebuild keys: lane holds K^[tok 4 grp + r][e = 16 nt + col]
-    f32x4 kh[NT];
+    const bool valid = FULL || col < nvalid;
+    // keys: lane holds K^T[dim 16 nt + 4 grp + r][token col]
+    float sc = 0.f;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      kh[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      f32x4 kh = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int st = 0; st < KS; ++st)
-        kh[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(buf.k[st], af[nt][st], kh[nt], 0, 0, 0);
+        kh = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[nt][st], kbuf[u][st], kh, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sc += qv[nt][r] * kh[r];
     }
-    // value block -> LDS, token-major: element x of the block is
-    // (sub-block x/256, dim-in-block (x%256)/16, token x%16)
-#pragma unroll
-    for (int c = 0; c < VC; ++c) {
-      const int x0 = (c * 64 + lane) * 8;
-      const int r = (x0 / 256) * 16 + (x0 % 256) / 16, tk = x0 % 16;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) vt[wave][tk + k][r] = buf.v[c][k];
-    }
-    // scores of the rebuilt keys against q'
-    float sc[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float a = 0.f;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) a += qv[nt] * kh[nt][r];
-      a = row_sum16(a);   // the 16 lanes of this lane group hold one token row
-      sc[r] = (FULL || 4 * grp + r < nvalid) ? a : -INFINITY;
-    }
-    float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mn = fmaxf(m, mx);
-    const float alpha = exp2_diff(m, mn);
-    float pr[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(sc[r] - mn);
-    lsum = lsum * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-    m = mn;
-    if (alpha != 1.f) {   // uniform: the wave holds one head
+    sc += __shfl_xor(sc, 16);
+    sc += __shfl_xor(sc, 32);
+    if (!FULL && !valid) sc = -INFINITY;
+    const float mx = row_max16(sc);       // the same in every lane group
+    if (mx > m + kLazy) {                 // wave-uniform
+      const float alpha = exp2_diff(m, mx);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) o[nt] *= alpha;
+      lsum *= alpha;
+      m = mx;
     }
-    // rebuild values: A operand = token rows of the transposed block
-    bf16x8 sv[KS];
+    const float pw = fast_exp2(sc - m);   // 0 for masked tokens
+    lsum += pw;
+    // values: lane holds V^T[dim 16 nt + 4 grp + r][token col]
+    bf16x8 vf[KS];
 #pragma unroll
-    for (int st = 0; st < KS; ++st) sv[st] = *reinterpret_cast<const bf16x8*>(&vt[wave][col][32 * st + 8 * grp]);
+    for (int st = 0; st < KS; ++st) {
+      typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+      unsigned char* vb = &vlds[wave][st * 1024];
+      *reinterpret_cast<bf16x8*>(vb + 16 * lane) = vbuf[u][st];
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + vro[0]));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + vro[1]));
+      vf[st] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       f32x4 vh = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int st = 0; st < KS; ++st) vh = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sv[st], bfr[nt][st], vh, 0, 0, 0);
-      float acc = o[nt];
+      for (int st = 0; st < KS; ++st) vh = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[nt][st], vf[st], vh, 0, 0, 0);
+      if (FULL) {
+        o[nt] += pw * vh;
+      } else {
+        // a masked token's rebuilt value may be anything (even NaN): select, not multiply
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc += (FULL || 4 * grp + r < nvalid) ? pr[r] * vh[r] : 0.f;
-      o[nt] = acc;
+        for (int r = 0; r < 4; ++r) o[nt][r] = valid ? o[nt][r] + pw * vh[r] : o[nt][r];
+      }
     }
   };
 
+  // decoders and q' have landed before the tile loads start: the loop's waits
+  // then only count tile loads, which complete in issue order
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   if (ntiles > 0) {
-    Buf buf[kPF];
-#pragma unroll
-    for (int u = 0; u < kPF; ++u) load(buf[u], u);
-    for (int base = 0; base < ntiles; base += kPF) {
-#pragma unroll
-      for (int u = 0; u < kPF; ++u) {
-        if (base + u < ntiles) {
-          const int nvalid = min(16, t1 - (t0 + (base + u) * 16));
-          if (nvalid == 16)
-            step(buf[u], 16, std::true_type{});
-          else
-            step(buf[u], nvalid, std::false_type{});
-        }
-        load(buf[u], base + u + kPF);   // clamped: always a valid tile
-      }
+    // prologue in slot order (the loop's waits assume loads complete in it)
+    static_for<kPF>([&](auto U) {
+      issue(U, decltype(U)::value);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    // main loop over whole groups of full tiles: no branches in the body, so
+    // every register set is refilled in place and the waits count exactly
+    const int nfull = (t1 - t0) / 16;
+    int base = 0;
+    for (; base + kPF <= nfull; base += kPF) {
+      static_for<kPF>([&](auto U) {
+        step(U, 16, std::true_type{});
+        __builtin_amdgcn_sched_barrier(0);   // keep each refill below its consumer
+        issue(U, base + decltype(U)::value + kPF);   // clamped: always a valid tile
+        __builtin_amdgcn_sched_barrier(0);
+      });
     }
+    // the rest (fewer than kPF full tiles and a ragged last one) is already in flight
+    static_for<kPF>([&](auto U) {
+      constexpr int u = decltype(U)::value;
+      if (base + u < ntiles) {
+        const int nvalid = min(16, t1 - (t0 + (base + u) * 16));
+        if (nvalid == 16)
+          step(U, 16, std::true_type{});
+        else
+          step(U, nvalid, std::false_type{});
+      }
+    });
   }
-  // totals over the four lane groups (each held 4 tokens per tile)
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
+  // totals over the 16 token lanes (the four lane groups hold the same tokens)
+  lsum = row_sum16(lsum);
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    o[nt] += __shfl_xor(o[nt], 16);
-    o[nt] += __shfl_xor(o[nt], 32);
-  }
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) o[nt][r] = row_sum16(o[nt][r]);
   const int64_t row = ((int64_t)b * p.S + s) * p.H + h;
   if (lane == 0) {
     p.part_ml[row * 2 + 0] = m;
     p.part_ml[row * 2 + 1] = lsum;
   }
-  if (grp == 0) {
+  if (col == 0) {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) p.part_o[row * p.Dp + 16 * nt + col] = o[nt];
+    for (int nt = 0; nt < NT; ++nt) *reinterpret_cast<f32x4*>(p.part_o + row * p.Dp + 16 * nt + 4 * grp) = o[nt];
   }
 }
 
@@ -205,7 +259,7 @@ hipError_t launch_r(const DecodeParams& p, hipStream_t st) {
 
 bool scan_reconstruct_mfma_supports(const DecodeParams& p) {
   return p.bf16 && p.hpg == 1 && p.rk == p.rv && (p.rk == 32 || p.rk == 64) &&
-         (p.dh == 64 || p.dh == 128);
+         (p.dh == 64 || p.dh == 128) && p.max_pages <= kPageTab;
 }
 
 hipError_t launch_scan_reconstruct_mfma(const DecodeParams& p, hipStream_t s) {
