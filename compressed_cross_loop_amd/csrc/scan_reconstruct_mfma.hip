@@ -149,16 +149,18 @@ __global__ __launch_bounds__(kThreads, (R == 32 || DH == 64) ? 2 : 1) void k_sca
     constexpr bool FULL = decltype(full)::value;
     const bool valid = FULL || col < nvalid;
     // keys: lane holds K^T[dim 16 nt + 4 grp + r][token col]
-    float sc = 0.f;
+    // four independent partial sums (one per r), so the products do not
+    // form one dependent chain
+    f32x4 sc4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       f32x4 kh = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int st = 0; st < KS; ++st)
         kh = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[nt][st], kbuf[u][st], kh, 0, 0, 0);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sc += qv[nt][r] * kh[r];
+      sc4 += qv[nt] * kh;
     }
+    float sc = (sc4[0] + sc4[1]) + (sc4[2] + sc4[3]);
     sc += __shfl_xor(sc, 16);
     sc += __shfl_xor(sc, 32);
     if (!FULL && !valid) sc = -INFINITY;
