@@ -55,6 +55,10 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
 constexpr float kLazy = 8.f;   // running-max slack of the attention softmax (exp2 units)
+// Initial running maximum of the attention softmax: finite, so that 2^(s - m)
+// needs no special case (a masked score is -inf and gives 0; the first real
+// maximum replaces it and scales the empty sums by 2^(-huge) = 0)
+constexpr float kMinMax = -1e30f;
 constexpr int kAttnQB = 2;                  // query blocks of 16 positions per wave
 constexpr int kAttnQT = 4 * 16 * kAttnQB;   // positions per attention workgroup (4 waves)
 static_assert(kParQueryTile % kAttnQT == 0, "padding must cover whole query tiles");
@@ -261,7 +265,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_par_attn(ParParams p) {
   float m[QB], l[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    m[qb] = -INFINITY;
+    m[qb] = kMinMax;
     l[qb] = 0.f;
   }
 
@@ -403,32 +407,36 @@ __global__ __launch_bounds__(kThreads, 2) void k_par_attn(ParParams p) {
       // online softmax per position (column) over the 32 keys; sc becomes P
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        float mx = fmaxf(fmaxf(fmaxf(sc[0][qb][0], sc[0][qb][1]), fmaxf(sc[0][qb][2], sc[0][qb][3])),
-                         fmaxf(fmaxf(sc[1][qb][0], sc[1][qb][1]), fmaxf(sc[1][qb][2], sc[1][qb][3])));
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        // The running max moves only when the new one exceeds it by more than
+        // The running max moves only when a new score exceeds it by more than
         // kLazy (exp2 units): weights relative to a slightly stale max stay
         // below 2^kLazy, exact in fp32 and bf16, and the output divides by a
-        // sum taken relative to the same max.  The accumulators (in AGPRs)
-        // are then rescaled rarely instead of every few tiles.
-        const float mn = mx > m[qb] + kLazy ? mx : m[qb];
-        const float alpha = exp2_diff(m[qb], mn);
-        m[qb] = mn;
+        // sum taken relative to the same max.  Each lane first checks its own
+        // 8 scores; only when some lane of the wave sees such a score is the
+        // maximum of each position reduced over its four lane groups and the
+        // accumulators rescaled, which is rare after the first tiles.
+        const float lmx = fmaxf(fmaxf(fmaxf(sc[0][qb][0], sc[0][qb][1]), fmaxf(sc[0][qb][2], sc[0][qb][3])),
+                                fmaxf(fmaxf(sc[1][qb][0], sc[1][qb][1]), fmaxf(sc[1][qb][2], sc[1][qb][3])));
+        if (__any(lmx > m[qb] + kLazy)) {
+          float mx = fmaxf(lmx, __shfl_xor(lmx, 16));
+          mx = fmaxf(mx, __shfl_xor(mx, 32));
+          const float mn = mx > m[qb] + kLazy ? mx : m[qb];
+          const float alpha = fast_exp2(m[qb] - mn);
+          m[qb] = mn;
+          l[qb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) acc[qb][db] *= alpha;
+        }
+        const float mn = m[qb];
         float sum = 0.f;
 #pragma unroll
         for (int hs = 0; hs < 2; ++hs)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float pr = exp2_diff(sc[hs][qb][r], mn);
+            const float pr = fast_exp2(sc[hs][qb][r] - mn);
             sc[hs][qb][r] = pr;
             sum += pr;
           }
-        l[qb] = l[qb] * alpha + sum;
-        if (__any(alpha != 1.f)) {
-#pragma unroll
-          for (int db = 0; db < DB; ++db) acc[qb][db] *= alpha;
-        }
+        l[qb] += sum;
       }
       // values: the latent and exact parts of P against their own values.
       // The value MFMA's K index e of this lane is token 4 grp + e % 4 of
@@ -446,7 +454,14 @@ __global__ __launch_bounds__(kThreads, 2) void k_par_attn(ParParams p) {
       if (lat_u) {
         bf16x8 pl[QB];
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) pl[qb] = p_part(qb, true);
+        for (int qb = 0; qb < QB; ++qb) {
+          if (pure) {   // every key of the half is a latent token for every position
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pl[qb][e] = static_cast<bf16>(sc[e / 4][qb][e % 4]);
+          } else {
+            pl[qb] = p_part(qb, true);
+          }
+        }
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
           const bf16* vrow = &vl_s[(16 * db + col) * LDV + 32 * u + 4 * grp];
