@@ -260,7 +260,7 @@ lla_status check_parallel_desc(const lla_set_desc* d) {
 int parallel_pad(int n_max) { return (n_max + kParQueryTile - 1) / kParQueryTile * kParQueryTile; }
 
 struct ParWs {
-  size_t sk, sv, qr, kr, vt, kh, vht, total;
+  size_t sk, sv, qr, kr, kh, vh, total;
 };
 
 ParWs parallel_ws_layout(const lla_set_desc& d, int B, int n_max) {
@@ -272,9 +272,8 @@ ParWs parallel_ws_layout(const lla_set_desc& d, int B, int n_max) {
   w.sv = off;  off = up256(off + (size_t)B * np * G * d.r_v * 2);
   w.qr = off;  off = up256(off + head_rows);
   w.kr = off;  off = up256(off + head_rows);
-  w.vt = off;  off = up256(off + head_rows);
   w.kh = off;  off = up256(off + head_rows);
-  w.vht = off; off = up256(off + head_rows);
+  w.vh = off;  off = up256(off + head_rows);
   w.total = off;
   return w;
 }
@@ -492,8 +491,8 @@ lla_status hla_attention_parallel(const lla_set_desc* d, const lla_store* st, in
   p.scale = (float)(1.4426950408889634 / std::sqrt((double)d->head_dim));
   p.n_tok = a->n_tok; p.bt = st->block_table; p.pages = st->pages;
   p.q = a->q; p.k = a->k; p.v = a->v; p.A = a->A; p.Bm = a->B; p.out = a->out;
-  p.sk = ws + w.sk; p.sv = ws + w.sv; p.qr = ws + w.qr; p.kr = ws + w.kr; p.vt = ws + w.vt;
-  p.kh = ws + w.kh; p.vht = ws + w.vht;
+  p.sk = ws + w.sk; p.sv = ws + w.sv; p.qr = ws + w.qr; p.kr = ws + w.kr;
+  p.kh = ws + w.kh; p.vh = ws + w.vh;
   return hip_status(launch_parallel(p, static_cast<hipStream_t>(stream), static_cast<hipEvent_t*>(a->attn_events)));
 }
 

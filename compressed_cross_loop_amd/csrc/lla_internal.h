@@ -105,9 +105,8 @@ struct ParParams {
   void* sv;                       // [B][n_pad][G][r_v]
   void* qr;                       // [B][n_pad][H][d_h]  R_i q * scale
   void* kr;                       // [B][n_pad][H][d_h]  R_j k
-  void* vt;                       // [B][H][d_h][n_pad]  v, dimension-major
   void* kh;                       // [B][n_pad][H][d_h]  rebuilt keys
-  void* vht;                      // [B][H][d_h][n_pad]  rebuilt values, dimension-major
+  void* vh;                       // [B][n_pad][H][d_h]  rebuilt values
 };
 constexpr int kParQueryTile = 256;   // positions per attention workgroup (n_pad multiple)
 // events: optional pair recorded around the attention kernel

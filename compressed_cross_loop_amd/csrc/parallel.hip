@@ -11,13 +11,12 @@
 // without rotary embedding.  Five launches:
 //
 //   k_par_prep    q' = R_i q * log2(e)/sqrt(d_h) and k' = R_j k (token-major,
-//                 bf16), v transposed to [H][d_h][tokens]; zero past n_tok
+//                 bf16); zero past n_tok
 //   k_par_gather  the latents a position can read (j < n_tok - 1 - W) as
 //                 token-major rows; the store's dimension-major value
 //                 sub-blocks are transposed through LDS; zero rows elsewhere
 //   k_gemm_nt     K^ [tokens][H d_h] = S^K A_t^T, per latent group
-//   k_gemm_nt     V^^T [H d_h][tokens] = B_t^T S^V^T (dimension-major, the
-//                 layout the attention's value product reads)
+//   k_gemm_nt     V^ [tokens][H d_h] = S^V B_t, per latent group
 //   k_par_attn    causal flash attention over the two key sources, one
 //                 online softmax per (position, head), exp2 domain
 //
@@ -26,10 +25,10 @@
 // wave on each SIMD runs its MFMAs while the first works through its
 // softmax; a wave of 64 positions needs more than the 256 registers that
 // allows and was 1.6x slower).  Key tiles of 64 tokens are staged in
-// LDS (rebuilt and exact keys token-major, values dimension-major), the next
-// tile's global loads in flight while the current one is consumed; a source
-// is staged only when some position of the workgroup reads it.  Per 16-token
-// sub-tile and query block:
+// LDS (keys and values token-major: the exact values straight from the
+// caller's v), the next tile's global loads in flight while the current one
+// is consumed; a source is staged only when some position of the workgroup
+// reads it.  Per 16-token sub-tile and query block:
 //   scores  S^T[16 tok x 16 pos] = K[16 x d_h] . Q'^T   (v_mfma_f32_16x16x32_bf16)
 //           per element: j > i masked, j < i - W from the rebuilt keys, else
 //           from the exact keys
@@ -37,7 +36,11 @@
 //           (v_mfma_f32_16x16x32_bf16; the 32 tokens are two sub-tiles, and
 //           each lane's 8 K values are tokens 4g..4g+3 of both, which is the
 //           score MFMA's output layout, so P never leaves registers), the
-//           latent and exact parts of P against their own values
+//           latent and exact parts of P against their own values.  The V^T
+//           operand comes out of the token-major value tile through the gfx950
+//           transposing read ds_read_b64_tr_b16 (inside each 16-lane group lane
+//           i receives element i % 4 of lanes i / 4, 4 + i / 4, 8 + i / 4 and
+//           12 + i / 4): two reads give a lane dim 16 db + i of its 8 tokens.
 // Workgroups are issued longest (last positions) first.
 #include "device_common.h"
 #include "gemm_nt.h"
@@ -52,6 +55,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr float kLazy = 8.f;   // running-max slack of the attention softmax (exp2 units)
@@ -77,7 +81,6 @@ __global__ __launch_bounds__(kThreads) void k_par_prep(ParParams p, int hpw) {
   const int n = p.n_tok[b], H = p.H;
   __shared__ float cs[T][DH / 2][2];
   __shared__ double theta[DH / 2];
-  __shared__ __attribute__((aligned(16))) bf16 vtile[T][DH + 8];
   const bool rope = p.rope_base != 0.f;
   if (tid < DH / 2) theta[tid] = rope ? rope_theta(p.rope_base, DH, tid) : 0.0;
   __syncthreads();
@@ -91,10 +94,8 @@ __global__ __launch_bounds__(kThreads) void k_par_prep(ParParams p, int hpw) {
   __syncthreads();
   const bf16* q = static_cast<const bf16*>(p.q);
   const bf16* k = static_cast<const bf16*>(p.k);
-  const bf16* v = static_cast<const bf16*>(p.v);
   bf16* qr = static_cast<bf16*>(p.qr);
   bf16* kr = static_cast<bf16*>(p.kr);
-  bf16* vt = static_cast<bf16*>(p.vt);
   bf16x8 z;
 #pragma unroll
   for (int e = 0; e < 8; ++e) z[e] = static_cast<bf16>(0.f);
@@ -140,25 +141,6 @@ __global__ __launch_bounds__(kThreads) void k_par_prep(ParParams p, int hpw) {
       *reinterpret_cast<bf16x8*>(qr + orow + d0) = qo;
       *reinterpret_cast<bf16x8*>(kr + orow + d0) = ko;
     }
-  }
-  // v^T, one head at a time through LDS (T * C8 chunks: DH = 128 -> 4 per thread)
-  for (int hh = 0; hh < hpw; ++hh) {
-    const int h = h0 + hh;
-    for (int x = tid; x < T * C8; x += kThreads) {
-      const int t = x / C8, c8 = x % C8, i = i0 + t;
-      const bf16x8 val =
-          i < n ? *reinterpret_cast<const bf16x8*>(v + (((int64_t)b * p.n_max + i) * H + h) * DH + 8 * c8) : z;
-      *reinterpret_cast<bf16x8*>(&vtile[t][8 * c8]) = val;
-    }
-    __syncthreads();
-    for (int x = tid; x < DH * (T / 8); x += kThreads) {
-      const int d = x / (T / 8), t8 = 8 * (x % (T / 8));
-      bf16x8 o;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = vtile[t8 + e][d];
-      *reinterpret_cast<bf16x8*>(vt + (((int64_t)b * H + h) * DH + d) * p.n_pad + i0 + t8) = o;
-    }
-    __syncthreads();
   }
 }
 
@@ -222,13 +204,13 @@ __global__ __launch_bounds__(kThreads, 2) void k_par_attn(ParParams p) {
   constexpr int QB = kAttnQB;       // query blocks of 16 per wave
   constexpr int KS = DH / 32;       // K steps of the score MFMA
   constexpr int DB = DH / 16;       // 16-dim blocks of the output
-  constexpr int LDK = DH + 8;       // LDS row of a key tile (bf16)
-  constexpr int LDV = KT + 8;       // LDS row of a value^T tile
+  constexpr int LDK = DH + 8;       // LDS row of a key tile (bf16): 16-byte reads of 16 rows hit distinct banks
+  constexpr int LDV = DH + 16;      // LDS row of a value tile: the 4 rows x 32 bytes of a transposing read do
   constexpr int CK = KT * DH / 8 / kThreads;   // 16-B chunks per thread per tile and operand
   __shared__ __attribute__((aligned(16))) bf16 kl_s[KT * LDK];
   __shared__ __attribute__((aligned(16))) bf16 ke_s[KT * LDK];
-  __shared__ __attribute__((aligned(16))) bf16 vl_s[DH * LDV];
-  __shared__ __attribute__((aligned(16))) bf16 ve_s[DH * LDV];
+  __shared__ __attribute__((aligned(16))) bf16 vl_s[KT * LDV];
+  __shared__ __attribute__((aligned(16))) bf16 ve_s[KT * LDV];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
@@ -248,8 +230,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_par_attn(ParParams p) {
   const bf16* qr = static_cast<const bf16*>(p.qr) + (int64_t)b * p.n_pad * trow + h * DH;
   const bf16* kh = static_cast<const bf16*>(p.kh) + (int64_t)b * p.n_pad * trow + h * DH;
   const bf16* kr = static_cast<const bf16*>(p.kr) + (int64_t)b * p.n_pad * trow + h * DH;
-  const bf16* vht = static_cast<const bf16*>(p.vht) + ((int64_t)b * H + h) * DH * p.n_pad;
-  const bf16* vt = static_cast<const bf16*>(p.vt) + ((int64_t)b * H + h) * DH * p.n_pad;
+  const bf16* vh = static_cast<const bf16*>(p.vh) + (int64_t)b * p.n_pad * trow + h * DH;
+  const bf16* vx = static_cast<const bf16*>(p.v) + (int64_t)b * p.n_max * trow + h * DH;   // caller's v
 
   bf16x8 qf[QB][KS];
 #pragma unroll
@@ -282,13 +264,12 @@ __global__ __launch_bounds__(kThreads, 2) void k_par_attn(ParParams p) {
   // tiles around the window edge) is copied on the spot when the tile is
   // staged.
   u32x4 rk_[CK], rv_[CK];
-  auto chunk_k = [&](const bf16* src, int j0, int c) {
+  // chunk c of this thread: token row j0 + idx / (DH/8) (clamped to rmax),
+  // dims 8 (idx % (DH/8)) ..
+  auto chunk = [&](const bf16* src, int j0, int c, int rmax) {
     const int idx = tid + kThreads * c;
-    return reinterpret_cast<const u32x4*>(src + (int64_t)(j0 + idx / (DH / 8)) * trow + 8 * (idx % (DH / 8)));
-  };
-  auto chunk_v = [&](const bf16* src, int j0, int c) {
-    const int idx = tid + kThreads * c;
-    return reinterpret_cast<const u32x4*>(src + (int64_t)(idx / (KT / 8)) * p.n_pad + j0 + 8 * (idx % (KT / 8)));
+    return reinterpret_cast<const u32x4*>(src + (int64_t)min(j0 + idx / (DH / 8), rmax) * trow +
+                                          8 * (idx % (DH / 8)));
   };
   auto lds_k = [&](bf16* dst, int c) {
     const int idx = tid + kThreads * c;
@@ -296,17 +277,19 @@ __global__ __launch_bounds__(kThreads, 2) void k_par_attn(ParParams p) {
   };
   auto lds_v = [&](bf16* dst, int c) {
     const int idx = tid + kThreads * c;
-    return reinterpret_cast<u32x4*>(dst + (idx / (KT / 8)) * LDV + 8 * (idx % (KT / 8)));
+    return reinterpret_cast<u32x4*>(dst + (idx / (DH / 8)) * LDV + 8 * (idx % (DH / 8)));
   };
+  // rows past the sequence are never read by a valid position; the caller's
+  // v has n_max rows only, so its rows are clamped to n - 1
   auto load_tile = [&](int jt) {
     const int j0 = jt * KT;
     const bool ln = need_lat(jt);
     const bf16* ks = ln ? kh : kr;
-    const bf16* vs = ln ? vht : vt;
+    const bf16* vs = ln ? vh : vx;
 #pragma unroll
     for (int c = 0; c < CK; ++c) {
-      rk_[c] = *chunk_k(ks, j0, c);
-      rv_[c] = *chunk_v(vs, j0, c);
+      rk_[c] = *chunk(ks, j0, c, p.n_pad - 1);
+      rv_[c] = *chunk(vs, j0, c, ln ? p.n_pad - 1 : n - 1);
     }
   };
   auto store_tile = [&](int jt) {
@@ -320,8 +303,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_par_attn(ParParams p) {
     if (ln && en) {
 #pragma unroll
       for (int c = 0; c < CK; ++c) {
-        *lds_k(ke_s, c) = *chunk_k(kr, j0, c);
-        *lds_v(ve_s, c) = *chunk_v(vt, j0, c);
+        *lds_k(ke_s, c) = *chunk(kr, j0, c, p.n_pad - 1);
+        *lds_v(ve_s, c) = *chunk(vx, j0, c, n - 1);
       }
     }
   };
@@ -441,6 +424,17 @@ __global__ __launch_bounds__(kThreads, 2) void k_par_attn(ParParams p) {
       // values: the latent and exact parts of P against their own values.
       // The value MFMA's K index e of this lane is token 4 grp + e % 4 of
       // sub-tile 2u + e / 4.
+      // V^T[dims 16 db ..][tokens of this half] as the value MFMA's A operand:
+      // lane (col, grp) needs dim 16 db + col of tokens 32 u + 4 grp + e and
+      // 32 u + 16 + 4 grp + e (e < 4); each transposing read takes 4 token
+      // rows x 4 dims per lane group and hands lane i its dim i
+      auto v_operand = [&](const bf16* vt_s, int db) {
+        typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+        const bf16* base = vt_s + (32 * u + 4 * grp + (col >> 2)) * LDV + 16 * db + 4 * (col & 3);
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)base);
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + 16 * LDV));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
       auto p_part = [&](int qb, bool latent) {
         const int i = qw0 + 16 * qb + col;
         bf16x8 pp;
@@ -464,10 +458,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_par_attn(ParParams p) {
         }
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const bf16* vrow = &vl_s[(16 * db + col) * LDV + 32 * u + 4 * grp];
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 16);
-          const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+          const bf16x8 vf = v_operand(vl_s, db);
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb)
             acc[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pl[qb], acc[qb][db], 0, 0, 0);
@@ -479,10 +470,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_par_attn(ParParams p) {
         for (int qb = 0; qb < QB; ++qb) pe[qb] = p_part(qb, false);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const bf16* vrow = &ve_s[(16 * db + col) * LDV + 32 * u + 4 * grp];
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 16);
-          const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+          const bf16x8 vf = v_operand(ve_s, db);
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb)
             acc[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pe[qb], acc[qb][db], 0, 0, 0);
@@ -545,16 +533,16 @@ hipError_t launch_dh(const ParParams& p, hipStream_t s, hipEvent_t* ev) {
   gk.syb = 0; gk.syg = (int64_t)hd * p.rk;
   gk.scb = (int64_t)p.n_pad * p.H * DH; gk.scg = hd;
   if ((e = launch_gemm(gk, p.B, s)) != hipSuccess) return e;
-  // V^^T[b][g hd + c][t] = sum_d B^T[g hd + c][d] S^V[b][t][g][d]
+  // V^[b][t][g hd + c] = sum_d S^V[b][t][g][d] B^T[g hd + c][d]
   GemmParams<bf16> gv{};
-  gv.X = static_cast<const bf16*>(p.Bm);
-  gv.Y = static_cast<const bf16*>(p.sv);
-  gv.C = static_cast<bf16*>(p.vht);
-  gv.M = hd; gv.N = p.n_pad; gv.K = p.rv; gv.kseg = p.rv;
-  gv.ldx = p.rv; gv.ldy = p.G * p.rv; gv.ldc = p.n_pad; gv.G = p.G;
-  gv.sxb = 0; gv.sxg = (int64_t)hd * p.rv;
-  gv.syb = (int64_t)p.n_pad * p.G * p.rv; gv.syg = p.rv;
-  gv.scb = (int64_t)p.H * DH * p.n_pad; gv.scg = (int64_t)hd * p.n_pad;
+  gv.X = static_cast<const bf16*>(p.sv);
+  gv.Y = static_cast<const bf16*>(p.Bm);
+  gv.C = static_cast<bf16*>(p.vh);
+  gv.M = p.n_pad; gv.N = hd; gv.K = p.rv; gv.kseg = p.rv;
+  gv.ldx = p.G * p.rv; gv.ldy = p.rv; gv.ldc = p.H * DH; gv.G = p.G;
+  gv.sxb = (int64_t)p.n_pad * p.G * p.rv; gv.sxg = p.rv;
+  gv.syb = 0; gv.syg = (int64_t)hd * p.rv;
+  gv.scb = (int64_t)p.n_pad * p.H * DH; gv.scg = hd;
   if ((e = launch_gemm(gv, p.B, s)) != hipSuccess) return e;
   const int wgs = (p.n_pad / kAttnQT) * p.B * p.H;
   if (ev && (e = hipEventRecord(ev[0], s)) != hipSuccess) return e;

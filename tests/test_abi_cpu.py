@@ -336,9 +336,9 @@ def test_parallel_null_structs_and_workspace():
         B.LLA_ERR_WORKSPACE_TOO_SMALL
     w = B.lla_parallel_workspace_bytes
     assert w(d, 2, 100) == w(d, 2, 256) < w(d, 2, 257) < w(d, 4, 257)
-    # rebuilt and exact keys / values plus rotated queries: 5 head-space rows
-    # of bf16 per padded position, and the gathered latents
-    assert w(d, 1, 256) >= 256 * (5 * 16 * 128 + 1024) * 2
+    # rebuilt keys and values, rotated exact keys and queries: 4 head-space
+    # rows of bf16 per padded position, and the gathered latents
+    assert w(d, 1, 256) >= 256 * (4 * 16 * 128 + 1024) * 2
     assert w(d, 0, 256) == 0 and w(d, 1, 0) == 0
 
 
