@@ -64,7 +64,9 @@ constexpr float kLazy = 8.f;   // running-max slack of the attention softmax (ex
 // maximum replaces it and scales the empty sums by 2^(-huge) = 0)
 constexpr float kMinMax = -1e30f;
 constexpr int kAttnQB = 2;                  // query blocks of 16 positions per wave
-constexpr int kAttnQT = 4 * 16 * kAttnQB;   // positions per attention workgroup (4 waves)
+constexpr int kAttnWaves = 8;               // waves per attention workgroup
+constexpr int kAttnThreads = 64 * kAttnWaves;
+constexpr int kAttnQT = kAttnWaves * 16 * kAttnQB;   // positions per attention workgroup
 static_assert(kParQueryTile % kAttnQT == 0, "padding must cover whole query tiles");
 
 // ------------------------------------------------------------------ prep
@@ -199,18 +201,20 @@ __global__ __launch_bounds__(kThreads) void k_par_gather(ParParams p) {
 
 // ------------------------------------------------------------------ attention
 template <int DH>
-__global__ __launch_bounds__(kThreads, 2) void k_par_attn(ParParams p) {
+__global__ __launch_bounds__(kAttnThreads, 1) void k_par_attn(ParParams p) {
   constexpr int KT = 64;            // keys per tile
   constexpr int QB = kAttnQB;       // query blocks of 16 per wave
   constexpr int KS = DH / 32;       // K steps of the score MFMA
   constexpr int DB = DH / 16;       // 16-dim blocks of the output
   constexpr int LDK = DH + 8;       // LDS row of a key tile (bf16): 16-byte reads of 16 rows hit distinct banks
   constexpr int LDV = DH + 16;      // LDS row of a value tile: the 4 rows x 32 bytes of a transposing read do
-  constexpr int CK = KT * DH / 8 / kThreads;   // 16-B chunks per thread per tile and operand
-  __shared__ __attribute__((aligned(16))) bf16 kl_s[KT * LDK];
-  __shared__ __attribute__((aligned(16))) bf16 ke_s[KT * LDK];
-  __shared__ __attribute__((aligned(16))) bf16 vl_s[KT * LDV];
-  __shared__ __attribute__((aligned(16))) bf16 ve_s[KT * LDV];
+  constexpr int CK = KT * DH / 8 / kAttnThreads;   // 16-B chunks per thread per tile and operand
+  static_assert(CK >= 1, "tile too small for the workgroup");
+  // two buffers of each staged tile: tile jt + 1 is stored while tile jt is read
+  __shared__ __attribute__((aligned(16))) bf16 kl_s[2][KT * LDK];
+  __shared__ __attribute__((aligned(16))) bf16 ke_s[2][KT * LDK];
+  __shared__ __attribute__((aligned(16))) bf16 vl_s[2][KT * LDV];
+  __shared__ __attribute__((aligned(16))) bf16 ve_s[2][KT * LDV];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
@@ -258,61 +262,70 @@ __global__ __launch_bounds__(kThreads, 2) void k_par_attn(ParParams p) {
   auto need_ex = [&](int jt) { return jt * KT + KT - 1 >= q0 - W; };
   const int ntile = qe / KT + 1;
 
-  // The next tile's keys and values wait in registers while the current one
-  // is consumed: the rebuilt ones when the workgroup reads them, else the
-  // exact ones.  The exact source of a tile that needs both (the one to three
-  // tiles around the window edge) is copied on the spot when the tile is
-  // staged.
-  u32x4 rk_[CK], rv_[CK];
+  // The next tile's keys and values wait in registers (both sources of the
+  // one to three tiles around the window edge, else the one the workgroup
+  // reads) while the current tile is consumed, and are stored into the other
+  // LDS buffer right after the barrier that ends the reads of the tile before.
+  u32x4 rkl[CK], rvl[CK], rke[CK], rve[CK];
   // chunk c of this thread: token row j0 + idx / (DH/8) (clamped to rmax),
   // dims 8 (idx % (DH/8)) ..
   auto chunk = [&](const bf16* src, int j0, int c, int rmax) {
-    const int idx = tid + kThreads * c;
+    const int idx = tid + kAttnThreads * c;
     return reinterpret_cast<const u32x4*>(src + (int64_t)min(j0 + idx / (DH / 8), rmax) * trow +
                                           8 * (idx % (DH / 8)));
   };
   auto lds_k = [&](bf16* dst, int c) {
-    const int idx = tid + kThreads * c;
+    const int idx = tid + kAttnThreads * c;
     return reinterpret_cast<u32x4*>(dst + (idx / (DH / 8)) * LDK + 8 * (idx % (DH / 8)));
   };
   auto lds_v = [&](bf16* dst, int c) {
-    const int idx = tid + kThreads * c;
+    const int idx = tid + kAttnThreads * c;
     return reinterpret_cast<u32x4*>(dst + (idx / (DH / 8)) * LDV + 8 * (idx % (DH / 8)));
   };
   // rows past the sequence are never read by a valid position; the caller's
   // v has n_max rows only, so its rows are clamped to n - 1
   auto load_tile = [&](int jt) {
     const int j0 = jt * KT;
-    const bool ln = need_lat(jt);
-    const bf16* ks = ln ? kh : kr;
-    const bf16* vs = ln ? vh : vx;
-#pragma unroll
-    for (int c = 0; c < CK; ++c) {
-      rk_[c] = *chunk(ks, j0, c, p.n_pad - 1);
-      rv_[c] = *chunk(vs, j0, c, ln ? p.n_pad - 1 : n - 1);
-    }
-  };
-  auto store_tile = [&](int jt) {
-    const int j0 = jt * KT;
-    const bool ln = need_lat(jt), en = need_ex(jt);
-#pragma unroll
-    for (int c = 0; c < CK; ++c) {
-      *lds_k(ln ? kl_s : ke_s, c) = rk_[c];
-      *lds_v(ln ? vl_s : ve_s, c) = rv_[c];
-    }
-    if (ln && en) {
+    if (need_lat(jt)) {
 #pragma unroll
       for (int c = 0; c < CK; ++c) {
-        *lds_k(ke_s, c) = *chunk(kr, j0, c, p.n_pad - 1);
-        *lds_v(ve_s, c) = *chunk(vx, j0, c, n - 1);
+        rkl[c] = *chunk(kh, j0, c, p.n_pad - 1);
+        rvl[c] = *chunk(vh, j0, c, p.n_pad - 1);
+      }
+    }
+    if (need_ex(jt)) {
+#pragma unroll
+      for (int c = 0; c < CK; ++c) {
+        rke[c] = *chunk(kr, j0, c, p.n_pad - 1);
+        rve[c] = *chunk(vx, j0, c, n - 1);
+      }
+    }
+  };
+  auto store_tile = [&](int jt, int buf) {
+    if (need_lat(jt)) {
+#pragma unroll
+      for (int c = 0; c < CK; ++c) {
+        *lds_k(kl_s[buf], c) = rkl[c];
+        *lds_v(vl_s[buf], c) = rvl[c];
+      }
+    }
+    if (need_ex(jt)) {
+#pragma unroll
+      for (int c = 0; c < CK; ++c) {
+        *lds_k(ke_s[buf], c) = rke[c];
+        *lds_v(ve_s[buf], c) = rve[c];
       }
     }
   };
 
   // one tile: two halves of 32 keys (sub-tiles 2u, 2u+1), each scored,
   // folded into the online softmax and multiplied into the values in turn
-  auto compute = [&](int jt) {
+  auto compute = [&](int jt, int buf) {
     const int j0 = jt * KT;
+    const bf16* KL = kl_s[buf];
+    const bf16* KE = ke_s[buf];
+    const bf16* VL = vl_s[buf];
+    const bf16* VE = ve_s[buf];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       f32x4 sc[2][QB];
@@ -328,7 +341,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_par_attn(ParParams p) {
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) {
             const bf16x8 kf =
-                *reinterpret_cast<const bf16x8*>(&kl_s[(16 * (2 * u + hs) + col) * LDK + 32 * ks + 8 * grp]);
+                *reinterpret_cast<const bf16x8*>(&KL[(16 * (2 * u + hs) + col) * LDK + 32 * ks + 8 * grp]);
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb)
               sc[hs][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qb][ks], sc[hs][qb], 0, 0, 0);
@@ -354,7 +367,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_par_attn(ParParams p) {
           for (int qb = 0; qb < QB; ++qb) sl[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&kl_s[(16 * ts + col) * LDK + 32 * ks + 8 * grp]);
+            const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&KL[(16 * ts + col) * LDK + 32 * ks + 8 * grp]);
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb)
               sl[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qb][ks], sl[qb], 0, 0, 0);
@@ -371,7 +384,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_par_attn(ParParams p) {
           for (int qb = 0; qb < QB; ++qb) se[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&ke_s[(16 * ts + col) * LDK + 32 * ks + 8 * grp]);
+            const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&KE[(16 * ts + col) * LDK + 32 * ks + 8 * grp]);
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb)
               se[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qb][ks], se[qb], 0, 0, 0);
@@ -458,7 +471,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_par_attn(ParParams p) {
         }
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const bf16x8 vf = v_operand(vl_s, db);
+          const bf16x8 vf = v_operand(VL, db);
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb)
             acc[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pl[qb], acc[qb][db], 0, 0, 0);
@@ -470,7 +483,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_par_attn(ParParams p) {
         for (int qb = 0; qb < QB; ++qb) pe[qb] = p_part(qb, false);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const bf16x8 vf = v_operand(ve_s, db);
+          const bf16x8 vf = v_operand(VE, db);
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb)
             acc[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pe[qb], acc[qb][db], 0, 0, 0);
@@ -480,16 +493,15 @@ __global__ __launch_bounds__(kThreads, 2) void k_par_attn(ParParams p) {
   };
 
   load_tile(0);
-  store_tile(0);
-  __syncthreads();
+  store_tile(0, 0);
   if (ntile > 1) load_tile(1);
   for (int jt = 0; jt < ntile; ++jt) {
-    // a wave whose positions all precede the tile has nothing to add
-    if (wave_on && jt * KT <= qw1) compute(jt);
+    // tile jt is in LDS, and every wave is done with tile jt - 1's buffer
     __syncthreads();
-    if (jt + 1 < ntile) store_tile(jt + 1);
+    if (jt + 1 < ntile) store_tile(jt + 1, (jt + 1) & 1);
     if (jt + 2 < ntile) load_tile(jt + 2);
-    __syncthreads();
+    // a wave whose positions all precede the tile has nothing to add
+    if (wave_on && jt * KT <= qw1) compute(jt, jt & 1);
   }
 
   if (!wave_on) return;
@@ -546,7 +558,7 @@ hipError_t launch_dh(const ParParams& p, hipStream_t s, hipEvent_t* ev) {
   if ((e = launch_gemm(gv, p.B, s)) != hipSuccess) return e;
   const int wgs = (p.n_pad / kAttnQT) * p.B * p.H;
   if (ev && (e = hipEventRecord(ev[0], s)) != hipSuccess) return e;
-  hipLaunchKernelGGL((k_par_attn<DH>), dim3(wgs), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL((k_par_attn<DH>), dim3(wgs), dim3(kAttnThreads), 0, s, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   return ev ? hipEventRecord(ev[1], s) : hipSuccess;
 }
