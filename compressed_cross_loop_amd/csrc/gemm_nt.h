@@ -9,8 +9,12 @@
 // K may be made of segments of kseg elements that lie apart in memory (the
 // loops of the latent writer: one segment per loop); every 32-wide K step
 // lies in one segment.  Rows past M and N are clamped on load and skipped on
-// store.
+// store.  With a bf16 C the products are taken transposed (Y fragment as the A
+// operand), so a lane holds four consecutive columns of one row; the tile is
+// written through LDS (8-byte writes) and leaves as whole 16-byte row chunks.
 #pragma once
+#include <type_traits>
+
 #include "device_common.h"
 
 namespace lla {
@@ -41,8 +45,12 @@ __global__ __launch_bounds__(256) void k_gemm_nt(GemmParams<TC> q) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
   const int wm = wave >> 1, wn = wave & 1;
-  __shared__ __attribute__((aligned(16))) bf16 xs[2][BM][LD];
-  __shared__ __attribute__((aligned(16))) bf16 ys[2][BN][LD];
+  constexpr bool kBf16C = std::is_same<TC, bf16>::value;
+  constexpr int LC = BN + 8;        // LDS row of the output tile (bf16)
+  __shared__ __attribute__((aligned(16))) bf16 smem[2 * (BM + BN) * LD];
+  static_assert(BM * LC <= 2 * (BM + BN) * LD, "output tile must fit the operand buffers");
+  bf16 (*xs)[BM][LD] = reinterpret_cast<bf16 (*)[BM][LD]>(smem);
+  bf16 (*ys)[BN][LD] = reinterpret_cast<bf16 (*)[BN][LD]>(smem + 2 * BM * LD);
   // loader: 2 chunks of 16 B per thread per operand and K step
   int xr[2], yr[2], kc[2];
 #pragma unroll
@@ -89,9 +97,43 @@ __global__ __launch_bounds__(256) void k_gemm_nt(GemmParams<TC> q) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bb[j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = kBf16C ? __builtin_amdgcn_mfma_f32_16x16x32_bf16(bb[j], a[i], acc[i][j], 0, 0, 0)
+                           : __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bb[j], acc[i][j], 0, 0, 0);
     if (kk + 1 < nk) store(cur ^ 1);
     __syncthreads();
+  }
+  if constexpr (kBf16C) {
+    // lane holds C[row col][columns 4 grp .. + 3] of each 16 x 16 block; the
+    // loop's last barrier has released the operand buffers
+    typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bf16x4_t v;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = static_cast<bf16>(acc[i][j][r]);
+        *reinterpret_cast<bf16x4_t*>(&smem[(64 * wm + 16 * i + col) * LC + 64 * wn + 16 * j + 4 * grp]) = v;
+      }
+    __syncthreads();
+    const bool vec = (q.ldc % 8 == 0) && (reinterpret_cast<uintptr_t>(C) % 16 == 0);
+#pragma unroll
+    for (int c = 0; c < BM * BN / 8 / NT; ++c) {
+      const int idx = tid + NT * c, row = idx / (BN / 8), c8 = 8 * (idx % (BN / 8));
+      const int m = m0 + row, n = n0 + c8;
+      if (m >= q.M) continue;
+      const bf16x8_t v = *reinterpret_cast<const bf16x8_t*>(&smem[row * LC + c8]);
+      TC* dst = C + (int64_t)m * q.ldc + n;
+      if (vec && n + 7 < q.N) {
+        *reinterpret_cast<bf16x8_t*>(dst) = v;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (n + e < q.N) dst[e] = v[e];
+      }
+    }
+    return;
   }
   // lane holds C[4 grp + r][col] of each 16 x 16 block
 #pragma unroll
