@@ -4,9 +4,14 @@
 // sequence,
 //   K^[tokens x H d_h] = S^K[tokens x r] . A^T [r x H d_h]
 //   V^[tokens x H d_h] = S^V[tokens x r] . B_t [r x H d_h]
-// with an attention epilogue per head.  One workgroup = (context split,
-// sequence, 2 heads), four waves = {K^, V^} x 2 heads; each wave rebuilds a
-// 128-token x d_h tile of its head over the latent width in K steps of 32 on
+// with an attention epilogue per head.  Two forms: the LDS-staged one further
+// down (d_h = 64 or 96, the usual case) and the register-streamed one here
+// (d_h = 128, and stores whose page table does not fit the staged form's LDS
+// table).
+//
+// Register-streamed form: one workgroup = (context split, sequence, 2 heads),
+// four waves = {K^, V^} x 2 heads; each wave rebuilds a 128-token x d_h tile
+// of its head over the latent width in K steps of 32 on
 // v_mfma_f32_16x16x32_bf16.
 //
 // No operand is shared between the waves of a workgroup (each wave owns one
