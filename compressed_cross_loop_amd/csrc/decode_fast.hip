@@ -344,7 +344,71 @@ __global__ __launch_bounds__(kThreads) void k_combine_mfma(DecodeParams p) {
     wl[tid] = (b0 + tid < p.B) ? 1.f / l : 0.f;
   }
   __syncthreads();
-  {
+  // A workgroup with all 16 sequences gives each thread one sequence; with
+  // fewer (small batches, where the splits are many) the threads share the
+  // splits of one sequence at a time and add their sums through LDS.
+  const int nb = min(16, p.B - b0);
+  float* rbuf = &red[0][0][0];
+  if (nb < 16) {
+    constexpr int C4 = RV / 4;            // float4 columns
+    constexpr int SG = kThreads / C4;     // split groups
+    const int c4 = tid % C4, sg = tid / C4;
+    for (int bl = 0; bl < 16; ++bl) {
+      f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+      if (bl < nb) {
+        const int b = b0 + bl;
+#pragma unroll 4
+        for (int s = sg; s < S; s += SG) {
+          const float4 t = *reinterpret_cast<const float4*>(p.part_o + (((int64_t)b * S + s) * H + h) * p.Dp + 4 * c4);
+          sum += pm[bl][s] * f32x4{t.x, t.y, t.z, t.w};
+        }
+      }
+      reinterpret_cast<f32x4*>(rbuf)[tid] = sum;
+      __syncthreads();
+      if (tid < C4) {
+        f32x4 tot = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int g = 0; g < SG; ++g) tot += reinterpret_cast<const f32x4*>(rbuf)[g * C4 + tid];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) ob[bl][4 * tid + k] = tot[k];
+      }
+      __syncthreads();
+      if (bl + 1 >= nb) {   // the remaining rows are zero
+        for (int x = tid; x < (15 - bl) * RV; x += kThreads) ob[bl + 1 + x / RV][x % RV] = 0.f;
+        break;
+      }
+    }
+    // window sums: thread -> (8 consecutive dims, slice group of 16)
+    const int e8 = (tid % 16) * 8, wg = tid / 16;
+    for (int bl = 0; bl < nb; ++bl) {
+      const int b = b0 + bl;
+      f32x4 w0 = {0.f, 0.f, 0.f, 0.f}, w1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+      for (int sl = wg; sl < WS; sl += kThreads / 16) {
+        const float4* src = reinterpret_cast<const float4*>(p.win_o + (((int64_t)b * WS + sl) * H + h) * DH + e8);
+        const float4 a = src[0], c = src[1];
+        const float w = pm[bl][S + sl];
+        w0 += w * f32x4{a.x, a.y, a.z, a.w};
+        w1 += w * f32x4{c.x, c.y, c.z, c.w};
+      }
+      reinterpret_cast<f32x4*>(rbuf)[2 * tid] = w0;
+      reinterpret_cast<f32x4*>(rbuf)[2 * tid + 1] = w1;
+      __syncthreads();
+      if (tid < 16) {
+        f32x4 t0 = {0.f, 0.f, 0.f, 0.f}, t1 = {0.f, 0.f, 0.f, 0.f};
+        for (int g = 0; g < kThreads / 16; ++g) {
+          t0 += reinterpret_cast<const f32x4*>(rbuf)[2 * (16 * g + tid)];
+          t1 += reinterpret_cast<const f32x4*>(rbuf)[2 * (16 * g + tid) + 1];
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          wo[bl][e8 + k] = t0[k];
+          wo[bl][e8 + 4 + k] = t1[k];
+        }
+      }
+      __syncthreads();
+    }
+  } else {
     // thread -> (sequence bl, float4 columns k4, k4 + 16, ...); loads for four
     // splits are issued together
     constexpr int C4 = RV / 4;
@@ -389,7 +453,7 @@ __global__ __launch_bounds__(kThreads) void k_combine_mfma(DecodeParams p) {
       }
     }
   }
-  {
+  if (nb == 16) {
     // window sums: thread -> (sequence bl, 8 consecutive dims), all slices'
     // loads issued together (four at a time)
     const int bl = tid / 16, e8 = (tid % 16) * 8, b = b0 + bl;
