@@ -345,22 +345,35 @@ __global__ __launch_bounds__(kThreads) void k_combine(DecodeParams p) {
   float* ww = sm + S;        // [WS]  window slice weights
   float* ob = sm + S + WS;   // [Dp]  (absorbed: latent-space sum)
   const int b = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
-  float M = -INFINITY;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, p.part_ml[(((int64_t)b * S + s) * H + h) * 2]);
-  for (int s = 0; s < WS; ++s) M = fmaxf(M, p.win_ml[(((int64_t)b * WS + s) * H + h) * 2]);
-  float l = 0.f;
-  for (int s = 0; s < S; ++s) {
-    const int64_t row = ((int64_t)b * S + s) * H + h;
-    const float w = exp2_diff(p.part_ml[row * 2], M);
-    l += w * p.part_ml[row * 2 + 1];
-    if (tid == 0) ws[s] = w;
+  __shared__ float red[kThreads / 64];
+  // block-wide max / sum of one value per thread (every thread gets the result)
+  auto block_reduce = [&](float v, bool is_max) {
+    v = is_max ? wave_max(v) : wave_sum(v);
+    __syncthreads();   // red is free
+    if ((tid & 63) == 0) red[tid >> 6] = v;
+    __syncthreads();
+    float t = red[0];
+    for (int w = 1; w < kThreads / 64; ++w) t = is_max ? fmaxf(t, red[w]) : t + red[w];
+    return t;
+  };
+  // (m, l) of every split and window slice: threads take parts tid, tid + kThreads, ..
+  auto part_m = [&](int j) {
+    return j < S ? p.part_ml[(((int64_t)b * S + j) * H + h) * 2] : p.win_ml[(((int64_t)b * WS + (j - S)) * H + h) * 2];
+  };
+  auto part_l = [&](int j) {
+    return j < S ? p.part_ml[(((int64_t)b * S + j) * H + h) * 2 + 1]
+                 : p.win_ml[(((int64_t)b * WS + (j - S)) * H + h) * 2 + 1];
+  };
+  float mloc = -INFINITY;
+  for (int j = tid; j < S + WS; j += kThreads) mloc = fmaxf(mloc, part_m(j));
+  const float M = block_reduce(mloc, true);
+  float lloc = 0.f;
+  for (int j = tid; j < S + WS; j += kThreads) {
+    const float w = exp2_diff(part_m(j), M);
+    lloc += w * part_l(j);
+    if (j < S) ws[j] = w; else ww[j - S] = w;
   }
-  for (int s = 0; s < WS; ++s) {
-    const int64_t row = ((int64_t)b * WS + s) * H + h;
-    const float w = exp2_diff(p.win_ml[row * 2], M);
-    l += w * p.win_ml[row * 2 + 1];
-    if (tid == 0) ww[s] = w;
-  }
+  const float l = block_reduce(lloc, false);
   const float inv = 1.f / l;
   __syncthreads();
   T* out = static_cast<T*>(p.out) + ((int64_t)b * H + h) * dh;
