@@ -331,17 +331,22 @@ __global__ __launch_bounds__(kThreads) void k_combine_mfma(DecodeParams p) {
     }
   }
   __syncthreads();
-  if (tid < 16) {
+  {
+    // the 16 lanes of a DPP row merge one sequence's parts: parts j = c,
+    // c + 16, .. per lane, then row reductions
     const int NP = S + WS;
+    const int bl = tid / 16, c = tid % 16;
     float M = -INFINITY;
-    for (int j = 0; j < NP; ++j) M = fmaxf(M, pm[tid][j]);
+    for (int j = c; j < NP; j += 16) M = fmaxf(M, pm[bl][j]);
+    M = row_max16(M);
     float l = 0.f;
-    for (int j = 0; j < NP; ++j) {
-      const float w = exp2_diff(pm[tid][j], M);
-      pm[tid][j] = w;        // from here on: merge weight of split / slice j
-      l += w * pl[tid][j];
+    for (int j = c; j < NP; j += 16) {
+      const float w = exp2_diff(pm[bl][j], M);
+      pm[bl][j] = w;         // from here on: merge weight of split / slice j
+      l += w * pl[bl][j];
     }
-    wl[tid] = (b0 + tid < p.B) ? 1.f / l : 0.f;
+    l = row_sum16(l);
+    if (c == 0) wl[bl] = (b0 + bl < p.B) ? 1.f / l : 0.f;
   }
   __syncthreads();
   // A workgroup with all 16 sequences gives each thread one sequence; with
