@@ -363,3 +363,22 @@ def test_fused_flag_rules():
     assert B.lla_decode_scan_kernel(d, 0, F) is None
     assert B.lla_decode_scan_kernel(d, 2, F | Gn) is None
     assert B.lla_decode_scan_kernel(hla_main(r_k=64, r_v=64, rope_baked=0, rope_base=0.0), 1, F) is None
+
+
+def test_decode_workspace_holds_regrouped_decoders():
+    """Head-folded bf16 sets with d_h 64 or 96 reserve a copy of A_t and B_t^T
+    (2 H d_h r_k bf16) in the decode workspace for the LDS-staged reconstruct;
+    other shapes do not."""
+    def desc(G, H, r, dh):
+        return B.set_desc(n_heads=H, head_dim=dh, groups=G, r_k=r, r_v=r, loop_first=1, loop_last=4,
+                          page_size=64, rope_baked=0, rope_base=0.0, dtype=B.LLA_BF16)
+    w = B.lla_decode_workspace_bytes
+    wide = desc(1, 55, 5280, 96)
+    assert w(wide, 64, 4095, 0) >= 2 * 55 * 96 * 5280 * 2
+    # the copy is the only region that grows with H d_h r_k alone: at batch 1
+    # and a short context it dominates
+    small = w(wide, 1, 200, 0)
+    assert 2 * 55 * 96 * 5280 * 2 <= small < 2 * 55 * 96 * 5280 * 2 + 8 * 1024 * 1024
+    # per-head latents (groups == heads) never take the head-folded path
+    per_head = desc(16, 16, 32, 128)
+    assert w(per_head, 1, 200, 0) < 2 * 16 * 128 * 32 * 2
