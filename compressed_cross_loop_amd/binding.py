@@ -78,8 +78,7 @@ class LlaParallelArgs(ctypes.Structure):
 
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is not built; run compressed_cross_loop_amd/build.py "
-                      "(or __graft_entry__.build()) first")
+    raise ImportError(f"{LIB_PATH} is not built; run python3 compressed_cross_loop_amd/build.py first")
 lib = ctypes.CDLL(LIB_PATH)
 
 _P = ctypes.POINTER
@@ -123,7 +122,7 @@ lib.lla_abi_version.argtypes = []
 ABI_VERSION = 4   # include/lla.h LLA_ABI_VERSION this binding marshals for
 if lib.lla_abi_version() != ABI_VERSION:
     raise ImportError(f"{LIB_PATH} has ABI version {lib.lla_abi_version()}, the binding expects {ABI_VERSION}: "
-                      "rebuild it (python -c 'import __graft_entry__ as g; g.build()')")
+                      "rebuild it (python3 compressed_cross_loop_amd/build.py)")
 
 
 class LlaError(RuntimeError):
