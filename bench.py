@@ -555,7 +555,7 @@ def measured_traffic(workload_name):
 def main():
     a = parse()
     if a.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "the library runs on one GPU per process; --gpus must be 1"}))
         sys.exit(2)
     if a.calibrate_copy:
         calibrate_copy(a.calibrate_copy)
