@@ -84,6 +84,20 @@ bool use_mfma_scan(const lla_set_desc& d, int flags) {
   return scan_absorbed_mfma_supports(p);
 }
 
+// the two-pass scan of one wide latent shared by all heads, for the bf16
+// shapes the one-pass matrix-core scan does not cover (the store's page
+// count is checked at decode time)
+bool use_wide_scan(const lla_set_desc& d, int flags) {
+  if (flags & (LLA_FLAG_GENERIC | LLA_FLAG_FUSED)) return false;
+  if (d.dtype != LLA_BF16 || use_mfma_scan(d, flags)) return false;
+  DecodeParams p{};
+  p.B = 1; p.H = d.n_heads; p.G = d.groups; p.hpg = d.n_heads / d.groups;
+  p.rk = d.r_k; p.rv = d.r_v; p.dh = d.head_dim;
+  p.bf16 = 1;
+  p.fp8 = d.latent_fp8;
+  return scan_absorbed_wide_supports(p);
+}
+
 bool use_mfma_reconstruct(const lla_set_desc& d, int flags) {
   if (flags & LLA_FLAG_GENERIC) return false;
   DecodeParams p{};
@@ -125,7 +139,10 @@ bool flags_ok(int flags) {
 // the latent-scan kernel family a decode call launches for this set
 const char* scan_kernel_name(const lla_set_desc& d, int absorbed, int flags) {
   if (absorbed && (flags & LLA_FLAG_FUSED)) return "k_fused_decode";
-  if (absorbed) return use_mfma_scan(d, flags) ? "k_scan_absorbed_mfma" : "k_scan_absorbed_generic";
+  if (absorbed) {
+    if (use_mfma_scan(d, flags)) return "k_scan_absorbed_mfma";
+    return use_wide_scan(d, flags) ? "k_scan_absorbed_wide" : "k_scan_absorbed_generic";
+  }
   if (use_mfma_reconstruct(d, flags)) return "k_scan_reconstruct_mfma";
   if (use_gemm_reconstruct(d, flags)) return "k_scan_reconstruct_gemm";
   return "k_scan_reconstruct_generic";
@@ -146,6 +163,10 @@ Plan plan_for(const lla_set_desc& d, int batch, int max_pos, int window, int spl
     // the matrix-core combine merges at most kCombineMaxParts splits + window
     // slices (one window slice per split when the scan takes the window along)
     return make_plan(batch, max_pos, window, splits, wgs, target, kChunk, kCombineMaxParts / 2);
+  } else if (absorbed && use_wide_scan(d, flags)) {
+    // the value pass runs one workgroup per (256-dim slab, split, sequence)
+    wgs = scan_absorbed_wide_slabs(d.r_v);
+    return make_plan(batch, max_pos, window, splits, wgs, target, kChunk, kCombineMaxParts / 2);
   }
   int gran = kChunk;
   if (!absorbed && use_mfma_reconstruct(d, flags)) {
@@ -159,7 +180,7 @@ Plan plan_for(const lla_set_desc& d, int batch, int max_pos, int window, int spl
 }
 
 struct WsLayout {
-  size_t qlat, qhead, part_ml, part_o, win_ml, win_o, dect, tickets, fpart, total;
+  size_t qlat, qhead, part_ml, part_o, win_ml, win_o, dect, wscore, wprob, tickets, fpart, total;
   bool has_dect;
 };
 
@@ -169,7 +190,8 @@ constexpr int kWindowSlice = 32;   // exact tokens per window slice (fast window
 
 int window_slices(int window) { return (window + 1 + kWindowSlice - 1) / kWindowSlice; }
 
-WsLayout ws_layout(const lla_set_desc& d, int B, int S, int WS, int Dp, bool fused = false) {
+// lcap > 0: the two-pass wide scan's score and probability rows of lcap tokens
+WsLayout ws_layout(const lla_set_desc& d, int B, int S, int WS, int Dp, bool fused = false, int lcap = 0) {
   WsLayout w{};
   const size_t H = d.n_heads, dh = d.head_dim;
   size_t off = 0;
@@ -190,6 +212,10 @@ WsLayout ws_layout(const lla_set_desc& d, int B, int S, int WS, int Dp, bool fus
   if (w.has_dect) {
     w.dect = off;  off = up256(off + (size_t)2 * H * dh * d.r_k * 2);
   }
+  if (lcap > 0) {
+    w.wscore = off; off = up256(off + (size_t)B * H * lcap * 4);
+    w.wprob = off;  off = up256(off + (size_t)B * H * lcap * 2);
+  }
   w.total = off;
   return w;
 }
@@ -204,8 +230,9 @@ size_t decode_ws_bytes(const lla_set_desc& d, int batch, int max_pos, int window
   for (int entry = 0; entry < 2; ++entry)
     for (int flags = 0; flags < 2; ++flags) {
       const int S = plan_for(d, batch, max_pos, window, splits, entry, flags).S;
+      const int lcap = (entry && use_wide_scan(d, flags)) ? scan_absorbed_wide_lcap(max_pos) : 0;
       best = std::max(best, ws_layout(d, batch, S, std::max(S, window_slices(window)),
-                                      partial_width(d, entry)).total);
+                                      partial_width(d, entry), false, lcap).total);
     }
   if (fused_shape(d)) {
     const int S = plan_for(d, batch, max_pos, window, splits, 1, LLA_FLAG_FUSED).S;
@@ -306,7 +333,13 @@ lla_status decode(const lla_set_desc* d, const lla_store* st, int32_t batch,
   const Plan plan = plan_for(*d, batch, a->max_pos_hint, a->window, a->splits, absorbed ? 1 : 0, a->flags);
   const int Dp = partial_width(*d, absorbed ? 1 : 0);
   const int WSmax = window_slices(a->window);
-  const WsLayout w = ws_layout(*d, batch, plan.S, std::max(plan.S, WSmax), Dp, fused);
+  // the wide scan keeps a score row per (sequence, head) covering every
+  // latent token the store can hold; a store with more pages than the
+  // workspace plan covers takes the one-pass general scan
+  const int lcap = (absorbed && use_wide_scan(*d, a->flags)) ? scan_absorbed_wide_lcap(a->max_pos_hint) : 0;
+  const bool wide_scan = lcap > 0 && (int64_t)st->max_pages_per_seq * d->page_size <= lcap &&
+                         st->max_pages_per_seq <= kWideMaxPages;
+  const WsLayout w = ws_layout(*d, batch, plan.S, std::max(plan.S, WSmax), Dp, fused, wide_scan ? lcap : 0);
   char* ws = static_cast<char*>(a->workspace);
 
   DecodeParams p{};
@@ -328,6 +361,11 @@ lla_status decode(const lla_set_desc* d, const lla_store* st, int32_t batch,
   p.win_ml = reinterpret_cast<float*>(ws + w.win_ml);
   p.win_o = reinterpret_cast<float*>(ws + w.win_o);
   p.dect = w.has_dect ? ws + w.dect : nullptr;
+  if (wide_scan) {
+    p.lcap = lcap;
+    p.wscore = reinterpret_cast<float*>(ws + w.wscore);
+    p.wprob = ws + w.wprob;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipEvent_t* ev = static_cast<hipEvent_t*>(a->scan_events);
   if (fused) {
@@ -352,8 +390,10 @@ lla_status decode(const lla_set_desc* d, const lla_store* st, int32_t batch,
     p.WS = fast_window ? WSmax : 1;
   }
   p.need_qhead = (!fast_window || !absorbed) ? 1 : 0;
-  hipError_t e = (!generic && qmap_mfma_supports(p)) ? launch_qmap_mfma(p, absorbed, s)
-                                                     : launch_qmap(p, absorbed, s);
+  const bool wide_maps = wide_scan && maps_wide_supports(p);
+  hipError_t e = wide_maps                                ? launch_qmap_wide(p, s)
+                 : (!generic && qmap_mfma_supports(p)) ? launch_qmap_mfma(p, absorbed, s)
+                                                       : launch_qmap(p, absorbed, s);
   if (e == hipSuccess && !p.fuse_window) e = fast_window ? launch_window_fast(p, s) : launch_window(p, s);
   const bool gemm_reconstruct = !absorbed && !use_mfma_reconstruct(*d, a->flags) && use_gemm_reconstruct(*d, a->flags);
   if (e == hipSuccess && gemm_reconstruct) e = launch_scan_reconstruct_gemm_prep(p, s);
@@ -369,12 +409,16 @@ lla_status decode(const lla_set_desc* d, const lla_store* st, int32_t batch,
     }
     else if (mfma_scan)
       e = launch_scan_absorbed_mfma(p, s);
+    else if (wide_scan)
+      e = launch_scan_absorbed_wide(p, s);
     else
       e = launch_scan_absorbed_generic(p, s);
   }
   if (e == hipSuccess && ev) e = hipEventRecord(ev[1], s);
   if (e == hipSuccess)
-    e = (!generic && combine_mfma_supports(p)) ? launch_combine_mfma(p, s) : launch_combine(p, s);
+    e = wide_maps                                  ? launch_combine_wide(p, s)
+        : (!generic && combine_mfma_supports(p)) ? launch_combine_mfma(p, s)
+                                                 : launch_combine(p, s);
   return hip_status(e);
 }
 

@@ -49,6 +49,11 @@ struct DecodeParams {
   // head-folded reconstruct (LDS-staged form): A_t and B_t^T rows regrouped
   // per K step of 32 latent dims, [H][2][r/32][d_h][32] bf16
   void* dect;
+  // two-pass absorbed scan of one wide shared latent: scores and
+  // probabilities of every latent token, rows of lcap tokens
+  int32_t lcap;
+  float* wscore;                  // [B][H][lcap]
+  void* wprob;                    // [B][H][lcap] bf16
   // fused single-launch path
   int32_t* tickets;               // [B][H] arrival counters
   float* fpart;                   // [B][H][S][2 + rv + dh]
@@ -122,6 +127,20 @@ hipError_t launch_combine(const DecodeParams& p, hipStream_t s);
 // they do not cover, before launching anything
 bool scan_absorbed_mfma_supports(const DecodeParams& p);
 hipError_t launch_scan_absorbed_mfma(const DecodeParams& p, hipStream_t s);
+
+// two passes (scores, then values) for a wide latent shared by all heads
+// (G = 1, up to 64 heads, r_k % 32 == 0, r_v % 16 == 0); needs lcap, wscore
+// and wprob, with every latent token of every sequence below lcap
+constexpr int kWideMaxPages = 8192;       // block-table row length it stages in LDS
+bool scan_absorbed_wide_supports(const DecodeParams& p);
+int scan_absorbed_wide_slabs(int rv);      // value-pass workgroups per (split, sequence)
+int scan_absorbed_wide_lcap(int max_pos);  // score row length covering positions <= max_pos
+hipError_t launch_scan_absorbed_wide(const DecodeParams& p, hipStream_t s);
+// query map and combine of the wide absorbed read: every sequence of a head
+// in one workgroup (d_h 64, 96 or 128, bf16)
+bool maps_wide_supports(const DecodeParams& p);
+hipError_t launch_qmap_wide(const DecodeParams& p, hipStream_t s);
+hipError_t launch_combine_wide(const DecodeParams& p, hipStream_t s);
 
 bool scan_reconstruct_mfma_supports(const DecodeParams& p);
 hipError_t launch_scan_reconstruct_mfma(const DecodeParams& p, hipStream_t s);

@@ -1,0 +1,318 @@
+// Absorbed latent scan for one very wide latent shared by all heads (the
+// head-folded LLA-D read: "Looped Latent Attention" abstract, LLA-D reading
+// latents without reconstruction; "Hybrid Latent Attention" summary, "Latent
+// Reader", Eqs. 3-4 first term).  With r in the thousands and dozens of heads
+// the running output O~[heads][r_v] of one sequence no longer fits a
+// workgroup, so the scan takes two passes over the store, each a batched
+// contraction on the matrix cores:
+//
+//   scores   S[b][h][j] = q~_h . c^K_j for every latent token j
+//            (M = 16-token blocks, N = heads, K = r_k; keys straight from the
+//            store's token-major rows, q~ from the query map's output)
+//   softmax  per (sequence, head): m = max_j S, P_j = 2^(S_j - m) in bf16,
+//            and per context split l_s = sum of 2^(S_j - m) over its tokens
+//            (exp2 domain: q~ carries log2(e)/sqrt(d_h))
+//   values   O~^T[r_v x heads] = C^V^T . P^T per context split and 256-dim
+//            slab of r_v (value blocks straight from the store's
+//            dimension-major 16 x 16 blocks)
+//
+// The partials (m, l_s, O~_s) have the layout of the one-pass scans, so the
+// combine kernel merges them and applies the value map as usual.  Both long
+// passes read every latent byte once: the extra traffic is S (fp32) and P
+// (bf16), 6 bytes per (head, token) against 2 (r_k + r_v) bytes of latents.
+#include <utility>
+
+#include "device_common.h"
+#include "lla_internal.h"
+
+namespace lla {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int kTokPerWave = 64;                   // scores: 4 row blocks of 16 tokens
+constexpr int kTokPerBlock = 4 * kTokPerWave;     // scores workgroup
+constexpr int kSlab = 256;                        // values: r_v dims per workgroup
+constexpr int kWidePageTab = kWideMaxPages;       // page ids of one split, in LDS
+
+template <typename F, int... U>
+__device__ __forceinline__ void wide_static_for_impl(F&& f, std::integer_sequence<int, U...>) {
+  (f(std::integral_constant<int, U>{}), ...);
+}
+template <int N, typename F> __device__ __forceinline__ void wide_static_for(F&& f) {
+  wide_static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+__device__ __forceinline__ int latent_tokens(const DecodeParams& p, int b) {
+  return min(max(0, p.pos[b] - p.W), p.lcap);
+}
+
+// ---------------------------------------------------------------- scores
+// One wave = 64 consecutive tokens x all heads (padded to 64), K = r_k in
+// steps of 32: per step 4 key fragments (one 16-byte load per lane, token =
+// lane % 16 of the row block) and 4 q~ fragments (head = lane % 16 of the
+// head block), 16 v_mfma_f32_16x16x32_bf16.  Steps are prefetched NPF deep.
+template <int NPF>
+__global__ __launch_bounds__(kThreads, 2) void k_scan_absorbed_wide_scores(DecodeParams p) {
+  const int b = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15, grp = lane >> 4;
+  const int n_lat = latent_tokens(p, b);
+  const int tw = blockIdx.x * kTokPerBlock + wave * kTokPerWave;
+  if (tw >= n_lat) return;                       // wave-uniform; no barrier in this kernel
+  const int H = p.H, rk = p.rk, P = p.P, R = p.rk + p.rv;
+  const bf16* pages = static_cast<const bf16*>(p.pages);
+  const bf16* krow[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    // tokens past the end read the last latent token (always written); their
+    // scores land in S but nothing reads them
+    const int t = min(tw + 16 * i + col, n_lat - 1);
+    const int64_t page = p.bt[(int64_t)b * p.max_pages + t / P];
+    krow[i] = pages + tile_base(page, 0, t % P, 1, P, R) + (t % 16) * rk + 8 * grp;
+  }
+  const bf16* qrow[4];
+#pragma unroll
+  for (int hb = 0; hb < 4; ++hb)
+    qrow[hb] = static_cast<const bf16*>(p.qlat) + ((int64_t)b * H + min(16 * hb + col, H - 1)) * rk + 8 * grp;
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) acc[i][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  bf16x8 ka[NPF][4], qa[NPF][4];
+  const int nk = rk / 32;
+  auto issue = [&](auto U, int ks) {
+    constexpr int u = decltype(U)::value;
+    const int k0 = 32 * min(ks, nk - 1);       // clamped: always a valid step
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ka[u][i] = *reinterpret_cast<const bf16x8*>(krow[i] + k0);
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) qa[u][hb] = *reinterpret_cast<const bf16x8*>(qrow[hb] + k0);
+  };
+  auto step = [&](auto U) {
+    constexpr int u = decltype(U)::value;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int hb = 0; hb < 4; ++hb)
+        acc[i][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[u][i], qa[u][hb], acc[i][hb], 0, 0, 0);
+  };
+  wide_static_for<NPF>([&](auto U) { issue(U, decltype(U)::value); });
+  int ks = 0;
+  for (; ks + NPF <= nk; ks += NPF) {
+    wide_static_for<NPF>([&](auto U) {
+      step(U);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(U, ks + decltype(U)::value + NPF);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  }
+  wide_static_for<NPF>([&](auto U) {
+    if (ks + decltype(U)::value < nk) step(U);
+  });
+  // lane holds S[head 16 hb + col][tokens 16 i + 4 grp .. + 3]
+#pragma unroll
+  for (int hb = 0; hb < 4; ++hb) {
+    const int h = 16 * hb + col;
+    if (h >= H) continue;
+    float* srow = p.wscore + ((int64_t)b * H + h) * p.lcap + tw + 4 * grp;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<f32x4*>(srow + 16 * i) = acc[i][hb];
+  }
+}
+
+// ---------------------------------------------------------------- softmax
+__device__ __forceinline__ float block_max(float v, float* red) {
+  v = wave_max(v);
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();                               // red is reused
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+// one workgroup per (head, sequence)
+__global__ __launch_bounds__(kThreads) void k_scan_absorbed_wide_softmax(DecodeParams p) {
+  __shared__ float red[4];
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int n_lat = latent_tokens(p, b);
+  const int64_t row = ((int64_t)b * p.H + h) * p.lcap;
+  const f32x4* s4 = reinterpret_cast<const f32x4*>(p.wscore + row);
+  const int n4 = (n_lat + 3) / 4;
+  float m = -INFINITY;
+  for (int x = tid; x < n4; x += kThreads) {
+    const f32x4 v = s4[x];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (4 * x + r < n_lat) m = fmaxf(m, v[r]);
+  }
+  m = block_max(m, red);
+  // probabilities for every token the value pass reads: up to the 16-token
+  // tile holding the last latent token (zero past n_lat)
+  const int n16 = (n_lat + 15) / 16 * 16;
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  bf16x4* p4 = reinterpret_cast<bf16x4*>(static_cast<bf16*>(p.wprob) + row);
+  for (int x = tid; x < n16 / 4; x += kThreads) {
+    const f32x4 v = s4[x];
+    bf16x4 o;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) o[r] = static_cast<bf16>(4 * x + r < n_lat ? fast_exp2(v[r] - m) : 0.f);
+    p4[x] = o;
+  }
+  // l per context split (the splits of the value pass and the combine)
+  for (int s = 0; s < p.S; ++s) {
+    int t0 = s * p.chunk;
+    const int t1 = (s == p.S - 1) ? n_lat : min(n_lat, t0 + p.chunk);
+    if (t0 > n_lat) t0 = n_lat;
+    float l = 0.f;
+    for (int j = t0 + tid; j < t1; j += kThreads) l += fast_exp2(p.wscore[row + j] - m);
+    l = block_sum(l, red);
+    if (tid == 0) {
+      const int64_t pr = ((int64_t)b * p.S + s) * p.H + h;
+      p.part_ml[pr * 2 + 0] = m;
+      p.part_ml[pr * 2 + 1] = l;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- values
+// One workgroup = (256-dim slab of r_v, context split, sequence); wave w owns
+// dims 64 w .. 64 w + 63 of the slab (4 value blocks) for all heads and walks
+// every 16-token tile of the split: per tile 4 value fragments (8 bytes per
+// lane, 512 contiguous bytes per block) and 4 probability fragments (4
+// tokens of head lane % 16), 16 v_mfma_f32_16x16x16_bf16.  Tiles are
+// prefetched NPF deep; the split's page ids are staged in LDS.
+template <int NPF>
+__global__ __launch_bounds__(kThreads, 2) void k_scan_absorbed_wide_values(DecodeParams p) {
+  __shared__ int32_t ptab[kWidePageTab];
+  const int s = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15, grp = lane >> 4;
+  const int H = p.H, rk = p.rk, rv = p.rv, P = p.P, R = p.rk + p.rv;
+  const int n_lat = latent_tokens(p, b);
+  int t0 = s * p.chunk;
+  const int t1 = (s == p.S - 1) ? n_lat : min(n_lat, t0 + p.chunk);
+  if (t0 > n_lat) t0 = n_lat;
+  const int pfirst = t0 / P;
+  {
+    const int npg = t1 > t0 ? (t1 - 1) / P - pfirst + 1 : 0;   // <= max_pages <= kWidePageTab
+    for (int x = tid; x < npg; x += kThreads) ptab[x] = p.bt[(int64_t)b * p.max_pages + pfirst + x];
+  }
+  __syncthreads();
+  const int nblk = rv / 16;
+  const int db0 = blockIdx.x * (kSlab / 16) + 4 * wave;         // first value block of this wave
+  if (db0 >= nblk) return;                                      // wave-uniform; no barrier follows
+  int voff[4];
+#pragma unroll
+  for (int jb = 0; jb < 4; ++jb) voff[jb] = 16 * rk + min(db0 + jb, nblk - 1) * 256 + col * 16 + 4 * grp;
+  const bf16* prow[4];
+#pragma unroll
+  for (int hb = 0; hb < 4; ++hb)
+    prow[hb] = static_cast<const bf16*>(p.wprob) + ((int64_t)b * H + min(16 * hb + col, H - 1)) * p.lcap + 4 * grp;
+  const bf16* pages = static_cast<const bf16*>(p.pages);
+  const int ntiles = (t1 - t0 + 15) / 16;
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) acc[jb][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  s16x4 va[NPF][4], pa[NPF][4];
+  auto issue = [&](auto U, int ti) {
+    constexpr int u = decltype(U)::value;
+    const int j0 = t0 + 16 * min(ti, ntiles - 1);              // clamped: always a valid tile
+    const int64_t page = ptab[j0 / P - pfirst];
+    const bf16* tp = pages + tile_base(page, 0, j0 % P, 1, P, R);
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) va[u][jb] = *reinterpret_cast<const s16x4*>(tp + voff[jb]);
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) pa[u][hb] = *reinterpret_cast<const s16x4*>(prow[hb] + j0);
+  };
+  auto step = [&](auto U, int nvalid) {
+    constexpr int u = decltype(U)::value;
+    if (nvalid < 16) {
+      // tokens past the end of the split: their value slots may hold anything
+      // (even NaN), and their probabilities are zero or belong to no split
+#pragma unroll
+      for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (4 * grp + r >= nvalid) va[u][jb][r] = 0;
+    }
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+      for (int hb = 0; hb < 4; ++hb)
+        acc[jb][hb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[u][jb], pa[u][hb], acc[jb][hb], 0, 0, 0);
+  };
+  if (ntiles > 0) {
+    wide_static_for<NPF>([&](auto U) { issue(U, decltype(U)::value); });
+    const int nfull = (t1 - t0) / 16;
+    int base = 0;
+    for (; base + NPF <= nfull; base += NPF) {
+      wide_static_for<NPF>([&](auto U) {
+        step(U, 16);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(U, base + decltype(U)::value + NPF);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    }
+    wide_static_for<NPF>([&](auto U) {
+      constexpr int u = decltype(U)::value;
+      if (base + u < ntiles) step(U, min(16, t1 - (t0 + 16 * (base + u))));
+    });
+  }
+  // lane holds O~[dims 16 db + 4 grp .. + 3][head 16 hb + col]
+#pragma unroll
+  for (int hb = 0; hb < 4; ++hb) {
+    const int h = 16 * hb + col;
+    if (h >= H) continue;
+    float* orow = p.part_o + (((int64_t)b * p.S + s) * H + h) * p.Dp;
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb)
+      if (db0 + jb < nblk) *reinterpret_cast<f32x4*>(orow + 16 * (db0 + jb) + 4 * grp) = acc[jb][hb];
+  }
+}
+
+}  // namespace
+
+bool scan_absorbed_wide_supports(const DecodeParams& p) {
+  return p.bf16 && !p.fp8 && p.G == 1 && p.H <= 64 && p.rk % 32 == 0 && p.rv % 16 == 0 && p.rk >= 32 &&
+         p.rv >= 16 && p.max_pages <= kWidePageTab;
+}
+
+int scan_absorbed_wide_slabs(int rv) { return (rv + kSlab - 1) / kSlab; }
+
+int scan_absorbed_wide_lcap(int max_pos) {
+  return (max(max_pos, 0) + 1 + kTokPerBlock - 1) / kTokPerBlock * kTokPerBlock;
+}
+
+hipError_t launch_scan_absorbed_wide(const DecodeParams& p, hipStream_t s) {
+  if (!scan_absorbed_wide_supports(p) || p.lcap % kTokPerBlock || !p.wscore || !p.wprob)
+    return hipErrorNotSupported;
+  hipLaunchKernelGGL(k_scan_absorbed_wide_scores<3>, dim3(p.lcap / kTokPerBlock, p.B), dim3(kThreads), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_scan_absorbed_wide_softmax, dim3(p.H, p.B), dim3(kThreads), 0, s, p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_scan_absorbed_wide_values<4>, dim3(scan_absorbed_wide_slabs(p.rv), p.S, p.B),
+                     dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace lla

@@ -249,7 +249,14 @@ lla_status hla_decode_windowed(const lla_set_desc* desc, const lla_store* store,
  * in lla_decode_args; 0 = automatic).  For bf16 sets with one latent shared
  * by all heads (groups == 1, r_k == r_v, d_h 64 or 96) it includes a copy of
  * A_t and B_t^T regrouped per 32 latent dims (2 H d_h r_k bf16), which the
- * reconstruct read refills on every call. */
+ * reconstruct read refills on every call.  For bf16 sets whose absorbed read
+ * takes the two-pass scan ("k_scan_absorbed_wide" below) it also includes an
+ * fp32 score and a bf16 probability per (sequence, head, latent token), for
+ * tokens up to max_pos + 1 rounded up to 256: 6 batch H L bytes.  A decode
+ * call uses that scan only when the store cannot hold more tokens than these
+ * rows cover (max_pages_per_seq * page_size <= L with L from max_pos_hint);
+ * otherwise it runs the one-pass general scan, so a larger pos[] stays
+ * correct. */
 size_t lla_decode_workspace_bytes(const lla_set_desc* desc, int32_t batch,
                                   int32_t max_pos, int32_t window, int32_t splits);
 
@@ -261,7 +268,10 @@ int32_t lla_decode_plan_splits(const lla_set_desc* desc, int32_t batch, int32_t 
 /* Name of the latent-scan kernel family a decode call with this set, entry
  * (0 = lla_decode_reconstruct, 1 = lla_decode_absorbed, 2 =
  * hla_decode_windowed) and flags launches: "k_scan_absorbed_mfma",
- * "k_scan_absorbed_generic", "k_scan_reconstruct_mfma",
+ * "k_scan_absorbed_wide" (bf16, one latent shared by up to 64 heads, r_k a
+ * multiple of 32, shapes the one-pass matrix-core scan does not take: a
+ * score pass, a softmax pass and a value pass, kernels named with this
+ * prefix), "k_scan_absorbed_generic", "k_scan_reconstruct_mfma",
  * "k_scan_reconstruct_gemm" or "k_scan_reconstruct_generic" (static
  * strings, for profilers).  NULL on invalid arguments.  Host only. */
 const char* lla_decode_scan_kernel(const lla_set_desc* desc, int32_t entry, int32_t flags);

@@ -192,7 +192,14 @@ def test_scan_kernel_query():
     assert B.lla_decode_scan_kernel(tiny, 0) == "k_scan_reconstruct_generic"
     wide = desc(B.LLA_BF16, 1, 55, 5280, 96)
     assert B.lla_decode_scan_kernel(wide, 0) == "k_scan_reconstruct_gemm"
-    assert B.lla_decode_scan_kernel(wide, 1) == "k_scan_absorbed_generic"
+    assert B.lla_decode_scan_kernel(wide, 1) == "k_scan_absorbed_wide"
+    assert B.lla_decode_scan_kernel(wide, 1, B.LLA_FLAG_GENERIC) == "k_scan_absorbed_generic"
+    # the two-pass form takes shared latents only, up to 64 heads, r_k % 32 == 0
+    assert B.lla_decode_scan_kernel(desc(B.LLA_BF16, 1, 65, 256, 64), 1) == "k_scan_absorbed_generic"
+    assert B.lla_decode_scan_kernel(desc(B.LLA_BF16, 1, 64, 256, 64), 1) == "k_scan_absorbed_wide"
+    assert B.lla_decode_scan_kernel(desc(B.LLA_BF16, 1, 4, 48, 64), 1) == "k_scan_absorbed_generic"
+    assert B.lla_decode_scan_kernel(desc(B.LLA_BF16, 2, 4, 1024, 64), 1) == "k_scan_absorbed_generic"
+    assert B.lla_decode_scan_kernel(desc(B.LLA_F32, 1, 55, 5280, 96), 1) == "k_scan_absorbed_generic"
     assert B.lla_decode_scan_kernel(hla, 3) is None
     assert B.lla_decode_scan_kernel(hla, 0, 2) is None
     bad = desc(B.LLA_BF16, 1, 16, 512, 128)
@@ -382,3 +389,19 @@ def test_decode_workspace_holds_regrouped_decoders():
     # per-head latents (groups == heads) never take the head-folded path
     per_head = desc(16, 16, 32, 128)
     assert w(per_head, 1, 200, 0) < 2 * 16 * 128 * 32 * 2
+
+
+def test_decode_workspace_holds_wide_scan_rows():
+    """The two-pass absorbed scan of a wide shared latent keeps an fp32 score and
+    a bf16 probability per (sequence, head, token) up to max_pos + 1 rounded up
+    to 256 tokens; the one-pass shapes keep none."""
+    def desc(G, H, r, dh):
+        return B.set_desc(n_heads=H, head_dim=dh, groups=G, r_k=r, r_v=r, loop_first=1, loop_last=4,
+                          page_size=64, rope_baked=0, rope_base=0.0, dtype=B.LLA_BF16)
+    w = B.lla_decode_workspace_bytes
+    wide = desc(1, 55, 5280, 96)
+    rows = 64 * 55 * 4096 * 6
+    assert w(wide, 64, 4095, 0) >= rows + 2 * 55 * 96 * 5280 * 2
+    assert w(wide, 64, 4096, 0) - w(wide, 64, 4095, 0) >= 64 * 55 * 256 * 6
+    hla = desc(1, 16, 512, 128)   # one-pass matrix-core scan: nothing per token
+    assert w(hla, 128, 4095, 128) < 128 * 16 * 4096 * 6

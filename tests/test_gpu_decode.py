@@ -9,7 +9,8 @@ import pytest
 import torch
 
 from synth import gen
-from tests.gpu_cases import TOL, oracle_decode, poison_unread, run_decode
+from compressed_cross_loop_amd import binding as B
+from tests.gpu_cases import TOL, desc_of, oracle_decode, poison_unread, run_decode
 from tests.util import max_rel_err
 
 pytestmark = pytest.mark.gpu
@@ -170,6 +171,34 @@ def test_reconstruct_shared_latent_bf16():
                           loop_last=8, latent_std=1.0, exact_std=1.0, paired=False,
                           map_scale=np.sqrt(192 / 96))
     check(poison_unread(c), "absorbed", "absorbed")
+
+
+@pytest.mark.parametrize("H, d_h, r_k, r_v", [(6, 96, 192, 192), (20, 64, 256, 256), (3, 64, 96, 32),
+                                              (55, 96, 1056, 1056), (64, 64, 64, 64), (2, 96, 5280, 5280)])
+@pytest.mark.parametrize("splits", [0, 1, 3])
+def test_absorbed_wide_shared_latent(H, d_h, r_k, r_v, splits):
+    """LLA-D over one latent shared by all heads, shapes the one-pass matrix-core
+    scan does not take (r not a power of two, more than 16 heads, r_k != r_v,
+    r in the thousands): the two-pass scan.  Ragged 16-token tiles, empty and
+    forced splits, 256-dim value slabs with a ragged last slab."""
+    c = gen.decode_inputs(700 + H + r_k + r_v + splits, batch=3, heads=H, head_dim=d_h, groups=1, r_k=r_k,
+                          r_v=r_v, positions=(300, 129, 7), window=4, dtype="bf16", loop=3, loop_first=1,
+                          loop_last=8, latent_std=1.0, exact_std=1.0, paired=False,
+                          map_scale=float(np.sqrt(r_k / d_h)))
+    assert B.lla_decode_scan_kernel(desc_of(c), 1) == "k_scan_absorbed_wide"
+    check(poison_unread(c), "absorbed", "absorbed", splits=splits)
+
+
+@pytest.mark.parametrize("hint", [100, 2000])
+def test_absorbed_wide_hint(hint):
+    """max_pos_hint below the positions (the store holds more tokens than the
+    planned score rows: the one-pass general scan runs) and far above them
+    (longer score rows than needed): both stay exact."""
+    c = gen.decode_inputs(760 + hint, batch=3, heads=6, head_dim=96, groups=1, r_k=192, r_v=192,
+                          positions=(300, 129, 7), window=4, dtype="bf16", loop=3, loop_first=1,
+                          loop_last=8, latent_std=1.0, exact_std=1.0, paired=False,
+                          map_scale=float(np.sqrt(2.0)))
+    check(poison_unread(c), "absorbed", "absorbed", max_pos_hint=hint)
 
 
 @pytest.mark.parametrize("H, d_h, r", [(5, 96, 192), (4, 128, 256), (3, 64, 96), (2, 96, 5280)])

@@ -121,6 +121,20 @@ def test_lla_per_head_absorbed_full_size():
     assert err < 2e-2
 
 
+def test_lla2d_absorbed_full_batch():
+    """LLA-D on workload 5 at its full batch of 64 (the two-pass wide scan in
+    the bench's launch configuration), sampled sequences against the oracle."""
+    w = configs.get(5)
+    c = build(w, 0, 17, seed=53)
+    assert B.lla_decode_scan_kernel(c["desc"], 1) == "k_scan_absorbed_wide"
+    out, ring0 = run(c, "absorbed")
+    seqs = [0, 37, 63]
+    err = max_rel_err(out[seqs], oracle_for(c, seqs, "absorbed", ring0))
+    print(f"max_rel_err={err:.3e}")
+    assert err < 2e-2
+    assert np.all(np.isfinite(out))
+
+
 @pytest.mark.parametrize("entry, form", [("reconstruct", "textbook"), ("absorbed", "absorbed")])
 def test_lla2d_full_width(entry, form):
     """LLA-2D: 55 heads x 96 from one 5280-wide K and V latent, 4k context."""
