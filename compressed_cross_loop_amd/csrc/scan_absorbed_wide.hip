@@ -31,6 +31,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kTokPerWave = 64;                   // scores: 4 row blocks of 16 tokens
@@ -51,19 +52,29 @@ __device__ __forceinline__ int latent_tokens(const DecodeParams& p, int b) {
 }
 
 // ---------------------------------------------------------------- scores
-// One wave = 64 consecutive tokens x all heads (padded to 64), K = r_k in
-// steps of 32: per step 4 key fragments (one 16-byte load per lane, token =
-// lane % 16 of the row block) and 4 q~ fragments (head = lane % 16 of the
-// head block), 16 v_mfma_f32_16x16x32_bf16.  Steps are prefetched NPF deep.
-template <int NPF>
+// One workgroup = 256 consecutive tokens x all heads (padded to 64); wave w
+// owns tokens 64 w .. 64 w + 63 (4 row blocks of 16), K = r_k in steps of 32
+// (v_mfma_f32_16x16x32_bf16, 16 per step).  Key fragments come straight from
+// the store (one 16-byte load per lane, token = lane % 16 of the row block),
+// kKeyAhead steps ahead.  q~ is shared by the four waves: it is staged in LDS
+// in chunks of 128 latent dims (64 head rows of 256 contiguous bytes, loaded
+// once per workgroup, double-buffered) and its fragments are read from there;
+// the 16-byte pieces of a row are XOR-swizzled by the row so that the 16
+// heads of a fragment read spread over the banks.
+constexpr int kKeyAhead = 4;      // = steps per q~ chunk (the key ring index is the step in the chunk)
+constexpr int kQChunk = 128;      // latent dims per staged q~ chunk
+
 __global__ __launch_bounds__(kThreads, 2) void k_scan_absorbed_wide_scores(DecodeParams p) {
+  __shared__ __attribute__((aligned(16))) bf16 qs[2][64 * kQChunk];
   const int b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
   const int n_lat = latent_tokens(p, b);
-  const int tw = blockIdx.x * kTokPerBlock + wave * kTokPerWave;
-  if (tw >= n_lat) return;                       // wave-uniform; no barrier in this kernel
+  const int tb = blockIdx.x * kTokPerBlock;
+  if (tb >= n_lat) return;                       // workgroup-uniform
+  // waves past the last latent token compute on clamped tokens and store nothing
+  const int tw = tb + wave * kTokPerWave;
   const int H = p.H, rk = p.rk, P = p.P, R = p.rk + p.rv;
   const bf16* pages = static_cast<const bf16*>(p.pages);
   const bf16* krow[4];
@@ -75,47 +86,75 @@ __global__ __launch_bounds__(kThreads, 2) void k_scan_absorbed_wide_scores(Decod
     const int64_t page = p.bt[(int64_t)b * p.max_pages + t / P];
     krow[i] = pages + tile_base(page, 0, t % P, 1, P, R) + (t % 16) * rk + 8 * grp;
   }
-  const bf16* qrow[4];
+  // q~ staging: piece x = tid + 256 k of a chunk is head row x / 16, dims
+  // 8 (x % 16) .. + 7, kept at slot (x % 16) ^ (row % 16) of its LDS row
+  const bf16* qsrc[4];
+  int qoff[4], qdst[4];
 #pragma unroll
-  for (int hb = 0; hb < 4; ++hb)
-    qrow[hb] = static_cast<const bf16*>(p.qlat) + ((int64_t)b * H + min(16 * hb + col, H - 1)) * rk + 8 * grp;
+  for (int k = 0; k < 4; ++k) {
+    const int x = tid + kThreads * k, row = x >> 4, c = x & 15;
+    qsrc[k] = static_cast<const bf16*>(p.qlat) + ((int64_t)b * H + min(row, H - 1)) * rk;
+    qoff[k] = 8 * c;
+    qdst[k] = row * kQChunk + 8 * (c ^ (row & 15));
+  }
+  u32x4 qreg[4];
+  auto q_load = [&](int kc0) {   // pieces past r_k feed no step (r_k % 32 == 0): clamp their address
+#pragma unroll
+    for (int k = 0; k < 4; ++k) qreg[k] = *reinterpret_cast<const u32x4*>(qsrc[k] + min(kc0 + qoff[k], rk - 8));
+  };
+  auto q_store = [&](int buf) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) *reinterpret_cast<u32x4*>(&qs[buf][qdst[k]]) = qreg[k];
+  };
 
   f32x4 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int hb = 0; hb < 4; ++hb) acc[i][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  bf16x8 ka[NPF][4], qa[NPF][4];
+  bf16x8 ka[kKeyAhead][4];
   const int nk = rk / 32;
   auto issue = [&](auto U, int ks) {
     constexpr int u = decltype(U)::value;
     const int k0 = 32 * min(ks, nk - 1);       // clamped: always a valid step
 #pragma unroll
     for (int i = 0; i < 4; ++i) ka[u][i] = *reinterpret_cast<const bf16x8*>(krow[i] + k0);
-#pragma unroll
-    for (int hb = 0; hb < 4; ++hb) qa[u][hb] = *reinterpret_cast<const bf16x8*>(qrow[hb] + k0);
   };
-  auto step = [&](auto U) {
+  // step U of the chunk in LDS buffer buf: B fragment of head block hb =
+  // q~[16 hb + col][32 U + 8 grp ..], piece 4 U + grp of the row
+  auto step = [&](auto U, int buf) {
     constexpr int u = decltype(U)::value;
+    bf16x8 qa[4];
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb)
+      qa[hb] = *reinterpret_cast<const bf16x8*>(&qs[buf][(16 * hb + col) * kQChunk + 8 * ((4 * u + grp) ^ col)]);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int hb = 0; hb < 4; ++hb)
-        acc[i][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[u][i], qa[u][hb], acc[i][hb], 0, 0, 0);
+        acc[i][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[u][i], qa[hb], acc[i][hb], 0, 0, 0);
   };
-  wide_static_for<NPF>([&](auto U) { issue(U, decltype(U)::value); });
-  int ks = 0;
-  for (; ks + NPF <= nk; ks += NPF) {
-    wide_static_for<NPF>([&](auto U) {
-      step(U);
+  const int nch = (nk + kKeyAhead - 1) / kKeyAhead;   // q~ chunks; every one but the last is whole
+  wide_static_for<kKeyAhead>([&](auto U) { issue(U, decltype(U)::value); });
+  q_load(0);
+  q_store(0);
+  __syncthreads();
+  int c = 0;
+  for (; c + 1 < nch; ++c) {
+    q_load(kQChunk * (c + 1));
+    wide_static_for<kKeyAhead>([&](auto U) {
+      step(U, c & 1);
       __builtin_amdgcn_sched_barrier(0);
-      issue(U, ks + decltype(U)::value + NPF);
+      issue(U, kKeyAhead * (c + 1) + decltype(U)::value);
       __builtin_amdgcn_sched_barrier(0);
     });
+    q_store((c + 1) & 1);
+    __syncthreads();
   }
-  wide_static_for<NPF>([&](auto U) {
-    if (ks + decltype(U)::value < nk) step(U);
+  wide_static_for<kKeyAhead>([&](auto U) {
+    if (kKeyAhead * c + decltype(U)::value < nk) step(U, c & 1);
   });
+  if (tw >= n_lat) return;
   // lane holds S[head 16 hb + col][tokens 16 i + 4 grp .. + 3]
 #pragma unroll
   for (int hb = 0; hb < 4; ++hb) {
@@ -193,12 +232,20 @@ __global__ __launch_bounds__(kThreads) void k_scan_absorbed_wide_softmax(DecodeP
 // One workgroup = (256-dim slab of r_v, context split, sequence); wave w owns
 // dims 64 w .. 64 w + 63 of the slab (4 value blocks) for all heads and walks
 // every 16-token tile of the split: per tile 4 value fragments (8 bytes per
-// lane, 512 contiguous bytes per block) and 4 probability fragments (4
-// tokens of head lane % 16), 16 v_mfma_f32_16x16x16_bf16.  Tiles are
-// prefetched NPF deep; the split's page ids are staged in LDS.
-template <int NPF>
+// lane, 512 contiguous bytes per block) straight from the store, prefetched
+// kTileAhead tiles ahead, and 16 v_mfma_f32_16x16x16_bf16.  The
+// probabilities are shared by the four waves: they are staged in LDS in
+// chunks of 128 tokens (64 head rows of 256 contiguous bytes, loaded once per
+// workgroup, double-buffered; rows padded by 16 bytes so that the 16 heads
+// of a fragment read fall in different banks).  The split's page ids are
+// staged in LDS too.
+constexpr int kTileAhead = 4;                 // value tiles in flight per wave
+constexpr int kPChunk = 128;                  // tokens per staged probability chunk (8 tiles)
+constexpr int kPRow = kPChunk + 8;            // its LDS row (bf16)
+
 __global__ __launch_bounds__(kThreads, 2) void k_scan_absorbed_wide_values(DecodeParams p) {
   __shared__ int32_t ptab[kWidePageTab];
+  __shared__ __attribute__((aligned(16))) bf16 ps[2][64 * kPRow];
   const int s = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -215,15 +262,31 @@ __global__ __launch_bounds__(kThreads, 2) void k_scan_absorbed_wide_values(Decod
   }
   __syncthreads();
   const int nblk = rv / 16;
-  const int db0 = blockIdx.x * (kSlab / 16) + 4 * wave;         // first value block of this wave
-  if (db0 >= nblk) return;                                      // wave-uniform; no barrier follows
+  // waves past the last value block load clamped blocks and store nothing
+  const int db0 = blockIdx.x * (kSlab / 16) + 4 * wave;
   int voff[4];
 #pragma unroll
   for (int jb = 0; jb < 4; ++jb) voff[jb] = 16 * rk + min(db0 + jb, nblk - 1) * 256 + col * 16 + 4 * grp;
-  const bf16* prow[4];
+  // probability staging: piece x = tid + 256 k of a chunk is head row x / 16,
+  // tokens 8 (x % 16) .. + 7
+  const bf16* psrc[4];
+  int poff[4], pdst[4];
 #pragma unroll
-  for (int hb = 0; hb < 4; ++hb)
-    prow[hb] = static_cast<const bf16*>(p.wprob) + ((int64_t)b * H + min(16 * hb + col, H - 1)) * p.lcap + 4 * grp;
+  for (int k = 0; k < 4; ++k) {
+    const int x = tid + kThreads * k, row = x >> 4, c = x & 15;
+    psrc[k] = static_cast<const bf16*>(p.wprob) + ((int64_t)b * H + min(row, H - 1)) * p.lcap;
+    poff[k] = 8 * c;
+    pdst[k] = row * kPRow + 8 * c;
+  }
+  u32x4 preg[4];
+  auto p_load = [&](int j0c) {   // tokens past the row feed no tile: clamp their address
+#pragma unroll
+    for (int k = 0; k < 4; ++k) preg[k] = *reinterpret_cast<const u32x4*>(psrc[k] + min(j0c + poff[k], p.lcap - 8));
+  };
+  auto p_store = [&](int buf) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) *reinterpret_cast<u32x4*>(&ps[buf][pdst[k]]) = preg[k];
+  };
   const bf16* pages = static_cast<const bf16*>(p.pages);
   const int ntiles = (t1 - t0 + 15) / 16;
 
@@ -232,7 +295,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_scan_absorbed_wide_values(Decod
   for (int jb = 0; jb < 4; ++jb)
 #pragma unroll
     for (int hb = 0; hb < 4; ++hb) acc[jb][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  s16x4 va[NPF][4], pa[NPF][4];
+  s16x4 va[kTileAhead][4];
   auto issue = [&](auto U, int ti) {
     constexpr int u = decltype(U)::value;
     const int j0 = t0 + 16 * min(ti, ntiles - 1);              // clamped: always a valid tile
@@ -240,10 +303,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_scan_absorbed_wide_values(Decod
     const bf16* tp = pages + tile_base(page, 0, j0 % P, 1, P, R);
 #pragma unroll
     for (int jb = 0; jb < 4; ++jb) va[u][jb] = *reinterpret_cast<const s16x4*>(tp + voff[jb]);
-#pragma unroll
-    for (int hb = 0; hb < 4; ++hb) pa[u][hb] = *reinterpret_cast<const s16x4*>(prow[hb] + j0);
   };
-  auto step = [&](auto U, int nvalid) {
+  // tile tl (0..7) of the chunk in LDS buffer buf; B fragment of head block hb
+  // = probabilities of head 16 hb + col, tokens 16 tl + 4 grp .. + 3
+  auto step = [&](auto U, int buf, int tl, int nvalid) {
     constexpr int u = decltype(U)::value;
     if (nvalid < 16) {
       // tokens past the end of the split: their value slots may hold anything
@@ -254,28 +317,49 @@ __global__ __launch_bounds__(kThreads, 2) void k_scan_absorbed_wide_values(Decod
         for (int r = 0; r < 4; ++r)
           if (4 * grp + r >= nvalid) va[u][jb][r] = 0;
     }
+    s16x4 pa[4];
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb)
+      pa[hb] = *reinterpret_cast<const s16x4*>(&ps[buf][(16 * hb + col) * kPRow + 16 * tl + 4 * grp]);
 #pragma unroll
     for (int jb = 0; jb < 4; ++jb)
 #pragma unroll
       for (int hb = 0; hb < 4; ++hb)
-        acc[jb][hb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[u][jb], pa[u][hb], acc[jb][hb], 0, 0, 0);
+        acc[jb][hb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[u][jb], pa[hb], acc[jb][hb], 0, 0, 0);
   };
-  if (ntiles > 0) {
-    wide_static_for<NPF>([&](auto U) { issue(U, decltype(U)::value); });
-    const int nfull = (t1 - t0) / 16;
-    int base = 0;
-    for (; base + NPF <= nfull; base += NPF) {
-      wide_static_for<NPF>([&](auto U) {
-        step(U, 16);
-        __builtin_amdgcn_sched_barrier(0);
-        issue(U, base + decltype(U)::value + NPF);
-        __builtin_amdgcn_sched_barrier(0);
+  constexpr int kTilesPerChunk = kPChunk / 16;
+  if (ntiles > 0) {                              // workgroup-uniform
+    const int nch = (ntiles + kTilesPerChunk - 1) / kTilesPerChunk;   // every chunk but the last is whole
+    wide_static_for<kTileAhead>([&](auto U) { issue(U, decltype(U)::value); });
+    p_load(t0);
+    p_store(0);
+    __syncthreads();
+    int c = 0;
+    for (; c + 1 < nch; ++c) {
+      p_load(t0 + kPChunk * (c + 1));
+#pragma unroll
+      for (int half = 0; half < kTilesPerChunk / kTileAhead; ++half) {
+        wide_static_for<kTileAhead>([&](auto U) {
+          const int tl = kTileAhead * half + decltype(U)::value;
+          step(U, c & 1, tl, 16);
+          __builtin_amdgcn_sched_barrier(0);
+          issue(U, kTilesPerChunk * c + tl + kTileAhead);
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      }
+      p_store((c + 1) & 1);
+      __syncthreads();
+    }
+#pragma unroll
+    for (int half = 0; half < kTilesPerChunk / kTileAhead; ++half) {
+      wide_static_for<kTileAhead>([&](auto U) {
+        const int tl = kTileAhead * half + decltype(U)::value, ti = kTilesPerChunk * c + tl;
+        if (ti < ntiles) {
+          step(U, c & 1, tl, min(16, t1 - (t0 + 16 * ti)));
+          if (half + 1 < kTilesPerChunk / kTileAhead) issue(U, ti + kTileAhead);
+        }
       });
     }
-    wide_static_for<NPF>([&](auto U) {
-      constexpr int u = decltype(U)::value;
-      if (base + u < ntiles) step(U, min(16, t1 - (t0 + 16 * (base + u))));
-    });
   }
   // lane holds O~[dims 16 db + 4 grp .. + 3][head 16 hb + col]
 #pragma unroll
@@ -305,12 +389,12 @@ int scan_absorbed_wide_lcap(int max_pos) {
 hipError_t launch_scan_absorbed_wide(const DecodeParams& p, hipStream_t s) {
   if (!scan_absorbed_wide_supports(p) || p.lcap % kTokPerBlock || !p.wscore || !p.wprob)
     return hipErrorNotSupported;
-  hipLaunchKernelGGL(k_scan_absorbed_wide_scores<3>, dim3(p.lcap / kTokPerBlock, p.B), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL(k_scan_absorbed_wide_scores, dim3(p.lcap / kTokPerBlock, p.B), dim3(kThreads), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_scan_absorbed_wide_softmax, dim3(p.H, p.B), dim3(kThreads), 0, s, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(k_scan_absorbed_wide_values<4>, dim3(scan_absorbed_wide_slabs(p.rv), p.S, p.B),
+  hipLaunchKernelGGL(k_scan_absorbed_wide_values, dim3(scan_absorbed_wide_slabs(p.rv), p.S, p.B),
                      dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
