@@ -5,13 +5,11 @@
 // about a MiB, so these kernels take every sequence of a head together and
 // read each map once per workgroup, instead of once per (sequence, head).
 //
-//   k_qmap_wide     workgroup = (slab of latent dims, head); a thread holds
-//                   its latent dim's column of A_t in registers (bf16 pairs)
-//                   and takes every sequence in turn: q is the same for the
-//                   whole workgroup, staged in LDS and read as broadcasts,
-//                   and each pair of products is one v_dot2_f32_bf16.  RoPE on the
-//                   latent (frequency-paired decoders) rotates dim pairs
-//                   (f, f + d_h/2) inside each d_h block, exchanged in LDS.
+//   k_qmap_wide     workgroup = (slab of latent dims, head): the slab of A_t
+//                   staged in LDS once, then every sequence on the matrix
+//                   cores.  RoPE on the latent (frequency-paired decoders)
+//                   rotates dim pairs (f, f + d_h/2) inside each d_h block,
+//                   exchanged in LDS.
 //   k_combine_wide  workgroup = (head, 16 sequences): merge weights of the
 //                   context splits and window slices per sequence, then
 //                   O~ B_t on the matrix cores (M = 16 sequences, N = d_h,
@@ -24,7 +22,6 @@
 namespace lla {
 namespace {
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -32,32 +29,60 @@ constexpr int kThreads = 256;
 constexpr int kSeqChunk = 16;   // sequences per LDS round of the query map / per combine workgroup
 
 // ---------------------------------------------------------------- query map
+// q~^T[n][b] = sum_e A_t[e][n] q[b][e] for a slab of latent dims n and every
+// sequence b, on the matrix cores (v_mfma_f32_16x16x16_bf16, M = 16 latent
+// dims, N = 16 sequences, K = d_h).  The slab of A_t (d_h rows of 512
+// contiguous bytes) is staged in LDS once; A_t is stored with the latent axis
+// contiguous, so its fragments (four consecutive e of one n per lane) come
+// back through the transposing LDS read ds_read_b64_tr_b16.  q fragments are
+// 8-byte loads.  Rows are padded by 32 bytes so that the 16 rows one
+// transposing read touches fall in different banks.
 template <int DH>
 __global__ __launch_bounds__(kThreads) void k_qmap_wide(DecodeParams p) {
-  constexpr int HALF = DH / 2;
-  __shared__ float ub[kSeqChunk][kThreads];
+  constexpr int HALF = DH / 2, KS = DH / 16, LDA = kThreads + 16;
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  __shared__ __attribute__((aligned(16))) bf16 at[DH * LDA];
+  __shared__ float ub[kSeqChunk][kThreads + 4];
   __shared__ float cs[kSeqChunk][HALF][2];
-  __shared__ __attribute__((aligned(16))) unsigned qs[kSeqChunk][HALF];   // q of the chunk, bf16 pairs
-  const int h = blockIdx.y, tid = threadIdx.x;
+  const int h = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, grp = lane >> 4;
   const int H = p.H, rk = p.rk, B = p.B;
   const bool rope = p.rope_base != 0.f;
   const int slab = rope ? (kThreads / DH) * DH : kThreads;   // whole d_h blocks when rotating
   const int n0 = blockIdx.x * slab;
-  const int n = n0 + tid;
-  const bool act = tid < slab && n < rk;
-  const unsigned short* Ah = static_cast<const unsigned short*>(p.A) + (int64_t)h * DH * rk;
-  const int nc = min(n, rk - 1);
-  unsigned acol[HALF];   // A_t[e][n], A_t[e+1][n] packed
+  {
+    // A_t[e][n0 .. n0 + slab): 16-byte pieces, columns past r_k clamped (never
+    // stored); every load of a thread is issued before the first LDS write
+    constexpr int NP = DH * (kThreads / 8) / kThreads;   // pieces per thread at the widest slab
+    const bf16* Ah = static_cast<const bf16*>(p.A) + (int64_t)h * DH * rk;
+    const int pr = slab / 8, npc = DH * pr;
+    u32x4 r[NP];
 #pragma unroll
-  for (int e2 = 0; e2 < HALF; ++e2)
-    acol[e2] = (unsigned)Ah[(int64_t)(2 * e2) * rk + nc] | ((unsigned)Ah[(int64_t)(2 * e2 + 1) * rk + nc] << 16);
+    for (int k = 0; k < NP; ++k) {
+      const int x = min(tid + kThreads * k, npc - 1), e = x / pr, c = x % pr;
+      r[k] = *reinterpret_cast<const u32x4*>(Ah + (int64_t)e * rk + min(n0 + 8 * c, rk - 8));
+    }
+#pragma unroll
+    for (int k = 0; k < NP; ++k) {
+      const int x = tid + kThreads * k, e = x / pr, c = x % pr;
+      if (x < npc) *reinterpret_cast<u32x4*>(&at[e * LDA + 8 * c]) = r[k];
+    }
+  }
+  __syncthreads();
   bf16* ql = static_cast<bf16*>(p.qlat);
+  const int nblk = slab / 16;
+  // B operand: q[b0 + col][16 ks + 4 grp .. + 3], one chunk ahead
+  s16x4 qn[KS];
+  auto q_load = [&](int b0) {
+    const bf16* q = static_cast<const bf16*>(p.q) + ((int64_t)min(b0 + col, B - 1) * H + h) * DH + 4 * grp;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qn[ks] = *reinterpret_cast<const s16x4*>(q + 16 * ks);
+  };
+  q_load(0);
   for (int b0 = 0; b0 < B; b0 += kSeqChunk) {
     const int nb = min(kSeqChunk, B - b0);
-    for (int x = tid; x < nb * HALF; x += kThreads) {
-      const int bb = x / HALF, e2 = x % HALF;
-      qs[bb][e2] = reinterpret_cast<const unsigned*>(static_cast<const bf16*>(p.q) + ((int64_t)(b0 + bb) * H + h) * DH)[e2];
-    }
     if (rope) {
       for (int x = tid; x < nb * HALF; x += kThreads) {
         const int bb = x / HALF, f = x % HALF;
@@ -67,33 +92,46 @@ __global__ __launch_bounds__(kThreads) void k_qmap_wide(DecodeParams p) {
         cs[bb][f][1] = s;
       }
     }
-    __syncthreads();
-    for (int bb = 0; bb < nb; ++bb) {
-      const unsigned* qp = qs[bb];   // same address in every lane: LDS broadcast
-      float acc = 0.f;
+    s16x4 qf[KS];
 #pragma unroll
-      for (int e2 = 0; e2 < HALF; ++e2)
-        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, acol[e2]),
-                                              __builtin_bit_cast(bf16x2, qp[e2]), acc, false);
-      if (rope)
-        ub[bb][tid] = acc;
-      else if (act)
-        ql[((int64_t)(b0 + bb) * H + h) * rk + n] = static_cast<bf16>(acc * p.scale);
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = qn[ks];
+    if (b0 + kSeqChunk < B) q_load(b0 + kSeqChunk);
+    for (int blk = wave; blk < nblk; blk += 4) {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        // lane l of the 16-lane group points at A_t[16 ks + 4 grp + l / 4][16 blk + 4 (l % 4)]
+        const bf16* a = &at[(16 * ks + 4 * grp + (col >> 2)) * LDA + 16 * blk + 4 * (col & 3)];
+        const s16x4 af = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)a);
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(af, qf[ks], acc, 0, 0, 0);
+      }
+      // lane holds q~[sequence b0 + col][n0 + 16 blk + 4 grp + r]
+      const int nl = 16 * blk + 4 * grp;
+      if (rope) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ub[col][nl + r] = acc[r];
+      } else if (col < nb && n0 + nl < rk) {
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        bf16x4 v;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = static_cast<bf16>(acc[r] * p.scale);
+        *reinterpret_cast<bf16x4*>(ql + ((int64_t)(b0 + col) * H + h) * rk + n0 + nl) = v;
+      }
     }
     if (rope) {
       __syncthreads();
-      if (act) {
-        const int f = n % DH;   // n0 is a multiple of d_h, so the partner is in this slab
+      for (int x = tid; x < nb * slab; x += kThreads) {
+        const int bb = x / slab, t = x % slab, n = n0 + t;
+        if (n >= rk) continue;
+        const int f = t % DH;   // n0 is a multiple of d_h, so the partner is in this slab
         const int fp = f < HALF ? f : f - HALF;
-        for (int bb = 0; bb < nb; ++bb) {
-          const float c = cs[bb][fp][0], s = cs[bb][fp][1];
-          const float u = ub[bb][tid];
-          const float v = f < HALF ? u * c - ub[bb][tid + HALF] * s : ub[bb][tid - HALF] * s + u * c;
-          ql[((int64_t)(b0 + bb) * H + h) * rk + n] = static_cast<bf16>(v * p.scale);
-        }
+        const float c = cs[bb][fp][0], sn = cs[bb][fp][1];
+        const float u = ub[bb][t];
+        const float v = f < HALF ? u * c - ub[bb][t + HALF] * sn : ub[bb][t - HALF] * sn + u * c;
+        ql[((int64_t)(b0 + bb) * H + h) * rk + n] = static_cast<bf16>(v * p.scale);
       }
+      __syncthreads();   // ub and cs are refilled next round
     }
-    __syncthreads();   // qs, ub and cs are refilled next round
   }
   // q rotated to its position (head space), for the exact-window kernel
   if (p.need_qhead && blockIdx.x == 0) {

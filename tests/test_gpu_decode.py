@@ -189,6 +189,19 @@ def test_absorbed_wide_shared_latent(H, d_h, r_k, r_v, splits):
     check(poison_unread(c), "absorbed", "absorbed", splits=splits)
 
 
+@pytest.mark.parametrize("H, d_h, r", [(20, 64, 256), (6, 96, 192), (18, 128, 1024)])
+@pytest.mark.parametrize("entry", ["absorbed", "hla"])
+def test_absorbed_wide_rope(H, d_h, r, entry):
+    """The two-pass scan with RoPE (frequency-paired decoders, rotation baked
+    into the stored key latents, q~ rotated per d_h block by the query map) and
+    an exact window, through both absorbed entry points."""
+    c = gen.decode_inputs(780 + H + r, batch=3, heads=H, head_dim=d_h, groups=1, r_k=r, r_v=r,
+                          positions=(300, 129, 17), window=16, dtype="bf16", rope_base=10000.0, rope_baked=1,
+                          loop=2, loop_first=2, loop_last=4, latent_std=1.0, exact_std=1.0)
+    assert B.lla_decode_scan_kernel(desc_of(c), 1) == "k_scan_absorbed_wide"
+    check(poison_unread(c), entry, "absorbed")
+
+
 @pytest.mark.parametrize("hint", [100, 2000])
 def test_absorbed_wide_hint(hint):
     """max_pos_hint below the positions (the store holds more tokens than the
