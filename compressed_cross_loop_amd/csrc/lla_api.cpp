@@ -213,7 +213,7 @@ WsLayout ws_layout(const lla_set_desc& d, int B, int S, int WS, int Dp, bool fus
     w.dect = off;  off = up256(off + (size_t)2 * H * dh * d.r_k * 2);
   }
   if (lcap > 0) {
-    w.wscore = off; off = up256(off + (size_t)B * H * lcap * 4);
+    w.wscore = off; off = up256(off + (size_t)scan_absorbed_wide_ksplit(B, lcap, d.r_k) * B * H * lcap * 4);
     w.wprob = off;  off = up256(off + (size_t)B * H * lcap * 2);
   }
   w.total = off;
@@ -363,6 +363,7 @@ lla_status decode(const lla_set_desc* d, const lla_store* st, int32_t batch,
   p.dect = w.has_dect ? ws + w.dect : nullptr;
   if (wide_scan) {
     p.lcap = lcap;
+    p.wsplit = scan_absorbed_wide_ksplit(batch, lcap, d->r_k);
     p.wscore = reinterpret_cast<float*>(ws + w.wscore);
     p.wprob = ws + w.wprob;
   }

@@ -52,7 +52,8 @@ struct DecodeParams {
   // two-pass absorbed scan of one wide shared latent: scores and
   // probabilities of every latent token, rows of lcap tokens
   int32_t lcap;
-  float* wscore;                  // [B][H][lcap]
+  int32_t wsplit;                 // parts of r_k the score pass is split into
+  float* wscore;                  // [wsplit][B][H][lcap]
   void* wprob;                    // [B][H][lcap] bf16
   // fused single-launch path
   int32_t* tickets;               // [B][H] arrival counters
@@ -135,6 +136,7 @@ constexpr int kWideMaxPages = 8192;       // block-table row length it stages in
 bool scan_absorbed_wide_supports(const DecodeParams& p);
 int scan_absorbed_wide_slabs(int rv);      // value-pass workgroups per (split, sequence)
 int scan_absorbed_wide_lcap(int max_pos);  // score row length covering positions <= max_pos
+int scan_absorbed_wide_ksplit(int B, int lcap, int rk);   // score-pass parts of r_k (small batches)
 hipError_t launch_scan_absorbed_wide(const DecodeParams& p, hipStream_t s);
 // query map and combine of the wide absorbed read: every sequence of a head
 // in one workgroup (d_h 64, 96 or 128, bf16)

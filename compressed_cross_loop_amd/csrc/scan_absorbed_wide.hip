@@ -20,6 +20,7 @@
 // combine kernel merges them and applies the value map as usual.  Both long
 // passes read every latent byte once: the extra traffic is S (fp32) and P
 // (bf16), 6 bytes per (head, token) against 2 (r_k + r_v) bytes of latents.
+#include <algorithm>
 #include <utility>
 
 #include "device_common.h"
@@ -38,6 +39,7 @@ constexpr int kTokPerWave = 64;                   // scores: 4 row blocks of 16 
 constexpr int kTokPerBlock = 4 * kTokPerWave;     // scores workgroup
 constexpr int kSlab = 256;                        // values: r_v dims per workgroup
 constexpr int kWidePageTab = kWideMaxPages;       // page ids of one split, in LDS
+constexpr int kScoreWorkgroups = 1024;            // score-pass workgroups aimed at (two rounds of two per CU)
 
 template <typename F, int... U>
 __device__ __forceinline__ void wide_static_for_impl(F&& f, std::integer_sequence<int, U...>) {
@@ -134,33 +136,37 @@ __global__ __launch_bounds__(kThreads, 2) void k_scan_absorbed_wide_scores(Decod
       for (int hb = 0; hb < 4; ++hb)
         acc[i][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[u][i], qa[hb], acc[i][hb], 0, 0, 0);
   };
-  const int nch = (nk + kKeyAhead - 1) / kKeyAhead;   // q~ chunks; every one but the last is whole
-  wide_static_for<kKeyAhead>([&](auto U) { issue(U, decltype(U)::value); });
-  q_load(0);
+  // q~ chunks of this workgroup's part of r_k (blockIdx.z of wsplit parts,
+  // none empty); every chunk but the last of r_k is whole
+  const int nch = (nk + kKeyAhead - 1) / kKeyAhead;
+  const int cpz = (nch + p.wsplit - 1) / p.wsplit;
+  const int c0 = blockIdx.z * cpz, c1 = min(nch, c0 + cpz);
+  wide_static_for<kKeyAhead>([&](auto U) { issue(U, kKeyAhead * c0 + decltype(U)::value); });
+  q_load(kQChunk * c0);
   q_store(0);
   __syncthreads();
-  int c = 0;
-  for (; c + 1 < nch; ++c) {
+  int c = c0;
+  for (; c + 1 < c1; ++c) {
     q_load(kQChunk * (c + 1));
     wide_static_for<kKeyAhead>([&](auto U) {
-      step(U, c & 1);
+      step(U, (c - c0) & 1);
       __builtin_amdgcn_sched_barrier(0);
       issue(U, kKeyAhead * (c + 1) + decltype(U)::value);
       __builtin_amdgcn_sched_barrier(0);
     });
-    q_store((c + 1) & 1);
+    q_store((c + 1 - c0) & 1);
     __syncthreads();
   }
   wide_static_for<kKeyAhead>([&](auto U) {
-    if (kKeyAhead * c + decltype(U)::value < nk) step(U, c & 1);
+    if (kKeyAhead * c + decltype(U)::value < nk) step(U, (c - c0) & 1);
   });
   if (tw >= n_lat) return;
-  // lane holds S[head 16 hb + col][tokens 16 i + 4 grp .. + 3]
+  // lane holds S[head 16 hb + col][tokens 16 i + 4 grp .. + 3] (this part's sum)
 #pragma unroll
   for (int hb = 0; hb < 4; ++hb) {
     const int h = 16 * hb + col;
     if (h >= H) continue;
-    float* srow = p.wscore + ((int64_t)b * H + h) * p.lcap + tw + 4 * grp;
+    float* srow = p.wscore + (((int64_t)blockIdx.z * p.B + b) * H + h) * p.lcap + tw + 4 * grp;
 #pragma unroll
     for (int i = 0; i < 4; ++i) *reinterpret_cast<f32x4*>(srow + 16 * i) = acc[i][hb];
   }
@@ -190,19 +196,24 @@ __global__ __launch_bounds__(kThreads) void k_scan_absorbed_wide_softmax(DecodeP
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int n_lat = latent_tokens(p, b);
   const int64_t row = ((int64_t)b * p.H + h) * p.lcap;
-  const f32x4* s4 = reinterpret_cast<const f32x4*>(p.wscore + row);
-  const int n4 = (n_lat + 3) / 4;
+  f32x4* s4 = reinterpret_cast<f32x4*>(p.wscore + row);
+  // probabilities for every token the value pass reads: up to the 16-token
+  // tile holding the last latent token (zero past n_lat)
+  const int n16 = (n_lat + 15) / 16 * 16;
+  // scores split along r_k are summed (fixed order) into the first part's row
+  const int64_t part = (int64_t)p.B * p.H * p.lcap / 4;
   float m = -INFINITY;
-  for (int x = tid; x < n4; x += kThreads) {
-    const f32x4 v = s4[x];
+  for (int x = tid; x < n16 / 4; x += kThreads) {
+    f32x4 v = s4[x];
+    if (p.wsplit > 1) {
+      for (int z = 1; z < p.wsplit; ++z) v += s4[z * part + x];
+      s4[x] = v;
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       if (4 * x + r < n_lat) m = fmaxf(m, v[r]);
   }
-  m = block_max(m, red);
-  // probabilities for every token the value pass reads: up to the 16-token
-  // tile holding the last latent token (zero past n_lat)
-  const int n16 = (n_lat + 15) / 16 * 16;
+  m = block_max(m, red);   // its barriers also publish the summed rows
   typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
   bf16x4* p4 = reinterpret_cast<bf16x4*>(static_cast<bf16*>(p.wprob) + row);
   for (int x = tid; x < n16 / 4; x += kThreads) {
@@ -386,10 +397,22 @@ int scan_absorbed_wide_lcap(int max_pos) {
   return (max(max_pos, 0) + 1 + kTokPerBlock - 1) / kTokPerBlock * kTokPerBlock;
 }
 
+// Parts of r_k the score pass is split into: enough workgroups to fill the
+// chip at small batches (a part is a whole number of 128-dim q~ chunks, and
+// no part is empty).
+int scan_absorbed_wide_ksplit(int B, int lcap, int rk) {
+  const int64_t base = (int64_t)(lcap / kTokPerBlock) * B;
+  const int nch = (rk / 32 + kKeyAhead - 1) / kKeyAhead;
+  int kz = (int)std::min<int64_t>(nch, std::max<int64_t>(1, (kScoreWorkgroups + base - 1) / base));
+  const int cpz = (nch + kz - 1) / kz;
+  return (nch + cpz - 1) / cpz;
+}
+
 hipError_t launch_scan_absorbed_wide(const DecodeParams& p, hipStream_t s) {
-  if (!scan_absorbed_wide_supports(p) || p.lcap % kTokPerBlock || !p.wscore || !p.wprob)
+  if (!scan_absorbed_wide_supports(p) || p.lcap % kTokPerBlock || !p.wscore || !p.wprob ||
+      p.wsplit != scan_absorbed_wide_ksplit(p.B, p.lcap, p.rk))
     return hipErrorNotSupported;
-  hipLaunchKernelGGL(k_scan_absorbed_wide_scores, dim3(p.lcap / kTokPerBlock, p.B), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL(k_scan_absorbed_wide_scores, dim3(p.lcap / kTokPerBlock, p.B, p.wsplit), dim3(kThreads), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_scan_absorbed_wide_softmax, dim3(p.H, p.B), dim3(kThreads), 0, s, p);

@@ -202,6 +202,16 @@ def test_absorbed_wide_rope(H, d_h, r, entry):
     check(poison_unread(c), entry, "absorbed")
 
 
+@pytest.mark.parametrize("positions", [(300,), (4000,), (5,)])
+def test_absorbed_wide_single_sequence(positions):
+    """Batch 1: the score pass splits r_k into parts (here 9 of 128 dims, the
+    last one 32) summed by the softmax pass; a context shorter than one tile."""
+    c = gen.decode_inputs(800 + positions[0], batch=1, heads=55, head_dim=96, groups=1, r_k=1056, r_v=1056,
+                          positions=positions, window=0, dtype="bf16", loop=3, loop_first=1, loop_last=8,
+                          latent_std=1.0, exact_std=1.0, paired=False, map_scale=float(np.sqrt(1056 / 96)))
+    check(poison_unread(c), "absorbed", "absorbed")
+
+
 @pytest.mark.parametrize("hint", [100, 2000])
 def test_absorbed_wide_hint(hint):
     """max_pos_hint below the positions (the store holds more tokens than the
