@@ -250,9 +250,11 @@ lla_status hla_decode_windowed(const lla_set_desc* desc, const lla_store* store,
  * by all heads (groups == 1, r_k == r_v, d_h 64 or 96) it includes a copy of
  * A_t and B_t^T regrouped per 32 latent dims (2 H d_h r_k bf16), which the
  * reconstruct read refills on every call.  For bf16 sets whose absorbed read
- * takes the two-pass scan ("k_scan_absorbed_wide" below) it also includes an
- * fp32 score and a bf16 probability per (sequence, head, latent token), for
- * tokens up to max_pos + 1 rounded up to 256: 6 batch H L bytes.  A decode
+ * takes the two-pass scan ("k_scan_absorbed_wide" below) it also includes a
+ * bf16 probability per (sequence, head, latent token) and an fp32 score per
+ * (part of r_k, sequence, head, latent token), for tokens up to max_pos + 1
+ * rounded up to 256: (4 parts + 2) batch H L bytes, with one part at large
+ * batches and up to r_k / 128 at small ones.  A decode
  * call uses that scan only when the store cannot hold more tokens than these
  * rows cover (max_pages_per_seq * page_size <= L with L from max_pos_hint);
  * otherwise it runs the one-pass general scan, so a larger pos[] stays
