@@ -156,7 +156,11 @@ __global__ __launch_bounds__(kThreads) void k_combine_wide(DecodeParams p) {
   extern __shared__ float wsm[];                           // [16][S + WS] merge weights
   __shared__ float red[4][kSeqChunk][DH + 4];
   __shared__ float inv[kSeqChunk];
-  const int h = blockIdx.x, b0 = blockIdx.y * kSeqChunk;
+  // workgroups are dealt to the 8 XCDs round-robin: every 16-sequence chunk of
+  // head h gets an id = h (mod 8), so B_h is fetched into one L2 only
+  const int span = 8 * ((p.B + kSeqChunk - 1) / kSeqChunk);
+  const int h = (blockIdx.x / span) * 8 + (blockIdx.x % 8), b0 = (blockIdx.x % span) / 8 * kSeqChunk;
+  if (h >= p.H) return;   // the id padding of the last 8 heads; before any barrier
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int H = p.H, S = p.S, WS = p.WS, NP = S + WS, B = p.B, rv = p.rv;
   // ---- merge weights: wave w takes sequences 4w .. 4w+3 of the chunk
@@ -275,7 +279,7 @@ hipError_t launch_qmap_wide(const DecodeParams& p, hipStream_t s) {
 
 hipError_t launch_combine_wide(const DecodeParams& p, hipStream_t s) {
   if (!maps_wide_supports(p) || p.mode != kAbsorbed) return hipErrorNotSupported;
-  const dim3 grid(p.H, (p.B + kSeqChunk - 1) / kSeqChunk);
+  const dim3 grid((p.H + 7) / 8 * 8 * ((p.B + kSeqChunk - 1) / kSeqChunk));
   const size_t lds = (size_t)kSeqChunk * (p.S + p.WS) * sizeof(float);
   switch (p.dh) {
     case 64: hipLaunchKernelGGL(k_combine_wide<64>, grid, dim3(kThreads), lds, s, p); break;
