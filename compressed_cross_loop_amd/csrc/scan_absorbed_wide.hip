@@ -18,8 +18,9 @@
 //
 // The partials (m, l_s, O~_s) have the layout of the one-pass scans, so the
 // combine kernel merges them and applies the value map as usual.  Both long
-// passes read every latent byte once: the extra traffic is S (fp32) and P
-// (bf16), 6 bytes per (head, token) against 2 (r_k + r_v) bytes of latents.
+// passes read every latent byte once: the extra traffic is S (fp32, one row
+// per part of r_k when small batches split the score pass) and P (bf16), 6
+// bytes per (head, token) at one part, against 2 (r_k + r_v) bytes of latents.
 #include <algorithm>
 #include <utility>
 
@@ -54,8 +55,9 @@ __device__ __forceinline__ int latent_tokens(const DecodeParams& p, int b) {
 }
 
 // ---------------------------------------------------------------- scores
-// One workgroup = 256 consecutive tokens x all heads (padded to 64); wave w
-// owns tokens 64 w .. 64 w + 63 (4 row blocks of 16), K = r_k in steps of 32
+// One workgroup = 256 consecutive tokens x all heads (padded to 64) x one part
+// of r_k (the whole of it unless the batch is small); wave w owns tokens
+// 64 w .. 64 w + 63 (4 row blocks of 16), K in steps of 32
 // (v_mfma_f32_16x16x32_bf16, 16 per step).  Key fragments come straight from
 // the store (one 16-byte load per lane, token = lane % 16 of the row block),
 // kKeyAhead steps ahead.  q~ is shared by the four waves: it is staged in LDS
