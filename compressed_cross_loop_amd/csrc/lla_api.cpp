@@ -160,6 +160,10 @@ Plan plan_for(const lla_set_desc& d, int batch, int max_pos, int window, int spl
     return make_plan(batch, max_pos, window, kMaxFusedSplits, wgs, target, kChunk);
   } else if (absorbed && use_mfma_scan(d, flags)) {
     wgs = d.groups;
+    // three quarters of a workgroup per CU (measured at 16k context and batch
+    // 32: 6 splits 202 us, 8 splits 207 us, 12 splits 242 us per call; batch
+    // 128 at 4k keeps its 2 splits)
+    target = 3 * kTargetWorkgroups / 4;
     // the matrix-core combine merges at most kCombineMaxParts splits + window
     // slices (one window slice per split when the scan takes the window along)
     return make_plan(batch, max_pos, window, splits, wgs, target, kChunk, kCombineMaxParts / 2);
