@@ -534,20 +534,21 @@ def stream_copy_gbs(nbytes=1 << 31, reps=10):
     return 2 * nbytes / dt / 1e9
 
 
-def scan_source_sha():
+def source_sha(name):
     import hashlib
-    path = os.path.join(ROOT, "compressed_cross_loop_amd", "csrc", "scan_absorbed_mfma.hip")
+    path = os.path.join(ROOT, "compressed_cross_loop_amd", "csrc", name)
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def measured_traffic(workload_name):
-    """HBM bytes per launch of the scan kernel from the profiler counters kept
-    in profiles/traffic.json, or None when they were taken on other source."""
+def measured_traffic(workload_name, kernel):
+    """HBM bytes per launch of the scan kernel family from the profiler counters
+    kept in profiles/traffic.json, or None when there are none for this
+    workload or they were taken on other source."""
     tp = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(tp):
         return None
-    rec = json.load(open(tp))
-    if rec.get("scan_source_sha") != scan_source_sha():
+    rec = json.load(open(tp)).get("kernels", {}).get(kernel)
+    if not rec or rec.get("source_sha") != source_sha(rec["source"]):
         return None
     return rec.get("workloads", {}).get(workload_name)
 
@@ -658,7 +659,7 @@ def main():
         roof = {"bound": "hbm", "achieved": scan_bytes / (scan_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = measured_traffic(w.name) if kname == "k_scan_absorbed_mfma" else None
+    roof["traffic"] = measured_traffic(w.name, kname) if st.entry_name in ("hla", "absorbed") else None
     roof.update({"kernel": f"{kname} (" + ("every (layer, loop) call" if st.entry_name == "full" else
                                          f"set serving loops {loops_served[0]}..{loops_served[1]}") + ")",
                  "avg_launch_ms": scan_ms, "bytes_per_launch": scan_bytes, "flop_per_launch": scan_flop})
