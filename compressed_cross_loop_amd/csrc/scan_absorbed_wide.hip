@@ -40,6 +40,7 @@ constexpr int kTokPerWave = 64;                   // scores: 4 row blocks of 16 
 constexpr int kTokPerBlock = 4 * kTokPerWave;     // scores workgroup
 constexpr int kSlab = 256;                        // values: r_v dims per workgroup
 constexpr int kWidePageTab = kWideMaxPages;       // page ids of one split, in LDS
+constexpr int kSoftmaxLdsTokens = 16384;          // longest score row the softmax pass keeps in LDS (64 KiB)
 constexpr int kScoreWorkgroups = 1024;            // score-pass workgroups aimed at (two rounds of two per CU)
 
 template <typename F, int... U>
@@ -192,46 +193,50 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return (red[0] + red[1]) + (red[2] + red[3]);
 }
 
-// one workgroup per (head, sequence)
+// one workgroup per (head, sequence).  With LDS the summed score row is kept
+// there after the first read (rows up to kSoftmaxLdsTokens tokens), so the
+// probability and split-sum passes do not read it from memory again.
+template <bool LDS>
 __global__ __launch_bounds__(kThreads) void k_scan_absorbed_wide_softmax(DecodeParams p) {
   __shared__ float red[4];
+  extern __shared__ __attribute__((aligned(16))) float srow[];   // [lcap] when LDS
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int n_lat = latent_tokens(p, b);
   const int64_t row = ((int64_t)b * p.H + h) * p.lcap;
   f32x4* s4 = reinterpret_cast<f32x4*>(p.wscore + row);
+  f32x4* r4 = LDS ? reinterpret_cast<f32x4*>(srow) : s4;   // where the summed row is read back
   // probabilities for every token the value pass reads: up to the 16-token
   // tile holding the last latent token (zero past n_lat)
   const int n16 = (n_lat + 15) / 16 * 16;
-  // scores split along r_k are summed (fixed order) into the first part's row
+  // scores split along r_k are summed (fixed order)
   const int64_t part = (int64_t)p.B * p.H * p.lcap / 4;
   float m = -INFINITY;
   for (int x = tid; x < n16 / 4; x += kThreads) {
     f32x4 v = s4[x];
-    if (p.wsplit > 1) {
-      for (int z = 1; z < p.wsplit; ++z) v += s4[z * part + x];
-      s4[x] = v;
-    }
+    for (int z = 1; z < p.wsplit; ++z) v += s4[z * part + x];
+    if (LDS || p.wsplit > 1) r4[x] = v;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       if (4 * x + r < n_lat) m = fmaxf(m, v[r]);
   }
-  m = block_max(m, red);   // its barriers also publish the summed rows
+  m = block_max(m, red);   // its barriers also publish the summed row
   typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
   bf16x4* p4 = reinterpret_cast<bf16x4*>(static_cast<bf16*>(p.wprob) + row);
   for (int x = tid; x < n16 / 4; x += kThreads) {
-    const f32x4 v = s4[x];
+    const f32x4 v = r4[x];
     bf16x4 o;
 #pragma unroll
     for (int r = 0; r < 4; ++r) o[r] = static_cast<bf16>(4 * x + r < n_lat ? fast_exp2(v[r] - m) : 0.f);
     p4[x] = o;
   }
   // l per context split (the splits of the value pass and the combine)
+  const float* rs = reinterpret_cast<const float*>(r4);
   for (int s = 0; s < p.S; ++s) {
     int t0 = s * p.chunk;
     const int t1 = (s == p.S - 1) ? n_lat : min(n_lat, t0 + p.chunk);
     if (t0 > n_lat) t0 = n_lat;
     float l = 0.f;
-    for (int j = t0 + tid; j < t1; j += kThreads) l += fast_exp2(p.wscore[row + j] - m);
+    for (int j = t0 + tid; j < t1; j += kThreads) l += fast_exp2(rs[j] - m);
     l = block_sum(l, red);
     if (tid == 0) {
       const int64_t pr = ((int64_t)b * p.S + s) * p.H + h;
@@ -417,7 +422,10 @@ hipError_t launch_scan_absorbed_wide(const DecodeParams& p, hipStream_t s) {
   hipLaunchKernelGGL(k_scan_absorbed_wide_scores, dim3(p.lcap / kTokPerBlock, p.B, p.wsplit), dim3(kThreads), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_scan_absorbed_wide_softmax, dim3(p.H, p.B), dim3(kThreads), 0, s, p);
+  if (p.lcap <= kSoftmaxLdsTokens)
+    hipLaunchKernelGGL(k_scan_absorbed_wide_softmax<true>, dim3(p.H, p.B), dim3(kThreads), (size_t)p.lcap * 4, s, p);
+  else
+    hipLaunchKernelGGL(k_scan_absorbed_wide_softmax<false>, dim3(p.H, p.B), dim3(kThreads), 0, s, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(k_scan_absorbed_wide_values, dim3(scan_absorbed_wide_slabs(p.rv), p.S, p.B),
                      dim3(kThreads), 0, s, p);

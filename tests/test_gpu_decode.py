@@ -212,11 +212,12 @@ def test_absorbed_wide_single_sequence(positions):
     check(poison_unread(c), "absorbed", "absorbed")
 
 
-@pytest.mark.parametrize("hint", [100, 2000])
+@pytest.mark.parametrize("hint", [100, 2000, 20000])
 def test_absorbed_wide_hint(hint):
     """max_pos_hint below the positions (the store holds more tokens than the
     planned score rows: the one-pass general scan runs) and far above them
-    (longer score rows than needed): both stay exact."""
+    (longer score rows than needed; at 20000 longer than the softmax pass keeps
+    in LDS): all stay exact."""
     c = gen.decode_inputs(760 + hint, batch=3, heads=6, head_dim=96, groups=1, r_k=192, r_v=192,
                           positions=(300, 129, 7), window=4, dtype="bf16", loop=3, loop_first=1,
                           loop_last=8, latent_std=1.0, exact_std=1.0, paired=False,
