@@ -396,6 +396,7 @@ lla_status decode(const lla_set_desc* d, const lla_store* st, int32_t batch,
   }
   p.need_qhead = (!fast_window || !absorbed) ? 1 : 0;
   const bool wide_maps = wide_scan && maps_wide_supports(p);
+  p.part_bf16 = wide_maps ? 1 : 0;
   hipError_t e = wide_maps                                ? launch_qmap_wide(p, s)
                  : (!generic && qmap_mfma_supports(p)) ? launch_qmap_mfma(p, absorbed, s)
                                                        : launch_qmap(p, absorbed, s);

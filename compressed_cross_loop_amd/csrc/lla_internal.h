@@ -43,7 +43,8 @@ struct DecodeParams {
   void* qlat;                     // [B][H][rk]  storage dtype
   float* qhead;                   // [B][H][dh]
   float* part_ml;                 // [B][S][H][2]
-  float* part_o;                  // [B][S][H][Dp]
+  float* part_o;                  // [B][S][H][Dp] (bf16 elements when part_bf16)
+  int32_t part_bf16;              // the wide scan leaves part_o in bf16 for the wide combine
   float* win_ml;                  // [B][WS][H][2]
   float* win_o;                   // [B][WS][H][dh]
   // head-folded reconstruct (LDS-staged form): A_t and B_t^T rows regrouped

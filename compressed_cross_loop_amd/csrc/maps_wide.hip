@@ -196,7 +196,8 @@ __global__ __launch_bounds__(kThreads) void k_combine_wide(DecodeParams p) {
   const int row = lane & 15, grp = lane >> 4;
   const int bA = min(b0 + row, B - 1);
   const float* wrow = wsm + row * NP;
-  const float* po = p.part_o + ((int64_t)bA * S * H + h) * p.Dp;   // split s at + s H Dp
+  // the wide scan leaves its partials in bf16 (rows of Dp elements)
+  const bf16* po = reinterpret_cast<const bf16*>(p.part_o) + ((int64_t)bA * S * H + h) * p.Dp;   // split s at + s H Dp
   const int64_t split_stride = (int64_t)H * p.Dp;
   const bf16* bt[NB];
 #pragma unroll
@@ -207,14 +208,13 @@ __global__ __launch_bounds__(kThreads) void k_combine_wide(DecodeParams p) {
   const int nk = (rv + 31) / 32;
   const float w0 = wrow[0];
   for (int ks0 = wave; ks0 < nk; ks0 += 4 * KB) {
-    f32x4 oa[KB][2];
+    bf16x8 oa[KB];
     bf16x8 ba[KB][NB];
 #pragma unroll
     for (int u = 0; u < KB; ++u) {
       const int ks = min(ks0 + 4 * u, nk - 1);
       const int k = min(32 * ks + 8 * grp, rv - 8);   // clamped; zeroed below when past r_v
-      oa[u][0] = *reinterpret_cast<const f32x4*>(po + k);
-      oa[u][1] = *reinterpret_cast<const f32x4*>(po + k + 4);
+      oa[u] = *reinterpret_cast<const bf16x8*>(po + k);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) ba[u][nb] = *reinterpret_cast<const bf16x8*>(bt[nb] + k);
     }
@@ -226,14 +226,14 @@ __global__ __launch_bounds__(kThreads) void k_combine_wide(DecodeParams p) {
       float o[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        o[e] = w0 * oa[u][0][e];
-        o[e + 4] = w0 * oa[u][1][e];
+        o[e] = w0 * static_cast<float>(oa[u][e]);
+        o[e + 4] = w0 * static_cast<float>(oa[u][e + 4]);
       }
       for (int s = 1; s < S; ++s) {                  // further context splits (forced or long contexts)
         const float ws = wrow[s];
-        const float* ps = po + s * split_stride + min(k, rv - 8);
+        const bf16x8 ps = *reinterpret_cast<const bf16x8*>(po + s * split_stride + min(k, rv - 8));
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] += ws * ps[e];
+        for (int e = 0; e < 8; ++e) o[e] += ws * static_cast<float>(ps[e]);
       }
       bf16x8 a;
 #pragma unroll
@@ -278,7 +278,7 @@ hipError_t launch_qmap_wide(const DecodeParams& p, hipStream_t s) {
 }
 
 hipError_t launch_combine_wide(const DecodeParams& p, hipStream_t s) {
-  if (!maps_wide_supports(p) || p.mode != kAbsorbed) return hipErrorNotSupported;
+  if (!maps_wide_supports(p) || p.mode != kAbsorbed || !p.part_bf16) return hipErrorNotSupported;
   const dim3 grid((p.H + 7) / 8 * 8 * ((p.B + kSeqChunk - 1) / kSeqChunk));
   const size_t lds = (size_t)kSeqChunk * (p.S + p.WS) * sizeof(float);
   switch (p.dh) {

@@ -384,10 +384,21 @@ __global__ __launch_bounds__(kThreads, 2) void k_scan_absorbed_wide_values(Decod
   for (int hb = 0; hb < 4; ++hb) {
     const int h = 16 * hb + col;
     if (h >= H) continue;
-    float* orow = p.part_o + (((int64_t)b * p.S + s) * H + h) * p.Dp;
+    const int64_t orow = (((int64_t)b * p.S + s) * H + h) * p.Dp;
 #pragma unroll
-    for (int jb = 0; jb < 4; ++jb)
-      if (db0 + jb < nblk) *reinterpret_cast<f32x4*>(orow + 16 * (db0 + jb) + 4 * grp) = acc[jb][hb];
+    for (int jb = 0; jb < 4; ++jb) {
+      if (db0 + jb >= nblk) continue;
+      const int d = 16 * (db0 + jb) + 4 * grp;
+      if (p.part_bf16) {   // the wide combine reads them in bf16, as it feeds them to its products
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        bf16x4 v;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = static_cast<bf16>(acc[jb][hb][r]);
+        *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(p.part_o) + orow + d) = v;
+      } else {
+        *reinterpret_cast<f32x4*>(p.part_o + orow + d) = acc[jb][hb];
+      }
+    }
   }
 }
 
