@@ -37,19 +37,21 @@ constexpr int kSeqChunk = 16;   // sequences per LDS round of the query map / pe
 // back through the transposing LDS read ds_read_b64_tr_b16.  q fragments are
 // 8-byte loads.  Rows are padded by 32 bytes so that the 16 rows one
 // transposing read touches fall in different banks.
-template <int DH>
+template <int DH, bool ROPE>
 __global__ __launch_bounds__(kThreads) void k_qmap_wide(DecodeParams p) {
   constexpr int HALF = DH / 2, KS = DH / 16, LDA = kThreads + 16;
   typedef short s16x4 __attribute__((ext_vector_type(4)));
   typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
   typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
   __shared__ __attribute__((aligned(16))) bf16 at[DH * LDA];
-  __shared__ float ub[kSeqChunk][kThreads + 4];
-  __shared__ float cs[kSeqChunk][HALF][2];
+  // rotation exchange buffers (one element when there is no rotation, so that
+  // more workgroups fit a CU)
+  __shared__ float ub[ROPE ? kSeqChunk : 1][ROPE ? kThreads + 4 : 1];
+  __shared__ float cs[ROPE ? kSeqChunk : 1][ROPE ? HALF : 1][2];
   const int h = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
   const int H = p.H, rk = p.rk, B = p.B;
-  const bool rope = p.rope_base != 0.f;
+  constexpr bool rope = ROPE;   // = (rope_base != 0)
   const int slab = rope ? (kThreads / DH) * DH : kThreads;   // whole d_h blocks when rotating
   const int n0 = blockIdx.x * slab;
   {
@@ -265,14 +267,22 @@ bool maps_wide_supports(const DecodeParams& p) {
   return p.bf16 && (p.dh == 64 || p.dh == 96 || p.dh == 128) && p.rv % 8 == 0 && p.S + p.WS <= 512;
 }
 
+template <int DH>
+void launch_qmap_dh(const DecodeParams& p, dim3 grid, hipStream_t s) {
+  if (p.rope_base != 0.f)
+    hipLaunchKernelGGL((k_qmap_wide<DH, true>), grid, dim3(kThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL((k_qmap_wide<DH, false>), grid, dim3(kThreads), 0, s, p);
+}
+
 hipError_t launch_qmap_wide(const DecodeParams& p, hipStream_t s) {
   if (!maps_wide_supports(p)) return hipErrorNotSupported;
   const int slab = p.rope_base != 0.f ? (kThreads / p.dh) * p.dh : kThreads;
   const dim3 grid((p.rk + slab - 1) / slab, p.H);
   switch (p.dh) {
-    case 64: hipLaunchKernelGGL(k_qmap_wide<64>, grid, dim3(kThreads), 0, s, p); break;
-    case 96: hipLaunchKernelGGL(k_qmap_wide<96>, grid, dim3(kThreads), 0, s, p); break;
-    default: hipLaunchKernelGGL(k_qmap_wide<128>, grid, dim3(kThreads), 0, s, p); break;
+    case 64: launch_qmap_dh<64>(p, grid, s); break;
+    case 96: launch_qmap_dh<96>(p, grid, s); break;
+    default: launch_qmap_dh<128>(p, grid, s); break;
   }
   return hipGetLastError();
 }
