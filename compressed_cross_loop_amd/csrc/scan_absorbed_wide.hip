@@ -37,11 +37,13 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kTokPerWave = 64;                   // scores: 4 row blocks of 16 tokens
-constexpr int kTokPerBlock = 4 * kTokPerWave;     // scores workgroup
+constexpr int kScoreWaves = 8;                    // scores workgroup: 8 waves share each staged q~ chunk
+constexpr int kScoreThreads = 64 * kScoreWaves;
+constexpr int kTokPerBlock = kScoreWaves * kTokPerWave;   // scores workgroup
 constexpr int kSlab = 256;                        // values: r_v dims per workgroup
 constexpr int kWidePageTab = kWideMaxPages;       // page ids of one split, in LDS
 constexpr int kSoftmaxLdsTokens = 16384;          // longest score row the softmax pass keeps in LDS (64 KiB)
-constexpr int kScoreWorkgroups = 1024;            // score-pass workgroups aimed at (two rounds of two per CU)
+constexpr int kScoreWorkgroups = 512;             // score-pass workgroups aimed at (two rounds of one per CU)
 
 template <typename F, int... U>
 __device__ __forceinline__ void wide_static_for_impl(F&& f, std::integer_sequence<int, U...>) {
@@ -56,12 +58,12 @@ __device__ __forceinline__ int latent_tokens(const DecodeParams& p, int b) {
 }
 
 // ---------------------------------------------------------------- scores
-// One workgroup = 256 consecutive tokens x all heads (padded to 64) x one part
-// of r_k (the whole of it unless the batch is small); wave w owns tokens
+// One workgroup = 512 consecutive tokens x all heads (padded to 64) x one part
+// of r_k (the whole of it unless the batch is small); wave w (of 8) owns tokens
 // 64 w .. 64 w + 63 (4 row blocks of 16), K in steps of 32
 // (v_mfma_f32_16x16x32_bf16, 16 per step).  Key fragments come straight from
 // the store (one 16-byte load per lane, token = lane % 16 of the row block),
-// kKeyAhead steps ahead.  q~ is shared by the four waves: it is staged in LDS
+// kKeyAhead steps ahead.  q~ is shared by the eight waves: it is staged in LDS
 // in chunks of 128 latent dims (64 head rows of 256 contiguous bytes, loaded
 // once per workgroup, double-buffered) and its fragments are read from there;
 // the 16-byte pieces of a row are XOR-swizzled by the row so that the 16
@@ -69,7 +71,7 @@ __device__ __forceinline__ int latent_tokens(const DecodeParams& p, int b) {
 constexpr int kKeyAhead = 4;      // = steps per q~ chunk (the key ring index is the step in the chunk)
 constexpr int kQChunk = 128;      // latent dims per staged q~ chunk
 
-__global__ __launch_bounds__(kThreads, 2) void k_scan_absorbed_wide_scores(DecodeParams p) {
+__global__ __launch_bounds__(kScoreThreads) void k_scan_absorbed_wide_scores(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) bf16 qs[2][64 * kQChunk];
   const int b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -91,25 +93,26 @@ __global__ __launch_bounds__(kThreads, 2) void k_scan_absorbed_wide_scores(Decod
     const int64_t page = p.bt[(int64_t)b * p.max_pages + t / P];
     krow[i] = pages + tile_base(page, 0, t % P, 1, P, R) + (t % 16) * rk + 8 * grp;
   }
-  // q~ staging: piece x = tid + 256 k of a chunk is head row x / 16, dims
-  // 8 (x % 16) .. + 7, kept at slot (x % 16) ^ (row % 16) of its LDS row
-  const bf16* qsrc[4];
-  int qoff[4], qdst[4];
+  // q~ staging: piece x = tid + kScoreThreads k of a chunk is head row x / 16,
+  // dims 8 (x % 16) .. + 7, kept at slot (x % 16) ^ (row % 16) of its LDS row
+  constexpr int QP = 64 * 16 / kScoreThreads;   // pieces per thread
+  const bf16* qsrc[QP];
+  int qoff[QP], qdst[QP];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int x = tid + kThreads * k, row = x >> 4, c = x & 15;
+  for (int k = 0; k < QP; ++k) {
+    const int x = tid + kScoreThreads * k, row = x >> 4, c = x & 15;
     qsrc[k] = static_cast<const bf16*>(p.qlat) + ((int64_t)b * H + min(row, H - 1)) * rk;
     qoff[k] = 8 * c;
     qdst[k] = row * kQChunk + 8 * (c ^ (row & 15));
   }
-  u32x4 qreg[4];
+  u32x4 qreg[QP];
   auto q_load = [&](int kc0) {   // pieces past r_k feed no step (r_k % 32 == 0): clamp their address
 #pragma unroll
-    for (int k = 0; k < 4; ++k) qreg[k] = *reinterpret_cast<const u32x4*>(qsrc[k] + min(kc0 + qoff[k], rk - 8));
+    for (int k = 0; k < QP; ++k) qreg[k] = *reinterpret_cast<const u32x4*>(qsrc[k] + min(kc0 + qoff[k], rk - 8));
   };
   auto q_store = [&](int buf) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) *reinterpret_cast<u32x4*>(&qs[buf][qdst[k]]) = qreg[k];
+    for (int k = 0; k < QP; ++k) *reinterpret_cast<u32x4*>(&qs[buf][qdst[k]]) = qreg[k];
   };
 
   f32x4 acc[4][4];
@@ -430,7 +433,7 @@ hipError_t launch_scan_absorbed_wide(const DecodeParams& p, hipStream_t s) {
   if (!scan_absorbed_wide_supports(p) || p.lcap % kTokPerBlock || !p.wscore || !p.wprob ||
       p.wsplit != scan_absorbed_wide_ksplit(p.B, p.lcap, p.rk))
     return hipErrorNotSupported;
-  hipLaunchKernelGGL(k_scan_absorbed_wide_scores, dim3(p.lcap / kTokPerBlock, p.B, p.wsplit), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL(k_scan_absorbed_wide_scores, dim3(p.lcap / kTokPerBlock, p.B, p.wsplit), dim3(kScoreThreads), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.lcap <= kSoftmaxLdsTokens)
