@@ -253,7 +253,7 @@ lla_status hla_decode_windowed(const lla_set_desc* desc, const lla_store* store,
  * takes the two-pass scan ("k_scan_absorbed_wide" below) it also includes a
  * bf16 probability per (sequence, head, latent token) and an fp32 score per
  * (part of r_k, sequence, head, latent token), for tokens up to max_pos + 1
- * rounded up to 256: (4 parts + 2) batch H L bytes, with one part at large
+ * rounded up to 512: (4 parts + 2) batch H L bytes, with one part at large
  * batches and up to r_k / 128 at small ones.  A decode
  * call uses that scan only when the store cannot hold more tokens than these
  * rows cover (max_pages_per_seq * page_size <= L with L from max_pos_hint);
