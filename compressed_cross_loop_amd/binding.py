@@ -112,6 +112,9 @@ lib.lla_parallel_workspace_bytes.restype = ctypes.c_size_t
 lib.lla_parallel_workspace_bytes.argtypes = [_P(LlaSetDesc), ctypes.c_int32, ctypes.c_int32]
 lib.lla_decode_scan_kernel.restype = ctypes.c_char_p
 lib.lla_decode_scan_kernel.argtypes = [_P(LlaSetDesc), ctypes.c_int32, ctypes.c_int32]
+lib.lla_decode_scan_kernel_for_store.restype = ctypes.c_char_p
+lib.lla_decode_scan_kernel_for_store.argtypes = [_P(LlaSetDesc), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                 ctypes.c_int32]
 lib.lla_bytes_per_token.restype = ctypes.c_size_t
 lib.lla_bytes_per_token.argtypes = [_P(LlaSetDesc)]
 lib.lla_status_string.restype = ctypes.c_char_p
@@ -119,7 +122,7 @@ lib.lla_status_string.argtypes = [ctypes.c_int]
 lib.lla_abi_version.restype = ctypes.c_int32
 lib.lla_abi_version.argtypes = []
 
-ABI_VERSION = 4   # include/lla.h LLA_ABI_VERSION this binding marshals for
+ABI_VERSION = 5   # include/lla.h LLA_ABI_VERSION this binding marshals for
 if lib.lla_abi_version() != ABI_VERSION:
     raise ImportError(f"{LIB_PATH} has ABI version {lib.lla_abi_version()}, the binding expects {ABI_VERSION}: "
                       "rebuild it (python3 compressed_cross_loop_amd/build.py)")
@@ -204,6 +207,13 @@ def lla_decode_scan_kernel(desc, entry, flags=0):
     """Latent-scan kernel family a decode call launches (entry 0 reconstruct,
     1 absorbed, 2 HLA windowed); None on invalid arguments."""
     r = lib.lla_decode_scan_kernel(ctypes.byref(desc), entry, flags)
+    return None if r is None else r.decode()
+
+
+def lla_decode_scan_kernel_for_store(desc, entry, max_pos_hint, max_pages_per_seq, flags=0):
+    """The scan kernel family a decode call launches on a store whose block
+    table has max_pages_per_seq columns; None on invalid arguments."""
+    r = lib.lla_decode_scan_kernel_for_store(ctypes.byref(desc), entry, flags, max_pos_hint, max_pages_per_seq)
     return None if r is None else r.decode()
 
 

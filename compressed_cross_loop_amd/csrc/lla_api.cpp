@@ -71,7 +71,10 @@ Plan make_plan(int batch, int max_pos, int window, int splits, int wgs, int targ
   return Plan{(int)S, (int)(per * gran)};
 }
 
-bool use_mfma_scan(const lla_set_desc& d, int flags) {
+// max_pages: columns of the store's block table, or 0 for the store-free
+// queries (workspace size, split plan, kernel name), which assume a table
+// within every matrix-core kernel's LDS page table
+bool use_mfma_scan(const lla_set_desc& d, int flags, int max_pages = 0) {
   if (flags & LLA_FLAG_GENERIC) return false;
   if (d.dtype != LLA_BF16) return false;
   DecodeParams p{};
@@ -81,12 +84,12 @@ bool use_mfma_scan(const lla_set_desc& d, int flags) {
   p.dh = d.head_dim;
   p.bf16 = 1;
   p.fp8 = d.latent_fp8;
+  p.max_pages = max_pages;
   return scan_absorbed_mfma_supports(p);
 }
 
 // the two-pass scan of one wide latent shared by all heads, for the bf16
-// shapes the one-pass matrix-core scan does not cover (the store's page
-// count is checked at decode time)
+// shapes the one-pass matrix-core scan does not cover
 bool use_wide_scan(const lla_set_desc& d, int flags) {
   if (flags & (LLA_FLAG_GENERIC | LLA_FLAG_FUSED)) return false;
   if (d.dtype != LLA_BF16 || use_mfma_scan(d, flags)) return false;
@@ -98,7 +101,7 @@ bool use_wide_scan(const lla_set_desc& d, int flags) {
   return scan_absorbed_wide_supports(p);
 }
 
-bool use_mfma_reconstruct(const lla_set_desc& d, int flags) {
+bool use_mfma_reconstruct(const lla_set_desc& d, int flags, int max_pages = 0) {
   if (flags & LLA_FLAG_GENERIC) return false;
   DecodeParams p{};
   p.hpg = d.n_heads / d.groups;
@@ -106,6 +109,7 @@ bool use_mfma_reconstruct(const lla_set_desc& d, int flags) {
   p.rv = d.r_v;
   p.dh = d.head_dim;
   p.bf16 = d.dtype == LLA_BF16;
+  p.max_pages = max_pages;
   return scan_reconstruct_mfma_supports(p);
 }
 
@@ -136,49 +140,83 @@ bool flags_ok(int flags) {
   return !(flags & ~kValidFlags) && (flags & kValidFlags) != kValidFlags;
 }
 
-// the latent-scan kernel family a decode call launches for this set
-const char* scan_kernel_name(const lla_set_desc& d, int absorbed, int flags) {
-  if (absorbed && (flags & LLA_FLAG_FUSED)) return "k_fused_decode";
+// The latent-scan kernel family of one decode call.  Every decision that
+// depends on it (split plan, workspace layout, launches, the name reported to
+// profilers) goes through this one choice.
+enum class Scan {
+  kFused, kAbsorbedMfma, kAbsorbedWide, kAbsorbedGeneric, kReconstructMfma, kReconstructGemm,
+  kReconstructGeneric
+};
+
+// max_pages > 0: the call's store has a block table of that many columns
+// (and max_pos_hint is the call's): a table longer than a matrix-core scan's
+// LDS page table, or covering more tokens than the wide scan's score rows,
+// takes the general scan.  max_pages == 0: the store-free queries.
+Scan choose_scan(const lla_set_desc& d, bool absorbed, int flags, int max_pages = 0, int max_pos_hint = 0) {
   if (absorbed) {
-    if (use_mfma_scan(d, flags)) return "k_scan_absorbed_mfma";
-    return use_wide_scan(d, flags) ? "k_scan_absorbed_wide" : "k_scan_absorbed_generic";
+    if (flags & LLA_FLAG_FUSED) return Scan::kFused;
+    if (use_mfma_scan(d, flags)) return use_mfma_scan(d, flags, max_pages) ? Scan::kAbsorbedMfma
+                                                                             : Scan::kAbsorbedGeneric;
+    if (use_wide_scan(d, flags)) {
+      if (max_pages <= 0) return Scan::kAbsorbedWide;
+      const int lcap = scan_absorbed_wide_lcap(max_pos_hint);
+      const bool rows_cover = (int64_t)max_pages * d.page_size <= lcap && max_pages <= kWideMaxPages;
+      return rows_cover ? Scan::kAbsorbedWide : Scan::kAbsorbedGeneric;
+    }
+    return Scan::kAbsorbedGeneric;
   }
-  if (use_mfma_reconstruct(d, flags)) return "k_scan_reconstruct_mfma";
-  if (use_gemm_reconstruct(d, flags)) return "k_scan_reconstruct_gemm";
-  return "k_scan_reconstruct_generic";
+  if (use_mfma_reconstruct(d, flags))
+    return use_mfma_reconstruct(d, flags, max_pages) ? Scan::kReconstructMfma : Scan::kReconstructGeneric;
+  if (use_gemm_reconstruct(d, flags)) return Scan::kReconstructGemm;
+  return Scan::kReconstructGeneric;
 }
 
-Plan plan_for(const lla_set_desc& d, int batch, int max_pos, int window, int splits, int entry,
-              int flags) {
-  const bool absorbed = entry != 0;
+const char* scan_kernel_name(Scan k) {
+  switch (k) {
+    case Scan::kFused: return "k_fused_decode";
+    case Scan::kAbsorbedMfma: return "k_scan_absorbed_mfma";
+    case Scan::kAbsorbedWide: return "k_scan_absorbed_wide";
+    case Scan::kAbsorbedGeneric: return "k_scan_absorbed_generic";
+    case Scan::kReconstructMfma: return "k_scan_reconstruct_mfma";
+    case Scan::kReconstructGemm: return "k_scan_reconstruct_gemm";
+    case Scan::kReconstructGeneric: return "k_scan_reconstruct_generic";
+  }
+  return "k_scan_absorbed_generic";
+}
+
+Plan plan_for(const lla_set_desc& d, int batch, int max_pos, int window, int splits, Scan k) {
   int wgs = d.n_heads;                                  // general kernels: one per head
   int target = kTargetWorkgroups;
-  if (absorbed && (flags & LLA_FLAG_FUSED)) {
-    target = 2 * kTargetWorkgroups;   // small workgroups: a few resident per CU
-    const Plan pl = make_plan(batch, max_pos, window, splits, wgs, target, kChunk);
-    if (pl.S <= kMaxFusedSplits) return pl;
-    return make_plan(batch, max_pos, window, kMaxFusedSplits, wgs, target, kChunk);
-  } else if (absorbed && use_mfma_scan(d, flags)) {
-    wgs = d.groups;
-    // three quarters of a workgroup per CU (measured at 16k context and batch
-    // 32: 6 splits 202 us, 8 splits 207 us, 12 splits 242 us per call; batch
-    // 128 at 4k keeps its 2 splits)
-    target = 3 * kTargetWorkgroups / 4;
-    // the matrix-core combine merges at most kCombineMaxParts splits + window
-    // slices (one window slice per split when the scan takes the window along)
-    return make_plan(batch, max_pos, window, splits, wgs, target, kChunk, kCombineMaxParts / 2);
-  } else if (absorbed && use_wide_scan(d, flags)) {
-    // the value pass runs one workgroup per (256-dim slab, split, sequence)
-    wgs = scan_absorbed_wide_slabs(d.r_v);
-    return make_plan(batch, max_pos, window, splits, wgs, target, kChunk, kCombineMaxParts / 2);
-  }
   int gran = kChunk;
-  if (!absorbed && use_mfma_reconstruct(d, flags)) {
-    wgs = (d.n_heads + 3) / 4;
-    target = 2 * kTargetWorkgroups;   // small workgroups: two resident per CU
-  } else if (!absorbed && use_gemm_reconstruct(d, flags)) {
-    wgs = (d.n_heads + 1) / 2;          // two heads per workgroup
-    gran = scan_reconstruct_gemm_tile(d.head_dim);
+  switch (k) {
+    case Scan::kFused: {
+      target = 2 * kTargetWorkgroups;   // small workgroups: a few resident per CU
+      const Plan pl = make_plan(batch, max_pos, window, splits, wgs, target, kChunk);
+      if (pl.S <= kMaxFusedSplits) return pl;
+      return make_plan(batch, max_pos, window, kMaxFusedSplits, wgs, target, kChunk);
+    }
+    case Scan::kAbsorbedMfma:
+      // three quarters of a workgroup per CU (measured at 16k context and batch
+      // 32: 6 splits 202 us, 8 splits 207 us, 12 splits 242 us per call; batch
+      // 128 at 4k keeps its 2 splits); the matrix-core combine merges at most
+      // kCombineMaxParts splits + window slices (one window slice per split
+      // when the scan takes the window along)
+      return make_plan(batch, max_pos, window, splits, d.groups, 3 * kTargetWorkgroups / 4, kChunk,
+                       kCombineMaxParts / 2);
+    case Scan::kAbsorbedWide:
+      // the value pass runs one workgroup per (256-dim slab, split, sequence)
+      return make_plan(batch, max_pos, window, splits, scan_absorbed_wide_slabs(d.r_v), target, kChunk,
+                       kCombineMaxParts / 2);
+    case Scan::kReconstructMfma:
+      wgs = (d.n_heads + 3) / 4;
+      target = 2 * kTargetWorkgroups;   // small workgroups: two resident per CU
+      break;
+    case Scan::kReconstructGemm:
+      wgs = (d.n_heads + 1) / 2;          // two heads per workgroup
+      gran = scan_reconstruct_gemm_tile(d.head_dim);
+      break;
+    default:
+      break;
   }
   return make_plan(batch, max_pos, window, splits, wgs, target, gran);
 }
@@ -230,16 +268,19 @@ int partial_width(const lla_set_desc& d, int entry) { return entry ? d.r_v : d.h
 
 size_t decode_ws_bytes(const lla_set_desc& d, int batch, int max_pos, int window, int splits) {
   // enough for every entry point and kernel family at these sizes
+  // (the general kernels, which a store too long for a matrix-core kernel
+  // falls back to, are the LLA_FLAG_GENERIC choices)
   size_t best = 0;
   for (int entry = 0; entry < 2; ++entry)
     for (int flags = 0; flags < 2; ++flags) {
-      const int S = plan_for(d, batch, max_pos, window, splits, entry, flags).S;
-      const int lcap = (entry && use_wide_scan(d, flags)) ? scan_absorbed_wide_lcap(max_pos) : 0;
+      const Scan k = choose_scan(d, entry != 0, flags);
+      const int S = plan_for(d, batch, max_pos, window, splits, k).S;
+      const int lcap = k == Scan::kAbsorbedWide ? scan_absorbed_wide_lcap(max_pos) : 0;
       best = std::max(best, ws_layout(d, batch, S, std::max(S, window_slices(window)),
                                       partial_width(d, entry), false, lcap).total);
     }
   if (fused_shape(d)) {
-    const int S = plan_for(d, batch, max_pos, window, splits, 1, LLA_FLAG_FUSED).S;
+    const int S = plan_for(d, batch, max_pos, window, splits, Scan::kFused).S;
     best = std::max(best, ws_layout(d, batch, S, S, d.r_v, true).total);
   }
   return best;
@@ -334,16 +375,16 @@ lla_status decode(const lla_set_desc* d, const lla_store* st, int32_t batch,
 
   const bool absorbed = entry != 0;
   const bool generic = (a->flags & LLA_FLAG_GENERIC) != 0;
-  const Plan plan = plan_for(*d, batch, a->max_pos_hint, a->window, a->splits, absorbed ? 1 : 0, a->flags);
+  // the wide scan keeps a score row per (sequence, head) covering every
+  // latent token the store can hold, and the matrix-core scans stage the
+  // split's page ids in LDS: a store beyond either takes the general scan
+  const Scan kind = choose_scan(*d, absorbed, a->flags, st->max_pages_per_seq, a->max_pos_hint);
+  const Plan plan = plan_for(*d, batch, a->max_pos_hint, a->window, a->splits, kind);
   const int Dp = partial_width(*d, absorbed ? 1 : 0);
   const int WSmax = window_slices(a->window);
-  // the wide scan keeps a score row per (sequence, head) covering every
-  // latent token the store can hold; a store with more pages than the
-  // workspace plan covers takes the one-pass general scan
-  const int lcap = (absorbed && use_wide_scan(*d, a->flags)) ? scan_absorbed_wide_lcap(a->max_pos_hint) : 0;
-  const bool wide_scan = lcap > 0 && (int64_t)st->max_pages_per_seq * d->page_size <= lcap &&
-                         st->max_pages_per_seq <= kWideMaxPages;
-  const WsLayout w = ws_layout(*d, batch, plan.S, std::max(plan.S, WSmax), Dp, fused, wide_scan ? lcap : 0);
+  const bool wide_scan = kind == Scan::kAbsorbedWide;
+  const int lcap = wide_scan ? scan_absorbed_wide_lcap(a->max_pos_hint) : 0;
+  const WsLayout w = ws_layout(*d, batch, plan.S, std::max(plan.S, WSmax), Dp, fused, lcap);
   char* ws = static_cast<char*>(a->workspace);
 
   DecodeParams p{};
@@ -382,7 +423,7 @@ lla_status decode(const lla_set_desc* d, const lla_store* st, int32_t batch,
     if (e == hipSuccess && ev) e = hipEventRecord(ev[1], s);
     return hip_status(e);
   }
-  const bool mfma_scan = absorbed && use_mfma_scan(*d, a->flags);
+  const bool mfma_scan = kind == Scan::kAbsorbedMfma;
   const bool fast_window = !generic && window_fast_supports(p);
   // the matrix-core scan takes the window along when its group's heads fit
   // one workgroup (thread per 8 dims of a head)
@@ -401,24 +442,17 @@ lla_status decode(const lla_set_desc* d, const lla_store* st, int32_t batch,
                  : (!generic && qmap_mfma_supports(p)) ? launch_qmap_mfma(p, absorbed, s)
                                                        : launch_qmap(p, absorbed, s);
   if (e == hipSuccess && !p.fuse_window) e = fast_window ? launch_window_fast(p, s) : launch_window(p, s);
-  const bool gemm_reconstruct = !absorbed && !use_mfma_reconstruct(*d, a->flags) && use_gemm_reconstruct(*d, a->flags);
-  if (e == hipSuccess && gemm_reconstruct) e = launch_scan_reconstruct_gemm_prep(p, s);
+  if (e == hipSuccess && kind == Scan::kReconstructGemm) e = launch_scan_reconstruct_gemm_prep(p, s);
   if (e == hipSuccess && ev) e = hipEventRecord(ev[0], s);
   if (e == hipSuccess) {
-    if (!absorbed) {
-      if (use_mfma_reconstruct(*d, a->flags))
-        e = launch_scan_reconstruct_mfma(p, s);
-      else if (gemm_reconstruct)
-        e = launch_scan_reconstruct_gemm(p, s);
-      else
-        e = launch_scan_reconstruct_generic(p, s);
+    switch (kind) {
+      case Scan::kReconstructMfma: e = launch_scan_reconstruct_mfma(p, s); break;
+      case Scan::kReconstructGemm: e = launch_scan_reconstruct_gemm(p, s); break;
+      case Scan::kReconstructGeneric: e = launch_scan_reconstruct_generic(p, s); break;
+      case Scan::kAbsorbedMfma: e = launch_scan_absorbed_mfma(p, s); break;
+      case Scan::kAbsorbedWide: e = launch_scan_absorbed_wide(p, s); break;
+      default: e = launch_scan_absorbed_generic(p, s); break;
     }
-    else if (mfma_scan)
-      e = launch_scan_absorbed_mfma(p, s);
-    else if (wide_scan)
-      e = launch_scan_absorbed_wide(p, s);
-    else
-      e = launch_scan_absorbed_generic(p, s);
   }
   if (e == hipSuccess && ev) e = hipEventRecord(ev[1], s);
   if (e == hipSuccess)
@@ -500,13 +534,21 @@ size_t lla_decode_workspace_bytes(const lla_set_desc* desc, int32_t batch, int32
 int32_t lla_decode_plan_splits(const lla_set_desc* desc, int32_t batch, int32_t max_pos,
                                int32_t window, int32_t splits, int32_t entry) {
   if (check_desc(desc) != LLA_OK || batch <= 0 || max_pos < 0 || window < 0 || splits < 0) return 0;
-  return plan_for(*desc, batch, max_pos, window, splits, entry ? 1 : 0, 0).S;
+  return plan_for(*desc, batch, max_pos, window, splits, choose_scan(*desc, entry != 0, 0)).S;
 }
 
 const char* lla_decode_scan_kernel(const lla_set_desc* desc, int32_t entry, int32_t flags) {
   if (check_desc(desc) != LLA_OK || entry < 0 || entry > 2 || !flags_ok(flags)) return nullptr;
   if ((flags & LLA_FLAG_FUSED) && (entry == 0 || !fused_shape(*desc))) return nullptr;
-  return scan_kernel_name(*desc, entry != 0, flags);
+  return scan_kernel_name(choose_scan(*desc, entry != 0, flags));
+}
+
+const char* lla_decode_scan_kernel_for_store(const lla_set_desc* desc, int32_t entry, int32_t flags,
+                                             int32_t max_pos_hint, int32_t max_pages_per_seq) {
+  if (check_desc(desc) != LLA_OK || entry < 0 || entry > 2 || !flags_ok(flags)) return nullptr;
+  if ((flags & LLA_FLAG_FUSED) && (entry == 0 || !fused_shape(*desc))) return nullptr;
+  if (max_pos_hint < 0 || max_pages_per_seq <= 0) return nullptr;
+  return scan_kernel_name(choose_scan(*desc, entry != 0, flags, max_pages_per_seq, max_pos_hint));
 }
 
 size_t lla_parallel_workspace_bytes(const lla_set_desc* desc, int32_t batch, int32_t n_max) {

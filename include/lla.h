@@ -48,8 +48,9 @@
 extern "C" {
 #endif
 
-#define LLA_ABI_VERSION 4   /* 2: value decoder passed as B_t^T [H][d_h][r_v]; 3: latent_fp8;
-                                4: parallel attention over whole sequences */
+#define LLA_ABI_VERSION 5   /* 2: value decoder passed as B_t^T [H][d_h][r_v]; 3: latent_fp8;
+                                4: parallel attention over whole sequences;
+                                5: lla_decode_scan_kernel_for_store */
 
 typedef void* lla_stream_t; /* a hipStream_t */
 
@@ -275,8 +276,23 @@ int32_t lla_decode_plan_splits(const lla_set_desc* desc, int32_t batch, int32_t 
  * score pass, a softmax pass and a value pass, kernels named with this
  * prefix), "k_scan_absorbed_generic", "k_scan_reconstruct_mfma",
  * "k_scan_reconstruct_gemm" or "k_scan_reconstruct_generic" (static
- * strings, for profilers).  NULL on invalid arguments.  Host only. */
+ * strings, for profilers).  The name assumes a store whose block table fits
+ * the matrix-core scans' page tables (at most 8192 columns for
+ * "k_scan_absorbed_mfma" and "k_scan_absorbed_wide", 4096 for
+ * "k_scan_reconstruct_mfma"); lla_decode_scan_kernel_for_store answers for a
+ * given store.  NULL on invalid arguments.  Host only. */
 const char* lla_decode_scan_kernel(const lla_set_desc* desc, int32_t entry, int32_t flags);
+
+/* The latent-scan kernel family a decode call launches on a store whose
+ * block table has max_pages_per_seq columns, with this max_pos_hint: as
+ * lla_decode_scan_kernel, except that a table longer than a matrix-core
+ * scan's page table, or (for "k_scan_absorbed_wide") a store holding more
+ * tokens per sequence than the score rows planned from max_pos_hint cover,
+ * names the general scan ("k_scan_absorbed_generic" /
+ * "k_scan_reconstruct_generic"), which the call then runs.  NULL on invalid
+ * arguments (max_pos_hint < 0, max_pages_per_seq <= 0).  Host only. */
+const char* lla_decode_scan_kernel_for_store(const lla_set_desc* desc, int32_t entry, int32_t flags,
+                                             int32_t max_pos_hint, int32_t max_pages_per_seq);
 
 /* Bytes one set stores per token (all groups): G*(r_k + r_v)*sizeof(dtype)
  * ([HLA] "Latent Writer": r_k + r_v (+ 2 r_1) numbers per token per layer).

@@ -47,6 +47,10 @@ class Workload:
     page_size: int = 64
     family: str = "hla"      # "hla" (absorbed + window) or "lla" (one set, loops 1..T)
     value_scale: str = "unit"
+    # "iid": latents, maps and exact K/V drawn directly; "trajectory": per-head
+    # loop trajectories of rank 8 plus noise, decoders fit to a calibration
+    # sample, latents written through the writer (gen.trajectory_codec)
+    inputs: str = "iid"
 
     @property
     def pos(self) -> int:
@@ -73,7 +77,7 @@ W1 = Workload(
 W2 = Workload(
     key=2, name="lla-per-head-ouro1.4b", layers=24, loops=4, d_model=2048, heads=16,
     head_dim=128, batch=32, context=4096, window=0, dtype="bf16", rope_base=0.0,
-    rope_baked=0, sets=[SetSpec(1, 4, 16, 32, 32, 256)], family="lla")
+    rope_baked=0, sets=[SetSpec(1, 4, 16, 32, 32, 256)], family="lla", inputs="trajectory")
 
 # 3: HLA absorbed + exact window, Ouro-1.4B shape, 72 KiB/token
 W3 = Workload(

@@ -305,3 +305,85 @@ def device_normal(shape, dtype: str, seed: int, std: float = 1.0,
     t = torch.empty(shape, dtype=torch.float32, device=device)
     t.normal_(0.0, std, generator=gen)
     return t.to(TORCH_DTYPE[dtype])
+
+
+@dataclass
+class TrajectoryCodec:
+    """A per-head LLA codec fit to synthetic loop trajectories.
+
+    For every head h and part p (0 = keys, 1 = values) a token's trajectory
+    over the T loops is one vector X in R^(T d_h) (loop t holds dims
+    t d_h .. (t+1) d_h - 1), drawn as X = M alpha + noise eps with M [T d_h,
+    rank] of orthonormal columns times sqrt(T d_h / rank) (so the elements of
+    X have about unit variance), alpha ~ N(0, I_rank), eps ~ N(0, I).
+    U [T d_h, r] holds the top-r left singular vectors of a calibration sample
+    of n_cal such trajectories (fp64, from the symmetric eigendecomposition of
+    X X^T).  Shapes: M [H, 2, T d_h, rank], U [H, 2, T d_h, r]."""
+    loops: int
+    head_dim: int
+    noise: float
+    M: np.ndarray
+    U: np.ndarray
+
+    @property
+    def heads(self) -> int:
+        return int(self.M.shape[0])
+
+    @property
+    def rank(self) -> int:
+        return int(self.U.shape[3])
+
+    def encoders(self) -> np.ndarray:
+        """enc [T, H, 2r, 2 d_h]: E_t of head h = blockdiag(U^K_t^T, U^V_t^T),
+        mapping a loop's [k_t; v_t] to its contribution to [s^K; s^V]."""
+        T, dh, r, H = self.loops, self.head_dim, self.rank, self.heads
+        enc = np.zeros((T, H, 2 * r, 2 * dh))
+        for t in range(T):
+            blk = self.U[:, :, t * dh:(t + 1) * dh, :]          # [H, 2, d_h, r]
+            enc[t, :, :r, :dh] = blk[:, 0].transpose(0, 2, 1)
+            enc[t, :, r:, dh:] = blk[:, 1].transpose(0, 2, 1)
+        return enc
+
+    def decoders(self, loop: int):
+        """(A_t [H, d_h, r], Bv_t [H, r, d_h]) of loop t (1-based): the key
+        decoder U^K_t and the value decoder B_t = U^V_t^T (v = B_t^T s^V)."""
+        dh = self.head_dim
+        blk = self.U[:, :, (loop - 1) * dh:loop * dh, :]
+        return blk[:, 0].copy(), blk[:, 1].transpose(0, 2, 1).copy()
+
+
+def trajectory_codec(seed: int, *, heads: int, head_dim: int, loops: int, rank: int = 8, r: int = 32,
+                     noise: float = 0.05, n_cal: int = 2048) -> TrajectoryCodec:
+    """Draw the trajectory bases M and fit U (see TrajectoryCodec)."""
+    g = rng(seed, 31)
+    D = loops * head_dim
+    M = np.empty((heads, 2, D, rank))
+    U = np.empty((heads, 2, D, r))
+    for h in range(heads):
+        for p in range(2):
+            m = gaussian_orthonormal(g, D, rank, np.sqrt(D / rank))
+            X = m @ g.standard_normal((rank, n_cal)) + noise * g.standard_normal((D, n_cal))
+            _, vec = np.linalg.eigh(X @ X.T)      # ascending eigenvalues
+            U[h, p] = vec[:, ::-1][:, :r]
+            M[h, p] = m
+    return TrajectoryCodec(loops=loops, head_dim=head_dim, noise=noise, M=M, U=U)
+
+
+def trajectory_tokens(codec: TrajectoryCodec, *, batch: int, n_tok: int, seed: int, dtype: str = "bf16",
+                      device: str = "cuda") -> torch.Tensor:
+    """Fresh token trajectories of `batch` sequences x `n_tok` tokens, laid out
+    as writer inputs x [B, n_tok, T, H, 2 d_h]: x[b, j, t, h] = [k; v] of
+    token j, loop t, head h (the loop-t slices of X^K and X^V).  Drawn on
+    `device` from a seeded torch generator."""
+    H, T, dh, rank = codec.heads, codec.loops, codec.head_dim, codec.M.shape[3]
+    D = T * dh
+    gen_ = torch.Generator(device=device)
+    gen_.manual_seed(int(seed))
+    n = batch * n_tok
+    Mt = torch.from_numpy(codec.M.reshape(H * 2, D, rank).transpose(0, 2, 1).copy()).float().to(device)
+    alpha = torch.empty((H * 2, n, rank), dtype=torch.float32, device=device).normal_(generator=gen_)
+    X = torch.bmm(alpha, Mt.contiguous())                   # [2H, n, D]
+    del alpha
+    X.add_(torch.empty_like(X).normal_(generator=gen_), alpha=codec.noise)
+    X = X.view(H, 2, batch, n_tok, T, dh).permute(2, 3, 4, 0, 1, 5)
+    return X.reshape(batch, n_tok, T, H, 2 * dh).to(TORCH_DTYPE[dtype]).contiguous()

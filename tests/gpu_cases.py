@@ -59,6 +59,20 @@ def poison_unread(c: gen.DecodeInputs):
     return c
 
 
+def widen_block_table(c: gen.DecodeInputs, columns: int):
+    """Give every sequence a block table of `columns` columns: the extra
+    columns name a page no sequence owns (poisoned by poison_unread, so a call
+    that read one would return NaN).  Call after poison_unread."""
+    bt = c.block_table.numpy()
+    assert columns >= bt.shape[1]
+    spare = sorted(set(range(c.n_pages)) - set(bt.ravel().tolist()))
+    assert spare, "the store needs an unowned page"
+    wide = np.full((bt.shape[0], columns), spare[0], dtype=np.int32)
+    wide[:, :bt.shape[1]] = bt
+    c.block_table = torch.from_numpy(wide)
+    return c
+
+
 def run_decode(entry, c: gen.DecodeInputs, *, splits=0, flags=0, max_pos_hint=None):
     dev = "cuda"
     desc = desc_of(c)

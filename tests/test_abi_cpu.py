@@ -32,7 +32,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert B.lla_abi_version() == 4 == B.ABI_VERSION
+    assert B.lla_abi_version() == 5 == B.ABI_VERSION
     for s in range(5):
         assert B.lla_status_string(s)
     assert B.lla_status_string(99) == "unknown status"
@@ -205,6 +205,32 @@ def test_scan_kernel_query():
     bad = desc(B.LLA_BF16, 1, 16, 512, 128)
     bad.head_dim = 0
     assert B.lla_decode_scan_kernel(bad, 0) is None
+
+
+def test_scan_kernel_query_for_store():
+    """A block table longer than a matrix-core scan stages in LDS (8192 page ids
+    for the absorbed scans, 4096 for the per-head reconstruct scan), or a store
+    holding more tokens than the wide scan's score rows cover, takes the
+    general scan; the store-free query names the matrix-core kernel."""
+    def desc(G, H, r, dh, P=64):
+        return B.set_desc(n_heads=H, head_dim=dh, groups=G, r_k=r, r_v=r, loop_first=1, loop_last=4,
+                          page_size=P, rope_baked=0, rope_base=0.0, dtype=B.LLA_BF16)
+    q = B.lla_decode_scan_kernel_for_store
+    per_head = desc(16, 16, 32, 128, P=16)
+    assert q(per_head, 0, 100, 4096) == "k_scan_reconstruct_mfma"
+    assert q(per_head, 0, 100, 4097) == "k_scan_reconstruct_generic"
+    assert q(per_head, 1, 100, 8192) == "k_scan_absorbed_mfma"
+    assert q(per_head, 1, 100, 8193) == "k_scan_absorbed_generic"
+    hla = desc(1, 16, 256, 128, P=16)
+    assert q(hla, 2, 100, 8193) == "k_scan_absorbed_generic"
+    assert q(hla, 2, 100, 8192) == "k_scan_absorbed_mfma"
+    # the wide scan: score rows of max_pos_hint + 1 tokens rounded up to 512
+    wide = desc(1, 6, 192, 96)
+    assert q(wide, 1, 100, 8) == "k_scan_absorbed_wide"        # 512 tokens
+    assert q(wide, 1, 100, 9) == "k_scan_absorbed_generic"     # 576 > 512
+    assert q(wide, 1, 600, 16) == "k_scan_absorbed_wide"       # 1024 rows
+    assert q(wide, 1, 100, 8, B.LLA_FLAG_GENERIC) == "k_scan_absorbed_generic"
+    assert q(wide, 1, -1, 8) is None and q(wide, 1, 100, 0) is None
 
 
 def _kv(**kw):
@@ -395,7 +421,7 @@ def test_decode_workspace_holds_regrouped_decoders():
 def test_decode_workspace_holds_wide_scan_rows():
     """The two-pass absorbed scan of a wide shared latent keeps an fp32 score and
     a bf16 probability per (sequence, head, token) up to max_pos + 1 rounded up
-    to 256 tokens; the one-pass shapes keep none."""
+    to 512 tokens; the one-pass shapes keep none."""
     def desc(G, H, r, dh):
         return B.set_desc(n_heads=H, head_dim=dh, groups=G, r_k=r, r_v=r, loop_first=1, loop_last=4,
                           page_size=64, rope_baked=0, rope_base=0.0, dtype=B.LLA_BF16)

@@ -10,7 +10,7 @@ import torch
 
 from synth import gen
 from compressed_cross_loop_amd import binding as B
-from tests.gpu_cases import TOL, desc_of, oracle_decode, poison_unread, run_decode
+from tests.gpu_cases import TOL, desc_of, oracle_decode, poison_unread, run_decode, widen_block_table
 from tests.util import max_rel_err
 
 pytestmark = pytest.mark.gpu
@@ -212,17 +212,47 @@ def test_absorbed_wide_single_sequence(positions):
     check(poison_unread(c), "absorbed", "absorbed")
 
 
-@pytest.mark.parametrize("hint", [100, 2000, 20000])
-def test_absorbed_wide_hint(hint):
-    """max_pos_hint below the positions (the store holds more tokens than the
-    planned score rows: the one-pass general scan runs) and far above them
-    (longer score rows than needed; at 20000 longer than the softmax pass keeps
-    in LDS): all stay exact."""
+@pytest.mark.parametrize("hint, columns, kernel", [(100, 16, "k_scan_absorbed_generic"),
+                                                   (2000, 5, "k_scan_absorbed_wide"),
+                                                   (20000, 5, "k_scan_absorbed_wide")])
+def test_absorbed_wide_hint(hint, columns, kernel):
+    """max_pos_hint below the positions with a block table of 16 pages (1024
+    tokens, more than the 512-token score rows planned from the hint: the
+    one-pass general scan runs, between the matrix-core query map and combine),
+    and far above them (longer score rows than needed; at 20000 longer than
+    the softmax pass keeps in LDS): all stay exact."""
     c = gen.decode_inputs(760 + hint, batch=3, heads=6, head_dim=96, groups=1, r_k=192, r_v=192,
                           positions=(300, 129, 7), window=4, dtype="bf16", loop=3, loop_first=1,
                           loop_last=8, latent_std=1.0, exact_std=1.0, paired=False,
                           map_scale=float(np.sqrt(2.0)))
-    check(poison_unread(c), "absorbed", "absorbed", max_pos_hint=hint)
+    c = widen_block_table(poison_unread(c), columns)
+    assert B.lla_decode_scan_kernel_for_store(desc_of(c), 1, hint, columns) == kernel
+    check(c, "absorbed", "absorbed", max_pos_hint=hint)
+
+
+@pytest.mark.parametrize("entry, form, G, r, columns, kernel", [
+    ("reconstruct", "textbook", 16, 32, 4097, "k_scan_reconstruct_generic"),
+    ("reconstruct", "textbook", 16, 32, 4096, "k_scan_reconstruct_mfma"),
+    ("absorbed", "absorbed", 16, 32, 8193, "k_scan_absorbed_generic"),
+    ("hla", "absorbed", 1, 256, 8193, "k_scan_absorbed_generic"),
+    ("hla", "absorbed", 1, 256, 8192, "k_scan_absorbed_mfma"),
+])
+def test_long_block_table(entry, form, G, r, columns, kernel):
+    """16-token pages and a block table longer than the matrix-core scans
+    stage in LDS (4096 page ids per split for the per-head reconstruct scan,
+    8192 for the absorbed scan): the call takes the general scan and stays
+    exact; at the limit the matrix-core scan runs."""
+    H, d_h = 16, 128
+    rope = G == 1
+    c = gen.decode_inputs(900 + columns + r, batch=2, heads=H, head_dim=d_h, groups=G, r_k=r, r_v=r,
+                          positions=(150, 41), window=5, dtype="bf16", page_size=16,
+                          rope_base=10000.0 if rope else 0.0, rope_baked=int(rope), loop=2,
+                          loop_first=1 if not rope else 2, loop_last=4, latent_std=2.0,
+                          exact_std=1.0, paired=rope)
+    c = widen_block_table(poison_unread(c), columns)
+    assert B.lla_decode_scan_kernel_for_store(desc_of(c), {"reconstruct": 0, "absorbed": 1, "hla": 2}[entry],
+                                              150, columns) == kernel
+    check(c, entry, form)
 
 
 @pytest.mark.parametrize("H, d_h, r", [(5, 96, 192), (4, 128, 256), (3, 64, 96), (2, 96, 5280)])

@@ -159,3 +159,108 @@ def test_writer_bf16_shapes(case):
         positions = np.tile(np.arange(n_tok), (Bsz, 1)) + 7 * np.arange(Bsz)[:, None]
     got, want = run_writer(dtype="bf16", positions=positions, seed=12, **case)
     assert max_rel_err(got, want) < TOL["bf16"]
+
+
+def test_writer_lla2d_decode_shape():
+    """The writer call the bench times on workload 5: 64 tokens (one per
+    sequence, at positions anywhere in a 4k context), 32 loops x d_in 10560 ->
+    5280 + 5280, one group; K = 32 x 10560 is cut into many splits of several
+    rounds each.  Encoders and inputs are drawn on the device (E_t entries
+    N(0, 1/d_in), x ~ N(0, 1), as the bench draws them); four sampled tokens
+    are checked in full (all 10560 latent dims) against the oracle's Eq. 2, in
+    chunks of encoder rows, and every other store element keeps its NaN."""
+    from synth import configs
+    w = configs.get(5)
+    s = w.sets[0]
+    Bsz, R, P = w.batch, s.r_k + s.r_v, w.page_size
+    print(f"[case] writer workload 5 B={Bsz} loops={s.n_loops} d_in={s.d_in} R={R}", flush=True)
+    enc = gen.device_normal((s.n_loops, 1, R, s.d_in), "bf16", 501, 1.0 / np.sqrt(s.d_in))
+    x = gen.device_normal((Bsz, 1, s.n_loops, 1, s.d_in), "bf16", 502)
+    positions = gen.rng(13, 1).integers(0, w.context, size=(Bsz, 1)).astype(np.int32)
+    pps = -(-w.context // P)
+    bt, n_pages = gen.block_table(gen.rng(13, 2), Bsz, pps, 2)
+    pages = torch.full((n_pages, P * R), float("nan"), dtype=torch.bfloat16, device="cuda")
+    desc = B.set_desc(n_heads=w.heads, head_dim=w.head_dim, groups=1, r_k=s.r_k, r_v=s.r_v, loop_first=1,
+                      loop_last=s.n_loops, page_size=P, rope_baked=0, rope_base=0.0, dtype=B.LLA_BF16)
+    nbytes = B.lla_write_workspace_bytes(desc, Bsz, 1, s.d_in)
+    ws = torch.full((max(nbytes, 4) // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    B.lla_write_latents(desc, B.store(pages, torch.from_numpy(bt).cuda()), pos=torch.from_numpy(positions).cuda(),
+                        x=x, enc=enc, workspace=ws)
+    torch.cuda.synchronize()
+    # nothing but the 64 written rows changed
+    assert int((~torch.isnan(pages)).sum()) == Bsz * R
+    kw = dict(groups=1, page_size=P, r_k=s.r_k, r_v=s.r_v)
+    flat = pages.view(-1)
+    seqs = [0, 21, 42, 63]
+    got = []
+    for b in seqs:
+        p = int(positions[b, 0])
+        pg, sl = int(bt[b, p // P]), p % P
+        ko = O.store_key_offset(pg, 0, sl, np.arange(s.r_k), **kw)
+        vo = O.store_value_offset(pg, 0, sl, np.arange(s.r_v), **kw)
+        got.append(flat[torch.from_numpy(np.concatenate([ko, vo])).cuda()].double().cpu().numpy())
+    xs = x[seqs].double().cpu().numpy()
+    want = np.concatenate([
+        O.write_latents(xs, enc[:, :, r0:r0 + 1056].double().cpu().numpy(), positions[seqs], r_k=1056)[:, 0, 0]
+        for r0 in range(0, R, 1056)], axis=-1)
+    err = max_rel_err(np.stack(got), want)
+    print(f"max_rel_err={err:.3e}", flush=True)
+    assert err < TOL["bf16"]
+
+
+@pytest.mark.parametrize("loop", [1, 2, 3, 4])
+def test_tiny_fp32_writer_then_decode(loop):
+    """Workload 1 end to end in fp32: h_j,t ~ N(0, 1) for every token and loop,
+    E_t, A_t, B_t Gaussian-QR x 1/sqrt(d_h); the GPU writer fills both sets of
+    the layer (loop 1: r_1 = 32; loops 2..4: 128 + 128) at positions 0..255, then
+    the decode at i = 255 with W = 16 runs through every entry point that
+    reads the loop's set (hla_decode_windowed, lla_decode_absorbed,
+    lla_decode_reconstruct).  Exact window / current K and V ~ N(0, sigma^2),
+    sigma the RMS of the latent keys the loop's decoder rebuilds.  The oracle
+    writes its own fp64 latents from the same inputs; tolerance 1e-5."""
+    from synth import configs
+    w = configs.get(1)
+    H, dh, W, P, N = w.heads, w.head_dim, w.window, w.page_size, w.context
+    i = N - 1
+    sc = 1.0 / np.sqrt(dh)
+    k = w.set_for_loop(loop)
+    s = w.sets[k]
+    g = gen.rng(40 + loop)
+    h = g.standard_normal((1, N, w.loops, 1, w.d_model))
+    x = h[:, :, s.loop_first - 1:s.loop_last]                    # this set's loops
+    enc = np.stack([gen.gaussian_orthonormal(g, s.r_k + s.r_v, s.d_in, sc)[None] for _ in range(s.n_loops)])
+    A = np.stack([gen.gaussian_orthonormal(g, dh, s.r_k, sc) for _ in range(H)])
+    Bv = np.stack([gen.gaussian_orthonormal(g, s.r_v, dh, sc) for _ in range(H)])
+    q = g.standard_normal((1, H, dh))
+    pos = np.arange(N)[None]
+    lat = O.write_latents(x, enc, pos, r_k=s.r_k)[0]              # [N, 1, r_k + r_v] fp64
+    sigma = float(np.sqrt(np.mean(np.einsum("hdr,nr->nhd", A, lat[:, 0, :s.r_k]) ** 2)))
+    kc, vc = (g.standard_normal((1, H, dh)) * sigma for _ in range(2))
+    ring_k, ring_v = (g.standard_normal((1, W + 1, H, dh)) * sigma for _ in range(2))
+    pps = -(-N // P)
+    bt, n_pages = gen.block_table(g, 1, pps, 1)
+    desc = B.set_desc(n_heads=H, head_dim=dh, groups=1, r_k=s.r_k, r_v=s.r_v, loop_first=s.loop_first,
+                      loop_last=s.loop_last, page_size=P, rope_baked=0, rope_base=0.0, dtype=B.LLA_F32)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).float().cuda()
+    pages = torch.full((n_pages, P * (s.r_k + s.r_v)), float("nan"), dtype=torch.float32, device="cuda")
+    st = B.store(pages, torch.from_numpy(bt).cuda())
+    ws = torch.empty(max(B.lla_write_workspace_bytes(desc, 1, N, s.d_in), 4), dtype=torch.uint8, device="cuda")
+    B.lla_write_latents(desc, st, pos=torch.from_numpy(pos.astype(np.int32)).cuda(), x=dev(x), enc=dev(enc),
+                        workspace=ws)
+    sK, sV = [lat[:i - W, :, :s.r_k]], [lat[:i - W, :, s.r_k:]]
+    ref = {f: fn(sK, sV, [i], q, kc, vc, ring_k, ring_v, A, Bv, window=W, rope_base=0.0)
+           for f, fn in (("absorbed", O.absorbed_decode), ("textbook", O.textbook_decode))}
+    entries = [("absorbed", "absorbed"), ("reconstruct", "textbook"), ("hla", "absorbed")]
+    for entry, form in entries:
+        print(f"[case] workload 1 writer -> {entry} loop={loop}", flush=True)
+        out = torch.full((1, H, dh), float("nan"), dtype=torch.float32, device="cuda")
+        dws = torch.full((B.lla_decode_workspace_bytes(desc, 1, i, W) // 4,), float("nan"), device="cuda")
+        args = B.decode_args(loop=loop, window=W, pos=torch.tensor([i], dtype=torch.int32, device="cuda"),
+                             q=dev(q), k_cur=dev(kc), v_cur=dev(vc), ring_k=dev(ring_k), ring_v=dev(ring_v),
+                             A=dev(A), B=dev(Bv.transpose(0, 2, 1)), out=out, workspace=dws, max_pos_hint=i)
+        {"absorbed": B.lla_decode_absorbed, "reconstruct": B.lla_decode_reconstruct,
+         "hla": B.hla_decode_windowed}[entry](desc, st, 1, args)
+        torch.cuda.synchronize()
+        err = max_rel_err(out.cpu().numpy(), ref[form])
+        print(f"max_rel_err={err:.3e}", flush=True)
+        assert err < TOL["f32"]
