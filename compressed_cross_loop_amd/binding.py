@@ -112,6 +112,9 @@ lib.lla_parallel_workspace_bytes.restype = ctypes.c_size_t
 lib.lla_parallel_workspace_bytes.argtypes = [_P(LlaSetDesc), ctypes.c_int32, ctypes.c_int32]
 lib.lla_decode_scan_kernel.restype = ctypes.c_char_p
 lib.lla_decode_scan_kernel.argtypes = [_P(LlaSetDesc), ctypes.c_int32, ctypes.c_int32]
+lib.hla_decode_windowed_noalloc.restype = ctypes.c_int
+lib.hla_decode_windowed_noalloc.argtypes = [_P(LlaSetDesc), _P(LlaStore), ctypes.c_int32, _P(LlaDecodeArgs),
+                                            ctypes.c_void_p]
 lib.lla_decode_scan_kernel_for_store.restype = ctypes.c_char_p
 lib.lla_decode_scan_kernel_for_store.argtypes = [_P(LlaSetDesc), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                  ctypes.c_int32]
@@ -255,6 +258,15 @@ def lla_decode_absorbed(desc, st, batch, args, stream=None):
 
 def hla_decode_windowed(desc, st, batch, args, stream=None):
     _decode(lib.hla_decode_windowed, desc, st, batch, args, stream)
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20   # include/lla.h LLA_NOALLOC_SCRATCH_BYTES
+
+
+def hla_decode_windowed_noalloc(desc, st, batch, args, stream=None):
+    """hla_decode_windowed with the library's per-GPU scratch array as the
+    workspace: build `args` with workspace=None."""
+    _decode(lib.hla_decode_windowed_noalloc, desc, st, batch, args, stream)
 
 
 # ---------------------------------------------------------------- full cache

@@ -35,7 +35,8 @@
  *     position; in a key latent of m = r_k/d_h blocks every block rotates the
  *     same way (R~_p = I_m (x) R_p, [HLA] "Rotary Embedding Alignment").
  *     rope_base == 0 disables it.
- *   - The library is re-entrant and holds no state.  Calls that share a
+ *   - The library is re-entrant and holds no state, except the per-GPU
+ *     scratch array of hla_decode_windowed_noalloc.  Calls that share a
  *     workspace, store or ring must be ordered on one stream by the caller.
  */
 #ifndef LLA_H
@@ -245,6 +246,28 @@ lla_status lla_decode_absorbed(const lla_set_desc* desc, const lla_store* store,
 lla_status hla_decode_windowed(const lla_set_desc* desc, const lla_store* store,
                                int32_t batch, const lla_decode_args* args,
                                lla_stream_t stream);
+
+/*
+ * hla_decode_windowed without a caller workspace, for callers that cannot
+ * allocate device memory (code under graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The workspace lives in a file-scope
+ * device array of LLA_NOALLOC_SCRATCH_BYTES per GPU, which the library holds
+ * until the process ends; its address is looked up on the first call on
+ * each device.  The call allocates nothing.
+ *   args->workspace must be NULL and args->workspace_bytes 0 (else
+ *   INVALID_ARGUMENT); WORKSPACE_TOO_SMALL when lla_decode_workspace_bytes()
+ *   for these sizes exceeds LLA_NOALLOC_SCRATCH_BYTES (32 MiB: the HLA sets of
+ *   the Ouro-1.4B shape need 16.1 MiB at batch 128 and 4k context); LLA_ERR_HIP
+ *   when the array's address cannot be looked up; otherwise as
+ *   hla_decode_windowed.
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents: calls that overlap on one GPU (other streams, other threads
+ * without ordering) race.
+ */
+#define LLA_NOALLOC_SCRATCH_BYTES (32u << 20)
+lla_status hla_decode_windowed_noalloc(const lla_set_desc* desc, const lla_store* store,
+                                       int32_t batch, const lla_decode_args* args,
+                                       lla_stream_t stream);
 
 /* Workspace bytes any decode entry point needs for these sizes (splits as
  * in lla_decode_args; 0 = automatic).  For bf16 sets with one latent shared
