@@ -423,6 +423,18 @@ lla_status decode(const lla_set_desc* d, const lla_store* st, int32_t batch,
     if (e == hipSuccess && ev) e = hipEventRecord(ev[1], s);
     return hip_status(e);
   }
+  if (kind == Scan::kReconstructMfma) {
+    // one kernel does the query rotation, the latent scan and the exact
+    // window (split s takes window slice s); then the split merge
+    p.fuse_window = 1;
+    p.WS = 0;
+    p.tw = (a->window + 1 + plan.S - 1) / plan.S;
+    hipError_t e = ev ? hipEventRecord(ev[0], s) : hipSuccess;
+    if (e == hipSuccess) e = launch_scan_reconstruct_mfma(p, s);
+    if (e == hipSuccess && ev) e = hipEventRecord(ev[1], s);
+    if (e == hipSuccess) e = launch_combine(p, s);
+    return hip_status(e);
+  }
   const bool mfma_scan = kind == Scan::kAbsorbedMfma;
   const bool fast_window = !generic && window_fast_supports(p);
   // the matrix-core scan takes the window along when its group's heads fit

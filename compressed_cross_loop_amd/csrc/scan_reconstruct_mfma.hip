@@ -29,6 +29,14 @@
 // A wave's LDS operations run in order, so one slot per wave needs no
 // barrier.  Several tiles are in flight per wave, all in registers; the page
 // ids of the split are staged in LDS first.
+//
+// The whole call is this kernel and the split merge: each wave rotates and
+// scales its head's query itself (q' = s R_i q at the lane's dims; the
+// partner of dim d is d +- d_h/2, i.e. block nt +- NT/2 of the same lane),
+// and split s also takes slice s of the exact tokens of Eq. 4 (ring tokens
+// i-W .. i-1 and the current one, 16 per step in the same token-per-lane
+// layout, read straight from the ring rows) into the same running softmax;
+// the lanes holding the current token append R_i k_cur, v_cur to the ring.
 #include <type_traits>
 #include <utility>
 
@@ -56,6 +64,10 @@ template <int N, typename F> __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
+__device__ __forceinline__ short bf16_bits(float x) {
+  return __builtin_bit_cast(short, static_cast<bf16>(x));
+}
+
 // 16-byte chunk slot of a value copy: bit 3 ^= bit 4, so that the two
 // 16-lane groups a transposing read serves together hit different banks
 __device__ __forceinline__ int val_slot(int ch) { return ch ^ (((ch >> 4) & 1) << 3); }
@@ -67,6 +79,7 @@ __global__ __launch_bounds__(kThreads, (R == 32 || DH == 64) ? 2 : 1) void k_sca
   constexpr int kPF = R == 32 ? 6 : 3;   // tiles in flight per wave
   __shared__ int32_t ptab[kPageTab];
   __shared__ __attribute__((aligned(16))) unsigned char vlds[kWaves][KS * 1024];
+  __shared__ float csn[DH / 2][2];       // (cos, sin) of i theta_f
   const int s = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -84,9 +97,39 @@ __global__ __launch_bounds__(kThreads, (R == 32 || DH == 64) ? 2 : 1) void k_sca
   const int pfirst = t0 / P;
   const int npg = t1 > t0 ? (t1 - 1) / P - pfirst + 1 : 0;
   for (int x = tid; x < npg; x += kThreads) ptab[x] = p.bt[(int64_t)b * p.max_pages + pfirst + x];
+  const bool rope = p.rope_base != 0.f;
+  if (rope && tid < DH / 2) {
+    float c, sn;
+    rope_cs(p.rope_base, DH, tid, i, c, sn);
+    csn[tid][0] = c;
+    csn[tid][1] = sn;
+  }
   __syncthreads();
   if (h >= p.H) return;                  // wave-uniform; no barrier follows
   const int g = h / p.hpg;
+  // R_i x at this lane's dims 16 nt + 4 grp + r, from x at the same dims
+  auto rotate = [&](f32x4 (&x)[NT]) {
+    if (!rope) return;
+    f32x4 y[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int f = (16 * nt + 4 * grp + r) % (DH / 2);
+        const float c = csn[f][0], sn = csn[f][1];
+        const float other = x[(nt + NT / 2) % NT][r];
+        y[nt][r] = nt < NT / 2 ? x[nt][r] * c - other * sn : other * sn + x[nt][r] * c;
+      }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) x[nt] = y[nt];
+  };
+  // 4 consecutive bf16 of a head row at the lane's dims of block nt (a bf16
+  // is the upper half of the fp32 with the same value)
+  auto load4 = [&](const bf16* row, int nt) {
+    const uint2 u = *reinterpret_cast<const uint2*>(row + 16 * nt + 4 * grp);
+    return f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                 __uint_as_float(u.y & 0xffff0000u)};
+  };
 
   // decoders of this head in A-operand layout (lane: row 16 nt + col, latent
   // dims 32 st + 8 grp ..)
@@ -100,12 +143,15 @@ __global__ __launch_bounds__(kThreads, (R == 32 || DH == 64) ? 2 : 1) void k_sca
       af[nt][st] = *reinterpret_cast<const bf16x8*>(Ah + (int64_t)(16 * nt + col) * R + 32 * st + 8 * grp);
       bfr[nt][st] = *reinterpret_cast<const bf16x8*>(Bh + (int64_t)(16 * nt + col) * R + 32 * st + 8 * grp);
     }
-  // q' at this lane's dims 16 nt + 4 grp + r
+  // q' = s R_i q at this lane's dims 16 nt + 4 grp + r
   f32x4 qv[NT];
   {
-    const float* qh = p.qhead + ((int64_t)b * p.H + h) * DH;
+    const bf16* qh = static_cast<const bf16*>(p.q) + ((int64_t)b * p.H + h) * DH;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) qv[nt] = *reinterpret_cast<const f32x4*>(qh + 16 * nt + 4 * grp);
+    for (int nt = 0; nt < NT; ++nt) qv[nt] = load4(qh, nt);
+    rotate(qv);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) qv[nt] *= p.scale;
   }
 
   const bf16* pages = static_cast<const bf16*>(p.pages);
@@ -232,6 +278,71 @@ __global__ __launch_bounds__(kThreads, (R == 32 || DH == 64) ? 2 : 1) void k_sca
           step(U, nvalid, std::false_type{});
       }
     });
+  }
+  // exact tokens t = e0 .. e1-1 of 0..nw (ring tokens j0 + t, t == nw the
+  // current one), 16 per step, token tb + col in this lane
+  {
+    const int W = p.W;
+    const int j0 = max(0, i - W), nw = i - j0;
+    const int e0 = s * p.tw, e1 = min(e0 + p.tw, nw + 1);
+    const int64_t rs = (int64_t)p.H * DH;                 // elements per ring slot
+    const bf16* ring_k = static_cast<const bf16*>(p.ring_k);
+    const bf16* ring_v = static_cast<const bf16*>(p.ring_v);
+    for (int tb = e0; tb < e1; tb += 16) {
+      const int t = tb + col;
+      const bool valid = t < e1;
+      f32x4 kx[NT], vx[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) kx[nt] = vx[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (valid && t < nw) {
+        const int64_t off = ((int64_t)b * (W + 1) + (j0 + t) % (W + 1)) * rs + (int64_t)h * DH;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          kx[nt] = load4(ring_k + off, nt);
+          vx[nt] = load4(ring_v + off, nt);
+        }
+      } else if (valid) {
+        const int64_t off = ((int64_t)b * p.H + h) * DH;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          kx[nt] = load4(static_cast<const bf16*>(p.k_cur) + off, nt);
+          vx[nt] = load4(static_cast<const bf16*>(p.v_cur) + off, nt);
+        }
+        rotate(kx);
+        // ring append: slot i mod (W+1) held token i-W-1, which no slice reads
+        const int64_t so = ((int64_t)b * (W + 1) + i % (W + 1)) * rs + (int64_t)h * DH;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          s16x4 kw, vw;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            kw[r] = bf16_bits(kx[nt][r]);
+            vw[r] = bf16_bits(vx[nt][r]);
+          }
+          *reinterpret_cast<s16x4*>(static_cast<bf16*>(p.ring_k) + so + 16 * nt + 4 * grp) = kw;
+          *reinterpret_cast<s16x4*>(static_cast<bf16*>(p.ring_v) + so + 16 * nt + 4 * grp) = vw;
+        }
+      }
+      f32x4 sc4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) sc4 += qv[nt] * kx[nt];
+      float sc = (sc4[0] + sc4[1]) + (sc4[2] + sc4[3]);
+      sc += __shfl_xor(sc, 16);
+      sc += __shfl_xor(sc, 32);
+      if (!valid) sc = -INFINITY;
+      const float mx = row_max16(sc);     // finite: token tb is valid
+      if (mx > m + kLazy) {
+        const float alpha = exp2_diff(m, mx);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) o[nt] *= alpha;
+        lsum *= alpha;
+        m = mx;
+      }
+      const float pw = fast_exp2(sc - m);
+      lsum += pw;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) o[nt] += pw * vx[nt];
+    }
   }
   // totals over the 16 token lanes (the four lane groups hold the same tokens)
   lsum = row_sum16(lsum);
