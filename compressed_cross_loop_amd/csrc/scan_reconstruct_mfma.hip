@@ -76,7 +76,7 @@ template <int R, int DH>
 __global__ __launch_bounds__(kThreads, (R == 32 || DH == 64) ? 2 : 1) void k_scan_reconstruct_mfma(DecodeParams p) {
   constexpr int NT = DH / 16;            // 16-dim blocks of d_h
   constexpr int KS = R / 32;             // K steps over the latent width = KiB of values per tile
-  constexpr int kPF = R == 32 ? 6 : 3;   // tiles in flight per wave
+  constexpr int kPF = 3;                 // tiles in flight per wave
   __shared__ int32_t ptab[kPageTab];
   __shared__ __attribute__((aligned(16))) unsigned char vlds[kWaves][KS * 1024];
   __shared__ float csn[DH / 2][2];       // (cos, sin) of i theta_f
@@ -189,23 +189,46 @@ __global__ __launch_bounds__(kThreads, (R == 32 || DH == 64) ? 2 : 1) void k_sca
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // consume slot U holding tile ti (nvalid tokens valid; FULL: all 16)
+  // consume slot U holding tile ti (nvalid tokens valid; FULL: all 16).
+  // Order: the value block goes through LDS first (its transposing reads
+  // are in flight during the key products), then all key and value products
+  // are issued into their own accumulators, so that the softmax arithmetic
+  // reads results that have long landed instead of waiting on each product.
   auto step = [&](auto U, int nvalid, auto full) {
     constexpr int u = decltype(U)::value;
     constexpr bool FULL = decltype(full)::value;
     const bool valid = FULL || col < nvalid;
-    // keys: lane holds K^T[dim 16 nt + 4 grp + r][token col]
+    bf16x8 vf[KS];
+#pragma unroll
+    for (int st = 0; st < KS; ++st) {
+      typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+      unsigned char* vb = &vlds[wave][st * 1024];
+      *reinterpret_cast<bf16x8*>(vb + 16 * lane) = vbuf[u][st];
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + vro[0]));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + vro[1]));
+      vf[st] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+    // keys: lane holds K^T[dim 16 nt + 4 grp + r][token col]; values likewise V^T
+    f32x4 kh[NT], vh[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      kh[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < KS; ++st)
+        kh[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[nt][st], kbuf[u][st], kh[nt], 0, 0, 0);
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      vh[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < KS; ++st)
+        vh[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[nt][st], vf[st], vh[nt], 0, 0, 0);
+    }
     // four independent partial sums (one per r), so the products do not
     // form one dependent chain
     f32x4 sc4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      f32x4 kh = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int st = 0; st < KS; ++st)
-        kh = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[nt][st], kbuf[u][st], kh, 0, 0, 0);
-      sc4 += qv[nt] * kh;
-    }
+    for (int nt = 0; nt < NT; ++nt) sc4 += qv[nt] * kh[nt];
     float sc = (sc4[0] + sc4[1]) + (sc4[2] + sc4[3]);
     sc += __shfl_xor(sc, 16);
     sc += __shfl_xor(sc, 32);
@@ -220,28 +243,14 @@ __global__ __launch_bounds__(kThreads, (R == 32 || DH == 64) ? 2 : 1) void k_sca
     }
     const float pw = fast_exp2(sc - m);   // 0 for masked tokens
     lsum += pw;
-    // values: lane holds V^T[dim 16 nt + 4 grp + r][token col]
-    bf16x8 vf[KS];
-#pragma unroll
-    for (int st = 0; st < KS; ++st) {
-      typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-      unsigned char* vb = &vlds[wave][st * 1024];
-      *reinterpret_cast<bf16x8*>(vb + 16 * lane) = vbuf[u][st];
-      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + vro[0]));
-      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + vro[1]));
-      vf[st] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      f32x4 vh = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int st = 0; st < KS; ++st) vh = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[nt][st], vf[st], vh, 0, 0, 0);
       if (FULL) {
-        o[nt] += pw * vh;
+        o[nt] += pw * vh[nt];
       } else {
         // a masked token's rebuilt value may be anything (even NaN): select, not multiply
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o[nt][r] = valid ? o[nt][r] + pw * vh[r] : o[nt][r];
+        for (int r = 0; r < 4; ++r) o[nt][r] = valid ? o[nt][r] + pw * vh[nt][r] : o[nt][r];
       }
     }
   };
