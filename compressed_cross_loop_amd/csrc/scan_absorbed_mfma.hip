@@ -22,6 +22,10 @@
 // With fuse_window set, split s also handles slice s of the exact window
 // (window_slice below), so those bytes stream in the same launch.
 //
+// Latent tiles and ring rows are read exactly once per call, so their loads
+// are non-temporal (measured: 211.7 -> 201.0 us per main-set call on the
+// Ouro-1.4B shape at batch 128, 4k).
+//
 // The tile loop is software-pipelined (keys two to four tiles ahead, values
 // one to four, by latent width).  q~ is read from LDS to leave registers for
 // the key pipeline.  At the end the
@@ -65,14 +69,14 @@ template <int RK>
 __device__ __forceinline__ void load_keys(bf16x8 (&k)[RK / 32], const char* tile_b, int col, int grp) {
   const bf16* kp = reinterpret_cast<const bf16*>(tile_b) + col * RK + grp * 8;
 #pragma unroll
-  for (int st = 0; st < RK / 32; ++st) k[st] = *reinterpret_cast<const bf16x8*>(kp + st * 32);
+  for (int st = 0; st < RK / 32; ++st) k[st] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(kp + st * 32));
 }
 
 template <int RK, int RV>
 __device__ __forceinline__ void load_values(s16x4 (&v)[RV / 16], const char* tile_b, int col, int grp) {
   const bf16* vp = reinterpret_cast<const bf16*>(tile_b) + 16 * RK + col * 16 + grp * 4;
 #pragma unroll
-  for (int vt = 0; vt < RV / 16; ++vt) v[vt] = *reinterpret_cast<const s16x4*>(vp + vt * 256);
+  for (int vt = 0; vt < RV / 16; ++vt) v[vt] = __builtin_nontemporal_load(reinterpret_cast<const s16x4*>(vp + vt * 256));
 }
 
 __device__ __forceinline__ short bf16_bits(float x) {
@@ -169,16 +173,16 @@ template <int RK, int RV>
 __device__ __forceinline__ void load_keys8(Keys8<RK>& k, const char* tile, int col, int grp) {
   const char* kp = tile + col * RK + grp * 16;
 #pragma unroll
-  for (int u = 0; u < RK / 64; ++u) k.v[u] = *reinterpret_cast<const u32x4*>(kp + u * 64);
-  k.s = *reinterpret_cast<const f32x4*>(tile + 16 * (RK + RV) + 16 * grp);
+  for (int u = 0; u < RK / 64; ++u) k.v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + u * 64));
+  k.s = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(tile + 16 * (RK + RV) + 16 * grp));
 }
 
 template <int RK, int RV>
 __device__ __forceinline__ void load_values8(Vals8<RV>& v, const char* tile, int col, int grp) {
   const char* vp = tile + 16 * RK + col * 64 + grp * 16;
 #pragma unroll
-  for (int q = 0; q < RV / 64; ++q) v.v[q] = *reinterpret_cast<const u32x4*>(vp + q * 1024);
-  v.s = *reinterpret_cast<const f32x4*>(tile + 16 * (RK + RV) + 64 + 16 * grp);
+  for (int q = 0; q < RV / 64; ++q) v.v[q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp + q * 1024));
+  v.s = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(tile + 16 * (RK + RV) + 64 + 16 * grp));
 }
 
 // two bf16 from the e4m3 codes in bytes (2 hi, 2 hi + 1) of w
@@ -289,8 +293,8 @@ __device__ void window_slice(const DecodeParams& p, int b, int slice, int g, con
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t off = base + slot_of(tb + u) * rs;
-      kr[u] = *reinterpret_cast<const bf16x8*>(ring_k + off);
-      vr[u] = *reinterpret_cast<const bf16x8*>(ring_v + off);
+      kr[u] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(ring_k + off));
+      vr[u] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(ring_v + off));
     }
   };
   // one batch: U independent score reductions, one max, then the weighted
