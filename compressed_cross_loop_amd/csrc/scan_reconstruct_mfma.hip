@@ -169,7 +169,8 @@ __global__ __launch_bounds__(kThreads, (R == 32 || DH == 64) ? 2 : 1) void k_sca
     const int d = 8 * grp + 4 * hh + (col >> 2), c4 = col & 3;
     vro[hh] = val_slot((d >> 4) * 32 + (d & 15) * 2 + (c4 >> 1)) * 16 + (c4 & 1) * 8;
   }
-  // this lane's 16-byte chunk of each value KiB: read from chunk
+  // Tiles are read exactly once per call: non-temporal loads.
+  // This lane's 16-byte chunk of each value KiB: read from chunk
   // val_slot(lane) of the block, stored at slot `lane` of the wave's LDS KiB
   const int vsrc = val_slot(lane) * 8;
   bf16x8 kbuf[kPF][KS], vbuf[kPF][KS];
@@ -179,8 +180,8 @@ __global__ __launch_bounds__(kThreads, (R == 32 || DH == 64) ? 2 : 1) void k_sca
     const bf16* tp = tile_ptr(ti);
 #pragma unroll
     for (int st = 0; st < KS; ++st) {
-      kbuf[u][st] = *reinterpret_cast<const bf16x8*>(tp + col * R + 32 * st + 8 * grp);
-      vbuf[u][st] = *reinterpret_cast<const bf16x8*>(tp + 16 * R + st * 512 + vsrc);
+      kbuf[u][st] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(tp + col * R + 32 * st + 8 * grp));
+      vbuf[u][st] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(tp + 16 * R + st * 512 + vsrc));
     }
   };
 
