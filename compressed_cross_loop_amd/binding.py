@@ -118,6 +118,9 @@ lib.hla_decode_windowed_noalloc.argtypes = [_P(LlaSetDesc), _P(LlaStore), ctypes
 lib.lla_decode_scan_kernel_for_store.restype = ctypes.c_char_p
 lib.lla_decode_scan_kernel_for_store.argtypes = [_P(LlaSetDesc), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                  ctypes.c_int32]
+lib.lla_check_indices.restype = ctypes.c_int
+lib.lla_check_indices.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                  ctypes.c_int32]
 lib.lla_bytes_per_token.restype = ctypes.c_size_t
 lib.lla_bytes_per_token.argtypes = [_P(LlaSetDesc)]
 lib.lla_status_string.restype = ctypes.c_char_p
@@ -204,6 +207,16 @@ def lla_decode_workspace_bytes(desc, batch, max_pos, window, splits=0):
 
 def lla_decode_plan_splits(desc, batch, max_pos, window, splits=0, entry=1):
     return lib.lla_decode_plan_splits(ctypes.byref(desc), batch, max_pos, window, splits, entry)
+
+
+def lla_check_indices(pos, block_table, n_pages, page_size):
+    """Host check of positions and block-table entries (CPU int32 tensors or
+    arrays); returns the status (LLA_OK or LLA_ERR_INVALID_ARGUMENT)."""
+    import numpy as _np
+    pos = _np.ascontiguousarray(_np.asarray(pos, dtype=_np.int32))
+    bt = _np.ascontiguousarray(_np.asarray(block_table, dtype=_np.int32))
+    return lib.lla_check_indices(pos.ctypes.data, int(pos.shape[0]), bt.ctypes.data, int(bt.shape[1]),
+                                 int(page_size), int(n_pages))
 
 
 def lla_decode_scan_kernel(desc, entry, flags=0):

@@ -8,9 +8,9 @@
 //   scan      latent tokens j < i-W of one context split, online softmax:
 //             absorbed    -- scores q~ . sK_j, accumulate sum a_j sV_j
 //             reconstruct -- rebuild k_j = A sK_j and v_j = B^T sV_j first
-//                            (Looped Latent Attention, "reconstructs
-//                            loop-specific K/V vectors only when attention
-//                            reads them")
+//                            (Looped Latent Attention abstracts: keys and
+//                            values are rebuilt from the latents when
+//                            attention reads them)
 //   combine   merge split and window partials (one softmax over all tokens,
 //             Eq. 4) and apply B_t^T to the latent sum (absorbed)
 // with s = log2(e)/sqrt(d_h): scores live in the exp2 domain.

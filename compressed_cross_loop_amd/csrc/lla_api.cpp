@@ -656,6 +656,20 @@ lla_status lla_decode_full_cache(const lla_kv_desc* d, const lla_kv_cache* c, in
   return hip_status(e);
 }
 
+lla_status lla_check_indices(const int32_t* pos_host, int32_t batch, const int32_t* block_table_host,
+                             int32_t max_pages_per_seq, int32_t page_size, int32_t n_pages) {
+  if (!pos_host || !block_table_host || batch <= 0 || max_pages_per_seq <= 0 || page_size <= 0 || n_pages <= 0)
+    return LLA_ERR_INVALID_ARGUMENT;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int32_t i = pos_host[b];
+    if (i < 0 || (int64_t)i >= (int64_t)max_pages_per_seq * page_size) return LLA_ERR_INVALID_ARGUMENT;
+    const int32_t* row = block_table_host + (int64_t)b * max_pages_per_seq;
+    for (int32_t pg = 0; pg <= i / page_size; ++pg)
+      if (row[pg] < 0 || row[pg] >= n_pages) return LLA_ERR_INVALID_ARGUMENT;
+  }
+  return LLA_OK;
+}
+
 size_t lla_bytes_per_token(const lla_set_desc* desc) {
   if (check_desc(desc) != LLA_OK) return 0;
   if (desc->latent_fp8) return (size_t)desc->groups * (desc->r_k + desc->r_v + 8);   // codes + 2 fp32 scales

@@ -1,6 +1,6 @@
 // Reconstruct-on-read latent scan for per-head Looped Latent Attention on the
-// gfx950 matrix cores ("Looped Latent Attention" abstracts: the codec
-// "reconstructs loop-specific K/V vectors only when attention reads them").
+// gfx950 matrix cores ("Looped Latent Attention" abstracts: the codec keeps
+// only latents and rebuilds a loop's keys and values when attention reads them).
 //
 // One wave per head (each head has its own latent group), four waves per
 // workgroup, one workgroup per (context split, sequence, 4 heads).  Per

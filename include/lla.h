@@ -51,7 +51,8 @@ extern "C" {
 
 #define LLA_ABI_VERSION 5   /* 2: value decoder passed as B_t^T [H][d_h][r_v]; 3: latent_fp8;
                                 4: parallel attention over whole sequences;
-                                5: lla_decode_scan_kernel_for_store */
+                                5: lla_decode_scan_kernel_for_store, lla_check_indices,
+                                hla_decode_windowed_noalloc */
 
 typedef void* lla_stream_t; /* a hipStream_t */
 
@@ -217,8 +218,9 @@ typedef struct {
 } lla_decode_args;
 
 /*
- * Reconstruct-on-read (LLA, [LLA-A] / [LLA-S]: "reconstructs loop-specific
- * K/V vectors only when attention reads them"): every latent token's key
+ * Reconstruct-on-read (LLA, [LLA-A] / [LLA-S]: the codec rebuilds a loop's
+ * keys and values from the latents at the moment attention reads them, and
+ * keeps only the latents): every latent token's key
  * k_j = A^(h) sK_j and value v_j = B^(h)T sV_j are rebuilt, then ordinary
  * attention with q' = R_i q runs over latent, window and current tokens.
  * With a baked store, A^(h) sK_j is the rotated key when A_t is
@@ -229,7 +231,8 @@ lla_status lla_decode_reconstruct(const lla_set_desc* desc, const lla_store* sto
                                   lla_stream_t stream);
 
 /*
- * Absorbed read (LLA-D, [LLA-A]: "reads latents without reconstruction";
+ * Absorbed read (LLA-D, [LLA-A]: attention reads the latents directly, with
+ * no rebuilt keys or values;
  * [HLA] Eqs. 3-4): q~ = R~_i A_t^T q, latent scores q~ . sK_j / sqrt(d_h),
  * o = B_t^T sum_lat a_j sV_j + sum_exact a_j v_j.  Any G.  Needs
  * rope_baked == 1 or rope_base == 0 (else UNSUPPORTED).
@@ -316,6 +319,23 @@ const char* lla_decode_scan_kernel(const lla_set_desc* desc, int32_t entry, int3
  * arguments (max_pos_hint < 0, max_pages_per_seq <= 0).  Host only. */
 const char* lla_decode_scan_kernel_for_store(const lla_set_desc* desc, int32_t entry, int32_t flags,
                                              int32_t max_pos_hint, int32_t max_pages_per_seq);
+
+/*
+ * Host-side check of the device-resident indices a decode or write call will
+ * use, on host copies (pos_host, block_table_host).  Kernels do not check
+ * these (out-of-range values there are undefined behaviour); a caller that
+ * wants the check runs this on copies before enqueuing, and no debug build of
+ * the kernels exists.  For every sequence b < batch: pos_host[b] >= 0 and
+ * pos_host[b] < max_pages_per_seq * page_size (the page of the current
+ * position exists), and every block-table entry of logical pages 0 ..
+ * pos_host[b] / page_size lies in [0, n_pages).  Returns LLA_OK or
+ * LLA_ERR_INVALID_ARGUMENT; never touches the GPU.
+ *   pos_host          (host) [batch] positions (decode: i; writer: any token's)
+ *   block_table_host  (host) [batch][max_pages_per_seq]
+ *   n_pages           pages in the store
+ */
+lla_status lla_check_indices(const int32_t* pos_host, int32_t batch, const int32_t* block_table_host,
+                             int32_t max_pages_per_seq, int32_t page_size, int32_t n_pages);
 
 /* Bytes one set stores per token (all groups): G*(r_k + r_v)*sizeof(dtype)
  * ([HLA] "Latent Writer": r_k + r_v (+ 2 r_1) numbers per token per layer).

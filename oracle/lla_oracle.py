@@ -32,7 +32,7 @@ Readings taken where the pages are silent (each also applies to the GPU path):
   R8  Rotary embedding, head space: pairs (f, f+d_h/2), angle p*theta_f with
       theta_f = base^(-2f/d_h), 0-based absolute positions; base 0 = none.
   R9  Latent space rotation: R~_p = I_m (x) R_p over m = r_k/d_h consecutive
-      d_h-blocks of the key latent ("m pairs per frequency").
+      d_h-blocks of the key latent (m latent pairs per rotary frequency).
   R10 Key latents are stored already rotated ("baked"), R~_p c^K, when the set
       uses rotary embedding; the reader rotates the query by R~_i.
   (R11, R15, R17, R18 concern the synthetic maps, bf16 rounding, the error

@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import oracle as O
@@ -432,3 +433,17 @@ def test_decode_workspace_holds_wide_scan_rows():
     assert w(wide, 64, 4096, 0) - w(wide, 64, 4095, 0) >= 64 * 55 * 256 * 6
     hla = desc(1, 16, 512, 128)   # one-pass matrix-core scan: nothing per token
     assert w(hla, 128, 4095, 128) < 128 * 16 * 4096 * 6
+
+
+def test_check_indices_on_host_copies():
+    """The host-side index check: positions inside the block table's reach and
+    block-table entries of the pages in use inside the store; nothing beyond
+    the current position's page is inspected."""
+    bt = np.array([[3, 0, 7, -1], [1, 2, 4, 5]], dtype=np.int32)
+    ok = B.LLA_OK
+    assert B.lla_check_indices([130, 255], bt, n_pages=8, page_size=64) == ok
+    assert B.lla_check_indices([256, 0], bt, n_pages=8, page_size=64) == B.LLA_ERR_INVALID_ARGUMENT   # past the table
+    assert B.lla_check_indices([-1, 0], bt, n_pages=8, page_size=64) == B.LLA_ERR_INVALID_ARGUMENT
+    assert B.lla_check_indices([192, 0], bt, n_pages=8, page_size=64) == B.LLA_ERR_INVALID_ARGUMENT   # page id -1
+    assert B.lla_check_indices([130, 255], bt, n_pages=7, page_size=64) == B.LLA_ERR_INVALID_ARGUMENT  # id 7 of 7
+    assert B.lla_check_indices([63, 0], bt, n_pages=4, page_size=64) == ok                           # only page 0 used
