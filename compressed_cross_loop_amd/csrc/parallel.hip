@@ -243,6 +243,11 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_par_attn(ParParams p) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       qf[qb][ks] = *reinterpret_cast<const bf16x8*>(qr + (int64_t)(qw0 + 16 * qb + col) * trow + 32 * ks + 8 * grp);
+  // q has landed before any tile load is issued: the waits inside the tile
+  // loop then count only tile loads (without this the compiler cannot tell
+  // the q fragments apart from them and waits for the prefetched tile before
+  // every score product)
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   f32x4 acc[QB][DB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb)
