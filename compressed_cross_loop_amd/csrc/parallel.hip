@@ -216,7 +216,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_par_attn(ParParams p) {
   __shared__ __attribute__((aligned(16))) bf16 vl_s[2][KT * LDV];
   __shared__ __attribute__((aligned(16))) bf16 ve_s[2][KT * LDV];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: per-wave choices are scalar branches
   const int col = lane & 15, grp = lane >> 4;
   const int H = p.H, W = p.W;
   const int nqt = p.n_pad / kAttnQT, BH = p.B * H;
