@@ -710,7 +710,7 @@ def main():
         roof = {"bound": "hbm", "achieved": scan_bytes / (scan_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = measured_traffic(w.name, kname) if st.entry_name in ("hla", "absorbed") else None
+    roof["traffic"] = measured_traffic(w.name, kname) if st.entry_name != "parallel" else None
     roof.update({"kernel": f"{kname} (" + ("every (layer, loop) call" if st.entry_name == "full" else
                                          f"set serving loops {loops_served[0]}..{loops_served[1]}") + ")",
                  "avg_launch_ms": scan_ms, "bytes_per_launch": scan_bytes, "flop_per_launch": scan_flop})
