@@ -285,7 +285,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_scan_reconstruct_gemm(DecodePar
 // latent dims every operand the step needs -- the key rows and value blocks
 // of the 256 tokens, both heads' A_t and B_t^T rows -- is copied into LDS with
 // direct global -> LDS loads (lane i's 16 bytes land at base + 16 i, one
-// 1 KiB copy per instruction), double buffered with one barrier per step.
+// 1 KiB copy per instruction), in three buffers with one barrier per step:
+// the copies run two K steps ahead of the products.
 // The four K^ (V^) waves share the latent tiles and the two token halves
 // share the decoder rows, so a latent or decoder byte crosses the load path
 // once per workgroup instead of once per wave, and every load instruction
@@ -309,7 +310,8 @@ namespace staged {
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kPageTab = 4096;      // page ids of the split, staged in LDS
+constexpr int kPageTab = 2048;      // page ids of the split, staged in LDS (with three
+                                    // 48 KiB stage buffers the workgroup takes 157 KiB)
 
 template <int DH> struct Shape {
   static constexpr int NT = DH / 16;            // column tiles per head
@@ -320,10 +322,11 @@ template <int DH> struct Shape {
   // 1 KiB copies per step, in LDS order: key pieces, value pieces, A rows of
   // both heads, B rows of both heads
   static constexpr int QV = NTT, QA = 2 * NTT, QB = 2 * NTT + 2 * NT, NQ = 2 * NTT + 4 * NT;
-  static constexpr int PER_WAVE = NQ / kWaves;
+  static constexpr int PER_WAVE = NQ / kWaves;   // copies per wave and step (< 16: vmcnt immediate)
   static constexpr int STAGE = NQ * 1024;
   static constexpr int MAXP = (NTT + kWaves - 1) / kWaves;   // store tiles per wave, at most
   static_assert(NQ % kWaves == 0 && PER_WAVE >= 2 * MAXP, "copies must divide evenly over the waves");
+  static_assert(PER_WAVE < 16, "the step wait names the copies in flight as a vmcnt immediate");
 };
 
 __device__ __forceinline__ int row_slot(int row, int c) { return 4 * row + (c ^ ((row >> 2) & 3)); }
@@ -333,7 +336,38 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr unsigned kWaitVm0 = 0x0F70;   // s_waitcnt vmcnt(0), expcnt / lgkmcnt untouched
 
-// LDS regions of the staged kernel.  The two stage buffers are separate
+// The staged kernel's copies and step barrier.
+//
+// A copy is one global_load_lds_dwordx4 (lane i's 16 bytes land at LDS
+// address m0 + 16 i), written as an asm statement so that the compiler's
+// wait insertion does not track it: it cannot tell the three stage buffers'
+// copies apart once the step loop's control flow joins, and would wait for
+// every copy in flight before each buffer read.  The kernel waits for its
+// copies itself: each wave's copies complete in issue order, so after
+// "vmcnt(n)" every copy but the wave's last n has landed, however many other
+// memory operations were issued meanwhile.  m0 is an input of the statement
+// (the compiler sets it); s_nop 0 keeps the one wait state that an SALU write
+// of m0 needs before an LDS DMA reads it.
+__device__ __forceinline__ void copy_to_lds(const bf16* src, const unsigned char* lds) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)lds;
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(m0) : "memory");
+}
+
+// Step barrier: this wave's copies of the step have landed (at most N, the
+// next step's, still in flight) and its LDS reads have returned, then all
+// waves meet.  No fence: a workgroup fence, even one on LDS alone, would
+// also wait for every copy in flight.  The asm statements keep the compiler
+// from moving memory accesses across.
+template <int N>
+__device__ __forceinline__ void step_barrier() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0070 | N);   // vmcnt(N) lgkmcnt(0), expcnt untouched
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// LDS regions of the staged kernel.  The three stage buffers are separate
 // LDS variables and every access names one of them statically: the compiler
 // then knows that copies into one buffer cannot alias reads of the other and
 // does not wait for the copies in flight before reading.
@@ -350,7 +384,8 @@ template <int DH> struct Smem {
 // at the end.
 template <int DH, int KIND>
 __device__ __forceinline__ void staged_wave(const DecodeParams& p, Smem<DH>& sm, unsigned char* stage0,
-                                            unsigned char* stage1, int b, int s, int hb, int hl,
+                                            unsigned char* stage1, unsigned char* stage2, int b, int s,
+                                            int hb, int hl,
                                             int th, int wave, int t0, int t1) {
   using Sh = Shape<DH>;
   constexpr int NT = Sh::NT, MTW = Sh::MTW, TMW = Sh::TMW, TM = Sh::TM;
@@ -410,8 +445,7 @@ __device__ __forceinline__ void staged_wave(const DecodeParams& p, Smem<DH>& sm,
         src = dect + (doff[u] + (uint32_t)ks * (DH * KC));
         slot = dslot[u];
       }
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                       (__attribute__((address_space(3))) void*)(dst + slot * 1024), 16, 0, 0);
+      copy_to_lds(src, dst + slot * 1024);
     }
   };
 
@@ -460,21 +494,27 @@ __device__ __forceinline__ void staged_wave(const DecodeParams& p, Smem<DH>& sm,
     for (int j = 0; j < MTW; ++j)
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) acc[j][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // Every tile starts in buffer 0 (K steps alternate 0, 1, 0, ..).  Buffer 0
-    // is free here: its last reader passed the previous tile's score barrier.
+    // Every tile starts in buffer 0 (K steps rotate 0, 1, 2, 0, ..).  Buffers 0
+    // and 1 are free here: their last readers passed the previous tile's
+    // score barrier.
     prep(tile);
     issue(0, stage0);
-    for (int ks = 0; ks < nks; ks += 2) {
-      __builtin_amdgcn_s_waitcnt(kWaitVm0);   // this wave's copies of step ks have landed
-      __syncthreads();                        // everyone's have; buffer 1 is free
-      if (ks + 1 < nks) issue(ks + 1, stage1);
-      compute(stage0);
-      if (ks + 1 < nks) {
-        __builtin_amdgcn_s_waitcnt(kWaitVm0);
-        __syncthreads();
-        if (ks + 2 < nks) issue(ks + 2, stage0);
-        compute(stage1);
-      }
+    if (nks > 1) issue(1, stage1);
+    // Step k: this wave's copies of step k have landed once at most those of
+    // step k + 1 are in flight; after the barrier everyone's have, and the
+    // buffer of step k - 1 (read before the barrier) takes step k + 2.
+    auto step = [&](int k, const unsigned char* cur, unsigned char* nxt) {
+      if (k + 1 < nks)
+        step_barrier<Sh::PER_WAVE>();
+      else
+        step_barrier<0>();
+      if (k + 2 < nks) issue(k + 2, nxt);
+      compute(cur);
+    };
+    for (int ks = 0; ks < nks; ks += 3) {
+      step(ks, stage0, stage2);
+      if (ks + 1 < nks) step(ks + 1, stage1, stage0);
+      if (ks + 2 < nks) step(ks + 2, stage2, stage1);
     }
 
     // ---- attention epilogue; lane holds X^[token 16 j + 4 kg + r of this half][dim 16 nt + col]
@@ -561,6 +601,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_scan_reconstruct_staged(DecodeP
   __shared__ __attribute__((aligned(1024))) Smem<DH> sm;
   __shared__ __attribute__((aligned(1024))) unsigned char stage0[Shape<DH>::STAGE];
   __shared__ __attribute__((aligned(1024))) unsigned char stage1[Shape<DH>::STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char stage2[Shape<DH>::STAGE];
   const int L = blockIdx.x;
   const int lam = (L % kXcds) * (n_wg / kXcds) + L / kXcds;
   const int grp_i = lam / (kGroupItems * n_hp), hb = (lam / kGroupItems) % n_hp;
@@ -587,9 +628,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_scan_reconstruct_staged(DecodeP
 
   const int hl = (wave >> 1) & 1, th = wave >> 2;
   if (wave & 1)
-    staged_wave<DH, 1>(p, sm, stage0, stage1, b, s, hb, hl, th, wave, t0, t1);
+    staged_wave<DH, 1>(p, sm, stage0, stage1, stage2, b, s, hb, hl, th, wave, t0, t1);
   else
-    staged_wave<DH, 0>(p, sm, stage0, stage1, b, s, hb, hl, th, wave, t0, t1);
+    staged_wave<DH, 0>(p, sm, stage0, stage1, stage2, b, s, hb, hl, th, wave, t0, t1);
 }
 
 // dect[h][ab][ks][d][k] = (ab ? B_t^T : A_t)[h][d][32 ks + k], 16 bytes per thread

@@ -255,6 +255,22 @@ def test_long_block_table(entry, form, G, r, columns, kernel):
     check(c, entry, form)
 
 
+@pytest.mark.parametrize("d_h", [96, 64])
+@pytest.mark.parametrize("columns", [2048, 2049])
+def test_reconstruct_shared_latent_long_block_table(d_h, columns):
+    """16-token pages and a block table at, and one past, the 2048 page ids
+    per split that the LDS-staged head-folded reconstruct holds: the staged
+    form, then the register-streamed one; both exact."""
+    r = 192
+    c = gen.decode_inputs(1300 + columns + d_h, batch=2, heads=5, head_dim=d_h, groups=1, r_k=r, r_v=r,
+                          positions=(150, 41), window=5, dtype="bf16", page_size=16, loop=3,
+                          loop_first=1, loop_last=8, latent_std=1.0, exact_std=1.0, paired=False,
+                          map_scale=float(np.sqrt(r / d_h)))
+    c = widen_block_table(poison_unread(c), columns)
+    assert B.lla_decode_scan_kernel_for_store(desc_of(c), 0, 150, columns) == "k_scan_reconstruct_gemm"
+    check(c, "reconstruct", "textbook")
+
+
 @pytest.mark.parametrize("H, d_h, r", [(5, 96, 192), (4, 128, 256), (3, 64, 96), (2, 96, 5280)])
 @pytest.mark.parametrize("splits", [0, 2])
 def test_reconstruct_shared_latent_shapes(H, d_h, r, splits):
