@@ -33,14 +33,17 @@ constexpr int kThreads = 256;
 // (columns n0 + 8c .. n0 + 8c + 7, c = lane % 16) and regroups them in
 // registers, so product j yields the columns {n0 + 8c + j}.  With rotary the
 // partner column n +- d_h/2 of a pair then sits in lane c ^ (d_h / 16) of the
-// same product, one lane swap away.  The sequences' rotation angles are
-// tabulated once per workgroup.
+// same product, one lane swap away.
+// Nothing waits for the operand loads before the products: the sequences'
+// rotation table is built while they are in flight (wave w takes sequences
+// w, w + 4, .. with their positions as scalar loads, lane f frequency f),
+// and q' = s R_i q for the window (first column block only) is formed after
+// the products from q values requested at entry.
 template <int DH>
 __global__ __launch_bounds__(kThreads) void k_qmap_mfma(DecodeParams p, int want_qlat) {
   constexpr int KS = DH / 32;
-  __shared__ __attribute__((aligned(16))) float csn[16][DH / 2][2];   // (cos, sin)
-  __shared__ double theta[DH / 2];
-  __shared__ int posb[16];
+  constexpr int NF = DH / 2;                // rotary frequency pairs
+  __shared__ __attribute__((aligned(16))) float csn[16][NF][2];   // (cos, sin)
   const int h = blockIdx.x, b0 = blockIdx.z * 16;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -51,7 +54,17 @@ __global__ __launch_bounds__(kThreads) void k_qmap_mfma(DecodeParams p, int want
   const int n0 = (blockIdx.y * 4 + wave) * 128;
   const bool active = want_qlat && n0 < rk;   // uniform over the wave
   const int ncol = n0 + 8 * col;
+  const bool do_qhead = blockIdx.y == 0 && p.need_qhead;
+  const int fl = min(lane, NF - 1);
 
+  // q of sequences wave + 4 k at dims fl and fl + NF (for q')
+  float qa[4], qb[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const bf16* qr = q + ((int64_t)min(b0 + wave + 4 * k, p.B - 1) * H + h) * DH;
+    qa[k] = to_f(qr[fl]);
+    qb[k] = to_f(qr[fl + NF]);
+  }
   // A^(h) rows e = 32 st + 8 grp + i, columns ncol .. ncol + 7 (clamped into
   // the row; lanes past r_k store nothing)
   bf16x8 araw[KS][8];
@@ -63,89 +76,91 @@ __global__ __launch_bounds__(kThreads) void k_qmap_mfma(DecodeParams p, int want
       for (int i = 0; i < 8; ++i)
         araw[st][i] = *reinterpret_cast<const bf16x8*>(Ah + (int64_t)(32 * st + 8 * grp + i) * rk);
   }
-  // A operand: q row of sequence b0 + col, dims 32 st + 8 grp ..
+  // A operand: q row of sequence b0 + col (rows past the batch read the last
+  // sequence and are zeroed), dims 32 st + 8 grp ..
   const int brow = b0 + col;
   bf16x8 aq[KS];
 #pragma unroll
   for (int st = 0; st < KS; ++st) {
-    if (brow < p.B) {
-      aq[st] = *reinterpret_cast<const bf16x8*>(q + ((int64_t)brow * H + h) * DH + st * 32 + grp * 8);
-    } else {
+    aq[st] = *reinterpret_cast<const bf16x8*>(q + ((int64_t)min(brow, p.B - 1) * H + h) * DH + st * 32 + grp * 8);
+    if (brow >= p.B) {
 #pragma unroll
       for (int k = 0; k < 8; ++k) aq[st][k] = static_cast<bf16>(0.f);
     }
   }
-  if (tid < 16) posb[tid] = p.pos[min(b0 + tid, p.B - 1)];
-  if (rope && tid < DH / 2) theta[tid] = rope_theta(p.rope_base, DH, tid);
-  __syncthreads();
   if (rope) {
-    for (int x = tid; x < 16 * (DH / 2); x += kThreads) {
-      const int bl = x / (DH / 2), f = x % (DH / 2);
+    const double th = rope_theta(p.rope_base, DH, fl);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int bl = wave + 4 * k;
+      const int pos = p.pos[min(b0 + bl, p.B - 1)];
       float c, sn;
-      rope_cs_theta(theta[f], posb[bl], c, sn);
-      csn[bl][f][0] = c;
-      csn[bl][f][1] = sn;
+      rope_cs_theta(th, pos, c, sn);
+      if (lane < NF) {
+        csn[bl][lane][0] = c;
+        csn[bl][lane][1] = sn;
+      }
+    }
+  }
+  __syncthreads();
+
+  if (active) {
+    f32x4 acc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < KS; ++st)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        bf16x8 bj;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) bj[i] = araw[st][i][j];
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[st], bj, acc[j], 0, 0, 0);
+      }
+    // lane: C[b0 + 4 grp + r][ncol + j]
+    bf16* ql = static_cast<bf16*>(p.qlat);
+    const bool lo_half = (8 * col) % DH < DH / 2;   // n0 is a multiple of d_h
+    const int f0 = (8 * col) % (DH / 2);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int bl = 4 * grp + r, bb = b0 + bl;
+      float v[8];
+      if (rope) {
+        const float4* cs = reinterpret_cast<const float4*>(&csn[bl][f0][0]);
+#pragma unroll
+        for (int j2 = 0; j2 < 4; ++j2) {
+          const float4 t = cs[j2];   // (cos, sin) of frequencies f0 + 2 j2, f0 + 2 j2 + 1
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int j = 2 * j2 + u;
+            const float c = u ? t.z : t.x, sn = u ? t.w : t.y;
+            const float mine = acc[j][r], other = __shfl_xor(mine, DH / 16);
+            v[j] = lo_half ? (mine * c - other * sn) : (other * sn + mine * c);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = acc[j][r];
+      }
+      if (bb < p.B && ncol < rk) {
+        bf16x8 o;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[j] = static_cast<bf16>(v[j] * p.scale);
+        *reinterpret_cast<bf16x8*>(ql + ((int64_t)bb * H + h) * rk + ncol) = o;
+      }
     }
   }
   // q' = s R_i q (head space, fp32) when a later kernel reads it
-  if (blockIdx.y == 0 && p.need_qhead) {
-    for (int x = tid; x < 16 * (DH / 2); x += kThreads) {
-      const int bl = x / (DH / 2), f = x % (DH / 2), bb = b0 + bl;
-      if (bb >= p.B) continue;
-      float c = 1.f, sn = 0.f;
-      if (rope) rope_cs_theta(theta[f], posb[bl], c, sn);
-      const bf16* qr = q + ((int64_t)bb * H + h) * DH;
-      const float a = to_f(qr[f]), b = to_f(qr[f + DH / 2]);
-      float* qh = p.qhead + ((int64_t)bb * H + h) * DH;
-      qh[f] = p.scale * (a * c - b * sn);
-      qh[f + DH / 2] = p.scale * (a * sn + b * c);
-    }
-  }
-  __syncthreads();
-  if (!active) return;
-
-  f32x4 acc[8];
+  if (do_qhead) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int st = 0; st < KS; ++st)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      bf16x8 bj;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) bj[i] = araw[st][i][j];
-      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[st], bj, acc[j], 0, 0, 0);
-    }
-  // lane: C[b0 + 4 grp + r][ncol + j]
-  bf16* ql = static_cast<bf16*>(p.qlat);
-  const bool lo_half = (8 * col) % DH < DH / 2;   // n0 is a multiple of d_h
-  const int f0 = (8 * col) % (DH / 2);
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int bl = 4 * grp + r, bb = b0 + bl;
-    float v[8];
-    if (rope) {
-      const float4* cs = reinterpret_cast<const float4*>(&csn[bl][f0][0]);
-#pragma unroll
-      for (int j2 = 0; j2 < 4; ++j2) {
-        const float4 t = cs[j2];   // (cos, sin) of frequencies f0 + 2 j2, f0 + 2 j2 + 1
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int j = 2 * j2 + u;
-          const float c = u ? t.z : t.x, sn = u ? t.w : t.y;
-          const float mine = acc[j][r], other = __shfl_xor(mine, DH / 16);
-          v[j] = lo_half ? (mine * c - other * sn) : (other * sn + mine * c);
-        }
+    for (int k = 0; k < 4; ++k) {
+      const int bl = wave + 4 * k, bb = b0 + bl;
+      if (bb < p.B && lane < NF) {
+        const float c = rope ? csn[bl][lane][0] : 1.f, sn = rope ? csn[bl][lane][1] : 0.f;
+        float* qh = p.qhead + ((int64_t)bb * H + h) * DH;
+        qh[lane] = p.scale * (qa[k] * c - qb[k] * sn);
+        qh[lane + NF] = p.scale * (qa[k] * sn + qb[k] * c);
       }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = acc[j][r];
-    }
-    if (bb < p.B && ncol < rk) {
-      bf16x8 o;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) o[j] = static_cast<bf16>(v[j] * p.scale);
-      *reinterpret_cast<bf16x8*>(ql + ((int64_t)bb * H + h) * rk + ncol) = o;
     }
   }
 }
@@ -285,7 +300,10 @@ __global__ __launch_bounds__(kThreads) void k_window_fast(DecodeParams p) {
 // are issued at entry so their latency overlaps the merge.  The fp32 latent
 // sums enter as bf16 hi + lo parts (two products), which keeps the product at
 // fp32-level accuracy.  The four waves' partial results are summed through LDS
-// and written as 16-byte rows.
+// and written as 16-byte rows.  With all 16 sequences present (large
+// batches, few splits) the first two splits' latent sums and the first two
+// window slices are requested at entry as well, so the merge barrier waits
+// for one memory round trip instead of three.
 template <int RV>
 __global__ __launch_bounds__(kThreads) void k_combine_mfma(DecodeParams p) {
   constexpr int DH = 128;
@@ -309,6 +327,42 @@ __global__ __launch_bounds__(kThreads) void k_combine_mfma(DecodeParams p) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
         bfr[u][nt] = *reinterpret_cast<const bf16x8*>(Bh + (int64_t)(16 * nt + col) * RV + 32 * st + 8 * grp);
+    }
+  }
+
+  constexpr int C4 = RV / 4;               // float4 columns of a latent sum
+  constexpr int PER = (C4 + 15) / 16;
+  const bool full16 = p.B - b0 >= 16;
+  // full16: thread -> (sequence fbl, float4 columns fk4, fk4 + 16, .., and 8
+  // window dims from fe8)
+  const int fbl = tid / 16, fk4 = tid % 16, fe8 = (tid % 16) * 8, fb = b0 + fbl;
+  f32x4 pv[2][PER], wv[2][2];
+  if (full16) {
+#pragma unroll
+    for (int ss = 0; ss < 2; ++ss) {
+      const float4* row = reinterpret_cast<const float4*>(p.part_o + (((int64_t)fb * S + min(ss, S - 1)) * H + h) * p.Dp);
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        const int cc = fk4 + 16 * u;
+        if (cc < C4) {
+          const float4 t = row[cc];
+          pv[ss][u] = f32x4{t.x, t.y, t.z, t.w};
+        } else {
+          pv[ss][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+    }
+#pragma unroll
+    for (int ss = 0; ss < 2; ++ss) {
+      if (WS > 0) {
+        const float4* src = reinterpret_cast<const float4*>(
+            p.win_o + (((int64_t)fb * WS + min(ss, WS - 1)) * H + h) * DH + fe8);
+        const float4 a = src[0], c = src[1];
+        wv[ss][0] = f32x4{a.x, a.y, a.z, a.w};
+        wv[ss][1] = f32x4{c.x, c.y, c.z, c.w};
+      } else {
+        wv[ss][0] = wv[ss][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
     }
   }
 
@@ -354,8 +408,7 @@ __global__ __launch_bounds__(kThreads) void k_combine_mfma(DecodeParams p) {
   // splits of one sequence at a time and add their sums through LDS.
   const int nb = min(16, p.B - b0);
   float* rbuf = &red[0][0][0];
-  if (nb < 16) {
-    constexpr int C4 = RV / 4;            // float4 columns
+  if (!full16) {
     constexpr int SG = kThreads / C4;     // split groups
     const int c4 = tid % C4, sg = tid / C4;
     for (int bl = 0; bl < 16; ++bl) {
@@ -414,79 +467,80 @@ __global__ __launch_bounds__(kThreads) void k_combine_mfma(DecodeParams p) {
       __syncthreads();
     }
   } else {
-    // thread -> (sequence bl, float4 columns k4, k4 + 16, ...); loads for four
-    // splits are issued together
-    constexpr int C4 = RV / 4;
-    constexpr int PER = (C4 + 15) / 16;
-    const int bl = tid / 16, k4 = tid % 16, b = b0 + bl;
+    // thread -> (sequence fbl, float4 columns fk4, fk4 + 16, ...): splits 0, 1
+    // from the registers filled at entry, the rest four at a time
     f32x4 sum[PER];
 #pragma unroll
-    for (int u = 0; u < PER; ++u) sum[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (b < p.B) {
-      for (int s0 = 0; s0 < S; s0 += 4) {
-        f32x4 v[4][PER];
+    for (int u = 0; u < PER; ++u) sum[u] = pm[fbl][0] * pv[0][u];
+    if (S > 1) {
 #pragma unroll
-        for (int ss = 0; ss < 4; ++ss) {
-          const int s = s0 + ss;
-          const float4* row = reinterpret_cast<const float4*>(
-              p.part_o + (((int64_t)b * S + min(s, S - 1)) * H + h) * p.Dp);
+      for (int u = 0; u < PER; ++u) sum[u] += pm[fbl][1] * pv[1][u];
+    }
+    for (int s0 = 2; s0 < S; s0 += 4) {
+      f32x4 v[4][PER];
 #pragma unroll
-          for (int u = 0; u < PER; ++u) {
-            const int cc = k4 + 16 * u;
-            if (s < S && cc < C4) {
-              const float4 t = row[cc];
-              v[ss][u] = f32x4{t.x, t.y, t.z, t.w};
-            } else {
-              v[ss][u] = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
+      for (int ss = 0; ss < 4; ++ss) {
+        const int s = s0 + ss;
+        const float4* row = reinterpret_cast<const float4*>(
+            p.part_o + (((int64_t)fb * S + min(s, S - 1)) * H + h) * p.Dp);
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+          const int cc = fk4 + 16 * u;
+          if (s < S && cc < C4) {
+            const float4 t = row[cc];
+            v[ss][u] = f32x4{t.x, t.y, t.z, t.w};
+          } else {
+            v[ss][u] = f32x4{0.f, 0.f, 0.f, 0.f};
           }
         }
+      }
 #pragma unroll
-        for (int ss = 0; ss < 4; ++ss) {
-          const float w = (s0 + ss < S) ? pm[bl][s0 + ss] : 0.f;
+      for (int ss = 0; ss < 4; ++ss) {
+        const float w = (s0 + ss < S) ? pm[fbl][s0 + ss] : 0.f;
 #pragma unroll
-          for (int u = 0; u < PER; ++u) sum[u] += w * v[ss][u];
-        }
+        for (int u = 0; u < PER; ++u) sum[u] += w * v[ss][u];
       }
     }
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
-      const int cc = k4 + 16 * u;
+      const int cc = fk4 + 16 * u;
       if (cc < C4) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) ob[bl][4 * cc + k] = sum[u][k];
+        for (int k = 0; k < 4; ++k) ob[fbl][4 * cc + k] = sum[u][k];
       }
     }
-  }
-  if (nb == 16) {
-    // window sums: thread -> (sequence bl, 8 consecutive dims), all slices'
-    // loads issued together (four at a time)
-    const int bl = tid / 16, e8 = (tid % 16) * 8, b = b0 + bl;
+    // window sums: slices 0, 1 from the entry registers, the rest four at a time
     f32x4 w0 = {0.f, 0.f, 0.f, 0.f}, w1 = {0.f, 0.f, 0.f, 0.f};
-    if (b < p.B) {
-      for (int s0 = 0; s0 < WS; s0 += 4) {
-        f32x4 v[4][2];
 #pragma unroll
-        for (int ss = 0; ss < 4; ++ss) {
-          const int sl = min(s0 + ss, WS - 1);
-          const float4* src = reinterpret_cast<const float4*>(
-              p.win_o + (((int64_t)b * WS + sl) * H + h) * DH + e8);
-          const float4 a = src[0], c = src[1];
-          v[ss][0] = f32x4{a.x, a.y, a.z, a.w};
-          v[ss][1] = f32x4{c.x, c.y, c.z, c.w};
-        }
+    for (int ss = 0; ss < 2; ++ss) {
+      if (ss < WS) {
+        const float w = pm[fbl][S + ss];
+        w0 += w * wv[ss][0];
+        w1 += w * wv[ss][1];
+      }
+    }
+    for (int s0 = 2; s0 < WS; s0 += 4) {
+      f32x4 v[4][2];
 #pragma unroll
-        for (int ss = 0; ss < 4; ++ss) {
-          const float w = (s0 + ss < WS) ? pm[bl][S + s0 + ss] : 0.f;
-          w0 += w * v[ss][0];
-          w1 += w * v[ss][1];
-        }
+      for (int ss = 0; ss < 4; ++ss) {
+        const int sl = min(s0 + ss, WS - 1);
+        const float4* src = reinterpret_cast<const float4*>(
+            p.win_o + (((int64_t)fb * WS + sl) * H + h) * DH + fe8);
+        const float4 a = src[0], c = src[1];
+        v[ss][0] = f32x4{a.x, a.y, a.z, a.w};
+        v[ss][1] = f32x4{c.x, c.y, c.z, c.w};
+      }
+#pragma unroll
+      for (int ss = 0; ss < 4; ++ss) {
+        const float w = (s0 + ss < WS) ? pm[fbl][S + s0 + ss] : 0.f;
+        w0 += w * v[ss][0];
+        w1 += w * v[ss][1];
       }
     }
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      wo[bl][e8 + k] = w0[k];
-      wo[bl][e8 + 4 + k] = w1[k];
+      wo[fbl][fe8 + k] = w0[k];
+      wo[fbl][fe8 + 4 + k] = w1[k];
     }
   }
   __syncthreads();

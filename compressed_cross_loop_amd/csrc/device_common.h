@@ -87,6 +87,14 @@ __device__ __forceinline__ void rope_cs(float base, int dh, int f, int pos, floa
   rope_cs_theta(rope_theta(base, dh, f), pos, c, s);
 }
 
+// Workgroup barrier ordering LDS accesses only: unlike __syncthreads(), whose
+// fence also covers global memory, it leaves the wave's global loads in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
