@@ -87,6 +87,20 @@ __device__ __forceinline__ void rope_cs(float base, int dh, int f, int pos, floa
   rope_cs_theta(rope_theta(base, dh, f), pos, c, s);
 }
 
+// One 1 KiB copy global -> LDS: global_load_lds_dwordx4, lane i's 16 bytes
+// land at LDS address lds + 16 i.  Written as an asm statement so that the
+// compiler's wait insertion does not track it (it waits conservatively for
+// every copy in flight before LDS reads it cannot prove disjoint); the caller
+// waits itself.  A wave's copies complete in issue order, so after
+// "vmcnt(n)" every copy but the wave's last n has landed, however many other
+// memory operations were issued meanwhile.  m0 is an input of the statement
+// (the compiler sets it); s_nop 0 keeps the one wait state that an SALU write
+// of m0 needs before an LDS DMA reads it.
+__device__ __forceinline__ void copy_to_lds(const void* src, const void* lds) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds;
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(m0) : "memory");
+}
+
 // Workgroup barrier ordering LDS accesses only: unlike __syncthreads(), whose
 // fence also covers global memory, it leaves the wave's global loads in flight.
 __device__ __forceinline__ void lds_barrier() {

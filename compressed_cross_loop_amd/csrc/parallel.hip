@@ -20,15 +20,14 @@
 //   k_par_attn    causal flash attention over the two key sources, one
 //                 online softmax per (position, head), exp2 domain
 //
-// k_par_attn: workgroup = (128 positions, sequence, head), four waves of 32
-// positions (two query blocks of 16), two workgroups per CU (the second
-// wave on each SIMD runs its MFMAs while the first works through its
-// softmax; a wave of 64 positions needs more than the 256 registers that
-// allows and was 1.6x slower).  Key tiles of 64 tokens are staged in
-// LDS (keys and values token-major: the exact values straight from the
-// caller's v), the next tile's global loads in flight while the current one
-// is consumed; a source is staged only when some position of the workgroup
-// reads it.  Per 16-token sub-tile and query block:
+// k_par_attn: workgroup = (256 positions, sequence, head), eight waves of 32
+// positions (two query blocks of 16), one workgroup per CU.  Key and value
+// tiles of 64 tokens are copied straight into LDS (global_load_lds, 1 KiB
+// per instruction; rows of d_h with their 16-byte chunks XOR-swizzled by row
+// against bank conflicts), double buffered: tile jt + 1's copies are in
+// flight while tile jt is read, one barrier per tile; a source is copied only
+// when some position of the workgroup reads it.  Per 16-token sub-tile and
+// query block:
 //   scores  S^T[16 tok x 16 pos] = K[16 x d_h] . Q'^T   (v_mfma_f32_16x16x32_bf16)
 //           per element: j > i masked, j < i - W from the rebuilt keys, else
 //           from the exact keys
@@ -41,6 +40,13 @@
 //           transposing read ds_read_b64_tr_b16 (inside each 16-lane group lane
 //           i receives element i % 4 of lanes i / 4, 4 + i / 4, 8 + i / 4 and
 //           12 + i / 4): two reads give a lane dim 16 db + i of its 8 tokens.
+// A wave's tiles whose keys are all latent tokens for all of its positions
+// (most of them) run a separate mask-free loop: scores start from -m so the
+// products give s - m, the lazy running-max test is an integer max3 chain on
+// the score bits, P is packed pairwise to bf16, and its row sums come from one
+// more product against ones.  Keeping that loop apart from the masked one
+// lets the value accumulators stay in place (a shared loop body made the
+// register allocator shuffle them every half-tile).
 // Workgroups are issued longest (last positions) first.
 #include "device_common.h"
 #include "gemm_nt.h"
@@ -206,15 +212,21 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_par_attn(ParParams p) {
   constexpr int QB = kAttnQB;       // query blocks of 16 per wave
   constexpr int KS = DH / 32;       // K steps of the score MFMA
   constexpr int DB = DH / 16;       // 16-dim blocks of the output
-  constexpr int LDK = DH + 8;       // LDS row of a key tile (bf16): 16-byte reads of 16 rows hit distinct banks
-  constexpr int LDV = DH + 16;      // LDS row of a value tile: the 4 rows x 32 bytes of a transposing read do
-  constexpr int CK = KT * DH / 8 / kAttnThreads;   // 16-B chunks per thread per tile and operand
-  static_assert(CK >= 1, "tile too small for the workgroup");
-  // two buffers of each staged tile: tile jt + 1 is stored while tile jt is read
-  __shared__ __attribute__((aligned(16))) bf16 kl_s[2][KT * LDK];
-  __shared__ __attribute__((aligned(16))) bf16 ke_s[2][KT * LDK];
-  __shared__ __attribute__((aligned(16))) bf16 vl_s[2][KT * LDV];
-  __shared__ __attribute__((aligned(16))) bf16 ve_s[2][KT * LDV];
+  // Tiles sit in LDS as plain [KT][d_h] rows with the 16-byte chunks of row r
+  // stored at chunk position c ^ (r % NCH), so that the 16-row key reads and
+  // the transposing value reads spread over the banks.  They are copied
+  // straight from global memory (copy_to_lds: 1 KiB per instruction, RPC rows
+  // each), the next tile's copies in flight while the current one is read.
+  constexpr int NCH = DH / 8;                 // 16-byte chunks per row
+  constexpr int RPC = 512 / DH;               // rows per 1 KiB copy
+  constexpr int NCP = KT * DH / 512;          // copies per source tile
+  constexpr int CPW = NCP / kAttnWaves;       // ... per wave
+  static_assert(NCP % kAttnWaves == 0, "tile copies must divide over the waves");
+  // two buffers of each staged tile: tile jt + 1 is copied while tile jt is read
+  __shared__ __attribute__((aligned(1024))) bf16 kl_s[2][KT * DH];
+  __shared__ __attribute__((aligned(1024))) bf16 ke_s[2][KT * DH];
+  __shared__ __attribute__((aligned(1024))) bf16 vl_s[2][KT * DH];
+  __shared__ __attribute__((aligned(1024))) bf16 ve_s[2][KT * DH];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: per-wave choices are scalar branches
@@ -255,11 +267,16 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_par_attn(ParParams p) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m[QB], l[QB];
+  f32x4 accl[QB];   // row sums of P from the no-mask halves (every entry: the position's sum)
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     m[qb] = kMinMax;
     l[qb] = 0.f;
+    accl[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = static_cast<bf16>(1.f);
 
   // a tile's sources, for the whole workgroup: rebuilt when some j of the
   // tile is below i - W for some position i <= qe, exact when some j lies in
@@ -268,64 +285,128 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_par_attn(ParParams p) {
   auto need_ex = [&](int jt) { return jt * KT + KT - 1 >= q0 - W; };
   const int ntile = qe / KT + 1;
 
-  // The next tile's keys and values wait in registers (both sources of the
-  // one to three tiles around the window edge, else the one the workgroup
-  // reads) while the current tile is consumed, and are stored into the other
-  // LDS buffer right after the barrier that ends the reads of the tile before.
-  u32x4 rkl[CK], rvl[CK], rke[CK], rve[CK];
-  // chunk c of this thread: token row j0 + idx / (DH/8) (clamped to rmax),
-  // dims 8 (idx % (DH/8)) ..
-  auto chunk = [&](const bf16* src, int j0, int c, int rmax) {
-    const int idx = tid + kAttnThreads * c;
-    return reinterpret_cast<const u32x4*>(src + (int64_t)min(j0 + idx / (DH / 8), rmax) * trow +
-                                          8 * (idx % (DH / 8)));
-  };
-  auto lds_k = [&](bf16* dst, int c) {
-    const int idx = tid + kAttnThreads * c;
-    return reinterpret_cast<u32x4*>(dst + (idx / (DH / 8)) * LDK + 8 * (idx % (DH / 8)));
-  };
-  auto lds_v = [&](bf16* dst, int c) {
-    const int idx = tid + kAttnThreads * c;
-    return reinterpret_cast<u32x4*>(dst + (idx / (DH / 8)) * LDV + 8 * (idx % (DH / 8)));
-  };
+  // this lane's row and source chunk in copy q of the wave (copy wave + 8 q)
+  int crow[CPW], cchunk[CPW];
+#pragma unroll
+  for (int q = 0; q < CPW; ++q) {
+    crow[q] = (wave + kAttnWaves * q) * RPC + lane / NCH;
+    cchunk[q] = (lane % NCH) ^ (crow[q] % NCH);
+  }
   // rows past the sequence are never read by a valid position; the caller's
   // v has n_max rows only, so its rows are clamped to n - 1
-  auto load_tile = [&](int jt) {
+  auto copy_source = [&](const bf16* src, int j0, int rmax, bf16* dst) {
+#pragma unroll
+    for (int q = 0; q < CPW; ++q)
+      copy_to_lds(src + (int64_t)min(j0 + crow[q], rmax) * trow + 8 * cchunk[q],
+                  dst + (wave + kAttnWaves * q) * 512);
+  };
+  auto issue_tile = [&](int jt, int buf) {
     const int j0 = jt * KT;
     if (need_lat(jt)) {
-#pragma unroll
-      for (int c = 0; c < CK; ++c) {
-        rkl[c] = *chunk(kh, j0, c, p.n_pad - 1);
-        rvl[c] = *chunk(vh, j0, c, p.n_pad - 1);
-      }
+      copy_source(kh, j0, p.n_pad - 1, kl_s[buf]);
+      copy_source(vh, j0, p.n_pad - 1, vl_s[buf]);
     }
     if (need_ex(jt)) {
-#pragma unroll
-      for (int c = 0; c < CK; ++c) {
-        rke[c] = *chunk(kr, j0, c, p.n_pad - 1);
-        rve[c] = *chunk(vx, j0, c, n - 1);
-      }
+      copy_source(kr, j0, p.n_pad - 1, ke_s[buf]);
+      copy_source(vx, j0, n - 1, ve_s[buf]);
     }
   };
-  auto store_tile = [&](int jt, int buf) {
-    if (need_lat(jt)) {
-#pragma unroll
-      for (int c = 0; c < CK; ++c) {
-        *lds_k(kl_s[buf], c) = rkl[c];
-        *lds_v(vl_s[buf], c) = rvl[c];
-      }
-    }
-    if (need_ex(jt)) {
-#pragma unroll
-      for (int c = 0; c < CK; ++c) {
-        *lds_k(ke_s[buf], c) = rke[c];
-        *lds_v(ve_s[buf], c) = rve[c];
-      }
-    }
+  // key row 16 ts + col, chunk 4 ks + grp (the row's swizzle is col % NCH)
+  auto key_frag = [&](const bf16* kt_s, int ts, int ks) {
+    return *reinterpret_cast<const bf16x8*>(&kt_s[(16 * ts + col) * DH + 8 * ((4 * ks + grp) ^ (col % NCH))]);
+  };
+  // V^T[dims 16 db ..][tokens of half u] as the value MFMA's A operand: lane
+  // (col, grp) needs dim 16 db + col of tokens 32 u + 4 grp + e and
+  // 32 u + 16 + 4 grp + e (e < 4); each transposing read takes 4 token rows x
+  // 4 dims per lane group and hands lane i its dim i.  Rows r and r + 16 share
+  // their chunk swizzle.
+  auto value_frag = [&](const bf16* vt_s, int u, int db) {
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const int r = 32 * u + 4 * grp + (col >> 2);
+    const int c = 2 * db + ((col & 3) >> 1);
+    const bf16* base = vt_s + r * DH + 8 * (c ^ (r % NCH)) + 4 * (col & 1);
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)base);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + 16 * DH));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
 
   // one tile: two halves of 32 keys (sub-tiles 2u, 2u+1), each scored,
   // folded into the online softmax and multiplied into the values in turn
+  // A tile whose keys are all latent tokens for every position of the wave
+  // (the common case, away from the window edge): no masks.  The score
+  // products start from -m, so they yield s - m directly; the lazy-max test
+  // reads the scores' bits as signed integers (for a positive threshold
+  // x > k exactly when int(x) > int(k)), which needs no float
+  // canonicalisation; the row sums of P come from one more product against
+  // ones.  Runs only once every position's running maximum is a real score.
+  auto fast_tile = [&](int jt, int buf) {
+    const bf16* KL = kl_s[buf];
+    const bf16* VL = vl_s[buf];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      f32x4 sc[2][QB];
+
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const float nm = -m[qb];
+#pragma unroll
+          for (int hs = 0; hs < 2; ++hs) sc[hs][qb] = f32x4{nm, nm, nm, nm};
+        }
+#pragma unroll
+        for (int hs = 0; hs < 2; ++hs) {
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 kf = key_frag(KL, 2 * u + hs, ks);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+              sc[hs][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qb][ks], sc[hs][qb], 0, 0, 0);
+          }
+        }
+        bf16x8 pf[QB];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const int b0i = max(max(__float_as_int(sc[0][qb][0]), __float_as_int(sc[0][qb][1])),
+                              __float_as_int(sc[0][qb][2]));
+          const int b1i = max(max(__float_as_int(sc[0][qb][3]), __float_as_int(sc[1][qb][0])),
+                              __float_as_int(sc[1][qb][1]));
+          const int b2i = max(max(__float_as_int(sc[1][qb][2]), __float_as_int(sc[1][qb][3])), b0i);
+          if (__any(max(b1i, b2i) > __float_as_int(kLazy))) {
+            float lmx = -INFINITY;
+#pragma unroll
+            for (int hs = 0; hs < 2; ++hs)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) lmx = fmaxf(lmx, sc[hs][qb][r]);
+            float mx = fmaxf(lmx, __shfl_xor(lmx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float d = mx > kLazy ? mx : 0.f;   // the position's maximum moves up by d
+            const float alpha = fast_exp2(-d);
+            m[qb] += d;
+            l[qb] *= alpha;
+            accl[qb] *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) acc[qb][db] *= alpha;
+#pragma unroll
+            for (int hs = 0; hs < 2; ++hs)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) sc[hs][qb][r] -= d;
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pf[qb][e] = static_cast<bf16>(fast_exp2(sc[e / 4][qb][e % 4]));
+        }
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const bf16x8 vf = value_frag(VL, u, db);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            acc[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[qb], acc[qb][db], 0, 0, 0);
+        }
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) accl[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[qb], accl[qb], 0, 0, 0);
+    }
+  };
+
+  // general tile (masks): tiles near the window edge or the diagonal, and a
+  // wave's first tile
   auto compute = [&](int jt, int buf) {
     const int j0 = jt * KT;
     const bf16* KL = kl_s[buf];
@@ -335,25 +416,11 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_par_attn(ParParams p) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       f32x4 sc[2][QB];
-      // every key of the half is a latent token for every position of the
-      // wave (the common case, away from the window edge): no masks
-      const bool pure = j0 + 32 * u + 31 < qw0 - W;
-      bool lat_u = pure, ex_u = false;
-      if (pure) {
-#pragma unroll
-        for (int hs = 0; hs < 2; ++hs) {
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) sc[hs][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8 kf =
-                *reinterpret_cast<const bf16x8*>(&KL[(16 * (2 * u + hs) + col) * LDK + 32 * ks + 8 * grp]);
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
-              sc[hs][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qb][ks], sc[hs][qb], 0, 0, 0);
-          }
-        }
-      } else {
+
+      // general path (masks): halves near the window edge or the diagonal,
+      // and a wave's first half
+      bool lat_u = false, ex_u = false;
+      {
 #pragma unroll
       for (int hs = 0; hs < 2; ++hs) {
         const int ts = 2 * u + hs;
@@ -373,7 +440,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_par_attn(ParParams p) {
           for (int qb = 0; qb < QB; ++qb) sl[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&KL[(16 * ts + col) * LDK + 32 * ks + 8 * grp]);
+            const bf16x8 kf = key_frag(KL, ts, ks);
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb)
               sl[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qb][ks], sl[qb], 0, 0, 0);
@@ -390,7 +457,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_par_attn(ParParams p) {
           for (int qb = 0; qb < QB; ++qb) se[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&KE[(16 * ts + col) * LDK + 32 * ks + 8 * grp]);
+            const bf16x8 kf = key_frag(KE, ts, ks);
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb)
               se[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qb][ks], se[qb], 0, 0, 0);
@@ -425,6 +492,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_par_attn(ParParams p) {
           const float alpha = fast_exp2(m[qb] - mn);
           m[qb] = mn;
           l[qb] *= alpha;
+          accl[qb] *= alpha;
 #pragma unroll
           for (int db = 0; db < DB; ++db) acc[qb][db] *= alpha;
         }
@@ -447,34 +515,21 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_par_attn(ParParams p) {
       // lane (col, grp) needs dim 16 db + col of tokens 32 u + 4 grp + e and
       // 32 u + 16 + 4 grp + e (e < 4); each transposing read takes 4 token
       // rows x 4 dims per lane group and hands lane i its dim i
-      auto v_operand = [&](const bf16* vt_s, int db) {
-        typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-        const bf16* base = vt_s + (32 * u + 4 * grp + (col >> 2)) * LDV + 16 * db + 4 * (col & 3);
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)base);
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + 16 * LDV));
-        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      };
+      auto v_operand = [&](const bf16* vt_s, int db) { return value_frag(vt_s, u, db); };
       auto p_part = [&](int qb, bool latent) {
         const int i = qw0 + 16 * qb + col;
         bf16x8 pp;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int j = j0 + 16 * (2 * u + e / 4) + 4 * grp + e % 4;
-          pp[e] = static_cast<bf16>((pure || (j < i - W) == latent) ? sc[e / 4][qb][e % 4] : 0.f);
+          pp[e] = static_cast<bf16>((j < i - W) == latent ? sc[e / 4][qb][e % 4] : 0.f);
         }
         return pp;
       };
       if (lat_u) {
         bf16x8 pl[QB];
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          if (pure) {   // every key of the half is a latent token for every position
-#pragma unroll
-            for (int e = 0; e < 8; ++e) pl[qb][e] = static_cast<bf16>(sc[e / 4][qb][e % 4]);
-          } else {
-            pl[qb] = p_part(qb, true);
-          }
-        }
+        for (int qb = 0; qb < QB; ++qb) pl[qb] = p_part(qb, true);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
           const bf16x8 vf = v_operand(VL, db);
@@ -498,14 +553,31 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_par_attn(ParParams p) {
     }
   };
 
-  load_tile(0);
-  store_tile(0, 0);
-  if (ntile > 1) load_tile(1);
-  for (int jt = 0; jt < ntile; ++jt) {
-    // tile jt is in LDS, and every wave is done with tile jt - 1's buffer
+  // Every tile starts with the same step: this wave's copies of tile jt have
+  // landed; after the barrier everyone's have, and every wave is done with
+  // tile jt - 1's buffer, which takes tile jt + 1.  Each wave passes one
+  // barrier per tile, in whichever of the loops below it is.
+  auto tile_start = [&](int jt) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     __syncthreads();
-    if (jt + 1 < ntile) store_tile(jt + 1, (jt + 1) & 1);
-    if (jt + 2 < ntile) load_tile(jt + 2);
+    if (jt + 1 < ntile) issue_tile(jt + 1, (jt + 1) & 1);
+  };
+  // tiles 1 .. jp - 1 are all latent for every position of the wave and run
+  // the mask-free loop (tile 0 sets the running maxima first)
+  const int jp = wave_on ? min(ntile, max(0, (qw0 - W) / KT)) : 0;
+  issue_tile(0, 0);
+  int jt = 0;
+  if (ntile > 0) {
+    tile_start(0);
+    if (wave_on) compute(0, 0);
+    jt = 1;
+  }
+  for (; jt < jp; ++jt) {
+    tile_start(jt);
+    fast_tile(jt, jt & 1);
+  }
+  for (; jt < ntile; ++jt) {
+    tile_start(jt);
     // a wave whose positions all precede the tile has nothing to add
     if (wave_on && jt * KT <= qw1) compute(jt, jt & 1);
   }
@@ -517,6 +589,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_par_attn(ParParams p) {
     float lt = l[qb];
     lt += __shfl_xor(lt, 16);
     lt += __shfl_xor(lt, 32);
+    lt += accl[qb][0];
     const int i = qw0 + 16 * qb + col;
     if (i > qe) continue;
     const float inv = 1.f / lt;

@@ -336,23 +336,10 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr unsigned kWaitVm0 = 0x0F70;   // s_waitcnt vmcnt(0), expcnt / lgkmcnt untouched
 
-// The staged kernel's copies and step barrier.
+// The staged kernel's copies (copy_to_lds) are not tracked by the compiler's
+// wait insertion, which cannot tell the three stage buffers' copies apart
+// once the step loop's control flow joins; the kernel waits for them itself.
 //
-// A copy is one global_load_lds_dwordx4 (lane i's 16 bytes land at LDS
-// address m0 + 16 i), written as an asm statement so that the compiler's
-// wait insertion does not track it: it cannot tell the three stage buffers'
-// copies apart once the step loop's control flow joins, and would wait for
-// every copy in flight before each buffer read.  The kernel waits for its
-// copies itself: each wave's copies complete in issue order, so after
-// "vmcnt(n)" every copy but the wave's last n has landed, however many other
-// memory operations were issued meanwhile.  m0 is an input of the statement
-// (the compiler sets it); s_nop 0 keeps the one wait state that an SALU write
-// of m0 needs before an LDS DMA reads it.
-__device__ __forceinline__ void copy_to_lds(const bf16* src, const unsigned char* lds) {
-  const uint32_t m0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)lds;
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(m0) : "memory");
-}
-
 // Step barrier: this wave's copies of the step have landed (at most N, the
 // next step's, still in flight) and its LDS reads have returned, then all
 // waves meet.  No fence: a workgroup fence, even one on LDS alone, would
