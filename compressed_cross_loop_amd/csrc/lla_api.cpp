@@ -19,6 +19,7 @@ constexpr int kMaxHeadDim = 256;
 constexpr int kMaxLatent = 16384;     // r_k + r_v limit of the general kernels
 constexpr int kMaxWindow = 8192;
 constexpr int kTargetWorkgroups = 256;  // one per compute unit on MI355X (256 CUs)
+constexpr int kLongSplit = 768;         // tokens per split above which the absorbed scan fills every CU
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -195,14 +196,22 @@ Plan plan_for(const lla_set_desc& d, int batch, int max_pos, int window, int spl
       if (pl.S <= kMaxFusedSplits) return pl;
       return make_plan(batch, max_pos, window, kMaxFusedSplits, wgs, target, kChunk);
     }
-    case Scan::kAbsorbedMfma:
-      // three quarters of a workgroup per CU (measured at 16k context and batch
-      // 32: 6 splits 202 us, 8 splits 207 us, 12 splits 242 us per call; batch
-      // 128 at 4k keeps its 2 splits); the matrix-core combine merges at most
-      // kCombineMaxParts splits + window slices (one window slice per split
-      // when the scan takes the window along)
+    case Scan::kAbsorbedMfma: {
+      // One workgroup per CU when that still leaves a split at least
+      // kLongSplit tokens (the launch then keeps every CU busy and loads its
+      // tiles as streaming), else three quarters of one per CU with cached
+      // loads.  Measured per call at the HLA shapes, 192 against 256
+      // workgroups: batch 32 at 16k 198.7 / 189.1 us, batch 64 at 4k 120.6 /
+      // 111.5 us, batch 32 at 4k 68.7 / 68.1 us, batch 16 at 4k 45.6 / 47.1 us;
+      // batch 128 at 4k takes 2 splits either way.  The matrix-core combine
+      // merges at most kCombineMaxParts splits + window slices (one window
+      // slice per split when the scan takes the window along).
+      const Plan full = make_plan(batch, max_pos, window, splits, d.groups, kTargetWorkgroups, kChunk,
+                                  kCombineMaxParts / 2);
+      if (splits > 0 || full.chunk >= kLongSplit) return full;
       return make_plan(batch, max_pos, window, splits, d.groups, 3 * kTargetWorkgroups / 4, kChunk,
                        kCombineMaxParts / 2);
+    }
     case Scan::kAbsorbedWide:
       // the value pass runs one workgroup per (256-dim slab, split, sequence)
       return make_plan(batch, max_pos, window, splits, scan_absorbed_wide_slabs(d.r_v), target, kChunk,

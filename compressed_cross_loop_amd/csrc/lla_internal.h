@@ -164,6 +164,9 @@ bool qmap_mfma_supports(const DecodeParams& p);
 hipError_t launch_qmap_mfma(const DecodeParams& p, bool want_qlat, hipStream_t s);
 bool window_fast_supports(const DecodeParams& p);
 hipError_t launch_window_fast(const DecodeParams& p, hipStream_t s);
+// a launch of at least this many workgroups keeps every CU of MI355X busy;
+// the latent scans then load their tiles as streaming (load_once)
+constexpr int kStreamWorkgroups = 256;
 constexpr int kCombineMaxParts = 160;   // splits + window slices the matrix-core combine merges
 bool combine_mfma_supports(const DecodeParams& p);
 hipError_t launch_combine_mfma(const DecodeParams& p, hipStream_t s);

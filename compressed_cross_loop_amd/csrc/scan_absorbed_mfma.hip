@@ -65,18 +65,18 @@ template <int RK> struct Pipe8 { static constexpr int keys = 4, values = 4, unro
 template <> struct Pipe8<256> { static constexpr int keys = 4, values = 2, unroll = 4; };
 template <> struct Pipe8<512> { static constexpr int keys = 2, values = 1, unroll = 2; };
 
-template <int RK>
+template <int RK, bool NT>
 __device__ __forceinline__ void load_keys(bf16x8 (&k)[RK / 32], const char* tile_b, int col, int grp) {
   const bf16* kp = reinterpret_cast<const bf16*>(tile_b) + col * RK + grp * 8;
 #pragma unroll
-  for (int st = 0; st < RK / 32; ++st) k[st] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(kp + st * 32));
+  for (int st = 0; st < RK / 32; ++st) k[st] = load_once<NT>(reinterpret_cast<const bf16x8*>(kp + st * 32));
 }
 
-template <int RK, int RV>
+template <int RK, int RV, bool NT>
 __device__ __forceinline__ void load_values(s16x4 (&v)[RV / 16], const char* tile_b, int col, int grp) {
   const bf16* vp = reinterpret_cast<const bf16*>(tile_b) + 16 * RK + col * 16 + grp * 4;
 #pragma unroll
-  for (int vt = 0; vt < RV / 16; ++vt) v[vt] = __builtin_nontemporal_load(reinterpret_cast<const s16x4*>(vp + vt * 256));
+  for (int vt = 0; vt < RV / 16; ++vt) v[vt] = load_once<NT>(reinterpret_cast<const s16x4*>(vp + vt * 256));
 }
 
 __device__ __forceinline__ short bf16_bits(float x) {
@@ -169,20 +169,20 @@ template <int RV> struct Vals8 {
   f32x4 s;   // value scales of tokens 4 grp .. 4 grp + 3
 };
 
-template <int RK, int RV>
+template <int RK, int RV, bool NT>
 __device__ __forceinline__ void load_keys8(Keys8<RK>& k, const char* tile, int col, int grp) {
   const char* kp = tile + col * RK + grp * 16;
 #pragma unroll
-  for (int u = 0; u < RK / 64; ++u) k.v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + u * 64));
-  k.s = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(tile + 16 * (RK + RV) + 16 * grp));
+  for (int u = 0; u < RK / 64; ++u) k.v[u] = load_once<NT>(reinterpret_cast<const u32x4*>(kp + u * 64));
+  k.s = load_once<NT>(reinterpret_cast<const f32x4*>(tile + 16 * (RK + RV) + 16 * grp));
 }
 
-template <int RK, int RV>
+template <int RK, int RV, bool NT>
 __device__ __forceinline__ void load_values8(Vals8<RV>& v, const char* tile, int col, int grp) {
   const char* vp = tile + 16 * RK + col * 64 + grp * 16;
 #pragma unroll
-  for (int q = 0; q < RV / 64; ++q) v.v[q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp + q * 1024));
-  v.s = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(tile + 16 * (RK + RV) + 64 + 16 * grp));
+  for (int q = 0; q < RV / 64; ++q) v.v[q] = load_once<NT>(reinterpret_cast<const u32x4*>(vp + q * 1024));
+  v.s = load_once<NT>(reinterpret_cast<const f32x4*>(tile + 16 * (RK + RV) + 64 + 16 * grp));
 }
 
 // two bf16 from the e4m3 codes in bytes (2 hi, 2 hi + 1) of w
@@ -238,6 +238,7 @@ __device__ __forceinline__ void tile_values8(const Vals8<RV>& v, s16x4 pb, f32x4
 // per-head online softmax, partial (m, l, o) in head space.  The slice that
 // holds the current token also appends R_i k_cur, v_cur to the ring.
 // cs[f] = (cos, sin) of i * theta_f.
+template <bool NT>
 __device__ void window_slice(const DecodeParams& p, int b, int slice, int g, const float (*cs)[2]) {
   const int DH = p.dh, TPH = DH / 8, H = p.H, W = p.W;
   const int tid = threadIdx.x;
@@ -293,8 +294,8 @@ __device__ void window_slice(const DecodeParams& p, int b, int slice, int g, con
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t off = base + slot_of(tb + u) * rs;
-      kr[u] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(ring_k + off));
-      vr[u] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(ring_v + off));
+      kr[u] = load_once<NT>(reinterpret_cast<const bf16x8*>(ring_k + off));
+      vr[u] = load_once<NT>(reinterpret_cast<const bf16x8*>(ring_v + off));
     }
   };
   // one batch: U independent score reductions, one max, then the weighted
@@ -372,7 +373,7 @@ __device__ void window_slice(const DecodeParams& p, int b, int slice, int g, con
   }
 }
 
-template <int RK, int RV, bool F8>
+template <int RK, int RV, bool F8, bool NT>
 __global__ __launch_bounds__(kThreads, 1) void k_scan_absorbed_mfma(DecodeParams p) {
   const int s = blockIdx.x, b = blockIdx.y, g = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -439,21 +440,21 @@ __global__ __launch_bounds__(kThreads, 1) void k_scan_absorbed_mfma(DecodeParams
     int ti = wave;
     if (ti < ntiles) {
 #pragma unroll
-      for (int u = 0; u < NK; ++u) load_keys<RK>(kb[u], tile_ptr(min(ti + u * kWaves, ntiles - 1)), col, grp);
+      for (int u = 0; u < NK; ++u) load_keys<RK, NT>(kb[u], tile_ptr(min(ti + u * kWaves, ntiles - 1)), col, grp);
 #pragma unroll
       for (int u = 0; u < NV; ++u)
-        load_values<RK, RV>(vb[u], tile_ptr(min(ti + u * kWaves, ntiles - 1)), col, grp);
+        load_values<RK, RV, NT>(vb[u], tile_ptr(min(ti + u * kWaves, ntiles - 1)), col, grp);
     }
     while (ti < ntiles) {
 #pragma unroll
       for (int u = 0; u < UN; ++u) {
         const f32x4 sc = tile_scores<RK>(kb[u % NK], qrow);
         __builtin_amdgcn_sched_barrier(0);   // keep each refill below its consumer
-        load_keys<RK>(kb[u % NK], tile_ptr(min(ti + NK * kWaves, ntiles - 1)), col, grp);
+        load_keys<RK, NT>(kb[u % NK], tile_ptr(min(ti + NK * kWaves, ntiles - 1)), col, grp);
         const s16x4 pb = tile_softmax<RV>(sc, acc, m, lsum, tile_valid(ti), grp);
         tile_values<RV>(vb[u % NV], pb, acc, tile_valid(ti), grp);
         __builtin_amdgcn_sched_barrier(0);
-        load_values<RK, RV>(vb[u % NV], tile_ptr(min(ti + NV * kWaves, ntiles - 1)), col, grp);
+        load_values<RK, RV, NT>(vb[u % NV], tile_ptr(min(ti + NV * kWaves, ntiles - 1)), col, grp);
         ti += kWaves;
         if (ti >= ntiles) break;
       }
@@ -467,10 +468,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_scan_absorbed_mfma(DecodeParams
     if (ti < ntiles) {
 #pragma unroll
       for (int u = 0; u < NK; ++u)
-        load_keys8<RK, RV>(kb[u], tile_ptr(min(ti + u * kWaves, ntiles - 1)), col, grp);
+        load_keys8<RK, RV, NT>(kb[u], tile_ptr(min(ti + u * kWaves, ntiles - 1)), col, grp);
 #pragma unroll
       for (int u = 0; u < NV; ++u)
-        load_values8<RK, RV>(vb[u], tile_ptr(min(ti + u * kWaves, ntiles - 1)), col, grp);
+        load_values8<RK, RV, NT>(vb[u], tile_ptr(min(ti + u * kWaves, ntiles - 1)), col, grp);
     }
     while (ti < ntiles) {
 #pragma unroll
@@ -478,11 +479,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_scan_absorbed_mfma(DecodeParams
         f32x4 sc = tile_scores8<RK, RV>(kb[u % NK], qcol, grp);
         __builtin_amdgcn_sched_barrier(0);
         const f32x4 vs = vb[u % NV].s;
-        load_keys8<RK, RV>(kb[u % NK], tile_ptr(min(ti + NK * kWaves, ntiles - 1)), col, grp);
+        load_keys8<RK, RV, NT>(kb[u % NK], tile_ptr(min(ti + NK * kWaves, ntiles - 1)), col, grp);
         const s16x4 pb = tile_softmax<RV, true>(sc, acc, m, lsum, tile_valid(ti), grp, vs);
         tile_values8<RV>(vb[u % NV], pb, acc, tile_valid(ti), grp);
         __builtin_amdgcn_sched_barrier(0);
-        load_values8<RK, RV>(vb[u % NV], tile_ptr(min(ti + NV * kWaves, ntiles - 1)), col, grp);
+        load_values8<RK, RV, NT>(vb[u % NV], tile_ptr(min(ti + NV * kWaves, ntiles - 1)), col, grp);
         ti += kWaves;
         if (ti >= ntiles) break;
       }
@@ -501,7 +502,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_scan_absorbed_mfma(DecodeParams
       cs[tid][1] = sn;
     }
     __syncthreads();
-    window_slice(p, b, s, g, cs);
+    window_slice<NT>(p, b, s, g, cs);
   }
 
   // ---- merge the four waves (fixed order) and write the split's partial
@@ -544,17 +545,24 @@ __global__ __launch_bounds__(kThreads, 1) void k_scan_absorbed_mfma(DecodeParams
   }
 }
 
-template <int RK, int RV>
-hipError_t launch_rk(const DecodeParams& p, hipStream_t st) {
+template <int RK, int RV, bool NT>
+hipError_t launch_rk_nt(const DecodeParams& p, hipStream_t st) {
   if (p.fp8) {
     if constexpr (RK % 64 == 0)
-      hipLaunchKernelGGL((k_scan_absorbed_mfma<RK, RV, true>), dim3(p.S, p.B, p.G), dim3(kThreads), 0, st, p);
+      hipLaunchKernelGGL((k_scan_absorbed_mfma<RK, RV, true, NT>), dim3(p.S, p.B, p.G), dim3(kThreads), 0, st, p);
     else
       return hipErrorNotSupported;
   } else {
-    hipLaunchKernelGGL((k_scan_absorbed_mfma<RK, RV, false>), dim3(p.S, p.B, p.G), dim3(kThreads), 0, st, p);
+    hipLaunchKernelGGL((k_scan_absorbed_mfma<RK, RV, false, NT>), dim3(p.S, p.B, p.G), dim3(kThreads), 0, st, p);
   }
   return hipGetLastError();
+}
+
+// streaming loads when the launch keeps every CU busy (load_once)
+template <int RK, int RV>
+hipError_t launch_rk(const DecodeParams& p, hipStream_t st) {
+  if ((int64_t)p.S * p.B * p.G >= kStreamWorkgroups) return launch_rk_nt<RK, RV, true>(p, st);
+  return launch_rk_nt<RK, RV, false>(p, st);
 }
 
 }  // namespace
