@@ -56,6 +56,8 @@ Readings taken where the pages are silent (each also applies to the GPU path):
 import numpy as np
 
 TILE = 16  # tokens per tile in the paged store layout
+WIDE_KEY_ROWS = 512  # key rows wider than this are stored in chunks of KEY_CHUNK dimensions
+KEY_CHUNK = 32
 
 
 # ----------------------------------------------------------------------------
@@ -101,11 +103,19 @@ def store_key_offset(page, group, slot, dim, *, groups, page_size, r_k, r_v):
     """Flat element offset of key-latent element `dim` of the token in `slot`
     of physical page `page`, group `group`.  A page holds, for each group, P
     tokens as P/16 tiles; a tile is 16 token rows of r_k key numbers followed
-    by the value block (see store_value_offset)."""
+    by the value block (see store_value_offset).  Key rows wider than
+    WIDE_KEY_ROWS numbers are kept chunk-major instead: chunk c (dimensions
+    32c .. 32c + 31, the last one narrower when r_k is not a multiple of 32)
+    holds the 16 tokens' pieces one after another, so that a 16-token x
+    32-dimension block is contiguous."""
     R = r_k + r_v
     page, group, slot, dim = (np.asarray(a, dtype=np.int64) for a in (page, group, slot, dim))
     base = (page * groups + group) * page_size * R + (slot // TILE) * TILE * R
-    return base + (slot % TILE) * r_k + dim
+    if r_k <= WIDE_KEY_ROWS:
+        return base + (slot % TILE) * r_k + dim
+    c = dim // KEY_CHUNK
+    width = np.minimum(KEY_CHUNK, r_k - KEY_CHUNK * c)
+    return base + c * (TILE * KEY_CHUNK) + (slot % TILE) * width + dim % KEY_CHUNK
 
 
 def store_value_offset(page, group, slot, dim, *, groups, page_size, r_k, r_v):

@@ -113,6 +113,10 @@ def test_dense_decoder_does_not_commute():
 def test_store_layout_fixture():
     kw = dict(groups=2, page_size=32, r_k=16, r_v=32)
     for line in golden_lines("store_layout.txt"):
+        if line.startswith("params"):
+            g_, p_, rk_, rv_ = (int(x) for x in line.split()[1:])
+            kw = dict(groups=g_, page_size=p_, r_k=rk_, r_v=rv_)
+            continue
         lhs, want = line.split(":")
         kind, page, group, slot, dim = lhs.split()
         fn = O.store_key_offset if kind == "key" else O.store_value_offset
@@ -128,6 +132,27 @@ def test_store_layout_is_a_bijection():
     vo = O.store_value_offset(p[..., None], g[..., None], s[..., None], np.arange(16), **kw)
     allo = np.concatenate([ko.ravel(), vo.ravel()])
     assert np.array_equal(np.sort(allo), np.arange(n_pages * 3 * 48 * R))
+
+
+@pytest.mark.parametrize("r_k, r_v", [(544, 16), (528, 48)])
+def test_wide_key_layout_is_a_bijection(r_k, r_v):
+    """Chunk-major wide key rows still tile the store exactly once."""
+    kw = dict(groups=2, page_size=32, r_k=r_k, r_v=r_v)
+    n_pages = 2
+    p, g, s = np.meshgrid(np.arange(n_pages), np.arange(2), np.arange(32), indexing="ij")
+    ko = O.store_key_offset(p[..., None], g[..., None], s[..., None], np.arange(r_k), **kw)
+    vo = O.store_value_offset(p[..., None], g[..., None], s[..., None], np.arange(r_v), **kw)
+    allo = np.concatenate([ko.ravel(), vo.ravel()])
+    assert np.array_equal(np.sort(allo), np.arange(n_pages * 2 * 32 * (r_k + r_v)))
+
+
+def test_wide_key_chunk_is_contiguous():
+    """The 16 tokens x 32 dimensions of one key chunk of a tile are one
+    contiguous run of 512 elements (what the wide readers rely on)."""
+    kw = dict(groups=1, page_size=16, r_k=1024, r_v=32)
+    s, d = np.meshgrid(np.arange(16), np.arange(64, 96), indexing="ij")
+    o = np.sort(O.store_key_offset(0, 0, s, d, **kw).ravel())
+    assert np.array_equal(o, np.arange(o[0], o[0] + 512)) and o[0] == 2 * 512
 
 
 def test_gather_follows_block_table():
