@@ -176,7 +176,9 @@ __global__ __launch_bounds__(kThreads) void k_fused_decode(DecodeParams p) {
     // every key row and value row of the tile requested before any is used
     float kk[kTile][DK];
 #pragma unroll
-    for (int t = 0; t < kTile; ++t) load_bf16<DK>(tile + t * R + lane * DK, kk[t]);
+    // key row t, dims lane DK .. (wide rows are chunk-major; DK <= 16 dims
+    // never cross a 32-dim chunk)
+    for (int t = 0; t < kTile; ++t) load_bf16<DK>(tile + key_in_tile(t, lane * DK, R), kk[t]);
     // values: dimension d of the tile sits in sub-block d/16, row d%16, 16 tokens contiguous
     const bf16* vb = tile + kTile * R;
     float vv[DK][kTile];

@@ -206,8 +206,8 @@ __global__ __launch_bounds__(kThreads) void k_scan_absorbed_generic(DecodeParams
         const uint8_t* kr = bytes + key_off8(pg[t], g, slot, 0, G, P, rk, rv);
         for (int k = lane; k < rk; k += 64) acc += ql[k] * e4m3_to_f(kr[k]);
       } else {
-        const T* kr = pages + key_off(pg[t], g, slot, 0, G, P, R, rk);
-        for (int k = lane; k < rk; k += 64) acc += ql[k] * to_f(kr[k]);
+        const T* kt = pages + tile_base(pg[t], g, slot, G, P, R);
+        for (int k = lane; k < rk; k += 64) acc += ql[k] * to_f(kt[key_in_tile(slot & 15, k, rk)]);
       }
       acc = wave_sum(acc);
       if (lane == 0) sc[t] = p.fp8 ? acc * kscale[t] : acc;

@@ -20,9 +20,22 @@ template <> __device__ __forceinline__ bf16 from_f<bf16>(float x) { return stati
 __device__ __forceinline__ int64_t tile_base(int64_t page, int g, int slot, int G, int P, int R) {
   return ((page * G + g) * (int64_t)P + (slot & ~15)) * (int64_t)R;
 }
+// Inside a tile, key rows of up to kWideKeyRows numbers are token-major
+// ([16][r_k]); wider ones are chunk-major: chunk c (dims 32c .. 32c + 31, the
+// last one narrower when r_k % 32 != 0) holds the 16 tokens' pieces one after
+// another, so that a 16-token x 32-dimension block is one contiguous 1 KiB.
+constexpr int kWideKeyRows = 512;
+constexpr int kKeyChunk = 32;
+__device__ __forceinline__ bool wide_keys(int rk) { return rk > kWideKeyRows; }
+// offset of key element d of the token in tile slot s (0..15) from the tile start
+__device__ __forceinline__ int64_t key_in_tile(int s, int d, int rk) {
+  if (!wide_keys(rk)) return (int64_t)s * rk + d;
+  const int c = d / kKeyChunk;
+  return (int64_t)c * (16 * kKeyChunk) + s * min(kKeyChunk, rk - kKeyChunk * c) + d % kKeyChunk;
+}
 __device__ __forceinline__ int64_t key_off(int64_t page, int g, int slot, int d, int G, int P, int R,
                                            int rk) {
-  return tile_base(page, g, slot, G, P, R) + (slot & 15) * rk + d;
+  return tile_base(page, g, slot, G, P, R) + key_in_tile(slot & 15, d, rk);
 }
 __device__ __forceinline__ int64_t val_off(int64_t page, int g, int slot, int d, int G, int P, int R,
                                            int rk) {

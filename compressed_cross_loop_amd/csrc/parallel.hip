@@ -175,7 +175,7 @@ __global__ __launch_bounds__(kThreads) void k_par_gather(ParParams p) {
   // keys: 16 rows of r_k, token-major in the store as here
   for (int x = tid; x < kTile * (rk / 8); x += kThreads) {
     const int t = x / (rk / 8), c = 8 * (x % (rk / 8));
-    const bf16x8 val = t < nv ? *reinterpret_cast<const bf16x8*>(tile + t * rk + c) : z;
+    const bf16x8 val = t < nv ? *reinterpret_cast<const bf16x8*>(tile + key_in_tile(t, c, rk)) : z;
     *reinterpret_cast<bf16x8*>(sk + (int64_t)t * G * rk + c) = val;
   }
   // values: sub-block d/16 holds [16 dims][16 tokens]

@@ -84,6 +84,10 @@ __global__ __launch_bounds__(kScoreThreads) void k_scan_absorbed_wide_scores(Dec
   const int tw = tb + wave * kTokPerWave;
   const int H = p.H, rk = p.rk, P = p.P, R = p.rk + p.rv;
   const bf16* pages = static_cast<const bf16*>(p.pages);
+  // a lane's 8 key dims of K step ks: row (t % 16) of the tile, dims 32 ks +
+  // 8 grp; wide rows are chunk-major, so a step is one contiguous KiB per tile
+  const bool wide = wide_keys(rk);
+  const int kstep = wide ? 16 * kKeyChunk : 32;
   const bf16* krow[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -91,7 +95,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_scan_absorbed_wide_scores(Dec
     // scores land in S but nothing reads them
     const int t = min(tw + 16 * i + col, n_lat - 1);
     const int64_t page = p.bt[(int64_t)b * p.max_pages + t / P];
-    krow[i] = pages + tile_base(page, 0, t % P, 1, P, R) + (t % 16) * rk + 8 * grp;
+    krow[i] = pages + tile_base(page, 0, t % P, 1, P, R) + (t % 16) * (wide ? kKeyChunk : rk) + 8 * grp;
   }
   // q~ staging: piece x = tid + kScoreThreads k of a chunk is head row x / 16,
   // dims 8 (x % 16) .. + 7, kept at slot (x % 16) ^ (row % 16) of its LDS row
@@ -124,7 +128,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_scan_absorbed_wide_scores(Dec
   const int nk = rk / 32;
   auto issue = [&](auto U, int ks) {
     constexpr int u = decltype(U)::value;
-    const int k0 = 32 * min(ks, nk - 1);       // clamped: always a valid step
+    const int k0 = kstep * min(ks, nk - 1);    // clamped: always a valid step
 #pragma unroll
     for (int i = 0; i < 4; ++i) ka[u][i] = *reinterpret_cast<const bf16x8*>(krow[i] + k0);
   };

@@ -90,7 +90,11 @@ __device__ __forceinline__ void wave_main(const DecodeParams& p, float (*sc)[2][
   // This wave's decoder (A_t or B_t^T, both [DH][R]): fragment nt is row
   // 16 nt + col, latent dims ks*32 + 8 kg ..
   const bf16* dec = static_cast<const bf16*>(KIND ? p.Bm : p.A) + (int64_t)hc * DH * R;
-  const uint32_t lane_off = (uint32_t)(col * R + 8 * kg);   // row col, dims 8 kg .. (decoder and key rows)
+  const uint32_t lane_off = (uint32_t)(col * R + 8 * kg);   // row col, dims 8 kg .. (decoder rows)
+  // key rows: token-major (row col, like the decoders), or chunk-major when wide
+  const bool wide = wide_keys(R);
+  const uint32_t key_lane_off = wide ? (uint32_t)(col * kKeyChunk + 8 * kg) : lane_off;
+  const int key_step = wide ? 16 * kKeyChunk : KC;
 
   float qv[NT];
   if (KIND == 0) {
@@ -116,7 +120,7 @@ __device__ __forceinline__ void wave_main(const DecodeParams& p, float (*sc)[2][
     if (KIND == 0) {
 #pragma unroll
       for (int j = 0; j < MT; ++j)
-        st.a[j] = *reinterpret_cast<const bf16x8*>(kbase[j] + ks * KC + lane_off);
+        st.a[j] = *reinterpret_cast<const bf16x8*>(kbase[j] + ks * key_step + key_lane_off);
     } else {
       // dims ks*32 + 8 kg + k (k = 0..7) of this lane's 8 tokens: sub-block
       // 2 ks + kg/2, dim row 8 (kg%2) + k
@@ -396,7 +400,11 @@ __device__ __forceinline__ void staged_wave(const DecodeParams& p, Smem<DH>& sm,
   int dstart = 0;                                          // first decoder copy of this wave
   for (int w = 0; w < wave; ++w) dstart += Sh::PER_WAVE - 2 * ((Sh::NTT - w + kWaves - 1) / kWaves);
   const int row = lane >> 2, cq = (lane & 3) ^ ((row >> 2) & 3);
-  const uint32_t koff = row * R + 8 * cq;                  // key rows: row, chunk cq
+  // key rows: row, chunk cq (token-major, or chunk-major when wide: then a
+  // step's 16 rows x 64 B are one contiguous KiB)
+  const bool wide = wide_keys(R);
+  const uint32_t koff = wide ? row * kKeyChunk + 8 * cq : row * R + 8 * cq;
+  const uint32_t kstep = wide ? 16 * kKeyChunk : KC;
   const int vch = val_slot(lane);
   const uint32_t voff = 16 * R + (vch >> 5) * 256 + ((vch >> 1) & 15) * 16 + (vch & 1) * 8;
   uint32_t doff[Sh::PER_WAVE];
@@ -426,7 +434,7 @@ __device__ __forceinline__ void staged_wave(const DecodeParams& p, Smem<DH>& sm,
       int slot;
       if (u < 2 * np) {
         const int k = u >> 1, tt = wave + kWaves * k;
-        src = (u & 1) ? tbase[k] + (voff + (uint32_t)ks * 512) : tbase[k] + (koff + (uint32_t)ks * KC);
+        src = (u & 1) ? tbase[k] + (voff + (uint32_t)ks * 512) : tbase[k] + (koff + (uint32_t)ks * kstep);
         slot = (u & 1) ? Sh::QV + tt : tt;
       } else {
         src = dect + (doff[u] + (uint32_t)ks * (DH * KC));

@@ -123,6 +123,13 @@ typedef struct {
  *                  stored dimension-major (16 tokens of one dim contiguous).
  *                Element offset of key dim d of slot u, group g, page pg:
  *                  ((pg*G + g)*P + (u/16)*16)*(r_k+r_v) + (u%16)*r_k + d
+ *                for r_k <= 512; key rows wider than 512 numbers are
+ *                chunk-major (chunk c = dims 32c .. 32c+31, the last one
+ *                w_c = min(32, r_k - 32c) wide, holds the 16 tokens' pieces
+ *                in turn), key dim d then at
+ *                  ((pg*G + g)*P + (u/16)*16)*(r_k+r_v) + 512*(d/32)
+ *                    + (u%16)*w_(d/32) + d%32
+ *                (fp8 stores keep token-major key rows at every width);
  *                and of value dim d:
  *                  ((pg*G + g)*P + (u/16)*16)*(r_k+r_v) + 16*r_k
  *                    + (d/16)*256 + (d%16)*16 + u%16
