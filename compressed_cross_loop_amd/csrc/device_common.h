@@ -126,6 +126,20 @@ __device__ __forceinline__ void copy_to_lds(const void* src, const void* lds) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(m0) : "memory");
 }
 
+// Barrier after copy_to_lds copies: this wave's copies have landed but for its
+// last N (the ones issued after those the barrier is for) and its LDS reads
+// have returned, then all waves meet.  No fence: a workgroup fence, even one
+// on LDS alone, would also wait for every copy in flight.  The asm statements
+// keep the compiler from moving memory accesses across.
+template <int N>
+__device__ __forceinline__ void copy_barrier() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0070 | N);   // vmcnt(N) lgkmcnt(0), expcnt untouched
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Workgroup barrier ordering LDS accesses only: unlike __syncthreads(), whose
 // fence also covers global memory, it leaves the wave's global loads in flight.
 __device__ __forceinline__ void lds_barrier() {

@@ -344,19 +344,6 @@ constexpr unsigned kWaitVm0 = 0x0F70;   // s_waitcnt vmcnt(0), expcnt / lgkmcnt 
 // wait insertion, which cannot tell the three stage buffers' copies apart
 // once the step loop's control flow joins; the kernel waits for them itself.
 //
-// Step barrier: this wave's copies of the step have landed (at most N, the
-// next step's, still in flight) and its LDS reads have returned, then all
-// waves meet.  No fence: a workgroup fence, even one on LDS alone, would
-// also wait for every copy in flight.  The asm statements keep the compiler
-// from moving memory accesses across.
-template <int N>
-__device__ __forceinline__ void step_barrier() {
-  static_assert(N >= 0 && N < 16, "vmcnt immediate");
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0x0070 | N);   // vmcnt(N) lgkmcnt(0), expcnt untouched
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
 
 // LDS regions of the staged kernel.  The three stage buffers are separate
 // LDS variables and every access names one of them statically: the compiler
@@ -500,9 +487,9 @@ __device__ __forceinline__ void staged_wave(const DecodeParams& p, Smem<DH>& sm,
     // buffer of step k - 1 (read before the barrier) takes step k + 2.
     auto step = [&](int k, const unsigned char* cur, unsigned char* nxt) {
       if (k + 1 < nks)
-        step_barrier<Sh::PER_WAVE>();
+        copy_barrier<Sh::PER_WAVE>();
       else
-        step_barrier<0>();
+        copy_barrier<0>();
       if (k + 2 < nks) issue(k + 2, nxt);
       compute(cur);
     };
