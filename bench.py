@@ -53,8 +53,9 @@ def parse():
     ap.add_argument("--writes", choices=["auto", "serial", "overlapped"], default="auto",
                     help="serial: the step's latent writes after all its decode calls, on one stream; "
                          "overlapped: each layer's writes on a second stream once its last-loop decode call is "
-                         "issued; auto: overlapped for the HLA entry (workload 3: 19.60 -> 18.90 ms per step), "
-                         "serial for the LLA entries (workload 2's writes slowed its scans by 3.7%%)")
+                         "issued; auto: overlapped for the HLA entry (workload 3: 19.00 -> 18.94 ms per step with "
+                         "the GPU idle before each run), serial for the LLA entries (workload 2's writes slowed its "
+                         "scans)")
     ap.add_argument("--no-graph", action="store_true",
                     help="launch every kernel eagerly instead of replaying the step as one HIP graph")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
