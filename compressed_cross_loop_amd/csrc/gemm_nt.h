@@ -4,10 +4,11 @@
 //
 // 128 x 128 tiles, 4 waves of 64 x 64 (v_mfma_f32_16x16x32_bf16: A = 8
 // consecutive k of one X row, B = 8 consecutive k of one Y row, both 16-byte
-// loads in the natural row-major layouts), K steps of 32 staged in LDS and
-// double-buffered (the next step's loads in flight during the products).
-// K may be made of segments of kseg elements that lie apart in memory (the
-// loops of the latent writer: one segment per loop); every 32-wide K step
+// loads in the natural row-major layouts), K steps of BK staged in LDS and
+// double-buffered (the next step's loads in flight during the products): BK =
+// 64 for long reductions whose K segments allow it (one barrier per 32
+// products of a wave), else 32.  K may be made of segments of kseg elements that lie apart in
+// memory (the loops of the latent writer: one segment per loop); every K step
 // lies in one segment.  Rows past M and N are clamped on load and skipped on
 // store.  With a bf16 C the products are taken transposed (Y fragment as the A
 // operand), so a lane holds four consecutive columns of one row; the tile is
@@ -31,12 +32,16 @@ struct GemmParams {
   int64_t sxb, sxg, syb, syg, scb, scg;
 };
 
-template <typename TC>
+template <typename TC, int BK>
 __global__ __launch_bounds__(256) void k_gemm_nt(GemmParams<TC> q) {
   typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
   typedef float f32x4_t __attribute__((ext_vector_type(4)));
   typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
-  constexpr int BM = 128, BN = 128, BK = 32, LD = BK + 8, NT = 256;
+  // LDS rows of BK + 8 bf16: the 16 rows a fragment read touches start in
+  // distinct 4-bank groups
+  constexpr int BM = 128, BN = 128, LD = BK + 8, NT = 256;
+  constexpr int CH = BM * BK / 8 / NT;   // 16-byte chunks per thread per operand and K step
+  constexpr int KS = BK / 32;            // products per fragment pair and K step
   const int z = blockIdx.z, zb = z / q.G, zg = z % q.G;
   const bf16* X = q.X + zb * q.sxb + zg * q.sxg;
   const bf16* Y = q.Y + zb * q.syb + zg * q.syg;
@@ -51,30 +56,30 @@ __global__ __launch_bounds__(256) void k_gemm_nt(GemmParams<TC> q) {
   static_assert(BM * LC <= 2 * (BM + BN) * LD, "output tile must fit the operand buffers");
   bf16 (*xs)[BM][LD] = reinterpret_cast<bf16 (*)[BM][LD]>(smem);
   bf16 (*ys)[BN][LD] = reinterpret_cast<bf16 (*)[BN][LD]>(smem + 2 * BM * LD);
-  // loader: 2 chunks of 16 B per thread per operand and K step
-  int xr[2], yr[2], kc[2];
+  // loader: CH chunks of 16 B per thread per operand and K step
+  int xr[CH], yr[CH], kc[CH];
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
+  for (int c = 0; c < CH; ++c) {
     const int idx = tid + NT * c;
-    kc[c] = 8 * (idx % 4);
-    xr[c] = min(m0 + idx / 4, q.M - 1);
-    yr[c] = min(n0 + idx / 4, q.N - 1);
+    kc[c] = 8 * (idx % (BK / 8));
+    xr[c] = min(m0 + idx / (BK / 8), q.M - 1);
+    yr[c] = min(n0 + idx / (BK / 8), q.N - 1);
   }
-  u32x4_t rx[2], ry[2];
+  u32x4_t rx[CH], ry[CH];
   auto load = [&](int k0) {
     const int seg = k0 / q.kseg, kk = k0 - seg * q.kseg;
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
+    for (int c = 0; c < CH; ++c) {
       rx[c] = *reinterpret_cast<const u32x4_t*>(X + (int64_t)xr[c] * q.ldx + seg * q.sxk + kk + kc[c]);
       ry[c] = *reinterpret_cast<const u32x4_t*>(Y + (int64_t)yr[c] * q.ldy + seg * q.syk + kk + kc[c]);
     }
   };
   auto store = [&](int buf) {
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
+    for (int c = 0; c < CH; ++c) {
       const int idx = tid + NT * c;
-      *reinterpret_cast<u32x4_t*>(&xs[buf][idx / 4][kc[c]]) = rx[c];
-      *reinterpret_cast<u32x4_t*>(&ys[buf][idx / 4][kc[c]]) = ry[c];
+      *reinterpret_cast<u32x4_t*>(&xs[buf][idx / (BK / 8)][kc[c]]) = rx[c];
+      *reinterpret_cast<u32x4_t*>(&ys[buf][idx / (BK / 8)][kc[c]]) = ry[c];
     }
   };
   f32x4_t acc[4][4];
@@ -89,17 +94,22 @@ __global__ __launch_bounds__(256) void k_gemm_nt(GemmParams<TC> q) {
   for (int kk = 0; kk < nk; ++kk) {
     const int cur = kk & 1;
     if (kk + 1 < nk) load((kk + 1) * BK);
-    bf16x8_t a[4], bb[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const bf16x8_t*>(&xs[cur][64 * wm + 16 * i + col][8 * grp]);
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8_t a[4], bb[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) bb[j] = *reinterpret_cast<const bf16x8_t*>(&ys[cur][64 * wn + 16 * j + col][8 * grp]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i)
+        a[i] = *reinterpret_cast<const bf16x8_t*>(&xs[cur][64 * wm + 16 * i + col][32 * ks + 8 * grp]);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        acc[i][j] = kBf16C ? __builtin_amdgcn_mfma_f32_16x16x32_bf16(bb[j], a[i], acc[i][j], 0, 0, 0)
-                           : __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bb[j], acc[i][j], 0, 0, 0);
+        bb[j] = *reinterpret_cast<const bf16x8_t*>(&ys[cur][64 * wn + 16 * j + col][32 * ks + 8 * grp]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = kBf16C ? __builtin_amdgcn_mfma_f32_16x16x32_bf16(bb[j], a[i], acc[i][j], 0, 0, 0)
+                             : __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bb[j], acc[i][j], 0, 0, 0);
+    }
     if (kk + 1 < nk) store(cur ^ 1);
     __syncthreads();
   }
@@ -153,7 +163,14 @@ __global__ __launch_bounds__(256) void k_gemm_nt(GemmParams<TC> q) {
 template <typename TC>
 hipError_t launch_gemm(const GemmParams<TC>& g, int batches, hipStream_t s) {
   const dim3 grid((g.N + 127) / 128, (g.M + 127) / 128, batches * g.G);
-  hipLaunchKernelGGL(k_gemm_nt<TC>, grid, dim3(256), 0, s, g);
+  // K steps of 64 for long reductions (the bulk writer's K = loops x d_in:
+  // 188.6 -> 167 us at 16384 x 1024 x 6144); at K = 512 (the parallel pass's
+  // rebuild) the shorter loop did not pay for the lower occupancy (44.8 ->
+  // 46.0 us)
+  if (g.K >= 1024 && g.K % 64 == 0 && g.kseg % 64 == 0)
+    hipLaunchKernelGGL((k_gemm_nt<TC, 64>), grid, dim3(256), 0, s, g);
+  else
+    hipLaunchKernelGGL((k_gemm_nt<TC, 32>), grid, dim3(256), 0, s, g);
   return hipGetLastError();
 }
 
