@@ -371,17 +371,25 @@ __global__ __launch_bounds__(kThreads) void k_combine_mfma(DecodeParams p) {
   __shared__ float pm[16][kCombineMaxParts], pl[16][kCombineMaxParts];
   {
     const int NP = S + WS;
-    for (int x = tid; x < 16 * NP; x += kThreads) {
-      const int bl = x / NP, j = x % NP, b = b0 + bl;
-      float mm = -INFINITY, ll = 0.f;
-      if (b < p.B) {
+    constexpr int MU = (16 * kCombineMaxParts + kThreads - 1) / kThreads;
+    float2 ml[MU];
+#pragma unroll
+    for (int u = 0; u < MU; ++u) {
+      const int x = tid + u * kThreads, bl = x / NP, j = x % NP, b = b0 + bl;
+      ml[u] = make_float2(-INFINITY, 0.f);
+      if (x < 16 * NP && b < p.B) {
         const float* src = (j < S) ? p.part_ml + (((int64_t)b * S + j) * H + h) * 2
                                    : p.win_ml + (((int64_t)b * WS + (j - S)) * H + h) * 2;
-        mm = src[0];
-        ll = src[1];
+        ml[u] = *reinterpret_cast<const float2*>(src);
       }
-      pm[bl][j] = mm;
-      pl[bl][j] = ll;
+    }
+#pragma unroll
+    for (int u = 0; u < MU; ++u) {
+      const int x = tid + u * kThreads, bl = x / NP, j = x % NP;
+      if (x < 16 * NP) {
+        pm[bl][j] = ml[u].x;
+        pl[bl][j] = ml[u].y;
+      }
     }
   }
   __syncthreads();
@@ -414,11 +422,23 @@ __global__ __launch_bounds__(kThreads) void k_combine_mfma(DecodeParams p) {
     for (int bl = 0; bl < 16; ++bl) {
       f32x4 sum = {0.f, 0.f, 0.f, 0.f};
       if (bl < nb) {
+        // 16 splits' rows requested together (the address is clamped to the
+        // last split, whose weight is then replaced by 0), so a sequence's
+        // many splits cost a few memory round trips, not one each
         const int b = b0 + bl;
-#pragma unroll 4
-        for (int s = sg; s < S; s += SG) {
-          const float4 t = *reinterpret_cast<const float4*>(p.part_o + (((int64_t)b * S + s) * H + h) * p.Dp + 4 * c4);
-          sum += pm[bl][s] * f32x4{t.x, t.y, t.z, t.w};
+        const float* base = p.part_o + ((int64_t)b * S * H + h) * p.Dp + 4 * c4;
+        const int64_t sstride = (int64_t)H * p.Dp;
+        constexpr int UL = 16;
+        for (int s0 = sg; s0 < S; s0 += UL * SG) {
+          float4 t[UL];
+#pragma unroll
+          for (int u = 0; u < UL; ++u)
+            t[u] = *reinterpret_cast<const float4*>(base + min(s0 + u * SG, S - 1) * sstride);
+#pragma unroll
+          for (int u = 0; u < UL; ++u) {
+            const float w = (s0 + u * SG < S) ? pm[bl][s0 + u * SG] : 0.f;
+            sum += w * f32x4{t[u].x, t[u].y, t[u].z, t[u].w};
+          }
         }
       }
       reinterpret_cast<f32x4*>(rbuf)[tid] = sum;
@@ -441,13 +461,23 @@ __global__ __launch_bounds__(kThreads) void k_combine_mfma(DecodeParams p) {
     for (int bl = 0; bl < nb; ++bl) {
       const int b = b0 + bl;
       f32x4 w0 = {0.f, 0.f, 0.f, 0.f}, w1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-      for (int sl = wg; sl < WS; sl += kThreads / 16) {
-        const float4* src = reinterpret_cast<const float4*>(p.win_o + (((int64_t)b * WS + sl) * H + h) * DH + e8);
-        const float4 a = src[0], c = src[1];
-        const float w = pm[bl][S + sl];
-        w0 += w * f32x4{a.x, a.y, a.z, a.w};
-        w1 += w * f32x4{c.x, c.y, c.z, c.w};
+      constexpr int WL = 4;   // slices of this thread requested together (clamped, weight 0)
+      for (int sl0 = wg; sl0 < WS; sl0 += WL * (kThreads / 16)) {
+        float4 a[WL], c[WL];
+#pragma unroll
+        for (int u = 0; u < WL; ++u) {
+          const int sl = min(sl0 + u * (kThreads / 16), WS - 1);
+          const float4* src = reinterpret_cast<const float4*>(p.win_o + (((int64_t)b * WS + sl) * H + h) * DH + e8);
+          a[u] = src[0];
+          c[u] = src[1];
+        }
+#pragma unroll
+        for (int u = 0; u < WL; ++u) {
+          const int sl = sl0 + u * (kThreads / 16);
+          const float w = sl < WS ? pm[bl][S + sl] : 0.f;
+          w0 += w * f32x4{a[u].x, a[u].y, a[u].z, a[u].w};
+          w1 += w * f32x4{c[u].x, c[u].y, c[u].z, c[u].w};
+        }
       }
       reinterpret_cast<f32x4*>(rbuf)[2 * tid] = w0;
       reinterpret_cast<f32x4*>(rbuf)[2 * tid + 1] = w1;

@@ -396,6 +396,33 @@ __global__ __launch_bounds__(kThreads) void k_combine(DecodeParams p) {
       for (int k = 0; k < rv; ++k) acc += to_f(Bh[(int64_t)e * rv + k]) * ob[k];
       out[e] = from_f<T>((acc + window_sum(e)) * inv);
     }
+  } else if (dh <= kThreads) {
+    // thread -> (dim e, split group sg): the groups take splits sg, sg + ng, ..
+    // eight at a time (addresses clamped to the last split, weight 0), so a
+    // long context's many splits cost a few memory round trips, not one each;
+    // the groups' sums then add through LDS in a fixed order
+    __shared__ float gsum[kThreads];
+    const int ng = kThreads / dh, e = tid % dh, sg = tid / dh;
+    float acc = 0.f;
+    if (sg < ng) {
+      const float* base = p.part_o + ((int64_t)b * S * H + h) * p.Dp + e;
+      const int64_t sstride = (int64_t)H * p.Dp;
+      constexpr int UL = 8;
+      for (int s0 = sg; s0 < S; s0 += UL * ng) {
+        float v[UL];
+#pragma unroll
+        for (int u = 0; u < UL; ++u) v[u] = base[min(s0 + u * ng, S - 1) * sstride];
+#pragma unroll
+        for (int u = 0; u < UL; ++u) acc += (s0 + u * ng < S ? ws[s0 + u * ng] : 0.f) * v[u];
+      }
+    }
+    gsum[tid] = acc;
+    __syncthreads();
+    if (tid < dh) {
+      float t = 0.f;
+      for (int g = 0; g < ng; ++g) t += gsum[g * dh + tid];
+      out[tid] = from_f<T>((t + window_sum(tid)) * inv);
+    }
   } else {
     for (int e = tid; e < dh; e += kThreads) {
       float acc = 0.f;
