@@ -303,8 +303,11 @@ __global__ __launch_bounds__(kThreads) void k_window_fast(DecodeParams p) {
 // and written as 16-byte rows.  With all 16 sequences present (large
 // batches, few splits) the first two splits' latent sums and the first two
 // window slices are requested at entry as well, so the merge barrier waits
-// for one memory round trip instead of three.
-template <int RV>
+// for one memory round trip instead of three.  PART: some workgroup may hold
+// fewer than 16 sequences (the batch is not a multiple of 16); the path for
+// those is compiled only then, so that it cannot change the register
+// allocation of the full-workgroup path.
+template <int RV, bool PART>
 __global__ __launch_bounds__(kThreads) void k_combine_mfma(DecodeParams p) {
   constexpr int DH = 128;
   constexpr int NT = DH / 16;              // output column tiles
@@ -332,7 +335,7 @@ __global__ __launch_bounds__(kThreads) void k_combine_mfma(DecodeParams p) {
 
   constexpr int C4 = RV / 4;               // float4 columns of a latent sum
   constexpr int PER = (C4 + 15) / 16;
-  const bool full16 = p.B - b0 >= 16;
+  const bool full16 = !PART || p.B - b0 >= 16;
   // full16: thread -> (sequence fbl, float4 columns fk4, fk4 + 16, .., and 8
   // window dims from fe8)
   const int fbl = tid / 16, fk4 = tid % 16, fe8 = (tid % 16) * 8, fb = b0 + fbl;
@@ -667,12 +670,22 @@ bool combine_mfma_supports(const DecodeParams& p) {
 hipError_t launch_combine_mfma(const DecodeParams& p, hipStream_t s) {
   if (!combine_mfma_supports(p)) return hipErrorNotSupported;
   const dim3 grid(p.H, (p.B + 15) / 16);
-  switch (p.rv) {
-    case 32: hipLaunchKernelGGL(k_combine_mfma<32>, grid, dim3(kThreads), 0, s, p); break;
-    case 64: hipLaunchKernelGGL(k_combine_mfma<64>, grid, dim3(kThreads), 0, s, p); break;
-    case 128: hipLaunchKernelGGL(k_combine_mfma<128>, grid, dim3(kThreads), 0, s, p); break;
-    case 256: hipLaunchKernelGGL(k_combine_mfma<256>, grid, dim3(kThreads), 0, s, p); break;
-    default: hipLaunchKernelGGL(k_combine_mfma<512>, grid, dim3(kThreads), 0, s, p); break;
+  if (p.B % 16 != 0) {
+    switch (p.rv) {
+      case 32: hipLaunchKernelGGL((k_combine_mfma<32, true>), grid, dim3(kThreads), 0, s, p); break;
+      case 64: hipLaunchKernelGGL((k_combine_mfma<64, true>), grid, dim3(kThreads), 0, s, p); break;
+      case 128: hipLaunchKernelGGL((k_combine_mfma<128, true>), grid, dim3(kThreads), 0, s, p); break;
+      case 256: hipLaunchKernelGGL((k_combine_mfma<256, true>), grid, dim3(kThreads), 0, s, p); break;
+      default: hipLaunchKernelGGL((k_combine_mfma<512, true>), grid, dim3(kThreads), 0, s, p); break;
+    }
+  } else {
+    switch (p.rv) {
+      case 32: hipLaunchKernelGGL((k_combine_mfma<32, false>), grid, dim3(kThreads), 0, s, p); break;
+      case 64: hipLaunchKernelGGL((k_combine_mfma<64, false>), grid, dim3(kThreads), 0, s, p); break;
+      case 128: hipLaunchKernelGGL((k_combine_mfma<128, false>), grid, dim3(kThreads), 0, s, p); break;
+      case 256: hipLaunchKernelGGL((k_combine_mfma<256, false>), grid, dim3(kThreads), 0, s, p); break;
+      default: hipLaunchKernelGGL((k_combine_mfma<512, false>), grid, dim3(kThreads), 0, s, p); break;
+    }
   }
   return hipGetLastError();
 }
