@@ -107,10 +107,10 @@ struct ParParams {
   const void* A;                  // [H][d_h][r_k]
   const void* Bm;                 // [H][d_h][r_v]
   void* out;
-  // workspace regions (bf16)
+  // workspace regions (bf16 unless noted)
   void* sk;                       // [B][n_pad][G][r_k]  latents some position reads, token-major
   void* sv;                       // [B][n_pad][G][r_v]
-  void* qr;                       // [B][n_pad][H][d_h]  R_i q * scale
+  void* rtab;                     // [n_pad][d_h/2] (cos, sin) of position i, frequency f (fp32 pairs)
   void* kr;                       // [B][n_pad][H][d_h]  R_j k
   void* kh;                       // [B][n_pad][H][d_h]  rebuilt keys
   void* vh;                       // [B][n_pad][H][d_h]  rebuilt values

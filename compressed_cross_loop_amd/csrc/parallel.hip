@@ -10,8 +10,9 @@
 // Eq. 3 when A_t commutes with the rotation (frequency-paired decoders) or
 // without rotary embedding.  Five launches:
 //
-//   k_par_prep    q' = R_i q * log2(e)/sqrt(d_h) and k' = R_j k (token-major,
-//                 bf16); zero past n_tok
+//   k_rope_table  (cos, sin) of every position and frequency, once per call
+//   k_par_prep    k' = R_j k (token-major, bf16; zero past n_tok); the
+//                 attention rotates its own query rows with the same table
 //   k_par_gather  the latents a position can read (j < n_tok - 1 - W) as
 //                 token-major rows; the store's dimension-major value
 //                 sub-blocks are transposed through LDS; zero rows elsewhere
@@ -76,8 +77,22 @@ constexpr int kAttnQT = kAttnWaves * 16 * kAttnQB;   // positions per attention 
 static_assert(kParQueryTile % kAttnQT == 0, "padding must cover whole query tiles");
 
 // ------------------------------------------------------------------ prep
-// workgroup = (64 positions, sequence, hpw heads); every thread first loads
-// all of its items, then rotates and stores them (one memory round trip)
+// (cos, sin) of position i and frequency f, for every position up to the
+// padded length: one thread per entry, fp64 angles (the same for every
+// sequence, layer and loop of the call)
+template <int DH>
+__global__ __launch_bounds__(kThreads) void k_rope_table(ParParams p) {
+  const int x = blockIdx.x * kThreads + threadIdx.x;
+  if (x >= p.n_pad * (DH / 2)) return;
+  const int i = x / (DH / 2), f = x % (DH / 2);
+  float c = 1.f, s = 0.f;
+  if (p.rope_base != 0.f) rope_cs(p.rope_base, DH, f, i, c, s);
+  static_cast<float2*>(p.rtab)[x] = make_float2(c, s);
+}
+
+// workgroup = (64 positions, sequence, hpw heads); the positions' table rows
+// are staged in LDS, then every thread loads all of its items, rotates and
+// stores them (one memory round trip)
 constexpr int kPrepTokens = 64;
 
 template <int DH>
@@ -87,40 +102,30 @@ __global__ __launch_bounds__(kThreads) void k_par_prep(ParParams p, int hpw) {
   constexpr int IPT = 4;                          // items per thread per round
   const int b = blockIdx.y, i0 = blockIdx.x * T, h0 = blockIdx.z * hpw, tid = threadIdx.x;
   const int n = p.n_tok[b], H = p.H;
-  __shared__ float cs[T][DH / 2][2];
-  __shared__ double theta[DH / 2];
-  const bool rope = p.rope_base != 0.f;
-  if (tid < DH / 2) theta[tid] = rope ? rope_theta(p.rope_base, DH, tid) : 0.0;
-  __syncthreads();
-  for (int x = tid; x < T * DH / 2; x += kThreads) {
-    const int t = x / (DH / 2), f = x % (DH / 2);
-    float c = 1.f, s = 0.f;
-    if (rope && i0 + t < n) rope_cs_theta(theta[f], i0 + t, c, s);
-    cs[t][f][0] = c;
-    cs[t][f][1] = s;
+  __shared__ __attribute__((aligned(16))) float cs[T][DH / 2][2];
+  {
+    // rows i0 .. i0 + T - 1 of the table are one contiguous block
+    const float4* src = static_cast<const float4*>(p.rtab) + (int64_t)i0 * (DH / 4);
+    for (int x = tid; x < T * DH / 4; x += kThreads) reinterpret_cast<float4*>(&cs[0][0][0])[x] = src[x];
   }
   __syncthreads();
-  const bf16* q = static_cast<const bf16*>(p.q);
   const bf16* k = static_cast<const bf16*>(p.k);
-  bf16* qr = static_cast<bf16*>(p.qr);
   bf16* kr = static_cast<bf16*>(p.kr);
   bf16x8 z;
 #pragma unroll
   for (int e = 0; e < 8; ++e) z[e] = static_cast<bf16>(0.f);
-  // q' and k': item = (token, head, 8 dims); pair (f, f + d_h/2)
+  // k': item = (token, head, 8 dims); pair (f, f + d_h/2)
   const int items = T * hpw * C8;
   for (int x0 = 0; x0 < items; x0 += IPT * kThreads) {
-    bf16x8 qa[IPT], qp[IPT], ka[IPT], kp[IPT];
+    bf16x8 ka[IPT], kp[IPT];
 #pragma unroll
     for (int u = 0; u < IPT; ++u) {
       const int x = x0 + u * kThreads + tid;
       const int c8 = x % C8, th = x / C8, h = h0 + th % hpw, t = th / hpw, i = i0 + t;
-      qa[u] = qp[u] = ka[u] = kp[u] = z;
+      ka[u] = kp[u] = z;
       if (x < items && i < n) {
         const int64_t row = (((int64_t)b * p.n_max + i) * H + h) * DH;
         const int d0 = 8 * c8, pd = d0 < DH / 2 ? d0 + DH / 2 : d0 - DH / 2;
-        qa[u] = *reinterpret_cast<const bf16x8*>(q + row + d0);
-        qp[u] = *reinterpret_cast<const bf16x8*>(q + row + pd);
         ka[u] = *reinterpret_cast<const bf16x8*>(k + row + d0);
         kp[u] = *reinterpret_cast<const bf16x8*>(k + row + pd);
       }
@@ -131,22 +136,18 @@ __global__ __launch_bounds__(kThreads) void k_par_prep(ParParams p, int hpw) {
       if (x >= items) continue;
       const int c8 = x % C8, th = x / C8, h = h0 + th % hpw, t = th / hpw, i = i0 + t;
       const int d0 = 8 * c8;
-      bf16x8 qo, ko;
+      bf16x8 ko;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int d = d0 + e;
         const int f = d < DH / 2 ? d : d - DH / 2;
         const float c = cs[t][f][0], sn = cs[t][f][1];
         // first half: x_f c - x_{f+h} s; second half: x_f s + x_{f+h} c
-        const float qv = d < DH / 2 ? (float)qa[u][e] * c - (float)qp[u][e] * sn
-                                    : (float)qp[u][e] * sn + (float)qa[u][e] * c;
         const float kv = d < DH / 2 ? (float)ka[u][e] * c - (float)kp[u][e] * sn
                                     : (float)kp[u][e] * sn + (float)ka[u][e] * c;
-        qo[e] = static_cast<bf16>(qv * p.scale);
         ko[e] = static_cast<bf16>(kv);
       }
       const int64_t orow = (((int64_t)b * p.n_pad + i) * H + h) * DH;
-      *reinterpret_cast<bf16x8*>(qr + orow + d0) = qo;
       *reinterpret_cast<bf16x8*>(kr + orow + d0) = ko;
     }
   }
@@ -244,23 +245,13 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_par_attn(ParParams p) {
   const int qw1 = min(qw0 + 16 * QB - 1, qe);         // its last valid position
 
   const int64_t trow = (int64_t)H * DH;               // token row stride of [tokens][H][d_h]
-  const bf16* qr = static_cast<const bf16*>(p.qr) + (int64_t)b * p.n_pad * trow + h * DH;
+  const bf16* qx = static_cast<const bf16*>(p.q) + (int64_t)b * p.n_max * trow + h * DH;     // caller's q
   const bf16* kh = static_cast<const bf16*>(p.kh) + (int64_t)b * p.n_pad * trow + h * DH;
   const bf16* kr = static_cast<const bf16*>(p.kr) + (int64_t)b * p.n_pad * trow + h * DH;
   const bf16* vh = static_cast<const bf16*>(p.vh) + (int64_t)b * p.n_pad * trow + h * DH;
   const bf16* vx = static_cast<const bf16*>(p.v) + (int64_t)b * p.n_max * trow + h * DH;   // caller's v
 
-  bf16x8 qf[QB][KS];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qf[qb][ks] = *reinterpret_cast<const bf16x8*>(qr + (int64_t)(qw0 + 16 * qb + col) * trow + 32 * ks + 8 * grp);
-  // q has landed before any tile load is issued: the waits inside the tile
-  // loop then count only tile loads (without this the compiler cannot tell
-  // the q fragments apart from them and waits for the prefetched tile before
-  // every score product)
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+  bf16x8 qf[QB][KS];   // q', filled once tile 0's copies are in flight (below)
   f32x4 acc[QB][DB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb)
@@ -565,7 +556,56 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_par_attn(ParParams p) {
   // tiles 1 .. jp - 1 are all latent for every position of the wave and run
   // the mask-free loop (tile 0 sets the running maxima first)
   const int jp = wave_on ? min(ntile, max(0, (qw0 - W) / KT)) : 0;
+  // q' = R_i q log2(e)/sqrt(d_h) as the score MFMA's B operand: lane (col,
+  // grp) holds dims 32 ks + 8 grp .. + 7 of position i = qw0 + 16 qb + col,
+  // and the rotation partner of a first-half dim d (ks < KS/2) is d + d_h/2,
+  // in the same lane's fragment ks + KS/2.  The angles come from the (cos,
+  // sin) table by angle addition, R_i = R_(i - col) R_col: row i - col is
+  // shared by the 16 lanes of a query block and rows 0..15 by every wave, so
+  // a workgroup reads a few KiB of the table instead of a row per position.
+  // Rows past the sequence are clamped to its last token (those positions
+  // write nothing).  The q rows and table entries are requested first, then
+  // tile 0's copies, and the rotation runs while the copies travel: the
+  // compiler's waits for the q loads do not wait for the younger copies.
+  // Everything has landed before the tile loop, whose waits then count only
+  // tile copies.
+  bf16x8 raw[QB][KS];
+  float4 csa[QB][KS / 2][4], csb[KS / 2][4];   // (cos, sin) of frequencies 32 ks + 8 grp + 2 c2, + 1
+  {
+    const float4* rt = static_cast<const float4*>(p.rtab);   // [n_pad][d_h/2] (cos, sin) pairs
+#pragma unroll
+    for (int ks = 0; ks < KS / 2; ++ks)
+#pragma unroll
+      for (int c2 = 0; c2 < 4; ++c2) csb[ks][c2] = rt[(col * (DH / 2) + 32 * ks + 8 * grp) / 2 + c2];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int i = qw0 + 16 * qb + col;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        raw[qb][ks] = *reinterpret_cast<const bf16x8*>(qx + (int64_t)min(i, n - 1) * trow + 32 * ks + 8 * grp);
+#pragma unroll
+      for (int ks = 0; ks < KS / 2; ++ks)
+#pragma unroll
+        for (int c2 = 0; c2 < 4; ++c2)
+          csa[qb][ks][c2] = rt[((int64_t)(qw0 + 16 * qb) * (DH / 2) + 32 * ks + 8 * grp) / 2 + c2];
+    }
+  }
   issue_tile(0, 0);
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int ks = 0; ks < KS / 2; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float4 ta = csa[qb][ks][e / 2], tb = csb[ks][e / 2];
+        const float ca = (e & 1) ? ta.z : ta.x, sa = (e & 1) ? ta.w : ta.y;
+        const float cb = (e & 1) ? tb.z : tb.x, sb = (e & 1) ? tb.w : tb.y;
+        const float c = ca * cb - sa * sb, sn = sa * cb + ca * sb;
+        const float x0 = (float)raw[qb][ks][e], x1 = (float)raw[qb][ks + KS / 2][e];
+        qf[qb][ks][e] = static_cast<bf16>((x0 * c - x1 * sn) * p.scale);
+        qf[qb][ks + KS / 2][e] = static_cast<bf16>((x0 * sn + x1 * c) * p.scale);
+      }
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   int jt = 0;
   if (ntile > 0) {
     tile_start(0);
@@ -607,8 +647,11 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_par_attn(ParParams p) {
 template <int DH>
 hipError_t launch_dh(const ParParams& p, hipStream_t s, hipEvent_t* ev) {
   const int hpw = p.H % 4 == 0 ? 4 : (p.H % 2 == 0 ? 2 : 1);   // heads per prep workgroup
-  hipLaunchKernelGGL((k_par_prep<DH>), dim3(p.n_pad / kPrepTokens, p.B, p.H / hpw), dim3(kThreads), 0, s, p, hpw);
+  hipLaunchKernelGGL((k_rope_table<DH>), dim3((p.n_pad * (DH / 2) + kThreads - 1) / kThreads), dim3(kThreads), 0, s, p);
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_par_prep<DH>), dim3(p.n_pad / kPrepTokens, p.B, p.H / hpw), dim3(kThreads), 0, s, p, hpw);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_par_gather, dim3(p.n_pad / kTile, p.B, p.G), dim3(kThreads), 0, s, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
