@@ -341,7 +341,7 @@ lla_status check_parallel_desc(const lla_set_desc* d) {
 int parallel_pad(int n_max) { return (n_max + kParQueryTile - 1) / kParQueryTile * kParQueryTile; }
 
 struct ParWs {
-  size_t sk, sv, rtab, kr, kh, vh, total;
+  size_t sk, sv, rtab, kh, vh, total;
 };
 
 ParWs parallel_ws_layout(const lla_set_desc& d, int B, int n_max) {
@@ -352,7 +352,6 @@ ParWs parallel_ws_layout(const lla_set_desc& d, int B, int n_max) {
   w.sk = off;  off = up256(off + (size_t)B * np * G * d.r_k * 2);
   w.sv = off;  off = up256(off + (size_t)B * np * G * d.r_v * 2);
   w.rtab = off;  off = up256(off + np * (dh / 2) * 8);
-  w.kr = off;  off = up256(off + head_rows);
   w.kh = off;  off = up256(off + head_rows);
   w.vh = off;  off = up256(off + head_rows);
   w.total = off;
@@ -604,7 +603,7 @@ lla_status hla_attention_parallel(const lla_set_desc* d, const lla_store* st, in
   p.scale = (float)(1.4426950408889634 / std::sqrt((double)d->head_dim));
   p.n_tok = a->n_tok; p.bt = st->block_table; p.pages = st->pages;
   p.q = a->q; p.k = a->k; p.v = a->v; p.A = a->A; p.Bm = a->B; p.out = a->out;
-  p.sk = ws + w.sk; p.sv = ws + w.sv; p.rtab = ws + w.rtab; p.kr = ws + w.kr;
+  p.sk = ws + w.sk; p.sv = ws + w.sv; p.rtab = ws + w.rtab;
   p.kh = ws + w.kh; p.vh = ws + w.vh;
   return hip_status(launch_parallel(p, static_cast<hipStream_t>(stream), static_cast<hipEvent_t*>(a->attn_events)));
 }

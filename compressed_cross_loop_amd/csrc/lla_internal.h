@@ -111,7 +111,6 @@ struct ParParams {
   void* sk;                       // [B][n_pad][G][r_k]  latents some position reads, token-major
   void* sv;                       // [B][n_pad][G][r_v]
   void* rtab;                     // [n_pad][d_h/2] (cos, sin) of position i, frequency f (fp32 pairs)
-  void* kr;                       // [B][n_pad][H][d_h]  R_j k
   void* kh;                       // [B][n_pad][H][d_h]  rebuilt keys
   void* vh;                       // [B][n_pad][H][d_h]  rebuilt values
 };

@@ -11,8 +11,7 @@
 // without rotary embedding.  Five launches:
 //
 //   k_rope_table  (cos, sin) of every position and frequency, once per call
-//   k_par_prep    k' = R_j k (token-major, bf16; zero past n_tok); the
-//                 attention rotates its own query rows with the same table
+//                 (the attention rotates its query rows and exact keys with it)
 //   k_par_gather  the latents a position can read (j < n_tok - 1 - W) as
 //                 token-major rows; the store's dimension-major value
 //                 sub-blocks are transposed through LDS; zero rows elsewhere
@@ -27,7 +26,10 @@
 // per instruction; rows of d_h with their 16-byte chunks XOR-swizzled by row
 // against bank conflicts), double buffered: tile jt + 1's copies are in
 // flight while tile jt is read, one barrier per tile; a source is copied only
-// when some position of the workgroup reads it.  Per 16-token sub-tile and
+// when some position of the workgroup reads it.  The exact keys are copied
+// from the caller's k and rotated in LDS once they land (R_j k, with the
+// angles of the table by angle addition), behind one more barrier; the query
+// rows are rotated in registers.  Per 16-token sub-tile and
 // query block:
 //   scores  S^T[16 tok x 16 pos] = K[16 x d_h] . Q'^T   (v_mfma_f32_16x16x32_bf16)
 //           per element: j > i masked, j < i - W from the rebuilt keys, else
@@ -76,7 +78,7 @@ constexpr int kAttnThreads = 64 * kAttnWaves;
 constexpr int kAttnQT = kAttnWaves * 16 * kAttnQB;   // positions per attention workgroup
 static_assert(kParQueryTile % kAttnQT == 0, "padding must cover whole query tiles");
 
-// ------------------------------------------------------------------ prep
+// ------------------------------------------------------------------ rotary table
 // (cos, sin) of position i and frequency f, for every position up to the
 // padded length: one thread per entry, fp64 angles (the same for every
 // sequence, layer and loop of the call)
@@ -88,69 +90,6 @@ __global__ __launch_bounds__(kThreads) void k_rope_table(ParParams p) {
   float c = 1.f, s = 0.f;
   if (p.rope_base != 0.f) rope_cs(p.rope_base, DH, f, i, c, s);
   static_cast<float2*>(p.rtab)[x] = make_float2(c, s);
-}
-
-// workgroup = (64 positions, sequence, hpw heads); the positions' table rows
-// are staged in LDS, then every thread loads all of its items, rotates and
-// stores them (one memory round trip)
-constexpr int kPrepTokens = 64;
-
-template <int DH>
-__global__ __launch_bounds__(kThreads) void k_par_prep(ParParams p, int hpw) {
-  constexpr int T = kPrepTokens;
-  constexpr int C8 = DH / 8;                      // 16-byte chunks per head row
-  constexpr int IPT = 4;                          // items per thread per round
-  const int b = blockIdx.y, i0 = blockIdx.x * T, h0 = blockIdx.z * hpw, tid = threadIdx.x;
-  const int n = p.n_tok[b], H = p.H;
-  __shared__ __attribute__((aligned(16))) float cs[T][DH / 2][2];
-  {
-    // rows i0 .. i0 + T - 1 of the table are one contiguous block
-    const float4* src = static_cast<const float4*>(p.rtab) + (int64_t)i0 * (DH / 4);
-    for (int x = tid; x < T * DH / 4; x += kThreads) reinterpret_cast<float4*>(&cs[0][0][0])[x] = src[x];
-  }
-  __syncthreads();
-  const bf16* k = static_cast<const bf16*>(p.k);
-  bf16* kr = static_cast<bf16*>(p.kr);
-  bf16x8 z;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) z[e] = static_cast<bf16>(0.f);
-  // k': item = (token, head, 8 dims); pair (f, f + d_h/2)
-  const int items = T * hpw * C8;
-  for (int x0 = 0; x0 < items; x0 += IPT * kThreads) {
-    bf16x8 ka[IPT], kp[IPT];
-#pragma unroll
-    for (int u = 0; u < IPT; ++u) {
-      const int x = x0 + u * kThreads + tid;
-      const int c8 = x % C8, th = x / C8, h = h0 + th % hpw, t = th / hpw, i = i0 + t;
-      ka[u] = kp[u] = z;
-      if (x < items && i < n) {
-        const int64_t row = (((int64_t)b * p.n_max + i) * H + h) * DH;
-        const int d0 = 8 * c8, pd = d0 < DH / 2 ? d0 + DH / 2 : d0 - DH / 2;
-        ka[u] = *reinterpret_cast<const bf16x8*>(k + row + d0);
-        kp[u] = *reinterpret_cast<const bf16x8*>(k + row + pd);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < IPT; ++u) {
-      const int x = x0 + u * kThreads + tid;
-      if (x >= items) continue;
-      const int c8 = x % C8, th = x / C8, h = h0 + th % hpw, t = th / hpw, i = i0 + t;
-      const int d0 = 8 * c8;
-      bf16x8 ko;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = d0 + e;
-        const int f = d < DH / 2 ? d : d - DH / 2;
-        const float c = cs[t][f][0], sn = cs[t][f][1];
-        // first half: x_f c - x_{f+h} s; second half: x_f s + x_{f+h} c
-        const float kv = d < DH / 2 ? (float)ka[u][e] * c - (float)kp[u][e] * sn
-                                    : (float)kp[u][e] * sn + (float)ka[u][e] * c;
-        ko[e] = static_cast<bf16>(kv);
-      }
-      const int64_t orow = (((int64_t)b * p.n_pad + i) * H + h) * DH;
-      *reinterpret_cast<bf16x8*>(kr + orow + d0) = ko;
-    }
-  }
 }
 
 // ------------------------------------------------------------------ gather
@@ -228,6 +167,13 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_par_attn(ParParams p) {
   __shared__ __attribute__((aligned(1024))) bf16 ke_s[2][KT * DH];
   __shared__ __attribute__((aligned(1024))) bf16 vl_s[2][KT * DH];
   __shared__ __attribute__((aligned(1024))) bf16 ve_s[2][KT * DH];
+  // (cos, sin) rows for the exact keys' rotation, R_j = R_(j - j % 16) R_(j % 16),
+  // per wave for the RPC x CPW rows its own copies bring: its RPC offset rows
+  // (j % 16, the same for every tile; 2 KiB) and, per buffer, the rows of
+  // the 16-token blocks its rows fall in (one per copy; 1 KiB)
+  __shared__ __attribute__((aligned(1024))) char tb_s[kAttnWaves][2048];
+  __shared__ __attribute__((aligned(1024))) char ta_s[2][kAttnWaves][1024];
+  static_assert(RPC * 4 * DH == 2048 && CPW * 4 * DH <= 1024 && 16 % RPC == 0, "rotation table slots");
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: per-wave choices are scalar branches
@@ -247,7 +193,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_par_attn(ParParams p) {
   const int64_t trow = (int64_t)H * DH;               // token row stride of [tokens][H][d_h]
   const bf16* qx = static_cast<const bf16*>(p.q) + (int64_t)b * p.n_max * trow + h * DH;     // caller's q
   const bf16* kh = static_cast<const bf16*>(p.kh) + (int64_t)b * p.n_pad * trow + h * DH;
-  const bf16* kr = static_cast<const bf16*>(p.kr) + (int64_t)b * p.n_pad * trow + h * DH;
+  const bf16* kx = static_cast<const bf16*>(p.k) + (int64_t)b * p.n_max * trow + h * DH;     // caller's k
   const bf16* vh = static_cast<const bf16*>(p.vh) + (int64_t)b * p.n_pad * trow + h * DH;
   const bf16* vx = static_cast<const bf16*>(p.v) + (int64_t)b * p.n_max * trow + h * DH;   // caller's v
 
@@ -298,9 +244,48 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_par_attn(ParParams p) {
       copy_source(vh, j0, p.n_pad - 1, vl_s[buf]);
     }
     if (need_ex(jt)) {
-      copy_source(kr, j0, p.n_pad - 1, ke_s[buf]);
+      copy_source(kx, j0, n - 1, ke_s[buf]);
       copy_source(vx, j0, n - 1, ve_s[buf]);
+      // block rows: lane group q (64 / CPW lanes) takes the row of copy q's
+      // 16-token block; a row is 4 d_h bytes (lanes past it repeat it)
+      const int qg = lane / (64 / CPW);
+      copy_to_lds(static_cast<const char*>(p.rtab) +
+                      (int64_t)(j0 + 16 * (((wave + kAttnWaves * qg) * RPC) / 16)) * (4 * DH) +
+                      16 * (lane % (DH / 4)),
+                  &ta_s[buf][wave][0]);
     }
+  };
+  // R_j k of the exact keys this wave copied (rows (wave + 8 q) RPC + x),
+  // in place once they have landed: lane -> (row, dims 8 c .. 8 c + 7 and
+  // their partners d + d_h/2); nothing another wave wrote is read
+  auto rotate_own = [&](int buf) {
+    constexpr int PPR = NCH / 2;   // chunk pairs per row
+    if (lane >= CPW * RPC * PPR) return;
+    const int ri = lane / PPR, c = lane % PPR, qg = ri / RPC, x = ri % RPC;
+    const int r = (wave + kAttnWaves * qg) * RPC + x;
+    bf16x8* plo = reinterpret_cast<bf16x8*>(&ke_s[buf][r * DH + 8 * (c ^ (r % NCH))]);
+    bf16x8* phi = reinterpret_cast<bf16x8*>(&ke_s[buf][r * DH + 8 * ((c + PPR) ^ (r % NCH))]);
+    const bf16x8 lo = *plo, hi = *phi;
+    const float4* ta = reinterpret_cast<const float4*>(&ta_s[buf][wave][qg * (1024 / CPW) + 64 * c]);
+    const float4* tb = reinterpret_cast<const float4*>(&tb_s[wave][x * 4 * DH + 64 * c]);
+    bf16x8 olo, ohi;
+#pragma unroll
+    for (int c2 = 0; c2 < 4; ++c2) {
+      const float4 a4 = ta[c2], b4 = tb[c2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int e = 2 * c2 + u;
+        const float ca = u ? a4.z : a4.x, sa = u ? a4.w : a4.y;
+        const float cb = u ? b4.z : b4.x, sb = u ? b4.w : b4.y;
+        const float cc = ca * cb - sa * sb, sn = sa * cb + ca * sb;
+        const float x0 = (float)lo[e], x1 = (float)hi[e];
+        // first half: x_f c - x_{f+h} s; second half: x_f s + x_{f+h} c
+        olo[e] = static_cast<bf16>(x0 * cc - x1 * sn);
+        ohi[e] = static_cast<bf16>(x0 * sn + x1 * cc);
+      }
+    }
+    *plo = olo;
+    *phi = ohi;
   };
   // key row 16 ts + col, chunk 4 ks + grp (the row's swizzle is col % NCH)
   auto key_frag = [&](const bf16* kt_s, int ts, int ks) {
@@ -548,8 +533,11 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_par_attn(ParParams p) {
   // landed; after the barrier everyone's have, and every wave is done with
   // tile jt - 1's buffer, which takes tile jt + 1.  Each wave passes one
   // barrier per tile, in whichever of the loops below it is.
+  // A tile with exact keys has each wave rotate the rows it copied before
+  // the barrier.
   auto tile_start = [&](int jt) {
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    if (need_ex(jt)) rotate_own(jt & 1);
     __syncthreads();
     if (jt + 1 < ntile) issue_tile(jt + 1, (jt + 1) & 1);
   };
@@ -590,6 +578,12 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_par_attn(ParParams p) {
           csa[qb][ks][c2] = rt[((int64_t)(qw0 + 16 * qb) * (DH / 2) + 32 * ks + 8 * grp) / 2 + c2];
     }
   }
+  // this wave's offset rows (j % 16 of its rows: RPC rows from (wave RPC) % 16)
+#pragma unroll
+  for (int k2 = 0; k2 < 2; ++k2)
+    copy_to_lds(static_cast<const char*>(p.rtab) +
+                    (int64_t)((wave * RPC) % 16 + k2 * (256 / DH) + lane / (DH / 4)) * (4 * DH) + 16 * (lane % (DH / 4)),
+                &tb_s[wave][k2 * 1024]);
   issue_tile(0, 0);
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb)
@@ -646,12 +640,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_par_attn(ParParams p) {
 
 template <int DH>
 hipError_t launch_dh(const ParParams& p, hipStream_t s, hipEvent_t* ev) {
-  const int hpw = p.H % 4 == 0 ? 4 : (p.H % 2 == 0 ? 2 : 1);   // heads per prep workgroup
   hipLaunchKernelGGL((k_rope_table<DH>), dim3((p.n_pad * (DH / 2) + kThreads - 1) / kThreads), dim3(kThreads), 0, s, p);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_par_prep<DH>), dim3(p.n_pad / kPrepTokens, p.B, p.H / hpw), dim3(kThreads), 0, s, p, hpw);
-  e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_par_gather, dim3(p.n_pad / kTile, p.B, p.G), dim3(kThreads), 0, s, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -370,10 +370,10 @@ def test_parallel_null_structs_and_workspace():
         B.LLA_ERR_WORKSPACE_TOO_SMALL
     w = B.lla_parallel_workspace_bytes
     assert w(d, 2, 100) == w(d, 2, 256) < w(d, 2, 257) < w(d, 4, 257)
-    # rebuilt keys and values, rotated exact keys: 3 head-space rows of bf16
-    # per padded position, the gathered latents, and the (cos, sin) table
-    # (d_h / 2 fp32 pairs per position)
-    assert w(d, 1, 256) >= 256 * (3 * 16 * 128 + 1024) * 2 + 256 * 64 * 8
+    # rebuilt keys and values: 2 head-space rows of bf16 per padded position,
+    # the gathered latents, and the (cos, sin) table (d_h / 2 fp32 pairs per
+    # position)
+    assert w(d, 1, 256) >= 256 * (2 * 16 * 128 + 1024) * 2 + 256 * 64 * 8
     assert w(d, 0, 256) == 0 and w(d, 1, 0) == 0
 
 
