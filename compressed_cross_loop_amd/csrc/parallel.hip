@@ -315,7 +315,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_par_attn(ParParams p) {
   // x > k exactly when int(x) > int(k)), which needs no float
   // canonicalisation; the row sums of P come from one more product against
   // ones.  Runs only once every position's running maximum is a real score.
-  auto fast_tile = [&](int jt, int buf) {
+  auto fast_tile = [&](int buf) {
     const bf16* KL = kl_s[buf];
     const bf16* VL = vl_s[buf];
 #pragma unroll
@@ -608,7 +608,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_par_attn(ParParams p) {
   }
   for (; jt < jp; ++jt) {
     tile_start(jt);
-    fast_tile(jt, jt & 1);
+    fast_tile(jt & 1);
   }
   for (; jt < ntile; ++jt) {
     tile_start(jt);
