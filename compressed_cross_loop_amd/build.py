@@ -39,7 +39,8 @@ def build(verbose=False):
         if verbose and errs.strip():
             print(errs, file=sys.stderr)
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp] + [o for o, _ in results]
+    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp] + [o for o, _ in results] + \
+        ["-L/opt/rocm/lib", "-lhipblaslt"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stderr)

@@ -118,6 +118,15 @@ constexpr int kParQueryTile = 256;   // positions per attention workgroup (n_pad
 // events: optional pair recorded around the attention kernel
 hipError_t launch_parallel(const ParParams& p, hipStream_t s, hipEvent_t* events);
 
+// C[m][n] = sum_k X[m][k] Y[n][k] on hipBLASLt (X, Y bf16 row-major, leading
+// dims ldx, ldy; C fp32 or bf16, leading dim ldc), K made of nseg segments of
+// kseg elements, segment t at X + t sxk and Y + t syk (elements), summed into
+// C.  Returns false when the library does not take the shape or its setup
+// would fall inside a graph capture (then nothing was launched), or when a
+// launch failed; the caller then runs its own GEMM, which writes all of C.
+bool lt_gemm_nt(const void* X, const void* Y, void* C, bool c_f32, int64_t M, int64_t N, int64_t kseg, int nseg,
+                int64_t ldx, int64_t ldy, int64_t ldc, int64_t sxk, int64_t syk, hipStream_t s);
+
 hipError_t launch_qmap(const DecodeParams& p, bool want_qlat, hipStream_t s);
 hipError_t launch_window(const DecodeParams& p, hipStream_t s);
 hipError_t launch_scan_absorbed_generic(const DecodeParams& p, hipStream_t s);

@@ -190,7 +190,12 @@ hipError_t launch_writer_mfma(const WriterParams& p, hipStream_t s) {
     q.ldx = p.n_loops * p.G * p.d_in; q.sxg = p.d_in; q.sxk = (int64_t)p.G * p.d_in;
     q.ldy = p.d_in; q.syg = (int64_t)p.R * p.d_in; q.syk = (int64_t)p.G * p.R * p.d_in;
     q.ldc = p.G * p.R; q.scg = p.R;
-    e = launch_gemm(q, 1, s);
+    // one latent group: x's K range is contiguous per token and each loop's
+    // encoder a plain [R][d_in] matrix, so the vendor GEMM takes it (one
+    // product per loop, summed), else the tiled GEMM
+    const bool lib = p.G == 1 && lt_gemm_nt(q.X, q.Y, q.C, true, q.M, q.N, q.kseg, q.K / q.kseg, q.ldx, q.ldy,
+                                            q.ldc, q.sxk, q.syk, s);
+    e = lib ? hipSuccess : launch_gemm(q, 1, s);
   } else {
     const dim3 grid((p.R + kTileN - 1) / kTileN, (M + kTileM - 1) / kTileM, p.G * p.ksplit);
     hipLaunchKernelGGL(k_writer_mfma, grid, dim3(kThreads), 0, s, p);
