@@ -162,6 +162,95 @@ __global__ __launch_bounds__(kReduceThreads) void k_writer_reduce(WriterParams p
   finish_latent<bf16, kReduceThreads>(p, c, csn, pos, page, pos % p.P, g);
 }
 
+// Bulk bf16 writes (prompts, the training pass): one workgroup per 16
+// consecutive tokens.  When they are one sequence's positions 16 j .. 16 j +
+// 15 (the usual case) they fill one 16-token tile of the store, which the
+// workgroup assembles in LDS and writes as 16-byte pieces: key rows, and per
+// value dimension the 16 tokens that lie next to each other in the
+// dimension-major value sub-blocks.  Written token by token, every value
+// element is a 2-byte store of its own and the 16 tokens sharing 32 bytes
+// come from 16 workgroups.  Other groups take the per-token epilogue.  The
+// partial is a single fp32 row per token (no K split for bulk writes);
+// rotation and rounding are the per-token path's, in the same order.
+constexpr int kTileTok = 16;
+
+__global__ __launch_bounds__(kReduceThreads) void k_writer_reduce_tile(WriterParams p) {
+  extern __shared__ float c[];                 // [16][R]
+  __shared__ float csn[kTileTok][64][2];       // per token (cos, sin), d_h <= 128 (two workgroups per CU at R = 1024)
+  __shared__ double theta[64];                 // frequencies, shared by the 16 tokens
+  __shared__ int tpos[kTileTok];
+  __shared__ int tile_ok;
+  const int m0 = blockIdx.x * kTileTok, g = blockIdx.y, tid = threadIdx.x;
+  const int M = p.B * p.n_tok, R = p.R, G = p.G, rk = p.rk, rv = p.rv, dh = p.dh, half = dh / 2;
+  const int nt = min(kTileTok, M - m0);
+  if (tid < kTileTok) tpos[tid] = tid < nt ? p.pos[m0 + tid] : -1;
+  if (p.rope_baked && tid < half) theta[tid] = rope_theta(p.rope_base, dh, tid);
+  const float* src = p.acc + ((int64_t)m0 * G + g) * R;
+  for (int x = tid; x < nt * (R / 4); x += kReduceThreads) {
+    const int t = x / (R / 4), u = x % (R / 4);
+    reinterpret_cast<float4*>(c + t * R)[u] = reinterpret_cast<const float4*>(src + (int64_t)t * G * R)[u];
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int ok = nt == kTileTok && m0 / p.n_tok == (m0 + kTileTok - 1) / p.n_tok && tpos[0] % kTileTok == 0;
+    for (int t = 1; t < kTileTok && ok; ++t) ok = tpos[t] == tpos[0] + t;
+    tile_ok = ok;
+  }
+  if (p.rope_baked) {
+    for (int x = tid; x < nt * half; x += kReduceThreads) {
+      const int t = x / half, f = x % half;
+      float cs, sn;
+      rope_cs_theta(theta[f], tpos[t], cs, sn);
+      csn[t][f][0] = cs;
+      csn[t][f][1] = sn;
+    }
+    __syncthreads();
+    for (int x = tid; x < nt * (rk / 2); x += kReduceThreads) {
+      const int t = x / (rk / 2), y = x % (rk / 2), blk = y / half, f = y % half;
+      const int lo = blk * dh + f, hi = lo + half;
+      float* ct = c + t * R;
+      const float cs = csn[t][f][0], sn = csn[t][f][1];
+      const float a = ct[lo], b = ct[hi];
+      ct[lo] = a * cs - b * sn;
+      ct[hi] = a * sn + b * cs;
+    }
+  }
+  __syncthreads();
+  if (tile_ok) {
+    const int b = m0 / p.n_tok, pos0 = tpos[0];
+    const int64_t page = p.bt[(int64_t)b * p.max_pages + pos0 / p.P];
+    bf16* tile = static_cast<bf16*>(p.pages) + tile_base(page, g, pos0 % p.P, G, p.P, R);
+    for (int x = tid; x < kTileTok * (rk / 8); x += kReduceThreads) {   // key rows, 8 dims a piece
+      const int t = x / (rk / 8), d = 8 * (x % (rk / 8));
+      bf16x8 o;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = from_f<bf16>(c[t * R + d + e]);
+      *reinterpret_cast<bf16x8*>(tile + key_in_tile(t, d, rk)) = o;
+    }
+    for (int x = tid; x < rv * 2; x += kReduceThreads) {   // value dim d, tokens t8 .. t8 + 7
+      const int d = x / 2, t8 = 8 * (x % 2);
+      bf16x8 o;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = from_f<bf16>(c[(t8 + e) * R + rk + d]);
+      *reinterpret_cast<bf16x8*>(tile + 16 * rk + (d >> 4) * 256 + (d & 15) * 16 + t8) = o;
+    }
+  } else {
+    WriterParams q = p;
+    q.rope_baked = 0;   // rotated above
+    for (int t = 0; t < nt; ++t) {
+      const int m = m0 + t, pos = tpos[t];
+      const int64_t page = p.bt[(int64_t)(m / p.n_tok) * p.max_pages + pos / p.P];
+      finish_latent<bf16, kReduceThreads>(q, c + t * R, nullptr, pos, page, pos % p.P, g);
+    }
+  }
+}
+
+// the tile epilogue's shapes: bf16 store, 16-byte pieces, the 16 rows in 64 KiB of LDS
+bool reduce_tile_supports(const WriterParams& p) {
+  return p.bf16 && !p.fp8 && p.rk % 8 == 0 && p.rv % 16 == 0 && p.R % 4 == 0 &&
+         (size_t)kTileTok * p.R * sizeof(float) <= 65536 && p.dh <= 128;
+}
+
 }  // namespace
 
 bool writer_mfma_supports(const WriterParams& p) { return p.bf16 && p.d_in % 32 == 0; }
@@ -202,7 +291,11 @@ hipError_t launch_writer_mfma(const WriterParams& p, hipStream_t s) {
     e = hipGetLastError();
   }
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_writer_reduce, dim3(M, p.G), dim3(kReduceThreads), (size_t)p.R * sizeof(float), s, p);
+  if (M >= kBulkTokens && reduce_tile_supports(p))
+    hipLaunchKernelGGL(k_writer_reduce_tile, dim3((M + kTileTok - 1) / kTileTok, p.G), dim3(kReduceThreads),
+                       (size_t)kTileTok * p.R * sizeof(float), s, p);
+  else
+    hipLaunchKernelGGL(k_writer_reduce, dim3(M, p.G), dim3(kReduceThreads), (size_t)p.R * sizeof(float), s, p);
   return hipGetLastError();
 }
 
