@@ -25,15 +25,19 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 
 // ------------------------------------------------------------------ q map
-// grid (H, ceil(r_k / 512), ceil(B / 16)); wave w of a workgroup produces the
-// 128 latent columns n0 = 128 (4 blockIdx.y + w) .. n0 + 127 of q~ for 16
-// sequences.  q~[b][n] = sum_e q[b][e] A[e][n] runs on
+// grid (H, ceil(r_k / 128), ceil(B / 16)); the workgroup produces the 128
+// latent columns n0 = 128 blockIdx.y .. n0 + 127 of q~ for 16 sequences, its
+// four waves splitting the contraction over the head dims (wave w takes the
+// 32-wide k steps w, w + 4, ..): each wave reads a quarter of the
+// workgroup's 32 KiB slab of A^(h), and the four partial products are summed
+// through LDS.  q~[b][n] = sum_e q[b][e] A[e][n] runs on
 // v_mfma_f32_16x16x32_bf16, which wants 8 consecutive e per lane while rows
 // of A^(h) are contiguous along n: each lane loads 8 rows x 8 columns
 // (columns n0 + 8c .. n0 + 8c + 7, c = lane % 16) and regroups them in
 // registers, so product j yields the columns {n0 + 8c + j}.  With rotary the
 // partner column n +- d_h/2 of a pair then sits in lane c ^ (d_h / 16) of the
-// same product, one lane swap away.
+// same product, one lane swap away; after the sum wave w holds rows
+// 4 grp + w of the block, so the swap stays inside the wave.
 // Nothing waits for the operand loads before the products: the sequences'
 // rotation table is built while they are in flight (wave w takes sequences
 // w, w + 4, .. with their positions as scalar loads, lane f frequency f),
@@ -42,8 +46,10 @@ constexpr int kThreads = 256;
 template <int DH>
 __global__ __launch_bounds__(kThreads) void k_qmap_mfma(DecodeParams p, int want_qlat) {
   constexpr int KS = DH / 32;
+  constexpr int KW = (KS + 3) / 4;          // k steps per wave
   constexpr int NF = DH / 2;                // rotary frequency pairs
   __shared__ __attribute__((aligned(16))) float csn[16][NF][2];   // (cos, sin)
+  __shared__ float red[4][8][4][64];        // per-wave partial products [wave][j][r][lane]
   const int h = blockIdx.x, b0 = blockIdx.z * 16;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -51,41 +57,44 @@ __global__ __launch_bounds__(kThreads) void k_qmap_mfma(DecodeParams p, int want
   const int H = p.H, rk = p.rk;
   const bool rope = p.rope_base != 0.f;
   const bf16* q = static_cast<const bf16*>(p.q);
-  const int n0 = (blockIdx.y * 4 + wave) * 128;
-  const bool active = want_qlat && n0 < rk;   // uniform over the wave
+  const int n0 = blockIdx.y * 128;
+  const bool active = want_qlat && n0 < rk;   // uniform over the workgroup
   const int ncol = n0 + 8 * col;
   const bool do_qhead = blockIdx.y == 0 && p.need_qhead;
   const int fl = min(lane, NF - 1);
 
   // q of sequences wave + 4 k at dims fl and fl + NF (for q')
   float qa[4], qb[4];
+  if (do_qhead) {
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const bf16* qr = q + ((int64_t)min(b0 + wave + 4 * k, p.B - 1) * H + h) * DH;
-    qa[k] = to_f(qr[fl]);
-    qb[k] = to_f(qr[fl + NF]);
+    for (int k = 0; k < 4; ++k) {
+      const bf16* qr = q + ((int64_t)min(b0 + wave + 4 * k, p.B - 1) * H + h) * DH;
+      qa[k] = to_f(qr[fl]);
+      qb[k] = to_f(qr[fl + NF]);
+    }
   }
-  // A^(h) rows e = 32 st + 8 grp + i, columns ncol .. ncol + 7 (clamped into
-  // the row; lanes past r_k store nothing)
-  bf16x8 araw[KS][8];
+  // A^(h) rows e = 32 st + 8 grp + i of this wave's k steps, columns ncol ..
+  // ncol + 7 (clamped into the row; lanes past r_k store nothing)
+  bf16x8 araw[KW][8];
+  bf16x8 aq[KW];
+  const int brow = b0 + col;
   if (active) {
     const bf16* Ah = static_cast<const bf16*>(p.A) + (int64_t)h * DH * rk + min(ncol, rk - 8);
 #pragma unroll
-    for (int st = 0; st < KS; ++st)
+    for (int u = 0; u < KW; ++u) {
+      const int st = wave + 4 * u;
+      if (st < KS) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        araw[st][i] = *reinterpret_cast<const bf16x8*>(Ah + (int64_t)(32 * st + 8 * grp + i) * rk);
-  }
-  // A operand: q row of sequence b0 + col (rows past the batch read the last
-  // sequence and are zeroed), dims 32 st + 8 grp ..
-  const int brow = b0 + col;
-  bf16x8 aq[KS];
+        for (int i = 0; i < 8; ++i)
+          araw[u][i] = *reinterpret_cast<const bf16x8*>(Ah + (int64_t)(32 * st + 8 * grp + i) * rk);
+        // A operand: q row of sequence b0 + col (rows past the batch read the
+        // last sequence and are zeroed), dims 32 st + 8 grp ..
+        aq[u] = *reinterpret_cast<const bf16x8*>(q + ((int64_t)min(brow, p.B - 1) * H + h) * DH + st * 32 + grp * 8);
+        if (brow >= p.B) {
 #pragma unroll
-  for (int st = 0; st < KS; ++st) {
-    aq[st] = *reinterpret_cast<const bf16x8*>(q + ((int64_t)min(brow, p.B - 1) * H + h) * DH + st * 32 + grp * 8);
-    if (brow >= p.B) {
-#pragma unroll
-      for (int k = 0; k < 8; ++k) aq[st][k] = static_cast<bf16>(0.f);
+          for (int k = 0; k < 8; ++k) aq[u][k] = static_cast<bf16>(0.f);
+        }
+      }
     }
   }
   if (rope) {
@@ -102,52 +111,64 @@ __global__ __launch_bounds__(kThreads) void k_qmap_mfma(DecodeParams p, int want
       }
     }
   }
-  __syncthreads();
 
   if (active) {
     f32x4 acc[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int st = 0; st < KS; ++st)
+    for (int u = 0; u < KW; ++u) {
+      if (wave + 4 * u < KS) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        bf16x8 bj;
+        for (int j = 0; j < 8; ++j) {
+          bf16x8 bj;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) bj[i] = araw[st][i][j];
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[st], bj, acc[j], 0, 0, 0);
+          for (int i = 0; i < 8; ++i) bj[i] = araw[u][i][j];
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[u], bj, acc[j], 0, 0, 0);
+        }
       }
-    // lane: C[b0 + 4 grp + r][ncol + j]
+    }
+    // lane: C[b0 + 4 grp + r][ncol + j] of this wave's k steps
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[wave][j][r][lane] = acc[j][r];
+  }
+  __syncthreads();
+  if (active) {
+    // wave w: row r = w of every lane's 4 x 8 block, summed over the waves
+    const int r = wave;
+    float mine[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      mine[j] = (red[0][j][r][lane] + red[1][j][r][lane]) + (red[2][j][r][lane] + red[3][j][r][lane]);
     bf16* ql = static_cast<bf16*>(p.qlat);
     const bool lo_half = (8 * col) % DH < DH / 2;   // n0 is a multiple of d_h
     const int f0 = (8 * col) % (DH / 2);
+    const int bl = 4 * grp + r, bb = b0 + bl;
+    float v[8];
+    if (rope) {
+      const float4* cs = reinterpret_cast<const float4*>(&csn[bl][f0][0]);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int bl = 4 * grp + r, bb = b0 + bl;
-      float v[8];
-      if (rope) {
-        const float4* cs = reinterpret_cast<const float4*>(&csn[bl][f0][0]);
+      for (int j2 = 0; j2 < 4; ++j2) {
+        const float4 t = cs[j2];   // (cos, sin) of frequencies f0 + 2 j2, f0 + 2 j2 + 1
 #pragma unroll
-        for (int j2 = 0; j2 < 4; ++j2) {
-          const float4 t = cs[j2];   // (cos, sin) of frequencies f0 + 2 j2, f0 + 2 j2 + 1
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int j = 2 * j2 + u;
-            const float c = u ? t.z : t.x, sn = u ? t.w : t.y;
-            const float mine = acc[j][r], other = __shfl_xor(mine, DH / 16);
-            v[j] = lo_half ? (mine * c - other * sn) : (other * sn + mine * c);
-          }
+        for (int u = 0; u < 2; ++u) {
+          const int j = 2 * j2 + u;
+          const float c = u ? t.z : t.x, sn = u ? t.w : t.y;
+          const float other = __shfl_xor(mine[j], DH / 16);
+          v[j] = lo_half ? (mine[j] * c - other * sn) : (other * sn + mine[j] * c);
         }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = acc[j][r];
       }
-      if (bb < p.B && ncol < rk) {
-        bf16x8 o;
+    } else {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) o[j] = static_cast<bf16>(v[j] * p.scale);
-        *reinterpret_cast<bf16x8*>(ql + ((int64_t)bb * H + h) * rk + ncol) = o;
-      }
+      for (int j = 0; j < 8; ++j) v[j] = mine[j];
+    }
+    if (bb < p.B && ncol < rk) {
+      bf16x8 o;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) o[j] = static_cast<bf16>(v[j] * p.scale);
+      *reinterpret_cast<bf16x8*>(ql + ((int64_t)bb * H + h) * rk + ncol) = o;
     }
   }
   // q' = s R_i q (head space, fp32) when a later kernel reads it
@@ -292,7 +313,10 @@ __global__ __launch_bounds__(kThreads) void k_window_fast(DecodeParams p) {
 }
 
 // ------------------------------------------------------------------ combine
-// grid (H, ceil(B / 16)); 4 waves; out[b][h] for 16 sequences, d_h = 128.
+// grid (H, ceil(B / 16), 4); 4 waves; out[b][h] for 16 sequences and the 32
+// output dims 32 blockIdx.z .. + 31 of d_h = 128 (the four workgroups of a
+// (head, sequence block) each read a quarter of B_t; they sit 128 workgroup
+// ids apart, on one XCD, and share its L2 for the partials they all merge).
 // The B_t^T product runs on v_mfma_f32_16x16x32_bf16.  The value decoder is
 // stored as B_t^T [d_h][r_v] (rows contiguous along the latent axis), so each
 // B-operand fragment (8 consecutive latent dims of one output column) is one
@@ -310,15 +334,16 @@ __global__ __launch_bounds__(kThreads) void k_window_fast(DecodeParams p) {
 template <int RV, bool PART>
 __global__ __launch_bounds__(kThreads) void k_combine_mfma(DecodeParams p) {
   constexpr int DH = 128;
-  constexpr int NT = DH / 16;              // output column tiles
+  constexpr int NT = 2;                    // output column tiles of this workgroup
   constexpr int KS = RV / 32;              // k steps
   constexpr int KW = (KS + 3) / 4;         // k steps per wave
   __shared__ float ob[16][RV + 1];         // latent-space sums
   __shared__ float wo[16][DH];             // window sums
   __shared__ float wl[16];                 // 1 / l
-  __shared__ __attribute__((aligned(16))) float red[4][16][DH + 4];   // per-wave products
+  __shared__ __attribute__((aligned(16))) float red[4][16][16 * NT + 4];   // per-wave products
   const int H = p.H, S = p.S, WS = p.WS;
   const int h = blockIdx.x, b0 = blockIdx.y * 16, tid = threadIdx.x;
+  const int e0 = 16 * NT * blockIdx.z;     // first output dim of this workgroup
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
   const bf16* Bh = static_cast<const bf16*>(p.Bm) + (int64_t)h * DH * RV;   // [DH][RV]
@@ -329,7 +354,7 @@ __global__ __launch_bounds__(kThreads) void k_combine_mfma(DecodeParams p) {
     if (st < KS) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
-        bfr[u][nt] = *reinterpret_cast<const bf16x8*>(Bh + (int64_t)(16 * nt + col) * RV + 32 * st + 8 * grp);
+        bfr[u][nt] = *reinterpret_cast<const bf16x8*>(Bh + (int64_t)(e0 + 16 * nt + col) * RV + 32 * st + 8 * grp);
     }
   }
 
@@ -600,18 +625,18 @@ __global__ __launch_bounds__(kThreads) void k_combine_mfma(DecodeParams p) {
       }
     }
   }
-  // lane holds C[b = 4 grp + r][e = 16 nt + col]
+  // lane holds C[b = 4 grp + r][e = e0 + 16 nt + col]
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
     for (int r = 0; r < 4; ++r) red[wave][4 * grp + r][16 * nt + col] = acc[nt][r];
   __syncthreads();
-  {
-    const int bl = tid / 16, e8 = (tid % 16) * 8, b = b0 + bl;
+  if (tid < 16 * (16 * NT / 8)) {
+    const int bl = tid / (2 * NT), e8 = (tid % (2 * NT)) * 8, b = b0 + bl;
     if (b < p.B) {
       float v[8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] = wo[bl][e8 + k];
+      for (int k = 0; k < 8; ++k) v[k] = wo[bl][e0 + e8 + k];
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         const float4 x0 = *reinterpret_cast<const float4*>(&red[w][bl][e8]);
@@ -622,14 +647,14 @@ __global__ __launch_bounds__(kThreads) void k_combine_mfma(DecodeParams p) {
       bf16x8 o;
 #pragma unroll
       for (int k = 0; k < 8; ++k) o[k] = static_cast<bf16>(v[k] * wl[bl]);
-      *reinterpret_cast<bf16x8*>(static_cast<bf16*>(p.out) + ((int64_t)b * H + h) * DH + e8) = o;
+      *reinterpret_cast<bf16x8*>(static_cast<bf16*>(p.out) + ((int64_t)b * H + h) * DH + e0 + e8) = o;
     }
   }
 }
 
 template <int DH>
 hipError_t qmap_launch(const DecodeParams& p, bool want, hipStream_t s) {
-  const dim3 grid(p.H, want ? (p.rk + 511) / 512 : 1, (p.B + 15) / 16);
+  const dim3 grid(p.H, want ? (p.rk + 127) / 128 : 1, (p.B + 15) / 16);
   hipLaunchKernelGGL((k_qmap_mfma<DH>), grid, dim3(kThreads), 0, s, p, want ? 1 : 0);
   return hipGetLastError();
 }
@@ -669,7 +694,7 @@ bool combine_mfma_supports(const DecodeParams& p) {
 
 hipError_t launch_combine_mfma(const DecodeParams& p, hipStream_t s) {
   if (!combine_mfma_supports(p)) return hipErrorNotSupported;
-  const dim3 grid(p.H, (p.B + 15) / 16);
+  const dim3 grid(p.H, (p.B + 15) / 16, 4);
   if (p.B % 16 != 0) {
     switch (p.rv) {
       case 32: hipLaunchKernelGGL((k_combine_mfma<32, true>), grid, dim3(kThreads), 0, s, p); break;
