@@ -217,7 +217,7 @@ Plan plan_for(const lla_set_desc& d, int batch, int max_pos, int window, int spl
       return make_plan(batch, max_pos, window, splits, scan_absorbed_wide_slabs(d.r_v), target, kChunk,
                        kCombineMaxParts / 2);
     case Scan::kReconstructMfma:
-      wgs = (d.n_heads + 3) / 4;
+      wgs = d.n_heads;                    // one head per workgroup
       target = 2 * kTargetWorkgroups;   // small workgroups: two resident per CU
       break;
     case Scan::kReconstructGemm:

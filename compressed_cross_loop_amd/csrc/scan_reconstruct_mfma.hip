@@ -2,10 +2,11 @@
 // gfx950 matrix cores ("Looped Latent Attention" abstracts: the codec keeps
 // only latents and rebuilds a loop's keys and values when attention reads them).
 //
-// One wave per head (each head has its own latent group), four waves per
-// workgroup, one workgroup per (context split, sequence, 4 heads).  Per
-// 16-token tile the wave rebuilds, for its head, the transposed keys and
-// values
+// One workgroup per (context split, sequence, head); each head has its own
+// latent group, and the four waves take interleaved 16-token tiles of the
+// split (wave w: tiles w, w + 4, ..), so a workgroup streams one contiguous
+// run of its group's tiles per page.  Per 16-token tile the wave rebuilds,
+// for the head, the transposed keys and values
 //   K^T [d_h x 16 tok] = A_t [d_h x r] . S^K^T [r x 16]   (v_mfma_f32_16x16x32_bf16)
 //   V^T [d_h x 16 tok] = B_t^T [d_h x r] . S^V^T [r x 16]
 // so that every lane ends with 4 dims of each 16-dim block for ONE token
@@ -16,7 +17,9 @@
 //   p      2^(score - m), running maximum m moved lazily (only when a tile's
 //          maximum exceeds it by more than 2^8), so rescaling is rare
 //   o      += p v^_tok for the lane's dims; o and the weight sum stay per
-//          token lane and are summed over the 16 token lanes once per split.
+//          token lane and are summed over the 16 token lanes once per split;
+//          the four waves' (m, l, o) are then merged in LDS (same-max
+//          rescale, fixed order) into the split's one partial.
 // Both decoders are stored [d_h][r] (rows contiguous along the latent axis),
 // i.e. directly in A-operand layout; they are held in registers for the whole
 // scan.  Key rows are token-major in the store: one 16-byte load per lane is
@@ -35,8 +38,9 @@
 // partner of dim d is d +- d_h/2, i.e. block nt +- NT/2 of the same lane),
 // and split s also takes slice s of the exact tokens of Eq. 4 (ring tokens
 // i-W .. i-1 and the current one, 16 per step in the same token-per-lane
-// layout, read straight from the ring rows) into the same running softmax;
-// the lanes holding the current token append R_i k_cur, v_cur to the ring.
+// layout, read straight from the ring rows, the steps dealt to the waves in
+// turn) into the same running softmax; the lanes holding the current token
+// append R_i k_cur, v_cur to the ring.
 #include <type_traits>
 #include <utility>
 
@@ -80,11 +84,13 @@ __global__ __launch_bounds__(kThreads, (R == 32 || DH == 64) ? 2 : 1) void k_sca
   __shared__ int32_t ptab[kPageTab];
   __shared__ __attribute__((aligned(16))) unsigned char vlds[kWaves][KS * 1024];
   __shared__ float csn[DH / 2][2];       // (cos, sin) of i theta_f
+  __shared__ float mrg_o[kWaves][DH];    // per-wave (m, l, o) for the merge
+  __shared__ float mrg_ml[kWaves][2];
   const int s = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
-  const int h = blockIdx.z * kWaves + wave;
+  const int h = blockIdx.z;
   const int G = p.G, P = p.P, Rt = 2 * R;
   const int i = p.pos[b];
   const int n_lat = max(0, i - p.W);
@@ -105,7 +111,6 @@ __global__ __launch_bounds__(kThreads, (R == 32 || DH == 64) ? 2 : 1) void k_sca
     csn[tid][1] = sn;
   }
   __syncthreads();
-  if (h >= p.H) return;                  // wave-uniform; no barrier follows
   const int g = h / p.hpg;
   // R_i x at this lane's dims 16 nt + 4 grp + r, from x at the same dims
   auto rotate = [&](f32x4 (&x)[NT]) {
@@ -156,8 +161,10 @@ __global__ __launch_bounds__(kThreads, (R == 32 || DH == 64) ? 2 : 1) void k_sca
 
   const bf16* pages = static_cast<const bf16*>(p.pages);
   const int ntiles = (t1 - t0 + 15) / 16;
-  auto tile_ptr = [&](int ti) -> const bf16* {
-    const int j0 = t0 + min(ti, ntiles - 1) * 16;
+  // this wave's tiles w, w + 4, ..: local index lt is tile w + 4 lt
+  const int ntw = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
+  auto tile_ptr = [&](int lt) -> const bf16* {
+    const int j0 = t0 + (wave + kWaves * min(lt, ntw - 1)) * 16;
     const int pg = __builtin_amdgcn_readfirstlane(ptab[j0 / P - pfirst]);
     return pages + tile_base(pg, g, j0 % P, G, P, Rt);
   };
@@ -259,7 +266,7 @@ __global__ __launch_bounds__(kThreads, (R == 32 || DH == 64) ? 2 : 1) void k_sca
   // decoders and q' have landed before the tile loads start: the loop's waits
   // then only count tile loads, which complete in issue order
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-  if (ntiles > 0) {
+  if (ntw > 0) {                         // wave-uniform
     // prologue in slot order (the loop's waits assume loads complete in it)
     static_for<kPF>([&](auto U) {
       issue(U, decltype(U)::value);
@@ -268,8 +275,9 @@ __global__ __launch_bounds__(kThreads, (R == 32 || DH == 64) ? 2 : 1) void k_sca
     // main loop over whole groups of full tiles: no branches in the body, so
     // every register set is refilled in place and the waits count exactly
     const int nfull = (t1 - t0) / 16;
+    const int nfw = nfull > wave ? (nfull - wave + kWaves - 1) / kWaves : 0;
     int base = 0;
-    for (; base + kPF <= nfull; base += kPF) {
+    for (; base + kPF <= nfw; base += kPF) {
       static_for<kPF>([&](auto U) {
         step(U, 16, std::true_type{});
         __builtin_amdgcn_sched_barrier(0);   // keep each refill below its consumer
@@ -280,8 +288,8 @@ __global__ __launch_bounds__(kThreads, (R == 32 || DH == 64) ? 2 : 1) void k_sca
     // the rest (fewer than kPF full tiles and a ragged last one) is already in flight
     static_for<kPF>([&](auto U) {
       constexpr int u = decltype(U)::value;
-      if (base + u < ntiles) {
-        const int nvalid = min(16, t1 - (t0 + (base + u) * 16));
+      if (base + u < ntw) {
+        const int nvalid = min(16, t1 - (t0 + (wave + kWaves * (base + u)) * 16));
         if (nvalid == 16)
           step(U, 16, std::true_type{});
         else
@@ -298,7 +306,7 @@ __global__ __launch_bounds__(kThreads, (R == 32 || DH == 64) ? 2 : 1) void k_sca
     const int64_t rs = (int64_t)p.H * DH;                 // elements per ring slot
     const bf16* ring_k = static_cast<const bf16*>(p.ring_k);
     const bf16* ring_v = static_cast<const bf16*>(p.ring_v);
-    for (int tb = e0; tb < e1; tb += 16) {
+    for (int tb = e0 + 16 * wave; tb < e1; tb += 16 * kWaves) {
       const int t = tb + col;
       const bool valid = t < e1;
       f32x4 kx[NT], vx[NT];
@@ -360,20 +368,44 @@ __global__ __launch_bounds__(kThreads, (R == 32 || DH == 64) ? 2 : 1) void k_sca
   for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
     for (int r = 0; r < 4; ++r) o[nt][r] = row_sum16(o[nt][r]);
-  const int64_t row = ((int64_t)b * p.S + s) * p.H + h;
+  // merge of the four waves (each m is wave-uniform)
   if (lane == 0) {
-    p.part_ml[row * 2 + 0] = m;
-    p.part_ml[row * 2 + 1] = lsum;
+    mrg_ml[wave][0] = m;
+    mrg_ml[wave][1] = lsum;
   }
   if (col == 0) {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) *reinterpret_cast<f32x4*>(p.part_o + row * p.Dp + 16 * nt + 4 * grp) = o[nt];
+    for (int nt = 0; nt < NT; ++nt) *reinterpret_cast<f32x4*>(&mrg_o[wave][16 * nt + 4 * grp]) = o[nt];
+  }
+  __syncthreads();
+  if (wave == 0) {
+    float M = mrg_ml[0][0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, mrg_ml[w][0]);
+    float wt[kWaves], L = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      wt[w] = exp2_diff(mrg_ml[w][0], M);
+      L += wt[w] * mrg_ml[w][1];
+    }
+    const int64_t row = ((int64_t)b * p.S + s) * p.H + h;
+    if (lane == 0) {
+      p.part_ml[row * 2 + 0] = M;
+      p.part_ml[row * 2 + 1] = L;
+    }
+#pragma unroll
+    for (int d = lane; d < DH; d += 64) {
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) v += wt[w] * mrg_o[w][d];
+      p.part_o[row * p.Dp + d] = v;
+    }
   }
 }
 
 template <int R, int DH>
 hipError_t launch_r(const DecodeParams& p, hipStream_t st) {
-  const dim3 grid(p.S, p.B, (p.H + kWaves - 1) / kWaves);
+  const dim3 grid(p.S, p.B, p.H);
   hipLaunchKernelGGL((k_scan_reconstruct_mfma<R, DH>), grid, dim3(kThreads), 0, st, p);
   return hipGetLastError();
 }
