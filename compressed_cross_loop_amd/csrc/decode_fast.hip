@@ -364,6 +364,7 @@ __global__ __launch_bounds__(kThreads) void k_combine_mfma(DecodeParams p) {
   // full16: thread -> (sequence fbl, float4 columns fk4, fk4 + 16, .., and 8
   // window dims from fe8)
   const int fbl = tid / 16, fk4 = tid % 16, fe8 = (tid % 16) * 8, fb = b0 + fbl;
+  const bool wmine = (fe8 >> 5) == (int)blockIdx.z;   // window dims this workgroup outputs
   f32x4 pv[2][PER], wv[2][2];
   if (full16) {
 #pragma unroll
@@ -382,7 +383,7 @@ __global__ __launch_bounds__(kThreads) void k_combine_mfma(DecodeParams p) {
     }
 #pragma unroll
     for (int ss = 0; ss < 2; ++ss) {
-      if (WS > 0) {
+      if (WS > 0 && wmine) {
         const float4* src = reinterpret_cast<const float4*>(
             p.win_o + (((int64_t)fb * WS + min(ss, WS - 1)) * H + h) * DH + fe8);
         const float4 a = src[0], c = src[1];
@@ -577,7 +578,7 @@ __global__ __launch_bounds__(kThreads) void k_combine_mfma(DecodeParams p) {
         w1 += w * wv[ss][1];
       }
     }
-    for (int s0 = 2; s0 < WS; s0 += 4) {
+    for (int s0 = 2; s0 < (wmine ? WS : 0); s0 += 4) {
       f32x4 v[4][2];
 #pragma unroll
       for (int ss = 0; ss < 4; ++ss) {
