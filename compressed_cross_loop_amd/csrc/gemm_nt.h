@@ -7,7 +7,7 @@
 // loads in the natural row-major layouts).  BN = 256 (waves of 64 x 128)
 // reads a quarter fewer LDS bytes per product than BN = 128 and each Y row
 // half as often; it serves the wide rebuilds of the parallel pass (N a
-// multiple of 256).  K steps of BK staged in LDS and
+// multiple of 256, K of 512 up to 1023).  K steps of BK staged in LDS and
 // double-buffered (the next step's loads in flight during the products): BK =
 // 64 for long reductions whose K segments allow it (one barrier per 32
 // products of a wave), else 32.  K may be made of segments of kseg elements that lie apart in
@@ -169,8 +169,10 @@ __global__ __launch_bounds__(256, BN == 256 ? 2 : 1) void k_gemm_nt(GemmParams<T
 
 template <typename TC>
 hipError_t launch_gemm(const GemmParams<TC>& g, int batches, hipStream_t s) {
-  if (std::is_same<TC, bf16>::value && g.N % 256 == 0 && g.K < 1024) {
-    // wide bf16 outputs (the parallel pass's rebuild, N = heads x d_h)
+  if (std::is_same<TC, bf16>::value && g.N % 256 == 0 && g.K >= 512 && g.K < 1024) {
+    // wide bf16 outputs (the parallel pass's rebuild, N = heads x d_h):
+    // median 51.3 -> 49.1 us at K = 512; at K = 256 the 128 x 128 tiles are
+    // faster (31.1 against 32.6 us)
     const dim3 grid(g.N / 256, (g.M + 127) / 128, batches * g.G);
     hipLaunchKernelGGL((k_gemm_nt<TC, 32, 256>), grid, dim3(256), 0, s, g);
     return hipGetLastError();
