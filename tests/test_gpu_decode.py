@@ -146,6 +146,31 @@ def test_reconstruct_per_head_shapes(r, d_h, H, generic):
     check(c, "reconstruct", "textbook", splits=3, flags=1 if generic else 0)
 
 
+@pytest.mark.parametrize("splits", [1, 2])
+def test_reconstruct_per_head_long_window(splits):
+    """Per-head reconstruct with a window of 100 exact tokens: a split's exact
+    steps of 16 tokens are dealt to the four waves of its workgroup in turn
+    (the current token's ring append included); position 64 < W leaves no
+    latent token at all."""
+    c = per_head_case(470 + splits, positions=(333, 120, 64), W=100)
+    check(c, "reconstruct", "textbook", splits=splits)
+
+
+@pytest.mark.parametrize("d_h, r, rope", [(64, 192, True), (128, 208, False)])
+def test_qmap_partial_column_block(d_h, r, rope):
+    """Matrix-core query map with latent widths that are not a whole number
+    of its 128-column blocks (the last block partly past r_k; with rotary the
+    partner columns stay inside it), two latent groups so that the one-pass
+    general scan reads q~ (the HLA entry takes one group only, whose wide
+    shapes have their own query map)."""
+    c = gen.decode_inputs(480 + r, batch=3, heads=4, head_dim=d_h, groups=2, r_k=r, r_v=r,
+                          positions=(400, 77, 5), window=5, dtype="bf16",
+                          rope_base=10000.0 if rope else 0.0, rope_baked=int(rope), loop=2,
+                          loop_first=1, loop_last=3, latent_std=np.sqrt(3.0), exact_std=np.sqrt(3.0),
+                          paired=rope)
+    check(poison_unread(c), "absorbed", "absorbed")
+
+
 @pytest.mark.parametrize("generic", [False, True])
 def test_lla_d_per_head_bf16(generic):
     check(per_head_case(410), "absorbed", "absorbed", flags=1 if generic else 0)
