@@ -1,7 +1,8 @@
 // bf16 decode kernels around the latent scan, shaped for gfx950:
-//   k_qmap_mfma     q~ = s R~_i A_t^T q for a block of sequences and 128
-//                   latent columns per wave, on the matrix cores; the latent
-//                   rotation pairs (f, f + d_h/2) land one lane swap apart, so
+//   k_qmap_mfma     q~ = s R~_i A_t^T q for a block of 16 sequences and 128
+//                   latent columns per workgroup (its waves split the d_h
+//                   contraction), on the matrix cores; the latent rotation
+//                   pairs (f, f + d_h/2) land one lane swap apart, so
 //                   R~_i is applied in registers ("Hybrid Latent Attention"
 //                   summary, "Latent Reader" Eq. 3, "Rotary Embedding
 //                   Alignment")
@@ -11,7 +12,8 @@
 //                   contiguous [H][d_h] ring rows), per-head online softmax
 //   k_combine_mfma  merge of the latent and window partials of 16 sequences
 //                   and one head, then o = (B_t^T O_latent + O_window) / l
-//                   with the B_t^T product on the bf16 matrix cores
+//                   for 32 of the head's output dims per workgroup, with the
+//                   B_t^T product on the bf16 matrix cores
 #include "device_common.h"
 #include "lla_internal.h"
 
