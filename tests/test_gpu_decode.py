@@ -58,6 +58,17 @@ def test_hla_bf16_window_slices(W, positions):
     check(hla_case(150 + W, positions=positions, W=W), "hla", "absorbed", flags=1)
 
 
+@pytest.mark.parametrize("r, loop", [(512, 3), (256, 1)])
+@pytest.mark.parametrize("positions", [(4095,), (16383,), (700,), (4095, 300, 2000, 77, 1500)])
+def test_hla_small_batch_combine(r, loop, positions):
+    """Batches below 16: the matrix-core combine's small-batch form requests
+    the first sequence's split rows and window slices at entry; at 16k the
+    plan's 80 splits and 80 window slices take a second round of both, and
+    with five sequences the others load theirs after the merge."""
+    c = hla_case(820 + sum(positions) % 97 + r, r=r, positions=positions, W=128, loop=loop)
+    check(c, "hla", "absorbed")
+
+
 def test_hla_bf16_many_splits():
     """More context splits than the fast combine takes: the general combine merges them."""
     c = hla_case(160, positions=(4700,), W=16)
