@@ -44,6 +44,7 @@ constexpr int kSlab = 256;                        // values: r_v dims per workgr
 constexpr int kWidePageTab = kWideMaxPages;       // page ids of one split, in LDS
 constexpr int kSoftmaxLdsTokens = 16384;          // longest score row the softmax pass keeps in LDS (64 KiB)
 constexpr int kScoreWorkgroups = 512;             // score-pass workgroups aimed at (two rounds of one per CU)
+constexpr int kXcds = 8;                          // XCDs of the GPU; workgroups are dealt to them round-robin
 
 template <typename F, int... U>
 __device__ __forceinline__ void wide_static_for_impl(F&& f, std::integer_sequence<int, U...>) {
@@ -71,14 +72,26 @@ __device__ __forceinline__ int latent_tokens(const DecodeParams& p, int b) {
 constexpr int kKeyAhead = 4;      // = steps per q~ chunk (the key ring index is the step in the chunk)
 constexpr int kQChunk = 128;      // latent dims per staged q~ chunk
 
-__global__ __launch_bounds__(kScoreThreads) void k_scan_absorbed_wide_scores(DecodeParams p) {
+__global__ __launch_bounds__(kScoreThreads) void k_scan_absorbed_wide_scores(DecodeParams p, int by_xcd) {
   __shared__ __attribute__((aligned(16))) bf16 qs[2][64 * kQChunk];
-  const int b = blockIdx.y;
+  // workgroup -> (token block, sequence, part of r_k); with `by_xcd` the grid
+  // is one-dimensional and the ids of one sequence's workgroups are
+  // congruent mod 8, so the round-robin dealing puts them on one XCD and
+  // its L2 serves their q~ re-reads
+  int wx = blockIdx.x, wb = blockIdx.y, wz = blockIdx.z;
+  if (by_xcd) {
+    const int nx = p.lcap / kTokPerBlock, per = nx * p.wsplit;
+    const int L = blockIdx.x, xcd = L % kXcds, k = L / kXcds;
+    wb = (k / per) * kXcds + xcd;
+    wx = (k % per) % nx;
+    wz = (k % per) / nx;
+  }
+  const int b = wb;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
   const int n_lat = latent_tokens(p, b);
-  const int tb = blockIdx.x * kTokPerBlock;
+  const int tb = wx * kTokPerBlock;
   if (tb >= n_lat) return;                       // workgroup-uniform
   // waves past the last latent token compute on clamped tokens and store nothing
   const int tw = tb + wave * kTokPerWave;
@@ -146,11 +159,11 @@ __global__ __launch_bounds__(kScoreThreads) void k_scan_absorbed_wide_scores(Dec
       for (int hb = 0; hb < 4; ++hb)
         acc[i][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[u][i], qa[hb], acc[i][hb], 0, 0, 0);
   };
-  // q~ chunks of this workgroup's part of r_k (blockIdx.z of wsplit parts,
+  // q~ chunks of this workgroup's part of r_k (part wz of wsplit parts,
   // none empty); every chunk but the last of r_k is whole
   const int nch = (nk + kKeyAhead - 1) / kKeyAhead;
   const int cpz = (nch + p.wsplit - 1) / p.wsplit;
-  const int c0 = blockIdx.z * cpz, c1 = min(nch, c0 + cpz);
+  const int c0 = wz * cpz, c1 = min(nch, c0 + cpz);
   wide_static_for<kKeyAhead>([&](auto U) { issue(U, kKeyAhead * c0 + decltype(U)::value); });
   q_load(kQChunk * c0);
   q_store(0);
@@ -176,7 +189,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_scan_absorbed_wide_scores(Dec
   for (int hb = 0; hb < 4; ++hb) {
     const int h = 16 * hb + col;
     if (h >= H) continue;
-    float* srow = p.wscore + (((int64_t)blockIdx.z * p.B + b) * H + h) * p.lcap + tw + 4 * grp;
+    float* srow = p.wscore + (((int64_t)wz * p.B + b) * H + h) * p.lcap + tw + 4 * grp;
 #pragma unroll
     for (int i = 0; i < 4; ++i) *reinterpret_cast<f32x4*>(srow + 16 * i) = acc[i][hb];
   }
@@ -268,10 +281,22 @@ constexpr int kTileAhead = 4;                 // value tiles in flight per wave
 constexpr int kPChunk = 128;                  // tokens per staged probability chunk (8 tiles)
 constexpr int kPRow = kPChunk + 8;            // its LDS row (bf16)
 
-__global__ __launch_bounds__(kThreads, 2) void k_scan_absorbed_wide_values(DecodeParams p) {
+__global__ __launch_bounds__(kThreads, 2) void k_scan_absorbed_wide_values(DecodeParams p, int by_xcd) {
   __shared__ int32_t ptab[kWidePageTab];
   __shared__ __attribute__((aligned(16))) bf16 ps[2][64 * kPRow];
-  const int s = blockIdx.y, b = blockIdx.z;
+  // workgroup -> (slab, split, sequence); with `by_xcd` the grid is
+  // one-dimensional and the ids of one sequence's workgroups are congruent
+  // mod 8, so they share one XCD and its L2 serves their re-reads of the
+  // sequence's probabilities
+  int ws_ = blockIdx.x, ss = blockIdx.y, sb = blockIdx.z;
+  if (by_xcd) {
+    const int nsl = (p.rv + kSlab - 1) / kSlab, per = nsl * p.S;
+    const int L = blockIdx.x, xcd = L % kXcds, k = L / kXcds;
+    sb = (k / per) * kXcds + xcd;
+    ws_ = (k % per) % nsl;
+    ss = (k % per) / nsl;
+  }
+  const int s = ss, b = sb;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
@@ -288,7 +313,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_scan_absorbed_wide_values(Decod
   __syncthreads();
   const int nblk = rv / 16;
   // waves past the last value block load clamped blocks and store nothing
-  const int db0 = blockIdx.x * (kSlab / 16) + 4 * wave;
+  const int db0 = ws_ * (kSlab / 16) + 4 * wave;
   int voff[4];
 #pragma unroll
   for (int jb = 0; jb < 4; ++jb) voff[jb] = 16 * rk + min(db0 + jb, nblk - 1) * 256 + col * 16 + 4 * grp;
@@ -437,7 +462,13 @@ hipError_t launch_scan_absorbed_wide(const DecodeParams& p, hipStream_t s) {
   if (!scan_absorbed_wide_supports(p) || p.lcap % kTokPerBlock || !p.wscore || !p.wprob ||
       p.wsplit != scan_absorbed_wide_ksplit(p.B, p.lcap, p.rk))
     return hipErrorNotSupported;
-  hipLaunchKernelGGL(k_scan_absorbed_wide_scores, dim3(p.lcap / kTokPerBlock, p.B, p.wsplit), dim3(kScoreThreads), 0, s, p);
+  // a sequence's score workgroups on one XCD when every XCD still gets
+  // sequences (batch a multiple of 8), else the plain three-dimensional grid
+  const int nx = p.lcap / kTokPerBlock;
+  if (p.B % kXcds == 0)
+    hipLaunchKernelGGL(k_scan_absorbed_wide_scores, dim3(nx * p.B * p.wsplit), dim3(kScoreThreads), 0, s, p, 1);
+  else
+    hipLaunchKernelGGL(k_scan_absorbed_wide_scores, dim3(nx, p.B, p.wsplit), dim3(kScoreThreads), 0, s, p, 0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.lcap <= kSoftmaxLdsTokens)
@@ -445,8 +476,12 @@ hipError_t launch_scan_absorbed_wide(const DecodeParams& p, hipStream_t s) {
   else
     hipLaunchKernelGGL(k_scan_absorbed_wide_softmax<false>, dim3(p.H, p.B), dim3(kThreads), 0, s, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(k_scan_absorbed_wide_values, dim3(scan_absorbed_wide_slabs(p.rv), p.S, p.B),
-                     dim3(kThreads), 0, s, p);
+  if (p.B % kXcds == 0)
+    hipLaunchKernelGGL(k_scan_absorbed_wide_values, dim3(scan_absorbed_wide_slabs(p.rv) * p.S * p.B), dim3(kThreads),
+                       0, s, p, 1);
+  else
+    hipLaunchKernelGGL(k_scan_absorbed_wide_values, dim3(scan_absorbed_wide_slabs(p.rv), p.S, p.B), dim3(kThreads),
+                       0, s, p, 0);
   return hipGetLastError();
 }
 
