@@ -252,7 +252,8 @@ WsLayout ws_layout(const lla_set_desc& d, int B, int S, int WS, int Dp, bool fus
     w.total = off;
     return w;
   }
-  w.qlat = off;    off = up256(off + (size_t)B * H * d.r_k * elem_bytes(d));
+  // (the two-pass scan of a wide latent keeps q~ as bf16 hi and lo parts)
+  w.qlat = off;    off = up256(off + (size_t)B * H * d.r_k * elem_bytes(d) * (lcap > 0 ? 2 : 1));
   w.qhead = off;   off = up256(off + (size_t)B * H * dh * 4);
   w.part_ml = off; off = up256(off + (size_t)B * S * H * 2 * 4);
   w.part_o = off;  off = up256(off + (size_t)B * S * H * Dp * 4);

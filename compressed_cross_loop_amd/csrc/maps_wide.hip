@@ -73,7 +73,10 @@ __global__ __launch_bounds__(kThreads) void k_qmap_wide(DecodeParams p) {
     }
   }
   __syncthreads();
+  // q~ leaves as bf16 hi and lo parts (lo = the rounding remainder, at
+  // qlat + B H r_k), so that the score pass keeps it at fp32-level accuracy
   bf16* ql = static_cast<bf16*>(p.qlat);
+  const int64_t qlo = (int64_t)B * H * rk;
   const int nblk = slab / 16;
   // B operand: q[b0 + col][16 ks + 4 grp .. + 3], one chunk ahead
   s16x4 qn[KS];
@@ -114,10 +117,16 @@ __global__ __launch_bounds__(kThreads) void k_qmap_wide(DecodeParams p) {
         for (int r = 0; r < 4; ++r) ub[col][nl + r] = acc[r];
       } else if (col < nb && n0 + nl < rk) {
         typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-        bf16x4 v;
+        bf16x4 v, w;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = static_cast<bf16>(acc[r] * p.scale);
-        *reinterpret_cast<bf16x4*>(ql + ((int64_t)(b0 + col) * H + h) * rk + n0 + nl) = v;
+        for (int r = 0; r < 4; ++r) {
+          const float x = acc[r] * p.scale;
+          v[r] = static_cast<bf16>(x);
+          w[r] = static_cast<bf16>(x - static_cast<float>(v[r]));
+        }
+        const int64_t o = ((int64_t)(b0 + col) * H + h) * rk + n0 + nl;
+        *reinterpret_cast<bf16x4*>(ql + o) = v;
+        *reinterpret_cast<bf16x4*>(ql + qlo + o) = w;
       }
     }
     if (rope) {
@@ -130,7 +139,11 @@ __global__ __launch_bounds__(kThreads) void k_qmap_wide(DecodeParams p) {
         const float c = cs[bb][fp][0], sn = cs[bb][fp][1];
         const float u = ub[bb][t];
         const float v = f < HALF ? u * c - ub[bb][t + HALF] * sn : ub[bb][t - HALF] * sn + u * c;
-        ql[((int64_t)(b0 + bb) * H + h) * rk + n] = static_cast<bf16>(v * p.scale);
+        const float xs = v * p.scale;
+        const bf16 hi = static_cast<bf16>(xs);
+        const int64_t o = ((int64_t)(b0 + bb) * H + h) * rk + n;
+        ql[o] = hi;
+        ql[qlo + o] = static_cast<bf16>(xs - static_cast<float>(hi));
       }
       __syncthreads();   // ub and cs are refilled next round
     }

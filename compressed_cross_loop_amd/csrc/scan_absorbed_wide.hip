@@ -73,7 +73,8 @@ constexpr int kKeyAhead = 4;      // = steps per q~ chunk (the key ring index is
 constexpr int kQChunk = 128;      // latent dims per staged q~ chunk
 
 __global__ __launch_bounds__(kScoreThreads) void k_scan_absorbed_wide_scores(DecodeParams p, int by_xcd) {
-  __shared__ __attribute__((aligned(16))) bf16 qs[2][64 * kQChunk];
+  __shared__ __attribute__((aligned(16))) bf16 qs[2][64 * kQChunk];   // q~ hi part, double-buffered
+  __shared__ __attribute__((aligned(16))) bf16 ql[2][64 * kQChunk];   // q~ lo part
   // workgroup -> (token block, sequence, part of r_k); with `by_xcd` the grid
   // is one-dimensional and the ids of one sequence's workgroups are
   // congruent mod 8, so the round-robin dealing puts them on one XCD and
@@ -113,8 +114,11 @@ __global__ __launch_bounds__(kScoreThreads) void k_scan_absorbed_wide_scores(Dec
   // q~ staging: piece x = tid + kScoreThreads k of a chunk is head row x / 16,
   // dims 8 (x % 16) .. + 7, kept at slot (x % 16) ^ (row % 16) of its LDS row
   constexpr int QP = 64 * 16 / kScoreThreads;   // pieces per thread
+  // the query map leaves q~ as bf16 hi and lo parts (lo at qlat + B H r_k);
+  // each K step multiplies both, which keeps the scores at fp32-level accuracy
   const bf16* qsrc[QP];
   int qoff[QP], qdst[QP];
+  const int64_t qlo = (int64_t)p.B * H * rk;
 #pragma unroll
   for (int k = 0; k < QP; ++k) {
     const int x = tid + kScoreThreads * k, row = x >> 4, c = x & 15;
@@ -122,14 +126,21 @@ __global__ __launch_bounds__(kScoreThreads) void k_scan_absorbed_wide_scores(Dec
     qoff[k] = 8 * c;
     qdst[k] = row * kQChunk + 8 * (c ^ (row & 15));
   }
-  u32x4 qreg[QP];
+  u32x4 qreg[QP], qreg_lo[QP];
   auto q_load = [&](int kc0) {   // pieces past r_k feed no step (r_k % 32 == 0): clamp their address
 #pragma unroll
-    for (int k = 0; k < QP; ++k) qreg[k] = *reinterpret_cast<const u32x4*>(qsrc[k] + min(kc0 + qoff[k], rk - 8));
+    for (int k = 0; k < QP; ++k) {
+      const bf16* src = qsrc[k] + min(kc0 + qoff[k], rk - 8);
+      qreg[k] = *reinterpret_cast<const u32x4*>(src);
+      qreg_lo[k] = *reinterpret_cast<const u32x4*>(src + qlo);
+    }
   };
   auto q_store = [&](int buf) {
 #pragma unroll
-    for (int k = 0; k < QP; ++k) *reinterpret_cast<u32x4*>(&qs[buf][qdst[k]]) = qreg[k];
+    for (int k = 0; k < QP; ++k) {
+      *reinterpret_cast<u32x4*>(&qs[buf][qdst[k]]) = qreg[k];
+      *reinterpret_cast<u32x4*>(&ql[buf][qdst[k]]) = qreg_lo[k];
+    }
   };
 
   f32x4 acc[4][4];
@@ -149,15 +160,20 @@ __global__ __launch_bounds__(kScoreThreads) void k_scan_absorbed_wide_scores(Dec
   // q~[16 hb + col][32 U + 8 grp ..], piece 4 U + grp of the row
   auto step = [&](auto U, int buf) {
     constexpr int u = decltype(U)::value;
-    bf16x8 qa[4];
+    bf16x8 qa[4], qb[4];
 #pragma unroll
-    for (int hb = 0; hb < 4; ++hb)
-      qa[hb] = *reinterpret_cast<const bf16x8*>(&qs[buf][(16 * hb + col) * kQChunk + 8 * ((4 * u + grp) ^ col)]);
+    for (int hb = 0; hb < 4; ++hb) {
+      const int o = (16 * hb + col) * kQChunk + 8 * ((4 * u + grp) ^ col);
+      qa[hb] = *reinterpret_cast<const bf16x8*>(&qs[buf][o]);
+      qb[hb] = *reinterpret_cast<const bf16x8*>(&ql[buf][o]);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int hb = 0; hb < 4; ++hb)
+      for (int hb = 0; hb < 4; ++hb) {
         acc[i][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[u][i], qa[hb], acc[i][hb], 0, 0, 0);
+        acc[i][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[u][i], qb[hb], acc[i][hb], 0, 0, 0);
+      }
   };
   // q~ chunks of this workgroup's part of r_k (part wz of wsplit parts,
   // none empty); every chunk but the last of r_k is whole

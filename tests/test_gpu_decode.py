@@ -225,6 +225,24 @@ def test_absorbed_wide_shared_latent(H, d_h, r_k, r_v, splits):
     check(poison_unread(c), "absorbed", "absorbed", splits=splits)
 
 
+@pytest.mark.parametrize("batch", [8, 16])
+@pytest.mark.parametrize("H, d_h, r_k, r_v, splits", [(6, 96, 192, 192, 0), (6, 96, 192, 192, 3),
+                                                      (55, 96, 1056, 1056, 0)])
+def test_absorbed_wide_xcd_grid(batch, H, d_h, r_k, r_v, splits):
+    """Batches that are a multiple of 8: the two-pass scan's score and value
+    passes run one-dimensional grids dealt so that a sequence's workgroups
+    share an XCD.  Ragged positions (one sequence with no latent token at all,
+    so all of its score workgroups return at once, one with a single latent
+    tile), forced splits, and the 1056-wide latent split over parts of r_k."""
+    positions = (1500, 700, 4, 1023, 1024, 20, 900, 1600, 64, 1300, 333, 1200, 2, 800, 1100, 450)[:batch]
+    c = gen.decode_inputs(860 + batch + r_k + splits, batch=batch, heads=H, head_dim=d_h, groups=1, r_k=r_k,
+                          r_v=r_v, positions=positions, window=4, dtype="bf16", loop=3, loop_first=1,
+                          loop_last=8, latent_std=1.0, exact_std=1.0, paired=False,
+                          map_scale=float(np.sqrt(r_k / d_h)))
+    assert B.lla_decode_scan_kernel(desc_of(c), 1) == "k_scan_absorbed_wide"
+    check(poison_unread(c), "absorbed", "absorbed", splits=splits)
+
+
 @pytest.mark.parametrize("H, d_h, r", [(20, 64, 256), (6, 96, 192), (18, 128, 1024)])
 @pytest.mark.parametrize("entry", ["absorbed", "hla"])
 def test_absorbed_wide_rope(H, d_h, r, entry):
