@@ -431,6 +431,8 @@ def test_decode_workspace_holds_wide_scan_rows():
     wide = desc(1, 55, 5280, 96)
     rows = 64 * 55 * 4096 * 6
     assert w(wide, 64, 4095, 0) >= rows + 2 * 55 * 96 * 5280 * 2
+    # and q~ as bf16 hi and lo parts (the lo part follows the hi part)
+    assert w(wide, 64, 4095, 0) >= rows + 2 * 55 * 96 * 5280 * 2 + 2 * 64 * 55 * 5280 * 2
     assert w(wide, 64, 4096, 0) - w(wide, 64, 4095, 0) >= 64 * 55 * 256 * 6
     hla = desc(1, 16, 512, 128)   # one-pass matrix-core scan: nothing per token
     assert w(hla, 128, 4095, 128) < 128 * 16 * 4096 * 6
